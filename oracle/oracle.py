@@ -1,0 +1,181 @@
+"""Python front of the fp64 WKV-7 oracle (test infrastructure only).
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this module. It loads `libwkv7_oracle.so`, built from
+`wkv7_oracle.c` in this directory by `build()`, and shares nothing with the
+GPU library. All inputs are upcast to fp64 (exact for fp32 and bf16 values).
+
+Semantics follow the token-order definition written out in wkv7_oracle.c:
+per (sequence, head) unit, S_t = S_{t-1} diag(w_t) + (S_{t-1} a_t) b_t^T
++ v_t k_t^T and y_t = S_t r_t, with state checkpoints every 16 tokens and the
+backward of L = sum <dy, y> + <ds_out, S_T>.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "wkv7_oracle.c")
+LIB = os.path.join(HERE, "libwkv7_oracle.so")
+CHUNK = 16
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc: fp64, -O2, no fast-math, OpenMP."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+               "-fno-fast-math", "-ffp-contract=off", SRC, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _configure(lib):
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    i = ctypes.c_int
+    lib.wkv7o_forward.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp,
+                                  i, ip, ip, ip, dp, dp, dp, dp, i, ip, i]
+    lib.wkv7o_forward.restype = i
+    lib.wkv7o_backward.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp,
+                                   i, ip, ip, dp, dp, dp,
+                                   dp, dp, dp, dp, dp, dp, dp, i, ip, i]
+    lib.wkv7o_backward.restype = i
+    lib.wkv7o_max_threads.restype = i
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build(force=True)
+        _lib = _configure(ctypes.CDLL(LIB))
+    return _lib
+
+
+class use_library:
+    """Context manager: route this module's calls through another build of
+    the oracle (the mutation tests load deliberately broken copies)."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = _load()
+        _lib = _configure(ctypes.CDLL(self.path))
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def max_threads() -> int:
+    return int(_load().wkv7o_max_threads())
+
+
+def _d(x):
+    if x is None:
+        return None
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _p(x, t=ctypes.c_double):
+    if x is None:
+        return None
+    return x.ctypes.data_as(ctypes.POINTER(t))
+
+
+def _segments(B, T, seq_start, seq_len):
+    if seq_start is None:
+        return 0, None, None, B
+    st = np.ascontiguousarray(seq_start, dtype=np.int32)
+    ln = np.ascontiguousarray(seq_len, dtype=np.int32)
+    return len(st), st, ln, len(st)
+
+
+def checkpoint_slots(T, seq_len=None, B=None):
+    """Checkpoint slot bases and total: dense rows use ceil(T/16) slots each."""
+    if seq_len is None:
+        nc = -(-T // CHUNK)
+        return np.arange(B, dtype=np.int32) * nc, B * nc
+    n = (np.asarray(seq_len, dtype=np.int64) + CHUNK - 1) // CHUNK
+    base = np.concatenate([[0], np.cumsum(n)[:-1]]).astype(np.int32) if len(n) else np.zeros(0, np.int32)
+    return base, int(n.sum())
+
+
+def forward(r, w, k, v, a, b, s0=None, *, seq_start=None, seq_len=None,
+            checkpoints=False, units=None, threads=0):
+    """Token-order fp64 forward.
+
+    Streams are [B, T, H, N]. Returns dict with y [B,T,H,N] (zeros at tokens
+    outside computed units), s_out [S,H,N,N] and, if requested, ckpt
+    [slots,H,N,N]. `units` is an optional list of (sequence, head) pairs."""
+    lib = _load()
+    B, T, H, N = r.shape
+    arrs = [_d(x) for x in (r, w, k, v, a, b)]
+    nseq, st, ln, S = _segments(B, T, seq_start, seq_len)
+    s0d = _d(s0)
+    y = np.zeros((B, T, H, N), dtype=np.float64)
+    s_out = np.zeros((S, H, N, N), dtype=np.float64)
+    ckpt = None
+    ck_base = None
+    if checkpoints:
+        ck_base, slots = checkpoint_slots(T, ln, B)
+        ckpt = np.zeros((slots, H, N, N), dtype=np.float64)
+    u = None if units is None else np.ascontiguousarray(np.asarray(units, dtype=np.int32).reshape(-1, 2))
+    rc = lib.wkv7o_forward(B, T, H, N, *[_p(x) for x in arrs], nseq,
+                           _p(st, ctypes.c_int32), _p(ln, ctypes.c_int32),
+                           _p(ck_base if nseq else None, ctypes.c_int32),
+                           _p(s0d), _p(y), _p(s_out), _p(ckpt),
+                           0 if u is None else len(u), _p(u, ctypes.c_int32), threads)
+    if rc != 0:
+        raise RuntimeError("oracle forward failed")
+    out = {"y": y, "s_out": s_out}
+    if checkpoints:
+        out["ckpt"] = ckpt
+        out["ckpt_base"] = ck_base
+    return out
+
+
+def backward(r, w, k, v, a, b, s0=None, dy=None, ds_out=None, *, seq_start=None,
+             seq_len=None, units=None, threads=0):
+    """fp64 reverse-mode gradients of L = sum <dy, y> + <ds_out, S_T>.
+    Returns dict dr, dw, dk, dv, da, db ([B,T,H,N]) and ds0 ([S,H,N,N])."""
+    lib = _load()
+    B, T, H, N = r.shape
+    arrs = [_d(x) for x in (r, w, k, v, a, b)]
+    nseq, st, ln, S = _segments(B, T, seq_start, seq_len)
+    grads = [np.zeros((B, T, H, N), dtype=np.float64) for _ in range(6)]
+    ds0 = np.zeros((S, H, N, N), dtype=np.float64)
+    u = None if units is None else np.ascontiguousarray(np.asarray(units, dtype=np.int32).reshape(-1, 2))
+    rc = lib.wkv7o_backward(B, T, H, N, *[_p(x) for x in arrs], nseq,
+                            _p(st, ctypes.c_int32), _p(ln, ctypes.c_int32),
+                            _p(_d(s0)), _p(_d(dy)), _p(_d(ds_out)),
+                            *[_p(g) for g in grads], _p(ds0),
+                            0 if u is None else len(u), _p(u, ctypes.c_int32), threads)
+    if rc != 0:
+        raise RuntimeError("oracle backward: out of memory for the state history")
+    names = ("dr", "dw", "dk", "dv", "da", "db")
+    out = dict(zip(names, grads))
+    out["ds0"] = ds0
+    return out
+
+
+def decode_step(r, w, k, v, a, b, s_in):
+    """One token per (sequence, head): streams [B, H, N], state [B, H, N, N].
+    Returns (y [B,H,N], s_out [B,H,N,N])."""
+    B, H, N = r.shape
+    streams = [np.asarray(x).reshape(B, 1, H, N) for x in (r, w, k, v, a, b)]
+    out = forward(*streams, s0=s_in)
+    return out["y"].reshape(B, H, N), out["s_out"]

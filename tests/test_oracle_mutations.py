@@ -1,0 +1,74 @@
+"""Planted mistakes: each test compiles a copy of the oracle with one plausible
+slip (wrong operand, wrong index, wrong state read, dropped term, misplaced
+checkpoint) and checks that at least one pin of test_oracle_pins.py fails for
+it. This shows the pins constrain the oracle, not merely agree with it."""
+import os
+import subprocess
+
+import pytest
+
+from oracle import oracle as O
+from tests import test_oracle_pins as P
+
+MUTATIONS = {
+    # forward (a conceptual slip is planted at every site that shares it,
+    # i.e. in the forward and in the backward's own forward sweep)
+    "a_term_reads_decayed_state": ("acc += S[i * N + j] * at[j];",
+                                   "acc += S[i * N + j] * wt[j] * at[j];", 1),
+    "a_and_b_swapped": ("sa[i] * bt[j] + vt[i] * kt[j];",
+                        "sa[i] * at[j] + vt[i] * kt[j];", 2),
+    "v_k_outer_transposed": ("sa[i] * bt[j] + vt[i] * kt[j];",
+                             "sa[i] * bt[j] + vt[j] * kt[i];", 2),
+    "y_reads_transposed_state": ("for (int j = 0; j < N; ++j) acc += S[i * N + j] * rt[j];",
+                                 "for (int j = 0; j < N; ++j) acc += S[j * N + i] * rt[j];", 1),
+    "decay_on_rows": ("S[i * N + j] = S[i * N + j] * wt[j] + sa[i]",
+                      "S[i * N + j] = S[i * N + j] * wt[i] + sa[i]", 1),
+    "checkpoint_one_token_late": ("if (ckpt && t % ORACLE_CHUNK == 0)",
+                                  "if (ckpt && t % ORACLE_CHUNK == 1)", 1),
+    "sequence_checkpoint_base_ignored": ("s[q].ckpt = seq_ckpt ? seq_ckpt[q] : 0;",
+                                         "s[q].ckpt = 0;", 1),
+    # backward
+    "dS_missing_a_term": ("dS[i * N + j] = dS[i * N + j] * wt[j] + dsa[i] * at[j];",
+                          "dS[i * N + j] = dS[i * N + j] * wt[j];", 1),
+    "dw_uses_updated_state": ("acc_w += dS[i * N + j] * Sp[i * N + j];",
+                              "acc_w += dS[i * N + j] * Sn[i * N + j];", 1),
+    "dr_uses_previous_state": ("for (int i = 0; i < N; ++i) acc += Sn[i * N + j] * dy[o + i];",
+                               "for (int i = 0; i < N; ++i) acc += Sp[i * N + j] * dy[o + i];", 1),
+    "da_uses_dS_row_sum": ("acc_a += dsa[i] * Sp[i * N + j];",
+                           "acc_a += dS[i * N + j] * Sp[i * N + j];", 1),
+    "db_uses_v": ("acc_b += dS[i * N + j] * sa[i];",
+                  "acc_b += dS[i * N + j] * vt[i];", 1),
+}
+
+
+def _all_pins_pass():
+    failed = []
+    for name, (fn, tol) in P.PINS.items():
+        try:
+            err = fn()
+        except Exception as e:  # a crash of a pin counts as a detection
+            failed.append((name, repr(e)))
+            continue
+        if not err <= tol:
+            failed.append((name, err))
+    return failed
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_mutation_is_caught(mutation, tmp_path):
+    old, new, count = MUTATIONS[mutation]
+    src = open(O.SRC).read()
+    assert src.count(old) == count, f"mutation site not found exactly {count}x: {old!r}"
+    mutated = src.replace(old, new)
+    c_path = tmp_path / "mut.c"
+    so_path = tmp_path / "libmut.so"
+    c_path.write_text(mutated)
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                    str(c_path), "-o", str(so_path)], check=True)
+    with O.use_library(str(so_path)):
+        failed = _all_pins_pass()
+    assert failed, f"no pin detects mutation {mutation}"
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert _all_pins_pass() == []
