@@ -1,0 +1,196 @@
+"""Benchmark of the WKV-7 hot path on one MI355X.
+
+One step = the whole path over one synthetic batch of the training workload
+(bf16 streams, fp32 state, B=4, T=4096, H=32, N=64, zero initial state,
+dy ~ N(0,1)): wkv7_forward writing 16-token checkpoints, then wkv7_backward.
+Inputs are resident in HBM before timing starts. The JSON line reports whole
+step throughput in tokens/s (a token spans all H heads), the roofline of the
+dominant kernel (HIP events on the launch stream), and the fp64 oracle timed
+on the host's cores over a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "WKV-7 tokens/sec fwd & fwd+bwd at H=32,N=64 bf16; % of HBM/FP32 roofline"
+N = 64
+# Algorithmic work of the token-order method per token-head.
+FWD_FLOP = 9 * N * N            # 36,864
+BWD_FLOP = 26 * N * N           # 106,496 (19 N^2 + 7 N^2 recompute)
+FWD_BYTES = 6 * 128 + 128       # bf16 streams in, y out: 896
+FWD_CKPT_BYTES = FWD_BYTES + 1024   # + one fp32 checkpoint per 16 tokens: 1920
+BWD_BYTES = 6 * 128 + 128 + 1024 + 6 * 128  # 2688
+PEAK_HBM = 8.0e12               # B/s
+PEAK_FP32 = 157.3e12            # FLOP/s, vector or matrix fp32
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def cpu_baseline(inp, budget_s):
+    """fp64 oracle forward + backward on whole (b, h) units of the same
+    workload until about budget_s seconds have been spent."""
+    from oracle import oracle as O
+    B, T, H, _ = inp.r.shape
+    threads = O.max_threads()
+    units = [(b, h) for b in range(B) for h in range(H)]
+    done = 0
+    t0 = time.perf_counter()
+    while done < len(units) and time.perf_counter() - t0 < budget_s:
+        batch = units[done:done + threads]
+        for_b = {}
+        for b, h in batch:
+            for_b.setdefault(b, []).append(h)
+        for b, hs in for_b.items():
+            sl = [x[b:b + 1, :, hs] for x in inp.streams()]
+            dy = inp.dy[b:b + 1, :, hs]
+            O.forward(*sl, checkpoints=True, threads=threads)
+            O.backward(*sl, dy=dy, threads=threads)
+        done += len(batch)
+    el = time.perf_counter() - t0
+    tok_heads = done * T
+    return {"value": tok_heads / H / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {B * H} (b,h) units x T={T}: fp64 forward with checkpoints + "
+                      f"backward, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    from linear_recurrent_lm_amd import synth
+    from linear_recurrent_lm_amd import wkv7 as W
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    W.lib()
+    B, T, H = 4, 4096, 32
+    inp = synth.make_inputs(B, T, H, N, seed=3, dtype="bf16", with_dy=True)
+    ts = [torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in inp.streams()]
+    dy = torch.from_numpy(inp.dy).to(dev).to(torch.bfloat16)
+    y = torch.empty_like(ts[0])
+    s_out = torch.empty((B, H, N, N), device=dev, dtype=torch.float32)
+    ckpt = torch.empty((W.checkpoint_slots(B, T), H, N, N), device=dev, dtype=torch.float32)
+    grads = {n: torch.empty_like(ts[0]) for n in ("dr", "dw", "dk", "dv", "da", "db")}
+
+    # Forward-only prefill workload (B=16, T=1024, H=32, random initial state).
+    pin = synth.make_inputs(16, 1024, H, N, seed=2, dtype="bf16", s0_std=0.1)
+    pts = [torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in pin.streams()]
+    ps0 = torch.from_numpy(pin.s0).to(dev)
+    py = torch.empty_like(pts[0])
+    pso = torch.empty_like(ps0)
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    fwd_ms, bwd_ms = [], []
+
+    def step(record):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record()
+        W.wkv7_forward(*ts, None, checkpoints=True, y=y, s_out=s_out, ckpt=ckpt)
+        e1.record()
+        W.wkv7_backward(*ts, ckpt, dy, None, grads=grads, want_ds0=True)
+        e2.record()
+        if record:
+            record.append((e0, e1, e2))
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for e0, e1, e2 in recs:
+        fwd_ms.append(e0.elapsed_time(e1))
+        bwd_ms.append(e1.elapsed_time(e2))
+    ms_step = wall * 1e3 / args.steps
+    tok = B * T
+    value = tok / (ms_step * 1e-3)
+
+    # prefill forward timing
+    for _ in range(args.warmup):
+        W.wkv7_forward(*pts, ps0, y=py, s_out=pso)
+    torch.cuda.synchronize()
+    pre = []
+    for _ in range(args.steps):
+        e0, e1 = ev(), ev()
+        e0.record()
+        W.wkv7_forward(*pts, ps0, y=py, s_out=pso)
+        e1.record()
+        pre.append((e0, e1))
+    torch.cuda.synchronize()
+    pre_ms = float(np.mean([a.elapsed_time(b) for a, b in pre]))
+
+    f_ms, b_ms = float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
+    th = tok * H
+    kernels = {
+        "wkv7_forward_ckpt": dict(ms=f_ms, flop=FWD_FLOP * th, bytes=FWD_CKPT_BYTES * th),
+        "wkv7_backward": dict(ms=b_ms, flop=BWD_FLOP * th, bytes=BWD_BYTES * th),
+    }
+    dom_name = max(kernels, key=lambda k: kernels[k]["ms"])
+    dom = kernels[dom_name]
+    t_hbm = dom["bytes"] / PEAK_HBM
+    t_fp = dom["flop"] / PEAK_FP32
+    if t_fp >= t_hbm:
+        achieved = dom["flop"] / (dom["ms"] * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32 / 1e12, "unit": "TFLOP/s"}
+    else:
+        achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom_name
+
+    def fracs(k):
+        kk = kernels[k]
+        t = kk["ms"] * 1e-3
+        return {"ms": kk["ms"], "tokens_per_s": tok / t,
+                "fp32_frac": kk["flop"] / t / PEAK_FP32, "hbm_frac": kk["bytes"] / t / PEAK_HBM}
+
+    pre_th = 16 * 1024 * H
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "WKV-7 forward (16-token checkpoints) + backward, bf16 streams, "
+                               "fp32 state, B=4 T=4096 H=32 N=64, zero initial state, dy~N(0,1)",
+                   "global_batch": B, "seq_len": T, "heads": H, "head_size": N,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "kernels": {k: fracs(k) for k in kernels},
+        "prefill_forward": {"workload": "bf16 B=16 T=1024 H=32, initial state N(0,0.1^2)",
+                            "ms": pre_ms, "tokens_per_s": 16 * 1024 / (pre_ms * 1e-3),
+                            "fp32_frac": FWD_FLOP * pre_th / (pre_ms * 1e-3) / PEAK_FP32,
+                            "hbm_frac": FWD_BYTES * pre_th / (pre_ms * 1e-3) / PEAK_HBM},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * wkv7.h -- C ABI of libwkv7.so, the MI355X (gfx950) WKV-7 recurrence library.
+ *
+ * The operation (RWKV-7 "Goose" WKV-7, the recurrence the rwkv-metal page's
+ * section "The Metal WKV-7 kernel" and the model card's "Transformers
+ * quickstart" section describe as the one custom kernel of the model): per
+ * independent unit -- one (sequence, head) pair -- with head size N = 64 and
+ * an fp32 state S in R^{64x64} indexed [value i, key j], every token t does
+ *
+ *     S_t = S_{t-1} diag(w_t) + (S_{t-1} a_t) b_t^T + v_t k_t^T,   y_t = S_t r_t
+ *
+ * where the a-term reads the undecayed S_{t-1} and y_t reads the updated S_t.
+ *
+ * Data layout (all buffers are device memory owned by the caller):
+ *   token streams r, w, k, v, a, b, y, dy, dr..db : [B, T, H, N], N contiguous,
+ *       element type given by wkv7_desc.dtype (fp32 or bf16);
+ *       the flat token index of (row b, position t) is b*T + t;
+ *   states s0, s_out, ds_out, ds0 : fp32 [S, H, N, N], row = value index i,
+ *       column = key index j; S = B in dense mode, num_seqs in segment mode;
+ *   checkpoints ckpt : fp32 [slots, H, N, N]; the checkpoint of chunk c of a
+ *       sequence (the state entering its token 16c, so chunk 0 holds its
+ *       initial state) sits at slot base + c, where base = b*ceil(T/16) for
+ *       dense row b and base = seq_ckpt[s] for sequence s in segment mode.
+ *       The state is checkpointed every 16 tokens as on the rwkv-metal page
+ *       (section "The Metal WKV-7 kernel") and the RWKV-MLX page (section
+ *       "Key Design Decisions", CHUNK_LEN=16 backward).
+ *
+ * Modes.
+ *   Dense (num_seqs == 0): each of the B rows is one sequence of T tokens.
+ *   Segment (num_seqs > 0): sequence s covers flat tokens
+ *       [seq_start[s], seq_start[s] + seq_len[s]), which must lie inside one
+ *       row; sequences must not overlap. Each sequence starts from its own
+ *       initial state (s0[s], or zero), so nothing crosses a boundary: this
+ *       serves packed streams with a state reset at every boundary (rwkv-lab
+ *       page, post-training trainer paragraph; model card, "Transformers
+ *       quickstart") and right-padded ragged rows (rwkv-metal page,
+ *       feature list). Tokens covered by no sequence are never read; the
+ *       forward writes y = 0 there and the backward writes zero gradients.
+ *   Any T >= 1 is accepted (no padding to a multiple of 16 is needed).
+ *
+ * Ownership and threading. The library allocates no device memory in these
+ * calls and keeps no pointer after return. Work is enqueued on `stream` (a
+ * hipStream_t passed as void*; NULL = the null stream) and the call returns
+ * without synchronising. Calls are thread-safe.
+ *
+ * Errors. Arguments are validated on the host before anything is enqueued;
+ * on any error nothing is launched. Segment tables live in device memory and
+ * cannot be checked by the host: wkv7_segments_check validates a host copy.
+ * The kernels skip (leave as zero) any sequence whose entry is out of range
+ * instead of touching memory outside the buffers. No C++ exception crosses
+ * this boundary.
+ */
+#ifndef WKV7_H
+#define WKV7_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WKV7_ABI_VERSION 1
+#define WKV7_HEAD_SIZE 64
+#define WKV7_CHUNK 16
+
+typedef enum {
+    WKV7_OK = 0,
+    WKV7_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, bad size, bad table */
+    WKV7_ERR_UNSUPPORTED = 2,        /* e.g. N != 64, unknown dtype, no gfx950 device */
+    WKV7_ERR_WORKSPACE_TOO_SMALL = 3,
+    WKV7_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} wkv7_status;
+
+typedef enum {
+    WKV7_F32 = 0,
+    WKV7_BF16 = 1
+} wkv7_dtype;
+
+typedef struct {
+    int32_t B;                  /* rows */
+    int32_t T;                  /* tokens per row, >= 1 */
+    int32_t H;                  /* heads, >= 1 */
+    int32_t N;                  /* head size; must be 64 */
+    int32_t dtype;              /* wkv7_dtype of r,w,k,v,a,b,y,dy and dr..db */
+    int32_t num_seqs;           /* 0 = dense mode */
+    const int32_t *seq_start;   /* device [num_seqs]: flat start token b*T + t */
+    const int32_t *seq_len;     /* device [num_seqs]: length >= 0 */
+    const int32_t *seq_ckpt;    /* device [num_seqs]: first checkpoint slot; needed
+                                   only when checkpoints are written or read */
+    int32_t ckpt_slots;         /* segment mode: slots in the ckpt buffer */
+} wkv7_desc;
+
+/*
+ * Forward over a batch: y (and optionally s_out, ckpt) from r..b and s0.
+ *   r, w, k, v, a, b : [B,T,H,N] inputs; w is the multiplicative decay.
+ *   s0    : [S,H,N,N] fp32 initial states, or NULL for zeros.
+ *   y     : [B,T,H,N] output (dtype); required.
+ *   s_out : [S,H,N,N] fp32 final states, or NULL. May not alias s0.
+ *   ckpt  : [slots,H,N,N] fp32 checkpoints for wkv7_backward, or NULL
+ *           (inference forward). Dense mode needs B*ceil(T/16) slots.
+ * All pointers 16-byte aligned.
+ */
+wkv7_status wkv7_forward(const wkv7_desc *d,
+                         const void *r, const void *w, const void *k,
+                         const void *v, const void *a, const void *b,
+                         const float *s0, void *y, float *s_out, float *ckpt,
+                         void *stream);
+
+/*
+ * Backward: gradients of L = sum <dy, y> + <ds_out, S_T> with respect to
+ * r, w, k, v, a, b (written in dtype) and the initial state (fp32).
+ *   ckpt   : checkpoints written by wkv7_forward on the same inputs and s0.
+ *   dy     : [B,T,H,N] upstream gradient of y (dtype), or NULL for zero.
+ *   ds_out : [S,H,N,N] fp32 upstream gradient of the final state, or NULL.
+ *   dr..db : [B,T,H,N] outputs (dtype); required.
+ *   ds0    : [S,H,N,N] fp32 gradient of the initial state, or NULL.
+ *   workspace / workspace_bytes : scratch of at least wkv7_workspace_bytes.
+ * The recurrence is recomputed from the 16-token checkpoints in fp32, not
+ * reconstructed by dividing by the decay.
+ */
+wkv7_status wkv7_backward(const wkv7_desc *d,
+                          const void *r, const void *w, const void *k,
+                          const void *v, const void *a, const void *b,
+                          const float *ckpt, const void *dy, const float *ds_out,
+                          void *dr, void *dw, void *dk, void *dv, void *da, void *db,
+                          float *ds0, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
+ * One decode step for B independent sequences (the rwkv-metal page's
+ * wkv7_step; the rwkv-lab page's in-place one-token state transition).
+ *   r..b  : [B,H,N] one token per sequence (dtype).
+ *   s_in  : [B,H,N,N] fp32 state before the token.
+ *   s_out : [B,H,N,N] fp32 state after the token; may equal s_in (in place),
+ *           otherwise must not overlap it.
+ *   y     : [B,H,N] output (dtype).
+ */
+wkv7_status wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype,
+                             const void *r, const void *w, const void *k,
+                             const void *v, const void *a, const void *b,
+                             const float *s_in, float *s_out, void *y, void *stream);
+
+/* Number of checkpoint slots a dense forward needs: B * ceil(T / 16). */
+wkv7_status wkv7_checkpoint_slots(int32_t B, int32_t T, int64_t *slots);
+
+/* Scratch bytes wkv7_backward needs for this descriptor (may be 0). */
+wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes);
+
+/*
+ * Host-side check of a segment table (host copies of seq_start / seq_len):
+ * lengths >= 0, every sequence inside one row of T tokens, starts sorted and
+ * sequences disjoint. Fills seq_ckpt_out[num_seqs] (may be NULL) with the
+ * exclusive prefix sum of ceil(len / 16) and *slots_out (may be NULL) with
+ * the total, i.e. the checkpoint layout wkv7_forward expects.
+ */
+wkv7_status wkv7_segments_check(int32_t B, int32_t T, int32_t num_seqs,
+                                const int32_t *seq_start, const int32_t *seq_len,
+                                int32_t *seq_ckpt_out, int64_t *slots_out);
+
+const char *wkv7_status_string(wkv7_status s);
+int32_t wkv7_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WKV7_H */

@@ -1,0 +1,225 @@
+// Host side of libwkv7.so: the C ABI declared in include/wkv7.h.
+// Every argument is checked before anything touches the HIP runtime, so the
+// validation paths work (and are tested) on machines without a GPU.
+#include <atomic>
+#include <cstring>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/wkv7.h"
+#include "wkv7_kernels.h"
+
+namespace {
+
+using wkv7::kChunk;
+using wkv7::kN;
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+size_t elem_size(int dtype) { return dtype == WKV7_BF16 ? 2 : 4; }
+
+wkv7_status check_desc(const wkv7_desc *d) {
+    if (!d) return WKV7_ERR_INVALID_ARGUMENT;
+    if (d->N != kN) return WKV7_ERR_UNSUPPORTED;
+    if (d->dtype != WKV7_F32 && d->dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
+    if (d->B < 1 || d->T < 1 || d->H < 1) return WKV7_ERR_INVALID_ARGUMENT;
+    const int64_t toks = (int64_t)d->B * d->T;
+    if (toks > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
+    if (toks * d->H * kN > kMaxElems) return WKV7_ERR_INVALID_ARGUMENT;
+    if (d->num_seqs < 0) return WKV7_ERR_INVALID_ARGUMENT;
+    if (d->num_seqs > 0 && (!d->seq_start || !d->seq_len)) return WKV7_ERR_INVALID_ARGUMENT;
+    const int64_t S = d->num_seqs > 0 ? d->num_seqs : d->B;
+    if (S * d->H > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
+    return WKV7_OK;
+}
+
+int64_t num_states(const wkv7_desc *d) { return d->num_seqs > 0 ? d->num_seqs : d->B; }
+
+wkv7_status check_streams(const void *const *ptrs, int n) {
+    for (int q = 0; q < n; ++q)
+        if (!ptrs[q] || !aligned16(ptrs[q])) return WKV7_ERR_INVALID_ARGUMENT;
+    return WKV7_OK;
+}
+
+wkv7_status check_ckpt(const wkv7_desc *d, const float *ckpt) {
+    if (!ckpt) return WKV7_OK;
+    if (!aligned16(ckpt)) return WKV7_ERR_INVALID_ARGUMENT;
+    if (d->num_seqs > 0 && (!d->seq_ckpt || d->ckpt_slots < 0)) return WKV7_ERR_INVALID_ARGUMENT;
+    return WKV7_OK;
+}
+
+// 0 = unknown, 1 = gfx950, 2 = other / unusable.
+std::atomic<int> g_dev_ok[64];
+
+wkv7_status check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return WKV7_ERR_HIP;
+    if (dev < 0 || dev >= 64) return WKV7_ERR_UNSUPPORTED;
+    int st = g_dev_ok[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return WKV7_ERR_HIP;
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_dev_ok[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? WKV7_OK : WKV7_ERR_UNSUPPORTED;
+}
+
+wkv7::SegParams seg_params(const wkv7_desc *d, bool need_ckpt) {
+    wkv7::SegParams s;
+    s.B = d->B; s.T = d->T; s.H = d->H;
+    s.num_seqs = d->num_seqs;
+    s.seq_start = d->seq_start;
+    s.seq_len = d->seq_len;
+    s.seq_ckpt = d->seq_ckpt;
+    s.ckpt_slots = d->ckpt_slots;
+    s.need_ckpt = need_ckpt ? 1 : 0;
+    return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t wkv7_abi_version(void) { return WKV7_ABI_VERSION; }
+
+const char *wkv7_status_string(wkv7_status s) {
+    switch (s) {
+    case WKV7_OK: return "ok";
+    case WKV7_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case WKV7_ERR_UNSUPPORTED: return "unsupported";
+    case WKV7_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case WKV7_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+wkv7_status wkv7_checkpoint_slots(int32_t B, int32_t T, int64_t *slots) {
+    if (!slots || B < 1 || T < 1) return WKV7_ERR_INVALID_ARGUMENT;
+    *slots = (int64_t)B * ((T + kChunk - 1) / kChunk);
+    return WKV7_OK;
+}
+
+wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes) {
+    if (!bytes) return WKV7_ERR_INVALID_ARGUMENT;
+    const wkv7_status st = check_desc(d);
+    if (st != WKV7_OK) return st;
+    *bytes = 0;
+    return WKV7_OK;
+}
+
+wkv7_status wkv7_segments_check(int32_t B, int32_t T, int32_t num_seqs, const int32_t *seq_start,
+                                const int32_t *seq_len, int32_t *seq_ckpt_out, int64_t *slots_out) {
+    if (B < 1 || T < 1 || num_seqs < 0) return WKV7_ERR_INVALID_ARGUMENT;
+    if (num_seqs > 0 && (!seq_start || !seq_len)) return WKV7_ERR_INVALID_ARGUMENT;
+    const int64_t total = (int64_t)B * T;
+    int64_t prev_end = 0, slots = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int64_t st = seq_start[s], ln = seq_len[s];
+        if (ln < 0 || st < 0 || st + ln > total) return WKV7_ERR_INVALID_ARGUMENT;
+        if (st < prev_end) return WKV7_ERR_INVALID_ARGUMENT;   // unsorted or overlapping
+        if (ln > 0 && st / T != (st + ln - 1) / T) return WKV7_ERR_INVALID_ARGUMENT;
+        prev_end = st + ln;
+        if (slots > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
+        if (seq_ckpt_out) seq_ckpt_out[s] = (int32_t)slots;
+        slots += (ln + kChunk - 1) / kChunk;
+    }
+    if (slots > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
+    if (slots_out) *slots_out = slots;
+    return WKV7_OK;
+}
+
+wkv7_status wkv7_forward(const wkv7_desc *d, const void *r, const void *w, const void *k,
+                         const void *v, const void *a, const void *b, const float *s0, void *y,
+                         float *s_out, float *ckpt, void *stream) {
+    wkv7_status st = check_desc(d);
+    if (st != WKV7_OK) return st;
+    const void *streams[7] = {r, w, k, v, a, b, y};
+    if ((st = check_streams(streams, 7)) != WKV7_OK) return st;
+    if ((s0 && !aligned16(s0)) || (s_out && !aligned16(s_out))) return WKV7_ERR_INVALID_ARGUMENT;
+    const size_t state_bytes = (size_t)num_states(d) * d->H * kN * kN * sizeof(float);
+    if (s0 && s_out && ranges_overlap(s0, state_bytes, s_out, state_bytes))
+        return WKV7_ERR_INVALID_ARGUMENT;
+    if ((st = check_ckpt(d, ckpt)) != WKV7_OK) return st;
+    if ((st = check_device()) != WKV7_OK) return st;
+
+    hipStream_t hs = (hipStream_t)stream;
+    wkv7::FwdArgs args;
+    args.seg = seg_params(d, ckpt != nullptr);
+    args.dtype = d->dtype;
+    args.r = r; args.w = w; args.k = k; args.v = v; args.a = a; args.b = b;
+    args.s0 = s0; args.y = y; args.s_out = s_out; args.ckpt = ckpt;
+    if (d->num_seqs > 0) {
+        void *outs[1] = {y};
+        if (wkv7::launch_zero_uncovered(args.seg, d->dtype, outs, 1, hs) != hipSuccess)
+            return WKV7_ERR_HIP;
+    }
+    if (wkv7::launch_forward(args, hs) != hipSuccess) return WKV7_ERR_HIP;
+    return WKV7_OK;
+}
+
+wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, const void *k,
+                          const void *v, const void *a, const void *b, const float *ckpt,
+                          const void *dy, const float *ds_out, void *dr, void *dw, void *dk,
+                          void *dv, void *da, void *db, float *ds0, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    wkv7_status st = check_desc(d);
+    if (st != WKV7_OK) return st;
+    const void *streams[12] = {r, w, k, v, a, b, dr, dw, dk, dv, da, db};
+    if ((st = check_streams(streams, 12)) != WKV7_OK) return st;
+    if (dy && !aligned16(dy)) return WKV7_ERR_INVALID_ARGUMENT;
+    if ((ds_out && !aligned16(ds_out)) || (ds0 && !aligned16(ds0))) return WKV7_ERR_INVALID_ARGUMENT;
+    if (!ckpt) return WKV7_ERR_INVALID_ARGUMENT;
+    if ((st = check_ckpt(d, ckpt)) != WKV7_OK) return st;
+    size_t need = 0;
+    wkv7_workspace_bytes(d, &need);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return WKV7_ERR_WORKSPACE_TOO_SMALL;
+    if ((st = check_device()) != WKV7_OK) return st;
+
+    hipStream_t hs = (hipStream_t)stream;
+    wkv7::BwdArgs args;
+    args.seg = seg_params(d, true);
+    args.dtype = d->dtype;
+    args.r = r; args.w = w; args.k = k; args.v = v; args.a = a; args.b = b;
+    args.ckpt = ckpt; args.dy = dy; args.ds_out = ds_out;
+    args.dr = dr; args.dw = dw; args.dk = dk; args.dv = dv; args.da = da; args.db = db;
+    args.ds0 = ds0;
+    if (d->num_seqs > 0) {
+        void *outs[6] = {dr, dw, dk, dv, da, db};
+        if (wkv7::launch_zero_uncovered(args.seg, d->dtype, outs, 6, hs) != hipSuccess)
+            return WKV7_ERR_HIP;
+    }
+    if (wkv7::launch_backward(args, hs) != hipSuccess) return WKV7_ERR_HIP;
+    return WKV7_OK;
+}
+
+wkv7_status wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, const void *r,
+                             const void *w, const void *k, const void *v, const void *a,
+                             const void *b, const float *s_in, float *s_out, void *y,
+                             void *stream) {
+    if (N != kN) return WKV7_ERR_UNSUPPORTED;
+    if (dtype != WKV7_F32 && dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || (int64_t)B * H > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
+    const void *streams[9] = {r, w, k, v, a, b, y, s_in, s_out};
+    wkv7_status st = check_streams(streams, 9);
+    if (st != WKV7_OK) return st;
+    const size_t state_bytes = (size_t)B * H * kN * kN * sizeof(float);
+    if (s_in != s_out && ranges_overlap(s_in, state_bytes, s_out, state_bytes))
+        return WKV7_ERR_INVALID_ARGUMENT;
+    if ((st = check_device()) != WKV7_OK) return st;
+    wkv7::DecArgs args;
+    args.B = B; args.H = H; args.dtype = dtype;
+    args.r = r; args.w = w; args.k = k; args.v = v; args.a = a; args.b = b;
+    args.s_in = s_in; args.s_out = s_out; args.y = y;
+    if (wkv7::launch_decode(args, (hipStream_t)stream) != hipSuccess) return WKV7_ERR_HIP;
+    return WKV7_OK;
+}
+
+}  // extern "C"

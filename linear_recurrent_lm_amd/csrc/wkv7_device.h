@@ -1,0 +1,96 @@
+// Device-side helpers shared by the WKV-7 kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wkv7 {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kN = 64;       // head size
+constexpr int kChunk = 16;   // checkpoint interval in tokens
+
+// Unit resolution: one (sequence, head) pair. Dense mode: sequence = row.
+struct SegParams {
+    int32_t B, T, H;
+    int32_t num_seqs;            // 0 = dense
+    const int32_t *seq_start;
+    const int32_t *seq_len;
+    const int32_t *seq_ckpt;
+    int32_t ckpt_slots;
+    int32_t need_ckpt;           // 1 when checkpoints are read or written
+};
+
+struct Unit {
+    int64_t start;   // flat token index of the first token
+    int32_t len;     // 0 = skip
+    int64_t ckpt;    // first checkpoint slot
+};
+
+// Reads the segment table entry of sequence s and rejects entries that would
+// leave the buffers (negative length, crossing a row, checkpoint slots out of
+// range): such a sequence is treated as empty.
+__device__ inline Unit resolve_unit(const SegParams &p, int s) {
+    Unit u;
+    const int64_t nc = (p.T + kChunk - 1) / kChunk;
+    if (p.num_seqs == 0) {
+        u.start = (int64_t)s * p.T;
+        u.len = p.T;
+        u.ckpt = (int64_t)s * nc;
+        return u;
+    }
+    const int64_t st = p.seq_start[s];
+    const int64_t ln = p.seq_len[s];
+    u.start = st;
+    u.len = (int32_t)ln;
+    u.ckpt = p.seq_ckpt ? (int64_t)p.seq_ckpt[s] : 0;
+    const int64_t total = (int64_t)p.B * p.T;
+    bool ok = ln >= 0 && st >= 0 && st + ln <= total;
+    if (ok && ln > 0) ok = (st / p.T) == ((st + ln - 1) / p.T);
+    if (ok && p.need_ckpt && ln > 0) {
+        const int64_t chunks = (ln + kChunk - 1) / kChunk;
+        ok = p.seq_ckpt != nullptr && u.ckpt >= 0 && u.ckpt + chunks <= p.ckpt_slots;
+    }
+    if (!ok) u.len = 0;
+    return u;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename TI> struct IO;
+
+template <> struct IO<float> {
+    __device__ static __forceinline__ float ld(const float *p, int64_t i) { return p[i]; }
+    __device__ static __forceinline__ void st(float *p, int64_t i, float x) { p[i] = x; }
+};
+
+template <> struct IO<uint16_t> {
+    __device__ static __forceinline__ float ld(const uint16_t *p, int64_t i) { return bf16_to_f32(p[i]); }
+    __device__ static __forceinline__ void st(uint16_t *p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
+};
+
+// Is flat token `tok` of a row-major [B*T] token space covered by a sequence?
+// Binary search over the (sorted) starts; used only to zero uncovered tokens.
+__device__ inline bool token_covered(const SegParams &p, int64_t tok) {
+    int lo = 0, hi = p.num_seqs - 1, found = -1;
+    while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)p.seq_start[mid] <= tok) { found = mid; lo = mid + 1; }
+        else hi = mid - 1;
+    }
+    if (found < 0) return false;
+    return tok < (int64_t)p.seq_start[found] + (int64_t)p.seq_len[found];
+}
+
+}  // namespace wkv7

@@ -1,0 +1,49 @@
+// Launch interfaces of the WKV-7 kernels (host side, C++).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wkv7_device.h"
+
+namespace wkv7 {
+
+struct FwdArgs {
+    SegParams seg;
+    int dtype;                       // 0 fp32, 1 bf16
+    const void *r, *w, *k, *v, *a, *b;
+    const float *s0;
+    void *y;
+    float *s_out;
+    float *ckpt;
+};
+
+struct BwdArgs {
+    SegParams seg;
+    int dtype;
+    const void *r, *w, *k, *v, *a, *b;
+    const float *ckpt;
+    const void *dy;
+    const float *ds_out;
+    void *dr, *dw, *dk, *dv, *da, *db;
+    float *ds0;
+};
+
+struct DecArgs {
+    int32_t B, H;
+    int dtype;
+    const void *r, *w, *k, *v, *a, *b;
+    const float *s_in;
+    float *s_out;
+    void *y;
+};
+
+hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
+hipError_t launch_decode(const DecArgs &a, hipStream_t stream);
+
+// Segment mode: write zeros to `nptr` token streams at tokens no sequence covers.
+hipError_t launch_zero_uncovered(const SegParams &seg, int dtype, void *const *ptrs,
+                                 int nptr, hipStream_t stream);
+
+}  // namespace wkv7

@@ -134,6 +134,16 @@ def packed_layout(lengths: np.ndarray, streams: int):
     return T_pad, start.astype(np.int32), lengths.astype(np.int32)
 
 
+def sorted_table(seq_start, seq_len):
+    """Order a segment table by start token (the library requires sorted
+    starts). Returns (order, start[order], len[order]); entry q of the sorted
+    table is sequence order[q] of the original table."""
+    seq_start = np.asarray(seq_start, dtype=np.int64)
+    order = np.argsort(seq_start, kind="stable")
+    return (order, seq_start[order].astype(np.int32),
+            np.asarray(seq_len)[order].astype(np.int32))
+
+
 def padded_layout(lengths: np.ndarray, T: int):
     """Right-padded layout: sequence i occupies row i from token 0."""
     lengths = np.asarray(lengths, dtype=np.int64)

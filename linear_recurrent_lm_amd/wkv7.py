@@ -1,0 +1,275 @@
+"""Thin Python binding of libwkv7.so (the C ABI in include/wkv7.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the launch stream, outputs are allocated with torch.empty.
+Every step of the recurrence runs in the library's HIP kernels; if the
+library is missing this module raises instead of computing anything.
+
+Functions carry the C names (wkv7_forward, wkv7_backward, wkv7_decode_step,
+...). Layouts: streams [B, T, H, 64] (fp32 or bf16, contiguous), states
+[S, H, 64, 64] fp32, checkpoints [slots, H, 64, 64] fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libwkv7.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "wkv7.h")
+
+N = 64
+CHUNK = 16
+F32, BF16 = 0, 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small",
+          4: "HIP runtime error"}
+
+
+class WKV7Error(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)} ({code})")
+        self.code = code
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("dtype", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("seq_start", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
+                ("seq_ckpt", ctypes.c_void_p), ("ckpt_slots", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/wkv7.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(wkv7_[a-z_]+)\s*\(", text)))
+
+
+def lib():
+    """Load libwkv7.so (built by linear_recurrent_lm_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run python -m linear_recurrent_lm_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        dptr = ctypes.POINTER(Desc)
+        L.wkv7_forward.argtypes = [dptr] + [vp] * 11
+        L.wkv7_backward.argtypes = [dptr] + [vp] * 16 + [vp, sz, vp]
+        L.wkv7_decode_step.argtypes = [i32, i32, i32, i32] + [vp] * 10
+        L.wkv7_checkpoint_slots.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int64)]
+        L.wkv7_workspace_bytes.argtypes = [dptr, ctypes.POINTER(ctypes.c_size_t)]
+        L.wkv7_segments_check.argtypes = [i32, i32, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
+        L.wkv7_status_string.argtypes = [i32]
+        L.wkv7_status_string.restype = ctypes.c_char_p
+        L.wkv7_abi_version.restype = i32
+        for fn in ("wkv7_forward", "wkv7_backward", "wkv7_decode_step", "wkv7_checkpoint_slots",
+                   "wkv7_workspace_bytes", "wkv7_segments_check"):
+            getattr(L, fn).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(fn, code):
+    if code != 0:
+        raise WKV7Error(fn, code)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _req(t, name, dev, dtype=None, shape=None):
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} must be on {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+class Segments:
+    """A validated segment table: host copies, device copies (int32) and the
+    per-sequence checkpoint slot bases. Build once, reuse across calls."""
+
+    def __init__(self, B, T, seq_start, seq_len, device):
+        torch = _torch()
+        st = np.ascontiguousarray(np.asarray(seq_start, dtype=np.int32))
+        ln = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int32))
+        if st.shape != ln.shape or st.ndim != 1 or len(st) == 0:
+            raise ValueError("seq_start / seq_len must be equal-length 1-D and non-empty")
+        base = np.zeros(len(st), dtype=np.int32)
+        slots = ctypes.c_int64(0)
+        _check("wkv7_segments_check", lib().wkv7_segments_check(
+            B, T, len(st), st.ctypes.data, ln.ctypes.data, base.ctypes.data, ctypes.byref(slots)))
+        self.B, self.T = B, T
+        self.host_start, self.host_len, self.host_ckpt = st, ln, base
+        self.slots = int(slots.value)
+        self.num_seqs = len(st)
+        self.start = torch.from_numpy(st).to(device)
+        self.len = torch.from_numpy(ln).to(device)
+        self.ckpt = torch.from_numpy(base).to(device)
+
+
+def _desc(B, T, H, dtype, seg: Segments | None):
+    d = Desc()
+    d.B, d.T, d.H, d.N, d.dtype = B, T, H, N, dtype
+    if seg is None:
+        d.num_seqs = 0
+        d.ckpt_slots = 0
+    else:
+        d.num_seqs = seg.num_seqs
+        d.seq_start = seg.start.data_ptr()
+        d.seq_len = seg.len.data_ptr()
+        d.seq_ckpt = seg.ckpt.data_ptr()
+        d.ckpt_slots = seg.slots
+    return d
+
+
+def checkpoint_slots(B, T, seg: Segments | None = None) -> int:
+    if seg is not None:
+        return seg.slots
+    n = ctypes.c_int64(0)
+    _check("wkv7_checkpoint_slots", lib().wkv7_checkpoint_slots(B, T, ctypes.byref(n)))
+    return int(n.value)
+
+
+def wkv7_forward(r, w, k, v, a, b, s0=None, *, segments: Segments | None = None,
+                 checkpoints: bool = False, state_out: bool = True, y=None, s_out=None,
+                 ckpt=None):
+    """y, s_out, ckpt = wkv7_forward(...). s_out/ckpt are None when not requested."""
+    torch = _torch()
+    B, T, H, n = r.shape
+    if n != N:
+        raise ValueError("head size must be 64")
+    dev = r.device
+    for name, t in zip("rwkvab", (r, w, k, v, a, b)):
+        _req(t, name, dev, r.dtype, r.shape)
+    S = segments.num_seqs if segments is not None else B
+    if s0 is not None:
+        _req(s0, "s0", dev, torch.float32, (S, H, N, N))
+    y = torch.empty_like(r) if y is None else y
+    _req(y, "y", dev, r.dtype, r.shape)
+    if state_out and s_out is None:
+        s_out = torch.empty((S, H, N, N), device=dev, dtype=torch.float32)
+    if not state_out:
+        s_out = None
+    if checkpoints and ckpt is None:
+        ckpt = torch.empty((checkpoint_slots(B, T, segments), H, N, N), device=dev,
+                           dtype=torch.float32)
+    if not checkpoints:
+        ckpt = None
+    d = _desc(B, T, H, _dtype_code(r), segments)
+    _check("wkv7_forward", lib().wkv7_forward(
+        ctypes.byref(d), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(s0), _ptr(y),
+        _ptr(s_out), _ptr(ckpt), _stream()))
+    return y, s_out, ckpt
+
+
+def wkv7_workspace_bytes(B, T, H, dtype, segments: Segments | None = None) -> int:
+    d = _desc(B, T, H, dtype, segments)
+    n = ctypes.c_size_t(0)
+    _check("wkv7_workspace_bytes", lib().wkv7_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return int(n.value)
+
+
+def wkv7_backward(r, w, k, v, a, b, ckpt, dy=None, ds_out=None, *,
+                  segments: Segments | None = None, want_ds0: bool = True, workspace=None,
+                  grads=None):
+    """Returns dict dr, dw, dk, dv, da, db (dtype of r) and ds0 (fp32 or None)."""
+    torch = _torch()
+    B, T, H, n = r.shape
+    dev = r.device
+    for name, t in zip("rwkvab", (r, w, k, v, a, b)):
+        _req(t, name, dev, r.dtype, r.shape)
+    S = segments.num_seqs if segments is not None else B
+    _req(ckpt, "ckpt", dev, torch.float32, (checkpoint_slots(B, T, segments), H, N, N))
+    if dy is not None:
+        _req(dy, "dy", dev, r.dtype, r.shape)
+    if ds_out is not None:
+        _req(ds_out, "ds_out", dev, torch.float32, (S, H, N, N))
+    names = ("dr", "dw", "dk", "dv", "da", "db")
+    if grads is None:
+        grads = {nm: torch.empty_like(r) for nm in names}
+    ds0 = torch.empty((S, H, N, N), device=dev, dtype=torch.float32) if want_ds0 else None
+    need = wkv7_workspace_bytes(B, T, H, _dtype_code(r), segments)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d = _desc(B, T, H, _dtype_code(r), segments)
+    _check("wkv7_backward", lib().wkv7_backward(
+        ctypes.byref(d), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(ckpt), _ptr(dy),
+        _ptr(ds_out), *[_ptr(grads[nm]) for nm in names], _ptr(ds0), _ptr(workspace),
+        ws_bytes, _stream()))
+    out = dict(grads)
+    out["ds0"] = ds0
+    return out
+
+
+def wkv7_decode_step(r, w, k, v, a, b, s_in, s_out=None, y=None):
+    """One token per (sequence, head): streams [B, H, 64], state [B, H, 64, 64].
+    Pass s_out=s_in to update the state in place. Returns (y, s_out)."""
+    torch = _torch()
+    B, H, n = r.shape
+    dev = r.device
+    for name, t in zip("rwkvab", (r, w, k, v, a, b)):
+        _req(t, name, dev, r.dtype, r.shape)
+    _req(s_in, "s_in", dev, torch.float32, (B, H, N, N))
+    if s_out is None:
+        s_out = torch.empty_like(s_in)
+    _req(s_out, "s_out", dev, torch.float32, (B, H, N, N))
+    y = torch.empty_like(r) if y is None else y
+    _check("wkv7_decode_step", lib().wkv7_decode_step(
+        B, H, n, _dtype_code(r), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(s_in),
+        _ptr(s_out), _ptr(y), _stream()))
+    return y, s_out
+
+
+def wkv7_abi_version() -> int:
+    return int(lib().wkv7_abi_version())
+
+
+def wkv7_status_string(code: int) -> str:
+    return lib().wkv7_status_string(code).decode()
+
+
+def wkv7_segments_check(B, T, seq_start, seq_len):
+    """Host validation of a segment table; returns (seq_ckpt, slots)."""
+    st = np.ascontiguousarray(np.asarray(seq_start, dtype=np.int32))
+    ln = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int32))
+    base = np.zeros(len(st), dtype=np.int32)
+    slots = ctypes.c_int64(0)
+    _check("wkv7_segments_check", lib().wkv7_segments_check(
+        B, T, len(st), st.ctypes.data if len(st) else None, ln.ctypes.data if len(ln) else None,
+        base.ctypes.data if len(st) else None, ctypes.byref(slots)))
+    return base, int(slots.value)
+
+
+def wkv7_checkpoint_slots(B, T) -> int:
+    return checkpoint_slots(B, T)

@@ -1,0 +1,92 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, run the
+oracle on the same (rounded) values, and measure per-unit relative error.
+
+Error metric (per output tensor X and per unit u = one (sequence, head)):
+    err_u = max |X_gpu - X_ref| / max(max |X_ref|, 1e-30)
+and a test reports max_u err_u. Tolerances: 1e-5 for fp32 streams and for
+every fp32 state output (final states, checkpoints); 2e-2 for bf16 y;
+5e-2 for gradients (r, w, k, v, a, b and the initial state).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TOL_F32 = 1e-5
+TOL_BF16_Y = 2e-2
+TOL_GRAD = 5e-2
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def dev_stream(x, dtype: str, device="cuda:0"):
+    """fp32 numpy array (bf16-representable when dtype == 'bf16') -> device tensor."""
+    torch = torch_mod()
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def dev_f32(x, device="cuda:0"):
+    torch = torch_mod()
+    return None if x is None else torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def unit_err_dense(x, ref):
+    """Streams [B,T,H,N]: unit = (b, h)."""
+    num = np.max(np.abs(x - ref), axis=(1, 3))
+    den = np.maximum(np.max(np.abs(ref), axis=(1, 3)), 1e-30)
+    return float(np.max(num / den))
+
+
+def unit_err_state(x, ref):
+    """States [S,H,N,N]: unit = (s, h)."""
+    num = np.max(np.abs(x - ref), axis=(2, 3))
+    den = np.maximum(np.max(np.abs(ref), axis=(2, 3)), 1e-30)
+    return float(np.max(num / den))
+
+
+def unit_err_ckpt(x, ref, bases, nchunks):
+    """Checkpoints [slots,H,N,N]: unit = (sequence, h) over its slots."""
+    worst = 0.0
+    for base, nc in zip(bases, nchunks):
+        if nc == 0:
+            continue
+        xs, rs = x[base:base + nc], ref[base:base + nc]
+        num = np.max(np.abs(xs - rs), axis=(0, 2, 3))
+        den = np.maximum(np.max(np.abs(rs), axis=(0, 2, 3)), 1e-30)
+        worst = max(worst, float(np.max(num / den)))
+    return worst
+
+
+def unit_err_segments(x, ref, starts, lengths, T):
+    """Streams [B,T,H,N] in segment mode: unit = (sequence, h)."""
+    xf = x.reshape(-1, *x.shape[2:])
+    rf = ref.reshape(-1, *ref.shape[2:])
+    worst = 0.0
+    for st, L in zip(starts, lengths):
+        if L == 0:
+            continue
+        xs, rs = xf[st:st + L], rf[st:st + L]
+        num = np.max(np.abs(xs - rs), axis=(0, 2))
+        den = np.maximum(np.max(np.abs(rs), axis=(0, 2)), 1e-30)
+        worst = max(worst, float(np.max(num / den)))
+    return worst
+
+
+def sample_units(S, H, n, seed):
+    rng = np.random.default_rng(seed)
+    picks = {(0, 0), (S - 1, H - 1)}
+    while len(picks) < min(n, S * H):
+        picks.add((int(rng.integers(S)), int(rng.integers(H))))
+    return sorted(picks)
+
+
+def gather_units_dense(x, units):
+    """[B,T,H,N] -> [n, T, N] rows of the sampled (b, h) units."""
+    return np.stack([x[b, :, h] for b, h in units])

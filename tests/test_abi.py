@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/wkv7.h declares, and rejects bad arguments with the documented status
+codes before touching the HIP runtime (no compute call is made here)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from linear_recurrent_lm_amd import wkv7 as W
+from linear_recurrent_lm_amd import synth
+
+INVALID, UNSUPPORTED, WS = 1, 2, 3
+
+# Fake, 16-byte aligned, non-null device addresses: validation must fail on
+# another argument before any of these could be dereferenced.
+P = [ctypes.c_void_p(0x1000 * (q + 1)) for q in range(20)]
+
+
+def desc(**kw):
+    d = W.Desc()
+    d.B, d.T, d.H, d.N, d.dtype, d.num_seqs, d.ckpt_slots = 2, 32, 4, 64, 1, 0, 0
+    for key, val in kw.items():
+        setattr(d, key, val)
+    return d
+
+
+def fwd(d, *, ptrs=None, s0=None, y=P[6], s_out=None, ckpt=None):
+    ptrs = ptrs or P[:6]
+    return W.lib().wkv7_forward(ctypes.byref(d) if d is not None else None, *ptrs, s0, y,
+                                s_out, ckpt, None)
+
+
+def test_library_exports_every_declared_function():
+    L = W.lib()
+    names = W.declared_functions()
+    assert {"wkv7_forward", "wkv7_backward", "wkv7_decode_step"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+
+
+def test_version_and_status_strings():
+    assert W.wkv7_abi_version() == 1
+    assert W.wkv7_status_string(0) == "ok"
+    assert W.wkv7_status_string(3) == "workspace too small"
+    assert W.wkv7_status_string(99) == "unknown status"
+
+
+def test_forward_rejects_bad_descriptors():
+    assert fwd(None) == INVALID
+    assert fwd(desc(N=128)) == UNSUPPORTED
+    assert fwd(desc(dtype=7)) == UNSUPPORTED
+    for bad in (dict(B=0), dict(T=0), dict(H=0), dict(T=-5), dict(num_seqs=-1)):
+        assert fwd(desc(**bad)) == INVALID, bad
+    assert fwd(desc(B=1 << 20, T=1 << 12)) == INVALID          # B*T over int32
+    assert fwd(desc(num_seqs=3)) == INVALID                     # tables missing
+
+
+def test_forward_rejects_bad_pointers():
+    d = desc()
+    for q in range(6):
+        ptrs = list(P[:6]); ptrs[q] = None
+        assert fwd(d, ptrs=ptrs) == INVALID
+        ptrs = list(P[:6]); ptrs[q] = ctypes.c_void_p(0x1004)
+        assert fwd(d, ptrs=ptrs) == INVALID
+    assert fwd(d, y=None) == INVALID
+    assert fwd(d, s0=ctypes.c_void_p(0x2008)) == INVALID
+    # s_out may not alias s0
+    assert fwd(d, s0=P[10], s_out=ctypes.c_void_p(P[10].value + 4096)) == INVALID
+    # segment-mode checkpoints need the slot table
+    arr = ctypes.c_void_p(0x9000)
+    assert fwd(desc(num_seqs=2, seq_start=arr.value, seq_len=arr.value), ckpt=P[12]) == INVALID
+
+
+def test_backward_rejects_bad_arguments():
+    L = W.lib()
+    d = desc()
+    grads = P[7:13]
+    call = lambda d, ckpt=P[6], grads=grads, ws=None, wsb=0: L.wkv7_backward(
+        ctypes.byref(d), *P[:6], ckpt, None, None, *grads, None, ws, wsb, None)
+    assert call(desc(N=32)) == UNSUPPORTED
+    assert call(d, ckpt=None) == INVALID
+    for q in range(6):
+        g = list(grads); g[q] = None
+        assert call(d, grads=g) == INVALID
+
+
+def test_decode_rejects_bad_arguments():
+    L = W.lib()
+    call = lambda B=4, H=2, N=64, dt=1, s_in=P[7], s_out=P[8], y=P[6]: L.wkv7_decode_step(
+        B, H, N, dt, *P[:6], s_in, s_out, y, None)
+    assert call(N=32) == UNSUPPORTED
+    assert call(dt=3) == UNSUPPORTED
+    assert call(B=0) == INVALID
+    assert call(s_in=None) == INVALID
+    assert call(y=None) == INVALID
+    # overlapping but not identical state buffers
+    assert call(s_in=P[7], s_out=ctypes.c_void_p(P[7].value + 16)) == INVALID
+
+
+def test_checkpoint_slots():
+    assert W.checkpoint_slots(3, 33) == 9
+    assert W.checkpoint_slots(2, 16) == 2
+    assert W.checkpoint_slots(1, 1) == 1
+    n = ctypes.c_int64()
+    assert W.lib().wkv7_checkpoint_slots(0, 5, ctypes.byref(n)) == INVALID
+
+
+def test_workspace_query():
+    assert W.wkv7_workspace_bytes(4, 64, 8, 1) >= 0
+    n = ctypes.c_size_t()
+    assert W.lib().wkv7_workspace_bytes(ctypes.byref(desc(N=48)), ctypes.byref(n)) == UNSUPPORTED
+
+
+def test_segments_check_matches_layout_helpers():
+    lengths = synth.ragged_lengths(64, 16, 2048, seed=4)
+    T_pad, st, ln = synth.packed_layout(lengths, 4)
+    order, st_s, ln_s = synth.sorted_table(st, ln)
+    base, slots = W.wkv7_segments_check(4, T_pad, st_s, ln_s)
+    ref_base, ref_slots = synth.checkpoint_bases(ln_s)
+    assert slots == ref_slots and np.array_equal(base, ref_base)
+    assert slots == synth.checkpoint_bases(lengths)[1]
+    st2, ln2 = synth.padded_layout(lengths, 2048)
+    base2, slots2 = W.wkv7_segments_check(64, 2048, st2, ln2)
+    assert np.array_equal(base2, synth.checkpoint_bases(lengths)[0])
+    # the packed table in sequence order is not sorted by start: rejected
+    with pytest.raises(W.WKV7Error):
+        W.wkv7_segments_check(4, T_pad, st, ln)
+
+
+@pytest.mark.parametrize("start,length", [
+    ([0, 10], [12, 4]),        # overlap
+    ([10, 0], [4, 4]),         # unsorted
+    ([30], [5]),               # crosses a row boundary (T=32)
+    ([0], [-1]),               # negative length
+    ([60], [10]),              # past the end (B*T = 64)
+])
+def test_segments_check_rejects(start, length):
+    with pytest.raises(W.WKV7Error) as e:
+        W.wkv7_segments_check(2, 32, start, length)
+    assert e.value.code == INVALID
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(W, "_lib", None)
+    monkeypatch.setattr(W, "LIB_PATH", "/nonexistent/libwkv7.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        W.lib()
