@@ -111,7 +111,7 @@ def main():
         e1.record()
         W.wkv7_backward(*ts, ckpt, dy, None, grads=grads, want_ds0=True)
         e2.record()
-        if record:
+        if record is not None:
             record.append((e0, e1, e2))
 
     for _ in range(args.warmup):
