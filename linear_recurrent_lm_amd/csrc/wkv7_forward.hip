@@ -1,123 +1,430 @@
-// WKV-7 forward, token order (RWKV-7 WKV-7 recurrence; the model card's
-// "eager" token-order form). One wave per (sequence, head); lane i keeps state
-// row S[i, :] in 64 VGPRs. Every 16 tokens the wave stages r, w, k, a, b, v of
-// the chunk into LDS as fp32 (coalesced loads of each 64-element vector) and
-// then walks the tokens: the key-indexed vectors are read back as LDS
-// broadcasts, v_t[i] is per lane.
+// WKV-7 forward, chunk-parallel form with FP32 MFMA for the dense products.
 //
-// Per token, lane i computes
-//     sa   = sum_j S[i,j] a[j]                      (undecayed S_{t-1})
-//     S[i,j] = S[i,j] w[j] + sa b[j] + v[i] k[j]
-//     y[i] = sum_j S[i,j] r[j]                      (updated S_t)
-// and the state entering tokens 0, 16, 32, ... of the sequence is stored as a
-// checkpoint when requested.
+// The recurrence (RWKV-7 WKV-7; the model card's "chunked" path computes the
+// same thing in a different operation order):
+//     S_t = S_{t-1} diag(w_t) + (S_{t-1} a_t) b_t^T + v_t k_t^T,   y_t = S_t r_t
+// is advanced 16 tokens at a time. Within a chunk with entering state S_0,
+// decays gamma_t = prod_{u<=t} w_u and D_{t,s} = prod_{s<u<=t} w_u, and
+// x_t = S_{t-1} a_t, unrolling the recurrence gives
+//     (I - L_ab) X = A^ S_0^T + L_ak V                (unit lower triangular)
+//     Y            = R^ S_0^T + M_rb X + M_rk V
+//     S_16         = S_0 diag(gamma_16) + X^T B^ + V^T K^
+// with rows A^_t = gamma_{t-1} a_t, R^_t = gamma_t r_t, B^_s = D_{16,s} b_s,
+// K^_s = D_{16,s} k_s and the 16x16 matrices
+//     L_ab[t,s] = <a_t, b_s D_{t-1,s}>  (s < t)     M_rb[t,s] = <r_t, b_s D_{t,s}>  (s <= t)
+// (L_ak, M_rk the same with k_s). The two dense contractions [A^;R^] S_0^T
+// (32x64x64) and [X|V]^T [B^;K^] (64x64x32) run on v_mfma_f32_16x16x4_f32;
+// everything else is VALU.
+//
+// The 16x16 matrices are built as dot products of precomputed rows using
+// 4-token sub-chunks: for t in sub-chunk p and s in an earlier sub-chunk q the
+// decay factorises division-free as D_{t-1,s} = [prod_{4p<=u<t} w_u] *
+// [prod_{s<u<4p} w_u]; for s in the same sub-chunk the within-sub-chunk
+// prefix F_s = prod_{4p<=u<=s} w_u is divided out, with every factor of F
+// clamped to >= 2^-30 so F >= 2^-120 stays a normal fp32 number (w = 0
+// then acts as 2^-30 on at most three neighbouring tokens of one sub-chunk).
+// The chunk-level decays (gamma, D_{16,s}) are exact products.
+//
+// Layout and work split: one 256-thread workgroup (4 waves) per (sequence,
+// head, block of RB value rows); value rows are independent, so a unit may be
+// split in 1, 2 or 4 row blocks to fill the machine. The state block lives in
+// the MFMA accumulators as S^T tiles: lane l of a wave holds
+// S[i0 + 16*it + l%16][16*jt + 4*(l/16) + r], r = 0..3, which is directly the
+// B operand of the next chunk's [A^;R^] S_0^T product. Inputs are staged to
+// LDS as fp32 with one 16-byte load per 8 bf16 values.
 #include "wkv7_kernels.h"
 
 namespace wkv7 {
 namespace {
 
-constexpr int kStreams = 6;  // r, w, k, a, b, v in LDS
+constexpr int kThreads = 256;
+constexpr int QLD = 68;    // row stride (floats) of Q and the C x C operand rows
+constexpr int KLD = 36;    // row stride of the transposed [B^;K^] and [X|V] tiles
+constexpr float kMinFactor = 9.313225746154785e-10f;  // 2^-30
+
+// LDS layout (floats).
+template <int RB>
+struct Lay {
+    static constexpr int IN = 0;                       // [5][16][64]: r w k a b
+    static constexpr int P = 0;                        // alias [WPI][32][RB]
+    static constexpr int LM = 2048;                    // alias [4][16][16]
+    static constexpr int Q = 5 * 16 * 64;              // [32][QLD]: A^, R^
+    static constexpr int BKT = Q + 32 * QLD;           // [64][KLD]: B^ | K^ (by column j)
+    static constexpr int XVT = BKT + 64 * KLD;         // [RB][KLD]: X | V (by row i)
+    static constexpr int AR = XVT + RB * KLD;          // [32][QLD]: A' (a), A' (r)
+    static constexpr int BV = AR + 32 * QLD;           // [40][QLD]: b versions
+    static constexpr int KV = BV + 40 * QLD;           // [40][QLD]: k versions
+    static constexpr int GC = KV + 40 * QLD;           // [64]: gamma_16
+    static constexpr int TOTAL = GC + 64;
+};
+
+enum { IR = 0, IW, IK, IA, IB };
+
+__device__ __forceinline__ int ver_off(int p) { return 2 * p * (p + 1); }
 
 template <typename TI>
-__global__ __launch_bounds__(64) void fwd_token_kernel(FwdArgs p) {
-    const int H = p.seg.H;
-    const int unit = blockIdx.x;
-    const int h = unit % H;
-    const int s = unit / H;
-    const Unit u = resolve_unit(p.seg, s);
-    const int i = threadIdx.x;
+__device__ __forceinline__ void load8(const TI *p, float *x);
 
-    const TI *__restrict__ r = (const TI *)p.r;
-    const TI *__restrict__ w = (const TI *)p.w;
-    const TI *__restrict__ k = (const TI *)p.k;
-    const TI *__restrict__ v = (const TI *)p.v;
-    const TI *__restrict__ a = (const TI *)p.a;
-    const TI *__restrict__ b = (const TI *)p.b;
-    TI *__restrict__ y = (TI *)p.y;
-
-    __shared__ float tile[kChunk][kStreams][kN];
-
-    float S[kN];
-    const int64_t srow = ((int64_t)s * H + h) * kN * kN + (int64_t)i * kN;
-    if (p.s0) {
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t *p, float *x) {
+    const uint4 q = *(const uint4 *)p;
+    const uint32_t u[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-        for (int j = 0; j < kN; j += 4) {
-            const float4 q = *(const float4 *)(p.s0 + srow + j);
-            S[j] = q.x; S[j + 1] = q.y; S[j + 2] = q.z; S[j + 3] = q.w;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kN; ++j) S[j] = 0.f;
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(u[e] << 16);
+        x[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
     }
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float *p, float *x) {
+    const float4 a = *(const float4 *)p;
+    const float4 b = *(const float4 *)(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <typename TI, int NIT>
+__global__ __launch_bounds__(kThreads, 2) void fwd_chunk_kernel(FwdArgs p, int32_t units) {
+    constexpr int RB = 16 * NIT;       // value rows per workgroup
+    constexpr int NRB = 4 / NIT;       // row blocks per unit
+    constexpr int WPI = 4 / NIT;       // waves sharing one 16-row tile (K split of D1)
+    constexpr int JPW = NIT;           // 16-column tiles of the state per wave
+    using LY = Lay<RB>;
+    extern __shared__ __align__(16) float sm[];
+
+    // Workgroup -> (unit, row block). Row blocks of one unit go to the same
+    // XCD (workgroups are dealt to the 8 XCDs round robin) so that their
+    // shared reads of r, w, k, a, b hit one L2.
+    int unit, rb;
+    if (NRB == 1) {
+        unit = blockIdx.x;
+        rb = 0;
+    } else {
+        const int g = blockIdx.x / (8 * NRB), wq = blockIdx.x % (8 * NRB);
+        unit = g * 8 + (wq & 7);
+        rb = wq >> 3;
+    }
+    if (unit >= units) return;
+    const int H = p.seg.H;
+    const int h = unit % H;
+    const int sq = unit / H;
+    const Unit u = resolve_unit(p.seg, sq);
+    const int i0 = rb * RB;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, kq = lane >> 4;
+    const int it = wave % NIT, jg = wave / NIT;
+    const int irow = 16 * it + l16;                      // local value row of this lane
 
     const int64_t ts = (int64_t)H * kN;
     const int64_t base = (u.start * H + h) * kN;
+    const int64_t sbase = ((int64_t)sq * H + h) * (kN * kN);
+
+    // State tiles: acc[q][r] = S[i0 + irow][16*jt + 4*kq + r], jt = jg*JPW + q.
+    f32x4 acc[JPW];
+#pragma unroll
+    for (int q = 0; q < JPW; ++q) {
+        const int jt = jg * JPW + q;
+        if (p.s0) {
+            const float4 v4 = *(const float4 *)(p.s0 + sbase + (int64_t)(i0 + irow) * kN + 16 * jt + 4 * kq);
+            acc[q] = f32x4{v4.x, v4.y, v4.z, v4.w};
+        } else {
+            acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    float *s_in = sm + LY::IN;
+    float *s_P = sm + LY::P;
+    float *s_L = sm + LY::LM;
+    float *s_Q = sm + LY::Q;
+    float *s_BKt = sm + LY::BKT;
+    float *s_XVt = sm + LY::XVT;
+    float *s_AR = sm + LY::AR;
+    float *s_BV = sm + LY::BV;
+    float *s_KV = sm + LY::KV;
+    float *s_gC = sm + LY::GC;
+
+    const int nch = (u.len + kChunk - 1) / kChunk;
 #pragma unroll 1
-    for (int t0 = 0; t0 < u.len; t0 += kChunk) {
+    for (int c = 0; c < nch; ++c) {
+        const int t0 = c * kChunk;
         const int L = min(kChunk, u.len - t0);
+        __syncthreads();
+
+        // ---- stage the chunk (identity tokens w=1, rest 0, past the end)
+#pragma unroll
+        for (int q = tid; q < 6 * 16 * 8; q += kThreads) {
+            const int st = q >> 7, t = (q >> 3) & 15, e0 = (q & 7) * 8;
+            float x[8];
+            if (t < L) {
+                const void *sp = st == IR ? p.r : st == IW ? p.w : st == IK ? p.k
+                               : st == IA ? p.a : st == IB ? p.b : p.v;
+                load8<TI>((const TI *)sp + base + (int64_t)(t0 + t) * ts + e0, x);
+            } else {
+                const float f = st == IW ? 1.f : 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = f;
+            }
+            if (st < 5) {
+                float *d = s_in + (st * 16 + t) * 64 + e0;
+                *(float4 *)d = make_float4(x[0], x[1], x[2], x[3]);
+                *(float4 *)(d + 4) = make_float4(x[4], x[5], x[6], x[7]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int row = e0 + e - i0;
+                    if (row >= 0 && row < RB) s_XVt[row * KLD + 16 + t] = x[e];
+                }
+            }
+        }
         if (p.ckpt) {
-            float *cp = p.ckpt + ((u.ckpt + t0 / kChunk) * H + h) * (int64_t)(kN * kN) + i * kN;
+            float *cp = p.ckpt + ((u.ckpt + c) * H + h) * (int64_t)(kN * kN) + (int64_t)(i0 + irow) * kN;
 #pragma unroll
-            for (int j = 0; j < kN; j += 4)
-                *(float4 *)(cp + j) = make_float4(S[j], S[j + 1], S[j + 2], S[j + 3]);
+            for (int q = 0; q < JPW; ++q) {
+                const int jt = jg * JPW + q;
+                *(float4 *)(cp + 16 * jt + 4 * kq) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+            }
         }
         __syncthreads();
-        for (int t = 0; t < L; ++t) {
-            const int64_t o = base + (int64_t)(t0 + t) * ts + i;
-            tile[t][0][i] = IO<TI>::ld(r, o);
-            tile[t][1][i] = IO<TI>::ld(w, o);
-            tile[t][2][i] = IO<TI>::ld(k, o);
-            tile[t][3][i] = IO<TI>::ld(a, o);
-            tile[t][4][i] = IO<TI>::ld(b, o);
-            tile[t][5][i] = IO<TI>::ld(v, o);
+
+        // ---- decays and operand rows (4 threads per key column j)
+        {
+            const int role = tid >> 6, j = tid & 63;
+            const float *w_ = s_in + IW * 1024 + j;
+            if (role == 0) {            // A^, R^ and gamma_16
+                float g = 1.f;
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    s_Q[t * QLD + j] = s_in[IA * 1024 + t * 64 + j] * g;
+                    g *= w_[t * 64];
+                    s_Q[(16 + t) * QLD + j] = s_in[IR * 1024 + t * 64 + j] * g;
+                }
+                s_gC[j] = g;
+            } else if (role == 1) {     // B^, K^ (transposed for the MFMA A operand)
+                float d = 1.f;
+#pragma unroll
+                for (int s = 15; s >= 0; --s) {
+                    s_BKt[j * KLD + s] = s_in[IB * 1024 + s * 64 + j] * d;
+                    s_BKt[j * KLD + 16 + s] = s_in[IK * 1024 + s * 64 + j] * d;
+                    d *= w_[s * 64];
+                }
+            } else if (role == 2) {     // within-sub-chunk prefix rows A' = a F_{t-1}, R' = r F_t
+#pragma unroll
+                for (int sc = 0; sc < 4; ++sc) {
+                    float f = 1.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 4 * sc + e;
+                        s_AR[t * QLD + j] = s_in[IA * 1024 + t * 64 + j] * f;
+                        f *= fmaxf(w_[t * 64], kMinFactor);
+                        s_AR[(16 + t) * QLD + j] = s_in[IR * 1024 + t * 64 + j] * f;
+                    }
+                }
+            } else {                    // b, k versions per target sub-chunk
+                float wv[16], W[4];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) wv[t] = w_[t * 64];
+#pragma unroll
+                for (int sc = 0; sc < 4; ++sc)
+                    W[sc] = (wv[4 * sc] * wv[4 * sc + 1]) * (wv[4 * sc + 2] * wv[4 * sc + 3]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float suf[4];
+                    suf[3] = 1.f;
+                    suf[2] = wv[4 * q + 3];
+                    suf[1] = wv[4 * q + 2] * suf[2];
+                    suf[0] = wv[4 * q + 1] * suf[1];
+                    float F = 1.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = 4 * q + e;
+                        F *= fmaxf(wv[s], kMinFactor);
+                        const float bs = s_in[IB * 1024 + s * 64 + j];
+                        const float ks = s_in[IK * 1024 + s * 64 + j];
+                        const float inv = 1.f / F;
+                        s_BV[(ver_off(q) + s) * QLD + j] = bs * inv;
+                        s_KV[(ver_off(q) + s) * QLD + j] = ks * inv;
+                        float m = suf[e];
+#pragma unroll
+                        for (int pp = q + 1; pp < 4; ++pp) {
+                            s_BV[(ver_off(pp) + s) * QLD + j] = bs * m;
+                            s_KV[(ver_off(pp) + s) * QLD + j] = ks * m;
+                            m *= W[pp];
+                        }
+                    }
+                }
+            }
         }
         __syncthreads();
-#pragma unroll 1
-        for (int t = 0; t < L; ++t) {
-            const float *rt = tile[t][0], *wt = tile[t][1], *kt = tile[t][2];
-            const float *at = tile[t][3], *bt = tile[t][4];
-            float s0a = 0.f, s1a = 0.f, s2a = 0.f, s3a = 0.f;
+
+        // ---- D1 on MFMA: P[t'][i] = sum_j Q[t'][j] S_0[i][j] (this wave's column tiles)
 #pragma unroll
-            for (int j = 0; j < kN; j += 4) {
-                s0a = fmaf(S[j], at[j], s0a);
-                s1a = fmaf(S[j + 1], at[j + 1], s1a);
-                s2a = fmaf(S[j + 2], at[j + 2], s2a);
-                s3a = fmaf(S[j + 3], at[j + 3], s3a);
-            }
-            const float sa = (s0a + s1a) + (s2a + s3a);
-            const float vi = tile[t][5][i];
-            float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
+        for (int tt = 0; tt < 2; ++tt) {
+            f32x4 d1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < kN; j += 4) {
-                S[j] = fmaf(S[j], wt[j], fmaf(sa, bt[j], vi * kt[j]));
-                S[j + 1] = fmaf(S[j + 1], wt[j + 1], fmaf(sa, bt[j + 1], vi * kt[j + 1]));
-                S[j + 2] = fmaf(S[j + 2], wt[j + 2], fmaf(sa, bt[j + 2], vi * kt[j + 2]));
-                S[j + 3] = fmaf(S[j + 3], wt[j + 3], fmaf(sa, bt[j + 3], vi * kt[j + 3]));
-                y0 = fmaf(S[j], rt[j], y0);
-                y1 = fmaf(S[j + 1], rt[j + 1], y1);
-                y2 = fmaf(S[j + 2], rt[j + 2], y2);
-                y3 = fmaf(S[j + 3], rt[j + 3], y3);
+            for (int q = 0; q < JPW; ++q) {
+                const int jt = jg * JPW + q;
+                const float4 a4 = *(const float4 *)(s_Q + (16 * tt + l16) * QLD + 16 * jt + 4 * kq);
+                d1 = mfma4(a4.x, acc[q][0], d1);
+                d1 = mfma4(a4.y, acc[q][1], d1);
+                d1 = mfma4(a4.z, acc[q][2], d1);
+                d1 = mfma4(a4.w, acc[q][3], d1);
             }
-            IO<TI>::st(y, base + (int64_t)(t0 + t) * ts + i, (y0 + y1) + (y2 + y3));
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                s_P[(jg * 32 + 16 * tt + 4 * kq + r) * RB + irow] = d1[r];
+        }
+
+        // ---- 16x16 matrices on VALU: 120 L items and 136 M items, one per thread
+        {
+            int t, s, mat;
+            if (tid < 120) {
+                t = 1;
+                while ((t + 1) * t / 2 <= tid) ++t;
+                s = tid - t * (t - 1) / 2;
+                mat = 0;
+            } else {
+                const int mi = tid - 120;
+                t = 0;
+                while ((t + 1) * (t + 2) / 2 <= mi) ++t;
+                s = mi - t * (t + 1) / 2;
+                mat = 1;
+            }
+            const int vrow = ver_off(t >> 2) + s;
+            const float *ar = s_AR + (16 * mat + t) * QLD;
+            const float *bv = s_BV + vrow * QLD;
+            const float *kv = s_KV + vrow * QLD;
+            float db0 = 0.f, db1 = 0.f, dk0 = 0.f, dk1 = 0.f;
+#pragma unroll
+            for (int j = 0; j < 64; j += 8) {
+                const float4 x0 = *(const float4 *)(ar + j), x1 = *(const float4 *)(ar + j + 4);
+                const float4 b0 = *(const float4 *)(bv + j), b1 = *(const float4 *)(bv + j + 4);
+                const float4 k0 = *(const float4 *)(kv + j), k1 = *(const float4 *)(kv + j + 4);
+                db0 = fmaf(x0.x, b0.x, db0); db1 = fmaf(x0.y, b0.y, db1);
+                db0 = fmaf(x0.z, b0.z, db0); db1 = fmaf(x0.w, b0.w, db1);
+                db0 = fmaf(x1.x, b1.x, db0); db1 = fmaf(x1.y, b1.y, db1);
+                db0 = fmaf(x1.z, b1.z, db0); db1 = fmaf(x1.w, b1.w, db1);
+                dk0 = fmaf(x0.x, k0.x, dk0); dk1 = fmaf(x0.y, k0.y, dk1);
+                dk0 = fmaf(x0.z, k0.z, dk0); dk1 = fmaf(x0.w, k0.w, dk1);
+                dk0 = fmaf(x1.x, k1.x, dk0); dk1 = fmaf(x1.y, k1.y, dk1);
+                dk0 = fmaf(x1.z, k1.z, dk0); dk1 = fmaf(x1.w, k1.w, dk1);
+            }
+            // s_L: [0] L_ab, [1] L_ak, [2] M_rb, [3] M_rk
+            s_L[(2 * mat) * 256 + t * 16 + s] = db0 + db1;
+            s_L[(2 * mat + 1) * 256 + t * 16 + s] = dk0 + dk1;
+        }
+        __syncthreads();
+
+        // ---- X by forward substitution (one thread per value row); V terms of Y
+        const float *Lab = s_L, *Lak = s_L + 256, *Mrb = s_L + 512, *Mrk = s_L + 768;
+        if (tid < RB) {
+            const int il = tid;
+            float vv[16], xx[16];
+#pragma unroll
+            for (int s = 0; s < 16; ++s) vv[s] = s_XVt[il * KLD + 16 + s];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                float pa = 0.f;
+#pragma unroll
+                for (int g = 0; g < WPI; ++g) pa += s_P[(g * 32 + t) * RB + il];
+                float acc0 = pa, acc1 = 0.f;
+#pragma unroll
+                for (int s = 0; s < t; ++s) {
+                    acc0 = fmaf(Lak[t * 16 + s], vv[s], acc0);
+                    acc1 = fmaf(Lab[t * 16 + s], xx[s], acc1);
+                }
+                xx[t] = acc0 + acc1;
+                s_XVt[il * KLD + t] = xx[t];
+            }
+        } else {
+            for (int q = tid - RB; q < 16 * RB; q += kThreads - RB) {
+                const int t = q / RB, il = q - t * RB;
+                float acc0 = 0.f;
+#pragma unroll
+                for (int g = 0; g < WPI; ++g) acc0 += s_P[(g * 32 + 16 + t) * RB + il];
+                for (int s = 0; s <= t; ++s) acc0 = fmaf(Mrk[t * 16 + s], s_XVt[il * KLD + 16 + s], acc0);
+                s_P[(16 + t) * RB + il] = acc0;
+            }
+        }
+        __syncthreads();
+
+        // ---- Y = (R^ S_0^T + M_rk V) + M_rb X, stored for the real tokens
+        for (int q = tid; q < 16 * RB; q += kThreads) {
+            const int t = q / RB, il = q - t * RB;
+            float y = s_P[(16 + t) * RB + il];
+            for (int s = 0; s <= t; ++s) y = fmaf(Mrb[t * 16 + s], s_XVt[il * KLD + s], y);
+            if (t < L) IO<TI>::st((TI *)p.y, base + (int64_t)(t0 + t) * ts + i0 + il, y);
+        }
+
+        // ---- D2 on MFMA: S^T[j][i] = gamma[j] S_0^T[j][i] + sum_k BK[k][j] XV[k][i]
+        {
+            float xv[8];
+            const float *xr = s_XVt + irow * KLD + 8 * kq;
+            const float4 x0 = *(const float4 *)xr, x1 = *(const float4 *)(xr + 4);
+            xv[0] = x0.x; xv[1] = x0.y; xv[2] = x0.z; xv[3] = x0.w;
+            xv[4] = x1.x; xv[5] = x1.y; xv[6] = x1.z; xv[7] = x1.w;
+#pragma unroll
+            for (int q = 0; q < JPW; ++q) {
+                const int jt = jg * JPW + q;
+                const float4 g4 = *(const float4 *)(s_gC + 16 * jt + 4 * kq);
+                acc[q][0] *= g4.x; acc[q][1] *= g4.y; acc[q][2] *= g4.z; acc[q][3] *= g4.w;
+                const float *br = s_BKt + (16 * jt + l16) * KLD + 8 * kq;
+                const float4 b0 = *(const float4 *)br, b1 = *(const float4 *)(br + 4);
+                acc[q] = mfma4(b0.x, xv[0], acc[q]);
+                acc[q] = mfma4(b0.y, xv[1], acc[q]);
+                acc[q] = mfma4(b0.z, xv[2], acc[q]);
+                acc[q] = mfma4(b0.w, xv[3], acc[q]);
+                acc[q] = mfma4(b1.x, xv[4], acc[q]);
+                acc[q] = mfma4(b1.y, xv[5], acc[q]);
+                acc[q] = mfma4(b1.z, xv[6], acc[q]);
+                acc[q] = mfma4(b1.w, xv[7], acc[q]);
+            }
         }
     }
+
     if (p.s_out) {
+        float *op = p.s_out + sbase + (int64_t)(i0 + irow) * kN;
 #pragma unroll
-        for (int j = 0; j < kN; j += 4)
-            *(float4 *)(p.s_out + srow + j) = make_float4(S[j], S[j + 1], S[j + 2], S[j + 3]);
+        for (int q = 0; q < JPW; ++q) {
+            const int jt = jg * JPW + q;
+            *(float4 *)(op + 16 * jt + 4 * kq) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+        }
     }
+}
+
+template <typename TI, int NIT>
+hipError_t launch_chunk(const FwdArgs &a, int32_t units, hipStream_t stream) {
+    constexpr int NRB = 4 / NIT;
+    const size_t lds = (size_t)Lay<16 * NIT>::TOTAL * sizeof(float);
+    auto fn = fwd_chunk_kernel<TI, NIT>;
+    hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int64_t blocks = NRB == 1 ? units : ((int64_t)units + 7) / 8 * 8 * NRB;
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), lds, stream, a, units);
+    return hipGetLastError();
+}
+
+template <typename TI>
+hipError_t launch_typed(const FwdArgs &a, hipStream_t stream) {
+    const int S = a.seg.num_seqs > 0 ? a.seg.num_seqs : a.seg.B;
+    const int32_t units = S * a.seg.H;
+    // Split value rows across workgroups when there are too few units to
+    // give every CU two workgroups.
+    if (units >= 512) return launch_chunk<TI, 4>(a, units, stream);
+    if (units >= 256) return launch_chunk<TI, 2>(a, units, stream);
+    return launch_chunk<TI, 1>(a, units, stream);
 }
 
 }  // namespace
 
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream) {
-    const int S = a.seg.num_seqs > 0 ? a.seg.num_seqs : a.seg.B;
-    const dim3 grid((unsigned)((int64_t)S * a.seg.H));
-    if (a.dtype == 1)
-        hipLaunchKernelGGL(fwd_token_kernel<uint16_t>, grid, dim3(64), 0, stream, a);
-    else
-        hipLaunchKernelGGL(fwd_token_kernel<float>, grid, dim3(64), 0, stream, a);
-    return hipGetLastError();
+    return a.dtype == 1 ? launch_typed<uint16_t>(a, stream) : launch_typed<float>(a, stream);
 }
 
 }  // namespace wkv7
