@@ -62,26 +62,60 @@ enum { IR = 0, IW, IK, IA, IB };
 
 __device__ __forceinline__ int ver_off(int p) { return 2 * p * (p + 1); }
 
-template <typename TI>
-__device__ __forceinline__ void load8(const TI *p, float *x);
+// Raw chunk data in flight: 3 vectors of 8 elements per thread.
+template <typename TI> struct Raw;
+template <> struct Raw<uint16_t> { uint4 q[3]; };
+template <> struct Raw<float> { float4 q[3][2]; };
 
-template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t *p, float *x) {
-    const uint4 q = *(const uint4 *)p;
-    const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+__device__ __forceinline__ void raw_load(const uint16_t *p, Raw<uint16_t> &r, int k) {
+    r.q[k] = *(const uint4 *)p;
+}
+__device__ __forceinline__ void raw_load(const float *p, Raw<float> &r, int k) {
+    r.q[k][0] = *(const float4 *)p;
+    r.q[k][1] = *(const float4 *)(p + 4);
+}
+__device__ __forceinline__ void raw_unpack(const Raw<uint16_t> &r, int k, float *x) {
+    const uint32_t u[4] = {r.q[k].x, r.q[k].y, r.q[k].z, r.q[k].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         x[2 * e] = __uint_as_float(u[e] << 16);
         x[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
     }
 }
+__device__ __forceinline__ void raw_unpack(const Raw<float> &r, int k, float *x) {
+    x[0] = r.q[k][0].x; x[1] = r.q[k][0].y; x[2] = r.q[k][0].z; x[3] = r.q[k][0].w;
+    x[4] = r.q[k][1].x; x[5] = r.q[k][1].y; x[6] = r.q[k][1].z; x[7] = r.q[k][1].w;
+}
 
-template <>
-__device__ __forceinline__ void load8<float>(const float *p, float *x) {
-    const float4 a = *(const float4 *)p;
-    const float4 b = *(const float4 *)(p + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+// Rows b_s * V^(p)_s and k_s * V^(p)_s of source sub-chunk Q for every target
+// sub-chunk p >= Q: for p > Q the division-free decay prod_{s<u<4p} w_u, for
+// p = Q the reciprocal of the clamped within-sub-chunk prefix F_s.
+template <int Q>
+__device__ __forceinline__ void b_k_versions(const float *wv, const float *W, const float *s_in,
+                                             float *s_BV, float *s_KV, int j) {
+    float suf[4];
+    suf[3] = 1.f;
+    suf[2] = wv[4 * Q + 3];
+    suf[1] = wv[4 * Q + 2] * suf[2];
+    suf[0] = wv[4 * Q + 1] * suf[1];
+    float F = 1.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int s = 4 * Q + e;
+        F *= fmaxf(wv[s], 9.313225746154785e-10f);
+        const float bs = s_in[4 * 1024 + s * 64 + j];
+        const float ks = s_in[2 * 1024 + s * 64 + j];
+        const float inv = __builtin_amdgcn_rcpf(F);
+        s_BV[(2 * Q * (Q + 1) + s) * 68 + j] = bs * inv;
+        s_KV[(2 * Q * (Q + 1) + s) * 68 + j] = ks * inv;
+        float m = suf[e];
+#pragma unroll
+        for (int pp = Q + 1; pp < 4; ++pp) {
+            s_BV[(2 * pp * (pp + 1) + s) * 68 + j] = bs * m;
+            s_KV[(2 * pp * (pp + 1) + s) * 68 + j] = ks * m;
+            m *= W[pp];
+        }
+    }
 }
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
@@ -151,21 +185,39 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_chunk_kernel(FwdArgs p, int32
     float *s_gC = sm + LY::GC;
 
     const int nch = (u.len + kChunk - 1) / kChunk;
+    Raw<TI> raw;
+    // Thread tid stages element group q = tid + 256k: stream 2k + (tid >> 7)
+    // (uniform per wave), token (q >> 3) & 15, elements 8*(q & 7) .. +7.
+    const int half = __builtin_amdgcn_readfirstlane(tid >> 7);
+    const TI *sp0 = (const TI *)(half ? p.w : p.r);
+    const TI *sp1 = (const TI *)(half ? p.a : p.k);
+    const TI *sp2 = (const TI *)(half ? p.v : p.b);
+    auto issue = [&](int cc) {
+        const int Lc = min(kChunk, u.len - cc * kChunk);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int q = tid + k * kThreads;
+            const int t = (q >> 3) & 15, e0 = (q & 7) * 8;
+            const TI *sp = k == 0 ? sp0 : k == 1 ? sp1 : sp2;
+            if (t < Lc) raw_load(sp + base + (int64_t)(cc * kChunk + t) * ts + e0, raw, k);
+        }
+    };
+    if (nch > 0) issue(0);
 #pragma unroll 1
     for (int c = 0; c < nch; ++c) {
         const int t0 = c * kChunk;
         const int L = min(kChunk, u.len - t0);
         __syncthreads();
 
-        // ---- stage the chunk (identity tokens w=1, rest 0, past the end)
+        // ---- stage chunk c from registers (identity tokens w=1, rest 0, past the end),
+        //      then start the loads of chunk c+1
 #pragma unroll
-        for (int q = tid; q < 6 * 16 * 8; q += kThreads) {
+        for (int k = 0; k < 3; ++k) {
+            const int q = tid + k * kThreads;
             const int st = q >> 7, t = (q >> 3) & 15, e0 = (q & 7) * 8;
             float x[8];
             if (t < L) {
-                const void *sp = st == IR ? p.r : st == IW ? p.w : st == IK ? p.k
-                               : st == IA ? p.a : st == IB ? p.b : p.v;
-                load8<TI>((const TI *)sp + base + (int64_t)(t0 + t) * ts + e0, x);
+                raw_unpack(raw, k, x);
             } else {
                 const float f = st == IW ? 1.f : 0.f;
 #pragma unroll
@@ -183,6 +235,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_chunk_kernel(FwdArgs p, int32
                 }
             }
         }
+        if (c + 1 < nch) issue(c + 1);
         if (p.ckpt) {
             float *cp = p.ckpt + ((u.ckpt + c) * H + h) * (int64_t)(kN * kN) + (int64_t)(i0 + irow) * kN;
 #pragma unroll
@@ -214,71 +267,60 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_chunk_kernel(FwdArgs p, int32
                     s_BKt[j * KLD + 16 + s] = s_in[IK * 1024 + s * 64 + j] * d;
                     d *= w_[s * 64];
                 }
-            } else if (role == 2) {     // within-sub-chunk prefix rows A' = a F_{t-1}, R' = r F_t
-#pragma unroll
-                for (int sc = 0; sc < 4; ++sc) {
-                    float f = 1.f;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 4 * sc + e;
-                        s_AR[t * QLD + j] = s_in[IA * 1024 + t * 64 + j] * f;
-                        f *= fmaxf(w_[t * 64], kMinFactor);
-                        s_AR[(16 + t) * QLD + j] = s_in[IR * 1024 + t * 64 + j] * f;
-                    }
-                }
-            } else {                    // b, k versions per target sub-chunk
+            } else {
+                // roles 2 and 3: b, k versions per target sub-chunk (role 3: source
+                // sub-chunks 0 and 1; role 2: 2 and 3, plus the prefix rows
+                // A' = a F_{t-1}, R' = r F_t)
                 float wv[16], W[4];
 #pragma unroll
                 for (int t = 0; t < 16; ++t) wv[t] = w_[t * 64];
 #pragma unroll
                 for (int sc = 0; sc < 4; ++sc)
                     W[sc] = (wv[4 * sc] * wv[4 * sc + 1]) * (wv[4 * sc + 2] * wv[4 * sc + 3]);
+                if (role == 2) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float suf[4];
-                    suf[3] = 1.f;
-                    suf[2] = wv[4 * q + 3];
-                    suf[1] = wv[4 * q + 2] * suf[2];
-                    suf[0] = wv[4 * q + 1] * suf[1];
-                    float F = 1.f;
+                    for (int sc = 0; sc < 4; ++sc) {
+                        float f = 1.f;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s = 4 * q + e;
-                        F *= fmaxf(wv[s], kMinFactor);
-                        const float bs = s_in[IB * 1024 + s * 64 + j];
-                        const float ks = s_in[IK * 1024 + s * 64 + j];
-                        const float inv = 1.f / F;
-                        s_BV[(ver_off(q) + s) * QLD + j] = bs * inv;
-                        s_KV[(ver_off(q) + s) * QLD + j] = ks * inv;
-                        float m = suf[e];
-#pragma unroll
-                        for (int pp = q + 1; pp < 4; ++pp) {
-                            s_BV[(ver_off(pp) + s) * QLD + j] = bs * m;
-                            s_KV[(ver_off(pp) + s) * QLD + j] = ks * m;
-                            m *= W[pp];
+                        for (int e = 0; e < 4; ++e) {
+                            const int t = 4 * sc + e;
+                            s_AR[t * QLD + j] = s_in[IA * 1024 + t * 64 + j] * f;
+                            f *= fmaxf(wv[t], kMinFactor);
+                            s_AR[(16 + t) * QLD + j] = s_in[IR * 1024 + t * 64 + j] * f;
                         }
                     }
+                }
+                if (role == 3) {
+                    b_k_versions<0>(wv, W, s_in, s_BV, s_KV, j);
+                    b_k_versions<1>(wv, W, s_in, s_BV, s_KV, j);
+                } else {
+                    b_k_versions<2>(wv, W, s_in, s_BV, s_KV, j);
+                    b_k_versions<3>(wv, W, s_in, s_BV, s_KV, j);
                 }
             }
         }
         __syncthreads();
 
-        // ---- D1 on MFMA: P[t'][i] = sum_j Q[t'][j] S_0[i][j] (this wave's column tiles)
+        // ---- D1 on MFMA: P[t'][i] = sum_j Q[t'][j] S_0[i][j] over this wave's
+        //      column tiles (a K split when several waves share one row tile)
+        f32x4 d1[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            f32x4 d1 = {0.f, 0.f, 0.f, 0.f};
+            d1[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int q = 0; q < JPW; ++q) {
                 const int jt = jg * JPW + q;
                 const float4 a4 = *(const float4 *)(s_Q + (16 * tt + l16) * QLD + 16 * jt + 4 * kq);
-                d1 = mfma4(a4.x, acc[q][0], d1);
-                d1 = mfma4(a4.y, acc[q][1], d1);
-                d1 = mfma4(a4.z, acc[q][2], d1);
-                d1 = mfma4(a4.w, acc[q][3], d1);
+                d1[tt] = mfma4(a4.x, acc[q][0], d1[tt]);
+                d1[tt] = mfma4(a4.y, acc[q][1], d1[tt]);
+                d1[tt] = mfma4(a4.z, acc[q][2], d1[tt]);
+                d1[tt] = mfma4(a4.w, acc[q][3], d1[tt]);
             }
+            if (WPI > 1) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                s_P[(jg * 32 + 16 * tt + 4 * kq + r) * RB + irow] = d1[r];
+                for (int r = 0; r < 4; ++r)
+                    s_P[(jg * 32 + 16 * tt + 4 * kq + r) * RB + irow] = d1[tt][r];
+            }
         }
 
         // ---- 16x16 matrices on VALU: 120 L items and 136 M items, one per thread
@@ -315,75 +357,101 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_chunk_kernel(FwdArgs p, int32
                 dk0 = fmaf(x1.x, k1.x, dk0); dk1 = fmaf(x1.y, k1.y, dk1);
                 dk0 = fmaf(x1.z, k1.z, dk0); dk1 = fmaf(x1.w, k1.w, dk1);
             }
-            // s_L: [0] L_ab, [1] L_ak, [2] M_rb, [3] M_rk
+            // row-major 16x16: [0] L_ab, [1] L_ak, [2] M_rb, [3] M_rk (upper parts zero)
             s_L[(2 * mat) * 256 + t * 16 + s] = db0 + db1;
             s_L[(2 * mat + 1) * 256 + t * 16 + s] = dk0 + dk1;
         }
         __syncthreads();
+        float *s_Lab = s_L, *s_Lak = s_L + 256, *s_Mrb = s_L + 512, *s_Mrk = s_L + 768;
+        float *s_Wi = s_L + 1024;                 // (I - L_ab)^-1, row-major
+        float *s_Y = s_L + 1280;                  // [16][RB] output tile
 
-        // ---- X by forward substitution (one thread per value row); V terms of Y
-        const float *Lab = s_L, *Lak = s_L + 256, *Mrb = s_L + 512, *Mrk = s_L + 768;
-        if (tid < RB) {
-            const int il = tid;
-            float vv[16], xx[16];
+        // ---- (I - L_ab)^-1 by column-oriented substitution (16 threads); the
+        //      strictly upper parts of the four matrices are cleared meanwhile
+        if (tid < 16) {
+            float x[16];
 #pragma unroll
-            for (int s = 0; s < 16; ++s) vv[s] = s_XVt[il * KLD + 16 + s];
+            for (int t = 0; t < 16; ++t) x[t] = t == tid ? 1.f : 0.f;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float pa = 0.f;
+            for (int s2 = 0; s2 < 15; ++s2) {
 #pragma unroll
-                for (int g = 0; g < WPI; ++g) pa += s_P[(g * 32 + t) * RB + il];
-                float acc0 = pa, acc1 = 0.f;
-#pragma unroll
-                for (int s = 0; s < t; ++s) {
-                    acc0 = fmaf(Lak[t * 16 + s], vv[s], acc0);
-                    acc1 = fmaf(Lab[t * 16 + s], xx[s], acc1);
-                }
-                xx[t] = acc0 + acc1;
-                s_XVt[il * KLD + t] = xx[t];
+                for (int t = s2 + 1; t < 16; ++t) x[t] = fmaf(s_Lab[t * 16 + s2], x[s2], x[t]);
             }
-        } else {
-            for (int q = tid - RB; q < 16 * RB; q += kThreads - RB) {
-                const int t = q / RB, il = q - t * RB;
-                float acc0 = 0.f;
 #pragma unroll
-                for (int g = 0; g < WPI; ++g) acc0 += s_P[(g * 32 + 16 + t) * RB + il];
-                for (int s = 0; s <= t; ++s) acc0 = fmaf(Mrk[t * 16 + s], s_XVt[il * KLD + 16 + s], acc0);
-                s_P[(16 + t) * RB + il] = acc0;
+            for (int t = 0; t < 16; ++t) s_Wi[t * 16 + tid] = x[t];
+        } else if (tid >= 64 && tid < 64 + 4 * 16) {
+            const int m = (tid - 64) >> 4, row = tid & 15;
+            const int first = (m == 0 || m == 1) ? row : row + 1;   // L: s >= t, M: s > t
+            for (int c2 = first; c2 < 16; ++c2) s_L[m * 256 + row * 16 + c2] = 0.f;
+        }
+        if (WPI > 1) {
+            for (int q = tid; q < 32 * RB; q += kThreads) {
+                float acc0 = s_P[q];
+#pragma unroll
+                for (int g = 1; g < WPI; ++g) acc0 += s_P[g * 32 * RB + q];
+                s_P[q] = acc0;
             }
         }
         __syncthreads();
 
-        // ---- Y = (R^ S_0^T + M_rk V) + M_rb X, stored for the real tokens
-        for (int q = tid; q < 16 * RB; q += kThreads) {
+        // ---- per 16-row tile (one owner wave): rhs = P_a + L_ak V; X = W rhs;
+        //      Y = P_r + M_rk V + M_rb X, all on MFMA; the 16x16 output layout
+        //      is the B-operand layout of the next product
+        if (jg == 0) {
+            f32x4 pa = d1[0], pr = d1[1];
+            if (WPI > 1) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pa[r] = s_P[(4 * kq + r) * RB + irow];
+                    pr[r] = s_P[(16 + 4 * kq + r) * RB + irow];
+                }
+            }
+            const float4 v4 = *(const float4 *)(s_XVt + irow * KLD + 16 + 4 * kq);
+            const float vb[4] = {v4.x, v4.y, v4.z, v4.w};
+            const float4 lak = *(const float4 *)(s_Lak + l16 * 16 + 4 * kq);
+            const float4 mrk = *(const float4 *)(s_Mrk + l16 * 16 + 4 * kq);
+            const float4 wi = *(const float4 *)(s_Wi + l16 * 16 + 4 * kq);
+            const float4 mrb = *(const float4 *)(s_Mrb + l16 * 16 + 4 * kq);
+            pa = mfma4(lak.x, vb[0], pa); pa = mfma4(lak.y, vb[1], pa);
+            pa = mfma4(lak.z, vb[2], pa); pa = mfma4(lak.w, vb[3], pa);
+            pr = mfma4(mrk.x, vb[0], pr); pr = mfma4(mrk.y, vb[1], pr);
+            pr = mfma4(mrk.z, vb[2], pr); pr = mfma4(mrk.w, vb[3], pr);
+            f32x4 xx = {0.f, 0.f, 0.f, 0.f};
+            xx = mfma4(wi.x, pa[0], xx); xx = mfma4(wi.y, pa[1], xx);
+            xx = mfma4(wi.z, pa[2], xx); xx = mfma4(wi.w, pa[3], xx);
+            pr = mfma4(mrb.x, xx[0], pr); pr = mfma4(mrb.y, xx[1], pr);
+            pr = mfma4(mrb.z, xx[2], pr); pr = mfma4(mrb.w, xx[3], pr);
+            *(float4 *)(s_XVt + irow * KLD + 4 * kq) = make_float4(xx[0], xx[1], xx[2], xx[3]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_Y[(4 * kq + r) * RB + irow] = pr[r];
+        }
+        __syncthreads();
+
+        // ---- store y for the real tokens (consecutive threads, consecutive channels)
+        for (int q = tid; q < L * RB; q += kThreads) {
             const int t = q / RB, il = q - t * RB;
-            float y = s_P[(16 + t) * RB + il];
-            for (int s = 0; s <= t; ++s) y = fmaf(Mrb[t * 16 + s], s_XVt[il * KLD + s], y);
-            if (t < L) IO<TI>::st((TI *)p.y, base + (int64_t)(t0 + t) * ts + i0 + il, y);
+            IO<TI>::st((TI *)p.y, base + (int64_t)(t0 + t) * ts + i0 + il, s_Y[q]);
         }
 
         // ---- D2 on MFMA: S^T[j][i] = gamma[j] S_0^T[j][i] + sum_k BK[k][j] XV[k][i]
         {
-            float xv[8];
-            const float *xr = s_XVt + irow * KLD + 8 * kq;
-            const float4 x0 = *(const float4 *)xr, x1 = *(const float4 *)(xr + 4);
-            xv[0] = x0.x; xv[1] = x0.y; xv[2] = x0.z; xv[3] = x0.w;
-            xv[4] = x1.x; xv[5] = x1.y; xv[6] = x1.z; xv[7] = x1.w;
+            const float *xr = s_XVt + irow * KLD + 4 * kq;
+            const float4 xa = *(const float4 *)xr, va = *(const float4 *)(xr + 16);
 #pragma unroll
             for (int q = 0; q < JPW; ++q) {
                 const int jt = jg * JPW + q;
                 const float4 g4 = *(const float4 *)(s_gC + 16 * jt + 4 * kq);
                 acc[q][0] *= g4.x; acc[q][1] *= g4.y; acc[q][2] *= g4.z; acc[q][3] *= g4.w;
-                const float *br = s_BKt + (16 * jt + l16) * KLD + 8 * kq;
-                const float4 b0 = *(const float4 *)br, b1 = *(const float4 *)(br + 4);
-                acc[q] = mfma4(b0.x, xv[0], acc[q]);
-                acc[q] = mfma4(b0.y, xv[1], acc[q]);
-                acc[q] = mfma4(b0.z, xv[2], acc[q]);
-                acc[q] = mfma4(b0.w, xv[3], acc[q]);
-                acc[q] = mfma4(b1.x, xv[4], acc[q]);
-                acc[q] = mfma4(b1.y, xv[5], acc[q]);
-                acc[q] = mfma4(b1.z, xv[6], acc[q]);
-                acc[q] = mfma4(b1.w, xv[7], acc[q]);
+                const float *br = s_BKt + (16 * jt + l16) * KLD + 4 * kq;
+                const float4 b0 = *(const float4 *)br, k0 = *(const float4 *)(br + 16);
+                acc[q] = mfma4(b0.x, xa.x, acc[q]);
+                acc[q] = mfma4(b0.y, xa.y, acc[q]);
+                acc[q] = mfma4(b0.z, xa.z, acc[q]);
+                acc[q] = mfma4(b0.w, xa.w, acc[q]);
+                acc[q] = mfma4(k0.x, va.x, acc[q]);
+                acc[q] = mfma4(k0.y, va.y, acc[q]);
+                acc[q] = mfma4(k0.z, va.z, acc[q]);
+                acc[q] = mfma4(k0.w, va.w, acc[q]);
             }
         }
     }
