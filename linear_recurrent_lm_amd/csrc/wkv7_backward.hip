@@ -1,185 +1,604 @@
-// WKV-7 backward from 16-token state checkpoints, token order.
+// WKV-7 backward from 16-token state checkpoints, chunk form on FP32 MFMA.
 //
-// Reverse-mode of S_t = S_{t-1} diag(w_t) + (S_{t-1} a_t) b_t^T + v_t k_t^T,
-// y_t = S_t r_t for L = sum <dy, y> + <ds_out, S_T>. With G = dL/dS_t and
-// sa_t = S_{t-1} a_t, each token (last to first) does
-//     G      += dy_t r_t^T
-//     dr_t    = S_t^T dy_t          dv_t = G k_t        dsa = G b_t
-//     dk_t    = G^T v_t             db_t = G^T sa_t
-//     dw_t[j] = sum_i G[i,j] S_{t-1}[i,j]               da_t = S_{t-1}^T dsa
-//     G       = G diag(w_t) + dsa a_t^T
-// The states S_{t-1} of a chunk are recomputed forward from its checkpoint
-// (the state entering the chunk), never reconstructed by dividing by w, as
-// the rwkv-metal page's section "The Metal WKV-7 kernel" motivates.
+// Forward recurrence (RWKV-7 WKV-7): S_t = S_{t-1} diag(w_t) + (S_{t-1} a_t) b_t^T
+// + v_t k_t^T, y_t = S_t r_t. Gradients of L = sum <dy, y> + <ds_out, S_T>.
+// Chunks are processed from last to first; each one starts from its stored
+// checkpoint S_0 (the state entering the chunk) and from dS_C, the gradient
+// of the state leaving it, so nothing is reconstructed by dividing by w.
 //
-// One 1024-thread workgroup per (sequence, head). Thread tid owns row
-// i = tid/16 and columns 4*(tid%16) .. +3 of G and of the recomputed states,
-// which stay in registers for the whole chunk. Row sums (sa, dv, dsa) reduce
-// over the 16 lanes of a row; column sums (dr, dk, db, dw, da) reduce over the
-// 4 rows inside a wave by lane exchange and over the 16 waves through LDS.
+// Within a chunk the forward is (tokens t = 0..15, as in the forward kernel)
+//     X = W (A^ S_0^T + L_ak V),  W = (I - L_ab)^-1
+//     Y = R^ S_0^T + M_rb X + M_rk V
+//     S_C = S_0 diag(gamma_C) + X^T B^ + V^T K^
+// and its reverse mode is
+//     dX   = B^ dS_C^T + M_rb^T dY          drhs = W^T dX
+//     dV   = K^ dS_C^T + M_rk^T dY + L_ak^T drhs
+//     dS_0 = dS_C diag(gamma_C) + drhs^T A^ + dY^T R^
+//     dA^ = drhs S_0, dR^ = dY S_0, dB^ = X dS_C, dK^ = V dS_C
+//     dL_ab = drhs X^T, dL_ak = drhs V^T (strictly lower), dM_rb = dY X^T,
+//     dM_rk = dY V^T (lower)
+// followed by the chain rule through the decay products. The 16x16 matrices
+// use the forward's 4-token sub-chunk factorisation (rows A' = a F_ex,
+// R' = r F_in and b/k "versions" b_s V_s, k_s V_s), so their gradients with
+// respect to r, a, b, k are weighted sums of those rows. The decay gradient
+// is assembled as u_m = w_m dw_m from the log-derivatives of every product
+// that contains w_m (prefix gamma, suffix D_{15,s}, and the pair decays of
+// the 16x16 matrices, whose contribution is a sum over the (s, t) pairs that
+// straddle m), then dw = u / w. The whole backward uses w' = max(w, 2^-30),
+// so dw is finite at w = 0 and equals the gradient there to within the clamp.
+//
+// One 256-thread workgroup (4 waves) per (sequence, head). 16x64 chunk
+// matrices and the two 64x64 states live in LDS, row-major; MFMA operands are
+// 16-byte loads along the contraction index where the layout allows it. Wave
+// w owns value rows 16w..16w+15 for the value-side products and key columns
+// 16w..16w+15 for the key-side ones; dS is carried between chunks in the
+// accumulators of the dS^T product.
 #include "wkv7_kernels.h"
 
 namespace wkv7 {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
-enum { SR = 0, SW, SK, SA, SB, SV, SDY, NSTREAM };
+constexpr int kThreads = 256;
+constexpr int LD = 68;                            // row pitch of 16x64 / 64x64 arrays
+constexpr float kMinW = 9.313225746154785e-10f;   // 2^-30
 
-__device__ __forceinline__ float sum16(float x) {
-    x += __shfl_xor(x, 1, 16);
-    x += __shfl_xor(x, 2, 16);
-    x += __shfl_xor(x, 4, 16);
-    x += __shfl_xor(x, 8, 16);
-    return x;
+// LDS layout (floats)
+constexpr int O_IN = 0;                      // [7][16][64] r w k a b v dy
+constexpr int O_Q = O_IN + 7 * 1024;         // [32][LD] A^ (0..15), R^ (16..31)
+constexpr int O_BK = O_Q + 32 * LD;          // [32][LD] B^, K^
+constexpr int O_AR = O_BK + 32 * LD;         // [32][LD] A', R'
+constexpr int O_BV = O_AR + 32 * LD;         // [40][LD] b versions
+constexpr int O_KV = O_BV + 40 * LD;         // [40][LD] k versions
+constexpr int O_VV = O_KV + 40 * LD;         // [40][LD] bare decay versions
+constexpr int O_S0 = O_VV + 40 * LD;         // [64][LD] S_0
+constexpr int O_DS = O_S0 + 64 * LD;         // [64][LD] dS_C
+constexpr int O_X = O_DS + 64 * LD;          // [16][LD] X[t][i]
+constexpr int O_DR = O_X + 16 * LD;          // [16][LD] drhs[t][i]
+constexpr int O_G = O_DR + 16 * LD;          // [4][16][LD] dA^, dR^, dB^, dK^ ([t][j])
+constexpr int O_M = O_G + 64 * LD;           // [9][256] Lab Lak Mrb Mrk W dLab dLak dMrb dMrk
+constexpr int O_GC = O_M + 9 * 256;          // [64] gamma_C
+constexpr int O_DGC = O_GC + 64;             // [64] d gamma_C
+constexpr int LDS_FLOATS = O_DGC + 64;
+static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
+
+enum { IR = 0, IW, IK, IA, IB, IV, IDY };
+enum { MLAB = 0, MLAK, MMRB, MMRK, MW, MDLAB, MDLAK, MDMRB, MDMRK };
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float sum_rows_in_wave(float x) {
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
-    return x;
+__device__ __forceinline__ int ver_off(int p) { return 2 * p * (p + 1); }
+
+// acc[m][n] += sum_k A[m][k] B[k][n] with A row-major (pitch lda) and B given
+// transposed, Bt[n][k] row-major (pitch ldb): both operands 16-byte loads.
+__device__ __forceinline__ f32x4 mm_AtBt(f32x4 acc, const float *A, int lda, const float *Bt, int ldb,
+                                         int l16, int kq, int kdim) {
+    for (int k0 = 0; k0 < kdim; k0 += 16) {
+        const float4 a = *(const float4 *)(A + l16 * lda + k0 + 4 * kq);
+        const float4 b = *(const float4 *)(Bt + l16 * ldb + k0 + 4 * kq);
+        acc = mfma4(a.x, b.x, acc); acc = mfma4(a.y, b.y, acc);
+        acc = mfma4(a.z, b.z, acc); acc = mfma4(a.w, b.w, acc);
+    }
+    return acc;
+}
+
+// acc += A B with A row-major (16-byte loads along k) and B row-major [k][n]
+// (scalar loads; consecutive lanes read consecutive n).
+__device__ __forceinline__ f32x4 mm_AtB(f32x4 acc, const float *A, int lda, const float *B, int ldb,
+                                        int l16, int kq, int kdim) {
+    for (int k0 = 0; k0 < kdim; k0 += 16) {
+        const float4 a = *(const float4 *)(A + l16 * lda + k0 + 4 * kq);
+        const float *bp = B + (k0 + 4 * kq) * ldb + l16;
+        acc = mfma4(a.x, bp[0], acc); acc = mfma4(a.y, bp[ldb], acc);
+        acc = mfma4(a.z, bp[2 * ldb], acc); acc = mfma4(a.w, bp[3 * ldb], acc);
+    }
+    return acc;
+}
+
+// acc += A^T B for A = [k][m], B = [k][n] row-major with 16 rows k.
+__device__ __forceinline__ f32x4 mm_TB(f32x4 acc, const float *A, int lda, const float *B, int ldb,
+                                       int l16, int kq) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int k = 4 * kq + e;
+        acc = mfma4(A[k * lda + l16], B[k * ldb + l16], acc);
+    }
+    return acc;
+}
+
+template <typename TI> struct Raw;
+template <> struct Raw<uint16_t> { uint4 q[4]; };
+template <> struct Raw<float> { float4 q[4][2]; };
+
+__device__ __forceinline__ void raw_load(const uint16_t *p, Raw<uint16_t> &r, int k) {
+    r.q[k] = *(const uint4 *)p;
+}
+__device__ __forceinline__ void raw_load(const float *p, Raw<float> &r, int k) {
+    r.q[k][0] = *(const float4 *)p;
+    r.q[k][1] = *(const float4 *)(p + 4);
+}
+__device__ __forceinline__ void raw_unpack(const Raw<uint16_t> &r, int k, float *x) {
+    const uint32_t u[4] = {r.q[k].x, r.q[k].y, r.q[k].z, r.q[k].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(u[e] << 16);
+        x[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void raw_unpack(const Raw<float> &r, int k, float *x) {
+    x[0] = r.q[k][0].x; x[1] = r.q[k][0].y; x[2] = r.q[k][0].z; x[3] = r.q[k][0].w;
+    x[4] = r.q[k][1].x; x[5] = r.q[k][1].y; x[6] = r.q[k][1].z; x[7] = r.q[k][1].w;
+}
+
+// Version rows of source sub-chunk Q (b_s V, k_s V and the bare factor V) for
+// every target sub-chunk p >= Q; V = prod_{s<u<4p} w_u for p > Q, 1 / F_s for p = Q.
+template <int Q>
+__device__ __forceinline__ void versions(const float *wv, const float *W, const float *s_in,
+                                         float *s_bv, float *s_kv, float *s_vv, int j) {
+    float suf[4];
+    suf[3] = 1.f;
+    suf[2] = wv[4 * Q + 3];
+    suf[1] = wv[4 * Q + 2] * suf[2];
+    suf[0] = wv[4 * Q + 1] * suf[1];
+    float F = 1.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int s = 4 * Q + e;
+        F *= wv[s];
+        const float bs = s_in[IB * 1024 + s * 64 + j];
+        const float ks = s_in[IK * 1024 + s * 64 + j];
+        const float inv = __builtin_amdgcn_rcpf(F);
+        const int r0 = (ver_off(Q) + s) * LD + j;
+        s_vv[r0] = inv;
+        s_bv[r0] = bs * inv;
+        s_kv[r0] = ks * inv;
+        float m = suf[e];
+#pragma unroll
+        for (int pp = Q + 1; pp < 4; ++pp) {
+            const int r1 = (ver_off(pp) + s) * LD + j;
+            s_vv[r1] = m;
+            s_bv[r1] = bs * m;
+            s_kv[r1] = ks * m;
+            m *= W[pp];
+        }
+    }
 }
 
 template <typename TI>
-__global__ __launch_bounds__(kThreads) void bwd_token_kernel(BwdArgs p) {
-    const int H = p.seg.H;
+__global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32_t units) {
+    extern __shared__ __align__(16) float sm[];
     const int unit = blockIdx.x;
+    if (unit >= units) return;
+    const int H = p.seg.H;
     const int h = unit % H;
-    const int s = unit / H;
-    const Unit u = resolve_unit(p.seg, s);
+    const int sq = unit / H;
+    const Unit u = resolve_unit(p.seg, sq);
+
     const int tid = threadIdx.x;
-    const int i = tid >> 4;
-    const int j0 = (tid & 15) * 4;
-    const int wave = tid >> 6;
-    const bool row_leader = (tid & 15) == 0;
-    const bool wave_row0 = ((tid >> 4) & 3) == 0;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, kq = lane >> 4;
+    const int i0 = 16 * wave;      // value rows of this wave
+    const int j0 = 16 * wave;      // key columns of this wave
 
-    __shared__ float tin[kChunk][NSTREAM][kN];
-    __shared__ float red[2][kWaves][5][kN];
-
-    TI *__restrict__ dvp = (TI *)p.dv;
-
-    const int64_t sidx = ((int64_t)s * H + h) * (kN * kN) + (int64_t)i * kN + j0;
-    float G[4];
-    if (p.ds_out) {
-        const float4 q = *(const float4 *)(p.ds_out + sidx);
-        G[0] = q.x; G[1] = q.y; G[2] = q.z; G[3] = q.w;
-    } else {
-        G[0] = G[1] = G[2] = G[3] = 0.f;
-    }
+    float *s_in = sm + O_IN;
+    float *s_Q = sm + O_Q, *s_BK = sm + O_BK, *s_AR = sm + O_AR;
+    float *s_BV = sm + O_BV, *s_KV = sm + O_KV, *s_VV = sm + O_VV;
+    float *s_S0 = sm + O_S0, *s_DS = sm + O_DS, *s_X = sm + O_X, *s_DR = sm + O_DR;
+    float *s_G = sm + O_G, *s_M = sm + O_M, *s_gC = sm + O_GC, *s_dgC = sm + O_DGC;
+    const float *sV = s_in + IV * 1024, *sDY = s_in + IDY * 1024;
 
     const int64_t ts = (int64_t)H * kN;
     const int64_t base = (u.start * H + h) * kN;
-    const int nchunks = (u.len + kChunk - 1) / kChunk;
+    const int64_t sbase = ((int64_t)sq * H + h) * (kN * kN);
+
+    // dS carried between chunks: ds[q][r] = dS[i0 + l16][16q + 4kq + r]
+    f32x4 ds[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (p.ds_out) {
+            const float4 v4 = *(const float4 *)(p.ds_out + sbase + (int64_t)(i0 + l16) * kN + 16 * q + 4 * kq);
+            ds[q] = f32x4{v4.x, v4.y, v4.z, v4.w};
+        } else {
+            ds[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    // Staging: element groups g = tid + 256k (k = 0..3) of 7 streams x 16
+    // tokens x 8 groups of 8; stream g >> 7 is uniform per wave.
+    const int nch = (u.len + kChunk - 1) / kChunk;
+    Raw<TI> raw;
+    auto issue = [&](int cc) {
+        const int Lc = min(kChunk, u.len - cc * kChunk);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int g = tid + k * kThreads;
+            const int st = __builtin_amdgcn_readfirstlane(g >> 7);
+            const int t = (g >> 3) & 15, e0 = (g & 7) * 8;
+            const void *vp = st == IR ? p.r : st == IW ? p.w : st == IK ? p.k : st == IA ? p.a
+                           : st == IB ? p.b : st == IV ? p.v : st == IDY ? p.dy : nullptr;
+            if (vp && t < Lc) raw_load((const TI *)vp + base + (int64_t)(cc * kChunk + t) * ts + e0, raw, k);
+        }
+    };
+    if (nch > 0) issue(nch - 1);
 
 #pragma unroll 1
-    for (int c = nchunks - 1; c >= 0; --c) {
+    for (int c = nch - 1; c >= 0; --c) {
         const int t0 = c * kChunk;
         const int L = min(kChunk, u.len - t0);
         __syncthreads();
-        for (int idx = tid; idx < L * NSTREAM * kN; idx += kThreads) {
-            const int t = idx / (NSTREAM * kN);
-            const int rem = idx - t * (NSTREAM * kN);
-            const int st = rem / kN;
-            const int e = rem - st * kN;
-            const int64_t o = base + (int64_t)(t0 + t) * ts + e;
-            const void *src = st == SR ? p.r : st == SW ? p.w : st == SK ? p.k
-                            : st == SA ? p.a : st == SB ? p.b : st == SV ? p.v : p.dy;
-            tin[t][st][e] = src ? IO<TI>::ld((const TI *)src, o) : 0.f;
+
+        // ---- stage inputs (w clamped; identity tokens past the end), the
+        //      checkpoint S_0 and dS_C; then prefetch chunk c-1
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int g = tid + k * kThreads;
+            if (g < 7 * 128) {
+                const int st = g >> 7, t = (g >> 3) & 15, e0 = (g & 7) * 8;
+                float x[8];
+                if (t < L && (st != IDY || p.dy != nullptr)) {
+                    raw_unpack(raw, k, x);
+                } else {
+                    const float f = st == IW ? 1.f : 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = f;
+                }
+                if (st == IW) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = fmaxf(x[e], kMinW);
+                }
+                float *d = s_in + (st * 16 + t) * 64 + e0;
+                *(float4 *)d = make_float4(x[0], x[1], x[2], x[3]);
+                *(float4 *)(d + 4) = make_float4(x[4], x[5], x[6], x[7]);
+            }
         }
-        float hist[kChunk + 1][4];
         {
-            const float4 q = *(const float4 *)(p.ckpt + ((u.ckpt + c) * H + h) * (int64_t)(kN * kN) +
-                                               (int64_t)i * kN + j0);
-            hist[0][0] = q.x; hist[0][1] = q.y; hist[0][2] = q.z; hist[0][3] = q.w;
+            const float *cp = p.ckpt + ((u.ckpt + c) * H + h) * (int64_t)(kN * kN);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int f4 = tid + k * kThreads;
+                const int row = f4 >> 4, col = (f4 & 15) * 4;
+                *(float4 *)(s_S0 + row * LD + col) = *(const float4 *)(cp + row * 64 + col);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *(float4 *)(s_DS + (i0 + l16) * LD + 16 * q + 4 * kq) =
+                    make_float4(ds[q][0], ds[q][1], ds[q][2], ds[q][3]);
+        }
+        if (c > 0) issue(c - 1);
+        __syncthreads();
+
+        // ---- decay products and operand rows (4 roles x 64 key columns);
+        //      d gamma_C[j] = sum_i dS_C[i][j] S_0[i][j]
+        {
+            const int role = tid >> 6, j = tid & 63;
+            const float *w_ = s_in + IW * 1024 + j;
+            if (role == 0) {
+                float g = 1.f;
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    s_Q[t * LD + j] = s_in[IA * 1024 + t * 64 + j] * g;
+                    g *= w_[t * 64];
+                    s_Q[(16 + t) * LD + j] = s_in[IR * 1024 + t * 64 + j] * g;
+                }
+                s_gC[j] = g;
+            } else if (role == 1) {
+                float d = 1.f;
+#pragma unroll
+                for (int s = 15; s >= 0; --s) {
+                    s_BK[s * LD + j] = s_in[IB * 1024 + s * 64 + j] * d;
+                    s_BK[(16 + s) * LD + j] = s_in[IK * 1024 + s * 64 + j] * d;
+                    d *= w_[s * 64];
+                }
+                float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll 8
+                for (int i = 0; i < 64; i += 2) {
+                    acc0 = fmaf(s_DS[i * LD + j], s_S0[i * LD + j], acc0);
+                    acc1 = fmaf(s_DS[(i + 1) * LD + j], s_S0[(i + 1) * LD + j], acc1);
+                }
+                s_dgC[j] = acc0 + acc1;
+            } else {
+                float wv[16], W[4];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) wv[t] = w_[t * 64];
+#pragma unroll
+                for (int sc = 0; sc < 4; ++sc)
+                    W[sc] = (wv[4 * sc] * wv[4 * sc + 1]) * (wv[4 * sc + 2] * wv[4 * sc + 3]);
+                if (role == 2) {
+#pragma unroll
+                    for (int sc = 0; sc < 4; ++sc) {
+                        float f = 1.f;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int t = 4 * sc + e;
+                            s_AR[t * LD + j] = s_in[IA * 1024 + t * 64 + j] * f;
+                            f *= wv[t];
+                            s_AR[(16 + t) * LD + j] = s_in[IR * 1024 + t * 64 + j] * f;
+                        }
+                    }
+                    versions<2>(wv, W, s_in, s_BV, s_KV, s_VV, j);
+                    versions<3>(wv, W, s_in, s_BV, s_KV, s_VV, j);
+                } else {
+                    versions<0>(wv, W, s_in, s_BV, s_KV, s_VV, j);
+                    versions<1>(wv, W, s_in, s_BV, s_KV, s_VV, j);
+                }
+            }
         }
         __syncthreads();
 
-        float sa_r[kChunk];
+        // ---- P_a = A^ S_0^T for this wave's value rows (MFMA); the four 16x16
+        //      matrices (VALU, one pair of dot products per thread)
+        f32x4 pa = {0.f, 0.f, 0.f, 0.f};
+        pa = mm_AtBt(pa, s_Q, LD, s_S0 + i0 * LD, LD, l16, kq, 64);
+        {
+            int t, s, mat;
+            if (tid < 120) {
+                t = 1;
+                while ((t + 1) * t / 2 <= tid) ++t;
+                s = tid - t * (t - 1) / 2;
+                mat = 0;
+            } else {
+                const int mi = tid - 120;
+                t = 0;
+                while ((t + 1) * (t + 2) / 2 <= mi) ++t;
+                s = mi - t * (t + 1) / 2;
+                mat = 1;
+            }
+            const int vrow = ver_off(t >> 2) + s;
+            const float *ar = s_AR + (16 * mat + t) * LD;
+            const float *bv = s_BV + vrow * LD;
+            const float *kv = s_KV + vrow * LD;
+            float db0 = 0.f, db1 = 0.f, dk0 = 0.f, dk1 = 0.f;
 #pragma unroll
-        for (int t = 0; t < kChunk; ++t) {
-            if (t < L) {
-                float part = 0.f;
+            for (int j = 0; j < 64; j += 8) {
+                const float4 x0 = *(const float4 *)(ar + j), x1 = *(const float4 *)(ar + j + 4);
+                const float4 b0 = *(const float4 *)(bv + j), b1 = *(const float4 *)(bv + j + 4);
+                const float4 k0 = *(const float4 *)(kv + j), k1 = *(const float4 *)(kv + j + 4);
+                db0 = fmaf(x0.x, b0.x, db0); db1 = fmaf(x0.y, b0.y, db1);
+                db0 = fmaf(x0.z, b0.z, db0); db1 = fmaf(x0.w, b0.w, db1);
+                db0 = fmaf(x1.x, b1.x, db0); db1 = fmaf(x1.y, b1.y, db1);
+                db0 = fmaf(x1.z, b1.z, db0); db1 = fmaf(x1.w, b1.w, db1);
+                dk0 = fmaf(x0.x, k0.x, dk0); dk1 = fmaf(x0.y, k0.y, dk1);
+                dk0 = fmaf(x0.z, k0.z, dk0); dk1 = fmaf(x0.w, k0.w, dk1);
+                dk0 = fmaf(x1.x, k1.x, dk0); dk1 = fmaf(x1.y, k1.y, dk1);
+                dk0 = fmaf(x1.z, k1.z, dk0); dk1 = fmaf(x1.w, k1.w, dk1);
+            }
+            s_M[(2 * mat) * 256 + t * 16 + s] = db0 + db1;
+            s_M[(2 * mat + 1) * 256 + t * 16 + s] = dk0 + dk1;
+        }
+        __syncthreads();
+
+        // ---- W = (I - L_ab)^-1 (16 threads); clear the upper parts
+        if (tid < 16) {
+            float x[16];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) part = fmaf(hist[t][e], tin[t][SA][j0 + e], part);
-                const float sa = sum16(part);
-                sa_r[t] = sa;
-                const float vi = tin[t][SV][i];
+            for (int t = 0; t < 16; ++t) x[t] = t == tid ? 1.f : 0.f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    hist[t + 1][e] = fmaf(hist[t][e], tin[t][SW][j0 + e],
-                                          fmaf(sa, tin[t][SB][j0 + e], vi * tin[t][SK][j0 + e]));
+            for (int s2 = 0; s2 < 15; ++s2) {
+#pragma unroll
+                for (int t = s2 + 1; t < 16; ++t) x[t] = fmaf(s_M[MLAB * 256 + t * 16 + s2], x[s2], x[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) s_M[MW * 256 + t * 16 + tid] = x[t];
+        } else if (tid >= 64 && tid < 128) {
+            const int m = (tid - 64) >> 4, row = tid & 15;
+            const int first = m < 2 ? row : row + 1;
+            for (int c2 = first; c2 < 16; ++c2) s_M[m * 256 + row * 16 + c2] = 0.f;
+        }
+        __syncthreads();
+
+        const float *Mlak = s_M + MLAK * 256, *Mmrb = s_M + MMRB * 256, *Mmrk = s_M + MMRK * 256;
+        const float *Mw = s_M + MW * 256;
+
+        // ---- value side (rows i0..i0+15): X = W (P_a + L_ak V);
+        //      dX = B^ dS_C^T + M_rb^T dY; drhs = W^T dX; dV = K^ dS_C^T + M_rk^T dY + L_ak^T drhs
+        {
+            const f32x4 rhs = mm_AtB(pa, Mlak, 16, sV + i0, 64, l16, kq, 16);
+            f32x4 xx = {0.f, 0.f, 0.f, 0.f};
+            {
+                const float4 wr = *(const float4 *)(Mw + l16 * 16 + 4 * kq);
+                xx = mfma4(wr.x, rhs[0], xx); xx = mfma4(wr.y, rhs[1], xx);
+                xx = mfma4(wr.z, rhs[2], xx); xx = mfma4(wr.w, rhs[3], xx);
+            }
+            f32x4 dx = {0.f, 0.f, 0.f, 0.f};
+            dx = mm_AtBt(dx, s_BK, LD, s_DS + i0 * LD, LD, l16, kq, 64);
+            dx = mm_TB(dx, Mmrb, 16, sDY + i0, 64, l16, kq);
+            f32x4 dr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dr = mfma4(Mw[(4 * kq + e) * 16 + l16], dx[e], dr);
+            f32x4 dv = {0.f, 0.f, 0.f, 0.f};
+            dv = mm_AtBt(dv, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq, 64);
+            dv = mm_TB(dv, Mmrk, 16, sDY + i0, 64, l16, kq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dv = mfma4(Mlak[(4 * kq + e) * 16 + l16], dr[e], dv);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * kq + r;
+                s_X[t * LD + i0 + l16] = xx[r];
+                s_DR[t * LD + i0 + l16] = dr[r];
+                if (t < L) IO<TI>::st((TI *)p.dv, base + (int64_t)(t0 + t) * ts + i0 + l16, dv[r]);
             }
         }
+        __syncthreads();
 
+        // ---- key side (columns j0..j0+15), contractions over i:
+        //      dA^ = drhs S_0, dR^ = dY S_0, dB^ = X dS_C, dK^ = V dS_C;
+        //      one 16x16 matrix gradient per wave; dS_0^T tiles (over t)
+        {
+            f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = g0, g2 = g0, g3 = g0;
+            g0 = mm_AtB(g0, s_DR, LD, s_S0 + j0, LD, l16, kq, 64);
+            g1 = mm_AtB(g1, sDY, 64, s_S0 + j0, LD, l16, kq, 64);
+            g2 = mm_AtB(g2, s_X, LD, s_DS + j0, LD, l16, kq, 64);
+            g3 = mm_AtB(g3, sV, 64, s_DS + j0, LD, l16, kq, 64);
 #pragma unroll
-        for (int t = kChunk - 1; t >= 0; --t) {
-            if (t < L) {
-                const float dyi = tin[t][SDY][i];
-                const float vi = tin[t][SV][i];
-                const float sa = sa_r[t];
-                float rr[4], ww[4], kk[4], aa[4], bb[4];
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * kq + r;
+                s_G[(0 * 16 + t) * LD + j0 + l16] = g0[r];
+                s_G[(1 * 16 + t) * LD + j0 + l16] = g1[r];
+                s_G[(2 * 16 + t) * LD + j0 + l16] = g2[r];
+                s_G[(3 * 16 + t) * LD + j0 + l16] = g3[r];
+            }
+            // wave 0: dL_ab = drhs X^T, 1: dL_ak = drhs V^T, 2: dM_rb = dY X^T, 3: dM_rk = dY V^T
+            const float *lhs = wave < 2 ? s_DR : sDY;
+            const int lld = wave < 2 ? LD : 64;
+            const float *rt = (wave & 1) ? sV : s_X;
+            const int rld = (wave & 1) ? 64 : LD;
+            f32x4 gm = {0.f, 0.f, 0.f, 0.f};
+            gm = mm_AtBt(gm, lhs, lld, rt, rld, l16, kq, 64);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    rr[e] = tin[t][SR][j0 + e]; ww[e] = tin[t][SW][j0 + e];
-                    kk[e] = tin[t][SK][j0 + e]; aa[e] = tin[t][SA][j0 + e];
-                    bb[e] = tin[t][SB][j0 + e];
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * kq + r;
+                const bool keep = wave < 2 ? (l16 < t) : (l16 <= t);
+                s_M[(MDLAB + wave) * 256 + t * 16 + l16] = keep ? gm[r] : 0.f;
+            }
+            // dS_0^T[j][i] = gamma_C[j] dS_C^T[j][i] + sum_t A^[t][j] drhs[t][i] + R^[t][j] dY[t][i]
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int jq = 16 * q;
+                const float4 g4 = *(const float4 *)(s_gC + jq + 4 * kq);
+                f32x4 acc = ds[q];
+                acc[0] *= g4.x; acc[1] *= g4.y; acc[2] *= g4.z; acc[3] *= g4.w;
+                acc = mm_TB(acc, s_Q + jq, LD, s_DR + i0, LD, l16, kq);
+                acc = mm_TB(acc, s_Q + 16 * LD + jq, LD, sDY + i0, 64, l16, kq);
+                ds[q] = acc;
+            }
+        }
+        __syncthreads();
+
+        // ---- key-side gradient assembly: thread (j, tq) owns tokens
+        //      {tq, 7-tq, 8+tq, 15-tq} of key column j (balanced pair counts)
+        {
+            const int j = tid >> 2, tq = tid & 3;
+            const int tk[4] = {tq, 7 - tq, 8 + tq, 15 - tq};
+            const float *Mdlab = s_M + MDLAB * 256, *Mdlak = s_M + MDLAK * 256;
+            const float *Mdmrb = s_M + MDMRB * 256, *Mdmrk = s_M + MDMRK * 256;
+            const float *wcol = s_in + IW * 1024 + j;
+
+            // Rows t of this thread: zl_s = dL_ab[t,s] b_s V + dL_ak[t,s] k_s V and
+            // zm_s (same with dM); da_t, dr_t pair parts are F_ex,t sum_s zl_s and
+            // F_in,t sum_s zm_s; u_m gets A'_t zl_s for s < m < t and R'_t zm_s
+            // for s < m <= t, accumulated through the prefix sums over s.
+            float um[16];
+#pragma unroll
+            for (int m = 0; m < 16; ++m) um[m] = 0.f;
+            float zl_tot[4], zm_tot[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int t = tk[q];
+                const int pv = ver_off(t >> 2);
+                const float ap = s_AR[t * LD + j], rp = s_AR[(16 + t) * LD + j];
+                float cl = 0.f, cm = 0.f;
+                for (int s = 0; s <= t; ++s) {
+                    const float bvs = s_BV[(pv + s) * LD + j], kvs = s_KV[(pv + s) * LD + j];
+                    const float zm = Mdmrb[t * 16 + s] * bvs + Mdmrk[t * 16 + s] * kvs;
+                    const float zl = Mdlab[t * 16 + s] * bvs + Mdlak[t * 16 + s] * kvs;  // 0 for s = t
+                    cl += zl;
+                    cm += zm;
+                    const int m = s + 1;
+                    if (m < t) um[m] += ap * cl;
+                    if (m <= t) um[m] += rp * cm;
                 }
-                float part[5][4];
-                float dvq = 0.f, dsq = 0.f;
+                zl_tot[q] = cl;
+                zm_tot[q] = cm;
+            }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    G[e] = fmaf(dyi, rr[e], G[e]);
-                    part[0][e] = hist[t + 1][e] * dyi;
-                    dvq = fmaf(G[e], kk[e], dvq);
-                    dsq = fmaf(G[e], bb[e], dsq);
+            for (int m = 0; m < 16; ++m) {
+                um[m] += __shfl_xor(um[m], 1, 64);
+                um[m] += __shfl_xor(um[m], 2, 64);
+            }
+            // db_s, dk_s pair parts: sum_{t>=s} (dL_ab[t,s] A'_t + dM_rb[t,s] R'_t) V^(p(t))_s
+            float db_p[4], dk_p[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int s = tk[q];
+                float accb = 0.f, acck = 0.f;
+                for (int t = s; t < 16; ++t) {
+                    const float vv = s_VV[(ver_off(t >> 2) + s) * LD + j];
+                    const float ap = s_AR[t * LD + j], rp = s_AR[(16 + t) * LD + j];
+                    const float cb = Mdlab[t * 16 + s] * ap + Mdmrb[t * 16 + s] * rp;
+                    const float ck = Mdlak[t * 16 + s] * ap + Mdmrk[t * 16 + s] * rp;
+                    accb = fmaf(cb, vv, accb);
+                    acck = fmaf(ck, vv, acck);
                 }
-                const float dv = sum16(dvq);
-                const float dsa = sum16(dsq);
+                db_p[q] = accb;
+                dk_p[q] = acck;
+            }
+            // chunk-level decays of column j: gamma_t, gamma_{t-1}, D_{15,s},
+            // within-sub-chunk prefixes F_ex, F_in
+            float gam[16], gprev[16], dend[16], fex[16], fin[16];
+            {
+                float g = 1.f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    part[1][e] = G[e] * vi;
-                    part[2][e] = G[e] * sa;
-                    part[3][e] = G[e] * hist[t][e];
-                    part[4][e] = dsa * hist[t][e];
-                    G[e] = fmaf(G[e], ww[e], dsa * aa[e]);
+                for (int t = 0; t < 16; ++t) { gprev[t] = g; g *= wcol[t * 64]; gam[t] = g; }
+                float d = 1.f;
+#pragma unroll
+                for (int s = 15; s >= 0; --s) { dend[s] = d; d *= wcol[s * 64]; }
+#pragma unroll
+                for (int sc = 0; sc < 4; ++sc) {
+                    float f = 1.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 4 * sc + e;
+                        fex[t] = f; f *= wcol[t * 64]; fin[t] = f;
+                    }
                 }
+            }
+            // u_m chunk-level part:
+            //   sum_{t>=m} dR^_t r_t gamma_t + sum_{t>m} dA^_t a_t gamma_{t-1}
+            //   + sum_{s<m} (dB^_s b_s + dK^_s k_s) D_{15,s} + dgamma_C gamma_C
+            const float *gA = s_G, *gR = s_G + 16 * LD, *gB = s_G + 32 * LD, *gK = s_G + 48 * LD;
+            float suf[17], pre[17];
+            suf[16] = 0.f;
 #pragma unroll
-                for (int g = 0; g < 5; ++g)
+            for (int t = 15; t >= 0; --t) {
+                float x = gR[t * LD + j] * s_in[IR * 1024 + t * 64 + j] * gam[t];
+                if (t < 15) x += gA[(t + 1) * LD + j] * s_in[IA * 1024 + (t + 1) * 64 + j] * gprev[t + 1];
+                suf[t] = suf[t + 1] + x;
+            }
+            pre[0] = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) part[g][e] = sum_rows_in_wave(part[g][e]);
-                if (wave_row0) {
+            for (int s = 0; s < 16; ++s)
+                pre[s + 1] = pre[s] + (gB[s * LD + j] * s_in[IB * 1024 + s * 64 + j] +
+                                       gK[s * LD + j] * s_in[IK * 1024 + s * 64 + j]) * dend[s];
+            const float dgc = s_dgC[j] * gam[15];
 #pragma unroll
-                    for (int g = 0; g < 5; ++g)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) red[t & 1][wave][g][j0 + e] = part[g][e];
-                }
-                const int64_t ot = base + (int64_t)(t0 + t) * ts;
-                if (row_leader) IO<TI>::st(dvp, ot + i, dv);
-                __syncthreads();
-                if (tid < 5 * kN) {
-                    const int g = tid >> 6, col = tid & 63;
-                    float acc = 0.f;
-#pragma unroll
-                    for (int q = 0; q < kWaves; ++q) acc += red[t & 1][q][g][col];
-                    void *dst = g == 0 ? p.dr : g == 1 ? p.dk : g == 2 ? p.db : g == 3 ? p.dw : p.da;
-                    IO<TI>::st((TI *)dst, ot + col, acc);
+            for (int q = 0; q < 4; ++q) {
+                const int t = tk[q];
+                const float uval = um[t] + suf[t] + pre[t] + dgc;
+                const float dwv = uval / wcol[t * 64];
+                const float dav = gA[t * LD + j] * gprev[t] + fex[t] * zl_tot[q];
+                const float drv = gR[t * LD + j] * gam[t] + fin[t] * zm_tot[q];
+                const float dbv = gB[t * LD + j] * dend[t] + db_p[q];
+                const float dkv = gK[t * LD + j] * dend[t] + dk_p[q];
+                if (t < L) {
+                    const int64_t o = base + (int64_t)(t0 + t) * ts + j;
+                    IO<TI>::st((TI *)p.dr, o, drv);
+                    IO<TI>::st((TI *)p.dw, o, dwv);
+                    IO<TI>::st((TI *)p.da, o, dav);
+                    IO<TI>::st((TI *)p.db, o, dbv);
+                    IO<TI>::st((TI *)p.dk, o, dkv);
                 }
             }
         }
     }
-    if (p.ds0) *(float4 *)(p.ds0 + sidx) = make_float4(G[0], G[1], G[2], G[3]);
+    if (p.ds0) {
+        float *op = p.ds0 + sbase + (int64_t)(i0 + l16) * kN;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *(float4 *)(op + 16 * q + 4 * kq) = make_float4(ds[q][0], ds[q][1], ds[q][2], ds[q][3]);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
     const int S = a.seg.num_seqs > 0 ? a.seg.num_seqs : a.seg.B;
-    const dim3 grid((unsigned)((int64_t)S * a.seg.H));
-    if (a.dtype == 1)
-        hipLaunchKernelGGL(bwd_token_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(bwd_token_kernel<float>, grid, dim3(kThreads), 0, stream, a);
+    const int32_t units = S * a.seg.H;
+    const size_t lds = (size_t)LDS_FLOATS * sizeof(float);
+    auto fn = a.dtype == 1 ? bwd_chunk_kernel<uint16_t> : bwd_chunk_kernel<float>;
+    hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, dim3((unsigned)units), dim3(kThreads), lds, stream, a, units);
     return hipGetLastError();
 }
 

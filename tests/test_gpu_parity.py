@@ -150,6 +150,27 @@ def test_backward_shapes(W, T, dtype):
     assert U.unit_err_state(g["ds0"], ref["ds0"]) <= gtol(dtype)
 
 
+def test_backward_zero_and_tiny_decay(W):
+    """w = 0 (a state reset) and w = 1e-12 inside chunks: gradients stay finite
+    and match the oracle (the kernels clamp decay factors at 2^-30)."""
+    B, T, H = 1, 50, 2
+    inp = synth.make_inputs(B, T, H, 64, seed=31, dtype="f32", s0_std=0.2, with_dy=True,
+                            ds_out_std=0.1)
+    inp.w[0, 5] = 0.0
+    inp.w[0, 21, 0, :9] = 0.0
+    inp.w[0, 33:38] = 1e-12
+    _, _, y, s_out, _ = run_forward(W, inp)
+    ref = O.forward(*inp.streams(), s0=inp.s0)
+    assert U.unit_err_dense(U.host(y), ref["y"]) <= U.TOL_F32
+    assert U.unit_err_state(U.host(s_out), ref["s_out"]) <= U.TOL_F32
+    g, _ = run_backward(W, inp)
+    gr = O.backward(*inp.streams(), s0=inp.s0, dy=inp.dy, ds_out=inp.ds_out)
+    for n in ("dr", "dw", "dk", "dv", "da", "db"):
+        assert np.all(np.isfinite(g[n])), n
+        assert U.unit_err_dense(g[n], gr[n]) <= 1e-4, n
+    assert U.unit_err_state(g["ds0"], gr["ds0"]) <= 1e-4
+
+
 def test_backward_no_upstream(W):
     """dy = NULL and ds_out = NULL give zero gradients everywhere."""
     inp = synth.make_inputs(1, 20, 2, 64, seed=5, dtype="f32", s0_std=0.1)
