@@ -42,7 +42,34 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 256 MiB device-to-device copy (counter calibration)")
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest(path):
+    import hashlib
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter runs, or None
+    when there is none or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "linear_recurrent_lm_amd", "csrc", rec["source"])
+    if not os.path.exists(src) or source_digest(src) != rec["source_sha256_16"]:
+        return None
+    return rec["bytes_per_launch"]
 
 
 def cpu_baseline(inp, budget_s):
@@ -82,6 +109,14 @@ def main():
     from linear_recurrent_lm_amd import wkv7 as W
 
     dev = "cuda:0"
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4}), flush=True)
+        return
     torch.cuda.set_device(0)
     W.lib()
     B, T, H = 4, 4096, 32
@@ -161,7 +196,7 @@ def main():
         achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom_name)
     roof["kernel"] = dom_name
 
     def fracs(k):

@@ -43,8 +43,8 @@ constexpr int LD = 68;                            // row pitch of 16x64 / 64x64 
 constexpr float kMinW = 9.313225746154785e-10f;   // 2^-30
 
 // LDS layout (floats)
-constexpr int O_IN = 0;                      // [7][16][64] r w k a b v dy
-constexpr int O_Q = O_IN + 7 * 1024;         // [32][LD] A^ (0..15), R^ (16..31)
+constexpr int O_IN = 0;                      // [7][16][LD] r w k a b v dy
+constexpr int O_Q = O_IN + 7 * 16 * LD;         // [32][LD] A^ (0..15), R^ (16..31)
 constexpr int O_BK = O_Q + 32 * LD;          // [32][LD] B^, K^
 constexpr int O_AR = O_BK + 32 * LD;         // [32][LD] A', R'
 constexpr int O_BV = O_AR + 32 * LD;         // [40][LD] b versions
@@ -146,8 +146,8 @@ __device__ __forceinline__ void versions(const float *wv, const float *W, const 
     for (int e = 0; e < 4; ++e) {
         const int s = 4 * Q + e;
         F *= wv[s];
-        const float bs = s_in[IB * 1024 + s * 64 + j];
-        const float ks = s_in[IK * 1024 + s * 64 + j];
+        const float bs = s_in[(IB * 16 + s) * LD + j];
+        const float ks = s_in[(IK * 16 + s) * LD + j];
         const float inv = __builtin_amdgcn_rcpf(F);
         const int r0 = (ver_off(Q) + s) * LD + j;
         s_vv[r0] = inv;
@@ -162,6 +162,126 @@ __device__ __forceinline__ void versions(const float *wv, const float *W, const 
             s_kv[r1] = ks * m;
             m *= W[pp];
         }
+    }
+}
+
+struct AsmArgs {
+    const float *s_in, *s_AR, *s_BV, *s_KV, *s_VV, *s_G, *s_M, *s_dgC;
+    float *s_U;          // [4][16][LD] partial pair parts of u (aliases S_0)
+    int j, wave;
+};
+
+// Pair parts for rows t in {T0..T3} of key column j: the prefix sums over s of
+// zl_s = dL_ab[t,s] b_s V + dL_ak[t,s] k_s V and zm_s (same with dM) give the
+// da_t, dr_t pair parts and the straddling-pair part of u (A'_t zl_s for
+// s < m < t, R'_t zm_s for s < m <= t); db_s, dk_s pair parts for s in {T0..T3}.
+template <int T0, int T1, int T2, int T3>
+__device__ __forceinline__ void assemble_rows(const AsmArgs &g, float (&st5)[4][5]) {
+    constexpr int TK[4] = {T0, T1, T2, T3};
+    const int j = g.j;
+    const float *Mdlab = g.s_M + MDLAB * 256, *Mdlak = g.s_M + MDLAK * 256;
+    const float *Mdmrb = g.s_M + MDMRB * 256, *Mdmrk = g.s_M + MDMRK * 256;
+    float um[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) um[m] = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int t = TK[q];
+        const int pv = ver_off(t >> 2);
+        const float ap = g.s_AR[t * LD + j], rp = g.s_AR[(16 + t) * LD + j];
+        float cl = 0.f, cm = 0.f;
+#pragma unroll
+        for (int s = 0; s <= t; ++s) {
+            const float bvs = g.s_BV[(pv + s) * LD + j], kvs = g.s_KV[(pv + s) * LD + j];
+            if (s < t) cl += Mdlab[t * 16 + s] * bvs + Mdlak[t * 16 + s] * kvs;
+            cm += Mdmrb[t * 16 + s] * bvs + Mdmrk[t * 16 + s] * kvs;
+            if (s + 1 < t) um[s + 1] = fmaf(ap, cl, um[s + 1]);
+            if (s + 1 <= t && s + 1 < 16) um[s + 1] = fmaf(rp, cm, um[s + 1]);
+        }
+        st5[q][2] = cl;          // da pair part (times F_ex later)
+        st5[q][0] = cm;          // dr pair part (times F_in later)
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) g.s_U[(g.wave * 16 + m) * LD + j] = um[m];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int s = TK[q];
+        float accb = 0.f, acck = 0.f;
+#pragma unroll
+        for (int t = s; t < 16; ++t) {
+            const float vv = g.s_VV[(ver_off(t >> 2) + s) * LD + j];
+            const float ap = g.s_AR[t * LD + j], rp = g.s_AR[(16 + t) * LD + j];
+            const float cb = (t > s ? Mdlab[t * 16 + s] * ap : 0.f) + Mdmrb[t * 16 + s] * rp;
+            const float ck = (t > s ? Mdlak[t * 16 + s] * ap : 0.f) + Mdmrk[t * 16 + s] * rp;
+            accb = fmaf(cb, vv, accb);
+            acck = fmaf(ck, vv, acck);
+        }
+        st5[q][3] = accb;
+        st5[q][4] = acck;
+    }
+}
+
+// Chunk-level parts and the final per-token gradients of key column j:
+//   u_m = pair part + sum_{t>=m} dR^_t r_t gamma_t + sum_{t>m} dA^_t a_t gamma_{t-1}
+//         + sum_{s<m} (dB^_s b_s + dK^_s k_s) D_{15,s} + dgamma_C gamma_C,  dw = u / w
+//   da = dA^ gamma_{t-1} + F_ex pair, dr = dR^ gamma_t + F_in pair,
+//   db = dB^ D_{15,t} + pair, dk = dK^ D_{15,t} + pair
+template <int T0, int T1, int T2, int T3>
+__device__ __forceinline__ void assemble_out(const AsmArgs &g, float (&st5)[4][5]) {
+    constexpr int TK[4] = {T0, T1, T2, T3};
+    const int j = g.j;
+    const float *wcol = g.s_in + IW * 16 * LD + j;
+    float wv[16], gam[16], gprev[16], dend[16], fex[16], fin[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) wv[t] = wcol[t * LD];
+    {
+        float gg = 1.f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) { gprev[t] = gg; gg *= wv[t]; gam[t] = gg; }
+        float d = 1.f;
+#pragma unroll
+        for (int s = 15; s >= 0; --s) { dend[s] = d; d *= wv[s]; }
+#pragma unroll
+        for (int sc = 0; sc < 4; ++sc) {
+            float f = 1.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * sc + e;
+                fex[t] = f; f *= wv[t]; fin[t] = f;
+            }
+        }
+    }
+    const float *gA = g.s_G, *gR = g.s_G + 16 * LD, *gB = g.s_G + 32 * LD, *gK = g.s_G + 48 * LD;
+    float suf[17], pre[17];
+    suf[16] = 0.f;
+#pragma unroll
+    for (int t = 15; t >= 0; --t) {
+        float x = gR[t * LD + j] * g.s_in[(IR * 16 + t) * LD + j] * gam[t];
+        if (t < 15) x += gA[(t + 1) * LD + j] * g.s_in[(IA * 16 + t + 1) * LD + j] * gprev[t + 1];
+        suf[t] = suf[t + 1] + x;
+    }
+    pre[0] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+        pre[s + 1] = pre[s] + (gB[s * LD + j] * g.s_in[(IB * 16 + s) * LD + j] +
+                               gK[s * LD + j] * g.s_in[(IK * 16 + s) * LD + j]) * dend[s];
+    const float dgc = g.s_dgC[j] * gam[15];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int t = TK[q];
+        float up = 0.f;
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) up += g.s_U[(w4 * 16 + t) * LD + j];
+        const float uval = up + suf[t] + pre[t] + dgc;
+        const float dr = gR[t * LD + j] * gam[t] + fin[t] * st5[q][0];
+        const float da = gA[t * LD + j] * gprev[t] + fex[t] * st5[q][2];
+        const float db = gB[t * LD + j] * dend[t] + st5[q][3];
+        const float dk = gK[t * LD + j] * dend[t] + st5[q][4];
+        st5[q][0] = dr;
+        st5[q][1] = uval / wv[t];
+        st5[q][2] = da;
+        st5[q][3] = db;
+        st5[q][4] = dk;
     }
 }
 
@@ -186,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
     float *s_BV = sm + O_BV, *s_KV = sm + O_KV, *s_VV = sm + O_VV;
     float *s_S0 = sm + O_S0, *s_DS = sm + O_DS, *s_X = sm + O_X, *s_DR = sm + O_DR;
     float *s_G = sm + O_G, *s_M = sm + O_M, *s_gC = sm + O_GC, *s_dgC = sm + O_DGC;
-    const float *sV = s_in + IV * 1024, *sDY = s_in + IDY * 1024;
+    const float *sV = s_in + IV * 16 * LD, *sDY = s_in + IDY * 16 * LD;
 
     const int64_t ts = (int64_t)H * kN;
     const int64_t base = (u.start * H + h) * kN;
@@ -247,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 #pragma unroll
                     for (int e = 0; e < 8; ++e) x[e] = fmaxf(x[e], kMinW);
                 }
-                float *d = s_in + (st * 16 + t) * 64 + e0;
+                float *d = s_in + (st * 16 + t) * LD + e0;
                 *(float4 *)d = make_float4(x[0], x[1], x[2], x[3]);
                 *(float4 *)(d + 4) = make_float4(x[4], x[5], x[6], x[7]);
             }
@@ -272,23 +392,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         //      d gamma_C[j] = sum_i dS_C[i][j] S_0[i][j]
         {
             const int role = tid >> 6, j = tid & 63;
-            const float *w_ = s_in + IW * 1024 + j;
+            const float *w_ = s_in + IW * 16 * LD + j;
             if (role == 0) {
                 float g = 1.f;
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
-                    s_Q[t * LD + j] = s_in[IA * 1024 + t * 64 + j] * g;
-                    g *= w_[t * 64];
-                    s_Q[(16 + t) * LD + j] = s_in[IR * 1024 + t * 64 + j] * g;
+                    s_Q[t * LD + j] = s_in[(IA * 16 + t) * LD + j] * g;
+                    g *= w_[t * LD];
+                    s_Q[(16 + t) * LD + j] = s_in[(IR * 16 + t) * LD + j] * g;
                 }
                 s_gC[j] = g;
             } else if (role == 1) {
                 float d = 1.f;
 #pragma unroll
                 for (int s = 15; s >= 0; --s) {
-                    s_BK[s * LD + j] = s_in[IB * 1024 + s * 64 + j] * d;
-                    s_BK[(16 + s) * LD + j] = s_in[IK * 1024 + s * 64 + j] * d;
-                    d *= w_[s * 64];
+                    s_BK[s * LD + j] = s_in[(IB * 16 + s) * LD + j] * d;
+                    s_BK[(16 + s) * LD + j] = s_in[(IK * 16 + s) * LD + j] * d;
+                    d *= w_[s * LD];
                 }
                 float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll 8
@@ -300,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             } else {
                 float wv[16], W[4];
 #pragma unroll
-                for (int t = 0; t < 16; ++t) wv[t] = w_[t * 64];
+                for (int t = 0; t < 16; ++t) wv[t] = w_[t * LD];
 #pragma unroll
                 for (int sc = 0; sc < 4; ++sc)
                     W[sc] = (wv[4 * sc] * wv[4 * sc + 1]) * (wv[4 * sc + 2] * wv[4 * sc + 3]);
@@ -311,9 +431,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int t = 4 * sc + e;
-                            s_AR[t * LD + j] = s_in[IA * 1024 + t * 64 + j] * f;
+                            s_AR[t * LD + j] = s_in[(IA * 16 + t) * LD + j] * f;
                             f *= wv[t];
-                            s_AR[(16 + t) * LD + j] = s_in[IR * 1024 + t * 64 + j] * f;
+                            s_AR[(16 + t) * LD + j] = s_in[(IR * 16 + t) * LD + j] * f;
                         }
                     }
                     versions<2>(wv, W, s_in, s_BV, s_KV, s_VV, j);
@@ -393,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         // ---- value side (rows i0..i0+15): X = W (P_a + L_ak V);
         //      dX = B^ dS_C^T + M_rb^T dY; drhs = W^T dX; dV = K^ dS_C^T + M_rk^T dY + L_ak^T drhs
         {
-            const f32x4 rhs = mm_AtB(pa, Mlak, 16, sV + i0, 64, l16, kq, 16);
+            const f32x4 rhs = mm_AtB(pa, Mlak, 16, sV + i0, LD, l16, kq, 16);
             f32x4 xx = {0.f, 0.f, 0.f, 0.f};
             {
                 const float4 wr = *(const float4 *)(Mw + l16 * 16 + 4 * kq);
@@ -402,13 +522,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             }
             f32x4 dx = {0.f, 0.f, 0.f, 0.f};
             dx = mm_AtBt(dx, s_BK, LD, s_DS + i0 * LD, LD, l16, kq, 64);
-            dx = mm_TB(dx, Mmrb, 16, sDY + i0, 64, l16, kq);
+            dx = mm_TB(dx, Mmrb, 16, sDY + i0, LD, l16, kq);
             f32x4 dr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int e = 0; e < 4; ++e) dr = mfma4(Mw[(4 * kq + e) * 16 + l16], dx[e], dr);
             f32x4 dv = {0.f, 0.f, 0.f, 0.f};
             dv = mm_AtBt(dv, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq, 64);
-            dv = mm_TB(dv, Mmrk, 16, sDY + i0, 64, l16, kq);
+            dv = mm_TB(dv, Mmrk, 16, sDY + i0, LD, l16, kq);
 #pragma unroll
             for (int e = 0; e < 4; ++e) dv = mfma4(Mlak[(4 * kq + e) * 16 + l16], dr[e], dv);
 #pragma unroll
@@ -427,9 +547,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         {
             f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = g0, g2 = g0, g3 = g0;
             g0 = mm_AtB(g0, s_DR, LD, s_S0 + j0, LD, l16, kq, 64);
-            g1 = mm_AtB(g1, sDY, 64, s_S0 + j0, LD, l16, kq, 64);
+            g1 = mm_AtB(g1, sDY, LD, s_S0 + j0, LD, l16, kq, 64);
             g2 = mm_AtB(g2, s_X, LD, s_DS + j0, LD, l16, kq, 64);
-            g3 = mm_AtB(g3, sV, 64, s_DS + j0, LD, l16, kq, 64);
+            g3 = mm_AtB(g3, sV, LD, s_DS + j0, LD, l16, kq, 64);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * kq + r;
@@ -440,9 +560,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             }
             // wave 0: dL_ab = drhs X^T, 1: dL_ak = drhs V^T, 2: dM_rb = dY X^T, 3: dM_rk = dY V^T
             const float *lhs = wave < 2 ? s_DR : sDY;
-            const int lld = wave < 2 ? LD : 64;
+            const int lld = LD;
             const float *rt = (wave & 1) ? sV : s_X;
-            const int rld = (wave & 1) ? 64 : LD;
+            const int rld = LD;
             f32x4 gm = {0.f, 0.f, 0.f, 0.f};
             gm = mm_AtBt(gm, lhs, lld, rt, rld, l16, kq, 64);
 #pragma unroll
@@ -459,124 +579,44 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 f32x4 acc = ds[q];
                 acc[0] *= g4.x; acc[1] *= g4.y; acc[2] *= g4.z; acc[3] *= g4.w;
                 acc = mm_TB(acc, s_Q + jq, LD, s_DR + i0, LD, l16, kq);
-                acc = mm_TB(acc, s_Q + 16 * LD + jq, LD, sDY + i0, 64, l16, kq);
+                acc = mm_TB(acc, s_Q + 16 * LD + jq, LD, sDY + i0, LD, l16, kq);
                 ds[q] = acc;
             }
         }
         __syncthreads();
 
-        // ---- key-side gradient assembly: thread (j, tq) owns tokens
-        //      {tq, 7-tq, 8+tq, 15-tq} of key column j (balanced pair counts)
+        // ---- key-side gradient assembly: wave w owns tokens {w, 7-w, 8+w, 15-w}
+        //      (equal pair counts) of key column j = lane + 64 * 0 .. (one column
+        //      per thread); the pair part of u is summed over the 4 waves in LDS
         {
-            const int j = tid >> 2, tq = tid & 3;
-            const int tk[4] = {tq, 7 - tq, 8 + tq, 15 - tq};
-            const float *Mdlab = s_M + MDLAB * 256, *Mdlak = s_M + MDLAK * 256;
-            const float *Mdmrb = s_M + MDMRB * 256, *Mdmrk = s_M + MDMRK * 256;
-            const float *wcol = s_in + IW * 1024 + j;
-
-            // Rows t of this thread: zl_s = dL_ab[t,s] b_s V + dL_ak[t,s] k_s V and
-            // zm_s (same with dM); da_t, dr_t pair parts are F_ex,t sum_s zl_s and
-            // F_in,t sum_s zm_s; u_m gets A'_t zl_s for s < m < t and R'_t zm_s
-            // for s < m <= t, accumulated through the prefix sums over s.
-            float um[16];
-#pragma unroll
-            for (int m = 0; m < 16; ++m) um[m] = 0.f;
-            float zl_tot[4], zm_tot[4];
+            const int j = lane + 0;
+            AsmArgs aa{s_in, s_AR, s_BV, s_KV, s_VV, s_G, s_M, s_dgC, s_S0, j, wave};
+            float st5[4][5];
+            switch (__builtin_amdgcn_readfirstlane(wave)) {
+            case 0: assemble_rows<0, 7, 8, 15>(aa, st5); break;
+            case 1: assemble_rows<1, 6, 9, 14>(aa, st5); break;
+            case 2: assemble_rows<2, 5, 10, 13>(aa, st5); break;
+            default: assemble_rows<3, 4, 11, 12>(aa, st5); break;
+            }
+            __syncthreads();
+            switch (__builtin_amdgcn_readfirstlane(wave)) {
+            case 0: assemble_out<0, 7, 8, 15>(aa, st5); break;
+            case 1: assemble_out<1, 6, 9, 14>(aa, st5); break;
+            case 2: assemble_out<2, 5, 10, 13>(aa, st5); break;
+            default: assemble_out<3, 4, 11, 12>(aa, st5); break;
+            }
+            // store: st5[q] = {dr, dw, da, db, dk} of token tk(q), column j
+            const int tks[4] = {wave, 7 - wave, 8 + wave, 15 - wave};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int t = tk[q];
-                const int pv = ver_off(t >> 2);
-                const float ap = s_AR[t * LD + j], rp = s_AR[(16 + t) * LD + j];
-                float cl = 0.f, cm = 0.f;
-                for (int s = 0; s <= t; ++s) {
-                    const float bvs = s_BV[(pv + s) * LD + j], kvs = s_KV[(pv + s) * LD + j];
-                    const float zm = Mdmrb[t * 16 + s] * bvs + Mdmrk[t * 16 + s] * kvs;
-                    const float zl = Mdlab[t * 16 + s] * bvs + Mdlak[t * 16 + s] * kvs;  // 0 for s = t
-                    cl += zl;
-                    cm += zm;
-                    const int m = s + 1;
-                    if (m < t) um[m] += ap * cl;
-                    if (m <= t) um[m] += rp * cm;
-                }
-                zl_tot[q] = cl;
-                zm_tot[q] = cm;
-            }
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                um[m] += __shfl_xor(um[m], 1, 64);
-                um[m] += __shfl_xor(um[m], 2, 64);
-            }
-            // db_s, dk_s pair parts: sum_{t>=s} (dL_ab[t,s] A'_t + dM_rb[t,s] R'_t) V^(p(t))_s
-            float db_p[4], dk_p[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int s = tk[q];
-                float accb = 0.f, acck = 0.f;
-                for (int t = s; t < 16; ++t) {
-                    const float vv = s_VV[(ver_off(t >> 2) + s) * LD + j];
-                    const float ap = s_AR[t * LD + j], rp = s_AR[(16 + t) * LD + j];
-                    const float cb = Mdlab[t * 16 + s] * ap + Mdmrb[t * 16 + s] * rp;
-                    const float ck = Mdlak[t * 16 + s] * ap + Mdmrk[t * 16 + s] * rp;
-                    accb = fmaf(cb, vv, accb);
-                    acck = fmaf(ck, vv, acck);
-                }
-                db_p[q] = accb;
-                dk_p[q] = acck;
-            }
-            // chunk-level decays of column j: gamma_t, gamma_{t-1}, D_{15,s},
-            // within-sub-chunk prefixes F_ex, F_in
-            float gam[16], gprev[16], dend[16], fex[16], fin[16];
-            {
-                float g = 1.f;
-#pragma unroll
-                for (int t = 0; t < 16; ++t) { gprev[t] = g; g *= wcol[t * 64]; gam[t] = g; }
-                float d = 1.f;
-#pragma unroll
-                for (int s = 15; s >= 0; --s) { dend[s] = d; d *= wcol[s * 64]; }
-#pragma unroll
-                for (int sc = 0; sc < 4; ++sc) {
-                    float f = 1.f;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 4 * sc + e;
-                        fex[t] = f; f *= wcol[t * 64]; fin[t] = f;
-                    }
-                }
-            }
-            // u_m chunk-level part:
-            //   sum_{t>=m} dR^_t r_t gamma_t + sum_{t>m} dA^_t a_t gamma_{t-1}
-            //   + sum_{s<m} (dB^_s b_s + dK^_s k_s) D_{15,s} + dgamma_C gamma_C
-            const float *gA = s_G, *gR = s_G + 16 * LD, *gB = s_G + 32 * LD, *gK = s_G + 48 * LD;
-            float suf[17], pre[17];
-            suf[16] = 0.f;
-#pragma unroll
-            for (int t = 15; t >= 0; --t) {
-                float x = gR[t * LD + j] * s_in[IR * 1024 + t * 64 + j] * gam[t];
-                if (t < 15) x += gA[(t + 1) * LD + j] * s_in[IA * 1024 + (t + 1) * 64 + j] * gprev[t + 1];
-                suf[t] = suf[t + 1] + x;
-            }
-            pre[0] = 0.f;
-#pragma unroll
-            for (int s = 0; s < 16; ++s)
-                pre[s + 1] = pre[s] + (gB[s * LD + j] * s_in[IB * 1024 + s * 64 + j] +
-                                       gK[s * LD + j] * s_in[IK * 1024 + s * 64 + j]) * dend[s];
-            const float dgc = s_dgC[j] * gam[15];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int t = tk[q];
-                const float uval = um[t] + suf[t] + pre[t] + dgc;
-                const float dwv = uval / wcol[t * 64];
-                const float dav = gA[t * LD + j] * gprev[t] + fex[t] * zl_tot[q];
-                const float drv = gR[t * LD + j] * gam[t] + fin[t] * zm_tot[q];
-                const float dbv = gB[t * LD + j] * dend[t] + db_p[q];
-                const float dkv = gK[t * LD + j] * dend[t] + dk_p[q];
+                const int t = tks[q];
                 if (t < L) {
                     const int64_t o = base + (int64_t)(t0 + t) * ts + j;
-                    IO<TI>::st((TI *)p.dr, o, drv);
-                    IO<TI>::st((TI *)p.dw, o, dwv);
-                    IO<TI>::st((TI *)p.da, o, dav);
-                    IO<TI>::st((TI *)p.db, o, dbv);
-                    IO<TI>::st((TI *)p.dk, o, dkv);
+                    IO<TI>::st((TI *)p.dr, o, st5[q][0]);
+                    IO<TI>::st((TI *)p.dw, o, st5[q][1]);
+                    IO<TI>::st((TI *)p.da, o, st5[q][2]);
+                    IO<TI>::st((TI *)p.db, o, st5[q][3]);
+                    IO<TI>::st((TI *)p.dk, o, st5[q][4]);
                 }
             }
         }
