@@ -38,7 +38,7 @@
 namespace wkv7 {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int LD = 68;                            // row pitch of 16x64 / 64x64 arrays
 constexpr float kMinW = 9.313225746154785e-10f;   // 2^-30
 
@@ -108,8 +108,8 @@ __device__ __forceinline__ f32x4 mm_TB(f32x4 acc, const float *A, int lda, const
 }
 
 template <typename TI> struct Raw;
-template <> struct Raw<uint16_t> { uint4 q[4]; };
-template <> struct Raw<float> { float4 q[4][2]; };
+template <> struct Raw<uint16_t> { uint4 q[2]; };
+template <> struct Raw<float> { float4 q[2][2]; };
 
 __device__ __forceinline__ void raw_load(const uint16_t *p, Raw<uint16_t> &r, int k) {
     r.q[k] = *(const uint4 *)p;
@@ -167,17 +167,17 @@ __device__ __forceinline__ void versions(const float *wv, const float *W, const 
 
 struct AsmArgs {
     const float *s_in, *s_AR, *s_BV, *s_KV, *s_VV, *s_G, *s_M, *s_dgC;
-    float *s_U;          // [4][16][LD] partial pair parts of u (aliases S_0)
+    float *s_U;          // [8][16][LD] partial pair parts of u (aliases S_0 and dS_C)
     int j, wave;
 };
 
-// Pair parts for rows t in {T0..T3} of key column j: the prefix sums over s of
-// zl_s = dL_ab[t,s] b_s V + dL_ak[t,s] k_s V and zm_s (same with dM) give the
-// da_t, dr_t pair parts and the straddling-pair part of u (A'_t zl_s for
-// s < m < t, R'_t zm_s for s < m <= t); db_s, dk_s pair parts for s in {T0..T3}.
-template <int T0, int T1, int T2, int T3>
-__device__ __forceinline__ void assemble_rows(const AsmArgs &g, float (&st5)[4][5]) {
-    constexpr int TK[4] = {T0, T1, T2, T3};
+// Pair parts for rows t in {T0, T1} of key column j: the prefix sums over s
+// of zl_s = dL_ab[t,s] b_s V + dL_ak[t,s] k_s V and zm_s (same with dM) give
+// the da_t, dr_t pair parts and the straddling-pair part of u (A'_t zl_s for
+// s < m < t, R'_t zm_s for s < m <= t); db_s, dk_s pair parts for s in {T0, T1}.
+template <int T0, int T1>
+__device__ __forceinline__ void assemble_rows(const AsmArgs &g, float (&st5)[2][5]) {
+    constexpr int TK[2] = {T0, T1};
     const int j = g.j;
     const float *Mdlab = g.s_M + MDLAB * 256, *Mdlak = g.s_M + MDLAK * 256;
     const float *Mdmrb = g.s_M + MDMRB * 256, *Mdmrk = g.s_M + MDMRK * 256;
@@ -185,7 +185,7 @@ __device__ __forceinline__ void assemble_rows(const AsmArgs &g, float (&st5)[4][
 #pragma unroll
     for (int m = 0; m < 16; ++m) um[m] = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
         const int t = TK[q];
         const int pv = ver_off(t >> 2);
         const float ap = g.s_AR[t * LD + j], rp = g.s_AR[(16 + t) * LD + j];
@@ -204,7 +204,7 @@ __device__ __forceinline__ void assemble_rows(const AsmArgs &g, float (&st5)[4][
 #pragma unroll
     for (int m = 0; m < 16; ++m) g.s_U[(g.wave * 16 + m) * LD + j] = um[m];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
         const int s = TK[q];
         float accb = 0.f, acck = 0.f;
 #pragma unroll
@@ -226,9 +226,9 @@ __device__ __forceinline__ void assemble_rows(const AsmArgs &g, float (&st5)[4][
 //         + sum_{s<m} (dB^_s b_s + dK^_s k_s) D_{15,s} + dgamma_C gamma_C,  dw = u / w
 //   da = dA^ gamma_{t-1} + F_ex pair, dr = dR^ gamma_t + F_in pair,
 //   db = dB^ D_{15,t} + pair, dk = dK^ D_{15,t} + pair
-template <int T0, int T1, int T2, int T3>
-__device__ __forceinline__ void assemble_out(const AsmArgs &g, float (&st5)[4][5]) {
-    constexpr int TK[4] = {T0, T1, T2, T3};
+template <int T0, int T1>
+__device__ __forceinline__ void assemble_out(const AsmArgs &g, float (&st5)[2][5]) {
+    constexpr int TK[2] = {T0, T1};
     const int j = g.j;
     const float *wcol = g.s_in + IW * 16 * LD + j;
     float wv[16], gam[16], gprev[16], dend[16], fex[16], fin[16];
@@ -267,11 +267,11 @@ __device__ __forceinline__ void assemble_out(const AsmArgs &g, float (&st5)[4][5
                                gK[s * LD + j] * g.s_in[(IK * 16 + s) * LD + j]) * dend[s];
     const float dgc = g.s_dgC[j] * gam[15];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
         const int t = TK[q];
         float up = 0.f;
 #pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) up += g.s_U[(w4 * 16 + t) * LD + j];
+        for (int w8 = 0; w8 < 8; ++w8) up += g.s_U[(w8 * 16 + t) * LD + j];
         const float uval = up + suf[t] + pre[t] + dgc;
         const float dr = gR[t * LD + j] * gam[t] + fin[t] * st5[q][0];
         const float da = gA[t * LD + j] * gprev[t] + fex[t] * st5[q][2];
@@ -296,10 +296,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
     const Unit u = resolve_unit(p.seg, sq);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, kq = lane >> 4;
-    const int i0 = 16 * wave;      // value rows of this wave
-    const int j0 = 16 * wave;      // key columns of this wave
+    const int lane0 = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 8 waves; w and w+4 share a SIMD
+    int lane = lane0, l16 = lane0 & 15, kq = lane0 >> 4;
+    // The lane indices are re-derived opaquely at the start of each phase, so
+    // that the many LDS addresses built from them are formed inside the phase
+    // instead of being hoisted out of the chunk loop and kept live throughout.
+    auto relane = [&]() {
+        int lv = lane0;
+        asm volatile("" : "+v"(lv));
+        lane = lv; l16 = lv & 15; kq = lv >> 4;
+    };
+    const int w4 = wave & 3;                         // 16-row / 16-column tile of this wave
+    const bool lo = wave < 4;
 
     float *s_in = sm + O_IN;
     float *s_Q = sm + O_Q, *s_BK = sm + O_BK, *s_AR = sm + O_AR;
@@ -307,31 +316,36 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
     float *s_S0 = sm + O_S0, *s_DS = sm + O_DS, *s_X = sm + O_X, *s_DR = sm + O_DR;
     float *s_G = sm + O_G, *s_M = sm + O_M, *s_gC = sm + O_GC, *s_dgC = sm + O_DGC;
     const float *sV = s_in + IV * 16 * LD, *sDY = s_in + IDY * 16 * LD;
+    const float *Mlak = s_M + MLAK * 256, *Mmrb = s_M + MMRB * 256, *Mmrk = s_M + MMRK * 256;
+    const float *Mw = s_M + MW * 256;
 
     const int64_t ts = (int64_t)H * kN;
     const int64_t base = (u.start * H + h) * kN;
     const int64_t sbase = ((int64_t)sq * H + h) * (kN * kN);
 
-    // dS carried between chunks: ds[q][r] = dS[i0 + l16][16q + 4kq + r]
-    f32x4 ds[4];
+    // dS carried between chunks, two 16x16 tiles per wave:
+    // ds[q][r] = dS[16*w4 + l16][16*jt + 4*kq + r], jt = 2*(wave >> 2) + q
+    const int it = w4;
+    f32x4 ds[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
+        const int jt = 2 * (wave >> 2) + q;
         if (p.ds_out) {
-            const float4 v4 = *(const float4 *)(p.ds_out + sbase + (int64_t)(i0 + l16) * kN + 16 * q + 4 * kq);
+            const float4 v4 = *(const float4 *)(p.ds_out + sbase + (int64_t)(16 * it + l16) * kN + 16 * jt + 4 * kq);
             ds[q] = f32x4{v4.x, v4.y, v4.z, v4.w};
         } else {
             ds[q] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
 
-    // Staging: element groups g = tid + 256k (k = 0..3) of 7 streams x 16
+    // Staging: element groups g = tid + 512k (k = 0, 1) of 7 streams x 16
     // tokens x 8 groups of 8; stream g >> 7 is uniform per wave.
     const int nch = (u.len + kChunk - 1) / kChunk;
     Raw<TI> raw;
     auto issue = [&](int cc) {
         const int Lc = min(kChunk, u.len - cc * kChunk);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 2; ++k) {
             const int g = tid + k * kThreads;
             const int st = __builtin_amdgcn_readfirstlane(g >> 7);
             const int t = (g >> 3) & 15, e0 = (g & 7) * 8;
@@ -347,11 +361,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         const int t0 = c * kChunk;
         const int L = min(kChunk, u.len - t0);
         __syncthreads();
+        relane();
 
         // ---- stage inputs (w clamped; identity tokens past the end), the
         //      checkpoint S_0 and dS_C; then prefetch chunk c-1
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 2; ++k) {
             const int g = tid + k * kThreads;
             if (g < 7 * 128) {
                 const int st = g >> 7, t = (g >> 3) & 15, e0 = (g & 7) * 8;
@@ -375,25 +390,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         {
             const float *cp = p.ckpt + ((u.ckpt + c) * H + h) * (int64_t)(kN * kN);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < 2; ++k) {
                 const int f4 = tid + k * kThreads;
                 const int row = f4 >> 4, col = (f4 & 15) * 4;
                 *(float4 *)(s_S0 + row * LD + col) = *(const float4 *)(cp + row * 64 + col);
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *(float4 *)(s_DS + (i0 + l16) * LD + 16 * q + 4 * kq) =
+            for (int q = 0; q < 2; ++q) {
+                const int jt = 2 * (wave >> 2) + q;
+                *(float4 *)(s_DS + (16 * it + l16) * LD + 16 * jt + 4 * kq) =
                     make_float4(ds[q][0], ds[q][1], ds[q][2], ds[q][3]);
+            }
         }
         if (c > 0) issue(c - 1);
         __syncthreads();
+        relane();
 
-        // ---- decay products and operand rows (4 roles x 64 key columns);
-        //      d gamma_C[j] = sum_i dS_C[i][j] S_0[i][j]
+        // ---- decay products and operand rows: one role per wave over the 64
+        //      key columns (lane = column)
         {
-            const int role = tid >> 6, j = tid & 63;
+            const int role = __builtin_amdgcn_readfirstlane(wave), j = lane;
             const float *w_ = s_in + IW * 16 * LD + j;
-            if (role == 0) {
+            if (role == 0) {             // A^, R^, gamma_C
                 float g = 1.f;
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
@@ -402,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                     s_Q[(16 + t) * LD + j] = s_in[(IR * 16 + t) * LD + j] * g;
                 }
                 s_gC[j] = g;
-            } else if (role == 1) {
+            } else if (role == 1) {      // B^, K^
                 float d = 1.f;
 #pragma unroll
                 for (int s = 15; s >= 0; --s) {
@@ -410,6 +428,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                     s_BK[(16 + s) * LD + j] = s_in[(IK * 16 + s) * LD + j] * d;
                     d *= w_[s * LD];
                 }
+            } else if (role == 2) {      // d gamma_C[j] = sum_i dS_C[i][j] S_0[i][j]
                 float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll 8
                 for (int i = 0; i < 64; i += 2) {
@@ -417,48 +436,54 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                     acc1 = fmaf(s_DS[(i + 1) * LD + j], s_S0[(i + 1) * LD + j], acc1);
                 }
                 s_dgC[j] = acc0 + acc1;
-            } else {
+            } else if (role == 3) {      // A' = a F_ex, R' = r F_in
+#pragma unroll
+                for (int sc = 0; sc < 4; ++sc) {
+                    float f = 1.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 4 * sc + e;
+                        s_AR[t * LD + j] = s_in[(IA * 16 + t) * LD + j] * f;
+                        f *= w_[t * LD];
+                        s_AR[(16 + t) * LD + j] = s_in[(IR * 16 + t) * LD + j] * f;
+                    }
+                }
+            } else {                     // b, k, bare versions of source sub-chunk role - 4
                 float wv[16], W[4];
 #pragma unroll
                 for (int t = 0; t < 16; ++t) wv[t] = w_[t * LD];
 #pragma unroll
                 for (int sc = 0; sc < 4; ++sc)
                     W[sc] = (wv[4 * sc] * wv[4 * sc + 1]) * (wv[4 * sc + 2] * wv[4 * sc + 3]);
-                if (role == 2) {
-#pragma unroll
-                    for (int sc = 0; sc < 4; ++sc) {
-                        float f = 1.f;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int t = 4 * sc + e;
-                            s_AR[t * LD + j] = s_in[(IA * 16 + t) * LD + j] * f;
-                            f *= wv[t];
-                            s_AR[(16 + t) * LD + j] = s_in[(IR * 16 + t) * LD + j] * f;
-                        }
-                    }
-                    versions<2>(wv, W, s_in, s_BV, s_KV, s_VV, j);
-                    versions<3>(wv, W, s_in, s_BV, s_KV, s_VV, j);
-                } else {
-                    versions<0>(wv, W, s_in, s_BV, s_KV, s_VV, j);
-                    versions<1>(wv, W, s_in, s_BV, s_KV, s_VV, j);
-                }
+                if (role == 4) versions<0>(wv, W, s_in, s_BV, s_KV, s_VV, j);
+                else if (role == 5) versions<1>(wv, W, s_in, s_BV, s_KV, s_VV, j);
+                else if (role == 6) versions<2>(wv, W, s_in, s_BV, s_KV, s_VV, j);
+                else versions<3>(wv, W, s_in, s_BV, s_KV, s_VV, j);
             }
         }
         __syncthreads();
+        relane();
 
-        // ---- P_a = A^ S_0^T for this wave's value rows (MFMA); the four 16x16
-        //      matrices (VALU, one pair of dot products per thread)
+        // ---- waves 0-3: P_a = A^ S_0^T (value rows 16*w4..). waves 4-7: the
+        //      four 16x16 matrices on VALU (one pair of dots per thread) and, on
+        //      MFMA, dR^ = dY S_0 and dK^ = V dS_C for key columns 16*w4..
         f32x4 pa = {0.f, 0.f, 0.f, 0.f};
-        pa = mm_AtBt(pa, s_Q, LD, s_S0 + i0 * LD, LD, l16, kq, 64);
-        {
+        if (lo) {
+            pa = mm_AtBt(pa, s_Q, LD, s_S0 + 16 * it * LD, LD, l16, kq, 64);
+        } else {
+            const int jc = 16 * w4;
+            f32x4 g1 = {0.f, 0.f, 0.f, 0.f}, g3 = g1;
+            g1 = mm_AtB(g1, sDY, LD, s_S0 + jc, LD, l16, kq, 64);
+            g3 = mm_AtB(g3, sV, LD, s_DS + jc, LD, l16, kq, 64);
+            const int item = tid - 256;
             int t, s, mat;
-            if (tid < 120) {
+            if (item < 120) {
                 t = 1;
-                while ((t + 1) * t / 2 <= tid) ++t;
-                s = tid - t * (t - 1) / 2;
+                while ((t + 1) * t / 2 <= item) ++t;
+                s = item - t * (t - 1) / 2;
                 mat = 0;
             } else {
-                const int mi = tid - 120;
+                const int mi = item - 120;
                 t = 0;
                 while ((t + 1) * (t + 2) / 2 <= mi) ++t;
                 s = mi - t * (t + 1) / 2;
@@ -485,34 +510,53 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             }
             s_M[(2 * mat) * 256 + t * 16 + s] = db0 + db1;
             s_M[(2 * mat + 1) * 256 + t * 16 + s] = dk0 + dk1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tt = 4 * kq + r;
+                s_G[(1 * 16 + tt) * LD + jc + l16] = g1[r];
+                s_G[(3 * 16 + tt) * LD + jc + l16] = g3[r];
+            }
         }
         __syncthreads();
+        relane();
 
-        // ---- W = (I - L_ab)^-1 (16 threads); clear the upper parts
-        if (tid < 16) {
-            float x[16];
+        // ---- W = (I - L_ab)^-1 (wave 0, 16 lanes); upper parts cleared (wave 1);
+        //      dM_rk = dY V^T (wave 2; lower part incl. the diagonal)
+        if (wave == 0) {
+            if (lane < 16) {
+                float x[16];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) x[t] = t == tid ? 1.f : 0.f;
+                for (int t = 0; t < 16; ++t) x[t] = t == lane ? 1.f : 0.f;
 #pragma unroll
-            for (int s2 = 0; s2 < 15; ++s2) {
+                for (int s2 = 0; s2 < 15; ++s2) {
 #pragma unroll
-                for (int t = s2 + 1; t < 16; ++t) x[t] = fmaf(s_M[MLAB * 256 + t * 16 + s2], x[s2], x[t]);
+                    for (int t = s2 + 1; t < 16; ++t) x[t] = fmaf(s_M[MLAB * 256 + t * 16 + s2], x[s2], x[t]);
+                }
+#pragma unroll
+                for (int t = 0; t < 16; ++t) s_M[MW * 256 + t * 16 + lane] = x[t];
             }
-#pragma unroll
-            for (int t = 0; t < 16; ++t) s_M[MW * 256 + t * 16 + tid] = x[t];
-        } else if (tid >= 64 && tid < 128) {
-            const int m = (tid - 64) >> 4, row = tid & 15;
+        } else if (wave == 1) {
+            const int m = lane >> 4, row = lane & 15;
             const int first = m < 2 ? row : row + 1;
             for (int c2 = first; c2 < 16; ++c2) s_M[m * 256 + row * 16 + c2] = 0.f;
+        } else if (wave == 2) {
+            f32x4 gm = {0.f, 0.f, 0.f, 0.f};
+            gm = mm_AtBt(gm, sDY, LD, sV, LD, l16, kq, 64);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * kq + r;
+                s_M[MDMRK * 256 + t * 16 + l16] = l16 <= t ? gm[r] : 0.f;
+            }
         }
         __syncthreads();
+        relane();
 
-        const float *Mlak = s_M + MLAK * 256, *Mmrb = s_M + MMRB * 256, *Mmrk = s_M + MMRK * 256;
-        const float *Mw = s_M + MW * 256;
-
-        // ---- value side (rows i0..i0+15): X = W (P_a + L_ak V);
-        //      dX = B^ dS_C^T + M_rb^T dY; drhs = W^T dX; dV = K^ dS_C^T + M_rk^T dY + L_ak^T drhs
-        {
+        // ---- value side. waves 0-3 (rows 16*w4..): X = W (P_a + L_ak V);
+        //      dX = B^ dS_C^T + M_rb^T dY; drhs = W^T dX.
+        //      waves 4-7 (same rows): dV partial = K^ dS_C^T + M_rk^T dY
+        const int i0 = 16 * it;
+        f32x4 dvp = {0.f, 0.f, 0.f, 0.f};
+        if (lo) {
             const f32x4 rhs = mm_AtB(pa, Mlak, 16, sV + i0, LD, l16, kq, 16);
             f32x4 xx = {0.f, 0.f, 0.f, 0.f};
             {
@@ -526,55 +570,63 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             f32x4 dr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int e = 0; e < 4; ++e) dr = mfma4(Mw[(4 * kq + e) * 16 + l16], dx[e], dr);
-            f32x4 dv = {0.f, 0.f, 0.f, 0.f};
-            dv = mm_AtBt(dv, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq, 64);
-            dv = mm_TB(dv, Mmrk, 16, sDY + i0, LD, l16, kq);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dv = mfma4(Mlak[(4 * kq + e) * 16 + l16], dr[e], dv);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * kq + r;
                 s_X[t * LD + i0 + l16] = xx[r];
                 s_DR[t * LD + i0 + l16] = dr[r];
-                if (t < L) IO<TI>::st((TI *)p.dv, base + (int64_t)(t0 + t) * ts + i0 + l16, dv[r]);
             }
+        } else {
+            dvp = mm_AtBt(dvp, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq, 64);
+            dvp = mm_TB(dvp, Mmrk, 16, sDY + i0, LD, l16, kq);
         }
         __syncthreads();
+        relane();
 
-        // ---- key side (columns j0..j0+15), contractions over i:
-        //      dA^ = drhs S_0, dR^ = dY S_0, dB^ = X dS_C, dK^ = V dS_C;
-        //      one 16x16 matrix gradient per wave; dS_0^T tiles (over t)
+        // ---- key side and the state gradient:
+        //      waves 4-7 finish dV = partial + L_ak^T drhs and store it;
+        //      waves 0-3: dA^ = drhs S_0, waves 4-7: dB^ = X dS_C (key columns 16*w4..);
+        //      waves 0, 1, 2: dL_ab = drhs X^T, dL_ak = drhs V^T, dM_rb = dY X^T;
+        //      every wave: its two dS_0^T tiles
         {
-            f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = g0, g2 = g0, g3 = g0;
-            g0 = mm_AtB(g0, s_DR, LD, s_S0 + j0, LD, l16, kq, 64);
-            g1 = mm_AtB(g1, sDY, LD, s_S0 + j0, LD, l16, kq, 64);
-            g2 = mm_AtB(g2, s_X, LD, s_DS + j0, LD, l16, kq, 64);
-            g3 = mm_AtB(g3, sV, LD, s_DS + j0, LD, l16, kq, 64);
+            const int jc = 16 * w4;
+            if (!lo) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * kq + r;
-                s_G[(0 * 16 + t) * LD + j0 + l16] = g0[r];
-                s_G[(1 * 16 + t) * LD + j0 + l16] = g1[r];
-                s_G[(2 * 16 + t) * LD + j0 + l16] = g2[r];
-                s_G[(3 * 16 + t) * LD + j0 + l16] = g3[r];
-            }
-            // wave 0: dL_ab = drhs X^T, 1: dL_ak = drhs V^T, 2: dM_rb = dY X^T, 3: dM_rk = dY V^T
-            const float *lhs = wave < 2 ? s_DR : sDY;
-            const int lld = LD;
-            const float *rt = (wave & 1) ? sV : s_X;
-            const int rld = LD;
-            f32x4 gm = {0.f, 0.f, 0.f, 0.f};
-            gm = mm_AtBt(gm, lhs, lld, rt, rld, l16, kq, 64);
+                for (int e = 0; e < 4; ++e) {
+                    const int k = 4 * kq + e;
+                    dvp = mfma4(Mlak[k * 16 + l16], s_DR[k * LD + i0 + l16], dvp);
+                }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * kq + r;
-                const bool keep = wave < 2 ? (l16 < t) : (l16 <= t);
-                s_M[(MDLAB + wave) * 256 + t * 16 + l16] = keep ? gm[r] : 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * kq + r;
+                    if (t < L) IO<TI>::st((TI *)p.dv, base + (int64_t)(t0 + t) * ts + i0 + l16, dvp[r]);
+                }
+                f32x4 g2 = {0.f, 0.f, 0.f, 0.f};
+                g2 = mm_AtB(g2, s_X, LD, s_DS + jc, LD, l16, kq, 64);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s_G[(2 * 16 + 4 * kq + r) * LD + jc + l16] = g2[r];
+            } else {
+                f32x4 g0 = {0.f, 0.f, 0.f, 0.f};
+                g0 = mm_AtB(g0, s_DR, LD, s_S0 + jc, LD, l16, kq, 64);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s_G[(0 * 16 + 4 * kq + r) * LD + jc + l16] = g0[r];
+                if (wave < 3) {
+                    const float *lhs = wave < 2 ? s_DR : sDY;
+                    const float *rt = wave == 1 ? sV : s_X;
+                    f32x4 gm = {0.f, 0.f, 0.f, 0.f};
+                    gm = mm_AtBt(gm, lhs, LD, rt, LD, l16, kq, 64);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 4 * kq + r;
+                        const bool keep = wave < 2 ? (l16 < t) : (l16 <= t);
+                        s_M[(MDLAB + wave) * 256 + t * 16 + l16] = keep ? gm[r] : 0.f;
+                    }
+                }
             }
             // dS_0^T[j][i] = gamma_C[j] dS_C^T[j][i] + sum_t A^[t][j] drhs[t][i] + R^[t][j] dY[t][i]
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int jq = 16 * q;
+            for (int q = 0; q < 2; ++q) {
+                const int jq = 16 * (2 * (wave >> 2) + q);
                 const float4 g4 = *(const float4 *)(s_gC + jq + 4 * kq);
                 f32x4 acc = ds[q];
                 acc[0] *= g4.x; acc[1] *= g4.y; acc[2] *= g4.z; acc[3] *= g4.w;
@@ -584,31 +636,39 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             }
         }
         __syncthreads();
+        relane();
 
-        // ---- key-side gradient assembly: wave w owns tokens {w, 7-w, 8+w, 15-w}
-        //      (equal pair counts) of key column j = lane + 64 * 0 .. (one column
-        //      per thread); the pair part of u is summed over the 4 waves in LDS
+        // ---- key-side gradient assembly: wave w owns tokens {w, 15-w} of every
+        //      key column (lane = column); u's pair part is summed over the 8 waves
         {
-            const int j = lane + 0;
+            const int j = lane;
             AsmArgs aa{s_in, s_AR, s_BV, s_KV, s_VV, s_G, s_M, s_dgC, s_S0, j, wave};
-            float st5[4][5];
+            float st5[2][5];
             switch (__builtin_amdgcn_readfirstlane(wave)) {
-            case 0: assemble_rows<0, 7, 8, 15>(aa, st5); break;
-            case 1: assemble_rows<1, 6, 9, 14>(aa, st5); break;
-            case 2: assemble_rows<2, 5, 10, 13>(aa, st5); break;
-            default: assemble_rows<3, 4, 11, 12>(aa, st5); break;
+            case 0: assemble_rows<0, 15>(aa, st5); break;
+            case 1: assemble_rows<1, 14>(aa, st5); break;
+            case 2: assemble_rows<2, 13>(aa, st5); break;
+            case 3: assemble_rows<3, 12>(aa, st5); break;
+            case 4: assemble_rows<4, 11>(aa, st5); break;
+            case 5: assemble_rows<5, 10>(aa, st5); break;
+            case 6: assemble_rows<6, 9>(aa, st5); break;
+            default: assemble_rows<7, 8>(aa, st5); break;
             }
             __syncthreads();
+            relane();
             switch (__builtin_amdgcn_readfirstlane(wave)) {
-            case 0: assemble_out<0, 7, 8, 15>(aa, st5); break;
-            case 1: assemble_out<1, 6, 9, 14>(aa, st5); break;
-            case 2: assemble_out<2, 5, 10, 13>(aa, st5); break;
-            default: assemble_out<3, 4, 11, 12>(aa, st5); break;
+            case 0: assemble_out<0, 15>(aa, st5); break;
+            case 1: assemble_out<1, 14>(aa, st5); break;
+            case 2: assemble_out<2, 13>(aa, st5); break;
+            case 3: assemble_out<3, 12>(aa, st5); break;
+            case 4: assemble_out<4, 11>(aa, st5); break;
+            case 5: assemble_out<5, 10>(aa, st5); break;
+            case 6: assemble_out<6, 9>(aa, st5); break;
+            default: assemble_out<7, 8>(aa, st5); break;
             }
-            // store: st5[q] = {dr, dw, da, db, dk} of token tk(q), column j
-            const int tks[4] = {wave, 7 - wave, 8 + wave, 15 - wave};
+            const int tks[2] = {wave, 15 - wave};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 2; ++q) {
                 const int t = tks[q];
                 if (t < L) {
                     const int64_t o = base + (int64_t)(t0 + t) * ts + j;
@@ -622,10 +682,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         }
     }
     if (p.ds0) {
-        float *op = p.ds0 + sbase + (int64_t)(i0 + l16) * kN;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            *(float4 *)(op + 16 * q + 4 * kq) = make_float4(ds[q][0], ds[q][1], ds[q][2], ds[q][3]);
+        for (int q = 0; q < 2; ++q) {
+            const int jt = 2 * (wave >> 2) + q;
+            *(float4 *)(p.ds0 + sbase + (int64_t)(16 * it + l16) * kN + 16 * jt + 4 * kq) =
+                make_float4(ds[q][0], ds[q][1], ds[q][2], ds[q][3]);
+        }
     }
 }
 
