@@ -342,17 +342,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
     // tokens x 8 groups of 8; stream g >> 7 is uniform per wave.
     const int nch = (u.len + kChunk - 1) / kChunk;
     Raw<TI> raw;
+    float4 ckr0, ckr1;                          // checkpoint of the chunk in flight
+    const TI *sp[2];                            // stream of each staged group (uniform)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int st = __builtin_amdgcn_readfirstlane((tid + k * kThreads) >> 7);
+        const void *vp = p.staged[st];
+        sp[k] = vp ? (const TI *)vp + base : nullptr;
+    }
     auto issue = [&](int cc) {
         const int Lc = min(kChunk, u.len - cc * kChunk);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int g = tid + k * kThreads;
-            const int st = __builtin_amdgcn_readfirstlane(g >> 7);
             const int t = (g >> 3) & 15, e0 = (g & 7) * 8;
-            const void *vp = st == IR ? p.r : st == IW ? p.w : st == IK ? p.k : st == IA ? p.a
-                           : st == IB ? p.b : st == IV ? p.v : st == IDY ? p.dy : nullptr;
-            if (vp && t < Lc) raw_load((const TI *)vp + base + (int64_t)(cc * kChunk + t) * ts + e0, raw, k);
+            if (sp[k] && t < Lc) raw_load(sp[k] + (int64_t)(cc * kChunk + t) * ts + e0, raw, k);
         }
+        // float4 f4 = tid + 512k of the 64x64 checkpoint: row f4 / 16, column 4 (f4 % 16)
+        const float *cp = p.ckpt + ((u.ckpt + cc) * H + h) * (int64_t)(kN * kN) + tid * 4;
+        ckr0 = *(const float4 *)cp;
+        ckr1 = *(const float4 *)(cp + kThreads * 4);
     };
     if (nch > 0) issue(nch - 1);
 
@@ -360,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
     for (int c = nch - 1; c >= 0; --c) {
         const int t0 = c * kChunk;
         const int L = min(kChunk, u.len - t0);
-        __syncthreads();
+        lds_barrier();
         relane();
 
         // ---- stage inputs (w clamped; identity tokens past the end), the
@@ -388,13 +397,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             }
         }
         {
-            const float *cp = p.ckpt + ((u.ckpt + c) * H + h) * (int64_t)(kN * kN);
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int f4 = tid + k * kThreads;
-                const int row = f4 >> 4, col = (f4 & 15) * 4;
-                *(float4 *)(s_S0 + row * LD + col) = *(const float4 *)(cp + row * 64 + col);
-            }
+            *(float4 *)(s_S0 + (tid >> 4) * LD + (tid & 15) * 4) = ckr0;
+            *(float4 *)(s_S0 + ((tid + kThreads) >> 4) * LD + (tid & 15) * 4) = ckr1;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int jt = 2 * (wave >> 2) + q;
@@ -403,7 +407,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             }
         }
         if (c > 0) issue(c - 1);
-        __syncthreads();
+        lds_barrier();
         relane();
 
         // ---- decay products and operand rows: one role per wave over the 64
@@ -461,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 else versions<3>(wv, W, s_in, s_BV, s_KV, s_VV, j);
             }
         }
-        __syncthreads();
+        lds_barrier();
         relane();
 
         // ---- waves 0-3: P_a = A^ S_0^T (value rows 16*w4..). waves 4-7: the
@@ -517,7 +521,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 s_G[(3 * 16 + tt) * LD + jc + l16] = g3[r];
             }
         }
-        __syncthreads();
+        lds_barrier();
         relane();
 
         // ---- W = (I - L_ab)^-1 (wave 0, 16 lanes); upper parts cleared (wave 1);
@@ -548,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 s_M[MDMRK * 256 + t * 16 + l16] = l16 <= t ? gm[r] : 0.f;
             }
         }
-        __syncthreads();
+        lds_barrier();
         relane();
 
         // ---- value side. waves 0-3 (rows 16*w4..): X = W (P_a + L_ak V);
@@ -580,7 +584,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             dvp = mm_AtBt(dvp, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq, 64);
             dvp = mm_TB(dvp, Mmrk, 16, sDY + i0, LD, l16, kq);
         }
-        __syncthreads();
+        lds_barrier();
         relane();
 
         // ---- key side and the state gradient:
@@ -635,7 +639,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 ds[q] = acc;
             }
         }
-        __syncthreads();
+        lds_barrier();
         relane();
 
         // ---- key-side gradient assembly: wave w owns tokens {w, 15-w} of every
@@ -654,7 +658,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             case 6: assemble_rows<6, 9>(aa, st5); break;
             default: assemble_rows<7, 8>(aa, st5); break;
             }
-            __syncthreads();
+            lds_barrier();
             relane();
             switch (__builtin_amdgcn_readfirstlane(wave)) {
             case 0: assemble_out<0, 15>(aa, st5); break;
@@ -693,7 +697,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 
 }  // namespace
 
-hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
+hipError_t launch_backward(const BwdArgs &args, hipStream_t stream) {
+    BwdArgs a = args;
+    const void *staged[8] = {a.r, a.w, a.k, a.a, a.b, a.v, a.dy, nullptr};
+    static_assert(IR == 0 && IW == 1 && IK == 2 && IA == 3 && IB == 4 && IV == 5 && IDY == 6,
+                  "staged stream order");
+    for (int i = 0; i < 8; ++i) a.staged[i] = staged[i];
     const int S = a.seg.num_seqs > 0 ? a.seg.num_seqs : a.seg.B;
     const int32_t units = S * a.seg.H;
     const size_t lds = (size_t)LDS_FLOATS * sizeof(float);

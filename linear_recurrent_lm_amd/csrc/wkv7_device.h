@@ -31,6 +31,15 @@ struct Unit {
 // Reads the segment table entry of sequence s and rejects entries that would
 // leave the buffers (negative length, crossing a row, checkpoint slots out of
 // range): such a sequence is treated as empty.
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
+// only, so global loads issued ahead (prefetch) and global stores stay in
+// flight across it. (__syncthreads also waits for every outstanding global
+// access of the wave.) The "memory" clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ inline Unit resolve_unit(const SegParams &p, int s) {
     Unit u;
     const int64_t nc = (p.T + kChunk - 1) / kChunk;

@@ -12,57 +12,70 @@
 // with rows A^_t = gamma_{t-1} a_t, R^_t = gamma_t r_t, B^_s = D_{16,s} b_s,
 // K^_s = D_{16,s} k_s and the 16x16 matrices
 //     L_ab[t,s] = <a_t, b_s D_{t-1,s}>  (s < t)     M_rb[t,s] = <r_t, b_s D_{t,s}>  (s <= t)
-// (L_ak, M_rk the same with k_s). The two dense contractions [A^;R^] S_0^T
-// (32x64x64) and [X|V]^T [B^;K^] (64x64x32) run on v_mfma_f32_16x16x4_f32;
-// everything else is VALU.
+// (L_ak, M_rk the same with k_s).
 //
-// The 16x16 matrices are built as dot products of precomputed rows using
-// 4-token sub-chunks: for t in sub-chunk p and s in an earlier sub-chunk q the
-// decay factorises division-free as D_{t-1,s} = [prod_{4p<=u<t} w_u] *
-// [prod_{s<u<4p} w_u]; for s in the same sub-chunk the within-sub-chunk
-// prefix F_s = prod_{4p<=u<=s} w_u is divided out, with every factor of F
-// clamped to >= 2^-30 so F >= 2^-120 stays a normal fp32 number (w = 0
-// then acts as 2^-30 on at most three neighbouring tokens of one sub-chunk).
-// The chunk-level decays (gamma, D_{16,s}) are exact products.
+// The 16x16 matrices. A pair decay splits at any token R with s < R <= t into
+// two factors that are both <= 1: D_{t-1,s} = [prod_{R<=u<t} w_u] [prod_{s<u<R} w_u].
+// With 4-token sub-chunks, every pair (t, s) in different sub-chunks has such a
+// split point shared by a whole block: R = 8 for t in 8..15, s in 0..7; R = 4
+// and R = 12 for the blocks (4..7, 0..3) and (12..15, 8..11). Those blocks are
+// two 16x16x64 MFMA products of precomputed rows (a, r rows scaled from R; b, k
+// rows scaled to R; the R = 4 and R = 12 blocks share one product whose two
+// off-diagonal quadrants are discarded). Pairs inside one sub-chunk divide out
+// the within-sub-chunk prefix F_s = prod_{4p<=u<=s} w_u instead, with every
+// factor clamped to >= 2^-30 so F >= 2^-120 stays a normal fp32 number (w = 0
+// then acts as 2^-30 on at most three neighbouring tokens); they are VALU dot
+// products. W = (I - L_ab)^-1 comes from column-wise forward substitution.
 //
-// Layout and work split: one 256-thread workgroup (4 waves) per (sequence,
-// head, block of RB value rows); value rows are independent, so a unit may be
-// split in 1, 2 or 4 row blocks to fill the machine. The state block lives in
-// the MFMA accumulators as S^T tiles: lane l of a wave holds
-// S[i0 + 16*it + l%16][16*jt + 4*(l/16) + r], r = 0..3, which is directly the
-// B operand of the next chunk's [A^;R^] S_0^T product. Inputs are staged to
-// LDS as fp32 with one 16-byte load per 8 bf16 values.
+// Work split (warp specialisation): a workgroup owns RB = 16*NMW value rows
+// of one (sequence, head) and has NMW "state" waves and 8 "operand" waves.
+// Only the state waves touch the state: each holds 16 rows x 64 columns of S
+// in MFMA accumulators as S^T tiles (lane l holds S[row0 + l%16][16*jt +
+// 4*(l/16) + r]), which is directly the B operand of the next chunk's
+// [A^;R^] S_0^T product, and the D1 -> chain -> D2 sequence of a chunk stays
+// in registers (the chain's outputs come out in the B-operand layout of the
+// next product). The operand waves stage inputs and build everything that does
+// not depend on the state (decay rows, the 16x16 matrices, W) for chunk c
+// while the state waves advance through chunk c-1; the two sides meet through
+// a double-buffered LDS hand-off, three workgroup barriers per chunk.
 #include "wkv7_kernels.h"
 
 namespace wkv7 {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int QLD = 68;    // row stride (floats) of Q and the C x C operand rows
-constexpr int KLD = 36;    // row stride of the transposed [B^;K^] and [X|V] tiles
+constexpr int kPrepWaves = 8;
+constexpr int QLD = 68;    // row stride (floats) of 64-wide rows
+constexpr int KLD = 36;    // row stride of the transposed [B^;K^] tile
+constexpr int VLD = 20;    // row stride of the transposed V tile
+constexpr int MLD = 20;    // row stride of the 16x16 matrices
 constexpr float kMinFactor = 9.313225746154785e-10f;  // 2^-30
 
-// LDS layout (floats).
-template <int RB>
-struct Lay {
-    static constexpr int IN = 0;                       // [5][16][64]: r w k a b
-    static constexpr int P = 0;                        // alias [WPI][32][RB]
-    static constexpr int LM = 2048;                    // alias [4][16][16]
-    static constexpr int Q = 5 * 16 * 64;              // [32][QLD]: A^, R^
-    static constexpr int BKT = Q + 32 * QLD;           // [64][KLD]: B^ | K^ (by column j)
-    static constexpr int XVT = BKT + 64 * KLD;         // [RB][KLD]: X | V (by row i)
-    static constexpr int AR = XVT + RB * KLD;          // [32][QLD]: A' (a), A' (r)
-    static constexpr int BV = AR + 32 * QLD;           // [40][QLD]: b versions
-    static constexpr int KV = BV + 40 * QLD;           // [40][QLD]: k versions
-    static constexpr int GC = KV + 40 * QLD;           // [64]: gamma_16
-    static constexpr int TOTAL = GC + 64;
-};
+enum { IR = 0, IW, IK, IA, IB, IV };
+enum { MLAK = 0, MMRK, MMRB, MWI };
 
-enum { IR = 0, IW, IK, IA, IB };
+// LDS layout (floats): the operand waves' private rows, then two hand-off
+// buffers (one per chunk parity) read by the state waves.
+namespace lay {
+constexpr int IN = 0;                       // [6][16][64] r w k a b v
+constexpr int AR = IN + 6 * 16 * 64;        // [32][QLD] A'_t = a_t F_ex(t), R'_t = r_t F_in(t)
+constexpr int AWR = AR + 32 * QLD;          // [8][QLD]  A'_t W_2, R'_t W_2 for t = 12..15
+constexpr int BD = AWR + 8 * QLD;           // [16][QLD] b_s / F_s
+constexpr int KD = BD + 16 * QLD;           // [16][QLD] k_s / F_s
+constexpr int BL = KD + 16 * QLD;           // [32][QLD] b, k rows scaled to the split points
+constexpr int LAB = BL + 32 * QLD;          // [16][MLD] L_ab (upper part stays zero)
+constexpr int BUF = LAB + 16 * MLD;
+// within a hand-off buffer
+constexpr int B_Q = 0;                      // [32][QLD] A^ (rows 0..15), R^ (16..31)
+constexpr int B_BKT = B_Q + 32 * QLD;       // [64][KLD] B^ | K^ by key column j
+constexpr int B_VT = B_BKT + 64 * KLD;      // [64][VLD] V by value row i
+constexpr int B_M = B_VT + 64 * VLD;        // [4][16][MLD] L_ak, M_rk, M_rb, W
+constexpr int B_GC = B_M + 4 * 16 * MLD;    // [64] gamma_16
+constexpr int BUF_SIZE = B_GC + 64;
+constexpr int TOTAL = BUF + 2 * BUF_SIZE;
+static_assert(BUF % 4 == 0 && BUF_SIZE % 4 == 0, "16-byte aligned buffers");
+}  // namespace lay
 
-__device__ __forceinline__ int ver_off(int p) { return 2 * p * (p + 1); }
-
-// Raw chunk data in flight: 3 vectors of 8 elements per thread.
+// Raw chunk data in flight: 3 vectors of 8 elements per staging thread.
 template <typename TI> struct Raw;
 template <> struct Raw<uint16_t> { uint4 q[3]; };
 template <> struct Raw<float> { float4 q[3][2]; };
@@ -87,53 +100,71 @@ __device__ __forceinline__ void raw_unpack(const Raw<float> &r, int k, float *x)
     x[4] = r.q[k][1].x; x[5] = r.q[k][1].y; x[6] = r.q[k][1].z; x[7] = r.q[k][1].w;
 }
 
-// Rows b_s * V^(p)_s and k_s * V^(p)_s of source sub-chunk Q for every target
-// sub-chunk p >= Q: for p > Q the division-free decay prod_{s<u<4p} w_u, for
-// p = Q the reciprocal of the clamped within-sub-chunk prefix F_s.
-template <int Q>
-__device__ __forceinline__ void b_k_versions(const float *wv, const float *W, const float *s_in,
-                                             float *s_BV, float *s_KV, int j) {
-    float suf[4];
-    suf[3] = 1.f;
-    suf[2] = wv[4 * Q + 3];
-    suf[1] = wv[4 * Q + 2] * suf[2];
-    suf[0] = wv[4 * Q + 1] * suf[1];
-    float F = 1.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int s = 4 * Q + e;
-        F *= fmaxf(wv[s], 9.313225746154785e-10f);
-        const float bs = s_in[4 * 1024 + s * 64 + j];
-        const float ks = s_in[2 * 1024 + s * 64 + j];
-        const float inv = __builtin_amdgcn_rcpf(F);
-        s_BV[(2 * Q * (Q + 1) + s) * 68 + j] = bs * inv;
-        s_KV[(2 * Q * (Q + 1) + s) * 68 + j] = ks * inv;
-        float m = suf[e];
-#pragma unroll
-        for (int pp = Q + 1; pp < 4; ++pp) {
-            s_BV[(2 * pp * (pp + 1) + s) * 68 + j] = bs * m;
-            s_KV[(2 * pp * (pp + 1) + s) * 68 + j] = ks * m;
-            m *= W[pp];
-        }
-    }
-}
-
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <typename TI, int NIT>
-__global__ __launch_bounds__(kThreads, 2) void fwd_chunk_kernel(FwdArgs p, int32_t units) {
-    constexpr int RB = 16 * NIT;       // value rows per workgroup
-    constexpr int NRB = 4 / NIT;       // row blocks per unit
-    constexpr int WPI = 4 / NIT;       // waves sharing one 16-row tile (K split of D1)
-    constexpr int JPW = NIT;           // 16-column tiles of the state per wave
-    using LY = Lay<RB>;
+// Lane permutations within groups of 4 lanes (DPP quad_perm).
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float quad_bcast(float v, int k) {   // value of quad lane k
+    switch (k) {
+    case 0: return quad_perm<0x00>(v);
+    case 1: return quad_perm<0x55>(v);
+    case 2: return quad_perm<0xaa>(v);
+    default: return quad_perm<0xff>(v);
+    }
+}
+__device__ __forceinline__ float quad_sum(float v) {
+    v += quad_perm<0xb1>(v);      // lanes ^1
+    v += quad_perm<0x4e>(v);      // lanes ^2
+    return v;
+}
+
+// 16x16 product over K = 64 on MFMA: D[m][n] = sum_j A_m[j] B_n[j], where this
+// lane supplies row m = lane % 16 of A (arow) and row n = lane % 16 of B (brow).
+__device__ __forceinline__ f32x4 rows_product(const float *arow, const float *brow, int kq) {
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const float4 a = *(const float4 *)(arow + 16 * g + 4 * kq);
+        const float4 b = *(const float4 *)(brow + 16 * g + 4 * kq);
+        d = mfma4(a.x, b.x, d); d = mfma4(a.y, b.y, d);
+        d = mfma4(a.z, b.z, d); d = mfma4(a.w, b.w, d);
+    }
+    return d;
+}
+
+// S^T tile q of a state wave: acc = diag(gamma) acc + B^^T X + K^^T V over the
+// chunk's 16 tokens (x, v: this lane's B-operand values X[4kq+e][i], V[4kq+e][i]).
+__device__ __forceinline__ f32x4 d2_tile(f32x4 acc, const float *buf, int q, int l16, int kq,
+                                         const f32x4 &x, const float4 &v) {
+    const float4 g4 = *(const float4 *)(buf + lay::B_GC + 16 * q + 4 * kq);
+    acc[0] *= g4.x; acc[1] *= g4.y; acc[2] *= g4.z; acc[3] *= g4.w;
+    const float *br = buf + lay::B_BKT + (16 * q + l16) * KLD + 4 * kq;
+    const float4 b0 = *(const float4 *)br, k0 = *(const float4 *)(br + 16);
+    acc = mfma4(b0.x, x[0], acc);
+    acc = mfma4(b0.y, x[1], acc);
+    acc = mfma4(b0.z, x[2], acc);
+    acc = mfma4(b0.w, x[3], acc);
+    acc = mfma4(k0.x, v.x, acc);
+    acc = mfma4(k0.y, v.y, acc);
+    acc = mfma4(k0.z, v.z, acc);
+    acc = mfma4(k0.w, v.w, acc);
+    return acc;
+}
+
+template <typename TI, int NMW>
+__global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdArgs p, int32_t units) {
+    constexpr int RB = 16 * NMW;       // value rows per workgroup
+    constexpr int NRB = 4 / NMW;       // row blocks per unit
     extern __shared__ __align__(16) float sm[];
 
     // Workgroup -> (unit, row block). Row blocks of one unit go to the same
     // XCD (workgroups are dealt to the 8 XCDs round robin) so that their
-    // shared reads of r, w, k, a, b hit one L2.
+    // shared reads of the inputs hit one L2.
     int unit, rb;
     if (NRB == 1) {
         unit = blockIdx.x;
@@ -151,330 +182,414 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_chunk_kernel(FwdArgs p, int32
     const int i0 = rb * RB;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int l16 = lane & 15, kq = lane >> 4;
-    const int it = wave % NIT, jg = wave / NIT;
-    const int irow = 16 * it + l16;                      // local value row of this lane
-
     const int64_t ts = (int64_t)H * kN;
     const int64_t base = (u.start * H + h) * kN;
     const int64_t sbase = ((int64_t)sq * H + h) * (kN * kN);
+    const int nch = (u.len + kChunk - 1) / kChunk;
 
-    // State tiles: acc[q][r] = S[i0 + irow][16*jt + 4*kq + r], jt = jg*JPW + q.
-    f32x4 acc[JPW];
+    if (wave < NMW) {
+        // ================= state waves =================
+        const int irow = i0 + 16 * wave + l16;           // value row of this lane
+        f32x4 acc[4];
 #pragma unroll
-    for (int q = 0; q < JPW; ++q) {
-        const int jt = jg * JPW + q;
-        if (p.s0) {
-            const float4 v4 = *(const float4 *)(p.s0 + sbase + (int64_t)(i0 + irow) * kN + 16 * jt + 4 * kq);
-            acc[q] = f32x4{v4.x, v4.y, v4.z, v4.w};
-        } else {
-            acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 4; ++q) {
+            if (p.s0) {
+                const float4 v4 = *(const float4 *)(p.s0 + sbase + (int64_t)irow * kN + 16 * q + 4 * kq);
+                acc[q] = f32x4{v4.x, v4.y, v4.z, v4.w};
+            } else {
+                acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
+#pragma unroll 1
+        for (int c = 0; c <= nch; ++c) {
+            const int cm = c - 1;                        // chunk advanced in this iteration
+            const float *buf = sm + lay::BUF + (cm & 1) * lay::BUF_SIZE;
+            f32x4 d1a = {0.f, 0.f, 0.f, 0.f}, d1r = d1a;
+            lds_barrier();
+            // ---- part 1: checkpoint, D1 = [A^;R^] S_0^T for this wave's rows
+            if (cm >= 0) {
+                if (p.ckpt) {
+                    float *cp = p.ckpt + ((u.ckpt + cm) * H + h) * (int64_t)(kN * kN) + (int64_t)irow * kN;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *(float4 *)(cp + 16 * q + 4 * kq) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 a4 = *(const float4 *)(buf + lay::B_Q + l16 * QLD + 16 * q + 4 * kq);
+                    const float4 r4 = *(const float4 *)(buf + lay::B_Q + (16 + l16) * QLD + 16 * q + 4 * kq);
+                    d1a = mfma4(a4.x, acc[q][0], d1a);
+                    d1r = mfma4(r4.x, acc[q][0], d1r);
+                    d1a = mfma4(a4.y, acc[q][1], d1a);
+                    d1r = mfma4(r4.y, acc[q][1], d1r);
+                    d1a = mfma4(a4.z, acc[q][2], d1a);
+                    d1r = mfma4(r4.z, acc[q][2], d1r);
+                    d1a = mfma4(a4.w, acc[q][3], d1a);
+                    d1r = mfma4(r4.w, acc[q][3], d1r);
+                }
+            }
+            lds_barrier();
+            // ---- part 2: rhs = P_a + L_ak V; X = W rhs; Y = P_r + M_rk V + M_rb X;
+            //      y out; D2 on state tiles 0, 1
+            f32x4 xx = {0.f, 0.f, 0.f, 0.f};
+            float4 vb = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (cm >= 0) {
+                vb = *(const float4 *)(buf + lay::B_VT + irow * VLD + 4 * kq);
+                const float *mrow = buf + lay::B_M + l16 * MLD + 4 * kq;
+                const float4 lak = *(const float4 *)(mrow + MLAK * 16 * MLD);
+                const float4 mrk = *(const float4 *)(mrow + MMRK * 16 * MLD);
+                const float4 mrb = *(const float4 *)(mrow + MMRB * 16 * MLD);
+                const float4 wi = *(const float4 *)(mrow + MWI * 16 * MLD);
+                d1a = mfma4(lak.x, vb.x, d1a); d1a = mfma4(lak.y, vb.y, d1a);
+                d1a = mfma4(lak.z, vb.z, d1a); d1a = mfma4(lak.w, vb.w, d1a);
+                d1r = mfma4(mrk.x, vb.x, d1r); d1r = mfma4(mrk.y, vb.y, d1r);
+                d1r = mfma4(mrk.z, vb.z, d1r); d1r = mfma4(mrk.w, vb.w, d1r);
+                xx = mfma4(wi.x, d1a[0], xx); xx = mfma4(wi.y, d1a[1], xx);
+                xx = mfma4(wi.z, d1a[2], xx); xx = mfma4(wi.w, d1a[3], xx);
+                d1r = mfma4(mrb.x, xx[0], d1r); d1r = mfma4(mrb.y, xx[1], d1r);
+                d1r = mfma4(mrb.z, xx[2], d1r); d1r = mfma4(mrb.w, xx[3], d1r);
+                acc[0] = d2_tile(acc[0], buf, 0, l16, kq, xx, vb);
+                acc[1] = d2_tile(acc[1], buf, 1, l16, kq, xx, vb);
+                const int t0 = cm * kChunk;
+                const int L = min(kChunk, u.len - t0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * kq + r;
+                    if (t < L) IO<TI>::st((TI *)p.y, base + (int64_t)(t0 + t) * ts + irow, d1r[r]);
+                }
+            }
+            lds_barrier();
+            // ---- part 3: D2 on state tiles 2, 3
+            if (cm >= 0) {
+                acc[2] = d2_tile(acc[2], buf, 2, l16, kq, xx, vb);
+                acc[3] = d2_tile(acc[3], buf, 3, l16, kq, xx, vb);
+            }
+        }
+        if (p.s_out) {
+            float *op = p.s_out + sbase + (int64_t)irow * kN;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *(float4 *)(op + 16 * q + 4 * kq) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+        }
+        return;
     }
 
-    float *s_in = sm + LY::IN;
-    float *s_P = sm + LY::P;
-    float *s_L = sm + LY::LM;
-    float *s_Q = sm + LY::Q;
-    float *s_BKt = sm + LY::BKT;
-    float *s_XVt = sm + LY::XVT;
-    float *s_AR = sm + LY::AR;
-    float *s_BV = sm + LY::BV;
-    float *s_KV = sm + LY::KV;
-    float *s_gC = sm + LY::GC;
+    // ================= operand waves =================
+    const int pw = wave - NMW;                 // 0..7, uniform
+    const int ptid = tid - 64 * NMW;           // 0..511
+    const int sid = ptid - 256;                // staging thread index (operand waves 4..7)
+    float *s_in = sm + lay::IN;
+    float *s_AR = sm + lay::AR;
+    float *s_AWR = sm + lay::AWR;
+    float *s_BD = sm + lay::BD;
+    float *s_KD = sm + lay::KD;
+    float *s_BL = sm + lay::BL;
+    float *s_Lab = sm + lay::LAB;
 
-    const int nch = (u.len + kChunk - 1) / kChunk;
+    // Staging (operand waves 4-7): element group g = sid + 256k (k = 0..2) of
+    // 6 streams x 16 tokens x 8 groups of 8 elements; stream g >> 7 is uniform
+    // per wave. Loads are issued one chunk ahead, unconditionally (chunk index
+    // and token rows clamped into the sequence), so that the registers in
+    // flight have exactly one definition per iteration.
     Raw<TI> raw;
-    // Thread tid stages element group q = tid + 256k: stream 2k + (tid >> 7)
-    // (uniform per wave), token (q >> 3) & 15, elements 8*(q & 7) .. +7.
-    const int half = __builtin_amdgcn_readfirstlane(tid >> 7);
-    const TI *sp0 = (const TI *)(half ? p.w : p.r);
-    const TI *sp1 = (const TI *)(half ? p.a : p.k);
-    const TI *sp2 = (const TI *)(half ? p.v : p.b);
-    auto issue = [&](int cc) {
+    const TI *sp[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int st = __builtin_amdgcn_readfirstlane((sid + 256 * k) >> 7);
+        const void *vp = st == IR ? p.r : st == IW ? p.w : st == IK ? p.k
+                       : st == IA ? p.a : st == IB ? p.b : p.v;
+        sp[k] = (const TI *)vp + base;
+    }
+    auto issue = [&](int cc) {               // 0 <= cc < nch
         const int Lc = min(kChunk, u.len - cc * kChunk);
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-            const int q = tid + k * kThreads;
-            const int t = (q >> 3) & 15, e0 = (q & 7) * 8;
-            const TI *sp = k == 0 ? sp0 : k == 1 ? sp1 : sp2;
-            if (t < Lc) raw_load(sp + base + (int64_t)(cc * kChunk + t) * ts + e0, raw, k);
+            const int g = sid + 256 * k;
+            const int t = min((g >> 3) & 15, Lc - 1), e0 = (g & 7) * 8;
+            raw_load(sp[k] + (int64_t)(cc * kChunk + t) * ts + e0, raw, k);
         }
     };
-    if (nch > 0) issue(0);
-#pragma unroll 1
-    for (int c = 0; c < nch; ++c) {
-        const int t0 = c * kChunk;
-        const int L = min(kChunk, u.len - t0);
-        __syncthreads();
-
-        // ---- stage chunk c from registers (identity tokens w=1, rest 0, past the end),
-        //      then start the loads of chunk c+1
+    auto stage = [&](int cc) {
+        const int Lc = min(kChunk, u.len - cc * kChunk);
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-            const int q = tid + k * kThreads;
-            const int st = q >> 7, t = (q >> 3) & 15, e0 = (q & 7) * 8;
+            const int g = sid + 256 * k;
+            const int st = g >> 7, t = (g >> 3) & 15, e0 = (g & 7) * 8;
             float x[8];
-            if (t < L) {
+            if (t < Lc) {
                 raw_unpack(raw, k, x);
-            } else {
+            } else {                           // identity tokens past the end
                 const float f = st == IW ? 1.f : 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = f;
             }
-            if (st < 5) {
-                float *d = s_in + (st * 16 + t) * 64 + e0;
-                *(float4 *)d = make_float4(x[0], x[1], x[2], x[3]);
-                *(float4 *)(d + 4) = make_float4(x[4], x[5], x[6], x[7]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int row = e0 + e - i0;
-                    if (row >= 0 && row < RB) s_XVt[row * KLD + 16 + t] = x[e];
-                }
-            }
+            float *d = s_in + (st * 16 + t) * 64 + e0;
+            *(float4 *)d = make_float4(x[0], x[1], x[2], x[3]);
+            *(float4 *)(d + 4) = make_float4(x[4], x[5], x[6], x[7]);
         }
-        if (c + 1 < nch) issue(c + 1);
-        if (p.ckpt) {
-            float *cp = p.ckpt + ((u.ckpt + c) * H + h) * (int64_t)(kN * kN) + (int64_t)(i0 + irow) * kN;
-#pragma unroll
-            for (int q = 0; q < JPW; ++q) {
-                const int jt = jg * JPW + q;
-                *(float4 *)(cp + 16 * jt + 4 * kq) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
-            }
-        }
-        __syncthreads();
+    };
 
-        // ---- decays and operand rows (4 threads per key column j)
-        {
-            const int role = tid >> 6, j = tid & 63;
-            const float *w_ = s_in + IW * 1024 + j;
-            if (role == 0) {            // A^, R^ and gamma_16
-                float g = 1.f;
+    // ---- phase A: per-column decay rows, one role per operand wave, lane = key column j
+    auto phase_a = [&](float *buf) {
+        const int j = lane;
+        const float *w_ = s_in + IW * 1024 + j;
+        if (pw == 0) {             // A^_t = a_t gamma_{t-1}; gamma_16
+            float g = 1.f;
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    s_Q[t * QLD + j] = s_in[IA * 1024 + t * 64 + j] * g;
-                    g *= w_[t * 64];
-                    s_Q[(16 + t) * QLD + j] = s_in[IR * 1024 + t * 64 + j] * g;
+            for (int t = 0; t < 16; ++t) {
+                buf[lay::B_Q + t * QLD + j] = s_in[IA * 1024 + t * 64 + j] * g;
+                g *= w_[t * 64];
+            }
+            buf[lay::B_GC + j] = g;
+        } else if (pw == 1) {      // R^_t = r_t gamma_t
+            float g = 1.f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                g *= w_[t * 64];
+                buf[lay::B_Q + (16 + t) * QLD + j] = s_in[IR * 1024 + t * 64 + j] * g;
+            }
+        } else if (pw == 2 || pw == 3) {   // B^ (2) or K^ (3), by column; V by row (2)
+            const int st = pw == 2 ? IB : IK;
+            float d = 1.f, x[16];
+#pragma unroll
+            for (int s = 15; s >= 0; --s) {
+                x[s] = s_in[st * 1024 + s * 64 + j] * d;
+                d *= w_[s * 64];
+            }
+            float *dst = buf + lay::B_BKT + j * KLD + (pw - 2) * 16;
+#pragma unroll
+            for (int s = 0; s < 16; s += 4) *(float4 *)(dst + s) = make_float4(x[s], x[s + 1], x[s + 2], x[s + 3]);
+            if (pw == 2) {
+#pragma unroll
+                for (int t = 0; t < 16; t += 4) {
+                    const float *vc = s_in + IV * 1024 + t * 64 + j;
+                    *(float4 *)(buf + lay::B_VT + j * VLD + t) = make_float4(vc[0], vc[64], vc[128], vc[192]);
                 }
-                s_gC[j] = g;
-            } else if (role == 1) {     // B^, K^ (transposed for the MFMA A operand)
-                float d = 1.f;
+            }
+        } else if (pw == 4 || pw == 5) {   // A' = a F_ex (4) or R' = r F_in (5); times W_2 for t >= 12
+            const int st = pw == 4 ? IA : IR;
+            const int inc = pw - 4;
+            float W2 = 1.f;
 #pragma unroll
-                for (int s = 15; s >= 0; --s) {
-                    s_BKt[j * KLD + s] = s_in[IB * 1024 + s * 64 + j] * d;
-                    s_BKt[j * KLD + 16 + s] = s_in[IK * 1024 + s * 64 + j] * d;
-                    d *= w_[s * 64];
+            for (int t = 8; t < 12; ++t) W2 *= w_[t * 64];
+#pragma unroll
+            for (int sc = 0; sc < 4; ++sc) {
+                float f = 1.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 4 * sc + e;
+                    const float wc = fmaxf(w_[t * 64], kMinFactor);
+                    if (inc) f *= wc;
+                    const float x = s_in[st * 1024 + t * 64 + j] * f;
+                    s_AR[(16 * inc + t) * QLD + j] = x;
+                    if (sc == 3) s_AWR[(4 * inc + e) * QLD + j] = x * W2;
+                    if (!inc) f *= wc;
                 }
-            } else {
-                // roles 2 and 3: b, k versions per target sub-chunk (role 3: source
-                // sub-chunks 0 and 1; role 2: 2 and 3, plus the prefix rows
-                // A' = a F_{t-1}, R' = r F_t)
-                float wv[16], W[4];
+            }
+        } else {                   // b (6) or k (7) rows: x_s / F_s, and scaled to the split points
+            const int st = pw == 6 ? IB : IK;
+            const int ko = pw - 6;             // row offset of the k rows in BL
+            float wv[16];
 #pragma unroll
-                for (int t = 0; t < 16; ++t) wv[t] = w_[t * 64];
+            for (int t = 0; t < 16; ++t) wv[t] = w_[t * 64];
+            const float W1 = (wv[4] * wv[5]) * (wv[6] * wv[7]);
+            float *dd = pw == 6 ? s_BD : s_KD;
 #pragma unroll
-                for (int sc = 0; sc < 4; ++sc)
-                    W[sc] = (wv[4 * sc] * wv[4 * sc + 1]) * (wv[4 * sc + 2] * wv[4 * sc + 3]);
-                if (role == 2) {
+            for (int q = 0; q < 4; ++q) {
+                float F = 1.f;
+                float suf = 1.f;                 // prod_{s<u<4q+4} w_u, built downwards
+                float xs[4];
 #pragma unroll
-                    for (int sc = 0; sc < 4; ++sc) {
-                        float f = 1.f;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int t = 4 * sc + e;
-                            s_AR[t * QLD + j] = s_in[IA * 1024 + t * 64 + j] * f;
-                            f *= fmaxf(wv[t], kMinFactor);
-                            s_AR[(16 + t) * QLD + j] = s_in[IR * 1024 + t * 64 + j] * f;
+                for (int e = 3; e >= 0; --e) {
+                    const int s = 4 * q + e;
+                    xs[e] = s_in[st * 1024 + s * 64 + j];
+                    if (q < 3) {
+                        const float bs = xs[e] * suf;
+                        if (q == 0) {
+                            s_BL[(8 * ko + s) * QLD + j] = bs * W1;     // scaled to 8
+                            s_BL[(16 + 4 * ko + s) * QLD + j] = bs;     // scaled to 4
+                        } else if (q == 1) {
+                            s_BL[(8 * ko + s) * QLD + j] = bs;          // scaled to 8
+                        } else {
+                            s_BL[(16 + 4 * ko + s) * QLD + j] = bs;     // scaled to 12
                         }
                     }
+                    suf *= wv[s];
                 }
-                if (role == 3) {
-                    b_k_versions<0>(wv, W, s_in, s_BV, s_KV, j);
-                    b_k_versions<1>(wv, W, s_in, s_BV, s_KV, j);
-                } else {
-                    b_k_versions<2>(wv, W, s_in, s_BV, s_KV, j);
-                    b_k_versions<3>(wv, W, s_in, s_BV, s_KV, j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = 4 * q + e;
+                    F *= fmaxf(wv[s], kMinFactor);
+                    dd[s * QLD + j] = xs[e] * __builtin_amdgcn_rcpf(F);
                 }
             }
         }
-        __syncthreads();
+    };
 
-        // ---- D1 on MFMA: P[t'][i] = sum_j Q[t'][j] S_0[i][j] over this wave's
-        //      column tiles (a K split when several waves share one row tile)
-        f32x4 d1[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            d1[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int q = 0; q < JPW; ++q) {
-                const int jt = jg * JPW + q;
-                const float4 a4 = *(const float4 *)(s_Q + (16 * tt + l16) * QLD + 16 * jt + 4 * kq);
-                d1[tt] = mfma4(a4.x, acc[q][0], d1[tt]);
-                d1[tt] = mfma4(a4.y, acc[q][1], d1[tt]);
-                d1[tt] = mfma4(a4.z, acc[q][2], d1[tt]);
-                d1[tt] = mfma4(a4.w, acc[q][3], d1[tt]);
-            }
-            if (WPI > 1) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    s_P[(jg * 32 + 16 * tt + 4 * kq + r) * RB + irow] = d1[tt][r];
-            }
-        }
-
-        // ---- 16x16 matrices on VALU: 120 L items and 136 M items, one per thread
-        {
-            int t, s, mat;
-            if (tid < 120) {
-                t = 1;
-                while ((t + 1) * t / 2 <= tid) ++t;
-                s = tid - t * (t - 1) / 2;
-                mat = 0;
+    // ---- phase B: the 16x16 matrices. Waves 0, 1: the cross-sub-chunk
+    //      blocks on MFMA; waves 2-5: the within-sub-chunk pairs on VALU
+    auto phase_b = [&](float *buf) {
+        if (pw < 2) {
+            // wave 0: split at 8: rows m < 8 are a rows t = 8+m, m >= 8 r rows t = m;
+            //         columns n < 8 are b rows s = n, n >= 8 k rows s = n-8.
+            // wave 1: splits at 4 and 12: m < 8 covers t in 4..7, m >= 8 t in 12..15
+            //         (a rows where m & 4 == 0); n likewise for s in 0..3 and 8..11.
+            const int m = l16;
+            const float *arow, *brow;
+            if (pw == 0) {
+                arow = m < 4 ? s_AR + (8 + m) * QLD : m < 8 ? s_AWR + (m - 4) * QLD
+                     : m < 12 ? s_AR + (16 + m) * QLD : s_AWR + (m - 8) * QLD;
+                brow = s_BL + l16 * QLD;
             } else {
-                const int mi = tid - 120;
-                t = 0;
-                while ((t + 1) * (t + 2) / 2 <= mi) ++t;
-                s = mi - t * (t + 1) / 2;
-                mat = 1;
+                arow = s_AR + ((m & 4) ? 16 + m : 4 + m) * QLD;
+                brow = s_BL + (16 + l16) * QLD;
             }
-            const int vrow = ver_off(t >> 2) + s;
-            const float *ar = s_AR + (16 * mat + t) * QLD;
-            const float *bv = s_BV + vrow * QLD;
-            const float *kv = s_KV + vrow * QLD;
-            float db0 = 0.f, db1 = 0.f, dk0 = 0.f, dk1 = 0.f;
+            const f32x4 d = rows_product(arow, brow, kq);
+            const int n = l16;
 #pragma unroll
-            for (int j = 0; j < 64; j += 8) {
-                const float4 x0 = *(const float4 *)(ar + j), x1 = *(const float4 *)(ar + j + 4);
-                const float4 b0 = *(const float4 *)(bv + j), b1 = *(const float4 *)(bv + j + 4);
-                const float4 k0 = *(const float4 *)(kv + j), k1 = *(const float4 *)(kv + j + 4);
-                db0 = fmaf(x0.x, b0.x, db0); db1 = fmaf(x0.y, b0.y, db1);
-                db0 = fmaf(x0.z, b0.z, db0); db1 = fmaf(x0.w, b0.w, db1);
-                db0 = fmaf(x1.x, b1.x, db0); db1 = fmaf(x1.y, b1.y, db1);
-                db0 = fmaf(x1.z, b1.z, db0); db1 = fmaf(x1.w, b1.w, db1);
-                dk0 = fmaf(x0.x, k0.x, dk0); dk1 = fmaf(x0.y, k0.y, dk1);
-                dk0 = fmaf(x0.z, k0.z, dk0); dk1 = fmaf(x0.w, k0.w, dk1);
-                dk0 = fmaf(x1.x, k1.x, dk0); dk1 = fmaf(x1.y, k1.y, dk1);
-                dk0 = fmaf(x1.z, k1.z, dk0); dk1 = fmaf(x1.w, k1.w, dk1);
+            for (int r = 0; r < 4; ++r) {
+                const int mm = 4 * kq + r;
+                bool isA, isB, valid = true;
+                int t, s;
+                if (pw == 0) {
+                    isA = mm < 8; t = isA ? 8 + mm : mm;
+                    isB = n < 8;  s = isB ? n : n - 8;
+                } else {
+                    isA = (mm & 4) == 0; t = isA ? 4 + mm : mm;
+                    isB = (n & 4) == 0;  s = isB ? n : n - 4;
+                    valid = (mm < 8) == (n < 8);
+                }
+                float *dst = isA ? (isB ? s_Lab : buf + lay::B_M + MLAK * 16 * MLD)
+                                 : buf + lay::B_M + (isB ? MMRB : MMRK) * 16 * MLD;
+                if (valid) dst[t * MLD + s] = d[r];
             }
-            // row-major 16x16: [0] L_ab, [1] L_ak, [2] M_rb, [3] M_rk (upper parts zero)
-            s_L[(2 * mat) * 256 + t * 16 + s] = db0 + db1;
-            s_L[(2 * mat + 1) * 256 + t * 16 + s] = dk0 + dk1;
-        }
-        __syncthreads();
-        float *s_Lab = s_L, *s_Lak = s_L + 256, *s_Mrb = s_L + 512, *s_Mrk = s_L + 768;
-        float *s_Wi = s_L + 1024;                 // (I - L_ab)^-1, row-major
-        float *s_Y = s_L + 1280;                  // [16][RB] output tile
-
-        // ---- (I - L_ab)^-1 by column-oriented substitution (16 threads); the
-        //      strictly upper parts of the four matrices are cleared meanwhile
-        if (tid < 16) {
-            float x[16];
-#pragma unroll
-            for (int t = 0; t < 16; ++t) x[t] = t == tid ? 1.f : 0.f;
-#pragma unroll
-            for (int s2 = 0; s2 < 15; ++s2) {
-#pragma unroll
-                for (int t = s2 + 1; t < 16; ++t) x[t] = fmaf(s_Lab[t * 16 + s2], x[s2], x[t]);
+        } else if (pw < 6) {
+            // 64 items (sub-chunk p, pair k) x 4 quarters of the 64 columns
+            const int dt = ptid - 128;
+            const int item = dt >> 2, qtr = dt & 3;
+            const int sc = item >> 4, k = item & 15;
+            int et, es;
+            const bool isL = k < 6;
+            if (isL) {                 // s < t
+                et = 1 + (k >= 1) + (k >= 3);
+                es = k - et * (et - 1) / 2;
+            } else {                   // s <= t
+                const int mi = k - 6;
+                et = (mi >= 1) + (mi >= 3) + (mi >= 6);
+                es = mi - et * (et + 1) / 2;
             }
+            const int t = 4 * sc + et, s = 4 * sc + es;
+            const float *ar = s_AR + ((isL ? 0 : 16) + t) * QLD + 16 * qtr;
+            const float *bd = s_BD + s * QLD + 16 * qtr;
+            const float *kd = s_KD + s * QLD + 16 * qtr;
+            float db = 0.f, dk = 0.f;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) s_Wi[t * 16 + tid] = x[t];
-        } else if (tid >= 64 && tid < 64 + 4 * 16) {
-            const int m = (tid - 64) >> 4, row = tid & 15;
-            const int first = (m == 0 || m == 1) ? row : row + 1;   // L: s >= t, M: s > t
-            for (int c2 = first; c2 < 16; ++c2) s_L[m * 256 + row * 16 + c2] = 0.f;
-        }
-        if (WPI > 1) {
-            for (int q = tid; q < 32 * RB; q += kThreads) {
-                float acc0 = s_P[q];
-#pragma unroll
-                for (int g = 1; g < WPI; ++g) acc0 += s_P[g * 32 * RB + q];
-                s_P[q] = acc0;
+            for (int jj = 0; jj < 16; jj += 4) {
+                const float4 x = *(const float4 *)(ar + jj);
+                const float4 b = *(const float4 *)(bd + jj);
+                const float4 kk = *(const float4 *)(kd + jj);
+                db = fmaf(x.x, b.x, db); dk = fmaf(x.x, kk.x, dk);
+                db = fmaf(x.y, b.y, db); dk = fmaf(x.y, kk.y, dk);
+                db = fmaf(x.z, b.z, db); dk = fmaf(x.z, kk.z, dk);
+                db = fmaf(x.w, b.w, db); dk = fmaf(x.w, kk.w, dk);
             }
-        }
-        __syncthreads();
-
-        // ---- per 16-row tile (one owner wave): rhs = P_a + L_ak V; X = W rhs;
-        //      Y = P_r + M_rk V + M_rb X, all on MFMA; the 16x16 output layout
-        //      is the B-operand layout of the next product
-        if (jg == 0) {
-            f32x4 pa = d1[0], pr = d1[1];
-            if (WPI > 1) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    pa[r] = s_P[(4 * kq + r) * RB + irow];
-                    pr[r] = s_P[(16 + 4 * kq + r) * RB + irow];
+            db = quad_sum(db);
+            dk = quad_sum(dk);
+            if (qtr == 0) {
+                float *mb = buf + lay::B_M + t * MLD + s;
+                if (isL) {
+                    s_Lab[t * MLD + s] = db;
+                    mb[MLAK * 16 * MLD] = dk;
+                } else {
+                    mb[MMRB * 16 * MLD] = db;
+                    mb[MMRK * 16 * MLD] = dk;
                 }
             }
-            const float4 v4 = *(const float4 *)(s_XVt + irow * KLD + 16 + 4 * kq);
-            const float vb[4] = {v4.x, v4.y, v4.z, v4.w};
-            const float4 lak = *(const float4 *)(s_Lak + l16 * 16 + 4 * kq);
-            const float4 mrk = *(const float4 *)(s_Mrk + l16 * 16 + 4 * kq);
-            const float4 wi = *(const float4 *)(s_Wi + l16 * 16 + 4 * kq);
-            const float4 mrb = *(const float4 *)(s_Mrb + l16 * 16 + 4 * kq);
-            pa = mfma4(lak.x, vb[0], pa); pa = mfma4(lak.y, vb[1], pa);
-            pa = mfma4(lak.z, vb[2], pa); pa = mfma4(lak.w, vb[3], pa);
-            pr = mfma4(mrk.x, vb[0], pr); pr = mfma4(mrk.y, vb[1], pr);
-            pr = mfma4(mrk.z, vb[2], pr); pr = mfma4(mrk.w, vb[3], pr);
-            f32x4 xx = {0.f, 0.f, 0.f, 0.f};
-            xx = mfma4(wi.x, pa[0], xx); xx = mfma4(wi.y, pa[1], xx);
-            xx = mfma4(wi.z, pa[2], xx); xx = mfma4(wi.w, pa[3], xx);
-            pr = mfma4(mrb.x, xx[0], pr); pr = mfma4(mrb.y, xx[1], pr);
-            pr = mfma4(mrb.z, xx[2], pr); pr = mfma4(mrb.w, xx[3], pr);
-            *(float4 *)(s_XVt + irow * KLD + 4 * kq) = make_float4(xx[0], xx[1], xx[2], xx[3]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s_Y[(4 * kq + r) * RB + irow] = pr[r];
         }
-        __syncthreads();
+    };
 
-        // ---- store y for the real tokens (consecutive threads, consecutive channels)
-        for (int q = tid; q < L * RB; q += kThreads) {
-            const int t = q / RB, il = q - t * RB;
-            IO<TI>::st((TI *)p.y, base + (int64_t)(t0 + t) * ts + i0 + il, s_Y[q]);
-        }
-
-        // ---- D2 on MFMA: S^T[j][i] = gamma[j] S_0^T[j][i] + sum_k BK[k][j] XV[k][i]
-        {
-            const float *xr = s_XVt + irow * KLD + 4 * kq;
-            const float4 xa = *(const float4 *)xr, va = *(const float4 *)(xr + 16);
+    // ---- W = (I - L_ab)^-1 (one wave: column c = lane / 4, rows t = lane % 4 + 4i
+    //      held by the 4 lanes of a quad, forward substitution over s)
+    auto solve_w = [&](float *buf) {
+        const int col = lane >> 2, q = lane & 3;
+        float Lr[4][16], x[4];
 #pragma unroll
-            for (int q = 0; q < JPW; ++q) {
-                const int jt = jg * JPW + q;
-                const float4 g4 = *(const float4 *)(s_gC + 16 * jt + 4 * kq);
-                acc[q][0] *= g4.x; acc[q][1] *= g4.y; acc[q][2] *= g4.z; acc[q][3] *= g4.w;
-                const float *br = s_BKt + (16 * jt + l16) * KLD + 4 * kq;
-                const float4 b0 = *(const float4 *)br, k0 = *(const float4 *)(br + 16);
-                acc[q] = mfma4(b0.x, xa.x, acc[q]);
-                acc[q] = mfma4(b0.y, xa.y, acc[q]);
-                acc[q] = mfma4(b0.z, xa.z, acc[q]);
-                acc[q] = mfma4(b0.w, xa.w, acc[q]);
-                acc[q] = mfma4(k0.x, va.x, acc[q]);
-                acc[q] = mfma4(k0.y, va.y, acc[q]);
-                acc[q] = mfma4(k0.z, va.z, acc[q]);
-                acc[q] = mfma4(k0.w, va.w, acc[q]);
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int s = 0; s < 16; s += 4) {
+                const float4 v = *(const float4 *)(s_Lab + (q + 4 * i) * MLD + s);
+                Lr[i][s] = v.x; Lr[i][s + 1] = v.y; Lr[i][s + 2] = v.z; Lr[i][s + 3] = v.w;
+            }
+            x[i] = q + 4 * i == col ? 1.f : 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < 15; ++s) {
+            const float xs = quad_bcast(x[s >> 2], s & 3);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float nx = fmaf(Lr[i][s], xs, x[i]);
+                x[i] = q + 4 * i > s ? nx : x[i];
             }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) buf[lay::B_M + MWI * 16 * MLD + (q + 4 * i) * MLD + col] = x[i];
+    };
+
+    // Entries of L_ab and of the hand-off matrices that are never written
+    // (upper parts) stay zero.
+    for (int q = ptid; q < 16 * MLD + 2 * lay::BUF_SIZE; q += 64 * kPrepWaves) sm[lay::LAB + q] = 0.f;
+    if (nch == 0) {            // nothing to build; match the state waves' three barriers
+        lds_barrier();
+        lds_barrier();
+        lds_barrier();
+        return;
     }
 
-    if (p.s_out) {
-        float *op = p.s_out + sbase + (int64_t)(i0 + irow) * kN;
-#pragma unroll
-        for (int q = 0; q < JPW; ++q) {
-            const int jt = jg * JPW + q;
-            *(float4 *)(op + 16 * jt + 4 * kq) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+    if (pw >= 4) {
+        issue(0);
+        stage(0);
+        issue(min(1, nch - 1));
+#pragma unroll 1
+        for (int c = 0; c <= nch; ++c) {
+            float *buf = sm + lay::BUF + (c & 1) * lay::BUF_SIZE;
+            const bool live = c < nch;
+            lds_barrier();
+            if (live) phase_a(buf);
+            lds_barrier();
+            if (live) phase_b(buf);
+            lds_barrier();
+            // phase C: stage chunk c+1, start loading chunk c+2
+            if (c + 1 < nch) stage(c + 1);
+            issue(min(c + 2, nch - 1));
+        }
+    } else {
+#pragma unroll 1
+        for (int c = 0; c <= nch; ++c) {
+            float *buf = sm + lay::BUF + (c & 1) * lay::BUF_SIZE;
+            const bool live = c < nch;
+            lds_barrier();
+            if (live) phase_a(buf);
+            lds_barrier();
+            if (live) phase_b(buf);
+            lds_barrier();
+            // phase C: W for chunk c
+            if (live && pw == 0) solve_w(buf);
         }
     }
 }
 
-template <typename TI, int NIT>
-hipError_t launch_chunk(const FwdArgs &a, int32_t units, hipStream_t stream) {
-    constexpr int NRB = 4 / NIT;
-    const size_t lds = (size_t)Lay<16 * NIT>::TOTAL * sizeof(float);
-    auto fn = fwd_chunk_kernel<TI, NIT>;
+template <typename TI, int NMW>
+hipError_t launch_ws(const FwdArgs &a, int32_t units, hipStream_t stream) {
+    constexpr int NRB = 4 / NMW;
+    const size_t lds = (size_t)lay::TOTAL * sizeof(float);
+    auto fn = fwd_ws_kernel<TI, NMW>;
     hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t blocks = NRB == 1 ? units : ((int64_t)units + 7) / 8 * 8 * NRB;
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), lds, stream, a, units);
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * (NMW + kPrepWaves)), lds, stream, a, units);
     return hipGetLastError();
 }
 
@@ -482,11 +597,11 @@ template <typename TI>
 hipError_t launch_typed(const FwdArgs &a, hipStream_t stream) {
     const int S = a.seg.num_seqs > 0 ? a.seg.num_seqs : a.seg.B;
     const int32_t units = S * a.seg.H;
-    // Split value rows across workgroups when there are too few units to
-    // give every CU two workgroups.
-    if (units >= 512) return launch_chunk<TI, 4>(a, units, stream);
-    if (units >= 256) return launch_chunk<TI, 2>(a, units, stream);
-    return launch_chunk<TI, 1>(a, units, stream);
+    // One workgroup per CU (LDS); split value rows across workgroups when
+    // there are fewer units than CUs.
+    if (units >= 256) return launch_ws<TI, 4>(a, units, stream);
+    if (units >= 128) return launch_ws<TI, 2>(a, units, stream);
+    return launch_ws<TI, 1>(a, units, stream);
 }
 
 }  // namespace

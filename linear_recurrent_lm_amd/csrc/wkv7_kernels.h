@@ -27,6 +27,7 @@ struct BwdArgs {
     const float *ds_out;
     void *dr, *dw, *dk, *dv, *da, *db;
     float *ds0;
+    const void *staged[8];           // filled by the launcher: r w k a b v dy, null
 };
 
 struct DecArgs {
