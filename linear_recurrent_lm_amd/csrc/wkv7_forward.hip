@@ -37,7 +37,8 @@
 // next product). The operand waves stage inputs and build everything that does
 // not depend on the state (decay rows, the 16x16 matrices, W) for chunk c
 // while the state waves advance through chunk c-1; the two sides meet through
-// a double-buffered LDS hand-off, three workgroup barriers per chunk.
+// a double-buffered LDS hand-off, two workgroup barriers per chunk (W of a
+// chunk is solved one phase later, while the state waves run its D1).
 #include "wkv7_kernels.h"
 
 namespace wkv7 {
@@ -56,8 +57,9 @@ enum { MLAK = 0, MMRK, MMRB, MWI };
 // LDS layout (floats): the operand waves' private rows, then two hand-off
 // buffers (one per chunk parity) read by the state waves.
 namespace lay {
-constexpr int IN = 0;                       // [6][16][64] r w k a b v
-constexpr int AR = IN + 6 * 16 * 64;        // [32][QLD] A'_t = a_t F_ex(t), R'_t = r_t F_in(t)
+constexpr int IN = 0;                       // [2][6][16][64] r w k a b v, by chunk parity
+constexpr int IN_SIZE = 6 * 16 * 64;
+constexpr int AR = IN + 2 * IN_SIZE;        // [32][QLD] A'_t = a_t F_ex(t), R'_t = r_t F_in(t)
 constexpr int AWR = AR + 32 * QLD;          // [8][QLD]  A'_t W_2, R'_t W_2 for t = 12..15
 constexpr int BD = AWR + 8 * QLD;           // [16][QLD] b_s / F_s
 constexpr int KD = BD + 16 * QLD;           // [16][QLD] k_s / F_s
@@ -75,10 +77,10 @@ constexpr int TOTAL = BUF + 2 * BUF_SIZE;
 static_assert(BUF % 4 == 0 && BUF_SIZE % 4 == 0, "16-byte aligned buffers");
 }  // namespace lay
 
-// Raw chunk data in flight: 3 vectors of 8 elements per staging thread.
+// Raw chunk data in flight: 4 vectors of 8 elements per staging thread.
 template <typename TI> struct Raw;
-template <> struct Raw<uint16_t> { uint4 q[3]; };
-template <> struct Raw<float> { float4 q[3][2]; };
+template <> struct Raw<uint16_t> { uint4 q[4]; };
+template <> struct Raw<float> { float4 q[4][2]; };
 
 __device__ __forceinline__ void raw_load(const uint16_t *p, Raw<uint16_t> &r, int k) {
     r.q[k] = *(const uint4 *)p;
@@ -209,7 +211,8 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
             const float *buf = sm + lay::BUF + (cm & 1) * lay::BUF_SIZE;
             f32x4 d1a = {0.f, 0.f, 0.f, 0.f}, d1r = d1a;
             lds_barrier();
-            // ---- part 1: checkpoint, D1 = [A^;R^] S_0^T for this wave's rows
+            // ---- phase X: checkpoint, D1 = [A^;R^] S_0^T for this wave's rows
+            //      (W for this chunk is being solved meanwhile)
             if (cm >= 0) {
                 if (p.ckpt) {
                     float *cp = p.ckpt + ((u.ckpt + cm) * H + h) * (int64_t)(kN * kN) + (int64_t)irow * kN;
@@ -232,12 +235,10 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
                 }
             }
             lds_barrier();
-            // ---- part 2: rhs = P_a + L_ak V; X = W rhs; Y = P_r + M_rk V + M_rb X;
-            //      y out; D2 on state tiles 0, 1
-            f32x4 xx = {0.f, 0.f, 0.f, 0.f};
-            float4 vb = make_float4(0.f, 0.f, 0.f, 0.f);
+            // ---- phase Y: rhs = P_a + L_ak V; X = W rhs; Y = P_r + M_rk V + M_rb X;
+            //      y out; D2 on the four state tiles
             if (cm >= 0) {
-                vb = *(const float4 *)(buf + lay::B_VT + irow * VLD + 4 * kq);
+                const float4 vb = *(const float4 *)(buf + lay::B_VT + irow * VLD + 4 * kq);
                 const float *mrow = buf + lay::B_M + l16 * MLD + 4 * kq;
                 const float4 lak = *(const float4 *)(mrow + MLAK * 16 * MLD);
                 const float4 mrk = *(const float4 *)(mrow + MMRK * 16 * MLD);
@@ -247,12 +248,13 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
                 d1a = mfma4(lak.z, vb.z, d1a); d1a = mfma4(lak.w, vb.w, d1a);
                 d1r = mfma4(mrk.x, vb.x, d1r); d1r = mfma4(mrk.y, vb.y, d1r);
                 d1r = mfma4(mrk.z, vb.z, d1r); d1r = mfma4(mrk.w, vb.w, d1r);
+                f32x4 xx = {0.f, 0.f, 0.f, 0.f};
                 xx = mfma4(wi.x, d1a[0], xx); xx = mfma4(wi.y, d1a[1], xx);
                 xx = mfma4(wi.z, d1a[2], xx); xx = mfma4(wi.w, d1a[3], xx);
                 d1r = mfma4(mrb.x, xx[0], d1r); d1r = mfma4(mrb.y, xx[1], d1r);
                 d1r = mfma4(mrb.z, xx[2], d1r); d1r = mfma4(mrb.w, xx[3], d1r);
-                acc[0] = d2_tile(acc[0], buf, 0, l16, kq, xx, vb);
-                acc[1] = d2_tile(acc[1], buf, 1, l16, kq, xx, vb);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] = d2_tile(acc[q], buf, q, l16, kq, xx, vb);
                 const int t0 = cm * kChunk;
                 const int L = min(kChunk, u.len - t0);
 #pragma unroll
@@ -260,12 +262,6 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
                     const int t = 4 * kq + r;
                     if (t < L) IO<TI>::st((TI *)p.y, base + (int64_t)(t0 + t) * ts + irow, d1r[r]);
                 }
-            }
-            lds_barrier();
-            // ---- part 3: D2 on state tiles 2, 3
-            if (cm >= 0) {
-                acc[2] = d2_tile(acc[2], buf, 2, l16, kq, xx, vb);
-                acc[3] = d2_tile(acc[3], buf, 3, l16, kq, xx, vb);
             }
         }
         if (p.s_out) {
@@ -280,8 +276,7 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
     // ================= operand waves =================
     const int pw = wave - NMW;                 // 0..7, uniform
     const int ptid = tid - 64 * NMW;           // 0..511
-    const int sid = ptid - 256;                // staging thread index (operand waves 4..7)
-    float *s_in = sm + lay::IN;
+    const int sid = ptid - 320;                // staging thread index (operand waves 5..7)
     float *s_AR = sm + lay::AR;
     float *s_AWR = sm + lay::AWR;
     float *s_BD = sm + lay::BD;
@@ -289,16 +284,16 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
     float *s_BL = sm + lay::BL;
     float *s_Lab = sm + lay::LAB;
 
-    // Staging (operand waves 4-7): element group g = sid + 256k (k = 0..2) of
+    // Staging (operand waves 5-7): element group g = sid + 192k (k = 0..3) of
     // 6 streams x 16 tokens x 8 groups of 8 elements; stream g >> 7 is uniform
     // per wave. Loads are issued one chunk ahead, unconditionally (chunk index
     // and token rows clamped into the sequence), so that the registers in
     // flight have exactly one definition per iteration.
     Raw<TI> raw;
-    const TI *sp[3];
+    const TI *sp[4];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        const int st = __builtin_amdgcn_readfirstlane((sid + 256 * k) >> 7);
+    for (int k = 0; k < 4; ++k) {
+        const int st = __builtin_amdgcn_readfirstlane((sid + 192 * k) >> 7);
         const void *vp = st == IR ? p.r : st == IW ? p.w : st == IK ? p.k
                        : st == IA ? p.a : st == IB ? p.b : p.v;
         sp[k] = (const TI *)vp + base;
@@ -306,17 +301,18 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
     auto issue = [&](int cc) {               // 0 <= cc < nch
         const int Lc = min(kChunk, u.len - cc * kChunk);
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            const int g = sid + 256 * k;
+        for (int k = 0; k < 4; ++k) {
+            const int g = sid + 192 * k;
             const int t = min((g >> 3) & 15, Lc - 1), e0 = (g & 7) * 8;
             raw_load(sp[k] + (int64_t)(cc * kChunk + t) * ts + e0, raw, k);
         }
     };
     auto stage = [&](int cc) {
         const int Lc = min(kChunk, u.len - cc * kChunk);
+        float *s_in = sm + lay::IN + (cc & 1) * lay::IN_SIZE;
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            const int g = sid + 256 * k;
+        for (int k = 0; k < 4; ++k) {
+            const int g = sid + 192 * k;
             const int st = g >> 7, t = (g >> 3) & 15, e0 = (g & 7) * 8;
             float x[8];
             if (t < Lc) {
@@ -332,106 +328,122 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
         }
     };
 
-    // ---- phase A: per-column decay rows, one role per operand wave, lane = key column j
-    auto phase_a = [&](float *buf) {
+    // Per-column decay rows, lane = key column j. Each role reads all its inputs
+    // before its first store (the stores go through runtime-offset pointers,
+    // which would otherwise order every later load behind them).
+    //
+    // ---- phase X (operand waves 1-4): the rows the 16x16 matrices are built
+    //      from: A' = a F_ex (wave 1), R' = r F_in (wave 2), b (3) and k (4) rows
+    auto matrix_rows = [&](const float *s_in) {
         const int j = lane;
-        const float *w_ = s_in + IW * 1024 + j;
-        if (pw == 0) {             // A^_t = a_t gamma_{t-1}; gamma_16
-            float g = 1.f;
+        const int role = pw - 1;
+        const int st = role == 0 ? IA : role == 1 ? IR : role == 2 ? IB : IK;
+        float wv[16], xv[16];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                buf[lay::B_Q + t * QLD + j] = s_in[IA * 1024 + t * 64 + j] * g;
-                g *= w_[t * 64];
-            }
-            buf[lay::B_GC + j] = g;
-        } else if (pw == 1) {      // R^_t = r_t gamma_t
-            float g = 1.f;
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                g *= w_[t * 64];
-                buf[lay::B_Q + (16 + t) * QLD + j] = s_in[IR * 1024 + t * 64 + j] * g;
-            }
-        } else if (pw == 2 || pw == 3) {   // B^ (2) or K^ (3), by column; V by row (2)
-            const int st = pw == 2 ? IB : IK;
-            float d = 1.f, x[16];
-#pragma unroll
-            for (int s = 15; s >= 0; --s) {
-                x[s] = s_in[st * 1024 + s * 64 + j] * d;
-                d *= w_[s * 64];
-            }
-            float *dst = buf + lay::B_BKT + j * KLD + (pw - 2) * 16;
-#pragma unroll
-            for (int s = 0; s < 16; s += 4) *(float4 *)(dst + s) = make_float4(x[s], x[s + 1], x[s + 2], x[s + 3]);
-            if (pw == 2) {
-#pragma unroll
-                for (int t = 0; t < 16; t += 4) {
-                    const float *vc = s_in + IV * 1024 + t * 64 + j;
-                    *(float4 *)(buf + lay::B_VT + j * VLD + t) = make_float4(vc[0], vc[64], vc[128], vc[192]);
-                }
-            }
-        } else if (pw == 4 || pw == 5) {   // A' = a F_ex (4) or R' = r F_in (5); times W_2 for t >= 12
-            const int st = pw == 4 ? IA : IR;
-            const int inc = pw - 4;
-            float W2 = 1.f;
-#pragma unroll
-            for (int t = 8; t < 12; ++t) W2 *= w_[t * 64];
+        for (int t = 0; t < 16; ++t) {
+            wv[t] = s_in[IW * 1024 + t * 64 + j];
+            xv[t] = s_in[st * 1024 + t * 64 + j];
+        }
+        if (role < 2) {            // times W_2 for t >= 12 as well
+            const int inc = role;
+            float o[16];
 #pragma unroll
             for (int sc = 0; sc < 4; ++sc) {
                 float f = 1.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 4 * sc + e;
-                    const float wc = fmaxf(w_[t * 64], kMinFactor);
+                    const float wc = fmaxf(wv[t], kMinFactor);
                     if (inc) f *= wc;
-                    const float x = s_in[st * 1024 + t * 64 + j] * f;
-                    s_AR[(16 * inc + t) * QLD + j] = x;
-                    if (sc == 3) s_AWR[(4 * inc + e) * QLD + j] = x * W2;
+                    o[t] = xv[t] * f;
                     if (!inc) f *= wc;
                 }
             }
-        } else {                   // b (6) or k (7) rows: x_s / F_s, and scaled to the split points
-            const int st = pw == 6 ? IB : IK;
-            const int ko = pw - 6;             // row offset of the k rows in BL
-            float wv[16];
+            const float W2 = (wv[8] * wv[9]) * (wv[10] * wv[11]);
 #pragma unroll
-            for (int t = 0; t < 16; ++t) wv[t] = w_[t * 64];
-            const float W1 = (wv[4] * wv[5]) * (wv[6] * wv[7]);
-            float *dd = pw == 6 ? s_BD : s_KD;
+            for (int t = 0; t < 16; ++t) s_AR[(16 * inc + t) * QLD + j] = o[t];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s_AWR[(4 * inc + e) * QLD + j] = o[12 + e] * W2;
+        } else {                   // x_s / F_s, and x_s scaled to the split points
+            const int ko = role - 2;           // row offset of the k rows in BL
+            float od[16], os[12];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                float F = 1.f;
-                float suf = 1.f;                 // prod_{s<u<4q+4} w_u, built downwards
-                float xs[4];
+                float F = 1.f, suf = 1.f;        // suf = prod_{s<u<4q+4} w_u, built downwards
 #pragma unroll
                 for (int e = 3; e >= 0; --e) {
-                    const int s = 4 * q + e;
-                    xs[e] = s_in[st * 1024 + s * 64 + j];
-                    if (q < 3) {
-                        const float bs = xs[e] * suf;
-                        if (q == 0) {
-                            s_BL[(8 * ko + s) * QLD + j] = bs * W1;     // scaled to 8
-                            s_BL[(16 + 4 * ko + s) * QLD + j] = bs;     // scaled to 4
-                        } else if (q == 1) {
-                            s_BL[(8 * ko + s) * QLD + j] = bs;          // scaled to 8
-                        } else {
-                            s_BL[(16 + 4 * ko + s) * QLD + j] = bs;     // scaled to 12
-                        }
-                    }
-                    suf *= wv[s];
+                    if (q < 3) os[4 * q + e] = xv[4 * q + e] * suf;
+                    suf *= wv[4 * q + e];
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int s = 4 * q + e;
-                    F *= fmaxf(wv[s], kMinFactor);
-                    dd[s * QLD + j] = xs[e] * __builtin_amdgcn_rcpf(F);
+                    F *= fmaxf(wv[4 * q + e], kMinFactor);
+                    od[4 * q + e] = xv[4 * q + e] * __builtin_amdgcn_rcpf(F);
                 }
+            }
+            const float W1 = (wv[4] * wv[5]) * (wv[6] * wv[7]);
+            float *dd = ko ? s_KD : s_BD;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) dd[s * QLD + j] = od[s];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s_BL[(8 * ko + e) * QLD + j] = os[e] * W1;          // s = e scaled to 8
+                s_BL[(16 + 4 * ko + e) * QLD + j] = os[e];          // s = e scaled to 4
+                s_BL[(8 * ko + 4 + e) * QLD + j] = os[4 + e];       // s = 4+e scaled to 8
+                s_BL[(24 + 4 * ko + e) * QLD + j] = os[8 + e];      // s = 8+e scaled to 12
             }
         }
     };
 
-    // ---- phase B: the 16x16 matrices. Waves 0, 1: the cross-sub-chunk
-    //      blocks on MFMA; waves 2-5: the within-sub-chunk pairs on VALU
-    auto phase_b = [&](float *buf) {
+    // ---- phase Y (operand waves 6, 7): the hand-off rows for the state waves:
+    //      A^_t = a_t gamma_{t-1}, R^_t = r_t gamma_t, gamma_16 (wave 6);
+    //      B^, K^ by key column and V by value row (wave 7)
+    auto handoff_rows = [&](const float *s_in, float *buf) {
+        const int j = lane;
+        float wv[16], xv[16], yv[16];
+        const int s1 = pw == 6 ? IA : IB, s2 = pw == 6 ? IR : IK;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            wv[t] = s_in[IW * 1024 + t * 64 + j];
+            xv[t] = s_in[s1 * 1024 + t * 64 + j];
+            yv[t] = s_in[s2 * 1024 + t * 64 + j];
+        }
+        if (pw == 6) {
+            float g = 1.f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                xv[t] *= g;
+                g *= wv[t];
+                yv[t] *= g;
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                buf[lay::B_Q + t * QLD + j] = xv[t];
+                buf[lay::B_Q + (16 + t) * QLD + j] = yv[t];
+            }
+            buf[lay::B_GC + j] = g;
+        } else {
+            float vv[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) vv[t] = s_in[IV * 1024 + t * 64 + j];
+            float d = 1.f;
+#pragma unroll
+            for (int s = 15; s >= 0; --s) { xv[s] *= d; yv[s] *= d; d *= wv[s]; }
+            float *dst = buf + lay::B_BKT + j * KLD;
+#pragma unroll
+            for (int s = 0; s < 16; s += 4) {
+                *(float4 *)(dst + s) = make_float4(xv[s], xv[s + 1], xv[s + 2], xv[s + 3]);
+                *(float4 *)(dst + 16 + s) = make_float4(yv[s], yv[s + 1], yv[s + 2], yv[s + 3]);
+            }
+#pragma unroll
+            for (int t = 0; t < 16; t += 4)
+                *(float4 *)(buf + lay::B_VT + j * VLD + t) = make_float4(vv[t], vv[t + 1], vv[t + 2], vv[t + 3]);
+        }
+    };
+
+    // ---- phase Y (operand waves 0-5): the 16x16 matrices. Waves 0, 1: the
+    //      cross-sub-chunk blocks on MFMA; waves 2-5: the within-sub-chunk pairs on VALU
+    auto matrices = [&](float *buf) {
         if (pw < 2) {
             // wave 0: split at 8: rows m < 8 are a rows t = 8+m, m >= 8 r rows t = m;
             //         columns n < 8 are b rows s = n, n >= 8 k rows s = n-8.
@@ -541,42 +553,46 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
     // Entries of L_ab and of the hand-off matrices that are never written
     // (upper parts) stay zero.
     for (int q = ptid; q < 16 * MLD + 2 * lay::BUF_SIZE; q += 64 * kPrepWaves) sm[lay::LAB + q] = 0.f;
-    if (nch == 0) {            // nothing to build; match the state waves' three barriers
-        lds_barrier();
+    if (nch == 0) {            // nothing to build; match the state waves' two barriers
         lds_barrier();
         lds_barrier();
         return;
     }
 
-    if (pw >= 4) {
+    // Per iteration c: phase X builds the matrix rows of chunk c, solves W of
+    // chunk c-1 and stages chunk c+1; phase Y builds the 16x16 matrices and the
+    // hand-off rows of chunk c. The state waves advance chunk c-1 meanwhile and
+    // need W only in phase Y.
+    if (pw >= 5) {
         issue(0);
         stage(0);
         issue(min(1, nch - 1));
 #pragma unroll 1
         for (int c = 0; c <= nch; ++c) {
             float *buf = sm + lay::BUF + (c & 1) * lay::BUF_SIZE;
-            const bool live = c < nch;
+            const float *s_in = sm + lay::IN + (c & 1) * lay::IN_SIZE;
             lds_barrier();
-            if (live) phase_a(buf);
-            lds_barrier();
-            if (live) phase_b(buf);
-            lds_barrier();
-            // phase C: stage chunk c+1, start loading chunk c+2
             if (c + 1 < nch) stage(c + 1);
             issue(min(c + 2, nch - 1));
+            lds_barrier();
+            if (c < nch) {
+                if (pw == 5) matrices(buf);
+                else handoff_rows(s_in, buf);
+            }
         }
     } else {
 #pragma unroll 1
         for (int c = 0; c <= nch; ++c) {
             float *buf = sm + lay::BUF + (c & 1) * lay::BUF_SIZE;
-            const bool live = c < nch;
+            const float *s_in = sm + lay::IN + (c & 1) * lay::IN_SIZE;
             lds_barrier();
-            if (live) phase_a(buf);
+            if (pw == 0) {
+                if (c >= 1) solve_w(sm + lay::BUF + ((c - 1) & 1) * lay::BUF_SIZE);
+            } else if (c < nch) {
+                matrix_rows(s_in);
+            }
             lds_barrier();
-            if (live) phase_b(buf);
-            lds_barrier();
-            // phase C: W for chunk c
-            if (live && pw == 0) solve_w(buf);
+            if (c < nch) matrices(buf);
         }
     }
 }
