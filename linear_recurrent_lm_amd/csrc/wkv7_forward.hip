@@ -139,25 +139,6 @@ __device__ __forceinline__ f32x4 rows_product(const float *arow, const float *br
     return d;
 }
 
-// S^T tile q of a state wave: acc = diag(gamma) acc + B^^T X + K^^T V over the
-// chunk's 16 tokens (x, v: this lane's B-operand values X[4kq+e][i], V[4kq+e][i]).
-__device__ __forceinline__ f32x4 d2_tile(f32x4 acc, const float *buf, int q, int l16, int kq,
-                                         const f32x4 &x, const float4 &v) {
-    const float4 g4 = *(const float4 *)(buf + lay::B_GC + 16 * q + 4 * kq);
-    acc[0] *= g4.x; acc[1] *= g4.y; acc[2] *= g4.z; acc[3] *= g4.w;
-    const float *br = buf + lay::B_BKT + (16 * q + l16) * KLD + 4 * kq;
-    const float4 b0 = *(const float4 *)br, k0 = *(const float4 *)(br + 16);
-    acc = mfma4(b0.x, x[0], acc);
-    acc = mfma4(b0.y, x[1], acc);
-    acc = mfma4(b0.z, x[2], acc);
-    acc = mfma4(b0.w, x[3], acc);
-    acc = mfma4(k0.x, v.x, acc);
-    acc = mfma4(k0.y, v.y, acc);
-    acc = mfma4(k0.z, v.z, acc);
-    acc = mfma4(k0.w, v.w, acc);
-    return acc;
-}
-
 template <typename TI, int NMW>
 __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdArgs p, int32_t units) {
     constexpr int RB = 16 * NMW;       // value rows per workgroup
@@ -210,9 +191,12 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
             const int cm = c - 1;                        // chunk advanced in this iteration
             const float *buf = sm + lay::BUF + (cm & 1) * lay::BUF_SIZE;
             f32x4 d1a = {0.f, 0.f, 0.f, 0.f}, d1r = d1a;
+            float4 bt[4];                                // B^ rows of the four state tiles
+            float4 mrb = make_float4(0.f, 0.f, 0.f, 0.f);
             lds_barrier();
-            // ---- phase X: checkpoint, D1 = [A^;R^] S_0^T for this wave's rows
-            //      (W for this chunk is being solved meanwhile)
+            // ---- phase X (W of this chunk is being solved meanwhile):
+            //      checkpoint; D1 = [A^;R^] S_0^T for this wave's rows;
+            //      P_a += L_ak V, P_r += M_rk V; S^T = diag(gamma) S^T + K^^T V
             if (cm >= 0) {
                 if (p.ckpt) {
                     float *cp = p.ckpt + ((u.ckpt + cm) * H + h) * (int64_t)(kN * kN) + (int64_t)irow * kN;
@@ -220,6 +204,11 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
                     for (int q = 0; q < 4; ++q)
                         *(float4 *)(cp + 16 * q + 4 * kq) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
                 }
+                const float4 vb = *(const float4 *)(buf + lay::B_VT + irow * VLD + 4 * kq);
+                const float *mrow = buf + lay::B_M + l16 * MLD + 4 * kq;
+                const float4 lak = *(const float4 *)(mrow + MLAK * 16 * MLD);
+                const float4 mrk = *(const float4 *)(mrow + MMRK * 16 * MLD);
+                mrb = *(const float4 *)(mrow + MMRB * 16 * MLD);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const float4 a4 = *(const float4 *)(buf + lay::B_Q + l16 * QLD + 16 * q + 4 * kq);
@@ -233,28 +222,39 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
                     d1a = mfma4(a4.w, acc[q][3], d1a);
                     d1r = mfma4(r4.w, acc[q][3], d1r);
                 }
-            }
-            lds_barrier();
-            // ---- phase Y: rhs = P_a + L_ak V; X = W rhs; Y = P_r + M_rk V + M_rb X;
-            //      y out; D2 on the four state tiles
-            if (cm >= 0) {
-                const float4 vb = *(const float4 *)(buf + lay::B_VT + irow * VLD + 4 * kq);
-                const float *mrow = buf + lay::B_M + l16 * MLD + 4 * kq;
-                const float4 lak = *(const float4 *)(mrow + MLAK * 16 * MLD);
-                const float4 mrk = *(const float4 *)(mrow + MMRK * 16 * MLD);
-                const float4 mrb = *(const float4 *)(mrow + MMRB * 16 * MLD);
-                const float4 wi = *(const float4 *)(mrow + MWI * 16 * MLD);
                 d1a = mfma4(lak.x, vb.x, d1a); d1a = mfma4(lak.y, vb.y, d1a);
                 d1a = mfma4(lak.z, vb.z, d1a); d1a = mfma4(lak.w, vb.w, d1a);
                 d1r = mfma4(mrk.x, vb.x, d1r); d1r = mfma4(mrk.y, vb.y, d1r);
                 d1r = mfma4(mrk.z, vb.z, d1r); d1r = mfma4(mrk.w, vb.w, d1r);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 g4 = *(const float4 *)(buf + lay::B_GC + 16 * q + 4 * kq);
+                    const float *br = buf + lay::B_BKT + (16 * q + l16) * KLD + 4 * kq;
+                    bt[q] = *(const float4 *)br;
+                    const float4 k4 = *(const float4 *)(br + 16);
+                    f32x4 a = acc[q];
+                    a[0] *= g4.x; a[1] *= g4.y; a[2] *= g4.z; a[3] *= g4.w;
+                    a = mfma4(k4.x, vb.x, a); a = mfma4(k4.y, vb.y, a);
+                    a = mfma4(k4.z, vb.z, a); a = mfma4(k4.w, vb.w, a);
+                    acc[q] = a;
+                }
+            }
+            lds_barrier();
+            // ---- phase Y: X = W rhs; Y = P_r + M_rk V + M_rb X; y out; S^T += B^^T X
+            if (cm >= 0) {
+                const float4 wi = *(const float4 *)(buf + lay::B_M + MWI * 16 * MLD + l16 * MLD + 4 * kq);
                 f32x4 xx = {0.f, 0.f, 0.f, 0.f};
                 xx = mfma4(wi.x, d1a[0], xx); xx = mfma4(wi.y, d1a[1], xx);
                 xx = mfma4(wi.z, d1a[2], xx); xx = mfma4(wi.w, d1a[3], xx);
                 d1r = mfma4(mrb.x, xx[0], d1r); d1r = mfma4(mrb.y, xx[1], d1r);
                 d1r = mfma4(mrb.z, xx[2], d1r); d1r = mfma4(mrb.w, xx[3], d1r);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc[q] = d2_tile(acc[q], buf, q, l16, kq, xx, vb);
+                for (int q = 0; q < 4; ++q) {
+                    f32x4 a = acc[q];
+                    a = mfma4(bt[q].x, xx[0], a); a = mfma4(bt[q].y, xx[1], a);
+                    a = mfma4(bt[q].z, xx[2], a); a = mfma4(bt[q].w, xx[3], a);
+                    acc[q] = a;
+                }
                 const int t0 = cm * kChunk;
                 const int L = min(kChunk, u.len - t0);
 #pragma unroll
