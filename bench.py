@@ -99,6 +99,23 @@ def cpu_baseline(inp, budget_s):
                       f"backward, {el:.1f} s"}
 
 
+def _time_ms(fn, warmup, steps, ev):
+    """Mean duration of fn() over `steps` calls, HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    rec = []
+    for _ in range(steps):
+        e0, e1 = ev(), ev()
+        e0.record()
+        fn()
+        e1.record()
+        rec.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in rec]))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -179,6 +196,31 @@ def main():
     torch.cuda.synchronize()
     pre_ms = float(np.mean([a.elapsed_time(b) for a, b in pre]))
 
+    # Ragged forward: 64 sequences, lengths ~ U[16, 2048], packed in 4 streams
+    # with a state reset at each sequence boundary.
+    lengths = synth.ragged_lengths(64, 16, 2048, seed=4)
+    flat, _ = synth.make_segment_inputs(lengths, H, N, seed=11, dtype="bf16")
+    T_rg, st_rg, ln_rg = synth.packed_layout(lengths, 4)
+    _, st_s, ln_s = synth.sorted_table(st_rg, ln_rg)
+    rg = synth.scatter_segments(flat, lengths, st_rg, 4, T_rg, fill=0.0, dtype="bf16")
+    rts = [torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in rg.streams()]
+    seg = W.Segments(4, T_rg, st_s, ln_s, dev)
+    ry = torch.empty_like(rts[0])
+    rso = torch.empty((len(lengths), H, N, N), device=dev, dtype=torch.float32)
+    ragged_ms = _time_ms(lambda: W.wkv7_forward(*rts, None, segments=seg, y=ry, s_out=rso),
+                         args.warmup, args.steps, ev)
+    rg_tok = int(np.sum(lengths))
+
+    # Decode: one step at B=512, H=32 reading and writing a 64x64 fp32 state per (b, h).
+    dinp = synth.make_decode_inputs(512, H, N, seed=4)
+    dts = [torch.from_numpy(x[:, 0]).to(dev).to(torch.bfloat16) for x in dinp.streams()]
+    ds_in = torch.from_numpy(dinp.s0).to(dev)
+    ds_out = torch.empty_like(ds_in)
+    dy_out = torch.empty_like(dts[0])
+    dec_ms = _time_ms(lambda: W.wkv7_decode_step(*dts, ds_in, s_out=ds_out, y=dy_out),
+                      args.warmup, args.steps, ev)
+    dec_bytes = 512 * H * (2 * N * N * 4 + 7 * N * 2)
+
     f_ms, b_ms = float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
     th = tok * H
     kernels = {
@@ -222,6 +264,14 @@ def main():
                             "fp32_frac": FWD_FLOP * pre_th / (pre_ms * 1e-3) / PEAK_FP32,
                             "hbm_frac": FWD_BYTES * pre_th / (pre_ms * 1e-3) / PEAK_HBM},
     }
+    out["ragged_forward"] = {"workload": "bf16 64 sequences, lengths ~ U[16, 2048] (%d tokens), packed in 4 "
+                                         "streams with per-sequence resets, H=32" % rg_tok,
+                             "ms": ragged_ms, "tokens_per_s": rg_tok / (ragged_ms * 1e-3),
+                             "fp32_frac": FWD_FLOP * rg_tok * H / (ragged_ms * 1e-3) / PEAK_FP32}
+    out["decode_step"] = {"workload": "bf16 B=512 T=1 H=32, fp32 state in and out",
+                          "us": dec_ms * 1e3, "sequence_steps_per_s": 512 / (dec_ms * 1e-3),
+                          "GB_per_s": dec_bytes / (dec_ms * 1e-3) / 1e9,
+                          "hbm_frac": dec_bytes / (dec_ms * 1e-3) / PEAK_HBM}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
