@@ -111,7 +111,15 @@ wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes) {
     if (!bytes) return WKV7_ERR_INVALID_ARGUMENT;
     const wkv7_status st = check_desc(d);
     if (st != WKV7_OK) return st;
-    *bytes = 0;
+    // one fp32 64x64 state-gradient slot per checkpoint slot and head
+    int64_t slots = 0;
+    if (d->num_seqs > 0) {
+        if (d->ckpt_slots < 0) return WKV7_ERR_INVALID_ARGUMENT;
+        slots = d->ckpt_slots;
+    } else {
+        slots = (int64_t)d->B * ((d->T + kChunk - 1) / kChunk);
+    }
+    *bytes = (size_t)slots * d->H * kN * kN * sizeof(float);
     return WKV7_OK;
 }
 
@@ -179,8 +187,9 @@ wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, cons
     if (!ckpt) return WKV7_ERR_INVALID_ARGUMENT;
     if ((st = check_ckpt(d, ckpt)) != WKV7_OK) return st;
     size_t need = 0;
-    wkv7_workspace_bytes(d, &need);
+    if ((st = wkv7_workspace_bytes(d, &need)) != WKV7_OK) return st;
     if (workspace_bytes < need || (need > 0 && !workspace)) return WKV7_ERR_WORKSPACE_TOO_SMALL;
+    if (workspace && !aligned16(workspace)) return WKV7_ERR_INVALID_ARGUMENT;
     if ((st = check_device()) != WKV7_OK) return st;
 
     hipStream_t hs = (hipStream_t)stream;
@@ -191,11 +200,13 @@ wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, cons
     args.ckpt = ckpt; args.dy = dy; args.ds_out = ds_out;
     args.dr = dr; args.dw = dw; args.dk = dk; args.dv = dv; args.da = da; args.db = db;
     args.ds0 = ds0;
+    args.ws = (float *)workspace;
     if (d->num_seqs > 0) {
         void *outs[6] = {dr, dw, dk, dv, da, db};
         if (wkv7::launch_zero_uncovered(args.seg, d->dtype, outs, 6, hs) != hipSuccess)
             return WKV7_ERR_HIP;
     }
+    if (wkv7::launch_backward_sweep(args, hs) != hipSuccess) return WKV7_ERR_HIP;
     if (wkv7::launch_backward(args, hs) != hipSuccess) return WKV7_ERR_HIP;
     return WKV7_OK;
 }

@@ -1,10 +1,12 @@
-// WKV-7 backward from 16-token state checkpoints, chunk form on FP32 MFMA.
+// WKV-7 backward, second pass: per-chunk gradients on FP32 MFMA.
 //
 // Forward recurrence (RWKV-7 WKV-7): S_t = S_{t-1} diag(w_t) + (S_{t-1} a_t) b_t^T
 // + v_t k_t^T, y_t = S_t r_t. Gradients of L = sum <dy, y> + <ds_out, S_T>.
-// Chunks are processed from last to first; each one starts from its stored
-// checkpoint S_0 (the state entering the chunk) and from dS_C, the gradient
-// of the state leaving it, so nothing is reconstructed by dividing by w.
+// Each chunk starts from its stored checkpoint S_0 (the state entering the
+// chunk) and from dS_C, the gradient of the state leaving it, written by the
+// first pass (the state-gradient sweep); with both given, chunks are
+// independent and run in parallel, kChunksPerGroup consecutive chunks per
+// workgroup. Nothing is reconstructed by dividing by w.
 //
 // Within a chunk the forward is (tokens t = 0..15, as in the forward kernel)
 //     X = W (A^ S_0^T + L_ak V),  W = (I - L_ab)^-1
@@ -13,7 +15,6 @@
 // and its reverse mode is
 //     dX   = B^ dS_C^T + M_rb^T dY          drhs = W^T dX
 //     dV   = K^ dS_C^T + M_rk^T dY + L_ak^T drhs
-//     dS_0 = dS_C diag(gamma_C) + drhs^T A^ + dY^T R^
 //     dA^ = drhs S_0, dR^ = dY S_0, dB^ = X dS_C, dK^ = V dS_C
 //     dL_ab = drhs X^T, dL_ak = drhs V^T (strictly lower), dM_rb = dY X^T,
 //     dM_rk = dY V^T (lower)
@@ -27,18 +28,18 @@
 // straddle m), then dw = u / w. The whole backward uses w' = max(w, 2^-30),
 // so dw is finite at w = 0 and equals the gradient there to within the clamp.
 //
-// One 256-thread workgroup (4 waves) per (sequence, head). 16x64 chunk
-// matrices and the two 64x64 states live in LDS, row-major; MFMA operands are
-// 16-byte loads along the contraction index where the layout allows it. Wave
-// w owns value rows 16w..16w+15 for the value-side products and key columns
-// 16w..16w+15 for the key-side ones; dS is carried between chunks in the
-// accumulators of the dS^T product.
+// One 512-thread workgroup (8 waves) per (sequence, head, chunk group). 16x64
+// chunk matrices and the two 64x64 states live in LDS, row-major; MFMA
+// operands are 16-byte loads along the contraction index where the layout
+// allows it. Waves w and w+4 share a SIMD and take complementary (MFMA and
+// VALU) work in each phase.
 #include "wkv7_kernels.h"
 
 namespace wkv7 {
 namespace {
 
 constexpr int kThreads = 512;
+constexpr int kChunksPerGroup = 8;                // chunks per workgroup (consecutive)
 constexpr int LD = 68;                            // row pitch of 16x64 / 64x64 arrays
 constexpr float kMinW = 9.313225746154785e-10f;   // 2^-30
 
@@ -288,8 +289,10 @@ __device__ __forceinline__ void assemble_out(const AsmArgs &g, float (&st5)[2][5
 template <typename TI>
 __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32_t units) {
     extern __shared__ __align__(16) float sm[];
-    const int unit = blockIdx.x;
-    if (unit >= units) return;
+    // Workgroup -> (unit, group of kChunksPerGroup chunks); chunks are
+    // independent given S_0 (checkpoint) and dS_C (first pass).
+    const int unit = blockIdx.x % units;
+    const int grp = blockIdx.x / units;
     const int H = p.seg.H;
     const int h = unit % H;
     const int sq = unit / H;
@@ -323,26 +326,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
     const int64_t base = (u.start * H + h) * kN;
     const int64_t sbase = ((int64_t)sq * H + h) * (kN * kN);
 
-    // dS carried between chunks, two 16x16 tiles per wave:
-    // ds[q][r] = dS[16*w4 + l16][16*jt + 4*kq + r], jt = 2*(wave >> 2) + q
     const int it = w4;
-    f32x4 ds[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int jt = 2 * (wave >> 2) + q;
-        if (p.ds_out) {
-            const float4 v4 = *(const float4 *)(p.ds_out + sbase + (int64_t)(16 * it + l16) * kN + 16 * jt + 4 * kq);
-            ds[q] = f32x4{v4.x, v4.y, v4.z, v4.w};
-        } else {
-            ds[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
 
     // Staging: element groups g = tid + 512k (k = 0, 1) of 7 streams x 16
     // tokens x 8 groups of 8; stream g >> 7 is uniform per wave.
     const int nch = (u.len + kChunk - 1) / kChunk;
+    const int c_lo = grp * kChunksPerGroup;
+    const int c_hi = min(nch, c_lo + kChunksPerGroup);
+    if (c_lo >= c_hi) return;
     Raw<TI> raw;
-    float4 ckr0, ckr1;                          // checkpoint of the chunk in flight
+    float4 ckr0, ckr1, dsr0, dsr1;              // checkpoint S_0 and dS_C of the chunk in flight
     const TI *sp[2];                            // stream of each staged group (uniform)
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -350,23 +343,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         const void *vp = p.staged[st];
         sp[k] = vp ? (const TI *)vp + base : nullptr;
     }
+    // Loads are issued one chunk ahead, unconditionally (token rows clamped
+    // into the sequence), so the registers in flight have one definition per
+    // iteration; groups of a missing stream (dy == NULL, or past the seven
+    // streams) load the w row instead and stage as fill.
+    const TI *wrow = (const TI *)p.w + base;
     auto issue = [&](int cc) {
         const int Lc = min(kChunk, u.len - cc * kChunk);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int g = tid + k * kThreads;
-            const int t = (g >> 3) & 15, e0 = (g & 7) * 8;
-            if (sp[k] && t < Lc) raw_load(sp[k] + (int64_t)(cc * kChunk + t) * ts + e0, raw, k);
+            const int t = min((g >> 3) & 15, Lc - 1), e0 = (g & 7) * 8;
+            raw_load((sp[k] ? sp[k] : wrow) + (int64_t)(cc * kChunk + t) * ts + e0, raw, k);
         }
-        // float4 f4 = tid + 512k of the 64x64 checkpoint: row f4 / 16, column 4 (f4 % 16)
-        const float *cp = p.ckpt + ((u.ckpt + cc) * H + h) * (int64_t)(kN * kN) + tid * 4;
-        ckr0 = *(const float4 *)cp;
-        ckr1 = *(const float4 *)(cp + kThreads * 4);
+        // float4 f4 = tid + 512k of a 64x64 state: row f4 / 16, column 4 (f4 % 16)
+        const int64_t so = ((u.ckpt + cc) * H + h) * (int64_t)(kN * kN) + tid * 4;
+        ckr0 = *(const float4 *)(p.ckpt + so);
+        ckr1 = *(const float4 *)(p.ckpt + so + kThreads * 4);
+        dsr0 = *(const float4 *)(p.ws + so);
+        dsr1 = *(const float4 *)(p.ws + so + kThreads * 4);
     };
-    if (nch > 0) issue(nch - 1);
+    issue(c_hi - 1);
 
 #pragma unroll 1
-    for (int c = nch - 1; c >= 0; --c) {
+    for (int c = c_hi - 1; c >= c_lo; --c) {
         const int t0 = c * kChunk;
         const int L = min(kChunk, u.len - t0);
         lds_barrier();
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             if (g < 7 * 128) {
                 const int st = g >> 7, t = (g >> 3) & 15, e0 = (g & 7) * 8;
                 float x[8];
-                if (t < L && (st != IDY || p.dy != nullptr)) {
+                if (t < L && sp[k] != nullptr) {
                     raw_unpack(raw, k, x);
                 } else {
                     const float f = st == IW ? 1.f : 0.f;
@@ -399,14 +399,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         {
             *(float4 *)(s_S0 + (tid >> 4) * LD + (tid & 15) * 4) = ckr0;
             *(float4 *)(s_S0 + ((tid + kThreads) >> 4) * LD + (tid & 15) * 4) = ckr1;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int jt = 2 * (wave >> 2) + q;
-                *(float4 *)(s_DS + (16 * it + l16) * LD + 16 * jt + 4 * kq) =
-                    make_float4(ds[q][0], ds[q][1], ds[q][2], ds[q][3]);
-            }
+            *(float4 *)(s_DS + (tid >> 4) * LD + (tid & 15) * 4) = dsr0;
+            *(float4 *)(s_DS + ((tid + kThreads) >> 4) * LD + (tid & 15) * 4) = dsr1;
         }
-        if (c > 0) issue(c - 1);
+        issue(max(c - 1, c_lo));
         lds_barrier();
         relane();
 
@@ -627,17 +623,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                     }
                 }
             }
-            // dS_0^T[j][i] = gamma_C[j] dS_C^T[j][i] + sum_t A^[t][j] drhs[t][i] + R^[t][j] dY[t][i]
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int jq = 16 * (2 * (wave >> 2) + q);
-                const float4 g4 = *(const float4 *)(s_gC + jq + 4 * kq);
-                f32x4 acc = ds[q];
-                acc[0] *= g4.x; acc[1] *= g4.y; acc[2] *= g4.z; acc[3] *= g4.w;
-                acc = mm_TB(acc, s_Q + jq, LD, s_DR + i0, LD, l16, kq);
-                acc = mm_TB(acc, s_Q + 16 * LD + jq, LD, sDY + i0, LD, l16, kq);
-                ds[q] = acc;
-            }
         }
         lds_barrier();
         relane();
@@ -685,14 +670,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             }
         }
     }
-    if (p.ds0) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int jt = 2 * (wave >> 2) + q;
-            *(float4 *)(p.ds0 + sbase + (int64_t)(16 * it + l16) * kN + 16 * jt + 4 * kq) =
-                make_float4(ds[q][0], ds[q][1], ds[q][2], ds[q][3]);
-        }
-    }
 }
 
 }  // namespace
@@ -709,7 +686,10 @@ hipError_t launch_backward(const BwdArgs &args, hipStream_t stream) {
     auto fn = a.dtype == 1 ? bwd_chunk_kernel<uint16_t> : bwd_chunk_kernel<float>;
     hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fn, dim3((unsigned)units), dim3(kThreads), lds, stream, a, units);
+    // A sequence lies within one row of T tokens, so it has at most ceil(T / 16) chunks.
+    const int max_chunks = (a.seg.T + kChunk - 1) / kChunk;
+    const int64_t groups = (max_chunks + kChunksPerGroup - 1) / kChunksPerGroup;
+    hipLaunchKernelGGL(fn, dim3((unsigned)(groups * units)), dim3(kThreads), lds, stream, a, units);
     return hipGetLastError();
 }
 

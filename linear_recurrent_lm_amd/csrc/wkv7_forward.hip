@@ -40,6 +40,7 @@
 // a double-buffered LDS hand-off, two workgroup barriers per chunk (W of a
 // chunk is solved one phase later, while the state waves run its D1).
 #include "wkv7_kernels.h"
+#include "wkv7_mfma.h"
 
 namespace wkv7 {
 namespace {
@@ -76,68 +77,6 @@ constexpr int BUF_SIZE = B_GC + 64;
 constexpr int TOTAL = BUF + 2 * BUF_SIZE;
 static_assert(BUF % 4 == 0 && BUF_SIZE % 4 == 0, "16-byte aligned buffers");
 }  // namespace lay
-
-// Raw chunk data in flight: 4 vectors of 8 elements per staging thread.
-template <typename TI> struct Raw;
-template <> struct Raw<uint16_t> { uint4 q[4]; };
-template <> struct Raw<float> { float4 q[4][2]; };
-
-__device__ __forceinline__ void raw_load(const uint16_t *p, Raw<uint16_t> &r, int k) {
-    r.q[k] = *(const uint4 *)p;
-}
-__device__ __forceinline__ void raw_load(const float *p, Raw<float> &r, int k) {
-    r.q[k][0] = *(const float4 *)p;
-    r.q[k][1] = *(const float4 *)(p + 4);
-}
-__device__ __forceinline__ void raw_unpack(const Raw<uint16_t> &r, int k, float *x) {
-    const uint32_t u[4] = {r.q[k].x, r.q[k].y, r.q[k].z, r.q[k].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        x[2 * e] = __uint_as_float(u[e] << 16);
-        x[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
-    }
-}
-__device__ __forceinline__ void raw_unpack(const Raw<float> &r, int k, float *x) {
-    x[0] = r.q[k][0].x; x[1] = r.q[k][0].y; x[2] = r.q[k][0].z; x[3] = r.q[k][0].w;
-    x[4] = r.q[k][1].x; x[5] = r.q[k][1].y; x[6] = r.q[k][1].z; x[7] = r.q[k][1].w;
-}
-
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Lane permutations within groups of 4 lanes (DPP quad_perm).
-template <int CTRL>
-__device__ __forceinline__ float quad_perm(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
-}
-__device__ __forceinline__ float quad_bcast(float v, int k) {   // value of quad lane k
-    switch (k) {
-    case 0: return quad_perm<0x00>(v);
-    case 1: return quad_perm<0x55>(v);
-    case 2: return quad_perm<0xaa>(v);
-    default: return quad_perm<0xff>(v);
-    }
-}
-__device__ __forceinline__ float quad_sum(float v) {
-    v += quad_perm<0xb1>(v);      // lanes ^1
-    v += quad_perm<0x4e>(v);      // lanes ^2
-    return v;
-}
-
-// 16x16 product over K = 64 on MFMA: D[m][n] = sum_j A_m[j] B_n[j], where this
-// lane supplies row m = lane % 16 of A (arow) and row n = lane % 16 of B (brow).
-__device__ __forceinline__ f32x4 rows_product(const float *arow, const float *brow, int kq) {
-    f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const float4 a = *(const float4 *)(arow + 16 * g + 4 * kq);
-        const float4 b = *(const float4 *)(brow + 16 * g + 4 * kq);
-        d = mfma4(a.x, b.x, d); d = mfma4(a.y, b.y, d);
-        d = mfma4(a.z, b.z, d); d = mfma4(a.w, b.w, d);
-    }
-    return d;
-}
 
 template <typename TI, int NMW>
 __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdArgs p, int32_t units) {
@@ -289,7 +228,7 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
     // per wave. Loads are issued one chunk ahead, unconditionally (chunk index
     // and token rows clamped into the sequence), so that the registers in
     // flight have exactly one definition per iteration.
-    Raw<TI> raw;
+    Raw<TI, 4> raw;
     const TI *sp[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {

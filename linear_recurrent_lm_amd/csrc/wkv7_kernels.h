@@ -27,6 +27,7 @@ struct BwdArgs {
     const float *ds_out;
     void *dr, *dw, *dk, *dv, *da, *db;
     float *ds0;
+    float *ws;                       // per-slot dS_C of the sweep ([slots][H][N][N] fp32)
     const void *staged[8];           // filled by the launcher: r w k a b v dy, null
 };
 
@@ -40,6 +41,9 @@ struct DecArgs {
 };
 
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
+// Backward, first pass: dS_C of every chunk into a.ws, and a.ds0.
+hipError_t launch_backward_sweep(const BwdArgs &a, hipStream_t stream);
+// Backward, second pass: per-chunk gradients from a.ckpt and a.ws.
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecArgs &a, hipStream_t stream);
 

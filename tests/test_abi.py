@@ -106,7 +106,9 @@ def test_checkpoint_slots():
 
 
 def test_workspace_query():
-    assert W.wkv7_workspace_bytes(4, 64, 8, 1) >= 0
+    # one fp32 64x64 state-gradient slot per checkpoint slot and head
+    assert W.wkv7_workspace_bytes(4, 64, 8, 1) == 4 * 4 * 8 * 64 * 64 * 4
+    assert W.wkv7_workspace_bytes(3, 33, 2, 0) == 9 * 2 * 64 * 64 * 4
     n = ctypes.c_size_t()
     assert W.lib().wkv7_workspace_bytes(ctypes.byref(desc(N=48)), ctypes.byref(n)) == UNSUPPORTED
 
