@@ -17,23 +17,36 @@
 //     dV   = K^ dS_C^T + M_rk^T dY + L_ak^T drhs
 //     dA^ = drhs S_0, dR^ = dY S_0, dB^ = X dS_C, dK^ = V dS_C
 //     dL_ab = drhs X^T, dL_ak = drhs V^T (strictly lower), dM_rb = dY X^T,
-//     dM_rk = dY V^T (lower)
-// followed by the chain rule through the decay products. The 16x16 matrices
-// use the forward's 4-token sub-chunk factorisation (rows A' = a F_ex,
-// R' = r F_in and b/k "versions" b_s V_s, k_s V_s), so their gradients with
-// respect to r, a, b, k are weighted sums of those rows. The decay gradient
-// is assembled as u_m = w_m dw_m from the log-derivatives of every product
-// that contains w_m (prefix gamma, suffix D_{15,s}, and the pair decays of
-// the 16x16 matrices, whose contribution is a sum over the (s, t) pairs that
-// straddle m), then dw = u / w. The whole backward uses w' = max(w, 2^-30),
-// so dw is finite at w = 0 and equals the gradient there to within the clamp.
+//     dM_rk = dY V^T (lower).
+// The 16x16 matrices are built as in the forward: the pairs in different
+// 4-token sub-chunks are two 16x16x64 MFMA products D = A_rows B_rows^T of
+// rows scaled to shared split points (tokens 8, and 4/12), the pairs inside a
+// sub-chunk are dot products of a_t F_ex(t) (r_t F_in(t)) with b_s / F_s. Their
+// gradients follow the same split: with dD the matrix gradients gathered in
+// the product's index map, dA_rows = dD B_rows and dB_rows = dD^T A_rows (two
+// more MFMA products per tile), scaled back by each row's decay factor; the
+// within-sub-chunk pairs are short VALU sums.
+//
+// The decay gradient is assembled as u_m = w_m dw_m, the sum of every decay
+// product that contains w_m times its gradient, then dw = u / w. For the
+// chunk-level rows these are sums of a_t dA^_t gamma_{t-1} over t > m, of
+// r_t dR^_t gamma_t over t >= m, of (b_s dB^_s + k_s dK^_s) D_{15,s} over s < m,
+// and dgamma_C gamma_C. For the pairs (t, s) of a split-point block with split
+// R, the pairs that contain w_m (s < m <= t for M, s < m < t for L) are, for
+// m >= R, all pairs of the rows t >= m: sum_{t >= m} r_t dr_t + sum_{t > m}
+// a_t da_t over the block's row gradients; for m < R, all pairs of the columns
+// s < m: sum_{s < m} b_s db_s + k_s dk_s over the block's column gradients.
+// Pairs inside m's own sub-chunk are summed directly. Every term carries w_m,
+// so nothing cancels when w_m is tiny. The backward uses w' = max(w, 2^-30)
+// throughout, so dw is finite at w = 0 and equals the gradient there to
+// within the clamp.
 //
 // One 512-thread workgroup (8 waves) per (sequence, head, chunk group). 16x64
 // chunk matrices and the two 64x64 states live in LDS, row-major; MFMA
 // operands are 16-byte loads along the contraction index where the layout
-// allows it. Waves w and w+4 share a SIMD and take complementary (MFMA and
-// VALU) work in each phase.
+// allows it. Waves w and w+4 share a SIMD and take complementary work.
 #include "wkv7_kernels.h"
+#include "wkv7_mfma.h"
 
 namespace wkv7 {
 namespace {
@@ -44,32 +57,34 @@ constexpr int LD = 68;                            // row pitch of 16x64 / 64x64 
 constexpr float kMinW = 9.313225746154785e-10f;   // 2^-30
 
 // LDS layout (floats)
-constexpr int O_IN = 0;                      // [7][16][LD] r w k a b v dy
-constexpr int O_Q = O_IN + 7 * 16 * LD;         // [32][LD] A^ (0..15), R^ (16..31)
+constexpr int O_IN = 0;                      // [7][16][LD] r w k a b v dy (w clamped)
+constexpr int O_Q = O_IN + 7 * 16 * LD;      // [32][LD] A^ (0..15), R^ (16..31); with B^, K^ later u terms 6..8
 constexpr int O_BK = O_Q + 32 * LD;          // [32][LD] B^, K^
-constexpr int O_AR = O_BK + 32 * LD;         // [32][LD] A', R'
-constexpr int O_BV = O_AR + 32 * LD;         // [40][LD] b versions
-constexpr int O_KV = O_BV + 40 * LD;         // [40][LD] k versions
-constexpr int O_VV = O_KV + 40 * LD;         // [40][LD] bare decay versions
-constexpr int O_S0 = O_VV + 40 * LD;         // [64][LD] S_0
-constexpr int O_DS = O_S0 + 64 * LD;         // [64][LD] dS_C
+constexpr int O_AR = O_BK + 32 * LD;         // [32][LD] A'_t = a_t F_ex(t), R'_t = r_t F_in(t)
+constexpr int O_AWR = O_AR + 32 * LD;        // [8][LD]  A'_t W_2, R'_t W_2 for t = 12..15
+constexpr int O_BD = O_AWR + 8 * LD;         // [16][LD] b_s / F_s
+constexpr int O_KD = O_BD + 16 * LD;         // [16][LD] k_s / F_s
+constexpr int O_BL = O_KD + 16 * LD;         // [32][LD] b, k rows scaled to the split points
+constexpr int O_S0 = O_BL + 32 * LD;         // [64][LD] S_0; later [4][16][LD] the pair products Z
+constexpr int O_DS = O_S0 + 64 * LD;         // [64][LD] dS_C; with X, drhs later u terms 0..5
 constexpr int O_X = O_DS + 64 * LD;          // [16][LD] X[t][i]
 constexpr int O_DR = O_X + 16 * LD;          // [16][LD] drhs[t][i]
 constexpr int O_G = O_DR + 16 * LD;          // [4][16][LD] dA^, dR^, dB^, dK^ ([t][j])
-constexpr int O_M = O_G + 64 * LD;           // [9][256] Lab Lak Mrb Mrk W dLab dLak dMrb dMrk
-constexpr int O_GC = O_M + 9 * 256;          // [64] gamma_C
+constexpr int O_M = O_G + 64 * LD;           // [11][256] Lab Lak Mrb Mrk W dLab dLak dMrb dMrk dD1 dD2
+constexpr int O_GC = O_M + 11 * 256;         // [64] gamma_C
 constexpr int O_DGC = O_GC + 64;             // [64] d gamma_C
 constexpr int LDS_FLOATS = O_DGC + 64;
 static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
 
 enum { IR = 0, IW, IK, IA, IB, IV, IDY };
-enum { MLAB = 0, MLAK, MMRB, MMRK, MW, MDLAB, MDLAK, MDMRB, MDMRK };
-
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ int ver_off(int p) { return 2 * p * (p + 1); }
+// dD1, dD2: the matrix gradients gathered in the index maps of the two
+// split-point products (entries outside a map stay zero)
+enum { MLAB = 0, MLAK, MMRB, MMRK, MW, MDLAB, MDLAK, MDMRB, MDMRK, MDD1, MDD2 };
+enum { ZA1 = 0, ZB1, ZA2, ZB2 };             // pair products: dA_rows, dB_rows of tiles 1, 2
+// u terms per token ([16][LD] each): chunk parts a dA^ g, r dR^ g, (b dB^ + k dK^) D;
+// block row parts (a da, r dr) of blocks R = 4 / 8 (rows 4..15) and R = 12
+// (rows 12..15); block column parts (b db + k dk) of R = 8 (0..7) and R = 4 / 12 (0..3, 8..11)
+enum { UCHA = 0, UCHR, UCHC, UR12A, UR12R, UR3A, UR3R, UC2, UC13, kUTerms };
 
 // acc[m][n] += sum_k A[m][k] B[k][n] with A row-major (pitch lda) and B given
 // transposed, Bt[n][k] row-major (pitch ldb): both operands 16-byte loads.
@@ -108,189 +123,45 @@ __device__ __forceinline__ f32x4 mm_TB(f32x4 acc, const float *A, int lda, const
     return acc;
 }
 
-template <typename TI> struct Raw;
-template <> struct Raw<uint16_t> { uint4 q[2]; };
-template <> struct Raw<float> { float4 q[2][2]; };
-
-__device__ __forceinline__ void raw_load(const uint16_t *p, Raw<uint16_t> &r, int k) {
-    r.q[k] = *(const uint4 *)p;
-}
-__device__ __forceinline__ void raw_load(const float *p, Raw<float> &r, int k) {
-    r.q[k][0] = *(const float4 *)p;
-    r.q[k][1] = *(const float4 *)(p + 4);
-}
-__device__ __forceinline__ void raw_unpack(const Raw<uint16_t> &r, int k, float *x) {
-    const uint32_t u[4] = {r.q[k].x, r.q[k].y, r.q[k].z, r.q[k].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        x[2 * e] = __uint_as_float(u[e] << 16);
-        x[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+// Index map of the two split-point products (the forward's tiles): output
+// element D[m][n] is the (t, s) entry of L (a rows, isA) or M (r rows), with
+// b (isB) or k columns. Tile 1 (split at 8): m < 8 a rows t = 8+m, m >= 8 r
+// rows t = m; n < 8 b rows s = n, n >= 8 k rows s = n-8. Tile 2 (splits at 4
+// and 12): a rows where m & 4 == 0 with t = 4+m, else r rows t = m; b columns
+// where n & 4 == 0 with s = n, else k columns s = n-4; only m, n on the same
+// side of 8 are valid.
+struct TileEntry { bool valid, isA, isB; int t, s; };
+__device__ __forceinline__ TileEntry tile_entry(int tile, int m, int n) {
+    TileEntry e;
+    if (tile == 0) {
+        e.isA = m < 8; e.t = e.isA ? 8 + m : m;
+        e.isB = n < 8; e.s = e.isB ? n : n - 8;
+        e.valid = true;
+    } else {
+        e.isA = (m & 4) == 0; e.t = e.isA ? 4 + m : m;
+        e.isB = (n & 4) == 0; e.s = e.isB ? n : n - 4;
+        e.valid = (m < 8) == (n < 8);
     }
+    return e;
 }
-__device__ __forceinline__ void raw_unpack(const Raw<float> &r, int k, float *x) {
-    x[0] = r.q[k][0].x; x[1] = r.q[k][0].y; x[2] = r.q[k][0].z; x[3] = r.q[k][0].w;
-    x[4] = r.q[k][1].x; x[5] = r.q[k][1].y; x[6] = r.q[k][1].z; x[7] = r.q[k][1].w;
-}
-
-// Version rows of source sub-chunk Q (b_s V, k_s V and the bare factor V) for
-// every target sub-chunk p >= Q; V = prod_{s<u<4p} w_u for p > Q, 1 / F_s for p = Q.
-template <int Q>
-__device__ __forceinline__ void versions(const float *wv, const float *W, const float *s_in,
-                                         float *s_bv, float *s_kv, float *s_vv, int j) {
-    float suf[4];
-    suf[3] = 1.f;
-    suf[2] = wv[4 * Q + 3];
-    suf[1] = wv[4 * Q + 2] * suf[2];
-    suf[0] = wv[4 * Q + 1] * suf[1];
-    float F = 1.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int s = 4 * Q + e;
-        F *= wv[s];
-        const float bs = s_in[(IB * 16 + s) * LD + j];
-        const float ks = s_in[(IK * 16 + s) * LD + j];
-        const float inv = __builtin_amdgcn_rcpf(F);
-        const int r0 = (ver_off(Q) + s) * LD + j;
-        s_vv[r0] = inv;
-        s_bv[r0] = bs * inv;
-        s_kv[r0] = ks * inv;
-        float m = suf[e];
-#pragma unroll
-        for (int pp = Q + 1; pp < 4; ++pp) {
-            const int r1 = (ver_off(pp) + s) * LD + j;
-            s_vv[r1] = m;
-            s_bv[r1] = bs * m;
-            s_kv[r1] = ks * m;
-            m *= W[pp];
-        }
-    }
+__device__ __forceinline__ int tile_matrix(const TileEntry &e, int base) {
+    return base + (e.isA ? (e.isB ? 0 : 1) : (e.isB ? 2 : 3));   // Lab Lak Mrb Mrk order
 }
 
-struct AsmArgs {
-    const float *s_in, *s_AR, *s_BV, *s_KV, *s_VV, *s_G, *s_M, *s_dgC;
-    float *s_U;          // [8][16][LD] partial pair parts of u (aliases S_0 and dS_C)
-    int j, wave;
-};
-
-// Pair parts for rows t in {T0, T1} of key column j: the prefix sums over s
-// of zl_s = dL_ab[t,s] b_s V + dL_ak[t,s] k_s V and zm_s (same with dM) give
-// the da_t, dr_t pair parts and the straddling-pair part of u (A'_t zl_s for
-// s < m < t, R'_t zm_s for s < m <= t); db_s, dk_s pair parts for s in {T0, T1}.
-template <int T0, int T1>
-__device__ __forceinline__ void assemble_rows(const AsmArgs &g, float (&st5)[2][5]) {
-    constexpr int TK[2] = {T0, T1};
-    const int j = g.j;
-    const float *Mdlab = g.s_M + MDLAB * 256, *Mdlak = g.s_M + MDLAK * 256;
-    const float *Mdmrb = g.s_M + MDMRB * 256, *Mdmrk = g.s_M + MDMRK * 256;
-    float um[16];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) um[m] = 0.f;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int t = TK[q];
-        const int pv = ver_off(t >> 2);
-        const float ap = g.s_AR[t * LD + j], rp = g.s_AR[(16 + t) * LD + j];
-        float cl = 0.f, cm = 0.f;
-#pragma unroll
-        for (int s = 0; s <= t; ++s) {
-            const float bvs = g.s_BV[(pv + s) * LD + j], kvs = g.s_KV[(pv + s) * LD + j];
-            if (s < t) cl += Mdlab[t * 16 + s] * bvs + Mdlak[t * 16 + s] * kvs;
-            cm += Mdmrb[t * 16 + s] * bvs + Mdmrk[t * 16 + s] * kvs;
-            if (s + 1 < t) um[s + 1] = fmaf(ap, cl, um[s + 1]);
-            if (s + 1 <= t && s + 1 < 16) um[s + 1] = fmaf(rp, cm, um[s + 1]);
-        }
-        st5[q][2] = cl;          // da pair part (times F_ex later)
-        st5[q][0] = cm;          // dr pair part (times F_in later)
-    }
-#pragma unroll
-    for (int m = 0; m < 16; ++m) g.s_U[(g.wave * 16 + m) * LD + j] = um[m];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int s = TK[q];
-        float accb = 0.f, acck = 0.f;
-#pragma unroll
-        for (int t = s; t < 16; ++t) {
-            const float vv = g.s_VV[(ver_off(t >> 2) + s) * LD + j];
-            const float ap = g.s_AR[t * LD + j], rp = g.s_AR[(16 + t) * LD + j];
-            const float cb = (t > s ? Mdlab[t * 16 + s] * ap : 0.f) + Mdmrb[t * 16 + s] * rp;
-            const float ck = (t > s ? Mdlak[t * 16 + s] * ap : 0.f) + Mdmrk[t * 16 + s] * rp;
-            accb = fmaf(cb, vv, accb);
-            acck = fmaf(ck, vv, acck);
-        }
-        st5[q][3] = accb;
-        st5[q][4] = acck;
-    }
+// The inverse maps: store the gradient v of entry (t, s) of L (isA) or M,
+// b (isB) or k column, at its place in dD1 and dD2, if it has one.
+__device__ __forceinline__ void tile_scatter(float *sM, bool isA, bool isB, int t, int s, float v) {
+    if (t >= 8 && s < 8) sM[MDD1 * 256 + (isA ? t - 8 : t) * 16 + (isB ? s : s + 8)] = v;
+    if (((t & 12) == 4 && s < 4) || ((t & 12) == 12 && (s & 12) == 8))
+        sM[MDD2 * 256 + (isA ? t - 4 : t) * 16 + (isB ? s : s + 4)] = v;
 }
 
-// Chunk-level parts and the final per-token gradients of key column j:
-//   u_m = pair part + sum_{t>=m} dR^_t r_t gamma_t + sum_{t>m} dA^_t a_t gamma_{t-1}
-//         + sum_{s<m} (dB^_s b_s + dK^_s k_s) D_{15,s} + dgamma_C gamma_C,  dw = u / w
-//   da = dA^ gamma_{t-1} + F_ex pair, dr = dR^ gamma_t + F_in pair,
-//   db = dB^ D_{15,t} + pair, dk = dK^ D_{15,t} + pair
-template <int T0, int T1>
-__device__ __forceinline__ void assemble_out(const AsmArgs &g, float (&st5)[2][5]) {
-    constexpr int TK[2] = {T0, T1};
-    const int j = g.j;
-    const float *wcol = g.s_in + IW * 16 * LD + j;
-    float wv[16], gam[16], gprev[16], dend[16], fex[16], fin[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) wv[t] = wcol[t * LD];
-    {
-        float gg = 1.f;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) { gprev[t] = gg; gg *= wv[t]; gam[t] = gg; }
-        float d = 1.f;
-#pragma unroll
-        for (int s = 15; s >= 0; --s) { dend[s] = d; d *= wv[s]; }
-#pragma unroll
-        for (int sc = 0; sc < 4; ++sc) {
-            float f = 1.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 4 * sc + e;
-                fex[t] = f; f *= wv[t]; fin[t] = f;
-            }
-        }
-    }
-    const float *gA = g.s_G, *gR = g.s_G + 16 * LD, *gB = g.s_G + 32 * LD, *gK = g.s_G + 48 * LD;
-    float suf[17], pre[17];
-    suf[16] = 0.f;
-#pragma unroll
-    for (int t = 15; t >= 0; --t) {
-        float x = gR[t * LD + j] * g.s_in[(IR * 16 + t) * LD + j] * gam[t];
-        if (t < 15) x += gA[(t + 1) * LD + j] * g.s_in[(IA * 16 + t + 1) * LD + j] * gprev[t + 1];
-        suf[t] = suf[t + 1] + x;
-    }
-    pre[0] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 16; ++s)
-        pre[s + 1] = pre[s] + (gB[s * LD + j] * g.s_in[(IB * 16 + s) * LD + j] +
-                               gK[s * LD + j] * g.s_in[(IK * 16 + s) * LD + j]) * dend[s];
-    const float dgc = g.s_dgC[j] * gam[15];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int t = TK[q];
-        float up = 0.f;
-#pragma unroll
-        for (int w8 = 0; w8 < 8; ++w8) up += g.s_U[(w8 * 16 + t) * LD + j];
-        const float uval = up + suf[t] + pre[t] + dgc;
-        const float dr = gR[t * LD + j] * gam[t] + fin[t] * st5[q][0];
-        const float da = gA[t * LD + j] * gprev[t] + fex[t] * st5[q][2];
-        const float db = gB[t * LD + j] * dend[t] + st5[q][3];
-        const float dk = gK[t * LD + j] * dend[t] + st5[q][4];
-        st5[q][0] = dr;
-        st5[q][1] = uval / wv[t];
-        st5[q][2] = da;
-        st5[q][3] = db;
-        st5[q][4] = dk;
-    }
-}
+template <int V> struct IC { static constexpr int value = V; };
 
 template <typename TI>
 __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32_t units) {
     extern __shared__ __align__(16) float sm[];
-    // Workgroup -> (unit, group of kChunksPerGroup chunks); chunks are
-    // independent given S_0 (checkpoint) and dS_C (first pass).
+    // Workgroup -> (unit, group of kChunksPerGroup chunks).
     const int unit = blockIdx.x % units;
     const int grp = blockIdx.x / units;
     const int H = p.seg.H;
@@ -312,41 +183,48 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
     };
     const int w4 = wave & 3;                         // 16-row / 16-column tile of this wave
     const bool lo = wave < 4;
+    const int it = w4;
 
     float *s_in = sm + O_IN;
-    float *s_Q = sm + O_Q, *s_BK = sm + O_BK, *s_AR = sm + O_AR;
-    float *s_BV = sm + O_BV, *s_KV = sm + O_KV, *s_VV = sm + O_VV;
+    float *s_Q = sm + O_Q, *s_BK = sm + O_BK;
+    float *s_AR = sm + O_AR, *s_AWR = sm + O_AWR, *s_BD = sm + O_BD, *s_KD = sm + O_KD, *s_BL = sm + O_BL;
     float *s_S0 = sm + O_S0, *s_DS = sm + O_DS, *s_X = sm + O_X, *s_DR = sm + O_DR;
     float *s_G = sm + O_G, *s_M = sm + O_M, *s_gC = sm + O_GC, *s_dgC = sm + O_DGC;
+    float *s_Z = s_S0;                               // reuses S_0 once consumed
+    // u terms reuse dS_C, X, drhs (6 arrays) and A^, R^, B^, K^ (3 arrays) once consumed
+    auto s_U = [&](int term) { return sm + (term < 6 ? O_DS + term * 16 * LD : O_Q + (term - 6) * 16 * LD); };
     const float *sV = s_in + IV * 16 * LD, *sDY = s_in + IDY * 16 * LD;
     const float *Mlak = s_M + MLAK * 256, *Mmrb = s_M + MMRB * 256, *Mmrk = s_M + MMRK * 256;
     const float *Mw = s_M + MW * 256;
 
     const int64_t ts = (int64_t)H * kN;
     const int64_t base = (u.start * H + h) * kN;
-    const int64_t sbase = ((int64_t)sq * H + h) * (kN * kN);
 
-    const int it = w4;
-
-    // Staging: element groups g = tid + 512k (k = 0, 1) of 7 streams x 16
-    // tokens x 8 groups of 8; stream g >> 7 is uniform per wave.
     const int nch = (u.len + kChunk - 1) / kChunk;
     const int c_lo = grp * kChunksPerGroup;
     const int c_hi = min(nch, c_lo + kChunksPerGroup);
     if (c_lo >= c_hi) return;
-    Raw<TI> raw;
+
+    // Upper parts of L_ab, L_ak, M_rb, M_rk and the entries of dD2 outside
+    // its index map are never written and stay zero.
+    for (int q = tid; q < 4 * 256; q += kThreads) s_M[q] = 0.f;
+    for (int q = tid; q < 256; q += kThreads) s_M[MDD2 * 256 + q] = 0.f;
+
+    // Staging: element groups g = tid + 512k (k = 0, 1) of 7 streams x 16
+    // tokens x 8 groups of 8; stream g >> 7 is uniform per wave. Loads are
+    // issued one chunk ahead, unconditionally (token rows clamped into the
+    // sequence), so the registers in flight have one definition per
+    // iteration; groups of a missing stream (dy == NULL, or past the seven
+    // streams) load the w row instead and stage as fill.
+    Raw<TI, 2> raw;
     float4 ckr0, ckr1, dsr0, dsr1;              // checkpoint S_0 and dS_C of the chunk in flight
-    const TI *sp[2];                            // stream of each staged group (uniform)
+    const TI *sp[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int st = __builtin_amdgcn_readfirstlane((tid + k * kThreads) >> 7);
         const void *vp = p.staged[st];
         sp[k] = vp ? (const TI *)vp + base : nullptr;
     }
-    // Loads are issued one chunk ahead, unconditionally (token rows clamped
-    // into the sequence), so the registers in flight have one definition per
-    // iteration; groups of a missing stream (dy == NULL, or past the seven
-    // streams) load the w row instead and stage as fill.
     const TI *wrow = (const TI *)p.w + base;
     auto issue = [&](int cc) {
         const int Lc = min(kChunk, u.len - cc * kChunk);
@@ -372,8 +250,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         lds_barrier();
         relane();
 
-        // ---- stage inputs (w clamped; identity tokens past the end), the
-        //      checkpoint S_0 and dS_C; then prefetch chunk c-1
+        // ---- P0: stage inputs (w clamped; identity tokens past the end), the
+        //      checkpoint S_0 and dS_C; then prefetch the next chunk
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int g = tid + k * kThreads;
@@ -396,162 +274,235 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 *(float4 *)(d + 4) = make_float4(x[4], x[5], x[6], x[7]);
             }
         }
-        {
-            *(float4 *)(s_S0 + (tid >> 4) * LD + (tid & 15) * 4) = ckr0;
-            *(float4 *)(s_S0 + ((tid + kThreads) >> 4) * LD + (tid & 15) * 4) = ckr1;
-            *(float4 *)(s_DS + (tid >> 4) * LD + (tid & 15) * 4) = dsr0;
-            *(float4 *)(s_DS + ((tid + kThreads) >> 4) * LD + (tid & 15) * 4) = dsr1;
-        }
+        *(float4 *)(s_S0 + (tid >> 4) * LD + (tid & 15) * 4) = ckr0;
+        *(float4 *)(s_S0 + ((tid + kThreads) >> 4) * LD + (tid & 15) * 4) = ckr1;
+        *(float4 *)(s_DS + (tid >> 4) * LD + (tid & 15) * 4) = dsr0;
+        *(float4 *)(s_DS + ((tid + kThreads) >> 4) * LD + (tid & 15) * 4) = dsr1;
         issue(max(c - 1, c_lo));
         lds_barrier();
         relane();
 
-        // ---- decay products and operand rows: one role per wave over the 64
-        //      key columns (lane = column)
+        // ---- P1: per-column rows, one role per wave (lane = key column j); each
+        //      role reads its inputs before its first store
         {
             const int role = __builtin_amdgcn_readfirstlane(wave), j = lane;
-            const float *w_ = s_in + IW * 16 * LD + j;
-            if (role == 0) {             // A^, R^, gamma_C
+            const int st = role == 0 || role == 4 ? IA : role == 1 || role == 5 ? IR
+                         : role == 2 || role == 6 ? IB : IK;
+            float wv[16], xv[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                wv[t] = s_in[(IW * 16 + t) * LD + j];
+                xv[t] = s_in[(st * 16 + t) * LD + j];
+            }
+            if (role == 0) {             // A^_t = a_t gamma_{t-1}; gamma_C
                 float g = 1.f;
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    s_Q[t * LD + j] = s_in[(IA * 16 + t) * LD + j] * g;
-                    g *= w_[t * LD];
-                    s_Q[(16 + t) * LD + j] = s_in[(IR * 16 + t) * LD + j] * g;
-                }
+                for (int t = 0; t < 16; ++t) { xv[t] *= g; g *= wv[t]; }
+#pragma unroll
+                for (int t = 0; t < 16; ++t) s_Q[t * LD + j] = xv[t];
                 s_gC[j] = g;
-            } else if (role == 1) {      // B^, K^
+            } else if (role == 1) {      // R^_t = r_t gamma_t
+                float g = 1.f;
+#pragma unroll
+                for (int t = 0; t < 16; ++t) { g *= wv[t]; xv[t] *= g; }
+#pragma unroll
+                for (int t = 0; t < 16; ++t) s_Q[(16 + t) * LD + j] = xv[t];
+            } else if (role == 2 || role == 3) {   // B^_s, K^_s = x_s D_{15,s}
                 float d = 1.f;
 #pragma unroll
-                for (int s = 15; s >= 0; --s) {
-                    s_BK[s * LD + j] = s_in[(IB * 16 + s) * LD + j] * d;
-                    s_BK[(16 + s) * LD + j] = s_in[(IK * 16 + s) * LD + j] * d;
-                    d *= w_[s * LD];
-                }
-            } else if (role == 2) {      // d gamma_C[j] = sum_i dS_C[i][j] S_0[i][j]
-                float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll 8
-                for (int i = 0; i < 64; i += 2) {
-                    acc0 = fmaf(s_DS[i * LD + j], s_S0[i * LD + j], acc0);
-                    acc1 = fmaf(s_DS[(i + 1) * LD + j], s_S0[(i + 1) * LD + j], acc1);
-                }
-                s_dgC[j] = acc0 + acc1;
-            } else if (role == 3) {      // A' = a F_ex, R' = r F_in
+                for (int s = 15; s >= 0; --s) { xv[s] *= d; d *= wv[s]; }
+#pragma unroll
+                for (int s = 0; s < 16; ++s) s_BK[(16 * (role - 2) + s) * LD + j] = xv[s];
+            } else if (role == 4 || role == 5) {   // A' = a F_ex, R' = r F_in; times W_2 for t >= 12
+                const int inc = role - 4;
 #pragma unroll
                 for (int sc = 0; sc < 4; ++sc) {
                     float f = 1.f;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int t = 4 * sc + e;
-                        s_AR[t * LD + j] = s_in[(IA * 16 + t) * LD + j] * f;
-                        f *= w_[t * LD];
-                        s_AR[(16 + t) * LD + j] = s_in[(IR * 16 + t) * LD + j] * f;
+                        if (inc) f *= wv[t];
+                        xv[t] *= f;
+                        if (!inc) f *= wv[t];
                     }
                 }
-            } else {                     // b, k, bare versions of source sub-chunk role - 4
-                float wv[16], W[4];
+                const float W2 = (wv[8] * wv[9]) * (wv[10] * wv[11]);
 #pragma unroll
-                for (int t = 0; t < 16; ++t) wv[t] = w_[t * LD];
+                for (int t = 0; t < 16; ++t) s_AR[(16 * inc + t) * LD + j] = xv[t];
 #pragma unroll
-                for (int sc = 0; sc < 4; ++sc)
-                    W[sc] = (wv[4 * sc] * wv[4 * sc + 1]) * (wv[4 * sc + 2] * wv[4 * sc + 3]);
-                if (role == 4) versions<0>(wv, W, s_in, s_BV, s_KV, s_VV, j);
-                else if (role == 5) versions<1>(wv, W, s_in, s_BV, s_KV, s_VV, j);
-                else if (role == 6) versions<2>(wv, W, s_in, s_BV, s_KV, s_VV, j);
-                else versions<3>(wv, W, s_in, s_BV, s_KV, s_VV, j);
-            }
-        }
-        lds_barrier();
-        relane();
-
-        // ---- waves 0-3: P_a = A^ S_0^T (value rows 16*w4..). waves 4-7: the
-        //      four 16x16 matrices on VALU (one pair of dots per thread) and, on
-        //      MFMA, dR^ = dY S_0 and dK^ = V dS_C for key columns 16*w4..
-        f32x4 pa = {0.f, 0.f, 0.f, 0.f};
-        if (lo) {
-            pa = mm_AtBt(pa, s_Q, LD, s_S0 + 16 * it * LD, LD, l16, kq, 64);
-        } else {
-            const int jc = 16 * w4;
-            f32x4 g1 = {0.f, 0.f, 0.f, 0.f}, g3 = g1;
-            g1 = mm_AtB(g1, sDY, LD, s_S0 + jc, LD, l16, kq, 64);
-            g3 = mm_AtB(g3, sV, LD, s_DS + jc, LD, l16, kq, 64);
-            const int item = tid - 256;
-            int t, s, mat;
-            if (item < 120) {
-                t = 1;
-                while ((t + 1) * t / 2 <= item) ++t;
-                s = item - t * (t - 1) / 2;
-                mat = 0;
-            } else {
-                const int mi = item - 120;
-                t = 0;
-                while ((t + 1) * (t + 2) / 2 <= mi) ++t;
-                s = mi - t * (t + 1) / 2;
-                mat = 1;
-            }
-            const int vrow = ver_off(t >> 2) + s;
-            const float *ar = s_AR + (16 * mat + t) * LD;
-            const float *bv = s_BV + vrow * LD;
-            const float *kv = s_KV + vrow * LD;
-            float db0 = 0.f, db1 = 0.f, dk0 = 0.f, dk1 = 0.f;
+                for (int e = 0; e < 4; ++e) s_AWR[(4 * inc + e) * LD + j] = xv[12 + e] * W2;
+            } else {                     // b (6), k (7) rows: x_s / F_s and scaled to the split points
+                const int ko = role - 6;
+                float od[16], os[12];
 #pragma unroll
-            for (int j = 0; j < 64; j += 8) {
-                const float4 x0 = *(const float4 *)(ar + j), x1 = *(const float4 *)(ar + j + 4);
-                const float4 b0 = *(const float4 *)(bv + j), b1 = *(const float4 *)(bv + j + 4);
-                const float4 k0 = *(const float4 *)(kv + j), k1 = *(const float4 *)(kv + j + 4);
-                db0 = fmaf(x0.x, b0.x, db0); db1 = fmaf(x0.y, b0.y, db1);
-                db0 = fmaf(x0.z, b0.z, db0); db1 = fmaf(x0.w, b0.w, db1);
-                db0 = fmaf(x1.x, b1.x, db0); db1 = fmaf(x1.y, b1.y, db1);
-                db0 = fmaf(x1.z, b1.z, db0); db1 = fmaf(x1.w, b1.w, db1);
-                dk0 = fmaf(x0.x, k0.x, dk0); dk1 = fmaf(x0.y, k0.y, dk1);
-                dk0 = fmaf(x0.z, k0.z, dk0); dk1 = fmaf(x0.w, k0.w, dk1);
-                dk0 = fmaf(x1.x, k1.x, dk0); dk1 = fmaf(x1.y, k1.y, dk1);
-                dk0 = fmaf(x1.z, k1.z, dk0); dk1 = fmaf(x1.w, k1.w, dk1);
-            }
-            s_M[(2 * mat) * 256 + t * 16 + s] = db0 + db1;
-            s_M[(2 * mat + 1) * 256 + t * 16 + s] = dk0 + dk1;
+                for (int q = 0; q < 4; ++q) {
+                    float F = 1.f, suf = 1.f;        // suf = prod_{s<u<4q+4} w_u, built downwards
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tt = 4 * kq + r;
-                s_G[(1 * 16 + tt) * LD + jc + l16] = g1[r];
-                s_G[(3 * 16 + tt) * LD + jc + l16] = g3[r];
-            }
-        }
-        lds_barrier();
-        relane();
-
-        // ---- W = (I - L_ab)^-1 (wave 0, 16 lanes); upper parts cleared (wave 1);
-        //      dM_rk = dY V^T (wave 2; lower part incl. the diagonal)
-        if (wave == 0) {
-            if (lane < 16) {
-                float x[16];
+                    for (int e = 3; e >= 0; --e) {
+                        if (q < 3) os[4 * q + e] = xv[4 * q + e] * suf;
+                        suf *= wv[4 * q + e];
+                    }
 #pragma unroll
-                for (int t = 0; t < 16; ++t) x[t] = t == lane ? 1.f : 0.f;
-#pragma unroll
-                for (int s2 = 0; s2 < 15; ++s2) {
-#pragma unroll
-                    for (int t = s2 + 1; t < 16; ++t) x[t] = fmaf(s_M[MLAB * 256 + t * 16 + s2], x[s2], x[t]);
+                    for (int e = 0; e < 4; ++e) {
+                        F *= wv[4 * q + e];
+                        od[4 * q + e] = xv[4 * q + e] * __builtin_amdgcn_rcpf(F);
+                    }
                 }
+                const float W1 = (wv[4] * wv[5]) * (wv[6] * wv[7]);
+                float *dd = ko ? s_KD : s_BD;
 #pragma unroll
-                for (int t = 0; t < 16; ++t) s_M[MW * 256 + t * 16 + lane] = x[t];
-            }
-        } else if (wave == 1) {
-            const int m = lane >> 4, row = lane & 15;
-            const int first = m < 2 ? row : row + 1;
-            for (int c2 = first; c2 < 16; ++c2) s_M[m * 256 + row * 16 + c2] = 0.f;
-        } else if (wave == 2) {
-            f32x4 gm = {0.f, 0.f, 0.f, 0.f};
-            gm = mm_AtBt(gm, sDY, LD, sV, LD, l16, kq, 64);
+                for (int s = 0; s < 16; ++s) dd[s * LD + j] = od[s];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * kq + r;
-                s_M[MDMRK * 256 + t * 16 + l16] = l16 <= t ? gm[r] : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    s_BL[(8 * ko + e) * LD + j] = os[e] * W1;          // s = e scaled to 8
+                    s_BL[(16 + 4 * ko + e) * LD + j] = os[e];          // s = e scaled to 4
+                    s_BL[(8 * ko + 4 + e) * LD + j] = os[4 + e];       // s = 4+e scaled to 8
+                    s_BL[(24 + 4 * ko + e) * LD + j] = os[8 + e];      // s = 8+e scaled to 12
+                }
             }
         }
         lds_barrier();
         relane();
 
-        // ---- value side. waves 0-3 (rows 16*w4..): X = W (P_a + L_ak V);
+        // ---- P2: waves 0-3: P_a = A^ S_0^T (value rows 16*w4..) and dR^ = dY S_0
+        //      (key columns 16*w4..). Waves 4, 5: the split-point products;
+        //      waves 6, 7: the within-sub-chunk pairs; waves 4-7: dK^ = V dS_C
+        //      (key columns 16*(w-4)..); wave 6: dM_rk = dY V^T
+        f32x4 pa = {0.f, 0.f, 0.f, 0.f};
+        {
+            const int jc = 16 * w4;
+            if (lo) {
+                pa = mm_AtBt(pa, s_Q, LD, s_S0 + 16 * it * LD, LD, l16, kq, 64);
+                f32x4 g1 = {0.f, 0.f, 0.f, 0.f};
+                g1 = mm_AtB(g1, sDY, LD, s_S0 + jc, LD, l16, kq, 64);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s_G[(1 * 16 + 4 * kq + r) * LD + jc + l16] = g1[r];
+            } else {
+                if (wave < 6) {
+                    const int tile = wave - 4, m = l16;
+                    const float *arow, *brow;
+                    if (tile == 0) {
+                        arow = m < 4 ? s_AR + (8 + m) * LD : m < 8 ? s_AWR + (m - 4) * LD
+                             : m < 12 ? s_AR + (16 + m) * LD : s_AWR + (m - 8) * LD;
+                        brow = s_BL + l16 * LD;
+                    } else {
+                        arow = s_AR + ((m & 4) ? 16 + m : 4 + m) * LD;
+                        brow = s_BL + (16 + l16) * LD;
+                    }
+                    const f32x4 d = rows_product(arow, brow, kq);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const TileEntry e = tile_entry(tile, 4 * kq + r, l16);
+                        if (e.valid) s_M[tile_matrix(e, MLAB) * 256 + e.t * 16 + e.s] = d[r];
+                    }
+                } else {
+                    // 64 items (sub-chunk p, pair k) x 4 quarters of the 64 columns
+                    // = 256 units, two per lane of waves 6 and 7
+                    float db[2], dk[2];
+                    int tt[2], ss[2];
+                    bool lt[2];
+#pragma unroll
+                    for (int v = 0; v < 2; ++v) {
+                        const int unit_ = tid - 384 + 128 * v;
+                        const int item = unit_ >> 2, qtr = unit_ & 3;
+                        const int sc = item >> 4, kk = item & 15;
+                        int et, es;
+                        const bool isL = kk < 6;
+                        if (isL) {                 // s < t
+                            et = 1 + (kk >= 1) + (kk >= 3);
+                            es = kk - et * (et - 1) / 2;
+                        } else {                   // s <= t
+                            const int mi = kk - 6;
+                            et = (mi >= 1) + (mi >= 3) + (mi >= 6);
+                            es = mi - et * (et + 1) / 2;
+                        }
+                        const int t = 4 * sc + et, s = 4 * sc + es;
+                        const float *ar = s_AR + ((isL ? 0 : 16) + t) * LD + 16 * qtr;
+                        const float *bd = s_BD + s * LD + 16 * qtr;
+                        const float *kd = s_KD + s * LD + 16 * qtr;
+                        float b_ = 0.f, k_ = 0.f;
+#pragma unroll
+                        for (int jj = 0; jj < 16; jj += 4) {
+                            const float4 x = *(const float4 *)(ar + jj);
+                            const float4 b = *(const float4 *)(bd + jj);
+                            const float4 k4 = *(const float4 *)(kd + jj);
+                            b_ = fmaf(x.x, b.x, b_); k_ = fmaf(x.x, k4.x, k_);
+                            b_ = fmaf(x.y, b.y, b_); k_ = fmaf(x.y, k4.y, k_);
+                            b_ = fmaf(x.z, b.z, b_); k_ = fmaf(x.z, k4.z, k_);
+                            b_ = fmaf(x.w, b.w, b_); k_ = fmaf(x.w, k4.w, k_);
+                        }
+                        db[v] = b_; dk[v] = k_; tt[v] = t; ss[v] = s; lt[v] = isL;
+                    }
+#pragma unroll
+                    for (int v = 0; v < 2; ++v) {
+                        const float b_ = quad_sum(db[v]), k_ = quad_sum(dk[v]);
+                        if ((lane & 3) == 0) {
+                            const int o = tt[v] * 16 + ss[v];
+                            s_M[(lt[v] ? MLAB : MMRB) * 256 + o] = b_;
+                            s_M[(lt[v] ? MLAK : MMRK) * 256 + o] = k_;
+                        }
+                    }
+                    if (wave == 6) {
+                        f32x4 gm = {0.f, 0.f, 0.f, 0.f};
+                        gm = mm_AtBt(gm, sDY, LD, sV, LD, l16, kq, 64);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int t = 4 * kq + r;
+                            const float v = l16 <= t ? gm[r] : 0.f;
+                            s_M[MDMRK * 256 + t * 16 + l16] = v;
+                            tile_scatter(s_M, false, false, t, l16, v);
+                        }
+                    }
+                }
+                f32x4 g3 = {0.f, 0.f, 0.f, 0.f};
+                g3 = mm_AtB(g3, sV, LD, s_DS + jc, LD, l16, kq, 64);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s_G[(3 * 16 + 4 * kq + r) * LD + jc + l16] = g3[r];
+            }
+        }
+        lds_barrier();
+        relane();
+
+        // ---- P3: W = (I - L_ab)^-1 (wave 0: column c = lane / 4, rows
+        //      t = lane % 4 + 4i held by the 4 lanes of a quad, forward
+        //      substitution); d gamma_C[j] = sum_i dS_C[i][j] S_0[i][j] (wave 1)
+        if (wave == 0) {
+            const int col = lane >> 2, q = lane & 3;
+            float Lr[4][16], x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int s = 0; s < 16; s += 4) {
+                    const float4 v = *(const float4 *)(s_M + MLAB * 256 + (q + 4 * i) * 16 + s);
+                    Lr[i][s] = v.x; Lr[i][s + 1] = v.y; Lr[i][s + 2] = v.z; Lr[i][s + 3] = v.w;
+                }
+                x[i] = q + 4 * i == col ? 1.f : 0.f;
+            }
+#pragma unroll
+            for (int s = 0; s < 15; ++s) {
+                const float xs = quad_bcast(x[s >> 2], s & 3);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float nx = fmaf(Lr[i][s], xs, x[i]);
+                    x[i] = q + 4 * i > s ? nx : x[i];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_M[MW * 256 + (q + 4 * i) * 16 + col] = x[i];
+        } else if (wave == 1) {
+            const int j = lane;
+            float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll 8
+            for (int i = 0; i < 64; i += 2) {
+                acc0 = fmaf(s_DS[i * LD + j], s_S0[i * LD + j], acc0);
+                acc1 = fmaf(s_DS[(i + 1) * LD + j], s_S0[(i + 1) * LD + j], acc1);
+            }
+            s_dgC[j] = acc0 + acc1;
+        }
+        lds_barrier();
+        relane();
+
+        // ---- P4: value side. waves 0-3 (rows 16*w4..): X = W (P_a + L_ak V);
         //      dX = B^ dS_C^T + M_rb^T dY; drhs = W^T dX.
         //      waves 4-7 (same rows): dV partial = K^ dS_C^T + M_rk^T dY
         const int i0 = 16 * it;
@@ -583,11 +534,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         lds_barrier();
         relane();
 
-        // ---- key side and the state gradient:
-        //      waves 4-7 finish dV = partial + L_ak^T drhs and store it;
-        //      waves 0-3: dA^ = drhs S_0, waves 4-7: dB^ = X dS_C (key columns 16*w4..);
-        //      waves 0, 1, 2: dL_ab = drhs X^T, dL_ak = drhs V^T, dM_rb = dY X^T;
-        //      every wave: its two dS_0^T tiles
+        // ---- P5: key side. waves 4-7 finish dV = partial + L_ak^T drhs and
+        //      store it; waves 0-3: dA^ = drhs S_0, waves 4-7: dB^ = X dS_C (key
+        //      columns 16*w4..); waves 0, 1, 2: dL_ab = drhs X^T, dL_ak = drhs V^T,
+        //      dM_rb = dY X^T
         {
             const int jc = 16 * w4;
             if (!lo) {
@@ -619,7 +569,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                     for (int r = 0; r < 4; ++r) {
                         const int t = 4 * kq + r;
                         const bool keep = wave < 2 ? (l16 < t) : (l16 <= t);
-                        s_M[(MDLAB + wave) * 256 + t * 16 + l16] = keep ? gm[r] : 0.f;
+                        const float v = keep ? gm[r] : 0.f;
+                        s_M[(MDLAB + wave) * 256 + t * 16 + l16] = v;
+                        tile_scatter(s_M, wave < 2, wave != 1, t, l16, v);
                     }
                 }
             }
@@ -627,46 +579,283 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         lds_barrier();
         relane();
 
-        // ---- key-side gradient assembly: wave w owns tokens {w, 15-w} of every
-        //      key column (lane = column); u's pair part is summed over the 8 waves
+        // ---- P6: pair-gradient products of the split-point tiles (waves 0-3):
+        //      Z_A = dD B_rows (wave 0: tile 1, wave 2: tile 2) and
+        //      Z_B = dD^T A_rows (waves 1, 3), with dD the gathered matrix
+        //      gradients; into s_Z (S_0 is consumed)
+        if (lo) {
+            const int tile = wave >> 1;
+            const bool zb = (wave & 1) != 0;
+            const float *dD = s_M + (MDD1 + tile) * 256;
+            // A operand: this lane's row l16 of dD (Z_A) or of dD^T (Z_B), k = 4kq+e
+            float av[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) av[e] = dD[zb ? (4 * kq + e) * 16 + l16 : l16 * 16 + 4 * kq + e];
+            // B operand rows k = 4kq+e: B_rows (Z_A) or A_rows (Z_B) of the tile
+            const float *brow[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r_ = 4 * kq + e;
+                if (!zb) {
+                    brow[e] = s_BL + (tile == 0 ? r_ : 16 + r_) * LD;
+                } else if (tile == 0) {
+                    brow[e] = r_ < 4 ? s_AR + (8 + r_) * LD : r_ < 8 ? s_AWR + (r_ - 4) * LD
+                            : r_ < 12 ? s_AR + (16 + r_) * LD : s_AWR + (r_ - 8) * LD;
+                } else {
+                    brow[e] = s_AR + ((r_ & 4) ? 16 + r_ : 4 + r_) * LD;
+                }
+            }
+            float bv[4][4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[q][e] = brow[e][16 * q + l16];
+            float *zo = s_Z + (2 * tile + (zb ? 1 : 0)) * 16 * LD;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) z = mfma4(av[e], bv[q][e], z);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) zo[(4 * kq + r) * LD + 16 * q + l16] = z[r];
+            }
+        }
+        lds_barrier();
+        relane();
+
+        // ---- P7a: per-token gradients of key column j = lane for tokens
+        //      {w, 15-w} (token bodies specialised at compile time): chunk parts,
+        //      split-point pair parts (Z scaled by the decay factors) and
+        //      within-sub-chunk pair parts give dr, da, db, dk (stored); the u
+        //      terms go to LDS (dS_C, X, drhs, A^..K^ are consumed)
         {
             const int j = lane;
-            AsmArgs aa{s_in, s_AR, s_BV, s_KV, s_VV, s_G, s_M, s_dgC, s_S0, j, wave};
-            float st5[2][5];
-            switch (__builtin_amdgcn_readfirstlane(wave)) {
-            case 0: assemble_rows<0, 15>(aa, st5); break;
-            case 1: assemble_rows<1, 14>(aa, st5); break;
-            case 2: assemble_rows<2, 13>(aa, st5); break;
-            case 3: assemble_rows<3, 12>(aa, st5); break;
-            case 4: assemble_rows<4, 11>(aa, st5); break;
-            case 5: assemble_rows<5, 10>(aa, st5); break;
-            case 6: assemble_rows<6, 9>(aa, st5); break;
-            default: assemble_rows<7, 8>(aa, st5); break;
-            }
-            lds_barrier();
-            relane();
-            switch (__builtin_amdgcn_readfirstlane(wave)) {
-            case 0: assemble_out<0, 15>(aa, st5); break;
-            case 1: assemble_out<1, 14>(aa, st5); break;
-            case 2: assemble_out<2, 13>(aa, st5); break;
-            case 3: assemble_out<3, 12>(aa, st5); break;
-            case 4: assemble_out<4, 11>(aa, st5); break;
-            case 5: assemble_out<5, 10>(aa, st5); break;
-            case 6: assemble_out<6, 9>(aa, st5); break;
-            default: assemble_out<7, 8>(aa, st5); break;
-            }
-            const int tks[2] = {wave, 15 - wave};
+            float wv[16];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int t = tks[q];
+            for (int t = 0; t < 16; ++t) wv[t] = s_in[(IW * 16 + t) * LD + j];
+            const float W1 = (wv[4] * wv[5]) * (wv[6] * wv[7]);
+            const float W2 = (wv[8] * wv[9]) * (wv[10] * wv[11]);
+            const float *dLab = s_M + MDLAB * 256, *dLak = s_M + MDLAK * 256;
+            const float *dMrb = s_M + MDMRB * 256, *dMrk = s_M + MDMRK * 256;
+            auto tok = [&](auto TT) {
+                constexpr int t = decltype(TT)::value;
+                constexpr int p0 = t & ~3;                    // first token of t's sub-chunk
+                // decay factors of column j at token t
+                float gam = 1.f, gprev = 1.f, dend = 1.f, fex = 1.f, fin = 1.f, suf = 1.f;
+#pragma unroll
+                for (int u2 = 0; u2 < 16; ++u2) {
+                    if (u2 < t) gprev *= wv[u2];
+                    if (u2 <= t) gam *= wv[u2];
+                    if (u2 > t) dend *= wv[u2];
+                    if (u2 >= p0 && u2 < t) fex *= wv[u2];
+                    if (u2 >= p0 && u2 <= t) fin *= wv[u2];
+                    if (u2 > t && u2 < p0 + 4) suf *= wv[u2];
+                }
+                const float invF = __builtin_amdgcn_rcpf(fin);
+                const float *zA1 = s_Z + ZA1 * 16 * LD + j, *zB1 = s_Z + ZB1 * 16 * LD + j;
+                const float *zA2 = s_Z + ZA2 * 16 * LD + j, *zB2 = s_Z + ZB2 * 16 * LD + j;
+                // split-point pair parts by block: rows of block R = 8 (t >= 8) and
+                // of R = 4 / 12 (t in 4..7 / 12..15); columns of R = 8 (s < 8) and
+                // of R = 4 / 12 (s in 0..3 / 8..11)
+                float a8 = 0.f, r8 = 0.f, a4 = 0.f, r4 = 0.f, b8 = 0.f, k8 = 0.f, b4 = 0.f, k4 = 0.f;
+                if (t >= 8) {
+                    const float sc = t >= 12 ? W2 : 1.f;
+                    a8 = fex * zA1[(t - 8) * LD] * sc;
+                    r8 = fin * zA1[t * LD] * sc;
+                }
+                if ((t & 4) != 0) {
+                    a4 = fex * zA2[(t - 4) * LD];
+                    r4 = fin * zA2[t * LD];
+                }
+                if (t < 8) {
+                    const float sc = t < 4 ? W1 : 1.f;
+                    b8 = suf * zB1[t * LD] * sc;
+                    k8 = suf * zB1[(8 + t) * LD] * sc;
+                }
+                if ((t & 4) == 0 && t < 12) {
+                    b4 = suf * zB2[t * LD];
+                    k4 = suf * zB2[(t + 4) * LD];
+                }
+                // within-sub-chunk pair parts: t as the row (s <= t) and as the
+                // column (rows s >= t of M, s > t of L)
+                float qa = 0.f, qr = 0.f, qb = 0.f, qk = 0.f;
+#pragma unroll
+                for (int s = p0; s < p0 + 4; ++s) {
+                    if (s <= t) {
+                        const float bd = s_BD[s * LD + j], kd = s_KD[s * LD + j];
+                        if (s < t) qa += dLab[t * 16 + s] * bd + dLak[t * 16 + s] * kd;
+                        qr += dMrb[t * 16 + s] * bd + dMrk[t * 16 + s] * kd;
+                    }
+                    if (s >= t) {
+                        const float rp = s_AR[(16 + s) * LD + j];
+                        qb += dMrb[s * 16 + t] * rp;
+                        qk += dMrk[s * 16 + t] * rp;
+                    }
+                    if (s > t) {
+                        const float ap = s_AR[s * LD + j];
+                        qb += dLab[s * 16 + t] * ap;
+                        qk += dLak[s * 16 + t] * ap;
+                    }
+                }
+                const float a_t = s_in[(IA * 16 + t) * LD + j], r_t = s_in[(IR * 16 + t) * LD + j];
+                const float b_t = s_in[(IB * 16 + t) * LD + j], k_t = s_in[(IK * 16 + t) * LD + j];
+                const float dAh = s_G[(0 * 16 + t) * LD + j], dRh = s_G[(1 * 16 + t) * LD + j];
+                const float dBh = s_G[(2 * 16 + t) * LD + j], dKh = s_G[(3 * 16 + t) * LD + j];
+                const float dac = dAh * gprev, drc = dRh * gam, dbc = dBh * dend, dkc = dKh * dend;
                 if (t < L) {
                     const int64_t o = base + (int64_t)(t0 + t) * ts + j;
-                    IO<TI>::st((TI *)p.dr, o, st5[q][0]);
-                    IO<TI>::st((TI *)p.dw, o, st5[q][1]);
-                    IO<TI>::st((TI *)p.da, o, st5[q][2]);
-                    IO<TI>::st((TI *)p.db, o, st5[q][3]);
-                    IO<TI>::st((TI *)p.dk, o, st5[q][4]);
+                    IO<TI>::st((TI *)p.dr, o, drc + fin * qr + r8 + r4);
+                    IO<TI>::st((TI *)p.da, o, dac + fex * qa + a8 + a4);
+                    IO<TI>::st((TI *)p.db, o, dbc + invF * qb + b8 + b4);
+                    IO<TI>::st((TI *)p.dk, o, dkc + invF * qk + k8 + k4);
                 }
+                // u terms that the scans below read (ranges with structural zeros
+                // are neither written nor read)
+                const int o = t * LD + j;
+                s_U(UCHA)[o] = a_t * dac;
+                s_U(UCHR)[o] = r_t * drc;
+                s_U(UCHC)[o] = b_t * dbc + k_t * dkc;
+                if (t >= 4) {
+                    s_U(UR12A)[o] = a_t * (a8 + (t >= 12 ? 0.f : a4));
+                    s_U(UR12R)[o] = r_t * (r8 + (t >= 12 ? 0.f : r4));
+                }
+                if (t >= 12) {
+                    s_U(UR3A)[o] = a_t * a4;
+                    s_U(UR3R)[o] = r_t * r4;
+                }
+                if (t < 8) s_U(UC2)[o] = b_t * b8 + k_t * k8;
+                if ((t & 4) == 0 && t < 12) s_U(UC13)[o] = b_t * b4 + k_t * k4;
+            };
+            switch (wave) {
+                case 0: tok(IC<0>{}); tok(IC<15>{}); break;
+                case 1: tok(IC<1>{}); tok(IC<14>{}); break;
+                case 2: tok(IC<2>{}); tok(IC<13>{}); break;
+                case 3: tok(IC<3>{}); tok(IC<12>{}); break;
+                case 4: tok(IC<4>{}); tok(IC<11>{}); break;
+                case 5: tok(IC<5>{}); tok(IC<10>{}); break;
+                case 6: tok(IC<6>{}); tok(IC<9>{}); break;
+                default: tok(IC<7>{}); tok(IC<8>{}); break;
+            }
+        }
+        lds_barrier();
+        relane();
+
+        // ---- P7b: per key column j = lane, the partial sums of u_m for all m
+        //      (each a prefix or suffix sum over one block's range, so no sum
+        //      is formed as a difference): wave 0 chunk rows (t >= m for r,
+        //      t > m for a), wave 1 chunk columns (s < m), wave 2 block rows,
+        //      wave 3 block columns, waves 4-7 the pairs of sub-chunk w-4 that
+        //      straddle m. Results [5][16][LD] into s_Z (4) and s_G (1).
+        {
+            const int j = lane;
+            const float *dLab = s_M + MDLAB * 256, *dLak = s_M + MDLAK * 256;
+            const float *dMrb = s_M + MDMRB * 256, *dMrk = s_M + MDMRK * 256;
+            if (wave == 0) {
+                float rr[16], aa[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) { rr[t] = s_U(UCHR)[t * LD + j]; aa[t] = s_U(UCHA)[t * LD + j]; }
+                float acc = 0.f;
+#pragma unroll
+                for (int t = 15; t >= 0; --t) { s_Z[t * LD + j] = acc + rr[t]; acc += rr[t] + aa[t]; }
+            } else if (wave == 1) {
+                float cc[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) cc[t] = s_U(UCHC)[t * LD + j];
+                float acc = 0.f;
+#pragma unroll
+                for (int t = 0; t < 16; ++t) { s_Z[(16 + t) * LD + j] = acc; acc += cc[t]; }
+            } else if (wave == 2) {
+                // block R = 8 rows t = 8..15 (with R = 12 rows t = 12..15 once
+                // m >= 12); block R = 4 rows t = 4..7
+                float rr[16], aa[16], r3[16], a3[16];
+#pragma unroll
+                for (int t = 4; t < 16; ++t) { rr[t] = s_U(UR12R)[t * LD + j]; aa[t] = s_U(UR12A)[t * LD + j]; }
+#pragma unroll
+                for (int t = 12; t < 16; ++t) { r3[t] = s_U(UR3R)[t * LD + j]; a3[t] = s_U(UR3A)[t * LD + j]; }
+                float *res = s_Z + 2 * 16 * LD + j;
+                float acc = 0.f, acc3 = 0.f;
+#pragma unroll
+                for (int t = 15; t >= 12; --t) {
+                    res[t * LD] = acc + acc3 + rr[t] + r3[t];
+                    acc += rr[t] + aa[t]; acc3 += r3[t] + a3[t];
+                }
+#pragma unroll
+                for (int t = 11; t >= 8; --t) { res[t * LD] = acc + rr[t]; acc += rr[t] + aa[t]; }
+                acc = 0.f;
+#pragma unroll
+                for (int t = 7; t >= 4; --t) { res[t * LD] = acc + rr[t]; acc += rr[t] + aa[t]; }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) res[t * LD] = 0.f;
+            } else if (wave == 3) {
+                // block R = 8 columns s = 0..7, R = 4 columns s = 0..3, R = 12 columns s = 8..11
+                float c2[8], c13[12];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) c2[t] = s_U(UC2)[t * LD + j];
+#pragma unroll
+                for (int t = 0; t < 12; ++t)
+                    if ((t & 4) == 0) c13[t] = s_U(UC13)[t * LD + j];
+                float *res = s_Z + 3 * 16 * LD + j;
+                float acc = 0.f, acc13 = 0.f;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) { res[t * LD] = acc + acc13; acc += c2[t]; acc13 += c13[t]; }
+#pragma unroll
+                for (int t = 4; t < 8; ++t) { res[t * LD] = acc; acc += c2[t]; }
+                acc = 0.f;
+#pragma unroll
+                for (int t = 8; t < 12; ++t) { res[t * LD] = acc; acc += c13[t]; }
+#pragma unroll
+                for (int t = 12; t < 16; ++t) res[t * LD] = 0.f;
+            } else {
+                // pairs (p0+tt, p0+ss), ss < tt, inside sub-chunk p0 = 4(w-4):
+                // M pairs contain w_m for ss < m-p0 <= tt, L pairs for ss < m-p0 < tt
+                const int p0 = 4 * (wave - 4);
+                float ap[4], rp[4], bd[3], kd[3];
+#pragma unroll
+                for (int e = 1; e < 4; ++e) {
+                    ap[e] = s_AR[(p0 + e) * LD + j];
+                    rp[e] = s_AR[(16 + p0 + e) * LD + j];
+                }
+#pragma unroll
+                for (int e = 0; e < 3; ++e) { bd[e] = s_BD[(p0 + e) * LD + j]; kd[e] = s_KD[(p0 + e) * LD + j]; }
+                float pm[4][3], pl[4][3];
+#pragma unroll
+                for (int tt = 1; tt < 4; ++tt)
+#pragma unroll
+                    for (int ss = 0; ss < tt; ++ss) {
+                        const int o = (p0 + tt) * 16 + p0 + ss;
+                        pm[tt][ss] = rp[tt] * (dMrb[o] * bd[ss] + dMrk[o] * kd[ss]);
+                        pl[tt][ss] = ap[tt] * (dLab[o] * bd[ss] + dLak[o] * kd[ss]);
+                    }
+                float *res = s_G + j;
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    float x = 0.f;
+#pragma unroll
+                    for (int tt = mi; tt < 4; ++tt)
+#pragma unroll
+                        for (int ss = 0; ss < mi; ++ss) {
+                            x += pm[tt][ss];
+                            if (tt > mi) x += pl[tt][ss];
+                        }
+                    res[(p0 + mi) * LD] = x;
+                }
+            }
+        }
+        lds_barrier();
+        relane();
+
+        // ---- P7c: u_m for m in {w, 15-w}: the five partial sums and
+        //      d gamma_C gamma_C; dw = u / w; store
+        {
+            const int j = lane;
+            const float dgc = s_dgC[j] * s_gC[j];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int m = q == 0 ? wave : 15 - wave;
+                const int o = m * LD + j;
+                const float x = dgc + ((s_Z[o] + s_Z[16 * LD + o]) + (s_Z[32 * LD + o] + s_Z[48 * LD + o]))
+                              + s_G[o];
+                if (m < L) IO<TI>::st((TI *)p.dw, base + (int64_t)(t0 + m) * ts + j, x / s_in[IW * 16 * LD + o]);
             }
         }
     }
