@@ -27,14 +27,17 @@
 // then acts as 2^-30 on at most three neighbouring tokens); they are VALU dot
 // products. W = (I - L_ab)^-1 comes from column-wise forward substitution.
 //
-// Work split (warp specialisation): a workgroup owns RB = 16*NMW value rows
-// of one (sequence, head) and has NMW "state" waves and 8 "operand" waves.
-// Only the state waves touch the state: each holds 16 rows x 64 columns of S
-// in MFMA accumulators as S^T tiles (lane l holds S[row0 + l%16][16*jt +
-// 4*(l/16) + r]), which is directly the B operand of the next chunk's
-// [A^;R^] S_0^T product, and the D1 -> chain -> D2 sequence of a chunk stays
-// in registers (the chain's outputs come out in the B-operand layout of the
-// next product). The operand waves stage inputs and build everything that does
+// Work split (warp specialisation): a workgroup owns RB = 16*NMW/KS value
+// rows of one (sequence, head) and has NMW "state" waves and 8 "operand"
+// waves. Only the state waves touch the state: each holds 16 rows x 64/KS
+// columns of S in MFMA accumulators as S^T tiles (lane l holds S[row0 +
+// l%16][16*jt + 4*(l/16) + r]), which is directly the B operand of the next
+// chunk's [A^;R^] S_0^T product, and the D1 -> chain -> D2 sequence of a chunk
+// stays in registers (the chain's outputs come out in the B-operand layout of
+// the next product). With KS = 2 the two waves that share 16 rows each hold
+// half of the key columns, so the serial per-chunk MFMA chain is spread over
+// all four SIMDs when a workgroup has only 32 rows; their partial D1 sums
+// (over their key columns) meet in LDS. The operand waves stage inputs and build everything that does
 // not depend on the state (decay rows, the 16x16 matrices, W) for chunk c
 // while the state waves advance through chunk c-1; the two sides meet through
 // a double-buffered LDS hand-off, two workgroup barriers per chunk (W of a
@@ -58,7 +61,9 @@ enum { MLAK = 0, MMRK, MMRB, MWI };
 // LDS layout (floats): the operand waves' private rows, then two hand-off
 // buffers (one per chunk parity) read by the state waves.
 namespace lay {
-constexpr int IN = 0;                       // [2][6][16][64] r w k a b v, by chunk parity
+// [2][6][16][64] r w k a b v, by chunk parity; column c of a row sits at
+// 32 (c & 4 ? 1 : 0) + 4 (c >> 3) + (c & 3)
+constexpr int IN = 0;
 constexpr int IN_SIZE = 6 * 16 * 64;
 constexpr int AR = IN + 2 * IN_SIZE;        // [32][QLD] A'_t = a_t F_ex(t), R'_t = r_t F_in(t)
 constexpr int AWR = AR + 32 * QLD;          // [8][QLD]  A'_t W_2, R'_t W_2 for t = 12..15
@@ -74,14 +79,18 @@ constexpr int B_VT = B_BKT + 64 * KLD;      // [64][VLD] V by value row i
 constexpr int B_M = B_VT + 64 * VLD;        // [4][16][MLD] L_ak, M_rk, M_rb, W
 constexpr int B_GC = B_M + 4 * 16 * MLD;    // [64] gamma_16
 constexpr int BUF_SIZE = B_GC + 64;
-constexpr int TOTAL = BUF + 2 * BUF_SIZE;
+constexpr int XCH = BUF + 2 * BUF_SIZE;     // [4 waves][2][64 lanes][4] partial D1 (key split)
+constexpr int TOTAL = XCH + 4 * 2 * 256;
 static_assert(BUF % 4 == 0 && BUF_SIZE % 4 == 0, "16-byte aligned buffers");
 }  // namespace lay
 
-template <typename TI, int NMW>
+template <typename TI, int NMW, int KS>
 __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdArgs p, int32_t units) {
-    constexpr int RB = 16 * NMW;       // value rows per workgroup
-    constexpr int NRB = 4 / NMW;       // row blocks per unit
+    constexpr int NG = NMW / KS;       // 16-row groups per workgroup
+    constexpr int RB = 16 * NG;        // value rows per workgroup
+    constexpr int NRB = 64 / RB;       // row blocks per unit
+    constexpr int NQ = 4 / KS;         // 16-column key tiles per state wave
+    static_assert(KS == 1 || KS == 2, "key split of 1 or 2");
     extern __shared__ __align__(16) float sm[];
 
     // Workgroup -> (unit, row block). Row blocks of one unit go to the same
@@ -114,34 +123,40 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
 
     if (wave < NMW) {
         // ================= state waves =================
-        const int irow = i0 + 16 * wave + l16;           // value row of this lane
-        f32x4 acc[4];
+        const int rg = wave % NG, kh = wave / NG;        // row group, key part
+        const int irow = i0 + 16 * rg + l16;             // value row of this lane
+        const int q0 = kh * NQ;                          // first key tile of this wave
+        f32x4 acc[NQ];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int qq = 0; qq < NQ; ++qq) {
             if (p.s0) {
-                const float4 v4 = *(const float4 *)(p.s0 + sbase + (int64_t)irow * kN + 16 * q + 4 * kq);
-                acc[q] = f32x4{v4.x, v4.y, v4.z, v4.w};
+                const float4 v4 = *(const float4 *)(p.s0 + sbase + (int64_t)irow * kN + 16 * (q0 + qq) + 4 * kq);
+                acc[qq] = f32x4{v4.x, v4.y, v4.z, v4.w};
             } else {
-                acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+                acc[qq] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
+        float *xch_own = sm + lay::XCH + wave * 512 + lane * 4;
+        const float *xch_mate = sm + lay::XCH + (rg + (1 - kh) * NG) * 512 + lane * 4;
 #pragma unroll 1
         for (int c = 0; c <= nch; ++c) {
             const int cm = c - 1;                        // chunk advanced in this iteration
             const float *buf = sm + lay::BUF + (cm & 1) * lay::BUF_SIZE;
             f32x4 d1a = {0.f, 0.f, 0.f, 0.f}, d1r = d1a;
-            float4 bt[4];                                // B^ rows of the four state tiles
+            float4 bt[NQ];                               // B^ rows of this wave's state tiles
             float4 mrb = make_float4(0.f, 0.f, 0.f, 0.f);
             lds_barrier();
             // ---- phase X (W of this chunk is being solved meanwhile):
-            //      checkpoint; D1 = [A^;R^] S_0^T for this wave's rows;
-            //      P_a += L_ak V, P_r += M_rk V; S^T = diag(gamma) S^T + K^^T V
+            //      checkpoint; D1 = [A^;R^] S_0^T for this wave's rows (over its
+            //      key columns); P_a += L_ak V, P_r += M_rk V (one of them per
+            //      key part when split); S^T = diag(gamma) S^T + K^^T V
             if (cm >= 0) {
                 if (p.ckpt) {
                     float *cp = p.ckpt + ((u.ckpt + cm) * H + h) * (int64_t)(kN * kN) + (int64_t)irow * kN;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *(float4 *)(cp + 16 * q + 4 * kq) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+                    for (int qq = 0; qq < NQ; ++qq)
+                        *(float4 *)(cp + 16 * (q0 + qq) + 4 * kq) =
+                            make_float4(acc[qq][0], acc[qq][1], acc[qq][2], acc[qq][3]);
                 }
                 const float4 vb = *(const float4 *)(buf + lay::B_VT + irow * VLD + 4 * kq);
                 const float *mrow = buf + lay::B_M + l16 * MLD + 4 * kq;
@@ -149,65 +164,84 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
                 const float4 mrk = *(const float4 *)(mrow + MMRK * 16 * MLD);
                 mrb = *(const float4 *)(mrow + MMRB * 16 * MLD);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int qq = 0; qq < NQ; ++qq) {
+                    const int q = q0 + qq;
                     const float4 a4 = *(const float4 *)(buf + lay::B_Q + l16 * QLD + 16 * q + 4 * kq);
                     const float4 r4 = *(const float4 *)(buf + lay::B_Q + (16 + l16) * QLD + 16 * q + 4 * kq);
-                    d1a = mfma4(a4.x, acc[q][0], d1a);
-                    d1r = mfma4(r4.x, acc[q][0], d1r);
-                    d1a = mfma4(a4.y, acc[q][1], d1a);
-                    d1r = mfma4(r4.y, acc[q][1], d1r);
-                    d1a = mfma4(a4.z, acc[q][2], d1a);
-                    d1r = mfma4(r4.z, acc[q][2], d1r);
-                    d1a = mfma4(a4.w, acc[q][3], d1a);
-                    d1r = mfma4(r4.w, acc[q][3], d1r);
+                    d1a = mfma4(a4.x, acc[qq][0], d1a);
+                    d1r = mfma4(r4.x, acc[qq][0], d1r);
+                    d1a = mfma4(a4.y, acc[qq][1], d1a);
+                    d1r = mfma4(r4.y, acc[qq][1], d1r);
+                    d1a = mfma4(a4.z, acc[qq][2], d1a);
+                    d1r = mfma4(r4.z, acc[qq][2], d1r);
+                    d1a = mfma4(a4.w, acc[qq][3], d1a);
+                    d1r = mfma4(r4.w, acc[qq][3], d1r);
                 }
-                d1a = mfma4(lak.x, vb.x, d1a); d1a = mfma4(lak.y, vb.y, d1a);
-                d1a = mfma4(lak.z, vb.z, d1a); d1a = mfma4(lak.w, vb.w, d1a);
-                d1r = mfma4(mrk.x, vb.x, d1r); d1r = mfma4(mrk.y, vb.y, d1r);
-                d1r = mfma4(mrk.z, vb.z, d1r); d1r = mfma4(mrk.w, vb.w, d1r);
+                if (KS == 1 || kh == 0) {
+                    d1a = mfma4(lak.x, vb.x, d1a); d1a = mfma4(lak.y, vb.y, d1a);
+                    d1a = mfma4(lak.z, vb.z, d1a); d1a = mfma4(lak.w, vb.w, d1a);
+                }
+                if (KS == 1 || kh == 1) {
+                    d1r = mfma4(mrk.x, vb.x, d1r); d1r = mfma4(mrk.y, vb.y, d1r);
+                    d1r = mfma4(mrk.z, vb.z, d1r); d1r = mfma4(mrk.w, vb.w, d1r);
+                }
+                if (KS > 1) {
+                    *(float4 *)xch_own = make_float4(d1a[0], d1a[1], d1a[2], d1a[3]);
+                    *(float4 *)(xch_own + 256) = make_float4(d1r[0], d1r[1], d1r[2], d1r[3]);
+                }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int qq = 0; qq < NQ; ++qq) {
+                    const int q = q0 + qq;
                     const float4 g4 = *(const float4 *)(buf + lay::B_GC + 16 * q + 4 * kq);
                     const float *br = buf + lay::B_BKT + (16 * q + l16) * KLD + 4 * kq;
-                    bt[q] = *(const float4 *)br;
+                    bt[qq] = *(const float4 *)br;
                     const float4 k4 = *(const float4 *)(br + 16);
-                    f32x4 a = acc[q];
+                    f32x4 a = acc[qq];
                     a[0] *= g4.x; a[1] *= g4.y; a[2] *= g4.z; a[3] *= g4.w;
                     a = mfma4(k4.x, vb.x, a); a = mfma4(k4.y, vb.y, a);
                     a = mfma4(k4.z, vb.z, a); a = mfma4(k4.w, vb.w, a);
-                    acc[q] = a;
+                    acc[qq] = a;
                 }
             }
             lds_barrier();
-            // ---- phase Y: X = W rhs; Y = P_r + M_rk V + M_rb X; y out; S^T += B^^T X
+            // ---- phase Y: (add the partner's partial D1); X = W rhs;
+            //      Y = P_r + M_rk V + M_rb X; y out; S^T += B^^T X
             if (cm >= 0) {
+                if (KS > 1) {
+                    const float4 pa = *(const float4 *)xch_mate;
+                    const float4 pr = *(const float4 *)(xch_mate + 256);
+                    d1a[0] += pa.x; d1a[1] += pa.y; d1a[2] += pa.z; d1a[3] += pa.w;
+                    d1r[0] += pr.x; d1r[1] += pr.y; d1r[2] += pr.z; d1r[3] += pr.w;
+                }
                 const float4 wi = *(const float4 *)(buf + lay::B_M + MWI * 16 * MLD + l16 * MLD + 4 * kq);
                 f32x4 xx = {0.f, 0.f, 0.f, 0.f};
                 xx = mfma4(wi.x, d1a[0], xx); xx = mfma4(wi.y, d1a[1], xx);
                 xx = mfma4(wi.z, d1a[2], xx); xx = mfma4(wi.w, d1a[3], xx);
-                d1r = mfma4(mrb.x, xx[0], d1r); d1r = mfma4(mrb.y, xx[1], d1r);
-                d1r = mfma4(mrb.z, xx[2], d1r); d1r = mfma4(mrb.w, xx[3], d1r);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    f32x4 a = acc[q];
-                    a = mfma4(bt[q].x, xx[0], a); a = mfma4(bt[q].y, xx[1], a);
-                    a = mfma4(bt[q].z, xx[2], a); a = mfma4(bt[q].w, xx[3], a);
-                    acc[q] = a;
+                for (int qq = 0; qq < NQ; ++qq) {
+                    f32x4 a = acc[qq];
+                    a = mfma4(bt[qq].x, xx[0], a); a = mfma4(bt[qq].y, xx[1], a);
+                    a = mfma4(bt[qq].z, xx[2], a); a = mfma4(bt[qq].w, xx[3], a);
+                    acc[qq] = a;
                 }
-                const int t0 = cm * kChunk;
-                const int L = min(kChunk, u.len - t0);
+                if (KS == 1 || kh == 0) {
+                    d1r = mfma4(mrb.x, xx[0], d1r); d1r = mfma4(mrb.y, xx[1], d1r);
+                    d1r = mfma4(mrb.z, xx[2], d1r); d1r = mfma4(mrb.w, xx[3], d1r);
+                    const int t0 = cm * kChunk;
+                    const int L = min(kChunk, u.len - t0);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 4 * kq + r;
-                    if (t < L) IO<TI>::st((TI *)p.y, base + (int64_t)(t0 + t) * ts + irow, d1r[r]);
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 4 * kq + r;
+                        if (t < L) IO<TI>::st((TI *)p.y, base + (int64_t)(t0 + t) * ts + irow, d1r[r]);
+                    }
                 }
             }
         }
         if (p.s_out) {
             float *op = p.s_out + sbase + (int64_t)irow * kN;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *(float4 *)(op + 16 * q + 4 * kq) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+            for (int qq = 0; qq < NQ; ++qq)
+                *(float4 *)(op + 16 * (q0 + qq) + 4 * kq) = make_float4(acc[qq][0], acc[qq][1], acc[qq][2], acc[qq][3]);
         }
         return;
     }
@@ -225,10 +259,14 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
 
     // Staging (operand waves 5-7): element group g = sid + 192k (k = 0..3) of
     // 6 streams x 16 tokens x 8 groups of 8 elements; stream g >> 7 is uniform
-    // per wave. Loads are issued one chunk ahead, unconditionally (chunk index
-    // and token rows clamped into the sequence), so that the registers in
-    // flight have exactly one definition per iteration.
-    Raw<TI, 4> raw;
+    // per wave. Loads are issued unconditionally (chunk index and token rows
+    // clamped into the sequence), so that the registers in flight have exactly
+    // one definition per iteration. For 16-bit inputs two register sets
+    // alternate, which keeps each chunk's loads in flight for two chunk
+    // periods (HBM latency under load exceeds one); fp32 inputs have room for
+    // one set only.
+    constexpr bool kTwoSets = sizeof(TI) == 2;
+    Raw<TI, 4> raw, raw1;
     const TI *sp[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -237,7 +275,7 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
                        : st == IA ? p.a : st == IB ? p.b : p.v;
         sp[k] = (const TI *)vp + base;
     }
-    auto issue = [&](int cc) {               // 0 <= cc < nch
+    auto issue = [&](int cc, Raw<TI, 4> &raw) {      // 0 <= cc < nch
         const int Lc = min(kChunk, u.len - cc * kChunk);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -246,24 +284,25 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
             raw_load(sp[k] + (int64_t)(cc * kChunk + t) * ts + e0, raw, k);
         }
     };
-    auto stage = [&](int cc) {
+    auto stage = [&](int cc, const Raw<TI, 4> &raw) {
         const int Lc = min(kChunk, u.len - cc * kChunk);
         float *s_in = sm + lay::IN + (cc & 1) * lay::IN_SIZE;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int g = sid + 192 * k;
             const int st = g >> 7, t = (g >> 3) & 15, e0 = (g & 7) * 8;
+            // unpacked unconditionally, then replaced by identity tokens past
+            // the end (a branch would leave the loads pending on one path)
             float x[8];
-            if (t < Lc) {
-                raw_unpack(raw, k, x);
-            } else {                           // identity tokens past the end
-                const float f = st == IW ? 1.f : 0.f;
+            raw_unpack(raw, k, x);
+            const float f = st == IW ? 1.f : 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = f;
-            }
-            float *d = s_in + (st * 16 + t) * 64 + e0;
+            for (int e = 0; e < 8; ++e) x[e] = t < Lc ? x[e] : f;
+            // columns e0..e0+3 to 4 (g & 7) and e0+4..e0+7 to 32 + 4 (g & 7):
+            // each store instruction covers whole 128-byte row segments
+            float *d = s_in + (st * 16 + t) * 64 + (e0 >> 1);
             *(float4 *)d = make_float4(x[0], x[1], x[2], x[3]);
-            *(float4 *)(d + 4) = make_float4(x[4], x[5], x[6], x[7]);
+            *(float4 *)(d + 32) = make_float4(x[4], x[5], x[6], x[7]);
         }
     };
 
@@ -274,14 +313,14 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
     // ---- phase X (operand waves 1-4): the rows the 16x16 matrices are built
     //      from: A' = a F_ex (wave 1), R' = r F_in (wave 2), b (3) and k (4) rows
     auto matrix_rows = [&](const float *s_in) {
-        const int j = lane;
+        const int j = lane, pj = ((lane & 4) << 3) + ((lane >> 3) << 2) + (lane & 3);
         const int role = pw - 1;
         const int st = role == 0 ? IA : role == 1 ? IR : role == 2 ? IB : IK;
         float wv[16], xv[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            wv[t] = s_in[IW * 1024 + t * 64 + j];
-            xv[t] = s_in[st * 1024 + t * 64 + j];
+            wv[t] = s_in[IW * 1024 + t * 64 + pj];
+            xv[t] = s_in[st * 1024 + t * 64 + pj];
         }
         if (role < 2) {            // times W_2 for t >= 12 as well
             const int inc = role;
@@ -338,14 +377,14 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
     //      A^_t = a_t gamma_{t-1}, R^_t = r_t gamma_t, gamma_16 (wave 6);
     //      B^, K^ by key column and V by value row (wave 7)
     auto handoff_rows = [&](const float *s_in, float *buf) {
-        const int j = lane;
+        const int j = lane, pj = ((lane & 4) << 3) + ((lane >> 3) << 2) + (lane & 3);
         float wv[16], xv[16], yv[16];
         const int s1 = pw == 6 ? IA : IB, s2 = pw == 6 ? IR : IK;
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            wv[t] = s_in[IW * 1024 + t * 64 + j];
-            xv[t] = s_in[s1 * 1024 + t * 64 + j];
-            yv[t] = s_in[s2 * 1024 + t * 64 + j];
+            wv[t] = s_in[IW * 1024 + t * 64 + pj];
+            xv[t] = s_in[s1 * 1024 + t * 64 + pj];
+            yv[t] = s_in[s2 * 1024 + t * 64 + pj];
         }
         if (pw == 6) {
             float g = 1.f;
@@ -364,7 +403,7 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
         } else {
             float vv[16];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) vv[t] = s_in[IV * 1024 + t * 64 + j];
+            for (int t = 0; t < 16; ++t) vv[t] = s_in[IV * 1024 + t * 64 + pj];
             float d = 1.f;
 #pragma unroll
             for (int s = 15; s >= 0; --s) { xv[s] *= d; yv[s] *= d; d *= wv[s]; }
@@ -503,21 +542,38 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
     // hand-off rows of chunk c. The state waves advance chunk c-1 meanwhile and
     // need W only in phase Y.
     if (pw >= 5) {
-        issue(0);
-        stage(0);
-        issue(min(1, nch - 1));
-#pragma unroll 1
-        for (int c = 0; c <= nch; ++c) {
+        // iteration c stages chunk c+1 from set rw and refills rw with chunk
+        // c+1+d (d = 2 with two sets, else 1)
+        auto step = [&](int c, Raw<TI, 4> &rw, int d) {
             float *buf = sm + lay::BUF + (c & 1) * lay::BUF_SIZE;
             const float *s_in = sm + lay::IN + (c & 1) * lay::IN_SIZE;
             lds_barrier();
-            if (c + 1 < nch) stage(c + 1);
-            issue(min(c + 2, nch - 1));
+            if (c + 1 < nch) stage(c + 1, rw);
+            issue(min(c + 1 + d, nch - 1), rw);
             lds_barrier();
             if (c < nch) {
                 if (pw == 5) matrices(buf);
                 else handoff_rows(s_in, buf);
             }
+        };
+        issue(0, raw);
+        stage(0, raw);
+        if constexpr (kTwoSets) {
+            issue(min(1, nch - 1), raw1);
+            // keep every load of chunk 1 ahead of chunk 2's, so that staging
+            // chunk 1 waits for its own loads only
+            __builtin_amdgcn_sched_barrier(0);
+            issue(min(2, nch - 1), raw);
+#pragma unroll 1
+            for (int c = 0; c <= nch; c += 2) {
+                step(c, raw1, 2);                  // chunk c+1 was loaded into raw1
+                if (c + 1 > nch) break;
+                step(c + 1, raw, 2);               // chunk c+2 was loaded into raw
+            }
+        } else {
+            issue(min(1, nch - 1), raw);
+#pragma unroll 1
+            for (int c = 0; c <= nch; ++c) step(c, raw, 1);
         }
     } else {
 #pragma unroll 1
@@ -536,11 +592,11 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
     }
 }
 
-template <typename TI, int NMW>
+template <typename TI, int NMW, int KS>
 hipError_t launch_ws(const FwdArgs &a, int32_t units, hipStream_t stream) {
-    constexpr int NRB = 4 / NMW;
+    constexpr int NRB = 64 / (16 * NMW / KS);
     const size_t lds = (size_t)lay::TOTAL * sizeof(float);
-    auto fn = fwd_ws_kernel<TI, NMW>;
+    auto fn = fwd_ws_kernel<TI, NMW, KS>;
     hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t blocks = NRB == 1 ? units : ((int64_t)units + 7) / 8 * 8 * NRB;
@@ -553,10 +609,11 @@ hipError_t launch_typed(const FwdArgs &a, hipStream_t stream) {
     const int S = a.seg.num_seqs > 0 ? a.seg.num_seqs : a.seg.B;
     const int32_t units = S * a.seg.H;
     // One workgroup per CU (LDS); split value rows across workgroups when
-    // there are fewer units than CUs.
-    if (units >= 256) return launch_ws<TI, 4>(a, units, stream);
-    if (units >= 128) return launch_ws<TI, 2>(a, units, stream);
-    return launch_ws<TI, 1>(a, units, stream);
+    // there are fewer units than CUs, and then key columns across the state
+    // waves that share rows.
+    if (units >= 256) return launch_ws<TI, 4, 1>(a, units, stream);
+    if (units >= 128) return launch_ws<TI, 4, 2>(a, units, stream);
+    return launch_ws<TI, 2, 2>(a, units, stream);
 }
 
 }  // namespace
