@@ -51,7 +51,7 @@
 namespace wkv7 {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 1024;
 constexpr int kChunksPerGroup = 8;                // chunks per workgroup (consecutive)
 constexpr int LD = 68;                            // row pitch of 16x64 / 64x64 arrays
 constexpr float kMinW = 9.313225746154785e-10f;   // 2^-30
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 
     const int tid = threadIdx.x;
     const int lane0 = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 8 waves; w and w+4 share a SIMD
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 16 waves; wave w runs on SIMD w % 4
     int lane = lane0, l16 = lane0 & 15, kq = lane0 >> 4;
     // The lane indices are re-derived opaquely at the start of each phase, so
     // that the many LDS addresses built from them are formed inside the phase
@@ -181,9 +181,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         asm volatile("" : "+v"(lv));
         lane = lv; l16 = lv & 15; kq = lv >> 4;
     };
-    const int w4 = wave & 3;                         // 16-row / 16-column tile of this wave
-    const bool lo = wave < 4;
-    const int it = w4;
+    const int w4 = wave & 3;                         // 16-row / 16-column block of this wave
 
     float *s_in = sm + O_IN;
     float *s_Q = sm + O_Q, *s_BK = sm + O_BK;
@@ -210,19 +208,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
     for (int q = tid; q < 4 * 256; q += kThreads) s_M[q] = 0.f;
     for (int q = tid; q < 256; q += kThreads) s_M[MDD2 * 256 + q] = 0.f;
 
-    // Staging: element groups g = tid + 512k (k = 0, 1) of 7 streams x 16
-    // tokens x 8 groups of 8; stream g >> 7 is uniform per wave. Loads are
-    // issued one chunk ahead, unconditionally (token rows clamped into the
-    // sequence), so the registers in flight have one definition per
-    // iteration; groups of a missing stream (dy == NULL, or past the seven
-    // streams) load the w row instead and stage as fill.
-    Raw<TI, 2> raw;
-    float4 ckr0, ckr1, dsr0, dsr1;              // checkpoint S_0 and dS_C of the chunk in flight
+    // Staging: element groups g = tid + 1024k (k = 0, 1) of 7 streams x 16
+    // tokens x 16 groups of 4 (a 16-byte LDS store per group, consecutive
+    // lanes on consecutive groups); stream g >> 8 is uniform per wave. Loads
+    // are issued one chunk ahead, unconditionally (token rows clamped into the
+    // sequence), so the registers in flight have one definition per iteration;
+    // groups of a missing stream (dy == NULL, or past the seven streams) load
+    // the w row instead and stage as fill.
+    Raw4<TI> raw[2];
+    float4 ckr, dsr;                            // checkpoint S_0 and dS_C of the chunk in flight
     const TI *sp[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        const int st = __builtin_amdgcn_readfirstlane((tid + k * kThreads) >> 7);
-        const void *vp = p.staged[st];
+        const int st = __builtin_amdgcn_readfirstlane((tid + k * kThreads) >> 8);
+        const void *vp = st < 7 ? p.staged[st] : nullptr;
         sp[k] = vp ? (const TI *)vp + base : nullptr;
     }
     const TI *wrow = (const TI *)p.w + base;
@@ -231,15 +230,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int g = tid + k * kThreads;
-            const int t = min((g >> 3) & 15, Lc - 1), e0 = (g & 7) * 8;
-            raw_load((sp[k] ? sp[k] : wrow) + (int64_t)(cc * kChunk + t) * ts + e0, raw, k);
+            const int t = min((g >> 4) & 15, Lc - 1), e0 = (g & 15) * 4;
+            raw4_load((sp[k] ? sp[k] : wrow) + (int64_t)(cc * kChunk + t) * ts + e0, raw[k]);
         }
-        // float4 f4 = tid + 512k of a 64x64 state: row f4 / 16, column 4 (f4 % 16)
+        // float4 tid of a 64x64 state: row tid / 16, column 4 (tid % 16)
         const int64_t so = ((u.ckpt + cc) * H + h) * (int64_t)(kN * kN) + tid * 4;
-        ckr0 = *(const float4 *)(p.ckpt + so);
-        ckr1 = *(const float4 *)(p.ckpt + so + kThreads * 4);
-        dsr0 = *(const float4 *)(p.ws + so);
-        dsr1 = *(const float4 *)(p.ws + so + kThreads * 4);
+        ckr = *(const float4 *)(p.ckpt + so);
+        dsr = *(const float4 *)(p.ws + so);
     };
     issue(c_hi - 1);
 
@@ -255,37 +252,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int g = tid + k * kThreads;
-            if (g < 7 * 128) {
-                const int st = g >> 7, t = (g >> 3) & 15, e0 = (g & 7) * 8;
-                float x[8];
-                if (t < L && sp[k] != nullptr) {
-                    raw_unpack(raw, k, x);
-                } else {
-                    const float f = st == IW ? 1.f : 0.f;
+            if (g < 7 * 256) {
+                const int st = g >> 8, t = (g >> 4) & 15, e0 = (g & 15) * 4;
+                float x[4];
+                raw4_unpack(raw[k], x);          // unconditional: no path leaves the loads pending
+                const bool keep = t < L && sp[k] != nullptr;
+                const float f = st == IW ? 1.f : 0.f;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = f;
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = keep ? x[e] : f;
+                    if (st == IW) x[e] = fmaxf(x[e], kMinW);
                 }
-                if (st == IW) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = fmaxf(x[e], kMinW);
-                }
-                float *d = s_in + (st * 16 + t) * LD + e0;
-                *(float4 *)d = make_float4(x[0], x[1], x[2], x[3]);
-                *(float4 *)(d + 4) = make_float4(x[4], x[5], x[6], x[7]);
+                *(float4 *)(s_in + (st * 16 + t) * LD + e0) = make_float4(x[0], x[1], x[2], x[3]);
             }
         }
-        *(float4 *)(s_S0 + (tid >> 4) * LD + (tid & 15) * 4) = ckr0;
-        *(float4 *)(s_S0 + ((tid + kThreads) >> 4) * LD + (tid & 15) * 4) = ckr1;
-        *(float4 *)(s_DS + (tid >> 4) * LD + (tid & 15) * 4) = dsr0;
-        *(float4 *)(s_DS + ((tid + kThreads) >> 4) * LD + (tid & 15) * 4) = dsr1;
+        *(float4 *)(s_S0 + (tid >> 4) * LD + (tid & 15) * 4) = ckr;
+        *(float4 *)(s_DS + (tid >> 4) * LD + (tid & 15) * 4) = dsr;
         issue(max(c - 1, c_lo));
         lds_barrier();
         relane();
 
-        // ---- P1: per-column rows, one role per wave (lane = key column j); each
-        //      role reads its inputs before its first store
-        {
-            const int role = __builtin_amdgcn_readfirstlane(wave), j = lane;
+        // ---- P1: waves 0-7: per-column rows, one role per wave (lane = key
+        //      column j), each role reading its inputs before its first store;
+        //      waves 8-11: dR^ = dY S_0, waves 12-15: dK^ = V dS_C (key columns
+        //      16 (w & 3)..)
+        if (wave < 8) {
+            const int role = wave, j = lane;
             const int st = role == 0 || role == 4 ? IA : role == 1 || role == 5 ? IR
                          : role == 2 || role == 6 ? IB : IK;
             float wv[16], xv[16];
@@ -360,25 +352,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                     s_BL[(24 + 4 * ko + e) * LD + j] = os[8 + e];      // s = 8+e scaled to 12
                 }
             }
+        } else {
+            const int jc = 16 * w4;
+            const bool isR = wave < 12;
+            f32x4 g = {0.f, 0.f, 0.f, 0.f};
+            g = mm_AtB(g, isR ? sDY : sV, LD, (isR ? s_S0 : s_DS) + jc, LD, l16, kq, 64);
+            float *dst = s_G + (isR ? 1 : 3) * 16 * LD + jc + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = g[r];
         }
         lds_barrier();
         relane();
 
-        // ---- P2: waves 0-3: P_a = A^ S_0^T (value rows 16*w4..) and dR^ = dY S_0
-        //      (key columns 16*w4..). Waves 4, 5: the split-point products;
-        //      waves 6, 7: the within-sub-chunk pairs; waves 4-7: dK^ = V dS_C
-        //      (key columns 16*(w-4)..); wave 6: dM_rk = dY V^T
-        f32x4 pa = {0.f, 0.f, 0.f, 0.f};
-        {
-            const int jc = 16 * w4;
-            if (lo) {
-                pa = mm_AtBt(pa, s_Q, LD, s_S0 + 16 * it * LD, LD, l16, kq, 64);
-                f32x4 g1 = {0.f, 0.f, 0.f, 0.f};
-                g1 = mm_AtB(g1, sDY, LD, s_S0 + jc, LD, l16, kq, 64);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) s_G[(1 * 16 + 4 * kq + r) * LD + jc + l16] = g1[r];
-            } else {
-                if (wave < 6) {
+        // ---- P2: waves 0-3: P_a = A^ S_0^T (value rows 16 w..); waves 4, 5: the
+        //      split-point products; waves 6-9: the within-sub-chunk pairs;
+        //      waves 10-13: dX = B^ dS_C^T (value rows 16 (w-10)..); wave 14:
+        //      dM_rk = dY V^T; wave 15: d gamma_C[j] = sum_i dS_C[i][j] S_0[i][j]
+        f32x4 pa = {0.f, 0.f, 0.f, 0.f};            // waves 0-3 (then rhs, X)
+        f32x4 dx = {0.f, 0.f, 0.f, 0.f};            // waves 10-13 (then drhs)
+        if (wave < 4) {
+            pa = mm_AtBt(pa, s_Q, LD, s_S0 + 16 * w4 * LD, LD, l16, kq, 64);
+        } else if (wave < 6) {
                     const int tile = wave - 4, m = l16;
                     const float *arow, *brow;
                     if (tile == 0) {
@@ -395,78 +389,82 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                         const TileEntry e = tile_entry(tile, 4 * kq + r, l16);
                         if (e.valid) s_M[tile_matrix(e, MLAB) * 256 + e.t * 16 + e.s] = d[r];
                     }
-                } else {
-                    // 64 items (sub-chunk p, pair k) x 4 quarters of the 64 columns
-                    // = 256 units, two per lane of waves 6 and 7
-                    float db[2], dk[2];
-                    int tt[2], ss[2];
-                    bool lt[2];
-#pragma unroll
-                    for (int v = 0; v < 2; ++v) {
-                        const int unit_ = tid - 384 + 128 * v;
-                        const int item = unit_ >> 2, qtr = unit_ & 3;
-                        const int sc = item >> 4, kk = item & 15;
-                        int et, es;
-                        const bool isL = kk < 6;
-                        if (isL) {                 // s < t
-                            et = 1 + (kk >= 1) + (kk >= 3);
-                            es = kk - et * (et - 1) / 2;
-                        } else {                   // s <= t
-                            const int mi = kk - 6;
-                            et = (mi >= 1) + (mi >= 3) + (mi >= 6);
-                            es = mi - et * (et + 1) / 2;
-                        }
-                        const int t = 4 * sc + et, s = 4 * sc + es;
-                        const float *ar = s_AR + ((isL ? 0 : 16) + t) * LD + 16 * qtr;
-                        const float *bd = s_BD + s * LD + 16 * qtr;
-                        const float *kd = s_KD + s * LD + 16 * qtr;
-                        float b_ = 0.f, k_ = 0.f;
-#pragma unroll
-                        for (int jj = 0; jj < 16; jj += 4) {
-                            const float4 x = *(const float4 *)(ar + jj);
-                            const float4 b = *(const float4 *)(bd + jj);
-                            const float4 k4 = *(const float4 *)(kd + jj);
-                            b_ = fmaf(x.x, b.x, b_); k_ = fmaf(x.x, k4.x, k_);
-                            b_ = fmaf(x.y, b.y, b_); k_ = fmaf(x.y, k4.y, k_);
-                            b_ = fmaf(x.z, b.z, b_); k_ = fmaf(x.z, k4.z, k_);
-                            b_ = fmaf(x.w, b.w, b_); k_ = fmaf(x.w, k4.w, k_);
-                        }
-                        db[v] = b_; dk[v] = k_; tt[v] = t; ss[v] = s; lt[v] = isL;
-                    }
-#pragma unroll
-                    for (int v = 0; v < 2; ++v) {
-                        const float b_ = quad_sum(db[v]), k_ = quad_sum(dk[v]);
-                        if ((lane & 3) == 0) {
-                            const int o = tt[v] * 16 + ss[v];
-                            s_M[(lt[v] ? MLAB : MMRB) * 256 + o] = b_;
-                            s_M[(lt[v] ? MLAK : MMRK) * 256 + o] = k_;
-                        }
-                    }
-                    if (wave == 6) {
-                        f32x4 gm = {0.f, 0.f, 0.f, 0.f};
-                        gm = mm_AtBt(gm, sDY, LD, sV, LD, l16, kq, 64);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int t = 4 * kq + r;
-                            const float v = l16 <= t ? gm[r] : 0.f;
-                            s_M[MDMRK * 256 + t * 16 + l16] = v;
-                            tile_scatter(s_M, false, false, t, l16, v);
-                        }
-                    }
-                }
-                f32x4 g3 = {0.f, 0.f, 0.f, 0.f};
-                g3 = mm_AtB(g3, sV, LD, s_DS + jc, LD, l16, kq, 64);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) s_G[(3 * 16 + 4 * kq + r) * LD + jc + l16] = g3[r];
+        } else if (wave < 10) {
+            // 64 items (sub-chunk p, pair k) x 4 quarters of the 64 columns
+            // = 256 units, one per lane of waves 6-9
+            const int unit_ = (wave - 6) * 64 + lane;
+            const int item = unit_ >> 2, qtr = unit_ & 3;
+            const int sc = item >> 4, kk = item & 15;
+            int et, es;
+            const bool isL = kk < 6;
+            if (isL) {                 // s < t
+                et = 1 + (kk >= 1) + (kk >= 3);
+                es = kk - et * (et - 1) / 2;
+            } else {                   // s <= t
+                const int mi = kk - 6;
+                et = (mi >= 1) + (mi >= 3) + (mi >= 6);
+                es = mi - et * (et + 1) / 2;
             }
+            const int t = 4 * sc + et, s = 4 * sc + es;
+            const float *ar = s_AR + ((isL ? 0 : 16) + t) * LD + 16 * qtr;
+            const float *bd = s_BD + s * LD + 16 * qtr;
+            const float *kd = s_KD + s * LD + 16 * qtr;
+            float b_ = 0.f, k_ = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 16; jj += 4) {
+                const float4 x = *(const float4 *)(ar + jj);
+                const float4 b = *(const float4 *)(bd + jj);
+                const float4 k4 = *(const float4 *)(kd + jj);
+                b_ = fmaf(x.x, b.x, b_); k_ = fmaf(x.x, k4.x, k_);
+                b_ = fmaf(x.y, b.y, b_); k_ = fmaf(x.y, k4.y, k_);
+                b_ = fmaf(x.z, b.z, b_); k_ = fmaf(x.z, k4.z, k_);
+                b_ = fmaf(x.w, b.w, b_); k_ = fmaf(x.w, k4.w, k_);
+            }
+            b_ = quad_sum(b_);
+            k_ = quad_sum(k_);
+            if ((lane & 3) == 0) {
+                const int o = t * 16 + s;
+                s_M[(isL ? MLAB : MMRB) * 256 + o] = b_;
+                s_M[(isL ? MLAK : MMRK) * 256 + o] = k_;
+            }
+        } else if (wave < 14) {
+            const int i0 = 16 * (wave - 10);
+            dx = mm_AtBt(dx, s_BK, LD, s_DS + i0 * LD, LD, l16, kq, 64);
+        } else if (wave == 14) {
+            f32x4 gm = {0.f, 0.f, 0.f, 0.f};
+            gm = mm_AtBt(gm, sDY, LD, sV, LD, l16, kq, 64);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * kq + r;
+                const float v = l16 <= t ? gm[r] : 0.f;
+                s_M[MDMRK * 256 + t * 16 + l16] = v;
+                tile_scatter(s_M, false, false, t, l16, v);
+            }
+        } else {
+            const int j = lane;
+            float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll 8
+            for (int i = 0; i < 64; i += 2) {
+                acc0 = fmaf(s_DS[i * LD + j], s_S0[i * LD + j], acc0);
+                acc1 = fmaf(s_DS[(i + 1) * LD + j], s_S0[(i + 1) * LD + j], acc1);
+            }
+            s_dgC[j] = acc0 + acc1;
         }
         lds_barrier();
         relane();
 
-        // ---- P3: W = (I - L_ab)^-1 (wave 0: column c = lane / 4, rows
-        //      t = lane % 4 + 4i held by the 4 lanes of a quad, forward
-        //      substitution); d gamma_C[j] = sum_i dS_C[i][j] S_0[i][j] (wave 1)
-        if (wave == 0) {
+        // ---- P3: wave 8: W = (I - L_ab)^-1 (column c = lane / 4, rows t =
+        //      lane % 4 + 4i held by the 4 lanes of a quad, forward substitution);
+        //      waves 0-3: rhs = P_a + L_ak V; waves 4-7: dV partial = K^ dS_C^T +
+        //      M_rk^T dY (value rows 16 (w-4)..); waves 10-13: dX += M_rb^T dY
+        f32x4 dvp = {0.f, 0.f, 0.f, 0.f};           // waves 4-7
+        if (wave < 4) {
+            pa = mm_AtB(pa, Mlak, 16, sV + 16 * w4, LD, l16, kq, 16);
+        } else if (wave < 8) {
+            const int i0 = 16 * w4;
+            dvp = mm_AtBt(dvp, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq, 64);
+            dvp = mm_TB(dvp, Mmrk, 16, sDY + i0, LD, l16, kq);
+        } else if (wave == 8) {
             const int col = lane >> 2, q = lane & 3;
             float Lr[4][16], x[4];
 #pragma unroll
@@ -489,142 +487,110 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) s_M[MW * 256 + (q + 4 * i) * 16 + col] = x[i];
-        } else if (wave == 1) {
-            const int j = lane;
-            float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll 8
-            for (int i = 0; i < 64; i += 2) {
-                acc0 = fmaf(s_DS[i * LD + j], s_S0[i * LD + j], acc0);
-                acc1 = fmaf(s_DS[(i + 1) * LD + j], s_S0[(i + 1) * LD + j], acc1);
-            }
-            s_dgC[j] = acc0 + acc1;
+        } else if (wave >= 10 && wave < 14) {
+            dx = mm_TB(dx, Mmrb, 16, sDY + 16 * (wave - 10), LD, l16, kq);
         }
         lds_barrier();
         relane();
 
-        // ---- P4: value side. waves 0-3 (rows 16*w4..): X = W (P_a + L_ak V);
-        //      dX = B^ dS_C^T + M_rb^T dY; drhs = W^T dX.
-        //      waves 4-7 (same rows): dV partial = K^ dS_C^T + M_rk^T dY
-        const int i0 = 16 * it;
-        f32x4 dvp = {0.f, 0.f, 0.f, 0.f};
-        if (lo) {
-            const f32x4 rhs = mm_AtB(pa, Mlak, 16, sV + i0, LD, l16, kq, 16);
-            f32x4 xx = {0.f, 0.f, 0.f, 0.f};
-            {
+        // ---- P4: waves 0-3: X = W rhs; waves 10-13: drhs = W^T dX (value rows
+        //      16 (w & 3)..), both into LDS
+        if (wave < 4 || (wave >= 10 && wave < 14)) {
+            const int i0 = 16 * (wave < 4 ? wave : wave - 10);
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+            if (wave < 4) {
                 const float4 wr = *(const float4 *)(Mw + l16 * 16 + 4 * kq);
-                xx = mfma4(wr.x, rhs[0], xx); xx = mfma4(wr.y, rhs[1], xx);
-                xx = mfma4(wr.z, rhs[2], xx); xx = mfma4(wr.w, rhs[3], xx);
-            }
-            f32x4 dx = {0.f, 0.f, 0.f, 0.f};
-            dx = mm_AtBt(dx, s_BK, LD, s_DS + i0 * LD, LD, l16, kq, 64);
-            dx = mm_TB(dx, Mmrb, 16, sDY + i0, LD, l16, kq);
-            f32x4 dr = {0.f, 0.f, 0.f, 0.f};
+                o = mfma4(wr.x, pa[0], o); o = mfma4(wr.y, pa[1], o);
+                o = mfma4(wr.z, pa[2], o); o = mfma4(wr.w, pa[3], o);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dr = mfma4(Mw[(4 * kq + e) * 16 + l16], dx[e], dr);
+                for (int e = 0; e < 4; ++e) o = mfma4(Mw[(4 * kq + e) * 16 + l16], dx[e], o);
+            }
+            float *dst = (wave < 4 ? s_X : s_DR) + i0 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = o[r];
+        }
+        lds_barrier();
+        relane();
+
+        // ---- P5: waves 4-7 finish dV = partial + L_ak^T drhs and store it;
+        //      waves 0-3: dA^ = drhs S_0, waves 8-11: dB^ = X dS_C (key columns
+        //      16 (w & 3)..); waves 12, 13, 14: dL_ab = drhs X^T, dL_ak = drhs V^T,
+        //      dM_rb = dY X^T
+        if (wave >= 4 && wave < 8) {
+            const int i0 = 16 * w4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int k = 4 * kq + e;
+                dvp = mfma4(Mlak[k * 16 + l16], s_DR[k * LD + i0 + l16], dvp);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * kq + r;
-                s_X[t * LD + i0 + l16] = xx[r];
-                s_DR[t * LD + i0 + l16] = dr[r];
+                if (t < L) IO<TI>::st((TI *)p.dv, base + (int64_t)(t0 + t) * ts + i0 + l16, dvp[r]);
             }
-        } else {
-            dvp = mm_AtBt(dvp, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq, 64);
-            dvp = mm_TB(dvp, Mmrk, 16, sDY + i0, LD, l16, kq);
-        }
-        lds_barrier();
-        relane();
-
-        // ---- P5: key side. waves 4-7 finish dV = partial + L_ak^T drhs and
-        //      store it; waves 0-3: dA^ = drhs S_0, waves 4-7: dB^ = X dS_C (key
-        //      columns 16*w4..); waves 0, 1, 2: dL_ab = drhs X^T, dL_ak = drhs V^T,
-        //      dM_rb = dY X^T
-        {
+        } else if (wave < 12) {
             const int jc = 16 * w4;
-            if (!lo) {
+            const bool isA = wave < 4;
+            f32x4 g = {0.f, 0.f, 0.f, 0.f};
+            g = mm_AtB(g, isA ? s_DR : s_X, LD, (isA ? s_S0 : s_DS) + jc, LD, l16, kq, 64);
+            float *dst = s_G + (isA ? 0 : 2) * 16 * LD + jc + l16;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int k = 4 * kq + e;
-                    dvp = mfma4(Mlak[k * 16 + l16], s_DR[k * LD + i0 + l16], dvp);
-                }
+            for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = g[r];
+        } else if (wave < 15) {
+            const int mi = wave - 12;                    // dL_ab, dL_ak, dM_rb
+            const float *lhs = mi < 2 ? s_DR : sDY;
+            const float *rt = mi == 1 ? sV : s_X;
+            f32x4 gm = {0.f, 0.f, 0.f, 0.f};
+            gm = mm_AtBt(gm, lhs, LD, rt, LD, l16, kq, 64);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 4 * kq + r;
-                    if (t < L) IO<TI>::st((TI *)p.dv, base + (int64_t)(t0 + t) * ts + i0 + l16, dvp[r]);
-                }
-                f32x4 g2 = {0.f, 0.f, 0.f, 0.f};
-                g2 = mm_AtB(g2, s_X, LD, s_DS + jc, LD, l16, kq, 64);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) s_G[(2 * 16 + 4 * kq + r) * LD + jc + l16] = g2[r];
-            } else {
-                f32x4 g0 = {0.f, 0.f, 0.f, 0.f};
-                g0 = mm_AtB(g0, s_DR, LD, s_S0 + jc, LD, l16, kq, 64);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) s_G[(0 * 16 + 4 * kq + r) * LD + jc + l16] = g0[r];
-                if (wave < 3) {
-                    const float *lhs = wave < 2 ? s_DR : sDY;
-                    const float *rt = wave == 1 ? sV : s_X;
-                    f32x4 gm = {0.f, 0.f, 0.f, 0.f};
-                    gm = mm_AtBt(gm, lhs, LD, rt, LD, l16, kq, 64);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = 4 * kq + r;
-                        const bool keep = wave < 2 ? (l16 < t) : (l16 <= t);
-                        const float v = keep ? gm[r] : 0.f;
-                        s_M[(MDLAB + wave) * 256 + t * 16 + l16] = v;
-                        tile_scatter(s_M, wave < 2, wave != 1, t, l16, v);
-                    }
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * kq + r;
+                const bool keep = mi < 2 ? (l16 < t) : (l16 <= t);
+                const float v = keep ? gm[r] : 0.f;
+                s_M[(MDLAB + mi) * 256 + t * 16 + l16] = v;
+                tile_scatter(s_M, mi < 2, mi != 1, t, l16, v);
             }
         }
         lds_barrier();
         relane();
 
-        // ---- P6: pair-gradient products of the split-point tiles (waves 0-3):
-        //      Z_A = dD B_rows (wave 0: tile 1, wave 2: tile 2) and
-        //      Z_B = dD^T A_rows (waves 1, 3), with dD the gathered matrix
-        //      gradients; into s_Z (S_0 is consumed)
-        if (lo) {
-            const int tile = wave >> 1;
-            const bool zb = (wave & 1) != 0;
+        // ---- P6: pair-gradient products of the split-point tiles: Z_A = dD B_rows
+        //      and Z_B = dD^T A_rows of tiles 1, 2 (product w >> 2: Z_A1, Z_B1,
+        //      Z_A2, Z_B2), 16-column block w & 3 of each; into s_Z (S_0 is consumed)
+        {
+            const int prod = wave >> 2, q = w4;
+            const int tile = prod >> 1;
+            const bool zb = (prod & 1) != 0;
             const float *dD = s_M + (MDD1 + tile) * 256;
-            // A operand: this lane's row l16 of dD (Z_A) or of dD^T (Z_B), k = 4kq+e
-            float av[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) av[e] = dD[zb ? (4 * kq + e) * 16 + l16 : l16 * 16 + 4 * kq + e];
-            // B operand rows k = 4kq+e: B_rows (Z_A) or A_rows (Z_B) of the tile
-            const float *brow[4];
+            float av[4], bv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+                av[e] = dD[zb ? (4 * kq + e) * 16 + l16 : l16 * 16 + 4 * kq + e];
                 const int r_ = 4 * kq + e;
+                const float *brow;
                 if (!zb) {
-                    brow[e] = s_BL + (tile == 0 ? r_ : 16 + r_) * LD;
+                    brow = s_BL + (tile == 0 ? r_ : 16 + r_) * LD;
                 } else if (tile == 0) {
-                    brow[e] = r_ < 4 ? s_AR + (8 + r_) * LD : r_ < 8 ? s_AWR + (r_ - 4) * LD
-                            : r_ < 12 ? s_AR + (16 + r_) * LD : s_AWR + (r_ - 8) * LD;
+                    brow = r_ < 4 ? s_AR + (8 + r_) * LD : r_ < 8 ? s_AWR + (r_ - 4) * LD
+                         : r_ < 12 ? s_AR + (16 + r_) * LD : s_AWR + (r_ - 8) * LD;
                 } else {
-                    brow[e] = s_AR + ((r_ & 4) ? 16 + r_ : 4 + r_) * LD;
+                    brow = s_AR + ((r_ & 4) ? 16 + r_ : 4 + r_) * LD;
                 }
+                bv[e] = brow[16 * q + l16];
             }
-            float bv[4][4];
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int e = 0; e < 4; ++e) z = mfma4(av[e], bv[e], z);
+            float *zo = s_Z + prod * 16 * LD + 16 * q + l16;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) bv[q][e] = brow[e][16 * q + l16];
-            float *zo = s_Z + (2 * tile + (zb ? 1 : 0)) * 16 * LD;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) z = mfma4(av[e], bv[q][e], z);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) zo[(4 * kq + r) * LD + 16 * q + l16] = z[r];
-            }
+            for (int r = 0; r < 4; ++r) zo[(4 * kq + r) * LD] = z[r];
         }
         lds_barrier();
         relane();
 
-        // ---- P7a: per-token gradients of key column j = lane for tokens
-        //      {w, 15-w} (token bodies specialised at compile time): chunk parts,
+        // ---- P7a: per-token gradients of key column j = lane for token t = w
+        //      (token bodies specialised at compile time): chunk parts,
         //      split-point pair parts (Z scaled by the decay factors) and
         //      within-sub-chunk pair parts give dr, da, db, dk (stored); the u
         //      terms go to LDS (dS_C, X, drhs, A^..K^ are consumed)
@@ -727,14 +693,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 if ((t & 4) == 0 && t < 12) s_U(UC13)[o] = b_t * b4 + k_t * k4;
             };
             switch (wave) {
-                case 0: tok(IC<0>{}); tok(IC<15>{}); break;
-                case 1: tok(IC<1>{}); tok(IC<14>{}); break;
-                case 2: tok(IC<2>{}); tok(IC<13>{}); break;
-                case 3: tok(IC<3>{}); tok(IC<12>{}); break;
-                case 4: tok(IC<4>{}); tok(IC<11>{}); break;
-                case 5: tok(IC<5>{}); tok(IC<10>{}); break;
-                case 6: tok(IC<6>{}); tok(IC<9>{}); break;
-                default: tok(IC<7>{}); tok(IC<8>{}); break;
+                case 0: tok(IC<0>{}); break;
+                case 1: tok(IC<1>{}); break;
+                case 2: tok(IC<2>{}); break;
+                case 3: tok(IC<3>{}); break;
+                case 4: tok(IC<4>{}); break;
+                case 5: tok(IC<5>{}); break;
+                case 6: tok(IC<6>{}); break;
+                case 7: tok(IC<7>{}); break;
+                case 8: tok(IC<8>{}); break;
+                case 9: tok(IC<9>{}); break;
+                case 10: tok(IC<10>{}); break;
+                case 11: tok(IC<11>{}); break;
+                case 12: tok(IC<12>{}); break;
+                case 13: tok(IC<13>{}); break;
+                case 14: tok(IC<14>{}); break;
+                default: tok(IC<15>{}); break;
             }
         }
         lds_barrier();
@@ -805,7 +779,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 for (int t = 8; t < 12; ++t) { res[t * LD] = acc; acc += c13[t]; }
 #pragma unroll
                 for (int t = 12; t < 16; ++t) res[t * LD] = 0.f;
-            } else {
+            } else if (wave < 8) {
                 // pairs (p0+tt, p0+ss), ss < tt, inside sub-chunk p0 = 4(w-4):
                 // M pairs contain w_m for ss < m-p0 <= tt, L pairs for ss < m-p0 < tt
                 const int p0 = 4 * (wave - 4);
@@ -844,19 +818,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         lds_barrier();
         relane();
 
-        // ---- P7c: u_m for m in {w, 15-w}: the five partial sums and
-        //      d gamma_C gamma_C; dw = u / w; store
+        // ---- P7c: u_m for m = w: the five partial sums and d gamma_C gamma_C;
+        //      dw = u / w; store
         {
-            const int j = lane;
-            const float dgc = s_dgC[j] * s_gC[j];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int m = q == 0 ? wave : 15 - wave;
-                const int o = m * LD + j;
-                const float x = dgc + ((s_Z[o] + s_Z[16 * LD + o]) + (s_Z[32 * LD + o] + s_Z[48 * LD + o]))
-                              + s_G[o];
-                if (m < L) IO<TI>::st((TI *)p.dw, base + (int64_t)(t0 + m) * ts + j, x / s_in[IW * 16 * LD + o]);
-            }
+            const int j = lane, m = wave;
+            const int o = m * LD + j;
+            const float x = s_dgC[j] * s_gC[j] + ((s_Z[o] + s_Z[16 * LD + o]) + (s_Z[32 * LD + o] + s_Z[48 * LD + o]))
+                          + s_G[o];
+            if (m < L) IO<TI>::st((TI *)p.dw, base + (int64_t)(t0 + m) * ts + j, x / s_in[IW * 16 * LD + o]);
         }
     }
 }

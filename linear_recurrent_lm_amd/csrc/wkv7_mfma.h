@@ -77,4 +77,18 @@ __device__ __forceinline__ void raw_unpack(const Raw<float, K> &r, int k, float 
     x[4] = r.q[k][1].x; x[5] = r.q[k][1].y; x[6] = r.q[k][1].z; x[7] = r.q[k][1].w;
 }
 
+// Four consecutive input elements (one 8- or 16-byte load) per staging group.
+template <typename TI> struct Raw4;
+template <> struct Raw4<uint16_t> { uint2 q; };
+template <> struct Raw4<float> { float4 q; };
+__device__ __forceinline__ void raw4_load(const uint16_t *p, Raw4<uint16_t> &r) { r.q = *(const uint2 *)p; }
+__device__ __forceinline__ void raw4_load(const float *p, Raw4<float> &r) { r.q = *(const float4 *)p; }
+__device__ __forceinline__ void raw4_unpack(const Raw4<uint16_t> &r, float *x) {
+    x[0] = __uint_as_float(r.q.x << 16); x[1] = __uint_as_float(r.q.x & 0xffff0000u);
+    x[2] = __uint_as_float(r.q.y << 16); x[3] = __uint_as_float(r.q.y & 0xffff0000u);
+}
+__device__ __forceinline__ void raw4_unpack(const Raw4<float> &r, float *x) {
+    x[0] = r.q.x; x[1] = r.q.y; x[2] = r.q.z; x[3] = r.q.w;
+}
+
 }  // namespace wkv7
