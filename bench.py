@@ -64,11 +64,12 @@ def measured_traffic(kernel):
             rec = json.load(fh).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec:
+    if not rec or "sources" not in rec:
         return None
-    src = os.path.join(ROOT, "linear_recurrent_lm_amd", "csrc", rec["source"])
-    if not os.path.exists(src) or source_digest(src) != rec["source_sha256_16"]:
-        return None
+    for name, sha in rec["sources"].items():
+        src = os.path.join(ROOT, "linear_recurrent_lm_amd", "csrc", name)
+        if not os.path.exists(src) or source_digest(src) != sha:
+            return None
     return rec["bytes_per_launch"]
 
 
@@ -239,7 +240,8 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(dom_name)
-    roof["kernel"] = dom_name
+    roof["kernel"] = {"wkv7_backward": "wkv7_backward (dsweep_kernel + bwd_chunk_kernel)",
+                      "wkv7_forward_ckpt": "wkv7_forward (fwd_ws_kernel)"}[dom_name]
 
     def fracs(k):
         kk = kernels[k]

@@ -115,9 +115,17 @@ wkv7_status wkv7_forward(const wkv7_desc *d,
  *   ds_out : [S,H,N,N] fp32 upstream gradient of the final state, or NULL.
  *   dr..db : [B,T,H,N] outputs (dtype); required.
  *   ds0    : [S,H,N,N] fp32 gradient of the initial state, or NULL.
- *   workspace / workspace_bytes : scratch of at least wkv7_workspace_bytes.
+ *   workspace / workspace_bytes : device memory of at least
+ *           wkv7_workspace_bytes, 16-byte aligned, owned by the caller. The
+ *           call overwrites it with the fp32 gradient of the state leaving
+ *           each 16-token chunk (one 64x64 slot per checkpoint slot and
+ *           head) and reads it back within the same call; calls that may run
+ *           concurrently need separate workspaces. Too small or NULL when
+ *           needed: WKV7_ERR_WORKSPACE_TOO_SMALL, before any HIP call.
  * The recurrence is recomputed from the 16-token checkpoints in fp32, not
- * reconstructed by dividing by the decay.
+ * reconstructed by dividing by the decay. Two kernels run back to back on
+ * `stream`: a reverse sweep that carries only the state gradient, then the
+ * per-chunk gradients, all chunks in parallel.
  */
 wkv7_status wkv7_backward(const wkv7_desc *d,
                           const void *r, const void *w, const void *k,
@@ -144,7 +152,9 @@ wkv7_status wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype,
 /* Number of checkpoint slots a dense forward needs: B * ceil(T / 16). */
 wkv7_status wkv7_checkpoint_slots(int32_t B, int32_t T, int64_t *slots);
 
-/* Scratch bytes wkv7_backward needs for this descriptor (may be 0). */
+/* Workspace bytes wkv7_backward needs for this descriptor: checkpoint slots
+ * (B * ceil(T / 16) dense, the segment table's slot count otherwise) x H x
+ * 64 x 64 x 4. */
 wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes);
 
 /*
