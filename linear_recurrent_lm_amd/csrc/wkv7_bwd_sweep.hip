@@ -17,8 +17,11 @@
 // other and are computed in parallel by the second pass.
 //
 // The structure mirrors the forward kernel: state waves hold 16 value rows x
-// 64 columns of dS^T in MFMA accumulators (lane l: dS[row0 + l%16][16*jt +
-// 4*(l/16) + r]); eight operand waves build, one chunk ahead, the rows B^,
+// 64/KS columns of dS^T in MFMA accumulators (lane l: dS[row0 + l%16][16*jt +
+// 4*(l/16) + r]); with KS = 2 the two waves sharing 16 rows hold one half of
+// the key columns each and add each other's partial dX (a sum over keys)
+// through LDS, so the serial chain spreads over four SIMDs when a workgroup
+// holds only 32 rows. Eight operand waves build, one chunk ahead, the rows B^,
 // A^, R^, gamma_C, dY and the 16x16 matrices M_rb and W (L_ab only feeds W),
 // with the same split-point products and within-sub-chunk dot products, into
 // a double-buffered LDS hand-off; two workgroup barriers per chunk. The
@@ -56,14 +59,18 @@ constexpr int B_DYT = B_ART + 64 * KLD;     // [64][VLD] dY by value row i
 constexpr int B_M = B_DYT + 64 * VLD;       // [2][16][MLD] M_rb^T, W^T
 constexpr int B_GC = B_M + 2 * 16 * MLD;    // [64] gamma_C
 constexpr int BUF_SIZE = B_GC + 64;
-constexpr int TOTAL = BUF + 2 * BUF_SIZE;
+constexpr int XCH = BUF + 2 * BUF_SIZE;     // [4 waves][64 lanes][4] partial dX (key split)
+constexpr int TOTAL = XCH + 4 * 256;
 static_assert(BUF % 4 == 0 && BUF_SIZE % 4 == 0 && IN_SIZE % 4 == 0, "16-byte aligned buffers");
 }  // namespace lay
 
-template <typename TI, int NMW>
+template <typename TI, int NMW, int KS>
 __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdArgs p, int32_t units) {
-    constexpr int RB = 16 * NMW;       // value rows per workgroup
-    constexpr int NRB = 4 / NMW;       // row blocks per unit
+    constexpr int NG = NMW / KS;       // 16-row groups per workgroup
+    constexpr int RB = 16 * NG;        // value rows per workgroup
+    constexpr int NRB = 64 / RB;       // row blocks per unit
+    constexpr int NQ = 4 / KS;         // 16-column key tiles per state wave
+    static_assert(KS == 1 || KS == 2, "key split of 1 or 2");
     extern __shared__ __align__(16) float sm[];
 
     int unit, rb;
@@ -93,17 +100,21 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
 
     if (wave < NMW) {
         // ================= state waves =================
-        const int irow = i0 + 16 * wave + l16;           // value row of this lane
-        f32x4 acc[4];                                    // dS^T tiles
+        const int rg = wave % NG, kh = wave / NG;        // row group, key part
+        const int irow = i0 + 16 * rg + l16;             // value row of this lane
+        const int q0 = kh * NQ;                          // first key tile of this wave
+        f32x4 acc[NQ];                                   // dS^T tiles
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int qq = 0; qq < NQ; ++qq) {
             if (p.ds_out) {
-                const float4 v4 = *(const float4 *)(p.ds_out + sbase + (int64_t)irow * kN + 16 * q + 4 * kq);
-                acc[q] = f32x4{v4.x, v4.y, v4.z, v4.w};
+                const float4 v4 = *(const float4 *)(p.ds_out + sbase + (int64_t)irow * kN + 16 * (q0 + qq) + 4 * kq);
+                acc[qq] = f32x4{v4.x, v4.y, v4.z, v4.w};
             } else {
-                acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+                acc[qq] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
+        float *xch_own = sm + lay::XCH + wave * 256 + lane * 4;
+        const float *xch_mate = sm + lay::XCH + (rg + (1 - kh) * NG) * 256 + lane * 4;
         // Iteration k advances chunk cs = nch - k (built in iteration k - 1).
 #pragma unroll 1
         for (int k = 0; k <= nch; ++k) {
@@ -112,57 +123,70 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
             f32x4 dx = {0.f, 0.f, 0.f, 0.f};
             lds_barrier();
             // ---- phase X (W of this chunk is being solved meanwhile): store dS_C;
-            //      dX = B^ dS_C^T + M_rb^T dY; dS^T = diag(gamma) dS^T + R^^T dY
+            //      dX = B^ dS_C^T (over this wave's key columns) + M_rb^T dY (one
+            //      key part when split); dS^T = diag(gamma) dS^T + R^^T dY
             if (k >= 1) {
                 float *wp = p.ws + ((u.ckpt + cs) * H + h) * (int64_t)(kN * kN) + (int64_t)irow * kN;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *(float4 *)(wp + 16 * q + 4 * kq) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+                for (int qq = 0; qq < NQ; ++qq)
+                    *(float4 *)(wp + 16 * (q0 + qq) + 4 * kq) =
+                        make_float4(acc[qq][0], acc[qq][1], acc[qq][2], acc[qq][3]);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int qq = 0; qq < NQ; ++qq) {
+                    const int q = q0 + qq;
                     const float4 b4 = *(const float4 *)(buf + lay::B_BH + l16 * QLD + 16 * q + 4 * kq);
-                    dx = mfma4(b4.x, acc[q][0], dx);
-                    dx = mfma4(b4.y, acc[q][1], dx);
-                    dx = mfma4(b4.z, acc[q][2], dx);
-                    dx = mfma4(b4.w, acc[q][3], dx);
+                    dx = mfma4(b4.x, acc[qq][0], dx);
+                    dx = mfma4(b4.y, acc[qq][1], dx);
+                    dx = mfma4(b4.z, acc[qq][2], dx);
+                    dx = mfma4(b4.w, acc[qq][3], dx);
                 }
                 const float4 dyb = *(const float4 *)(buf + lay::B_DYT + irow * VLD + 4 * kq);
-                const float4 mrbt = *(const float4 *)(buf + lay::B_M + MMRBT * 16 * MLD + l16 * MLD + 4 * kq);
-                dx = mfma4(mrbt.x, dyb.x, dx); dx = mfma4(mrbt.y, dyb.y, dx);
-                dx = mfma4(mrbt.z, dyb.z, dx); dx = mfma4(mrbt.w, dyb.w, dx);
+                if (KS == 1 || kh == 0) {
+                    const float4 mrbt = *(const float4 *)(buf + lay::B_M + MMRBT * 16 * MLD + l16 * MLD + 4 * kq);
+                    dx = mfma4(mrbt.x, dyb.x, dx); dx = mfma4(mrbt.y, dyb.y, dx);
+                    dx = mfma4(mrbt.z, dyb.z, dx); dx = mfma4(mrbt.w, dyb.w, dx);
+                }
+                if (KS > 1) *(float4 *)xch_own = make_float4(dx[0], dx[1], dx[2], dx[3]);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int qq = 0; qq < NQ; ++qq) {
+                    const int q = q0 + qq;
                     const float4 g4 = *(const float4 *)(buf + lay::B_GC + 16 * q + 4 * kq);
                     const float4 r4 = *(const float4 *)(buf + lay::B_ART + (16 * q + l16) * KLD + 16 + 4 * kq);
-                    f32x4 a = acc[q];
+                    f32x4 a = acc[qq];
                     a[0] *= g4.x; a[1] *= g4.y; a[2] *= g4.z; a[3] *= g4.w;
                     a = mfma4(r4.x, dyb.x, a); a = mfma4(r4.y, dyb.y, a);
                     a = mfma4(r4.z, dyb.z, a); a = mfma4(r4.w, dyb.w, a);
-                    acc[q] = a;
+                    acc[qq] = a;
                 }
             }
             lds_barrier();
-            // ---- phase Y: drhs = W^T dX; dS^T += A^^T drhs
+            // ---- phase Y: (add the partner's partial dX); drhs = W^T dX;
+            //      dS^T += A^^T drhs
             if (k >= 1) {
+                if (KS > 1) {
+                    const float4 pd = *(const float4 *)xch_mate;
+                    dx[0] += pd.x; dx[1] += pd.y; dx[2] += pd.z; dx[3] += pd.w;
+                }
                 const float4 wt = *(const float4 *)(buf + lay::B_M + MWT * 16 * MLD + l16 * MLD + 4 * kq);
                 f32x4 dr = {0.f, 0.f, 0.f, 0.f};
                 dr = mfma4(wt.x, dx[0], dr); dr = mfma4(wt.y, dx[1], dr);
                 dr = mfma4(wt.z, dx[2], dr); dr = mfma4(wt.w, dx[3], dr);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int qq = 0; qq < NQ; ++qq) {
+                    const int q = q0 + qq;
                     const float4 a4 = *(const float4 *)(buf + lay::B_ART + (16 * q + l16) * KLD + 4 * kq);
-                    f32x4 a = acc[q];
+                    f32x4 a = acc[qq];
                     a = mfma4(a4.x, dr[0], a); a = mfma4(a4.y, dr[1], a);
                     a = mfma4(a4.z, dr[2], a); a = mfma4(a4.w, dr[3], a);
-                    acc[q] = a;
+                    acc[qq] = a;
                 }
             }
         }
         if (p.ds0) {
             float *op = p.ds0 + sbase + (int64_t)irow * kN;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *(float4 *)(op + 16 * q + 4 * kq) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+            for (int qq = 0; qq < NQ; ++qq)
+                *(float4 *)(op + 16 * (q0 + qq) + 4 * kq) = make_float4(acc[qq][0], acc[qq][1], acc[qq][2], acc[qq][3]);
         }
         return;
     }
@@ -489,11 +513,11 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
     }
 }
 
-template <typename TI, int NMW>
+template <typename TI, int NMW, int KS>
 hipError_t launch_sweep(const BwdArgs &a, int32_t units, hipStream_t stream) {
-    constexpr int NRB = 4 / NMW;
+    constexpr int NRB = 64 / (16 * NMW / KS);
     const size_t lds = (size_t)lay::TOTAL * sizeof(float);
-    auto fn = dsweep_kernel<TI, NMW>;
+    auto fn = dsweep_kernel<TI, NMW, KS>;
     hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t blocks = NRB == 1 ? units : ((int64_t)units + 7) / 8 * 8 * NRB;
@@ -505,9 +529,9 @@ template <typename TI>
 hipError_t launch_sweep_typed(const BwdArgs &a, hipStream_t stream) {
     const int S = a.seg.num_seqs > 0 ? a.seg.num_seqs : a.seg.B;
     const int32_t units = S * a.seg.H;
-    if (units >= 256) return launch_sweep<TI, 4>(a, units, stream);
-    if (units >= 128) return launch_sweep<TI, 2>(a, units, stream);
-    return launch_sweep<TI, 1>(a, units, stream);
+    if (units >= 256) return launch_sweep<TI, 4, 1>(a, units, stream);
+    if (units >= 128) return launch_sweep<TI, 4, 2>(a, units, stream);
+    return launch_sweep<TI, 2, 2>(a, units, stream);
 }
 
 }  // namespace

@@ -117,6 +117,35 @@ def test_forward_d2048_prefill_sampled(W):
     assert e["y"] <= U.TOL_BF16_Y and e["s_out"] <= U.TOL_F32 and e["ckpt"] <= U.TOL_F32, e
 
 
+def test_forward_training_workload_sampled(W):
+    """bf16, B=4, T=4096, H=32 (128 units: two 32-row workgroups per unit,
+    state waves split by key columns), random initial state: y, s_out and
+    checkpoints on sampled units."""
+    e = _sampled_forward(W, 4, 4096, 32, seed=3, s0_std=0.1)
+    assert e["y"] <= U.TOL_BF16_Y and e["s_out"] <= U.TOL_F32 and e["ckpt"] <= U.TOL_F32, e
+
+
+@pytest.mark.parametrize("H", [64, 128])
+def test_workgroup_shapes_f32(W, H):
+    """fp32, B=2, T=77: 128 units run the forward and the state-gradient sweep
+    as two 32-row workgroups per unit with key-split state waves, 256 units as
+    one 64-row workgroup; every unit, forward and backward, against the oracle."""
+    B, T = 2, 77
+    inp = synth.make_inputs(B, T, H, 64, seed=300 + H, dtype="f32", s0_std=0.1,
+                            with_dy=True, ds_out_std=0.1)
+    _, _, y, s_out, ckpt = run_forward(W, inp)
+    ref = O.forward(*inp.streams(), s0=inp.s0, checkpoints=True)
+    nc = -(-T // 16)
+    assert U.unit_err_dense(U.host(y), ref["y"]) <= U.TOL_F32
+    assert U.unit_err_state(U.host(s_out), ref["s_out"]) <= U.TOL_F32
+    assert U.unit_err_ckpt(U.host(ckpt), ref["ckpt"], [0, nc], [nc, nc]) <= U.TOL_F32
+    g, _ = run_backward(W, inp)
+    gr = O.backward(*inp.streams(), s0=inp.s0, dy=inp.dy, ds_out=inp.ds_out)
+    for n in ("dr", "dw", "dk", "dv", "da", "db"):
+        assert U.unit_err_dense(g[n], gr[n]) <= 1e-4, n
+    assert U.unit_err_state(g["ds0"], gr["ds0"]) <= 1e-4
+
+
 def test_forward_deterministic(W):
     import torch
     inp = synth.make_inputs(2, 100, 4, 64, seed=9, dtype="bf16", s0_std=0.1)
