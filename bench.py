@@ -145,6 +145,7 @@ def main():
     s_out = torch.empty((B, H, N, N), device=dev, dtype=torch.float32)
     ckpt = torch.empty((W.checkpoint_slots(B, T), H, N, N), device=dev, dtype=torch.float32)
     grads = {n: torch.empty_like(ts[0]) for n in ("dr", "dw", "dk", "dv", "da", "db")}
+    ws = torch.empty(W.wkv7_workspace_bytes(B, T, H, W.BF16), device=dev, dtype=torch.uint8)
 
     # Forward-only prefill workload (B=16, T=1024, H=32, random initial state).
     pin = synth.make_inputs(16, 1024, H, N, seed=2, dtype="bf16", s0_std=0.1)
@@ -162,7 +163,7 @@ def main():
         e0.record()
         W.wkv7_forward(*ts, None, checkpoints=True, y=y, s_out=s_out, ckpt=ckpt)
         e1.record()
-        W.wkv7_backward(*ts, ckpt, dy, None, grads=grads, want_ds0=True)
+        W.wkv7_backward(*ts, ckpt, dy, None, grads=grads, want_ds0=True, workspace=ws)
         e2.record()
         if record is not None:
             record.append((e0, e1, e2))
@@ -222,6 +223,25 @@ def main():
                       args.warmup, args.steps, ev)
     dec_bytes = 512 * H * (2 * N * N * 4 + 7 * N * 2)
 
+    # I/O variants: the prefill workload drawn in fp16; the training step with
+    # w given as log(decay) and fp32 gradients.
+    fin = synth.make_inputs(16, 1024, H, N, seed=2, dtype="f16", s0_std=0.1)
+    fts = [torch.from_numpy(x).to(dev).to(torch.float16) for x in fin.streams()]
+    fy = torch.empty_like(fts[0])
+    f16_ms = _time_ms(lambda: W.wkv7_forward(*fts, ps0, y=fy, s_out=pso), args.warmup, args.steps, ev)
+    del fts, fy
+    lin = synth.make_inputs(B, T, H, N, seed=3, dtype="bf16", with_dy=True, decay="log")
+    lts = [torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in lin.streams()]
+    g32 = {n: torch.empty(lts[0].shape, device=dev, dtype=torch.float32) for n in grads}
+
+    def log_step():
+        W.wkv7_forward(*lts, None, checkpoints=True, y=y, s_out=s_out, ckpt=ckpt, decay="log")
+        W.wkv7_backward(*lts, ckpt, dy, None, grads=g32, want_ds0=True, workspace=ws,
+                        decay="log", grad_f32=True)
+
+    log_ms = _time_ms(log_step, args.warmup, args.steps, ev)
+    del lts, g32
+
     f_ms, b_ms = float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
     th = tok * H
     kernels = {
@@ -274,6 +294,15 @@ def main():
                           "us": dec_ms * 1e3, "sequence_steps_per_s": 512 / (dec_ms * 1e-3),
                           "GB_per_s": dec_bytes / (dec_ms * 1e-3) / 1e9,
                           "hbm_frac": dec_bytes / (dec_ms * 1e-3) / PEAK_HBM}
+    out["variants"] = {
+        "prefill_forward_f16": {"workload": "fp16 B=16 T=1024 H=32, initial state N(0,0.1^2)",
+                                "ms": f16_ms, "tokens_per_s": 16 * 1024 / (f16_ms * 1e-3),
+                                "fp32_frac": FWD_FLOP * pre_th / (f16_ms * 1e-3) / PEAK_FP32},
+        "train_step_log_decay_f32_grads": {
+            "workload": "bf16 B=4 T=4096 H=32, w as log(decay), gradients in fp32 "
+                        "(forward with checkpoints + backward)",
+            "ms": log_ms, "tokens_per_s": tok / (log_ms * 1e-3)},
+    }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -13,7 +13,9 @@
  *
  * Data layout (all buffers are device memory owned by the caller):
  *   token streams r, w, k, v, a, b, y, dy, dr..db : [B, T, H, N], N contiguous,
- *       element type given by wkv7_desc.dtype (fp32 or bf16);
+ *       element type given by wkv7_desc.dtype (fp32, bf16 or fp16: the model
+ *       card's "Transformers quickstart" section names BF16/FP16/FP32
+ *       activations); dr..db in fp32 instead when wkv7_desc.grad_f32 = 1;
  *       the flat token index of (row b, position t) is b*T + t;
  *   states s0, s_out, ds_out, ds0 : fp32 [S, H, N, N], row = value index i,
  *       column = key index j; S = B in dense mode, num_seqs in segment mode;
@@ -24,6 +26,13 @@
  *       The state is checkpointed every 16 tokens as on the rwkv-metal page
  *       (section "The Metal WKV-7 kernel") and the RWKV-MLX page (section
  *       "Key Design Decisions", CHUNK_LEN=16 backward).
+ *
+ * Decay input. With wkv7_desc.decay = WKV7_DECAY_MULT the w stream holds the
+ * multiplicative decay itself (in [0, 1]). With WKV7_DECAY_LOG it holds its
+ * natural logarithm and the decay is exp(w) (w <= 0), the form in which the
+ * wkv7 call on the rwkv-lab page (section "Highlight result -- GDN in RWKV-7")
+ * takes GDN's log-decay; dw is then the gradient with respect to that
+ * logarithm, i.e. decay * dL/d(decay).
  *
  * Modes.
  *   Dense (num_seqs == 0): each of the B rows is one sequence of T tokens.
@@ -60,7 +69,7 @@
 extern "C" {
 #endif
 
-#define WKV7_ABI_VERSION 1
+#define WKV7_ABI_VERSION 2
 #define WKV7_HEAD_SIZE 64
 #define WKV7_CHUNK 16
 
@@ -74,8 +83,14 @@ typedef enum {
 
 typedef enum {
     WKV7_F32 = 0,
-    WKV7_BF16 = 1
+    WKV7_BF16 = 1,
+    WKV7_F16 = 2
 } wkv7_dtype;
+
+typedef enum {
+    WKV7_DECAY_MULT = 0,        /* w is the decay */
+    WKV7_DECAY_LOG = 1          /* w is log(decay); decay = exp(w) */
+} wkv7_decay;
 
 typedef struct {
     int32_t B;                  /* rows */
@@ -89,6 +104,8 @@ typedef struct {
     const int32_t *seq_ckpt;    /* device [num_seqs]: first checkpoint slot; needed
                                    only when checkpoints are written or read */
     int32_t ckpt_slots;         /* segment mode: slots in the ckpt buffer */
+    int32_t decay;              /* wkv7_decay of the w stream (0 = multiplicative) */
+    int32_t grad_f32;           /* 1: dr..db are fp32 whatever dtype is; 0: dtype */
 } wkv7_desc;
 
 /*
@@ -113,7 +130,7 @@ wkv7_status wkv7_forward(const wkv7_desc *d,
  *   ckpt   : checkpoints written by wkv7_forward on the same inputs and s0.
  *   dy     : [B,T,H,N] upstream gradient of y (dtype), or NULL for zero.
  *   ds_out : [S,H,N,N] fp32 upstream gradient of the final state, or NULL.
- *   dr..db : [B,T,H,N] outputs (dtype); required.
+ *   dr..db : [B,T,H,N] outputs (dtype, or fp32 when grad_f32 = 1); required.
  *   ds0    : [S,H,N,N] fp32 gradient of the initial state, or NULL.
  *   workspace / workspace_bytes : device memory of at least
  *           wkv7_workspace_bytes, 16-byte aligned, owned by the caller. The
@@ -138,13 +155,14 @@ wkv7_status wkv7_backward(const wkv7_desc *d,
 /*
  * One decode step for B independent sequences (the rwkv-metal page's
  * wkv7_step; the rwkv-lab page's in-place one-token state transition).
+ *   dtype : wkv7_dtype of r..b and y; decay : wkv7_decay of w.
  *   r..b  : [B,H,N] one token per sequence (dtype).
  *   s_in  : [B,H,N,N] fp32 state before the token.
  *   s_out : [B,H,N,N] fp32 state after the token; may equal s_in (in place),
  *           otherwise must not overlap it.
  *   y     : [B,H,N] output (dtype).
  */
-wkv7_status wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype,
+wkv7_status wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, int32_t decay,
                              const void *r, const void *w, const void *k,
                              const void *v, const void *a, const void *b,
                              const float *s_in, float *s_out, void *y, void *stream);

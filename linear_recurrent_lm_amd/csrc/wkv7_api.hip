@@ -23,12 +23,16 @@ bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-size_t elem_size(int dtype) { return dtype == WKV7_BF16 ? 2 : 4; }
+size_t elem_size(int dtype) { return dtype == WKV7_F32 ? 4 : 2; }
+
+bool dtype_ok(int32_t dtype) { return dtype == WKV7_F32 || dtype == WKV7_BF16 || dtype == WKV7_F16; }
 
 wkv7_status check_desc(const wkv7_desc *d) {
     if (!d) return WKV7_ERR_INVALID_ARGUMENT;
     if (d->N != kN) return WKV7_ERR_UNSUPPORTED;
-    if (d->dtype != WKV7_F32 && d->dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
+    if (!dtype_ok(d->dtype)) return WKV7_ERR_UNSUPPORTED;
+    if (d->decay != WKV7_DECAY_MULT && d->decay != WKV7_DECAY_LOG) return WKV7_ERR_UNSUPPORTED;
+    if (d->grad_f32 != 0 && d->grad_f32 != 1) return WKV7_ERR_INVALID_ARGUMENT;
     if (d->B < 1 || d->T < 1 || d->H < 1) return WKV7_ERR_INVALID_ARGUMENT;
     const int64_t toks = (int64_t)d->B * d->T;
     if (toks > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
@@ -162,6 +166,7 @@ wkv7_status wkv7_forward(const wkv7_desc *d, const void *r, const void *w, const
     wkv7::FwdArgs args;
     args.seg = seg_params(d, ckpt != nullptr);
     args.dtype = d->dtype;
+    args.logw = d->decay == WKV7_DECAY_LOG;
     args.r = r; args.w = w; args.k = k; args.v = v; args.a = a; args.b = b;
     args.s0 = s0; args.y = y; args.s_out = s_out; args.ckpt = ckpt;
     if (d->num_seqs > 0) {
@@ -196,6 +201,8 @@ wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, cons
     wkv7::BwdArgs args;
     args.seg = seg_params(d, true);
     args.dtype = d->dtype;
+    args.logw = d->decay == WKV7_DECAY_LOG;
+    args.grad_f32 = d->grad_f32;
     args.r = r; args.w = w; args.k = k; args.v = v; args.a = a; args.b = b;
     args.ckpt = ckpt; args.dy = dy; args.ds_out = ds_out;
     args.dr = dr; args.dw = dw; args.dk = dk; args.dv = dv; args.da = da; args.db = db;
@@ -203,7 +210,7 @@ wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, cons
     args.ws = (float *)workspace;
     if (d->num_seqs > 0) {
         void *outs[6] = {dr, dw, dk, dv, da, db};
-        if (wkv7::launch_zero_uncovered(args.seg, d->dtype, outs, 6, hs) != hipSuccess)
+        if (wkv7::launch_zero_uncovered(args.seg, d->grad_f32 ? WKV7_F32 : d->dtype, outs, 6, hs) != hipSuccess)
             return WKV7_ERR_HIP;
     }
     if (wkv7::launch_backward_sweep(args, hs) != hipSuccess) return WKV7_ERR_HIP;
@@ -211,12 +218,14 @@ wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, cons
     return WKV7_OK;
 }
 
-wkv7_status wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, const void *r,
+wkv7_status wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, int32_t decay,
+                             const void *r,
                              const void *w, const void *k, const void *v, const void *a,
                              const void *b, const float *s_in, float *s_out, void *y,
                              void *stream) {
     if (N != kN) return WKV7_ERR_UNSUPPORTED;
-    if (dtype != WKV7_F32 && dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
+    if (!dtype_ok(dtype)) return WKV7_ERR_UNSUPPORTED;
+    if (decay != WKV7_DECAY_MULT && decay != WKV7_DECAY_LOG) return WKV7_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || (int64_t)B * H > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
     const void *streams[9] = {r, w, k, v, a, b, y, s_in, s_out};
     wkv7_status st = check_streams(streams, 9);
@@ -227,6 +236,7 @@ wkv7_status wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, con
     if ((st = check_device()) != WKV7_OK) return st;
     wkv7::DecArgs args;
     args.B = B; args.H = H; args.dtype = dtype;
+    args.logw = decay == WKV7_DECAY_LOG;
     args.r = r; args.w = w; args.k = k; args.v = v; args.a = a; args.b = b;
     args.s_in = s_in; args.s_out = s_out; args.y = y;
     if (wkv7::launch_decode(args, (hipStream_t)stream) != hipSuccess) return WKV7_ERR_HIP;

@@ -197,6 +197,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 
     const int64_t ts = (int64_t)H * kN;
     const int64_t base = (u.start * H + h) * kN;
+    // gradient stores: the I/O type, or fp32 when requested
+    auto gst = [&](void *ptr, int64_t o, float v) {
+        if (p.grad_f32) ((float *)ptr)[o] = v;
+        else IO<TI>::st((TI *)ptr, o, v);
+    };
 
     const int nch = (u.len + kChunk - 1) / kChunk;
     const int c_lo = grp * kChunksPerGroup;
@@ -260,8 +265,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 const float f = st == IW ? 1.f : 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    x[e] = keep ? x[e] : f;
-                    if (st == IW) x[e] = fmaxf(x[e], kMinW);
+                    float v = st == IW ? decay_of(x[e], p.logw) : x[e];
+                    v = keep ? v : f;
+                    x[e] = st == IW ? fmaxf(v, kMinW) : v;
                 }
                 *(float4 *)(s_in + (st * 16 + t) * LD + e0) = make_float4(x[0], x[1], x[2], x[3]);
             }
@@ -527,7 +533,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * kq + r;
-                if (t < L) IO<TI>::st((TI *)p.dv, base + (int64_t)(t0 + t) * ts + i0 + l16, dvp[r]);
+                if (t < L) gst(p.dv, base + (int64_t)(t0 + t) * ts + i0 + l16, dvp[r]);
             }
         } else if (wave < 12) {
             const int jc = 16 * w4;
@@ -670,10 +676,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 const float dac = dAh * gprev, drc = dRh * gam, dbc = dBh * dend, dkc = dKh * dend;
                 if (t < L) {
                     const int64_t o = base + (int64_t)(t0 + t) * ts + j;
-                    IO<TI>::st((TI *)p.dr, o, drc + fin * qr + r8 + r4);
-                    IO<TI>::st((TI *)p.da, o, dac + fex * qa + a8 + a4);
-                    IO<TI>::st((TI *)p.db, o, dbc + invF * qb + b8 + b4);
-                    IO<TI>::st((TI *)p.dk, o, dkc + invF * qk + k8 + k4);
+                    gst(p.dr, o, drc + fin * qr + r8 + r4);
+                    gst(p.da, o, dac + fex * qa + a8 + a4);
+                    gst(p.db, o, dbc + invF * qb + b8 + b4);
+                    gst(p.dk, o, dkc + invF * qk + k8 + k4);
                 }
                 // u terms that the scans below read (ranges with structural zeros
                 // are neither written nor read)
@@ -825,7 +831,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             const int o = m * LD + j;
             const float x = s_dgC[j] * s_gC[j] + ((s_Z[o] + s_Z[16 * LD + o]) + (s_Z[32 * LD + o] + s_Z[48 * LD + o]))
                           + s_G[o];
-            if (m < L) IO<TI>::st((TI *)p.dw, base + (int64_t)(t0 + m) * ts + j, x / s_in[IW * 16 * LD + o]);
+            // d/dw = u / w; for a log-decay input d/d log(w) = u itself
+            if (m < L) gst(p.dw, base + (int64_t)(t0 + m) * ts + j, p.logw ? x : x / s_in[IW * 16 * LD + o]);
         }
     }
 }
@@ -841,7 +848,8 @@ hipError_t launch_backward(const BwdArgs &args, hipStream_t stream) {
     const int S = a.seg.num_seqs > 0 ? a.seg.num_seqs : a.seg.B;
     const int32_t units = S * a.seg.H;
     const size_t lds = (size_t)LDS_FLOATS * sizeof(float);
-    auto fn = a.dtype == 1 ? bwd_chunk_kernel<uint16_t> : bwd_chunk_kernel<float>;
+    auto fn = a.dtype == 1 ? bwd_chunk_kernel<uint16_t>
+            : a.dtype == 2 ? bwd_chunk_kernel<_Float16> : bwd_chunk_kernel<float>;
     hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     // A sequence lies within one row of T tokens, so it has at most ceil(T / 16) chunks.

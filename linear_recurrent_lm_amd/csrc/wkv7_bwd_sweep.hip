@@ -240,7 +240,7 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
                 raw_unpack(raw, k, x);
                 if (st == SW) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = fmaxf(x[e], kMinW);
+                    for (int e = 0; e < 8; ++e) x[e] = fmaxf(decay_of(x[e], p.logw), kMinW);
                 }
             } else {                           // identity tokens past the end
                 const float f = st == SW ? 1.f : 0.f;
@@ -537,7 +537,9 @@ hipError_t launch_sweep_typed(const BwdArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_backward_sweep(const BwdArgs &a, hipStream_t stream) {
-    return a.dtype == 1 ? launch_sweep_typed<uint16_t>(a, stream) : launch_sweep_typed<float>(a, stream);
+    if (a.dtype == 1) return launch_sweep_typed<uint16_t>(a, stream);
+    if (a.dtype == 2) return launch_sweep_typed<_Float16>(a, stream);
+    return launch_sweep_typed<float>(a, stream);
 }
 
 }  // namespace wkv7

@@ -45,6 +45,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs p) {
     float a[4], w[4], b[4], k[4], r[4], vv[4];
     ld4((const TI *)p.a, vb + c0, a);
     ld4((const TI *)p.w, vb + c0, w);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = decay_of(w[e], p.logw);
     ld4((const TI *)p.b, vb + c0, b);
     ld4((const TI *)p.k, vb + c0, k);
     ld4((const TI *)p.r, vb + c0, r);
@@ -78,6 +80,8 @@ hipError_t launch_decode(const DecArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)a.B * a.H));
     if (a.dtype == 1)
         hipLaunchKernelGGL(decode_kernel<uint16_t>, grid, dim3(256), 0, stream, a);
+    else if (a.dtype == 2)
+        hipLaunchKernelGGL(decode_kernel<_Float16>, grid, dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL(decode_kernel<float>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();

@@ -89,6 +89,16 @@ template <> struct IO<uint16_t> {
     __device__ static __forceinline__ void st(uint16_t *p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
 };
 
+template <> struct IO<_Float16> {
+    __device__ static __forceinline__ float ld(const _Float16 *p, int64_t i) { return (float)p[i]; }
+    // fp32 -> fp16 conversion rounds to nearest even
+    __device__ static __forceinline__ void st(_Float16 *p, int64_t i, float x) { p[i] = (_Float16)x; }
+};
+
+// The decay a w-stream element stands for: the value itself, or its
+// exponential when the stream holds log(decay).
+__device__ __forceinline__ float decay_of(float x, int logw) { return logw ? expf(x) : x; }
+
 // Is flat token `tok` of a row-major [B*T] token space covered by a sequence?
 // Binary search over the (sorted) starts; used only to zero uncovered tokens.
 __device__ inline bool token_covered(const SegParams &p, int64_t tok) {

@@ -33,7 +33,7 @@ hipError_t launch_zero_uncovered(const SegParams &seg, int dtype, void *const *p
     for (int q = 0; q < nptr && q < 6; ++q) pk.p[q] = ptrs[q];
     const int64_t n = (int64_t)seg.B * seg.T * seg.H;
     const dim3 grid((unsigned)((n + 255) / 256));
-    if (dtype == 1)
+    if (dtype != 0)            // bf16 and fp16: 2-byte zeros
         hipLaunchKernelGGL(zero_uncovered_kernel<uint16_t>, grid, dim3(256), 0, stream, seg, pk, nptr);
     else
         hipLaunchKernelGGL(zero_uncovered_kernel<float>, grid, dim3(256), 0, stream, seg, pk, nptr);

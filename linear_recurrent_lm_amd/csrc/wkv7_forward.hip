@@ -295,6 +295,10 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
             // the end (a branch would leave the loads pending on one path)
             float x[8];
             raw_unpack(raw, k, x);
+            if (st == IW && p.logw) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = expf(x[e]);
+            }
             const float f = st == IW ? 1.f : 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = t < Lc ? x[e] : f;
@@ -619,7 +623,9 @@ hipError_t launch_typed(const FwdArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream) {
-    return a.dtype == 1 ? launch_typed<uint16_t>(a, stream) : launch_typed<float>(a, stream);
+    if (a.dtype == 1) return launch_typed<uint16_t>(a, stream);
+    if (a.dtype == 2) return launch_typed<_Float16>(a, stream);
+    return launch_typed<float>(a, stream);
 }
 
 }  // namespace wkv7

@@ -10,7 +10,8 @@ namespace wkv7 {
 
 struct FwdArgs {
     SegParams seg;
-    int dtype;                       // 0 fp32, 1 bf16
+    int dtype;                       // 0 fp32, 1 bf16, 2 fp16
+    int logw;                        // 1: the w stream holds log(decay)
     const void *r, *w, *k, *v, *a, *b;
     const float *s0;
     void *y;
@@ -21,6 +22,8 @@ struct FwdArgs {
 struct BwdArgs {
     SegParams seg;
     int dtype;
+    int logw;                        // 1: the w stream holds log(decay); dw is d/d log(decay)
+    int grad_f32;                    // 1: dr..db are fp32
     const void *r, *w, *k, *v, *a, *b;
     const float *ckpt;
     const void *dy;
@@ -34,6 +37,7 @@ struct BwdArgs {
 struct DecArgs {
     int32_t B, H;
     int dtype;
+    int logw;
     const void *r, *w, *k, *v, *a, *b;
     const float *s_in;
     float *s_out;

@@ -52,6 +52,7 @@ __device__ __forceinline__ float quad_sum(float v) {
 template <typename TI, int K> struct Raw;
 template <int K> struct Raw<uint16_t, K> { uint4 q[K]; };
 template <int K> struct Raw<float, K> { float4 q[K][2]; };
+template <int K> struct Raw<_Float16, K> { uint4 q[K]; };
 
 template <int K>
 __device__ __forceinline__ void raw_load(const uint16_t *p, Raw<uint16_t, K> &r, int k) {
@@ -72,6 +73,25 @@ __device__ __forceinline__ void raw_unpack(const Raw<uint16_t, K> &r, int k, flo
     }
 }
 template <int K>
+__device__ __forceinline__ void raw_load(const _Float16 *p, Raw<_Float16, K> &r, int k) {
+    r.q[k] = *(const uint4 *)p;
+}
+__device__ __forceinline__ float half_lo(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
+}
+__device__ __forceinline__ float half_hi(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+}
+template <int K>
+__device__ __forceinline__ void raw_unpack(const Raw<_Float16, K> &r, int k, float *x) {
+    const uint32_t u[4] = {r.q[k].x, r.q[k].y, r.q[k].z, r.q[k].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = half_lo(u[e]);
+        x[2 * e + 1] = half_hi(u[e]);
+    }
+}
+template <int K>
 __device__ __forceinline__ void raw_unpack(const Raw<float, K> &r, int k, float *x) {
     x[0] = r.q[k][0].x; x[1] = r.q[k][0].y; x[2] = r.q[k][0].z; x[3] = r.q[k][0].w;
     x[4] = r.q[k][1].x; x[5] = r.q[k][1].y; x[6] = r.q[k][1].z; x[7] = r.q[k][1].w;
@@ -81,11 +101,16 @@ __device__ __forceinline__ void raw_unpack(const Raw<float, K> &r, int k, float 
 template <typename TI> struct Raw4;
 template <> struct Raw4<uint16_t> { uint2 q; };
 template <> struct Raw4<float> { float4 q; };
+template <> struct Raw4<_Float16> { uint2 q; };
 __device__ __forceinline__ void raw4_load(const uint16_t *p, Raw4<uint16_t> &r) { r.q = *(const uint2 *)p; }
 __device__ __forceinline__ void raw4_load(const float *p, Raw4<float> &r) { r.q = *(const float4 *)p; }
 __device__ __forceinline__ void raw4_unpack(const Raw4<uint16_t> &r, float *x) {
     x[0] = __uint_as_float(r.q.x << 16); x[1] = __uint_as_float(r.q.x & 0xffff0000u);
     x[2] = __uint_as_float(r.q.y << 16); x[3] = __uint_as_float(r.q.y & 0xffff0000u);
+}
+__device__ __forceinline__ void raw4_load(const _Float16 *p, Raw4<_Float16> &r) { r.q = *(const uint2 *)p; }
+__device__ __forceinline__ void raw4_unpack(const Raw4<_Float16> &r, float *x) {
+    x[0] = half_lo(r.q.x); x[1] = half_hi(r.q.x); x[2] = half_lo(r.q.y); x[3] = half_hi(r.q.y);
 }
 __device__ __forceinline__ void raw4_unpack(const Raw4<float> &r, float *x) {
     x[0] = r.q.x; x[1] = r.q.y; x[2] = r.q.z; x[3] = r.q.w;

@@ -12,9 +12,11 @@ Distributions (the configuration recipe used throughout):
   kk = k / ||k||_2 over the head dimension, computed from the fp32 k
   a = -kk,  b = kk * sigmoid(z),  z ~ N(0, 1)
   optional initial state ~ N(0, std^2), upstream dy ~ N(0, 1)
-Values are produced in fp32 and, for bf16 workloads, rounded to bf16 with
-round-to-nearest-even; the fp32 arrays returned then hold exactly the rounded
-values, so upcasting them to fp64 is exact.
+With decay="log" the w stream instead holds -exp(x), the logarithm of the same
+decay (the kernels then take exp of it).
+Values are produced in fp32 and, for bf16 / fp16 workloads, rounded to that
+type with round-to-nearest-even; the fp32 arrays returned then hold exactly
+the rounded values, so upcasting them to fp64 is exact.
 
 Arrays use the [B, T, H, N] layout (N contiguous); states are [S, H, N, N]
 with the row index = value index and the column index = key index.
@@ -40,6 +42,23 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def round_f16(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest fp16 (ties to even); returns fp32."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Values of an 'f32', 'bf16' or 'f16' stream, held in fp32."""
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "f16":
+        return round_f16(x)
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+DTYPES = ("f32", "bf16", "f16")
+
+
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """Upper 16 bits of fp32 values that are already bf16-representable."""
     x = np.ascontiguousarray(x, dtype=np.float32)
@@ -49,7 +68,8 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 @dataclasses.dataclass
 class Inputs:
     """One batch of WKV-7 inputs. Float arrays are fp32 holding the exact
-    values the kernels read (bf16-rounded when dtype == 'bf16')."""
+    values the kernels read (rounded to dtype when it is 'bf16' or 'f16');
+    w holds log(decay) when decay == 'log'."""
     dtype: str
     r: np.ndarray
     w: np.ndarray
@@ -62,6 +82,7 @@ class Inputs:
     ds_out: np.ndarray | None = None
     seq_start: np.ndarray | None = None   # int32, flat token index b*T + t
     seq_len: np.ndarray | None = None     # int32
+    decay: str = "mult"
 
     @property
     def shape(self):
@@ -71,13 +92,13 @@ class Inputs:
         return (self.r, self.w, self.k, self.v, self.a, self.b)
 
 
-def _draw_streams(rng, shape):
+def _draw_streams(rng, shape, decay="mult"):
     r = rng.standard_normal(shape, dtype=np.float32)
     k = rng.standard_normal(shape, dtype=np.float32)
     v = rng.standard_normal(shape, dtype=np.float32)
     x = (np.float32(-6.0) + np.float32(5.5) * rng.random(shape, dtype=np.float32))
     z = rng.standard_normal(shape, dtype=np.float32)
-    w = np.exp(-np.exp(x))
+    w = -np.exp(x) if decay == "log" else np.exp(-np.exp(x))
     nrm = np.sqrt(np.sum(k.astype(np.float64) ** 2, axis=-1, keepdims=True))
     kk = (k / np.maximum(nrm, 1e-30)).astype(np.float32)
     a = -kk
@@ -87,27 +108,25 @@ def _draw_streams(rng, shape):
 
 def make_inputs(B: int, T: int, H: int, N: int = 64, *, seed: int = 0,
                 dtype: str = "bf16", s0_std: float = 0.0, with_dy: bool = False,
-                ds_out_std: float = 0.0) -> Inputs:
+                ds_out_std: float = 0.0, decay: str = "mult") -> Inputs:
     """Dense batch: B rows of T tokens, H heads of size N."""
-    if dtype not in ("bf16", "f32"):
+    if dtype not in DTYPES:
         raise ValueError(dtype)
+    if decay not in ("mult", "log"):
+        raise ValueError(decay)
     rng = np.random.Generator(np.random.PCG64(seed))
     shape = (B, T, H, N)
-    streams = _draw_streams(rng, shape)
-    if dtype == "bf16":
-        streams = [round_bf16(s) for s in streams]
+    streams = [round_to(s, dtype) for s in _draw_streams(rng, shape, decay)]
     s0 = None
     if s0_std > 0:
         s0 = (rng.standard_normal((B, H, N, N), dtype=np.float32) * np.float32(s0_std))
     dy = None
     if with_dy:
-        dy = rng.standard_normal(shape, dtype=np.float32)
-        if dtype == "bf16":
-            dy = round_bf16(dy)
+        dy = round_to(rng.standard_normal(shape, dtype=np.float32), dtype)
     ds_out = None
     if ds_out_std > 0:
         ds_out = rng.standard_normal((B, H, N, N), dtype=np.float32) * np.float32(ds_out_std)
-    return Inputs(dtype, *streams, s0=s0, dy=dy, ds_out=ds_out)
+    return Inputs(dtype, *streams, s0=s0, dy=dy, ds_out=ds_out, decay=decay)
 
 
 def ragged_lengths(num_seqs: int, lo: int, hi: int, seed: int) -> np.ndarray:

@@ -6,8 +6,9 @@ Every step of the recurrence runs in the library's HIP kernels; if the
 library is missing this module raises instead of computing anything.
 
 Functions carry the C names (wkv7_forward, wkv7_backward, wkv7_decode_step,
-...). Layouts: streams [B, T, H, 64] (fp32 or bf16, contiguous), states
-[S, H, 64, 64] fp32, checkpoints [slots, H, 64, 64] fp32.
+...). Layouts: streams [B, T, H, 64] (fp32, bf16 or fp16, contiguous), states
+[S, H, 64, 64] fp32, checkpoints [slots, H, 64, 64] fp32. decay="log" passes
+w as log(decay); grad_f32=True writes the gradients in fp32.
 """
 from __future__ import annotations
 
@@ -23,7 +24,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "wkv7.h")
 
 N = 64
 CHUNK = 16
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
+DECAY = {"mult": 0, "log": 1}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small",
           4: "HIP runtime error"}
 
@@ -38,7 +40,8 @@ class Desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("dtype", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("seq_start", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
-                ("seq_ckpt", ctypes.c_void_p), ("ckpt_slots", ctypes.c_int32)]
+                ("seq_ckpt", ctypes.c_void_p), ("ckpt_slots", ctypes.c_int32),
+                ("decay", ctypes.c_int32), ("grad_f32", ctypes.c_int32)]
 
 
 _lib = None
@@ -61,7 +64,7 @@ def lib():
         dptr = ctypes.POINTER(Desc)
         L.wkv7_forward.argtypes = [dptr] + [vp] * 11
         L.wkv7_backward.argtypes = [dptr] + [vp] * 16 + [vp, sz, vp]
-        L.wkv7_decode_step.argtypes = [i32, i32, i32, i32] + [vp] * 10
+        L.wkv7_decode_step.argtypes = [i32, i32, i32, i32, i32] + [vp] * 10
         L.wkv7_checkpoint_slots.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int64)]
         L.wkv7_workspace_bytes.argtypes = [dptr, ctypes.POINTER(ctypes.c_size_t)]
         L.wkv7_segments_check.argtypes = [i32, i32, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
@@ -91,6 +94,8 @@ def _dtype_code(t):
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
+    if t.dtype == torch.float16:
+        return F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -137,9 +142,17 @@ class Segments:
         self.ckpt = torch.from_numpy(base).to(device)
 
 
-def _desc(B, T, H, dtype, seg: Segments | None):
+def _decay(decay):
+    if decay not in DECAY:
+        raise ValueError(f"decay must be one of {sorted(DECAY)}")
+    return DECAY[decay]
+
+
+def _desc(B, T, H, dtype, seg: Segments | None, decay="mult", grad_f32=False):
     d = Desc()
     d.B, d.T, d.H, d.N, d.dtype = B, T, H, N, dtype
+    d.decay = _decay(decay)
+    d.grad_f32 = 1 if grad_f32 else 0
     if seg is None:
         d.num_seqs = 0
         d.ckpt_slots = 0
@@ -162,7 +175,7 @@ def checkpoint_slots(B, T, seg: Segments | None = None) -> int:
 
 def wkv7_forward(r, w, k, v, a, b, s0=None, *, segments: Segments | None = None,
                  checkpoints: bool = False, state_out: bool = True, y=None, s_out=None,
-                 ckpt=None):
+                 ckpt=None, decay: str = "mult"):
     """y, s_out, ckpt = wkv7_forward(...). s_out/ckpt are None when not requested."""
     torch = _torch()
     B, T, H, n = r.shape
@@ -185,7 +198,7 @@ def wkv7_forward(r, w, k, v, a, b, s0=None, *, segments: Segments | None = None,
                            dtype=torch.float32)
     if not checkpoints:
         ckpt = None
-    d = _desc(B, T, H, _dtype_code(r), segments)
+    d = _desc(B, T, H, _dtype_code(r), segments, decay)
     _check("wkv7_forward", lib().wkv7_forward(
         ctypes.byref(d), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(s0), _ptr(y),
         _ptr(s_out), _ptr(ckpt), _stream()))
@@ -201,8 +214,9 @@ def wkv7_workspace_bytes(B, T, H, dtype, segments: Segments | None = None) -> in
 
 def wkv7_backward(r, w, k, v, a, b, ckpt, dy=None, ds_out=None, *,
                   segments: Segments | None = None, want_ds0: bool = True, workspace=None,
-                  grads=None):
-    """Returns dict dr, dw, dk, dv, da, db (dtype of r) and ds0 (fp32 or None)."""
+                  grads=None, decay: str = "mult", grad_f32: bool = False):
+    """Returns dict dr, dw, dk, dv, da, db (dtype of r, or fp32 with grad_f32)
+    and ds0 (fp32 or None). With decay="log", dw is the gradient w.r.t. log(decay)."""
     torch = _torch()
     B, T, H, n = r.shape
     dev = r.device
@@ -215,14 +229,17 @@ def wkv7_backward(r, w, k, v, a, b, ckpt, dy=None, ds_out=None, *,
     if ds_out is not None:
         _req(ds_out, "ds_out", dev, torch.float32, (S, H, N, N))
     names = ("dr", "dw", "dk", "dv", "da", "db")
+    gdt = torch.float32 if grad_f32 else r.dtype
     if grads is None:
-        grads = {nm: torch.empty_like(r) for nm in names}
+        grads = {nm: torch.empty(r.shape, device=dev, dtype=gdt) for nm in names}
+    for nm in names:
+        _req(grads[nm], nm, dev, gdt, r.shape)
     ds0 = torch.empty((S, H, N, N), device=dev, dtype=torch.float32) if want_ds0 else None
     need = wkv7_workspace_bytes(B, T, H, _dtype_code(r), segments)
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    d = _desc(B, T, H, _dtype_code(r), segments)
+    d = _desc(B, T, H, _dtype_code(r), segments, decay, grad_f32)
     _check("wkv7_backward", lib().wkv7_backward(
         ctypes.byref(d), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(ckpt), _ptr(dy),
         _ptr(ds_out), *[_ptr(grads[nm]) for nm in names], _ptr(ds0), _ptr(workspace),
@@ -232,7 +249,7 @@ def wkv7_backward(r, w, k, v, a, b, ckpt, dy=None, ds_out=None, *,
     return out
 
 
-def wkv7_decode_step(r, w, k, v, a, b, s_in, s_out=None, y=None):
+def wkv7_decode_step(r, w, k, v, a, b, s_in, s_out=None, y=None, *, decay: str = "mult"):
     """One token per (sequence, head): streams [B, H, 64], state [B, H, 64, 64].
     Pass s_out=s_in to update the state in place. Returns (y, s_out)."""
     torch = _torch()
@@ -246,7 +263,7 @@ def wkv7_decode_step(r, w, k, v, a, b, s_in, s_out=None, y=None):
     _req(s_out, "s_out", dev, torch.float32, (B, H, N, N))
     y = torch.empty_like(r) if y is None else y
     _check("wkv7_decode_step", lib().wkv7_decode_step(
-        B, H, n, _dtype_code(r), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(s_in),
+        B, H, n, _dtype_code(r), _decay(decay), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(s_in),
         _ptr(s_out), _ptr(y), _stream()))
     return y, s_out
 

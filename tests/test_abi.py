@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert W.wkv7_abi_version() == 1
+    assert W.wkv7_abi_version() == 2
     assert W.wkv7_status_string(0) == "ok"
     assert W.wkv7_status_string(3) == "workspace too small"
     assert W.wkv7_status_string(99) == "unknown status"
@@ -49,6 +49,9 @@ def test_forward_rejects_bad_descriptors():
     assert fwd(None) == INVALID
     assert fwd(desc(N=128)) == UNSUPPORTED
     assert fwd(desc(dtype=7)) == UNSUPPORTED
+    assert fwd(desc(dtype=-1)) == UNSUPPORTED
+    assert fwd(desc(decay=2)) == UNSUPPORTED                    # neither multiplicative nor log
+    assert fwd(desc(grad_f32=3)) == INVALID
     for bad in (dict(B=0), dict(T=0), dict(H=0), dict(T=-5), dict(num_seqs=-1)):
         assert fwd(desc(**bad)) == INVALID, bad
     assert fwd(desc(B=1 << 20, T=1 << 12)) == INVALID          # B*T over int32
@@ -86,10 +89,11 @@ def test_backward_rejects_bad_arguments():
 
 def test_decode_rejects_bad_arguments():
     L = W.lib()
-    call = lambda B=4, H=2, N=64, dt=1, s_in=P[7], s_out=P[8], y=P[6]: L.wkv7_decode_step(
-        B, H, N, dt, *P[:6], s_in, s_out, y, None)
+    call = lambda B=4, H=2, N=64, dt=1, dc=0, s_in=P[7], s_out=P[8], y=P[6]: L.wkv7_decode_step(
+        B, H, N, dt, dc, *P[:6], s_in, s_out, y, None)
     assert call(N=32) == UNSUPPORTED
     assert call(dt=3) == UNSUPPORTED
+    assert call(dc=5) == UNSUPPORTED
     assert call(B=0) == INVALID
     assert call(s_in=None) == INVALID
     assert call(y=None) == INVALID
