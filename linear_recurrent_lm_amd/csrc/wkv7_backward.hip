@@ -171,17 +171,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 
     const int tid = threadIdx.x;
     const int lane0 = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 16 waves; wave w runs on SIMD w % 4
+    const int wave0 = __builtin_amdgcn_readfirstlane(tid >> 6);  // 16 waves; wave w runs on SIMD w % 4
     int lane = lane0, l16 = lane0 & 15, kq = lane0 >> 4;
-    // The lane indices are re-derived opaquely at the start of each phase, so
-    // that the many LDS addresses built from them are formed inside the phase
-    // instead of being hoisted out of the chunk loop and kept live throughout.
+    int wave = wave0, w4 = wave0 & 3;                // w4: 16-row / 16-column block of this wave
+    // The lane and wave indices are re-derived opaquely at the start of each
+    // phase, so that the many LDS addresses and role conditions built from
+    // them are formed inside the phase instead of being hoisted out of the
+    // chunk loop and kept live (or spilled) throughout.
     auto relane = [&]() {
-        int lv = lane0;
+        int lv = lane0, wv = wave0;
         asm volatile("" : "+v"(lv));
+        asm volatile("" : "+s"(wv));
         lane = lv; l16 = lv & 15; kq = lv >> 4;
+        wave = wv; w4 = wv & 3;
     };
-    const int w4 = wave & 3;                         // 16-row / 16-column block of this wave
 
     float *s_in = sm + O_IN;
     float *s_Q = sm + O_Q, *s_BK = sm + O_BK;

@@ -69,12 +69,9 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float((uint32_t)h << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN.
+// fp32 -> bf16, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950); NaN stays NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 template <typename TI> struct IO;
