@@ -564,36 +564,43 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         lds_barrier();
         relane();
 
-        // ---- P6: pair-gradient products of the split-point tiles: Z_A = dD B_rows
-        //      and Z_B = dD^T A_rows of tiles 1, 2 (product w >> 2: Z_A1, Z_B1,
-        //      Z_A2, Z_B2), 16-column block w & 3 of each; into s_Z (S_0 is consumed)
-        {
-            const int prod = wave >> 2, q = w4;
+        // ---- P6: pair-gradient products of the split-point tiles (waves 0-3):
+        //      Z_A = dD B_rows and Z_B = dD^T A_rows of tiles 1, 2 (wave w:
+        //      Z_A1, Z_B1, Z_A2, Z_B2), all 64 columns; into s_Z (S_0 is consumed)
+        if (wave < 4) {
+            const int prod = wave;
             const int tile = prod >> 1;
             const bool zb = (prod & 1) != 0;
             const float *dD = s_M + (MDD1 + tile) * 256;
-            float av[4], bv[4];
+            float av[4];
+            const float *brow[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 av[e] = dD[zb ? (4 * kq + e) * 16 + l16 : l16 * 16 + 4 * kq + e];
                 const int r_ = 4 * kq + e;
-                const float *brow;
                 if (!zb) {
-                    brow = s_BL + (tile == 0 ? r_ : 16 + r_) * LD;
+                    brow[e] = s_BL + (tile == 0 ? r_ : 16 + r_) * LD;
                 } else if (tile == 0) {
-                    brow = r_ < 4 ? s_AR + (8 + r_) * LD : r_ < 8 ? s_AWR + (r_ - 4) * LD
-                         : r_ < 12 ? s_AR + (16 + r_) * LD : s_AWR + (r_ - 8) * LD;
+                    brow[e] = r_ < 4 ? s_AR + (8 + r_) * LD : r_ < 8 ? s_AWR + (r_ - 4) * LD
+                            : r_ < 12 ? s_AR + (16 + r_) * LD : s_AWR + (r_ - 8) * LD;
                 } else {
-                    brow = s_AR + ((r_ & 4) ? 16 + r_ : 4 + r_) * LD;
+                    brow[e] = s_AR + ((r_ & 4) ? 16 + r_ : 4 + r_) * LD;
                 }
-                bv[e] = brow[16 * q + l16];
             }
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            float bv[4][4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) z = mfma4(av[e], bv[e], z);
-            float *zo = s_Z + prod * 16 * LD + 16 * q + l16;
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) zo[(4 * kq + r) * LD] = z[r];
+                for (int e = 0; e < 4; ++e) bv[q][e] = brow[e][16 * q + l16];
+            float *zo = s_Z + prod * 16 * LD + l16;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) z = mfma4(av[e], bv[q][e], z);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) zo[(4 * kq + r) * LD + 16 * q] = z[r];
+            }
         }
         lds_barrier();
         relane();
