@@ -264,12 +264,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 const int st = g >> 8, t = (g >> 4) & 15, e0 = (g & 15) * 4;
                 float x[4];
                 raw4_unpack(raw[k], x);          // unconditional: no path leaves the loads pending
+                if (st == IW) decay_of<4>(x, p.logw);
                 const bool keep = t < L && sp[k] != nullptr;
                 const float f = st == IW ? 1.f : 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float v = st == IW ? decay_of(x[e], p.logw) : x[e];
-                    v = keep ? v : f;
+                    const float v = keep ? x[e] : f;
                     x[e] = st == IW ? fmaxf(v, kMinW) : v;
                 }
                 *(float4 *)(s_in + (st * 16 + t) * LD + e0) = make_float4(x[0], x[1], x[2], x[3]);

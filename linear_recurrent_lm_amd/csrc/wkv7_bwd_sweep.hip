@@ -239,8 +239,9 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
             if (t < Lc && sv[k]) {
                 raw_unpack(raw, k, x);
                 if (st == SW) {
+                    decay_of<8>(x, p.logw);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = fmaxf(decay_of(x[e], p.logw), kMinW);
+                    for (int e = 0; e < 8; ++e) x[e] = fmaxf(x[e], kMinW);
                 }
             } else {                           // identity tokens past the end
                 const float f = st == SW ? 1.f : 0.f;

@@ -45,8 +45,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs p) {
     float a[4], w[4], b[4], k[4], r[4], vv[4];
     ld4((const TI *)p.a, vb + c0, a);
     ld4((const TI *)p.w, vb + c0, w);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = decay_of(w[e], p.logw);
+    decay_of<4>(w, p.logw);
     ld4((const TI *)p.b, vb + c0, b);
     ld4((const TI *)p.k, vb + c0, k);
     ld4((const TI *)p.r, vb + c0, r);

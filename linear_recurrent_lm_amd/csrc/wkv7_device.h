@@ -92,9 +92,17 @@ template <> struct IO<_Float16> {
     __device__ static __forceinline__ void st(_Float16 *p, int64_t i, float x) { p[i] = (_Float16)x; }
 };
 
-// The decay a w-stream element stands for: the value itself, or its
-// exponential when the stream holds log(decay).
-__device__ __forceinline__ float decay_of(float x, int logw) { return logw ? expf(x) : x; }
+// The decays n w-stream elements stand for: the values themselves, or their
+// exponentials when the stream holds log(decay). One uniform branch around
+// the whole group keeps the exponentials off the multiplicative path (a
+// per-element select would evaluate them anyway).
+template <int n>
+__device__ __forceinline__ void decay_of(float *x, int logw) {
+    if (logw) {
+#pragma unroll
+        for (int e = 0; e < n; ++e) x[e] = expf(x[e]);
+    }
+}
 
 // Is flat token `tok` of a row-major [B*T] token space covered by a sequence?
 // Binary search over the (sorted) starts; used only to zero uncovered tokens.

@@ -295,10 +295,7 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
             // the end (a branch would leave the loads pending on one path)
             float x[8];
             raw_unpack(raw, k, x);
-            if (st == IW && p.logw) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = expf(x[e]);
-            }
+            if (st == IW) decay_of<8>(x, p.logw);
             const float f = st == IW ? 1.f : 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = t < Lc ? x[e] : f;
