@@ -382,22 +382,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         if (wave < 4) {
             pa = mm_AtBt(pa, s_Q, LD, s_S0 + 16 * w4 * LD, LD, l16, kq, 64);
         } else if (wave < 6) {
-                    const int tile = wave - 4, m = l16;
-                    const float *arow, *brow;
-                    if (tile == 0) {
-                        arow = m < 4 ? s_AR + (8 + m) * LD : m < 8 ? s_AWR + (m - 4) * LD
-                             : m < 12 ? s_AR + (16 + m) * LD : s_AWR + (m - 8) * LD;
-                        brow = s_BL + l16 * LD;
-                    } else {
-                        arow = s_AR + ((m & 4) ? 16 + m : 4 + m) * LD;
-                        brow = s_BL + (16 + l16) * LD;
-                    }
-                    const f32x4 d = rows_product(arow, brow, kq);
+            // the tile index is made a compile-time constant so that the
+            // scatter's index map folds
+            auto product = [&](auto TILE) {
+                constexpr int tile = decltype(TILE)::value;
+                const int m = l16;
+                const float *arow, *brow;
+                if (tile == 0) {
+                    arow = m < 4 ? s_AR + (8 + m) * LD : m < 8 ? s_AWR + (m - 4) * LD
+                         : m < 12 ? s_AR + (16 + m) * LD : s_AWR + (m - 8) * LD;
+                    brow = s_BL + l16 * LD;
+                } else {
+                    arow = s_AR + ((m & 4) ? 16 + m : 4 + m) * LD;
+                    brow = s_BL + (16 + l16) * LD;
+                }
+                const f32x4 d = rows_product(arow, brow, kq);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const TileEntry e = tile_entry(tile, 4 * kq + r, l16);
-                        if (e.valid) s_M[tile_matrix(e, MLAB) * 256 + e.t * 16 + e.s] = d[r];
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    const TileEntry e = tile_entry(tile, 4 * kq + r, l16);
+                    if (e.valid) s_M[tile_matrix(e, MLAB) * 256 + e.t * 16 + e.s] = d[r];
+                }
+            };
+            if (wave == 4) product(IC<0>{});
+            else product(IC<1>{});
         } else if (wave < 10) {
             // 64 items (sub-chunk p, pair k) x 4 quarters of the 64 columns
             // = 256 units, one per lane of waves 6-9
@@ -547,19 +554,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = g[r];
         } else if (wave < 15) {
-            const int mi = wave - 12;                    // dL_ab, dL_ak, dM_rb
-            const float *lhs = mi < 2 ? s_DR : sDY;
-            const float *rt = mi == 1 ? sV : s_X;
-            f32x4 gm = {0.f, 0.f, 0.f, 0.f};
-            gm = mm_AtBt(gm, lhs, LD, rt, LD, l16, kq, 64);
+            // dL_ab, dL_ak, dM_rb; the matrix index is made a compile-time
+            // constant so that the scatter's index maps fold
+            auto product = [&](auto MI) {
+                constexpr int mi = decltype(MI)::value;
+                const float *lhs = mi < 2 ? s_DR : sDY;
+                const float *rt = mi == 1 ? sV : s_X;
+                f32x4 gm = {0.f, 0.f, 0.f, 0.f};
+                gm = mm_AtBt(gm, lhs, LD, rt, LD, l16, kq, 64);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * kq + r;
-                const bool keep = mi < 2 ? (l16 < t) : (l16 <= t);
-                const float v = keep ? gm[r] : 0.f;
-                s_M[(MDLAB + mi) * 256 + t * 16 + l16] = v;
-                tile_scatter(s_M, mi < 2, mi != 1, t, l16, v);
-            }
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * kq + r;
+                    const bool keep = mi < 2 ? (l16 < t) : (l16 <= t);
+                    const float v = keep ? gm[r] : 0.f;
+                    s_M[(MDLAB + mi) * 256 + t * 16 + l16] = v;
+                    tile_scatter(s_M, mi < 2, mi != 1, t, l16, v);
+                }
+            };
+            if (wave == 12) product(IC<0>{});
+            else if (wave == 13) product(IC<1>{});
+            else product(IC<2>{});
         }
         lds_barrier();
         relane();
@@ -623,16 +637,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 constexpr int t = decltype(TT)::value;
                 constexpr int p0 = t & ~3;                    // first token of t's sub-chunk
                 // decay factors of column j at token t
-                float gam = 1.f, gprev = 1.f, dend = 1.f, fex = 1.f, fin = 1.f, suf = 1.f;
+                // each product is one left-to-right chain; gam, fin and dend
+                // extend gprev, fex and suf
+                float gprev = 1.f, fex = 1.f, suf = 1.f;
 #pragma unroll
-                for (int u2 = 0; u2 < 16; ++u2) {
-                    if (u2 < t) gprev *= wv[u2];
-                    if (u2 <= t) gam *= wv[u2];
-                    if (u2 > t) dend *= wv[u2];
-                    if (u2 >= p0 && u2 < t) fex *= wv[u2];
-                    if (u2 >= p0 && u2 <= t) fin *= wv[u2];
-                    if (u2 > t && u2 < p0 + 4) suf *= wv[u2];
-                }
+                for (int u2 = 0; u2 < t; ++u2) gprev *= wv[u2];
+#pragma unroll
+                for (int u2 = p0; u2 < t; ++u2) fex *= wv[u2];
+#pragma unroll
+                for (int u2 = t + 1; u2 < p0 + 4; ++u2) suf *= wv[u2];
+                const float gam = gprev * wv[t], fin = fex * wv[t];
+                float dend = suf;
+#pragma unroll
+                for (int u2 = p0 + 4; u2 < 16; ++u2) dend *= wv[u2];
                 const float invF = __builtin_amdgcn_rcpf(fin);
                 const float *zA1 = s_Z + ZA1 * 16 * LD + j, *zB1 = s_Z + ZB1 * 16 * LD + j;
                 const float *zA2 = s_Z + ZA2 * 16 * LD + j, *zB2 = s_Z + ZB2 * 16 * LD + j;
