@@ -115,7 +115,8 @@ wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes) {
     if (!bytes) return WKV7_ERR_INVALID_ARGUMENT;
     const wkv7_status st = check_desc(d);
     if (st != WKV7_OK) return st;
-    // one fp32 64x64 state-gradient slot per checkpoint slot and head
+    // per checkpoint slot and head: the fp32 64x64 state gradient leaving the
+    // chunk and the fp32 16x64 drhs of the chunk
     int64_t slots = 0;
     if (d->num_seqs > 0) {
         if (d->ckpt_slots < 0) return WKV7_ERR_INVALID_ARGUMENT;
@@ -123,7 +124,7 @@ wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes) {
     } else {
         slots = (int64_t)d->B * ((d->T + kChunk - 1) / kChunk);
     }
-    *bytes = (size_t)slots * d->H * kN * kN * sizeof(float);
+    *bytes = (size_t)slots * d->H * (kN * kN + kChunk * kN) * sizeof(float);
     return WKV7_OK;
 }
 
@@ -208,6 +209,10 @@ wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, cons
     args.dr = dr; args.dw = dw; args.dk = dk; args.dv = dv; args.da = da; args.db = db;
     args.ds0 = ds0;
     args.ws = (float *)workspace;
+    {
+        const int64_t slots = d->num_seqs > 0 ? d->ckpt_slots : (int64_t)d->B * ((d->T + kChunk - 1) / kChunk);
+        args.ws_dr = args.ws + slots * d->H * kN * kN;
+    }
     if (d->num_seqs > 0) {
         void *outs[6] = {dr, dw, dk, dv, da, db};
         if (wkv7::launch_zero_uncovered(args.seg, d->grad_f32 ? WKV7_F32 : d->dtype, outs, 6, hs) != hipSuccess)

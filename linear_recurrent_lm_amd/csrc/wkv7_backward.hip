@@ -3,8 +3,9 @@
 // Forward recurrence (RWKV-7 WKV-7): S_t = S_{t-1} diag(w_t) + (S_{t-1} a_t) b_t^T
 // + v_t k_t^T, y_t = S_t r_t. Gradients of L = sum <dy, y> + <ds_out, S_T>.
 // Each chunk starts from its stored checkpoint S_0 (the state entering the
-// chunk) and from dS_C, the gradient of the state leaving it, written by the
-// first pass (the state-gradient sweep); with both given, chunks are
+// chunk), dS_C (the gradient of the state leaving it) and drhs = W^T dX (see
+// below); the last two are written by the first pass (the state-gradient
+// sweep), which computes them anyway. With these given, chunks are
 // independent and run in parallel, kChunksPerGroup consecutive chunks per
 // workgroup. Nothing is reconstructed by dividing by w.
 //
@@ -13,7 +14,7 @@
 //     Y = R^ S_0^T + M_rb X + M_rk V
 //     S_C = S_0 diag(gamma_C) + X^T B^ + V^T K^
 // and its reverse mode is
-//     dX   = B^ dS_C^T + M_rb^T dY          drhs = W^T dX
+//     dX   = B^ dS_C^T + M_rb^T dY          drhs = W^T dX   (both from the sweep)
 //     dV   = K^ dS_C^T + M_rk^T dY + L_ak^T drhs
 //     dA^ = drhs S_0, dR^ = dY S_0, dB^ = X dS_C, dK^ = V dS_C
 //     dL_ab = drhs X^T, dL_ak = drhs V^T (strictly lower), dM_rb = dY X^T,
@@ -41,10 +42,13 @@
 // throughout, so dw is finite at w = 0 and equals the gradient there to
 // within the clamp.
 //
-// One 512-thread workgroup (8 waves) per (sequence, head, chunk group). 16x64
-// chunk matrices and the two 64x64 states live in LDS, row-major; MFMA
+// One 1024-thread workgroup (16 waves) per (sequence, head, chunk group).
+// 16x64 chunk matrices and the two 64x64 states live in LDS, row-major; MFMA
 // operands are 16-byte loads along the contraction index where the layout
-// allows it. Waves w and w+4 share a SIMD and take complementary work.
+// allows it. Wave w runs on SIMD w % 4; the roles of a phase are spread so
+// that the four SIMDs carry similar MFMA and VALU work.
+#include <type_traits>
+
 #include "wkv7_kernels.h"
 #include "wkv7_mfma.h"
 
@@ -72,8 +76,9 @@ constexpr int O_DR = O_X + 16 * LD;          // [16][LD] drhs[t][i]
 constexpr int O_G = O_DR + 16 * LD;          // [4][16][LD] dA^, dR^, dB^, dK^ ([t][j])
 constexpr int O_M = O_G + 64 * LD;           // [11][256] Lab Lak Mrb Mrk W dLab dLak dMrb dMrk dD1 dD2
 constexpr int O_GC = O_M + 11 * 256;         // [64] gamma_C
-constexpr int O_DGC = O_GC + 64;             // [64] d gamma_C
-constexpr int LDS_FLOATS = O_DGC + 64;
+constexpr int O_DGC = O_GC + 64;             // [4][64] d gamma_C, partial sums over 16 rows each
+constexpr int O_GO = O_DGC + 4 * 64;         // [6][16][64] 16-bit gradients dv dr da db dk dw of a chunk
+constexpr int LDS_FLOATS = O_GO + 6 * 16 * 64 / 2;
 static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
 
 enum { IR = 0, IW, IK, IA, IB, IV, IDY };
@@ -88,9 +93,11 @@ enum { UCHA = 0, UCHR, UCHC, UR12A, UR12R, UR3A, UR3R, UC2, UC13, kUTerms };
 
 // acc[m][n] += sum_k A[m][k] B[k][n] with A row-major (pitch lda) and B given
 // transposed, Bt[n][k] row-major (pitch ldb): both operands 16-byte loads.
+template <int KDIM>
 __device__ __forceinline__ f32x4 mm_AtBt(f32x4 acc, const float *A, int lda, const float *Bt, int ldb,
-                                         int l16, int kq, int kdim) {
-    for (int k0 = 0; k0 < kdim; k0 += 16) {
+                                         int l16, int kq) {
+#pragma unroll
+    for (int k0 = 0; k0 < KDIM; k0 += 16) {
         const float4 a = *(const float4 *)(A + l16 * lda + k0 + 4 * kq);
         const float4 b = *(const float4 *)(Bt + l16 * ldb + k0 + 4 * kq);
         acc = mfma4(a.x, b.x, acc); acc = mfma4(a.y, b.y, acc);
@@ -101,9 +108,11 @@ __device__ __forceinline__ f32x4 mm_AtBt(f32x4 acc, const float *A, int lda, con
 
 // acc += A B with A row-major (16-byte loads along k) and B row-major [k][n]
 // (scalar loads; consecutive lanes read consecutive n).
+template <int KDIM>
 __device__ __forceinline__ f32x4 mm_AtB(f32x4 acc, const float *A, int lda, const float *B, int ldb,
-                                        int l16, int kq, int kdim) {
-    for (int k0 = 0; k0 < kdim; k0 += 16) {
+                                        int l16, int kq) {
+#pragma unroll
+    for (int k0 = 0; k0 < KDIM; k0 += 16) {
         const float4 a = *(const float4 *)(A + l16 * lda + k0 + 4 * kq);
         const float *bp = B + (k0 + 4 * kq) * ldb + l16;
         acc = mfma4(a.x, bp[0], acc); acc = mfma4(a.y, bp[ldb], acc);
@@ -111,6 +120,14 @@ __device__ __forceinline__ f32x4 mm_AtB(f32x4 acc, const float *A, int lda, cons
     }
     return acc;
 }
+
+// The 16-bit encoding of a gradient element (round to nearest even).
+template <typename TI> __device__ __forceinline__ uint16_t out_bits(float x);
+template <> __device__ __forceinline__ uint16_t out_bits<uint16_t>(float x) { return f32_to_bf16(x); }
+template <> __device__ __forceinline__ uint16_t out_bits<_Float16>(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+template <> __device__ __forceinline__ uint16_t out_bits<float>(float) { return 0; }   // not used
 
 // acc += A^T B for A = [k][m], B = [k][n] row-major with 16 rows k.
 __device__ __forceinline__ f32x4 mm_TB(f32x4 acc, const float *A, int lda, const float *B, int ldb,
@@ -195,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
     // u terms reuse dS_C, X, drhs (6 arrays) and A^, R^, B^, K^ (3 arrays) once consumed
     auto s_U = [&](int term) { return sm + (term < 6 ? O_DS + term * 16 * LD : O_Q + (term - 6) * 16 * LD); };
     const float *sV = s_in + IV * 16 * LD, *sDY = s_in + IDY * 16 * LD;
-    const float *Mlak = s_M + MLAK * 256, *Mmrb = s_M + MMRB * 256, *Mmrk = s_M + MMRK * 256;
+    const float *Mlak = s_M + MLAK * 256, *Mmrk = s_M + MMRK * 256;
     const float *Mw = s_M + MW * 256;
 
     const int64_t ts = (int64_t)H * kN;
@@ -216,37 +233,77 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
     for (int q = tid; q < 4 * 256; q += kThreads) s_M[q] = 0.f;
     for (int q = tid; q < 256; q += kThreads) s_M[MDD2 * 256 + q] = 0.f;
 
-    // Staging: element groups g = tid + 1024k (k = 0, 1) of 7 streams x 16
-    // tokens x 16 groups of 4 (a 16-byte LDS store per group, consecutive
-    // lanes on consecutive groups); stream g >> 8 is uniform per wave. Loads
-    // are issued one chunk ahead, unconditionally (token rows clamped into the
-    // sequence), so the registers in flight have one definition per iteration;
-    // groups of a missing stream (dy == NULL, or past the seven streams) load
-    // the w row instead and stage as fill.
-    Raw4<TI> raw[2];
-    float4 ckr, dsr;                            // checkpoint S_0 and dS_C of the chunk in flight
-    const TI *sp[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int st = __builtin_amdgcn_readfirstlane((tid + k * kThreads) >> 8);
-        const void *vp = st < 7 ? p.staged[st] : nullptr;
-        sp[k] = vp ? (const TI *)vp + base : nullptr;
-    }
-    const TI *wrow = (const TI *)p.w + base;
+    // Staging: thread tid stages 8 consecutive elements of stream tid / 128
+    // (uniform per wave; waves 14, 15 stage none): group g = tid % 128 is
+    // token g / 8, elements 8 (g % 8)... Loads are issued one chunk ahead with
+    // token rows clamped into the sequence; a missing stream (dy == NULL) is
+    // not loaded and stages as zeros.
+    Raw<TI, 1> raw;
+    float4 ckr, dsr, drr;                       // checkpoint S_0, dS_C, drhs of the chunk in flight
+    const int sst = __builtin_amdgcn_readfirstlane(tid >> 7);
+    const TI *ssp = sst < 7 && p.staged[sst] ? (const TI *)p.staged[sst] + base : nullptr;
     auto issue = [&](int cc) {
         const int Lc = min(kChunk, u.len - cc * kChunk);
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int g = tid + k * kThreads;
-            const int t = min((g >> 4) & 15, Lc - 1), e0 = (g & 15) * 4;
-            raw4_load((sp[k] ? sp[k] : wrow) + (int64_t)(cc * kChunk + t) * ts + e0, raw[k]);
+        if (ssp) {
+            const int g = tid & 127;
+            const int t = min(g >> 3, Lc - 1);
+            raw_load(ssp + (int64_t)(cc * kChunk + t) * ts + (g & 7) * 8, raw, 0);
         }
         // float4 tid of a 64x64 state: row tid / 16, column 4 (tid % 16)
         const int64_t so = ((u.ckpt + cc) * H + h) * (int64_t)(kN * kN) + tid * 4;
         ckr = *(const float4 *)(p.ckpt + so);
         dsr = *(const float4 *)(p.ws + so);
+        // drhs [16][64]: float4 tid of waves 0-3
+        if (wave < 4) drr = *(const float4 *)(p.ws_dr + ((u.ckpt + cc) * H + h) * (int64_t)(kChunk * kN) + tid * 4);
     };
     issue(c_hi - 1);
+
+    // Gradient stores of a chunk are issued in the next chunk's staging phase,
+    // after its loads have been waited for: loads and stores share one
+    // counter, so stores issued just before that wait would hold it until
+    // they are acknowledged. 16-bit gradients are gathered in LDS (s_GO) and
+    // leave as 16-byte stores, 8 elements per lane; fp32 gradients are held in
+    // registers and stored per lane: waves 4-7 hold dv of tokens 4 kq + r at
+    // value column 16 (w & 3) + l16, every wave dr, da, db, dk, dw of token w
+    // at key column lane.
+    const bool wide = !std::is_same<TI, float>::value && !p.grad_f32;
+    uint16_t *s_GO = (uint16_t *)(sm + O_GO);
+    float pdv[4] = {0.f, 0.f, 0.f, 0.f}, pg[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+    auto flush = [&](int cc) {
+        const int tc = cc * kChunk, Lc = min(kChunk, u.len - tc);
+        if (wide) {
+            if (wave < 12) {
+                // row tid / 8 of s_GO: gradient tid / 128 (uniform per wave), token (tid / 8) % 16
+                const int gi = __builtin_amdgcn_readfirstlane(tid >> 7);
+                const int t = (tid >> 3) & 15, c8 = (tid & 7) * 8;
+                const uint4 v = *(const uint4 *)(s_GO + (tid >> 3) * 64 + c8);
+                void *gp = gi == 0 ? p.dv : gi == 1 ? p.dr : gi == 2 ? p.da : gi == 3 ? p.db
+                         : gi == 4 ? p.dk : p.dw;
+                if (t < Lc) *(uint4 *)((uint16_t *)gp + base + (int64_t)(tc + t) * ts + c8) = v;
+            }
+            return;
+        }
+        if (wave >= 4 && wave < 8) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * kq + r;
+                if (t < Lc) gst(p.dv, base + (int64_t)(tc + t) * ts + 16 * w4 + l16, pdv[r]);
+            }
+        }
+        if (wave < Lc) {
+            const int64_t o = base + (int64_t)(tc + wave) * ts + lane;
+            gst(p.dr, o, pg[0]);
+            gst(p.da, o, pg[1]);
+            gst(p.db, o, pg[2]);
+            gst(p.dk, o, pg[3]);
+            gst(p.dw, o, pg[4]);
+        }
+    };
+    // one gradient element of a chunk: into s_GO (16-bit) or the registers
+    auto gput = [&](int gi, int t, int col, float v, float &reg) {
+        if (wide) s_GO[(gi * 16 + t) * 64 + col] = out_bits<TI>(v);
+        else reg = v;
+    };
 
 #pragma unroll 1
     for (int c = c_hi - 1; c >= c_lo; --c) {
@@ -257,27 +314,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 
         // ---- P0: stage inputs (w clamped; identity tokens past the end), the
         //      checkpoint S_0 and dS_C; then prefetch the next chunk
+        if (sst < 7) {
+            const int t = (tid >> 3) & 15, e0 = (tid & 7) * 8;
+            float x[8];
+            if (ssp) {
+                raw_unpack(raw, 0, x);
+            } else {
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int g = tid + k * kThreads;
-            if (g < 7 * 256) {
-                const int st = g >> 8, t = (g >> 4) & 15, e0 = (g & 15) * 4;
-                float x[4];
-                raw4_unpack(raw[k], x);          // unconditional: no path leaves the loads pending
-                if (st == IW) decay_of<4>(x, p.logw);
-                const bool keep = t < L && sp[k] != nullptr;
-                const float f = st == IW ? 1.f : 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float v = keep ? x[e] : f;
-                    x[e] = st == IW ? fmaxf(v, kMinW) : v;
-                }
-                *(float4 *)(s_in + (st * 16 + t) * LD + e0) = make_float4(x[0], x[1], x[2], x[3]);
+                for (int e = 0; e < 8; ++e) x[e] = 0.f;
             }
+            if (sst == IW) decay_of<8>(x, p.logw);
+            const bool keep = t < L;
+            const float f = sst == IW ? 1.f : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = keep ? x[e] : f;
+                x[e] = sst == IW ? fmaxf(v, kMinW) : v;
+            }
+            float *d = s_in + (sst * 16 + t) * LD + e0;
+            *(float4 *)d = make_float4(x[0], x[1], x[2], x[3]);
+            *(float4 *)(d + 4) = make_float4(x[4], x[5], x[6], x[7]);
         }
         *(float4 *)(s_S0 + (tid >> 4) * LD + (tid & 15) * 4) = ckr;
         *(float4 *)(s_DS + (tid >> 4) * LD + (tid & 15) * 4) = dsr;
+        if (wave < 4) *(float4 *)(s_DR + (tid >> 4) * LD + (tid & 15) * 4) = drr;
         issue(max(c - 1, c_lo));
+        if (c < c_hi - 1) flush(c + 1);
         lds_barrier();
         relane();
 
@@ -365,7 +427,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             const int jc = 16 * w4;
             const bool isR = wave < 12;
             f32x4 g = {0.f, 0.f, 0.f, 0.f};
-            g = mm_AtB(g, isR ? sDY : sV, LD, (isR ? s_S0 : s_DS) + jc, LD, l16, kq, 64);
+            g = mm_AtB<64>(g, isR ? sDY : sV, LD, (isR ? s_S0 : s_DS) + jc, LD, l16, kq);
             float *dst = s_G + (isR ? 1 : 3) * 16 * LD + jc + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = g[r];
@@ -375,12 +437,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 
         // ---- P2: waves 0-3: P_a = A^ S_0^T (value rows 16 w..); waves 4, 5: the
         //      split-point products; waves 6-9: the within-sub-chunk pairs;
-        //      waves 10-13: dX = B^ dS_C^T (value rows 16 (w-10)..); wave 14:
-        //      dM_rk = dY V^T; wave 15: d gamma_C[j] = sum_i dS_C[i][j] S_0[i][j]
+        //      waves 10-13: d gamma_C[j] = sum_i dS_C[i][j] S_0[i][j] over rows
+        //      16 (w-10)..; wave 14: dM_rk = dY V^T
         f32x4 pa = {0.f, 0.f, 0.f, 0.f};            // waves 0-3 (then rhs, X)
-        f32x4 dx = {0.f, 0.f, 0.f, 0.f};            // waves 10-13 (then drhs)
         if (wave < 4) {
-            pa = mm_AtBt(pa, s_Q, LD, s_S0 + 16 * w4 * LD, LD, l16, kq, 64);
+            pa = mm_AtBt<64>(pa, s_Q, LD, s_S0 + 16 * w4 * LD, LD, l16, kq);
         } else if (wave < 6) {
             // the tile index is made a compile-time constant so that the
             // scatter's index map folds
@@ -444,11 +505,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 s_M[(isL ? MLAK : MMRK) * 256 + o] = k_;
             }
         } else if (wave < 14) {
-            const int i0 = 16 * (wave - 10);
-            dx = mm_AtBt(dx, s_BK, LD, s_DS + i0 * LD, LD, l16, kq, 64);
+            const int j = lane, i0 = 16 * (wave - 10);
+            float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+            for (int i = i0; i < i0 + 16; i += 2) {
+                acc0 = fmaf(s_DS[i * LD + j], s_S0[i * LD + j], acc0);
+                acc1 = fmaf(s_DS[(i + 1) * LD + j], s_S0[(i + 1) * LD + j], acc1);
+            }
+            s_dgC[(wave - 10) * 64 + j] = acc0 + acc1;
         } else if (wave == 14) {
             f32x4 gm = {0.f, 0.f, 0.f, 0.f};
-            gm = mm_AtBt(gm, sDY, LD, sV, LD, l16, kq, 64);
+            gm = mm_AtBt<64>(gm, sDY, LD, sV, LD, l16, kq);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * kq + r;
@@ -456,15 +523,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 s_M[MDMRK * 256 + t * 16 + l16] = v;
                 tile_scatter(s_M, false, false, t, l16, v);
             }
-        } else {
-            const int j = lane;
-            float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll 8
-            for (int i = 0; i < 64; i += 2) {
-                acc0 = fmaf(s_DS[i * LD + j], s_S0[i * LD + j], acc0);
-                acc1 = fmaf(s_DS[(i + 1) * LD + j], s_S0[(i + 1) * LD + j], acc1);
-            }
-            s_dgC[j] = acc0 + acc1;
         }
         lds_barrier();
         relane();
@@ -472,13 +530,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         // ---- P3: wave 8: W = (I - L_ab)^-1 (column c = lane / 4, rows t =
         //      lane % 4 + 4i held by the 4 lanes of a quad, forward substitution);
         //      waves 0-3: rhs = P_a + L_ak V; waves 4-7: dV partial = K^ dS_C^T +
-        //      M_rk^T dY (value rows 16 (w-4)..); waves 10-13: dX += M_rb^T dY
+        //      M_rk^T dY (value rows 16 (w-4)..)
         f32x4 dvp = {0.f, 0.f, 0.f, 0.f};           // waves 4-7
         if (wave < 4) {
-            pa = mm_AtB(pa, Mlak, 16, sV + 16 * w4, LD, l16, kq, 16);
+            pa = mm_AtB<16>(pa, Mlak, 16, sV + 16 * w4, LD, l16, kq);
         } else if (wave < 8) {
             const int i0 = 16 * w4;
-            dvp = mm_AtBt(dvp, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq, 64);
+            dvp = mm_AtBt<64>(dvp, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq);
             dvp = mm_TB(dvp, Mmrk, 16, sDY + i0, LD, l16, kq);
         } else if (wave == 8) {
             const int col = lane >> 2, q = lane & 3;
@@ -503,36 +561,48 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) s_M[MW * 256 + (q + 4 * i) * 16 + col] = x[i];
-        } else if (wave >= 10 && wave < 14) {
-            dx = mm_TB(dx, Mmrb, 16, sDY + 16 * (wave - 10), LD, l16, kq);
         }
         lds_barrier();
         relane();
 
-        // ---- P4: waves 0-3: X = W rhs; waves 10-13: drhs = W^T dX (value rows
-        //      16 (w & 3)..), both into LDS
-        if (wave < 4 || (wave >= 10 && wave < 14)) {
-            const int i0 = 16 * (wave < 4 ? wave : wave - 10);
-            f32x4 o = {0.f, 0.f, 0.f, 0.f};
-            if (wave < 4) {
-                const float4 wr = *(const float4 *)(Mw + l16 * 16 + 4 * kq);
-                o = mfma4(wr.x, pa[0], o); o = mfma4(wr.y, pa[1], o);
-                o = mfma4(wr.z, pa[2], o); o = mfma4(wr.w, pa[3], o);
-            } else {
+        // dL_ab = drhs X^T, dL_ak = drhs V^T, dM_rb = dY X^T (mi = 0, 1, 2),
+        // with their scatter into the index maps of the split-point products;
+        // the matrix index is a compile-time constant so that the scatter's
+        // index maps fold
+        auto dlm_product = [&](auto MI) {
+            constexpr int mi = decltype(MI)::value;
+            const float *lhs = mi < 2 ? s_DR : sDY;
+            const float *rt = mi == 1 ? sV : s_X;
+            f32x4 gm = {0.f, 0.f, 0.f, 0.f};
+            gm = mm_AtBt<64>(gm, lhs, LD, rt, LD, l16, kq);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o = mfma4(Mw[(4 * kq + e) * 16 + l16], dx[e], o);
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * kq + r;
+                const bool keep = mi < 2 ? (l16 < t) : (l16 <= t);
+                const float v = keep ? gm[r] : 0.f;
+                s_M[(MDLAB + mi) * 256 + t * 16 + l16] = v;
+                tile_scatter(s_M, mi < 2, mi != 1, t, l16, v);
             }
-            float *dst = (wave < 4 ? s_X : s_DR) + i0 + l16;
+        };
+
+        // ---- P4: waves 0-3: X = W rhs (value rows 16 w..) into LDS. drhs =
+        //      W^T dX was staged from the sweep's output in P0.
+        if (wave < 4) {
+            const int i0 = 16 * wave;
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+            const float4 wr = *(const float4 *)(Mw + l16 * 16 + 4 * kq);
+            o = mfma4(wr.x, pa[0], o); o = mfma4(wr.y, pa[1], o);
+            o = mfma4(wr.z, pa[2], o); o = mfma4(wr.w, pa[3], o);
+            float *dst = s_X + i0 + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = o[r];
         }
         lds_barrier();
         relane();
 
-        // ---- P5: waves 4-7 finish dV = partial + L_ak^T drhs and store it;
-        //      waves 0-3: dA^ = drhs S_0, waves 8-11: dB^ = X dS_C (key columns
-        //      16 (w & 3)..); waves 12, 13, 14: dL_ab = drhs X^T, dL_ak = drhs V^T,
-        //      dM_rb = dY X^T
+        // ---- P5: waves 4-7 finish dV = partial + L_ak^T drhs (held for the
+        //      store); waves 0-3: dA^ = drhs S_0, waves 8-11: dB^ = X dS_C (key
+        //      columns 16 (w & 3)..); waves 12, 13, 14: dL_ab, dL_ak, dM_rb
         if (wave >= 4 && wave < 8) {
             const int i0 = 16 * w4;
 #pragma unroll
@@ -541,39 +611,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 dvp = mfma4(Mlak[k * 16 + l16], s_DR[k * LD + i0 + l16], dvp);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * kq + r;
-                if (t < L) gst(p.dv, base + (int64_t)(t0 + t) * ts + i0 + l16, dvp[r]);
-            }
+            for (int r = 0; r < 4; ++r) gput(0, 4 * kq + r, i0 + l16, dvp[r], pdv[r]);
         } else if (wave < 12) {
             const int jc = 16 * w4;
             const bool isA = wave < 4;
             f32x4 g = {0.f, 0.f, 0.f, 0.f};
-            g = mm_AtB(g, isA ? s_DR : s_X, LD, (isA ? s_S0 : s_DS) + jc, LD, l16, kq, 64);
+            g = mm_AtB<64>(g, isA ? s_DR : s_X, LD, (isA ? s_S0 : s_DS) + jc, LD, l16, kq);
             float *dst = s_G + (isA ? 0 : 2) * 16 * LD + jc + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = g[r];
-        } else if (wave < 15) {
-            // dL_ab, dL_ak, dM_rb; the matrix index is made a compile-time
-            // constant so that the scatter's index maps fold
-            auto product = [&](auto MI) {
-                constexpr int mi = decltype(MI)::value;
-                const float *lhs = mi < 2 ? s_DR : sDY;
-                const float *rt = mi == 1 ? sV : s_X;
-                f32x4 gm = {0.f, 0.f, 0.f, 0.f};
-                gm = mm_AtBt(gm, lhs, LD, rt, LD, l16, kq, 64);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 4 * kq + r;
-                    const bool keep = mi < 2 ? (l16 < t) : (l16 <= t);
-                    const float v = keep ? gm[r] : 0.f;
-                    s_M[(MDLAB + mi) * 256 + t * 16 + l16] = v;
-                    tile_scatter(s_M, mi < 2, mi != 1, t, l16, v);
-                }
-            };
-            if (wave == 12) product(IC<0>{});
-            else if (wave == 13) product(IC<1>{});
-            else product(IC<2>{});
+        } else if (wave == 12) {
+            dlm_product(IC<0>{});
+        } else if (wave == 13) {
+            dlm_product(IC<1>{});
+        } else if (wave == 14) {
+            dlm_product(IC<2>{});
         }
         lds_barrier();
         relane();
@@ -701,13 +753,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 const float dAh = s_G[(0 * 16 + t) * LD + j], dRh = s_G[(1 * 16 + t) * LD + j];
                 const float dBh = s_G[(2 * 16 + t) * LD + j], dKh = s_G[(3 * 16 + t) * LD + j];
                 const float dac = dAh * gprev, drc = dRh * gam, dbc = dBh * dend, dkc = dKh * dend;
-                if (t < L) {
-                    const int64_t o = base + (int64_t)(t0 + t) * ts + j;
-                    gst(p.dr, o, drc + fin * qr + r8 + r4);
-                    gst(p.da, o, dac + fex * qa + a8 + a4);
-                    gst(p.db, o, dbc + invF * qb + b8 + b4);
-                    gst(p.dk, o, dkc + invF * qk + k8 + k4);
-                }
+                gput(1, t, j, drc + fin * qr + r8 + r4, pg[0]);
+                gput(2, t, j, dac + fex * qa + a8 + a4, pg[1]);
+                gput(3, t, j, dbc + invF * qb + b8 + b4, pg[2]);
+                gput(4, t, j, dkc + invF * qk + k8 + k4, pg[3]);
                 // u terms that the scans below read (ranges with structural zeros
                 // are neither written nor read)
                 const int o = t * LD + j;
@@ -852,19 +901,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         relane();
 
         // ---- P7c: u_m for m = w: the five partial sums and d gamma_C gamma_C;
-        //      dw = u / w; store
+        //      dw = u / w (stored with the other gradients of the chunk)
         {
             const int j = lane, m = wave;
             const int o = m * LD + j;
-            const float x = s_dgC[j] * s_gC[j] + ((s_Z[o] + s_Z[16 * LD + o]) + (s_Z[32 * LD + o] + s_Z[48 * LD + o]))
+            const float dgc = (s_dgC[j] + s_dgC[64 + j]) + (s_dgC[128 + j] + s_dgC[192 + j]);
+            const float x = dgc * s_gC[j] + ((s_Z[o] + s_Z[16 * LD + o]) + (s_Z[32 * LD + o] + s_Z[48 * LD + o]))
                           + s_G[o];
             // d/dw = u / w (v_rcp_f32, within 1 ulp); for a log-decay input
             // d/d log(w) = u itself
-            if (m < L)
-                gst(p.dw, base + (int64_t)(t0 + m) * ts + j,
-                    p.logw ? x : x * __builtin_amdgcn_rcpf(s_in[IW * 16 * LD + o]));
+            gput(5, m, j, p.logw ? x : x * __builtin_amdgcn_rcpf(s_in[IW * 16 * LD + o]), pg[4]);
         }
     }
+    lds_barrier();
+    relane();
+    flush(c_lo);
 }
 
 }  // namespace

@@ -171,6 +171,11 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
                 f32x4 dr = {0.f, 0.f, 0.f, 0.f};
                 dr = mfma4(wt.x, dx[0], dr); dr = mfma4(wt.y, dx[1], dr);
                 dr = mfma4(wt.z, dx[2], dr); dr = mfma4(wt.w, dx[3], dr);
+                if (KS == 1 || kh == 0) {        // drhs[t][i] of this chunk for the second pass
+                    float *dp = p.ws_dr + ((u.ckpt + cs) * H + h) * (int64_t)(kChunk * kN) + irow;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dp[(4 * kq + r) * kN] = dr[r];
+                }
 #pragma unroll
                 for (int qq = 0; qq < NQ; ++qq) {
                     const int q = q0 + qq;

@@ -31,6 +31,7 @@ struct BwdArgs {
     void *dr, *dw, *dk, *dv, *da, *db;
     float *ds0;
     float *ws;                       // per-slot dS_C of the sweep ([slots][H][N][N] fp32)
+    float *ws_dr;                    // per-slot drhs = W^T dX of the sweep ([slots][H][16][N] fp32)
     const void *staged[8];           // filled by the launcher: r w k a b v dy, null
 };
 
