@@ -208,11 +208,14 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
 
     // Staging (operand waves 4-7): element group g = sid + 256k (k = 0..2) of
     // 5 streams x 16 tokens x 8 groups of 8 elements (groups 640.. unused);
-    // stream g >> 7 is uniform per wave. Loads are issued one chunk ahead,
+    // stream g >> 7 is uniform per wave. Loads are issued ahead,
     // unconditionally (chunk index and token rows clamped into the sequence;
     // a missing dy stages as zeros), so the registers in flight have exactly
-    // one definition per iteration.
-    Raw<TI, 3> raw;
+    // one definition per iteration. For 16-bit inputs two register sets
+    // alternate, which keeps each chunk's loads in flight for two chunk
+    // periods (HBM latency under load exceeds one).
+    constexpr bool kTwoSets = sizeof(TI) == 2;
+    Raw<TI, 3> raw, raw1;
     const TI *sp[3];
     bool sv[3];
 #pragma unroll
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
         sp[k] = (const TI *)vp + base;
         sv[k] = st < SDY || (st == SDY && p.dy != nullptr);
     }
-    auto issue = [&](int cc) {               // 0 <= cc < nch
+    auto issue = [&](int cc, Raw<TI, 3> &raw) {     // 0 <= cc < nch
         const int Lc = min(kChunk, u.len - cc * kChunk);
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
             raw_load(sp[k] + (int64_t)(cc * kChunk + t) * ts + e0, raw, k);
         }
     };
-    auto stage = [&](int cc) {
+    auto stage = [&](int cc, const Raw<TI, 3> &raw) {
         const int Lc = min(kChunk, u.len - cc * kChunk);
         float *s_in = sm + lay::IN + (cc & 1) * lay::IN_SIZE;
 #pragma unroll
@@ -294,16 +297,19 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
             float od[16], os[12];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                float F = 1.f, suf = 1.f;        // suf = prod_{s<u<4q+4} w_u, built downwards
+                float suf = 1.f;                 // suf = prod_{s<u<4q+4} w_u, built downwards
 #pragma unroll
                 for (int e = 3; e >= 0; --e) {
                     if (q < 3) os[4 * q + e] = xv[4 * q + e] * suf;
                     suf *= wv[4 * q + e];
                 }
+                // 1 / F_s from one reciprocal of the sub-chunk's product F_{4q+3},
+                // then 1 / F_{s-1} = w_s / F_s going down
+                float inv = __builtin_amdgcn_rcpf(suf);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    F *= wv[4 * q + e];
-                    od[4 * q + e] = xv[4 * q + e] * __builtin_amdgcn_rcpf(F);
+                for (int e = 3; e >= 0; --e) {
+                    od[4 * q + e] = xv[4 * q + e] * inv;
+                    inv *= wv[4 * q + e];
                 }
             }
             const float W1 = (wv[4] * wv[5]) * (wv[6] * wv[7]);
@@ -320,29 +326,34 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
     };
 
     // ---- phase Y (operand waves 6, 7): hand-off rows for the state waves:
-    //      B^ rows and gamma_C (wave 6); A^, R^ by key column and dY by value row (wave 7)
+    //      B^ rows, gamma_C and dY by value row (wave 6); A^, R^ by key column (wave 7)
     auto handoff_rows = [&](const float *s_in, float *buf) {
         const int j = lane;
         float wv[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) wv[t] = s_in[SW * 1024 + t * 64 + j];
         if (pw == 6) {
-            float bv[16];
+            float bv[16], dv[16];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) bv[t] = s_in[SB * 1024 + t * 64 + j];
+            for (int t = 0; t < 16; ++t) {
+                bv[t] = s_in[SB * 1024 + t * 64 + j];
+                dv[t] = s_in[SDY * 1024 + t * 64 + j];
+            }
             float d = 1.f;
 #pragma unroll
             for (int s = 15; s >= 0; --s) { bv[s] *= d; d *= wv[s]; }
 #pragma unroll
             for (int s = 0; s < 16; ++s) buf[lay::B_BH + s * QLD + j] = bv[s];
             buf[lay::B_GC + j] = d;
+#pragma unroll
+            for (int t = 0; t < 16; t += 4)
+                *(float4 *)(buf + lay::B_DYT + j * VLD + t) = make_float4(dv[t], dv[t + 1], dv[t + 2], dv[t + 3]);
         } else {
-            float av[16], rv[16], dv[16];
+            float av[16], rv[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 av[t] = s_in[SA * 1024 + t * 64 + j];
                 rv[t] = s_in[SR * 1024 + t * 64 + j];
-                dv[t] = s_in[SDY * 1024 + t * 64 + j];
             }
             float g = 1.f;
 #pragma unroll
@@ -356,7 +367,6 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
             for (int t = 0; t < 16; t += 4) {
                 *(float4 *)(dst + t) = make_float4(av[t], av[t + 1], av[t + 2], av[t + 3]);
                 *(float4 *)(dst + 16 + t) = make_float4(rv[t], rv[t + 1], rv[t + 2], rv[t + 3]);
-                *(float4 *)(buf + lay::B_DYT + j * VLD + t) = make_float4(dv[t], dv[t + 1], dv[t + 2], dv[t + 3]);
             }
         }
     };
@@ -487,19 +497,36 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
     // chunk cp + 1, staging of chunk cp - 1; phase Y: the 16x16 matrices and
     // the hand-off rows of chunk cp). The state waves need W only in phase Y.
     if (pw >= 4) {
-        issue(nch - 1);
-        stage(nch - 1);
-        issue(max(nch - 2, 0));
-#pragma unroll 1
-        for (int k = 0; k <= nch; ++k) {
+        // iteration k stages chunk cp - 1 from set rw and refills rw with
+        // chunk cp - 1 - d (d = 2 with two sets, else 1)
+        auto step = [&](int k, Raw<TI, 3> &rw, int d) {
             const int cp = nch - 1 - k;
             float *buf = sm + lay::BUF + (cp & 1) * lay::BUF_SIZE;
             const float *s_in = sm + lay::IN + (cp & 1) * lay::IN_SIZE;
             lds_barrier();
-            if (cp >= 1) stage(cp - 1);
-            issue(max(cp - 2, 0));
+            if (cp >= 1) stage(cp - 1, rw);
+            issue(max(cp - 1 - d, 0), rw);
             lds_barrier();
             if (cp >= 0 && pw >= 6) handoff_rows(s_in, buf);
+        };
+        issue(nch - 1, raw);
+        stage(nch - 1, raw);
+        if constexpr (kTwoSets) {
+            issue(max(nch - 2, 0), raw1);
+            // keep every load of chunk nch-2 ahead of chunk nch-3's, so that
+            // staging chunk nch-2 waits for its own loads only
+            __builtin_amdgcn_sched_barrier(0);
+            issue(max(nch - 3, 0), raw);
+#pragma unroll 1
+            for (int k = 0; k <= nch; k += 2) {
+                step(k, raw1, 2);                  // chunk nch-2-k was loaded into raw1
+                if (k + 1 > nch) break;
+                step(k + 1, raw, 2);               // chunk nch-3-k was loaded into raw
+            }
+        } else {
+            issue(max(nch - 2, 0), raw);
+#pragma unroll 1
+            for (int k = 0; k <= nch; ++k) step(k, raw, 1);
         }
     } else {
 #pragma unroll 1
