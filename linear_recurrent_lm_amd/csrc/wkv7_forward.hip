@@ -348,16 +348,25 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
             float od[16], os[12];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                float F = 1.f, suf = 1.f;        // suf = prod_{s<u<4q+4} w_u, built downwards
+                float suf = 1.f;                 // suf = prod_{s<u<4q+4} w_u, built downwards
 #pragma unroll
                 for (int e = 3; e >= 0; --e) {
                     if (q < 3) os[4 * q + e] = xv[4 * q + e] * suf;
                     suf *= wv[4 * q + e];
                 }
+                // 1 / F_s (factors clamped) from one reciprocal of the
+                // sub-chunk's product F_{4q+3}, then 1 / F_{s-1} = w_s / F_s
+                float wc[4], F = 1.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    F *= fmaxf(wv[4 * q + e], kMinFactor);
-                    od[4 * q + e] = xv[4 * q + e] * __builtin_amdgcn_rcpf(F);
+                    wc[e] = fmaxf(wv[4 * q + e], kMinFactor);
+                    F *= wc[e];
+                }
+                float inv = __builtin_amdgcn_rcpf(F);
+#pragma unroll
+                for (int e = 3; e >= 0; --e) {
+                    od[4 * q + e] = xv[4 * q + e] * inv;
+                    inv *= wc[e];
                 }
             }
             const float W1 = (wv[4] * wv[5]) * (wv[6] * wv[7]);
