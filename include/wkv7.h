@@ -136,8 +136,9 @@ wkv7_status wkv7_forward(const wkv7_desc *d,
  *           wkv7_workspace_bytes, 16-byte aligned, owned by the caller. The
  *           call overwrites it with fp32 per-chunk results of the first
  *           kernel (the gradient of the state leaving each 16-token chunk,
- *           64x64, and the 16x64 product of the chunk's triangular solve's
- *           transpose with its output gradient, per checkpoint slot and
+ *           64x64; the chunk's 16x16 inverse W of its unit-lower triangular
+ *           system; and the 16x64 product of W's transpose with the chunk's
+ *           gradient of that system's solution; per checkpoint slot and
  *           head) and reads them back within the same call; calls that may run
  *           concurrently need separate workspaces. Too small or NULL when
  *           needed: WKV7_ERR_WORKSPACE_TOO_SMALL, before any HIP call.
@@ -174,7 +175,7 @@ wkv7_status wkv7_checkpoint_slots(int32_t B, int32_t T, int64_t *slots);
 
 /* Workspace bytes wkv7_backward needs for this descriptor: checkpoint slots
  * (B * ceil(T / 16) dense, the segment table's slot count otherwise) x H x
- * (64 x 64 + 16 x 64) x 4. */
+ * (64 x 64 + 16 x 64 + 16 x 16) x 4. */
 wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes);
 
 /*

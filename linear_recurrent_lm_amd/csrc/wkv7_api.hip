@@ -116,7 +116,7 @@ wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes) {
     const wkv7_status st = check_desc(d);
     if (st != WKV7_OK) return st;
     // per checkpoint slot and head: the fp32 64x64 state gradient leaving the
-    // chunk and the fp32 16x64 drhs of the chunk
+    // chunk, the fp32 16x64 drhs and the fp32 16x16 W of the chunk
     int64_t slots = 0;
     if (d->num_seqs > 0) {
         if (d->ckpt_slots < 0) return WKV7_ERR_INVALID_ARGUMENT;
@@ -124,7 +124,7 @@ wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes) {
     } else {
         slots = (int64_t)d->B * ((d->T + kChunk - 1) / kChunk);
     }
-    *bytes = (size_t)slots * d->H * (kN * kN + kChunk * kN) * sizeof(float);
+    *bytes = (size_t)slots * d->H * (kN * kN + kChunk * kN + kChunk * kChunk) * sizeof(float);
     return WKV7_OK;
 }
 
@@ -212,6 +212,7 @@ wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, cons
     {
         const int64_t slots = d->num_seqs > 0 ? d->ckpt_slots : (int64_t)d->B * ((d->T + kChunk - 1) / kChunk);
         args.ws_dr = args.ws + slots * d->H * kN * kN;
+        args.ws_w = args.ws_dr + slots * d->H * kChunk * kN;
     }
     if (d->num_seqs > 0) {
         void *outs[6] = {dr, dw, dk, dv, da, db};

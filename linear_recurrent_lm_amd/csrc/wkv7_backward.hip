@@ -3,9 +3,9 @@
 // Forward recurrence (RWKV-7 WKV-7): S_t = S_{t-1} diag(w_t) + (S_{t-1} a_t) b_t^T
 // + v_t k_t^T, y_t = S_t r_t. Gradients of L = sum <dy, y> + <ds_out, S_T>.
 // Each chunk starts from its stored checkpoint S_0 (the state entering the
-// chunk), dS_C (the gradient of the state leaving it) and drhs = W^T dX (see
-// below); the last two are written by the first pass (the state-gradient
-// sweep), which computes them anyway. With these given, chunks are
+// chunk), dS_C (the gradient of the state leaving it), drhs = W^T dX and W
+// (see below); the last three are written by the first pass (the
+// state-gradient sweep), which computes them anyway. With these given, chunks are
 // independent and run in parallel, kChunksPerGroup consecutive chunks per
 // workgroup. Nothing is reconstructed by dividing by w.
 //
@@ -14,7 +14,7 @@
 //     Y = R^ S_0^T + M_rb X + M_rk V
 //     S_C = S_0 diag(gamma_C) + X^T B^ + V^T K^
 // and its reverse mode is
-//     dX   = B^ dS_C^T + M_rb^T dY          drhs = W^T dX   (both from the sweep)
+//     dX   = B^ dS_C^T + M_rb^T dY          drhs = W^T dX   (drhs and W from the sweep)
 //     dV   = K^ dS_C^T + M_rk^T dY + L_ak^T drhs
 //     dA^ = drhs S_0, dR^ = dY S_0, dB^ = X dS_C, dK^ = V dS_C
 //     dL_ab = drhs X^T, dL_ak = drhs V^T (strictly lower), dM_rb = dY X^T,
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
     // token rows clamped into the sequence; a missing stream (dy == NULL) is
     // not loaded and stages as zeros.
     Raw<TI, 1> raw;
-    float4 ckr, dsr, drr;                       // checkpoint S_0, dS_C, drhs of the chunk in flight
+    float4 ckr, dsr, drr, wwr;                  // checkpoint S_0, dS_C, drhs, W of the chunk in flight
     const int sst = __builtin_amdgcn_readfirstlane(tid >> 7);
     const TI *ssp = sst < 7 && p.staged[sst] ? (const TI *)p.staged[sst] + base : nullptr;
     auto issue = [&](int cc) {
@@ -253,8 +253,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         const int64_t so = ((u.ckpt + cc) * H + h) * (int64_t)(kN * kN) + tid * 4;
         ckr = *(const float4 *)(p.ckpt + so);
         dsr = *(const float4 *)(p.ws + so);
-        // drhs [16][64]: float4 tid of waves 0-3
+        // drhs [16][64]: float4 tid of waves 0-3; W [16][16]: float4 lane of wave 14
         if (wave < 4) drr = *(const float4 *)(p.ws_dr + ((u.ckpt + cc) * H + h) * (int64_t)(kChunk * kN) + tid * 4);
+        if (wave == 14) wwr = *(const float4 *)(p.ws_w + ((u.ckpt + cc) * H + h) * (int64_t)(kChunk * kChunk) + lane * 4);
     };
     issue(c_hi - 1);
 
@@ -313,7 +314,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         relane();
 
         // ---- P0: stage inputs (w clamped; identity tokens past the end), the
-        //      checkpoint S_0 and dS_C; then prefetch the next chunk
+        //      checkpoint S_0, dS_C, drhs and W; then prefetch the next chunk and
+        //      store the previous chunk's gradients
         if (sst < 7) {
             const int t = (tid >> 3) & 15, e0 = (tid & 7) * 8;
             float x[8];
@@ -338,16 +340,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         *(float4 *)(s_S0 + (tid >> 4) * LD + (tid & 15) * 4) = ckr;
         *(float4 *)(s_DS + (tid >> 4) * LD + (tid & 15) * 4) = dsr;
         if (wave < 4) *(float4 *)(s_DR + (tid >> 4) * LD + (tid & 15) * 4) = drr;
+        if (wave == 14) *(float4 *)(s_M + MW * 256 + lane * 4) = wwr;
         issue(max(c - 1, c_lo));
         if (c < c_hi - 1) flush(c + 1);
         lds_barrier();
         relane();
 
-        // ---- P1: waves 0-7: per-column rows, one role per wave (lane = key
-        //      column j), each role reading its inputs before its first store;
-        //      waves 8-11: dR^ = dY S_0, waves 12-15: dK^ = V dS_C (key columns
-        //      16 (w & 3)..)
-        if (wave < 8) {
+        // ---- P1: waves 0-7 but 2: per-column rows, one role per wave (lane =
+        //      key column j), each role reading its inputs before its first
+        //      store; waves 8-11: dR^ = dY S_0, waves 12-15: dK^ = V dS_C (key
+        //      columns 16 (w & 3)..). B^ (role 2) is not needed: it enters only
+        //      dX, which comes from the sweep.
+        if (wave < 8 && wave != 2) {
             const int role = wave, j = lane;
             const int st = role == 0 || role == 4 ? IA : role == 1 || role == 5 ? IR
                          : role == 2 || role == 6 ? IB : IK;
@@ -370,12 +374,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 for (int t = 0; t < 16; ++t) { g *= wv[t]; xv[t] *= g; }
 #pragma unroll
                 for (int t = 0; t < 16; ++t) s_Q[(16 + t) * LD + j] = xv[t];
-            } else if (role == 2 || role == 3) {   // B^_s, K^_s = x_s D_{15,s}
+            } else if (role == 3) {      // K^_s = k_s D_{15,s}
                 float d = 1.f;
 #pragma unroll
                 for (int s = 15; s >= 0; --s) { xv[s] *= d; d *= wv[s]; }
 #pragma unroll
-                for (int s = 0; s < 16; ++s) s_BK[(16 * (role - 2) + s) * LD + j] = xv[s];
+                for (int s = 0; s < 16; ++s) s_BK[(16 + s) * LD + j] = xv[s];
             } else if (role == 4 || role == 5) {   // A' = a F_ex, R' = r F_in; times W_2 for t >= 12
                 const int inc = role - 4;
 #pragma unroll
@@ -464,7 +468,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const TileEntry e = tile_entry(tile, 4 * kq + r, l16);
-                    if (e.valid) s_M[tile_matrix(e, MLAB) * 256 + e.t * 16 + e.s] = d[r];
+                    // L_ak and M_rk only: L_ab and M_rb enter only W and dX,
+                    // which come from the sweep
+                    if (e.valid && !e.isB) s_M[tile_matrix(e, MLAB) * 256 + e.t * 16 + e.s] = d[r];
                 }
             };
             if (wave == 4) product(IC<0>{});
@@ -487,26 +493,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             }
             const int t = 4 * sc + et, s = 4 * sc + es;
             const float *ar = s_AR + ((isL ? 0 : 16) + t) * LD + 16 * qtr;
-            const float *bd = s_BD + s * LD + 16 * qtr;
             const float *kd = s_KD + s * LD + 16 * qtr;
-            float b_ = 0.f, k_ = 0.f;
+            float k_ = 0.f;
 #pragma unroll
             for (int jj = 0; jj < 16; jj += 4) {
                 const float4 x = *(const float4 *)(ar + jj);
-                const float4 b = *(const float4 *)(bd + jj);
                 const float4 k4 = *(const float4 *)(kd + jj);
-                b_ = fmaf(x.x, b.x, b_); k_ = fmaf(x.x, k4.x, k_);
-                b_ = fmaf(x.y, b.y, b_); k_ = fmaf(x.y, k4.y, k_);
-                b_ = fmaf(x.z, b.z, b_); k_ = fmaf(x.z, k4.z, k_);
-                b_ = fmaf(x.w, b.w, b_); k_ = fmaf(x.w, k4.w, k_);
+                k_ = fmaf(x.x, k4.x, k_); k_ = fmaf(x.y, k4.y, k_);
+                k_ = fmaf(x.z, k4.z, k_); k_ = fmaf(x.w, k4.w, k_);
             }
-            b_ = quad_sum(b_);
             k_ = quad_sum(k_);
-            if ((lane & 3) == 0) {
-                const int o = t * 16 + s;
-                s_M[(isL ? MLAB : MMRB) * 256 + o] = b_;
-                s_M[(isL ? MLAK : MMRK) * 256 + o] = k_;
-            }
+            if ((lane & 3) == 0) s_M[(isL ? MLAK : MMRK) * 256 + t * 16 + s] = k_;
         } else if (wave < 14) {
             const int j = lane, i0 = 16 * (wave - 10);
             float acc0 = 0.f, acc1 = 0.f;
@@ -530,40 +527,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         lds_barrier();
         relane();
 
-        // ---- P3: wave 8: W = (I - L_ab)^-1 (column c = lane / 4, rows t =
-        //      lane % 4 + 4i held by the 4 lanes of a quad, forward substitution);
-        //      waves 0-3: rhs = P_a + L_ak V; waves 4-7: dV partial = K^ dS_C^T +
-        //      M_rk^T dY (value rows 16 (w-4)..)
+        // ---- P3: waves 0-3: rhs = P_a + L_ak V, then X = W rhs (value rows
+        //      16 w..) into LDS (W of the chunk was staged from the sweep's
+        //      output); waves 4-7: dV partial = K^ dS_C^T + M_rk^T dY (value
+        //      rows 16 (w-4)..)
         f32x4 dvp = {0.f, 0.f, 0.f, 0.f};           // waves 4-7
         if (wave < 4) {
             pa = mm_AtB<16>(pa, Mlak, 16, sV + 16 * w4, LD, l16, kq);
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+            const float4 wr = *(const float4 *)(Mw + l16 * 16 + 4 * kq);
+            o = mfma4(wr.x, pa[0], o); o = mfma4(wr.y, pa[1], o);
+            o = mfma4(wr.z, pa[2], o); o = mfma4(wr.w, pa[3], o);
+            float *dst = s_X + 16 * w4 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = o[r];
         } else if (wave < 8) {
             const int i0 = 16 * w4;
             dvp = mm_AtBt<64>(dvp, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq);
             dvp = mm_TB(dvp, Mmrk, 16, sDY + i0, LD, l16, kq);
-        } else if (wave == 8) {
-            const int col = lane >> 2, q = lane & 3;
-            float Lr[4][16], x[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int s = 0; s < 16; s += 4) {
-                    const float4 v = *(const float4 *)(s_M + MLAB * 256 + (q + 4 * i) * 16 + s);
-                    Lr[i][s] = v.x; Lr[i][s + 1] = v.y; Lr[i][s + 2] = v.z; Lr[i][s + 3] = v.w;
-                }
-                x[i] = q + 4 * i == col ? 1.f : 0.f;
-            }
-#pragma unroll
-            for (int s = 0; s < 15; ++s) {
-                const float xs = quad_bcast(x[s >> 2], s & 3);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float nx = fmaf(Lr[i][s], xs, x[i]);
-                    x[i] = q + 4 * i > s ? nx : x[i];
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s_M[MW * 256 + (q + 4 * i) * 16 + col] = x[i];
         }
         lds_barrier();
         relane();
@@ -588,22 +569,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             }
         };
 
-        // ---- P4: waves 0-3: X = W rhs (value rows 16 w..) into LDS. drhs =
-        //      W^T dX was staged from the sweep's output in P0.
-        if (wave < 4) {
-            const int i0 = 16 * wave;
-            f32x4 o = {0.f, 0.f, 0.f, 0.f};
-            const float4 wr = *(const float4 *)(Mw + l16 * 16 + 4 * kq);
-            o = mfma4(wr.x, pa[0], o); o = mfma4(wr.y, pa[1], o);
-            o = mfma4(wr.z, pa[2], o); o = mfma4(wr.w, pa[3], o);
-            float *dst = s_X + i0 + l16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = o[r];
-        }
-        lds_barrier();
-        relane();
-
-        // ---- P5: waves 4-7 finish dV = partial + L_ak^T drhs (held for the
+        // ---- P4: waves 4-7 finish dV = partial + L_ak^T drhs (held for the
         //      store); waves 0-3: dA^ = drhs S_0, waves 8-11: dB^ = X dS_C (key
         //      columns 16 (w & 3)..); waves 12, 13, 14: dL_ab, dL_ak, dM_rb
         if (wave >= 4 && wave < 8) {
@@ -633,7 +599,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         lds_barrier();
         relane();
 
-        // ---- P6: pair-gradient products of the split-point tiles (waves 0-3):
+        // ---- P5: pair-gradient products of the split-point tiles (waves 0-3):
         //      Z_A = dD B_rows and Z_B = dD^T A_rows of tiles 1, 2 (wave w:
         //      Z_A1, Z_B1, Z_A2, Z_B2), all 64 columns; into s_Z (S_0 is consumed)
         if (wave < 4) {
@@ -674,7 +640,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         lds_barrier();
         relane();
 
-        // ---- P7a: per-token gradients of key column j = lane for token t = w
+        // ---- P6a: per-token gradients of key column j = lane for token t = w
         //      (token bodies specialised at compile time): chunk parts,
         //      split-point pair parts (Z scaled by the decay factors) and
         //      within-sub-chunk pair parts give dr, da, db, dk (stored); the u
@@ -799,7 +765,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         lds_barrier();
         relane();
 
-        // ---- P7b: per key column j = lane, the partial sums of u_m for all m
+        // ---- P6b: per key column j = lane, the partial sums of u_m for all m
         //      (each a prefix or suffix sum over one block's range, so no sum
         //      is formed as a difference): wave 0 chunk rows (t >= m for r,
         //      t > m for a), wave 1 chunk columns (s < m), wave 2 block rows,
@@ -903,7 +869,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         lds_barrier();
         relane();
 
-        // ---- P7c: u_m for m = w: the five partial sums and d gamma_C gamma_C;
+        // ---- P6c: u_m for m = w: the five partial sums and d gamma_C gamma_C;
         //      dw = u / w (stored with the other gradients of the chunk)
         {
             const int j = lane, m = wave;

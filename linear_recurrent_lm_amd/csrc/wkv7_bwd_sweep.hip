@@ -457,8 +457,10 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
     };
 
     // ---- W^T = ((I - L_ab)^-1)^T (phase X, wave 0: column c = lane / 4 of W,
-    //      rows t = lane % 4 + 4i held by the 4 lanes of a quad, forward substitution)
-    auto solve_w = [&](float *buf) {
+    //      rows t = lane % 4 + 4i held by the 4 lanes of a quad, forward
+    //      substitution); W of chunk cw also goes to the workspace for the
+    //      second pass (from the first row block of the unit only)
+    auto solve_w = [&](float *buf, int cw) {
         const int col = lane >> 2, q = lane & 3;
         float Lr[4][16], x[4];
 #pragma unroll
@@ -482,6 +484,11 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
         // W^T[col][t] = W[t][col]: the quad's four lanes hold t = q + 4i
 #pragma unroll
         for (int i = 0; i < 4; ++i) buf[lay::B_M + MWT * 16 * MLD + col * MLD + q + 4 * i] = x[i];
+        if (rb == 0) {
+            float *wp = p.ws_w + ((u.ckpt + cw) * H + h) * (int64_t)(kChunk * kChunk) + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wp[(q + 4 * i) * kChunk] = x[i];
+        }
     };
 
     // Entries of L_ab and of the hand-off matrices that are never written
@@ -536,7 +543,7 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
             const float *s_in = sm + lay::IN + (cp & 1) * lay::IN_SIZE;
             lds_barrier();
             if (pw == 0) {
-                if (k >= 1) solve_w(sm + lay::BUF + ((cp + 1) & 1) * lay::BUF_SIZE);
+                if (k >= 1) solve_w(sm + lay::BUF + ((cp + 1) & 1) * lay::BUF_SIZE, cp + 1);
             } else if (cp >= 0) {
                 matrix_rows(s_in);
             }

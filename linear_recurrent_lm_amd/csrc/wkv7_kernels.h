@@ -32,6 +32,7 @@ struct BwdArgs {
     float *ds0;
     float *ws;                       // per-slot dS_C of the sweep ([slots][H][N][N] fp32)
     float *ws_dr;                    // per-slot drhs = W^T dX of the sweep ([slots][H][16][N] fp32)
+    float *ws_w;                     // per-slot W = (I - L_ab)^-1 of the sweep ([slots][H][16][16] fp32)
     const void *staged[8];           // filled by the launcher: r w k a b v dy, null
 };
 

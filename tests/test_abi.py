@@ -110,9 +110,10 @@ def test_checkpoint_slots():
 
 
 def test_workspace_query():
-    # per checkpoint slot and head: an fp32 64x64 state gradient and a 16x64 drhs
-    assert W.wkv7_workspace_bytes(4, 64, 8, 1) == 4 * 4 * 8 * (64 * 64 + 16 * 64) * 4
-    assert W.wkv7_workspace_bytes(3, 33, 2, 0) == 9 * 2 * (64 * 64 + 16 * 64) * 4
+    # per checkpoint slot and head: an fp32 64x64 state gradient, a 16x64 drhs, a 16x16 W
+    per = 64 * 64 + 16 * 64 + 16 * 16
+    assert W.wkv7_workspace_bytes(4, 64, 8, 1) == 4 * 4 * 8 * per * 4
+    assert W.wkv7_workspace_bytes(3, 33, 2, 0) == 9 * 2 * per * 4
     n = ctypes.c_size_t()
     assert W.lib().wkv7_workspace_bytes(ctypes.byref(desc(N=48)), ctypes.byref(n)) == UNSUPPORTED
 
