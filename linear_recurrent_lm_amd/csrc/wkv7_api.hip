@@ -15,6 +15,7 @@ using wkv7::kChunk;
 using wkv7::kN;
 
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
+constexpr int32_t kMaxHeads = 1 << 16;      // keeps a stream's row pitch H * 64 below 2^24
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -33,7 +34,7 @@ wkv7_status check_desc(const wkv7_desc *d) {
     if (!dtype_ok(d->dtype)) return WKV7_ERR_UNSUPPORTED;
     if (d->decay != WKV7_DECAY_MULT && d->decay != WKV7_DECAY_LOG) return WKV7_ERR_UNSUPPORTED;
     if (d->grad_f32 != 0 && d->grad_f32 != 1) return WKV7_ERR_INVALID_ARGUMENT;
-    if (d->B < 1 || d->T < 1 || d->H < 1) return WKV7_ERR_INVALID_ARGUMENT;
+    if (d->B < 1 || d->T < 1 || d->H < 1 || d->H > kMaxHeads) return WKV7_ERR_INVALID_ARGUMENT;
     const int64_t toks = (int64_t)d->B * d->T;
     if (toks > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
     if (toks * d->H * kN > kMaxElems) return WKV7_ERR_INVALID_ARGUMENT;

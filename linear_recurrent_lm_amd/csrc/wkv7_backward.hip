@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         if (ssp) {
             const int g = tid & 127;
             const int t = min(g >> 3, Lc - 1);
-            raw_load(ssp + (int64_t)(cc * kChunk + t) * ts + (g & 7) * 8, raw, 0);
+            raw_load(ssp + (int64_t)(cc * kChunk) * ts + row_off(t, ts, (g & 7) * 8), raw, 0);
         }
         // float4 tid of a 64x64 state: row tid / 16, column 4 (tid % 16)
         const int64_t so = ((u.ckpt + cc) * H + h) * (int64_t)(kN * kN) + tid * 4;
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 const uint4 v = *(const uint4 *)(s_GO + (tid >> 3) * 64 + c8);
                 void *gp = gi == 0 ? p.dv : gi == 1 ? p.dr : gi == 2 ? p.da : gi == 3 ? p.db
                          : gi == 4 ? p.dk : p.dw;
-                if (t < Lc) *(uint4 *)((uint16_t *)gp + base + (int64_t)(tc + t) * ts + c8) = v;
+                if (t < Lc) *(uint4 *)((uint16_t *)gp + base + (int64_t)tc * ts + row_off(t, ts, c8)) = v;
             }
             return;
         }
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * kq + r;
-                if (t < Lc) gst(p.dv, base + (int64_t)(tc + t) * ts + 16 * w4 + l16, pdv[r]);
+                if (t < Lc) gst(p.dv, base + (int64_t)tc * ts + row_off(t, ts, 16 * w4 + l16), pdv[r]);
             }
         }
         if (wave < Lc) {
@@ -325,13 +325,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = 0.f;
             }
-            if (sst == IW) decay_of<8>(x, p.logw);
             const bool keep = t < L;
-            const float f = sst == IW ? 1.f : 0.f;
+            if (sst == IW) {                    // uniform per wave: the clamp only on w
+                decay_of<8>(x, p.logw);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = keep ? x[e] : f;
-                x[e] = sst == IW ? fmaxf(v, kMinW) : v;
+                for (int e = 0; e < 8; ++e) x[e] = fmaxf(keep ? x[e] : 1.f, kMinW);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = keep ? x[e] : 0.f;
             }
             float *d = s_in + (sst * 16 + t) * LD + e0;
             *(float4 *)d = make_float4(x[0], x[1], x[2], x[3]);

@@ -232,7 +232,7 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
         for (int k = 0; k < 3; ++k) {
             const int g = sid + 256 * k;
             const int t = min((g >> 3) & 15, Lc - 1), e0 = (g & 7) * 8;
-            raw_load(sp[k] + (int64_t)(cc * kChunk + t) * ts + e0, raw, k);
+            raw_load(sp[k] + (int64_t)(cc * kChunk) * ts + row_off(t, ts, e0), raw, k);
         }
     };
     auto stage = [&](int cc, const Raw<TI, 3> &raw) {

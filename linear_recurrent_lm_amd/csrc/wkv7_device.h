@@ -65,6 +65,15 @@ __device__ inline Unit resolve_unit(const SegParams &p, int s) {
     return u;
 }
 
+// Offset t * ts + c of token t of a chunk (t < 16) in a [.., T, H, 64]
+// stream with row pitch ts = H * 64, in 32 bits: the API bounds H by 2^16,
+// so ts < 2^24 and one 24-bit multiply suffices (a 64-bit product per lane
+// takes three quarter-rate instructions). The chunk's own 64-bit offset is
+// added separately, from uniform values.
+__device__ __forceinline__ int32_t row_off(int t, int64_t ts, int c) {
+    return (int32_t)__umul24((unsigned)t, (unsigned)ts) + c;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float((uint32_t)h << 16);
 }

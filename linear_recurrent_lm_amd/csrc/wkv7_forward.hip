@@ -232,7 +232,7 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int t = 4 * kq + r;
-                        if (t < L) IO<TI>::st((TI *)p.y, base + (int64_t)(t0 + t) * ts + irow, d1r[r]);
+                        if (t < L) IO<TI>::st((TI *)p.y, base + (int64_t)t0 * ts + row_off(t, ts, irow), d1r[r]);
                     }
                 }
             }
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
         for (int k = 0; k < 4; ++k) {
             const int g = sid + 192 * k;
             const int t = min((g >> 3) & 15, Lc - 1), e0 = (g & 7) * 8;
-            raw_load(sp[k] + (int64_t)(cc * kChunk + t) * ts + e0, raw, k);
+            raw_load(sp[k] + (int64_t)(cc * kChunk) * ts + row_off(t, ts, e0), raw, k);
         }
     };
     auto stage = [&](int cc, const Raw<TI, 4> &raw) {

@@ -52,7 +52,7 @@ def test_forward_rejects_bad_descriptors():
     assert fwd(desc(dtype=-1)) == UNSUPPORTED
     assert fwd(desc(decay=2)) == UNSUPPORTED                    # neither multiplicative nor log
     assert fwd(desc(grad_f32=3)) == INVALID
-    for bad in (dict(B=0), dict(T=0), dict(H=0), dict(T=-5), dict(num_seqs=-1)):
+    for bad in (dict(B=0), dict(T=0), dict(H=0), dict(H=65537), dict(T=-5), dict(num_seqs=-1)):
         assert fwd(desc(**bad)) == INVALID, bad
     assert fwd(desc(B=1 << 20, T=1 << 12)) == INVALID          # B*T over int32
     assert fwd(desc(num_seqs=3)) == INVALID                     # tables missing
