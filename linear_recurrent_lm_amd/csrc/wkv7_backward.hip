@@ -242,13 +242,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
     float4 ckr, dsr, drr, wwr;                  // checkpoint S_0, dS_C, drhs, W of the chunk in flight
     const int sst = __builtin_amdgcn_readfirstlane(tid >> 7);
     const TI *ssp = sst < 7 && p.staged[sst] ? (const TI *)p.staged[sst] + base : nullptr;
-    auto issue = [&](int cc) {
+    // The loads of a chunk are issued in three groups, the inputs in the
+    // staging phase and the rest in P3 (waves 0-7) and P5 (waves 8-15), so
+    // that the vector-memory instructions of a chunk do not all queue in one
+    // phase.
+    auto issue_in = [&](int cc) {
         const int Lc = min(kChunk, u.len - cc * kChunk);
         if (ssp) {
             const int g = tid & 127;
             const int t = min(g >> 3, Lc - 1);
             raw_load(ssp + (int64_t)(cc * kChunk) * ts + row_off(t, ts, (g & 7) * 8), raw, 0);
         }
+    };
+    auto issue_st = [&](int cc) {
         // float4 tid of a 64x64 state: row tid / 16, column 4 (tid % 16)
         const int64_t so = ((u.ckpt + cc) * H + h) * (int64_t)(kN * kN) + tid * 4;
         ckr = *(const float4 *)(p.ckpt + so);
@@ -257,33 +263,38 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         if (wave < 4) drr = *(const float4 *)(p.ws_dr + ((u.ckpt + cc) * H + h) * (int64_t)(kChunk * kN) + tid * 4);
         if (wave == 14) wwr = *(const float4 *)(p.ws_w + ((u.ckpt + cc) * H + h) * (int64_t)(kChunk * kChunk) + lane * 4);
     };
-    issue(c_hi - 1);
+    issue_in(c_hi - 1);
+    issue_st(c_hi - 1);
 
-    // Gradient stores of a chunk are issued in the next chunk's staging phase,
-    // after its loads have been waited for: loads and stores share one
+    // Gradient stores of a chunk are issued during the next chunk, after its
+    // staging phase has waited for its loads: loads and stores share one
     // counter, so stores issued just before that wait would hold it until
     // they are acknowledged. 16-bit gradients are gathered in LDS (s_GO) and
-    // leave as 16-byte stores, 8 elements per lane; fp32 gradients are held in
-    // registers and stored per lane: waves 4-7 hold dv of tokens 4 kq + r at
-    // value column 16 (w & 3) + l16, every wave dr, da, db, dk, dw of token w
-    // at key column lane.
+    // leave as 16-byte stores, 8 elements per lane, from waves 8-15 in phase
+    // P3 (idle there, and before P4 rewrites s_GO); fp32 gradients are held
+    // in registers and stored per lane in the staging phase: waves 4-7 hold
+    // dv of tokens 4 kq + r at value column 16 (w & 3) + l16, every wave dr,
+    // da, db, dk, dw of token w at key column lane.
     const bool wide = !std::is_same<TI, float>::value && !p.grad_f32;
     uint16_t *s_GO = (uint16_t *)(sm + O_GO);
     float pdv[4] = {0.f, 0.f, 0.f, 0.f}, pg[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-    auto flush = [&](int cc) {
+    auto flush_wide = [&](int cc) {          // waves 8-15
         const int tc = cc * kChunk, Lc = min(kChunk, u.len - tc);
-        if (wide) {
-            if (wave < 12) {
-                // row tid / 8 of s_GO: gradient tid / 128 (uniform per wave), token (tid / 8) % 16
-                const int gi = __builtin_amdgcn_readfirstlane(tid >> 7);
-                const int t = (tid >> 3) & 15, c8 = (tid & 7) * 8;
-                const uint4 v = *(const uint4 *)(s_GO + (tid >> 3) * 64 + c8);
-                void *gp = gi == 0 ? p.dv : gi == 1 ? p.dr : gi == 2 ? p.da : gi == 3 ? p.db
-                         : gi == 4 ? p.dk : p.dw;
-                if (t < Lc) *(uint4 *)((uint16_t *)gp + base + (int64_t)tc * ts + row_off(t, ts, c8)) = v;
-            }
-            return;
-        }
+        // row r of s_GO is gradient r / 16 (uniform per wave), token r % 16;
+        // thread f = tid - 512 stores row f / 8 and, on waves 8-11, row 64 + f / 8
+        const int f = tid - 512, t = (f >> 3) & 15, c8 = (f & 7) * 8;
+        const int g0 = __builtin_amdgcn_readfirstlane(f >> 7);
+        auto one = [&](int gi, int row) {
+            const uint4 v = *(const uint4 *)(s_GO + row * 64 + c8);
+            void *gp = gi == 0 ? p.dv : gi == 1 ? p.dr : gi == 2 ? p.da : gi == 3 ? p.db
+                     : gi == 4 ? p.dk : p.dw;
+            if (t < Lc) *(uint4 *)((uint16_t *)gp + base + (int64_t)tc * ts + row_off(t, ts, c8)) = v;
+        };
+        one(g0, f >> 3);
+        if (wave < 12) one(4 + g0, 64 + (f >> 3));
+    };
+    auto flush_regs = [&](int cc) {
+        const int tc = cc * kChunk, Lc = min(kChunk, u.len - tc);
         if (wave >= 4 && wave < 8) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -314,8 +325,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         relane();
 
         // ---- P0: stage inputs (w clamped; identity tokens past the end), the
-        //      checkpoint S_0, dS_C, drhs and W; then prefetch the next chunk and
-        //      store the previous chunk's gradients
+        //      checkpoint S_0, dS_C, drhs and W; then prefetch the next chunk's
+        //      inputs (and store the previous chunk's fp32 gradients)
         if (sst < 7) {
             const int t = (tid >> 3) & 15, e0 = (tid & 7) * 8;
             float x[8];
@@ -342,8 +353,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         *(float4 *)(s_DS + (tid >> 4) * LD + (tid & 15) * 4) = dsr;
         if (wave < 4) *(float4 *)(s_DR + (tid >> 4) * LD + (tid & 15) * 4) = drr;
         if (wave == 14) *(float4 *)(s_M + MW * 256 + lane * 4) = wwr;
-        issue(max(c - 1, c_lo));
-        if (c < c_hi - 1) flush(c + 1);
+        issue_in(max(c - 1, c_lo));
+        if (!wide && c < c_hi - 1) flush_regs(c + 1);
         lds_barrier();
         relane();
 
@@ -531,7 +542,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         // ---- P3: waves 0-3: rhs = P_a + L_ak V, then X = W rhs (value rows
         //      16 w..) into LDS (W of the chunk was staged from the sweep's
         //      output); waves 4-7: dV partial = K^ dS_C^T + M_rk^T dY (value
-        //      rows 16 (w-4)..)
+        //      rows 16 (w-4)..); waves 8-15: the previous chunk's 16-bit
+        //      gradient stores. Then waves 0-7 issue their part of the next
+        //      chunk's loads of S_0, dS_C, drhs and W (waves 8-15 in P5).
         f32x4 dvp = {0.f, 0.f, 0.f, 0.f};           // waves 4-7
         if (wave < 4) {
             pa = mm_AtB<16>(pa, Mlak, 16, sV + 16 * w4, LD, l16, kq);
@@ -546,7 +559,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             const int i0 = 16 * w4;
             dvp = mm_AtBt<64>(dvp, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq);
             dvp = mm_TB(dvp, Mmrk, 16, sDY + i0, LD, l16, kq);
+        } else if (wide && c < c_hi - 1) {
+            flush_wide(c + 1);
         }
+        if (wave < 8) issue_st(max(c - 1, c_lo));
         lds_barrier();
         relane();
 
@@ -637,6 +653,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 #pragma unroll
                 for (int r = 0; r < 4; ++r) zo[(4 * kq + r) * LD + 16 * q] = z[r];
             }
+        } else if (wave >= 8) {
+            issue_st(max(c - 1, c_lo));
         }
         lds_barrier();
         relane();
@@ -885,7 +903,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
     }
     lds_barrier();
     relane();
-    flush(c_lo);
+    if (wide) {
+        if (wave >= 8) flush_wide(c_lo);
+    } else {
+        flush_regs(c_lo);
+    }
 }
 
 }  // namespace
