@@ -587,8 +587,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         };
 
         // ---- P4: waves 4-7 finish dV = partial + L_ak^T drhs (held for the
-        //      store); waves 0-3: dA^ = drhs S_0, waves 8-11: dB^ = X dS_C (key
-        //      columns 16 (w & 3)..); waves 12, 13, 14: dL_ab, dL_ak, dM_rb
+        //      store); waves 0-3: dA^ = drhs S_0 (key columns 16 (w & 3)..);
+        //      waves 12, 13, 14: dL_ab, dL_ak, dM_rb
         if (wave >= 4 && wave < 8) {
             const int i0 = 16 * w4;
 #pragma unroll
@@ -598,12 +598,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) gput(0, 4 * kq + r, i0 + l16, dvp[r], pdv[r]);
-        } else if (wave < 12) {
+        } else if (wave < 4) {
             const int jc = 16 * w4;
-            const bool isA = wave < 4;
             f32x4 g = {0.f, 0.f, 0.f, 0.f};
-            g = mm_AtB<64>(g, isA ? s_DR : s_X, LD, (isA ? s_S0 : s_DS) + jc, LD, l16, kq);
-            float *dst = s_G + (isA ? 0 : 2) * 16 * LD + jc + l16;
+            g = mm_AtB<64>(g, s_DR, LD, s_S0 + jc, LD, l16, kq);
+            float *dst = s_G + jc + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = g[r];
         } else if (wave == 12) {
@@ -618,7 +617,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 
         // ---- P5: pair-gradient products of the split-point tiles (waves 0-3):
         //      Z_A = dD B_rows and Z_B = dD^T A_rows of tiles 1, 2 (wave w:
-        //      Z_A1, Z_B1, Z_A2, Z_B2), all 64 columns; into s_Z (S_0 is consumed)
+        //      Z_A1, Z_B1, Z_A2, Z_B2), all 64 columns; into s_Z (S_0 is consumed).
+        //      Waves 8-11: dB^ = X dS_C; waves 8-15: their part of the next
+        //      chunk's loads
         if (wave < 4) {
             const int prod = wave;
             const int tile = prod >> 1;
@@ -654,6 +655,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 for (int r = 0; r < 4; ++r) zo[(4 * kq + r) * LD + 16 * q] = z[r];
             }
         } else if (wave >= 8) {
+            if (wave < 12) {          // dB^ = X dS_C (key columns 16 (w & 3)..)
+                const int jc = 16 * w4;
+                f32x4 g = {0.f, 0.f, 0.f, 0.f};
+                g = mm_AtB<64>(g, s_X, LD, s_DS + jc, LD, l16, kq);
+                float *dst = s_G + 2 * 16 * LD + jc + l16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = g[r];
+            }
             issue_st(max(c - 1, c_lo));
         }
         lds_barrier();
