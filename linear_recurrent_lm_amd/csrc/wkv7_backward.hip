@@ -358,12 +358,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         lds_barrier();
         relane();
 
-        // ---- P1: waves 0-7 but 2: per-column rows, one role per wave (lane =
-        //      key column j), each role reading its inputs before its first
-        //      store; waves 8-11: dR^ = dY S_0, waves 12-15: dK^ = V dS_C (key
-        //      columns 16 (w & 3)..). B^ (role 2) is not needed: it enters only
-        //      dX, which comes from the sweep.
-        if (wave < 8 && wave != 2) {
+        // ---- P1: waves 0-7: per-column rows, one role per wave (lane = key
+        //      column j), each role reading its inputs before its first store;
+        //      waves 8-11: dR^ = dY S_0, waves 12-15: dK^ = V dS_C (key columns
+        //      16 (w & 3)..). B^ is not needed (it enters only dX, which comes
+        //      from the sweep), so the b rows are split over roles 2 and 6, and
+        //      the k rows over roles 3 and 7.
+        if (wave < 8) {
             const int role = wave, j = lane;
             const int st = role == 0 || role == 4 ? IA : role == 1 || role == 5 ? IR
                          : role == 2 || role == 6 ? IB : IK;
@@ -386,7 +387,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 for (int t = 0; t < 16; ++t) { g *= wv[t]; xv[t] *= g; }
 #pragma unroll
                 for (int t = 0; t < 16; ++t) s_Q[(16 + t) * LD + j] = xv[t];
-            } else if (role == 3) {      // K^_s = k_s D_{15,s}
+            } else if (role == 3) {      // K^_s = k_s D_{15,s}; k_s / F_s
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // 1 / F_s from one reciprocal of the sub-chunk's product
+                    // F_{4q+3}, then 1 / F_{s-1} = w_s / F_s going down
+                    const float Fq = (wv[4 * q] * wv[4 * q + 1]) * (wv[4 * q + 2] * wv[4 * q + 3]);
+                    float inv = __builtin_amdgcn_rcpf(Fq);
+#pragma unroll
+                    for (int e = 3; e >= 0; --e) {
+                        s_KD[(4 * q + e) * LD + j] = xv[4 * q + e] * inv;
+                        inv *= wv[4 * q + e];
+                    }
+                }
                 float d = 1.f;
 #pragma unroll
                 for (int s = 15; s >= 0; --s) { xv[s] *= d; d *= wv[s]; }
@@ -410,8 +423,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 for (int t = 0; t < 16; ++t) s_AR[(16 * inc + t) * LD + j] = xv[t];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) s_AWR[(4 * inc + e) * LD + j] = xv[12 + e] * W2;
-            } else {                     // b (6), k (7) rows: x_s / F_s and scaled to the split points
-                const int ko = role - 6;
+            } else {
+                // b rows x_s / F_s (role 2) and scaled to the split points
+                // (role 6; B^ itself is not needed); k rows scaled to the
+                // split points (role 7; k_s / F_s comes from role 3)
+                const int ko = role == 7 ? 1 : 0;
+                const bool rows_d = role == 2, rows_l = role != 2;
                 float od[16], os[12];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -430,16 +447,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                         inv *= wv[4 * q + e];
                     }
                 }
-                const float W1 = (wv[4] * wv[5]) * (wv[6] * wv[7]);
-                float *dd = ko ? s_KD : s_BD;
+                if (rows_d) {
+                    float *dd = ko ? s_KD : s_BD;
 #pragma unroll
-                for (int s = 0; s < 16; ++s) dd[s * LD + j] = od[s];
+                    for (int s = 0; s < 16; ++s) dd[s * LD + j] = od[s];
+                }
+                if (rows_l) {
+                    const float W1 = (wv[4] * wv[5]) * (wv[6] * wv[7]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    s_BL[(8 * ko + e) * LD + j] = os[e] * W1;          // s = e scaled to 8
-                    s_BL[(16 + 4 * ko + e) * LD + j] = os[e];          // s = e scaled to 4
-                    s_BL[(8 * ko + 4 + e) * LD + j] = os[4 + e];       // s = 4+e scaled to 8
-                    s_BL[(24 + 4 * ko + e) * LD + j] = os[8 + e];      // s = 8+e scaled to 12
+                    for (int e = 0; e < 4; ++e) {
+                        s_BL[(8 * ko + e) * LD + j] = os[e] * W1;          // s = e scaled to 8
+                        s_BL[(16 + 4 * ko + e) * LD + j] = os[e];          // s = e scaled to 4
+                        s_BL[(8 * ko + 4 + e) * LD + j] = os[4 + e];       // s = 4+e scaled to 8
+                        s_BL[(24 + 4 * ko + e) * LD + j] = os[8 + e];      // s = 8+e scaled to 12
+                    }
                 }
             }
         } else {
