@@ -120,7 +120,7 @@ def _time_ms(fn, warmup, steps, ev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the kernels run on one GPU (units shard across GPUs without communication, which is not implemented here); --gpus must be 1"}))
         sys.exit(2)
     import torch
     from linear_recurrent_lm_amd import synth
