@@ -64,7 +64,7 @@ def _check(inp, out, f, g, ytol, stol, gtol):
     assert U.unit_err_state(gh["ds0"], g["ds0"]) <= gtol
 
 
-@pytest.mark.parametrize("T", [1, 17, 40, 100])
+@pytest.mark.parametrize("T", [1, 17, 40, 100, 273])
 def test_f16_forward_backward(W, T):
     inp = synth.make_inputs(2, T, 3, 64, seed=400 + T, dtype="f16", s0_std=0.1, with_dy=True,
                             ds_out_std=0.1)
@@ -88,11 +88,12 @@ def test_log_decay_forward_backward(W, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_f32_gradients_for_16bit_inputs(W, dtype):
+@pytest.mark.parametrize("T", [50, 273])
+def test_f32_gradients_for_16bit_inputs(W, dtype, T):
     """fp32 gradients of bf16/fp16 inputs: only the fp32 compute error remains,
     so they are held to the fp32 gradient bound."""
     import torch
-    inp = synth.make_inputs(2, 50, 3, 64, seed=420, dtype=dtype, s0_std=0.1, with_dy=True,
+    inp = synth.make_inputs(2, T, 3, 64, seed=420 + T, dtype=dtype, s0_std=0.1, with_dy=True,
                             ds_out_std=0.1)
     out = _run(W, inp, grad_f32=True)
     assert all(out[4][n].dtype == torch.float32 for n in NAMES)
