@@ -179,3 +179,26 @@ def decode_step(r, w, k, v, a, b, s_in):
     streams = [np.asarray(x).reshape(B, 1, H, N) for x in (r, w, k, v, a, b)]
     out = forward(*streams, s0=s_in)
     return out["y"].reshape(B, H, N), out["s_out"]
+
+
+def decode_step_fused(r, w, k, v, a, b, s_in, g, ln_w, ln_b, r_k, eps):
+    """One decode step followed by the per-head output epilogue that the
+    rwkv-lab page ("RWKV community research additions") fuses into its
+    one-token kernel: GroupNorm, the RWKV bonus and output gating. The
+    rwkv-metal page ("What's inside") names ln_x a GroupNorm per head. The
+    pages print no formula; the reading taken, per (sequence, head) h with
+    population mean and variance over the head's N values of y:
+
+        yn_i  = (y_i - mean(y)) / sqrt(var(y) + eps) * ln_w[h, i] + ln_b[h, i]
+        out_i = (yn_i + (sum_j r_j k_j r_k[h, j]) * v_i) * g_i
+
+    Streams and g [B, H, N]; ln_w, ln_b, r_k [H, N]; state [B, H, N, N].
+    Returns (out, y, s_out), all fp64."""
+    y, s_out = decode_step(r, w, k, v, a, b, s_in)
+    y = np.asarray(y, dtype=np.float64)
+    mean = y.mean(axis=-1, keepdims=True)
+    var = ((y - mean) ** 2).mean(axis=-1, keepdims=True)
+    yn = (y - mean) / np.sqrt(var + float(eps)) * _d(ln_w)[None] + _d(ln_b)[None]
+    bonus = (_d(r) * _d(k) * _d(r_k)[None]).sum(axis=-1, keepdims=True)
+    out = (yn + bonus * _d(v)) * _d(g)
+    return out, y, s_out

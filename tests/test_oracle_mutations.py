@@ -72,3 +72,45 @@ def test_mutation_is_caught(mutation, tmp_path):
 
 def test_unmutated_oracle_passes_all_pins():
     assert _all_pins_pass() == []
+
+
+# Slips in the fused decode epilogue (oracle.decode_step_fused, fp64 numpy):
+# each is a full restatement of the epilogue with one mistake, checked
+# against the p13 pins.
+def _epilogue(mut):
+    import numpy as np
+
+    def f(r, w, k, v, a, b, s_in, g, ln_w, ln_b, r_k, eps):
+        y, s_out = O.decode_step(r, w, k, v, a, b, s_in)
+        y = np.asarray(y, dtype=np.float64)
+        n = y.shape[-1]
+        mean = y.mean(axis=-1, keepdims=True)
+        var = ((y - mean) ** 2).sum(axis=-1, keepdims=True) / (n - 1 if mut == "sample_variance" else n)
+        den = np.sqrt(var) + eps if mut == "eps_outside_sqrt" else np.sqrt(var + eps)
+        yn = (y - mean) / den * ln_w[None] + ln_b[None]
+        rk = {"bonus_without_r_k": np.ones_like(r_k), "r_k_of_other_head": r_k[::-1]}.get(mut, r_k)
+        bonus = (r * k * rk[None]).sum(axis=-1, keepdims=True)
+        if mut == "gate_before_bonus":
+            return yn * g + bonus * v, y, s_out
+        if mut == "bias_after_gate":
+            return (yn - ln_b[None] + bonus * v) * g + ln_b[None], y, s_out
+        if mut == "bonus_scales_r":
+            return (yn + bonus * r) * g, y, s_out
+        return (yn + bonus * v) * g, y, s_out
+    return f
+
+
+EPILOGUE_SLIPS = ["sample_variance", "eps_outside_sqrt", "bonus_without_r_k", "r_k_of_other_head",
+                  "gate_before_bonus", "bias_after_gate", "bonus_scales_r"]
+
+
+@pytest.mark.parametrize("mutation", EPILOGUE_SLIPS)
+def test_epilogue_slip_is_caught(mutation, monkeypatch):
+    monkeypatch.setattr(O, "decode_step_fused", _epilogue(mutation))
+    failed = [n for n, (fn, tol) in P.PINS.items() if n.startswith("p13") and not fn() <= tol]
+    assert failed, f"no pin detects epilogue slip {mutation}"
+
+
+def test_epilogue_restatement_passes_pins(monkeypatch):
+    monkeypatch.setattr(O, "decode_step_fused", _epilogue("none"))
+    assert [n for n, (fn, tol) in P.PINS.items() if n.startswith("p13") and not fn() <= tol] == []

@@ -286,6 +286,99 @@ def pin_p12(seed=13, T=6, N=5, eps=1e-6):
     return worst
 
 
+# ------------------------------------------- fused decode epilogue (reading)
+
+def _fused_inputs(seed, B=3, H=2, N=16):
+    (r, w, k, v, a, b), s0 = rand_inputs(B, 1, H, N, seed, s0_std=0.3)
+    r, w, k, v, a, b = (x[:, 0] for x in (r, w, k, v, a, b))
+    rng = np.random.default_rng(seed)
+    g = rng.normal(size=r.shape)
+    ln_w = rng.normal(size=(H, N)); ln_b = rng.normal(size=(H, N)); r_k = rng.normal(size=(H, N))
+    return [r, w, k, v, a, b], s0, g, ln_w, ln_b, r_k
+
+
+def _y_equals_v(r, w, k, v, a, b, s0):
+    """Inputs whose decode output is exactly v: zero state, a = b = 0 and
+    r = k / |k|^2 give y = v (k . r) = v."""
+    k = k.copy()
+    r = k / np.sum(k * k, axis=-1, keepdims=True)
+    return [r, w, k, v, np.zeros_like(a), np.zeros_like(b)], np.zeros_like(s0)
+
+
+def pin_p13_normalised(seed=31):
+    """eps = 0, unit affine, no bonus, g = 1: each head's output has mean 0
+    and population variance 1."""
+    st, s0, g, ln_w, ln_b, r_k = _fused_inputs(seed)
+    out, _, _ = O.decode_step_fused(*st, s0, np.ones_like(g), np.ones_like(ln_w),
+                                    np.zeros_like(ln_b), np.zeros_like(r_k), 0.0)
+    return max(float(np.max(np.abs(out.mean(axis=-1)))),
+               float(np.max(np.abs((out ** 2).mean(axis=-1) - 1.0))))
+
+
+def pin_p13_affine_invariance(seed=32):
+    """eps = 0, no bonus: replacing y by alpha y + beta (alpha > 0) leaves the
+    output unchanged (y = v by construction)."""
+    st, s0, g, ln_w, ln_b, r_k = _fused_inputs(seed)
+    st, s0 = _y_equals_v(*st, s0)
+    z = np.zeros_like(r_k)
+    out1, _, _ = O.decode_step_fused(*st, s0, g, ln_w, ln_b, z, 0.0)
+    st2 = list(st); st2[3] = 2.5 * st[3] - 0.7
+    out2, _, _ = O.decode_step_fused(*st2, s0, g, ln_w, ln_b, z, 0.0)
+    return rel(out2, out1)
+
+
+def pin_p13_eps_closed_form(seed=33, eps=0.37):
+    """y = alternating +-1 per head (mean 0, variance 1), unit affine, no bonus,
+    g = 1: out = y / sqrt(1 + eps)."""
+    st, s0, g, ln_w, ln_b, r_k = _fused_inputs(seed)
+    st, s0 = _y_equals_v(*st, s0)
+    N = st[3].shape[-1]
+    st[3] = np.broadcast_to(np.where(np.arange(N) % 2 == 0, 1.0, -1.0), st[3].shape).copy()
+    out, _, _ = O.decode_step_fused(*st, s0, np.ones_like(g), np.ones_like(ln_w),
+                                    np.zeros_like(ln_b), np.zeros_like(r_k), eps)
+    return rel(out, st[3] / np.sqrt(1.0 + eps))
+
+
+def pin_p13_bonus_dot(seed=34):
+    """Zero affine, r_k = 1, g = 1: out = (r . k) v, the dot product by numpy."""
+    st, s0, g, ln_w, ln_b, r_k = _fused_inputs(seed)
+    out, _, _ = O.decode_step_fused(*st, s0, np.ones_like(g), np.zeros_like(ln_w),
+                                    np.zeros_like(ln_b), np.ones_like(r_k), 1e-5)
+    r, k, v = st[0], st[2], st[3]
+    dots = np.array([[np.dot(r[bb, h], k[bb, h]) for h in range(r.shape[1])] for bb in range(r.shape[0])])
+    return rel(out, dots[..., None] * v)
+
+
+def pin_p13_bonus_locality(seed=37):
+    """Zero affine, g = 1, r_k nonzero on head 0 only: the other heads output
+    zero, and head 0's output is homogeneous of degree 1 in r_k."""
+    st, s0, g, ln_w, ln_b, r_k = _fused_inputs(seed)
+    r_k[1:] = 0.0
+    z, one = np.zeros_like(ln_w), np.ones_like(g)
+    out1, _, _ = O.decode_step_fused(*st, s0, one, z, z, r_k, 1e-5)
+    out2, _, _ = O.decode_step_fused(*st, s0, one, z, z, 2.0 * r_k, 1e-5)
+    return max(float(np.max(np.abs(out1[:, 1:]))), rel(out2, 2.0 * out1))
+
+
+def pin_p13_gate_and_bias(seed=35):
+    """The gate scales the whole output elementwise, and a bias shift delta
+    moves the output by delta * g."""
+    st, s0, g, ln_w, ln_b, r_k = _fused_inputs(seed)
+    out_g, _, _ = O.decode_step_fused(*st, s0, g, ln_w, ln_b, r_k, 1e-3)
+    out_1, _, _ = O.decode_step_fused(*st, s0, np.ones_like(g), ln_w, ln_b, r_k, 1e-3)
+    delta = np.linspace(-1.0, 1.0, ln_b.size).reshape(ln_b.shape)
+    out_d, _, _ = O.decode_step_fused(*st, s0, g, ln_w, ln_b + delta, r_k, 1e-3)
+    return max(rel(out_g, out_1 * g), rel(out_d - out_g, delta[None] * g))
+
+
+def pin_p13_state_unchanged(seed=36):
+    """y and the new state are the plain decode step's."""
+    st, s0, g, ln_w, ln_b, r_k = _fused_inputs(seed)
+    _, y, s1 = O.decode_step_fused(*st, s0, g, ln_w, ln_b, r_k, 1e-5)
+    y_ref, s_ref = O.decode_step(*st, s0)
+    return max(rel(y, y_ref), rel(s1, s_ref))
+
+
 PINS = {
     "p1_cumulative": (pin_p1, 1e-12),
     "p2_w0_last_outer": (pin_p2, 1e-12),
@@ -300,6 +393,13 @@ PINS = {
     "p10_linearity": (pin_p10, 1e-12),
     "p11_gradient_identities": (pin_p11, 1e-10),
     "p12_finite_differences": (pin_p12, 1e-6),
+    "p13_fused_normalised": (pin_p13_normalised, 1e-12),
+    "p13_fused_affine_invariance": (pin_p13_affine_invariance, 1e-12),
+    "p13_fused_eps_closed_form": (pin_p13_eps_closed_form, 1e-12),
+    "p13_fused_bonus_dot": (pin_p13_bonus_dot, 1e-12),
+    "p13_fused_gate_and_bias": (pin_p13_gate_and_bias, 1e-12),
+    "p13_fused_bonus_locality": (pin_p13_bonus_locality, 1e-12),
+    "p13_fused_state_unchanged": (pin_p13_state_unchanged, 0.0),
 }
 
 
