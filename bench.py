@@ -223,6 +223,46 @@ def main():
                       args.warmup, args.steps, ev)
     dec_bytes = 512 * H * (2 * N * N * 4 + 7 * N * 2)
 
+    # Fused decode: the same step carried through the per-head GroupNorm, the
+    # bonus and the output gate (gate in, out instead of y).
+    frng = np.random.Generator(np.random.PCG64(5004))
+    fg = torch.from_numpy(synth.round_to(frng.uniform(0.0, 2.0, (512, H, N)).astype(np.float32),
+                                         "bf16")).to(dev).to(torch.bfloat16)
+    fln_w = torch.from_numpy((1.0 + 0.3 * frng.standard_normal((H, N))).astype(np.float32)).to(dev)
+    fln_b = torch.from_numpy((0.2 * frng.standard_normal((H, N))).astype(np.float32)).to(dev)
+    frk = torch.from_numpy((0.5 * frng.standard_normal((H, N))).astype(np.float32)).to(dev)
+    fout = torch.empty_like(dts[0])
+    fdec_ms = _time_ms(lambda: W.wkv7_decode_step_fused(*dts, ds_in, fg, fln_w, fln_b, frk, 64e-5,
+                                                         s_out=ds_out, out=fout),
+                       args.warmup, args.steps, ev)
+    fdec_bytes = 512 * H * (2 * N * N * 4 + 8 * N * 2)
+
+    # Launch cost of a decode loop: K fused steps at B=1, H=32 (state in place),
+    # launched one by one, then replayed from one captured graph.
+    K = 64
+    sinp = synth.make_inputs(1, K, H, N, seed=6, dtype="bf16")
+    lsteps = [[torch.from_numpy(np.ascontiguousarray(x[:, t])).to(dev).to(torch.bfloat16)
+               for x in sinp.streams()] for t in range(K)]
+    lstate = torch.zeros((1, H, N, N), device=dev, dtype=torch.float32)
+    lg = torch.ones((1, H, N), device=dev, dtype=torch.bfloat16)
+    louts = [torch.empty((1, H, N), device=dev, dtype=torch.bfloat16) for _ in range(K)]
+
+    def decode_loop():
+        for t in range(K):
+            W.wkv7_decode_step_fused(*lsteps[t], lstate, lg, fln_w, fln_b, frk, 64e-5,
+                                     s_out=lstate, out=louts[t])
+
+    loop_eager_ms = _time_ms(decode_loop, args.warmup, args.steps, ev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        decode_loop()
+    torch.cuda.current_stream().wait_stream(side)
+    loop_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(loop_graph):
+        decode_loop()
+    loop_graph_ms = _time_ms(loop_graph.replay, args.warmup, args.steps, ev)
+
     # I/O variants: the prefill workload drawn in fp16; the training step with
     # w given as log(decay) and fp32 gradients.
     fin = synth.make_inputs(16, 1024, H, N, seed=2, dtype="f16", s0_std=0.1)
@@ -294,6 +334,15 @@ def main():
                           "us": dec_ms * 1e3, "sequence_steps_per_s": 512 / (dec_ms * 1e-3),
                           "GB_per_s": dec_bytes / (dec_ms * 1e-3) / 1e9,
                           "hbm_frac": dec_bytes / (dec_ms * 1e-3) / PEAK_HBM}
+    out["decode_step_fused"] = {
+        "workload": "bf16 B=512 T=1 H=32, fp32 state in and out, then per-head GroupNorm, bonus and gate",
+        "us": fdec_ms * 1e3, "sequence_steps_per_s": 512 / (fdec_ms * 1e-3),
+        "GB_per_s": fdec_bytes / (fdec_ms * 1e-3) / 1e9,
+        "hbm_frac": fdec_bytes / (fdec_ms * 1e-3) / PEAK_HBM}
+    out["decode_loop_b1"] = {
+        "workload": "bf16 B=1 H=32, %d fused steps with the state in place" % K,
+        "us_per_step_launched": loop_eager_ms * 1e3 / K,
+        "us_per_step_graph_replay": loop_graph_ms * 1e3 / K}
     out["variants"] = {
         "prefill_forward_f16": {"workload": "fp16 B=16 T=1024 H=32, initial state N(0,0.1^2)",
                                 "ms": f16_ms, "tokens_per_s": 16 * 1024 / (f16_ms * 1e-3),

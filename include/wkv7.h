@@ -170,6 +170,32 @@ wkv7_status wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, int
                              const void *v, const void *a, const void *b,
                              const float *s_in, float *s_out, void *y, void *stream);
 
+/*
+ * One decode step fused with the per-head output epilogue: the rwkv-lab page
+ * ("RWKV community research additions") describes a one-token kernel that
+ * carries the fp32 state update through GroupNorm, the RWKV bonus and output
+ * gating, and the rwkv-metal page ("What's inside") names ln_x a GroupNorm per
+ * head. The pages print no formula; the reading taken, per (sequence, head h),
+ * with y the plain step's output and mean / var the population mean and
+ * variance of its N values:
+ *   yn_i  = (y_i - mean(y)) / sqrt(var(y) + eps) * ln_w[h][i] + ln_b[h][i]
+ *   out_i = (yn_i + (sum_j r_j k_j r_k[h][j]) * v_i) * g_i
+ * Arguments as wkv7_decode_step, and:
+ *   g          : [B,H,N] output gate (dtype); required.
+ *   ln_w, ln_b : [H,N] fp32 GroupNorm affine; required.
+ *   r_k        : [H,N] fp32 bonus weights; required.
+ *   eps        : finite, >= 0 (else WKV7_ERR_INVALID_ARGUMENT).
+ *   out        : [B,H,N] output (dtype); required.
+ *   y          : [B,H,N] the plain step's y (dtype), or NULL to skip it.
+ * The state is updated exactly as by wkv7_decode_step. All pointers 16-byte
+ * aligned.
+ */
+wkv7_status wkv7_decode_step_fused(int32_t B, int32_t H, int32_t N, int32_t dtype, int32_t decay,
+                                   const void *r, const void *w, const void *k, const void *v,
+                                   const void *a, const void *b, const float *s_in, float *s_out,
+                                   const void *g, const float *ln_w, const float *ln_b,
+                                   const float *r_k, float eps, void *out, void *y, void *stream);
+
 /* Number of checkpoint slots a dense forward needs: B * ceil(T / 16). */
 wkv7_status wkv7_checkpoint_slots(int32_t B, int32_t T, int64_t *slots);
 

@@ -1,6 +1,7 @@
 // Host side of libwkv7.so: the C ABI declared in include/wkv7.h.
 // Every argument is checked before anything touches the HIP runtime, so the
 // validation paths work (and are tested) on machines without a GPU.
+#include <cmath>
 #include <atomic>
 #include <cstring>
 
@@ -225,29 +226,59 @@ wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, cons
     return WKV7_OK;
 }
 
+static wkv7_status decode_impl(int32_t B, int32_t H, int32_t N, int32_t dtype, int32_t decay,
+                               const void *r, const void *w, const void *k, const void *v,
+                               const void *a, const void *b, const float *s_in, float *s_out,
+                               void *y, const void *g, const float *ln_w, const float *ln_b,
+                               const float *r_k, float eps, void *out, void *stream) {
+    const bool fused = out != nullptr;
+    if (N != kN) return WKV7_ERR_UNSUPPORTED;
+    if (!dtype_ok(dtype)) return WKV7_ERR_UNSUPPORTED;
+    if (decay != WKV7_DECAY_MULT && decay != WKV7_DECAY_LOG) return WKV7_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || (int64_t)B * H > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
+    const void *streams[9] = {r, w, k, v, a, b, fused ? out : y, s_in, s_out};
+    wkv7_status st = check_streams(streams, 9);
+    if (st != WKV7_OK) return st;
+    if (fused) {
+        const void *params[4] = {g, ln_w, ln_b, r_k};
+        if ((st = check_streams(params, 4)) != WKV7_OK) return st;
+        if (y && !aligned16(y)) return WKV7_ERR_INVALID_ARGUMENT;
+        if (!(eps >= 0.f) || !std::isfinite(eps)) return WKV7_ERR_INVALID_ARGUMENT;
+    }
+    const size_t state_bytes = (size_t)B * H * kN * kN * sizeof(float);
+    if (s_in != s_out && ranges_overlap(s_in, state_bytes, s_out, state_bytes))
+        return WKV7_ERR_INVALID_ARGUMENT;
+    if ((st = check_device()) != WKV7_OK) return st;
+    wkv7::DecArgs args{};
+    args.B = B; args.H = H; args.dtype = dtype;
+    args.logw = decay == WKV7_DECAY_LOG;
+    args.r = r; args.w = w; args.k = k; args.v = v; args.a = a; args.b = b;
+    args.s_in = s_in; args.s_out = s_out; args.y = y;
+    if (fused) {
+        args.g = g; args.ln_w = ln_w; args.ln_b = ln_b; args.r_k = r_k;
+        args.eps = eps; args.out = out;
+    }
+    if (wkv7::launch_decode(args, (hipStream_t)stream) != hipSuccess) return WKV7_ERR_HIP;
+    return WKV7_OK;
+}
+
 wkv7_status wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, int32_t decay,
                              const void *r,
                              const void *w, const void *k, const void *v, const void *a,
                              const void *b, const float *s_in, float *s_out, void *y,
                              void *stream) {
-    if (N != kN) return WKV7_ERR_UNSUPPORTED;
-    if (!dtype_ok(dtype)) return WKV7_ERR_UNSUPPORTED;
-    if (decay != WKV7_DECAY_MULT && decay != WKV7_DECAY_LOG) return WKV7_ERR_UNSUPPORTED;
-    if (B < 1 || H < 1 || (int64_t)B * H > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
-    const void *streams[9] = {r, w, k, v, a, b, y, s_in, s_out};
-    wkv7_status st = check_streams(streams, 9);
-    if (st != WKV7_OK) return st;
-    const size_t state_bytes = (size_t)B * H * kN * kN * sizeof(float);
-    if (s_in != s_out && ranges_overlap(s_in, state_bytes, s_out, state_bytes))
-        return WKV7_ERR_INVALID_ARGUMENT;
-    if ((st = check_device()) != WKV7_OK) return st;
-    wkv7::DecArgs args;
-    args.B = B; args.H = H; args.dtype = dtype;
-    args.logw = decay == WKV7_DECAY_LOG;
-    args.r = r; args.w = w; args.k = k; args.v = v; args.a = a; args.b = b;
-    args.s_in = s_in; args.s_out = s_out; args.y = y;
-    if (wkv7::launch_decode(args, (hipStream_t)stream) != hipSuccess) return WKV7_ERR_HIP;
-    return WKV7_OK;
+    return decode_impl(B, H, N, dtype, decay, r, w, k, v, a, b, s_in, s_out, y,
+                       nullptr, nullptr, nullptr, nullptr, 0.f, nullptr, stream);
+}
+
+wkv7_status wkv7_decode_step_fused(int32_t B, int32_t H, int32_t N, int32_t dtype, int32_t decay,
+                                   const void *r, const void *w, const void *k, const void *v,
+                                   const void *a, const void *b, const float *s_in, float *s_out,
+                                   const void *g, const float *ln_w, const float *ln_b,
+                                   const float *r_k, float eps, void *out, void *y, void *stream) {
+    if (!out) return WKV7_ERR_INVALID_ARGUMENT;
+    return decode_impl(B, H, N, dtype, decay, r, w, k, v, a, b, s_in, s_out, y,
+                       g, ln_w, ln_b, r_k, eps, out, stream);
 }
 
 }  // extern "C"

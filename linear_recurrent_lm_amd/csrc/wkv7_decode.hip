@@ -9,6 +9,17 @@
 // instruction of the workgroup covers 4 KiB of contiguous memory. Thread tid
 // then owns rows m*16 + tid/16 and columns 4*(tid%16) .. +3; the row sums
 // S a and S r reduce over the 16 lanes sharing a row (one DPP row).
+//
+// The fused variant carries y through the per-head output epilogue (the
+// rwkv-lab page, "RWKV community research additions": one kernel for the
+// state update, GroupNorm, the RWKV bonus and output gating; the rwkv-metal
+// page, "What's inside": ln_x is a GroupNorm per head):
+//     yn_i  = (y_i - mean(y)) / sqrt(var(y) + eps) * ln_w[h][i] + ln_b[h][i]
+//     out_i = (yn_i + (sum_j r_j k_j r_k[h][j]) v_i) * g_i
+// with the population mean and variance of the head's 64 values, formed in
+// two passes (sums over a wave's rows by lane exchange, then over the four
+// waves through LDS). The bonus sum runs over the key columns, which every
+// 16-lane row group already spans.
 #include "wkv7_kernels.h"
 
 namespace wkv7 {
@@ -28,7 +39,7 @@ __device__ __forceinline__ void ld4(const TI *p, int64_t o, float *x) {
     for (int e = 0; e < 4; ++e) x[e] = IO<TI>::ld(p, o + e);
 }
 
-template <typename TI>
+template <typename TI, bool FUSED>
 __global__ __launch_bounds__(256) void decode_kernel(DecArgs p) {
     const int64_t unit = blockIdx.x;
     const int tid = threadIdx.x;
@@ -67,9 +78,48 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs p) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
         __builtin_nontemporal_store(S[m], (f32x4 *)(p.s_out + sb) + m * 256 + tid);
-    if ((tid & 15) == 0) {
+    if (!FUSED || p.y) {
+        if ((tid & 15) == 0) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) IO<TI>::st((TI *)p.y, vb + m * 16 + rl, yv[m]);
+            for (int m = 0; m < 4; ++m) IO<TI>::st((TI *)p.y, vb + m * 16 + rl, yv[m]);
+        }
+    }
+    if constexpr (FUSED) {
+        __shared__ float red[8];
+        const int h = (int)(unit % p.H), wq = tid >> 6;
+        // a wave's 16 rows: its 4 row groups (lanes l, l^16, l^32, l^48) x 4 rows
+        float ps = (yv[0] + yv[1]) + (yv[2] + yv[3]);
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        if ((tid & 63) == 0) red[wq] = ps;
+        __syncthreads();
+        const float mean = ((red[0] + red[1]) + (red[2] + red[3])) * (1.f / kN);
+        float d[4], pq = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            d[m] = yv[m] - mean;
+            pq = fmaf(d[m], d[m], pq);
+        }
+        pq += __shfl_xor(pq, 16);
+        pq += __shfl_xor(pq, 32);
+        if ((tid & 63) == 0) red[4 + wq] = pq;
+        __syncthreads();
+        const float var = ((red[4] + red[5]) + (red[6] + red[7])) * (1.f / kN);
+        const float inv = 1.f / sqrtf(var + p.eps);
+        const float *rk = p.r_k + (int64_t)h * kN + c0;
+        float bz = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bz = fmaf(r[e] * k[e], rk[e], bz);
+        bz = sum16(bz);
+        if ((tid & 15) == 0) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int i = m * 16 + rl;
+                const float yn = fmaf(d[m] * inv, p.ln_w[(int64_t)h * kN + i], p.ln_b[(int64_t)h * kN + i]);
+                const float gi = IO<TI>::ld((const TI *)p.g, vb + i);
+                IO<TI>::st((TI *)p.out, vb + i, fmaf(bz, vv[m], yn) * gi);
+            }
+        }
     }
 }
 
@@ -77,12 +127,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs p) {
 
 hipError_t launch_decode(const DecArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)a.B * a.H));
-    if (a.dtype == 1)
-        hipLaunchKernelGGL(decode_kernel<uint16_t>, grid, dim3(256), 0, stream, a);
-    else if (a.dtype == 2)
-        hipLaunchKernelGGL(decode_kernel<_Float16>, grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL(decode_kernel<float>, grid, dim3(256), 0, stream, a);
+    const bool fused = a.out != nullptr;
+    if (a.dtype == 1) {
+        if (fused) hipLaunchKernelGGL((decode_kernel<uint16_t, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((decode_kernel<uint16_t, false>), grid, dim3(256), 0, stream, a);
+    } else if (a.dtype == 2) {
+        if (fused) hipLaunchKernelGGL((decode_kernel<_Float16, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((decode_kernel<_Float16, false>), grid, dim3(256), 0, stream, a);
+    } else {
+        if (fused) hipLaunchKernelGGL((decode_kernel<float, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((decode_kernel<float, false>), grid, dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

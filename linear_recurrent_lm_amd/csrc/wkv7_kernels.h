@@ -43,7 +43,14 @@ struct DecArgs {
     const void *r, *w, *k, *v, *a, *b;
     const float *s_in;
     float *s_out;
-    void *y;
+    void *y;                        // plain step: required; fused step: optional
+    // fused output epilogue (out != nullptr): per-head GroupNorm of y with the
+    // affine ln_w, ln_b ([H][N] fp32), plus the bonus (sum_j r_j k_j r_k[h][j]) v,
+    // times the gate g ([B][H][N], I/O type)
+    const void *g;
+    const float *ln_w, *ln_b, *r_k;
+    float eps;
+    void *out;
 };
 
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);

@@ -65,13 +65,16 @@ def lib():
         L.wkv7_forward.argtypes = [dptr] + [vp] * 11
         L.wkv7_backward.argtypes = [dptr] + [vp] * 16 + [vp, sz, vp]
         L.wkv7_decode_step.argtypes = [i32, i32, i32, i32, i32] + [vp] * 10
+        L.wkv7_decode_step_fused.argtypes = ([i32, i32, i32, i32, i32] + [vp] * 12
+                                             + [ctypes.c_float, vp, vp, vp])
         L.wkv7_checkpoint_slots.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int64)]
         L.wkv7_workspace_bytes.argtypes = [dptr, ctypes.POINTER(ctypes.c_size_t)]
         L.wkv7_segments_check.argtypes = [i32, i32, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
         L.wkv7_status_string.argtypes = [i32]
         L.wkv7_status_string.restype = ctypes.c_char_p
         L.wkv7_abi_version.restype = i32
-        for fn in ("wkv7_forward", "wkv7_backward", "wkv7_decode_step", "wkv7_checkpoint_slots",
+        for fn in ("wkv7_forward", "wkv7_backward", "wkv7_decode_step", "wkv7_decode_step_fused",
+                   "wkv7_checkpoint_slots",
                    "wkv7_workspace_bytes", "wkv7_segments_check"):
             getattr(L, fn).restype = i32
         _lib = L
@@ -266,6 +269,38 @@ def wkv7_decode_step(r, w, k, v, a, b, s_in, s_out=None, y=None, *, decay: str =
         B, H, n, _dtype_code(r), _decay(decay), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(s_in),
         _ptr(s_out), _ptr(y), _stream()))
     return y, s_out
+
+
+def wkv7_decode_step_fused(r, w, k, v, a, b, s_in, g, ln_w, ln_b, r_k, eps, s_out=None, out=None,
+                           y=None, *, want_y: bool = False, decay: str = "mult"):
+    """One decode step with the per-head output epilogue:
+    out = (GroupNorm_h(y) * ln_w + ln_b + (sum_j r_j k_j r_k[h, j]) v) * g.
+    Streams and g [B, H, 64] (one dtype); ln_w, ln_b, r_k [H, 64] fp32; state
+    [B, H, 64, 64] fp32 (s_out=s_in updates it in place). Returns
+    (out, s_out, y), y None unless want_y or given."""
+    torch = _torch()
+    B, H, n = r.shape
+    dev = r.device
+    for name, t in zip("rwkvab", (r, w, k, v, a, b)):
+        _req(t, name, dev, r.dtype, r.shape)
+    _req(g, "g", dev, r.dtype, r.shape)
+    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("r_k", r_k)):
+        _req(t, name, dev, torch.float32, (H, N))
+    _req(s_in, "s_in", dev, torch.float32, (B, H, N, N))
+    if s_out is None:
+        s_out = torch.empty_like(s_in)
+    _req(s_out, "s_out", dev, torch.float32, (B, H, N, N))
+    out = torch.empty_like(r) if out is None else out
+    _req(out, "out", dev, r.dtype, r.shape)
+    if y is None and want_y:
+        y = torch.empty_like(r)
+    if y is not None:
+        _req(y, "y", dev, r.dtype, r.shape)
+    _check("wkv7_decode_step_fused", lib().wkv7_decode_step_fused(
+        B, H, n, _dtype_code(r), _decay(decay), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(s_in),
+        _ptr(s_out), _ptr(g), _ptr(ln_w), _ptr(ln_b), _ptr(r_k), float(eps), _ptr(out), _ptr(y),
+        _stream()))
+    return out, s_out, y
 
 
 def wkv7_abi_version() -> int:

@@ -101,6 +101,27 @@ def test_decode_rejects_bad_arguments():
     assert call(s_in=P[7], s_out=ctypes.c_void_p(P[7].value + 16)) == INVALID
 
 
+def test_fused_decode_rejects_bad_arguments():
+    L = W.lib()
+
+    def call(B=4, H=2, N=64, dt=1, dc=0, g=P[9], ln_w=P[10], ln_b=P[11], r_k=P[12], eps=1e-5,
+             out=P[13], y=None, s_in=P[7], s_out=P[8]):
+        return L.wkv7_decode_step_fused(B, H, N, dt, dc, *P[:6], s_in, s_out, g, ln_w, ln_b, r_k,
+                                        eps, out, y, None)
+    assert call(N=32) == UNSUPPORTED
+    assert call(dt=3) == UNSUPPORTED
+    assert call(dc=5) == UNSUPPORTED
+    assert call(B=0) == INVALID
+    assert call(out=None) == INVALID
+    for name in ("g", "ln_w", "ln_b", "r_k"):
+        assert call(**{name: None}) == INVALID, name
+        assert call(**{name: ctypes.c_void_p(0x1004)}) == INVALID, name
+    assert call(y=ctypes.c_void_p(0x1008)) == INVALID            # y is optional but aligned
+    for eps in (-1e-5, float("nan"), float("inf")):
+        assert call(eps=eps) == INVALID, eps
+    assert call(s_in=P[7], s_out=ctypes.c_void_p(P[7].value + 16)) == INVALID
+
+
 def test_checkpoint_slots():
     assert W.checkpoint_slots(3, 33) == 9
     assert W.checkpoint_slots(2, 16) == 2
