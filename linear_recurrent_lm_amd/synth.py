@@ -226,3 +226,37 @@ def make_decode_inputs(B: int, H: int, N: int = 64, *, seed: int = 4, dtype: str
     rng = np.random.Generator(np.random.PCG64(seed + 2000))
     inp.s0 = rng.standard_normal((B, H, N, N), dtype=np.float32) * np.float32(state_std)
     return inp
+
+
+@dataclasses.dataclass
+class CEInputs:
+    """Inputs of the linear-head cross-entropy: h [M, D] and W [V, D] hold
+    bf16 values in fp32 arrays, targets [M] int32 (IGNORE on pad rows),
+    dloss [M] fp32."""
+    h: np.ndarray
+    W: np.ndarray
+    targets: np.ndarray
+    dloss: np.ndarray
+
+
+IGNORE = -100
+
+
+def make_ce_inputs(M: int, D: int, V: int, *, seed: int = 5, logit_std: float = 2.0,
+                   pad_frac: float = 0.05, dloss: str = "mean") -> CEInputs:
+    """h ~ N(0, 1) (a normalised hidden state), W ~ N(0, (logit_std^2) / D)
+    so the logits have standard deviation about logit_std, both rounded to
+    bf16; targets uniform on [0, V) with a fraction pad_frac of rows set to
+    IGNORE; dloss = 1 / (number of unmasked rows) on every row ("mean") or
+    N(0, 1) ("normal")."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    h = round_bf16(rng.standard_normal((M, D), dtype=np.float32))
+    W = round_bf16(rng.standard_normal((V, D), dtype=np.float32)
+                   * np.float32(logit_std / np.sqrt(D)))
+    t = rng.integers(0, V, size=M).astype(np.int32)
+    t[rng.random(M) < pad_frac] = IGNORE
+    if dloss == "mean":
+        dl = np.full(M, 1.0 / max(1, int((t != IGNORE).sum())), dtype=np.float32)
+    else:
+        dl = rng.standard_normal(M, dtype=np.float32)
+    return CEInputs(h, W, t, dl)
