@@ -1,0 +1,43 @@
+// Launch interfaces of the vocabulary cross-entropy kernels (host side, C++).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vce {
+
+// Macro tile of the bf16 MFMA GEMM: BI rows of A by BJ rows of B, BK along
+// the contraction per pipeline stage.
+constexpr int kBI = 256;
+constexpr int kBJ = 128;
+constexpr int kBK = 64;
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Forward split of the vocabulary: enough workgroups to fill the chip.
+struct FwdPlan {
+    int n_itiles, n_jtiles, nsplit, tiles_per_split;
+};
+FwdPlan fwd_plan(int M, int V);
+
+struct FwdArgs {
+    int M, D, V;
+    const uint16_t *h, *w;           // bf16 bits, [M, D] and [V, D]
+    const int32_t *targets;          // [M]
+    float *loss, *lse;               // [M]
+    float2 *part;                    // [nsplit, M] running (max, sum), base-2 units
+    float *zt;                       // [M] target logit
+};
+hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
+
+struct BwdArgs {
+    int M, D, V, Mc;                 // Mc: rows per chunk
+    const uint16_t *h, *w;
+    const int32_t *targets;
+    const float *lse, *dloss;
+    float *dh, *dw;
+    uint16_t *wt, *ht, *g, *gt;      // workspace: W^T [D, Vp], h_chunk^T [D, Mcp], G [Mcp, Vp], G^T [Vp, Mcp]
+};
+hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
+
+}  // namespace vce

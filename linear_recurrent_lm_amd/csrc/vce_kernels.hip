@@ -1,0 +1,432 @@
+// Linear-head cross-entropy over a large vocabulary, streamed over the
+// vocabulary (rwkv-metal, "Open problems / contributions welcome": an online
+// softmax in the forward, softmax-form gradients in the backward; rwkv-lab,
+// "From-scratch pretraining lab": fused LM-head cross-entropy with pad
+// masking). For hidden rows h[m] (D wide), head rows W[v] and targets t_m:
+//     z[m, v] = <h[m], W[v]>,  lse[m] = log sum_v exp z[m, v],
+//     loss[m] = lse[m] - z[m, t_m],  G = dloss (softmax - onehot),
+//     dh = G W,  dW = G^T h;  rows with t_m outside [0, V) are pad rows.
+//
+// One bf16 MFMA GEMM core, C[i][j] = sum_k A[i][k] B[j][k] with both operands
+// contiguous along k, serves every product through its epilogue:
+//   FWD   A = W, B = h: logits^T tiles (vocabulary down, tokens across). Each
+//         lane keeps a running (max, sum of exp) for its token columns over
+//         the vocabulary tiles of its split, in base-2 units; the target
+//         logit is taken from the tile that holds it. The [M, V] logits are
+//         never stored; a small kernel merges the splits into lse and loss.
+//   GRAD  the same tiles recomputed for one chunk of rows: G = dloss (2^(z
+//         log2 e - lse log2 e) - [v == t]) rounded to bf16 and stored twice,
+//         G [m][v] (contiguous along v, for dh) and G^T [v][m] (contiguous
+//         along m, for dW). The chunk bounds the memory to chunk x V.
+//   STORE dh = G (W^T)^T and dW = G^T (h^T)^T, with W^T and the chunk's h^T
+//         transposed copies padded with zeros, so that every product
+//         contracts along a contiguous, 64-aligned dimension; dW accumulates
+//         over chunks.
+//
+// The core: 256 threads as 2 x 2 waves, macro tile 256 x 128, wave tile
+// 128 x 64 = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (128 fp32
+// accumulators per lane). Operands go global -> registers -> LDS, 64 along k
+// per stage, double-buffered with one barrier per stage: the loads of stage
+// s+1 are in flight while the MFMAs of stage s run. LDS rows are padded to
+// 72 elements (144 B), so the 16-byte operand reads of 16 consecutive rows
+// cover all 64 banks once. Workgroup ids are remapped so that the
+// workgroups on one XCD (ids are dealt to the 8 XCDs in turn) take
+// consecutive tiles and share their A tile in that XCD's L2.
+#include "vce_kernels.h"
+
+namespace vce {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // plain vector: stays in registers
+
+constexpr int kThreads = 256;
+constexpr int LDK = kBK + 8;                         // LDS row stride (elements)
+constexpr int WI = 4, WJ = 2;                        // 32 x 32 blocks per wave
+constexpr int A_LOADS = kBI * kBK / 8 / kThreads;    // 16-byte loads per thread and stage
+constexpr int B_LOADS = kBJ * kBK / 8 / kThreads;
+constexpr int STAGE = (kBI + kBJ) * LDK;             // elements per stage
+constexpr size_t kGemmLds = 2 * STAGE * sizeof(uint16_t);
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum { EPI_FWD = 0, EPI_GRAD = 1, EPI_STORE = 2 };
+
+struct GemmArgs {
+    const uint16_t *A, *B;
+    int64_t lda, ldb;
+    int I, J, K;                 // live rows of A and B; K a multiple of kBK
+    int n_jtiles;
+    // FWD
+    int V, tiles_per_split, n_itiles;
+    const int32_t *targets;
+    float2 *part;
+    float *zt;
+    // GRAD
+    const float *lse, *dloss;
+    uint16_t *G, *Gt;
+    int64_t ldg, ldgt;
+    // STORE
+    float *C;
+    int64_t ldc;
+    int accumulate;
+};
+
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+    return (n & 7) ? b : (b & 7) * (n >> 3) + (b >> 3);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// (max, sum) pairs in base-2 units: sum_x 2^(x - max).
+__device__ __forceinline__ void lse_merge(float &m, float &s, float om, float os) {
+    const float mx = fmaxf(m, om);
+    if (mx == -INFINITY) return;
+    s = s * exp2f(m - mx) + os * exp2f(om - mx);
+    m = mx;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
+    extern __shared__ __align__(16) uint16_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wi = wave >> 1, wj = wave & 1;
+    const int b = xcd_remap(blockIdx.x, gridDim.x);
+    const int jt = b % p.n_jtiles;
+    int it_begin, it_end;
+    if (EPI == EPI_FWD) {
+        it_begin = (b / p.n_jtiles) * p.tiles_per_split;
+        it_end = min(it_begin + p.tiles_per_split, p.n_itiles);
+    } else {
+        it_begin = b / p.n_jtiles;
+        it_end = it_begin + 1;
+    }
+    const int j0 = jt * kBJ;
+
+    // Per-thread global rows of the staged tiles (rows past the live range
+    // are clamped to the last live row; their results are never used).
+    const int lrow = tid >> 3, lchunk = (tid & 7) * 8;
+    const uint16_t *bsrc[B_LOADS];
+#pragma unroll
+    for (int q = 0; q < B_LOADS; ++q) {
+        const int gj = min(j0 + q * 32 + lrow, p.J - 1);
+        bsrc[q] = p.B + (int64_t)gj * p.ldb + lchunk;
+    }
+
+    // Epilogue state (FWD): per token column of this lane, the running
+    // (max, sum) and the target row.
+    float run_m[WJ], run_s[WJ];
+    int tgt[WJ];
+#pragma unroll
+    for (int bj = 0; bj < WJ; ++bj) {
+        run_m[bj] = -INFINITY;
+        run_s[bj] = 0.f;
+        tgt[bj] = -1;
+        const int m = j0 + wj * 64 + bj * 32 + (lane & 31);
+        if ((EPI == EPI_FWD || EPI == EPI_GRAD) && m < p.J) {
+            const int t = p.targets[m];
+            tgt[bj] = (t >= 0 && t < p.V) ? t : -1;
+        }
+    }
+
+    const int nk = p.K / kBK;
+    for (int it = it_begin; it < it_end; ++it) {
+        const int i0 = it * kBI;
+        const uint16_t *asrc[A_LOADS];
+#pragma unroll
+        for (int q = 0; q < A_LOADS; ++q) {
+            const int gi = min(i0 + q * 32 + lrow, p.I - 1);
+            asrc[q] = p.A + (int64_t)gi * p.lda + lchunk;
+        }
+        f32x16 acc[WI][WJ];
+#pragma unroll
+        for (int bi = 0; bi < WI; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < WJ; ++bj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
+
+        u32x4 ra[A_LOADS], rb[B_LOADS];
+#define VCE_GLOAD(k0)                                                                      \
+    do {                                                                                   \
+        _Pragma("unroll") for (int q = 0; q < A_LOADS; ++q) ra[q] = *(const u32x4 *)(asrc[q] + (k0)); \
+        _Pragma("unroll") for (int q = 0; q < B_LOADS; ++q) rb[q] = *(const u32x4 *)(bsrc[q] + (k0)); \
+    } while (0)
+#define VCE_LSTORE(buf)                                                                    \
+    do {                                                                                   \
+        uint16_t *sa_ = lds + (buf) * STAGE;                                               \
+        uint16_t *sb_ = sa_ + kBI * LDK;                                                   \
+        _Pragma("unroll") for (int q = 0; q < A_LOADS; ++q)                                \
+            *(u32x4 *)(sa_ + (q * 32 + lrow) * LDK + lchunk) = ra[q];                      \
+        _Pragma("unroll") for (int q = 0; q < B_LOADS; ++q)                                \
+            *(u32x4 *)(sb_ + (q * 32 + lrow) * LDK + lchunk) = rb[q];                      \
+    } while (0)
+
+        __syncthreads();               // the previous tile's epilogue may still read LDS
+        VCE_GLOAD(0);
+        VCE_LSTORE(0);
+        __syncthreads();
+        for (int s = 0; s < nk; ++s) {
+            const int buf = s & 1;
+            if (s + 1 < nk) VCE_GLOAD((s + 1) * kBK);
+            const uint16_t *sa = lds + buf * STAGE + (wi * 128 + (lane & 31)) * LDK + (lane >> 5) * 8;
+            const uint16_t *sb = lds + buf * STAGE + kBI * LDK + (wj * 64 + (lane & 31)) * LDK + (lane >> 5) * 8;
+#pragma unroll
+            for (int kk = 0; kk < kBK / 16; ++kk) {
+                bf16x8 af[WI], bf[WJ];
+#pragma unroll
+                for (int bi = 0; bi < WI; ++bi) af[bi] = *(const bf16x8 *)(sa + bi * 32 * LDK + kk * 16);
+#pragma unroll
+                for (int bj = 0; bj < WJ; ++bj) bf[bj] = *(const bf16x8 *)(sb + bj * 32 * LDK + kk * 16);
+#pragma unroll
+                for (int bi = 0; bi < WI; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < WJ; ++bj)
+                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
+            }
+            if (s + 1 < nk) VCE_LSTORE(buf ^ 1);
+            __syncthreads();
+        }
+
+        // Accumulator (bi, bj, r) of lane l is C[i][j] with
+        //   i = i0 + wi*128 + bi*32 + 8*(r/4) + 4*(l/32) + r%4,
+        //   j = j0 + wj*64 + bj*32 + l%32.
+        const int ib = i0 + wi * 128 + 4 * (lane >> 5);
+        if (EPI == EPI_FWD) {
+#pragma unroll
+            for (int bj = 0; bj < WJ; ++bj) {
+                float tmax = -INFINITY;
+#pragma unroll
+                for (int bi = 0; bi < WI; ++bi)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int v = ib + bi * 32 + 8 * (r >> 2) + (r & 3);
+                        if (v < p.V) tmax = fmaxf(tmax, acc[bi][bj][r] * kLog2e);
+                    }
+                const float mnew = fmaxf(run_m[bj], tmax);
+                if (mnew != -INFINITY) {
+                    float sum = 0.f;
+#pragma unroll
+                    for (int bi = 0; bi < WI; ++bi)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int v = ib + bi * 32 + 8 * (r >> 2) + (r & 3);
+                            const float e = exp2f(fmaf(acc[bi][bj][r], kLog2e, -mnew));
+                            sum += v < p.V ? e : 0.f;
+                        }
+                    run_s[bj] = run_s[bj] * exp2f(run_m[bj] - mnew) + sum;
+                    run_m[bj] = mnew;
+                }
+                // Target logit: the one lane that holds row t of this column.
+                const int d = tgt[bj] - ib;
+                if (d >= 0 && d < 128 && ((d >> 2) & 1) == 0) {
+                    const int tbi = d >> 5, tr = ((d >> 3) & 3) * 4 + (d & 3);
+                    float z = 0.f;
+#pragma unroll
+                    for (int bi = 0; bi < WI; ++bi)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if (bi == tbi && r == tr) z = acc[bi][bj][r];
+                    p.zt[j0 + wj * 64 + bj * 32 + (lane & 31)] = z;
+                }
+            }
+        } else if (EPI == EPI_GRAD) {
+#pragma unroll
+            for (int bj = 0; bj < WJ; ++bj) {
+                const int m = j0 + wj * 64 + bj * 32 + (lane & 31);
+                const bool live = m < p.J && tgt[bj] >= 0;
+                const float l2 = live ? p.lse[m] * kLog2e : 0.f;
+                const float dl = live ? p.dloss[m] : 0.f;
+#pragma unroll
+                for (int bi = 0; bi < WI; ++bi)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int vb = ib + bi * 32 + 8 * r4;
+                        uint16_t g[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int v = vb + e;
+                            float x = exp2f(fmaf(acc[bi][bj][r4 * 4 + e], kLog2e, -l2));
+                            x = (v == tgt[bj]) ? x - 1.f : x;
+                            x = (live && v < p.V) ? x * dl : 0.f;
+                            g[e] = to_bf16(x);
+                            p.Gt[(int64_t)v * p.ldgt + m] = g[e];
+                        }
+                        uint2 pk;
+                        pk.x = (uint32_t)g[0] | ((uint32_t)g[1] << 16);
+                        pk.y = (uint32_t)g[2] | ((uint32_t)g[3] << 16);
+                        *(uint2 *)(p.G + (int64_t)m * p.ldg + vb) = pk;
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int bj = 0; bj < WJ; ++bj) {
+                const int j = j0 + wj * 64 + bj * 32 + (lane & 31);
+                if (j >= p.J) continue;
+#pragma unroll
+                for (int bi = 0; bi < WI; ++bi)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = ib + bi * 32 + 8 * (r >> 2) + (r & 3);
+                        if (i < p.I) {
+                            float *c = p.C + (int64_t)i * p.ldc + j;
+                            *c = p.accumulate ? *c + acc[bi][bj][r] : acc[bi][bj][r];
+                        }
+                    }
+            }
+        }
+    }
+
+#undef VCE_GLOAD
+#undef VCE_LSTORE
+
+    if (EPI == EPI_FWD) {
+        // Merge the two lanes that share each column, then the two waves
+        // (wi = 0, 1) that share it, and write this split's partial.
+#pragma unroll
+        for (int bj = 0; bj < WJ; ++bj) {
+            const float om = __shfl_xor(run_m[bj], 32), os = __shfl_xor(run_s[bj], 32);
+            lse_merge(run_m[bj], run_s[bj], om, os);
+        }
+        float2 *red = (float2 *)lds;
+        __syncthreads();
+        if (wi == 1 && lane < 32)
+#pragma unroll
+            for (int bj = 0; bj < WJ; ++bj) red[wj * 64 + bj * 32 + lane] = make_float2(run_m[bj], run_s[bj]);
+        __syncthreads();
+        if (wi == 0 && lane < 32) {
+            const int split = b / p.n_jtiles;
+#pragma unroll
+            for (int bj = 0; bj < WJ; ++bj) {
+                const float2 o = red[wj * 64 + bj * 32 + lane];
+                lse_merge(run_m[bj], run_s[bj], o.x, o.y);
+                const int m = j0 + wj * 64 + bj * 32 + lane;
+                if (m < p.J) p.part[(int64_t)split * p.J + m] = make_float2(run_m[bj], run_s[bj]);
+            }
+        }
+    }
+}
+
+// lse and loss per row from the splits' partials.
+__global__ __launch_bounds__(256) void combine_kernel(int M, int V, int nsplit, const float2 *part,
+                                                      const float *zt, const int32_t *targets,
+                                                      float *loss, float *lse) {
+    const int m = blockIdx.x * 256 + threadIdx.x;
+    if (m >= M) return;
+    float mx = -INFINITY, s = 0.f;
+    for (int q = 0; q < nsplit; ++q) {
+        const float2 o = part[(int64_t)q * M + m];
+        lse_merge(mx, s, o.x, o.y);
+    }
+    const float l = (mx + log2f(s)) * kLn2;
+    lse[m] = l;
+    const int t = targets[m];
+    loss[m] = (t >= 0 && t < V) ? l - zt[m] : 0.f;
+}
+
+// out[c][r] = in[r][c] for r < R, c < C, and 0 for R <= r < ldo: a 64 x 64
+// tile per workgroup through LDS (ldo a multiple of 64).
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t *in, int64_t ldi, int R, int C,
+                                                            uint16_t *out, int64_t ldo) {
+    __shared__ uint16_t t[64][66];
+    const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int r = r0 + q * 4 + ty, c = c0 + tx;
+        t[q * 4 + ty][tx] = (r < R && c < C) ? in[(int64_t)r * ldi + c] : (uint16_t)0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int c = c0 + q * 4 + ty, r = r0 + tx;
+        if (c < C) out[(int64_t)c * ldo + r] = t[tx][q * 4 + ty];
+    }
+}
+
+template <int EPI>
+hipError_t launch_gemm(const GemmArgs &a, int blocks, hipStream_t stream) {
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<EPI>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_kernel<EPI>, dim3((unsigned)blocks), dim3(kThreads), kGemmLds, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose(const uint16_t *in, int64_t ldi, int R, int C, uint16_t *out, int64_t ldo,
+                            hipStream_t stream) {
+    dim3 grid((unsigned)(ldo / 64), (unsigned)((C + 63) / 64));
+    hipLaunchKernelGGL(transpose_pad_kernel, grid, dim3(256), 0, stream, in, ldi, R, C, out, ldo);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+FwdPlan fwd_plan(int M, int V) {
+    FwdPlan f;
+    f.n_itiles = (int)((V + kBI - 1) / kBI);
+    f.n_jtiles = (int)((M + kBJ - 1) / kBJ);
+    const int want = (2048 + f.n_jtiles - 1) / f.n_jtiles;
+    const int ns = want < f.n_itiles ? want : f.n_itiles;
+    f.tiles_per_split = (f.n_itiles + ns - 1) / ns;
+    f.nsplit = (f.n_itiles + f.tiles_per_split - 1) / f.tiles_per_split;
+    return f;
+}
+
+hipError_t launch_forward(const FwdArgs &a, hipStream_t stream) {
+    const FwdPlan f = fwd_plan(a.M, a.V);
+    GemmArgs g{};
+    g.A = a.w; g.lda = a.D; g.I = a.V;
+    g.B = a.h; g.ldb = a.D; g.J = a.M;
+    g.K = a.D;
+    g.n_jtiles = f.n_jtiles;
+    g.V = a.V; g.tiles_per_split = f.tiles_per_split; g.n_itiles = f.n_itiles;
+    g.targets = a.targets; g.part = a.part; g.zt = a.zt;
+    hipError_t e = launch_gemm<EPI_FWD>(g, f.n_jtiles * f.nsplit, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((a.M + 255) / 256)), dim3(256), 0, stream, a.M, a.V,
+                       f.nsplit, a.part, a.zt, a.targets, a.loss, a.lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
+    hipError_t e;
+    const int64_t Vp = round_up(a.V, kBI);
+    const int64_t Mcp = round_up(a.Mc, kBJ);
+    if ((e = launch_transpose(a.w, a.D, a.V, a.D, a.wt, Vp, stream)) != hipSuccess) return e;
+    for (int m0 = 0; m0 < a.M; m0 += a.Mc) {
+        const int mc = a.M - m0 < a.Mc ? a.M - m0 : a.Mc;
+        const int mcp = (int)round_up(mc, kBJ);
+        if ((e = launch_transpose(a.h + (int64_t)m0 * a.D, a.D, mc, a.D, a.ht, Mcp, stream)) != hipSuccess)
+            return e;
+
+        GemmArgs g{};                 // G and G^T of this chunk
+        g.A = a.w; g.lda = a.D; g.I = a.V;
+        g.B = a.h + (int64_t)m0 * a.D; g.ldb = a.D; g.J = mc;
+        g.K = a.D; g.V = a.V;
+        g.n_jtiles = mcp / kBJ;
+        g.targets = a.targets + m0; g.lse = a.lse + m0; g.dloss = a.dloss + m0;
+        g.G = a.g; g.ldg = Vp; g.Gt = a.gt; g.ldgt = Mcp;
+        if ((e = launch_gemm<EPI_GRAD>(g, (int)(Vp / kBI) * g.n_jtiles, stream)) != hipSuccess) return e;
+
+        GemmArgs d{};                 // dh rows of the chunk = G W
+        d.A = a.g; d.lda = Vp; d.I = mc;
+        d.B = a.wt; d.ldb = Vp; d.J = a.D;
+        d.K = (int)Vp;
+        d.n_jtiles = (a.D + kBJ - 1) / kBJ;
+        d.C = a.dh + (int64_t)m0 * a.D; d.ldc = a.D; d.accumulate = 0;
+        if ((e = launch_gemm<EPI_STORE>(d, (mc + kBI - 1) / kBI * d.n_jtiles, stream)) != hipSuccess) return e;
+
+        GemmArgs w{};                 // dW (+)= G^T h over the chunk
+        w.A = a.gt; w.lda = Mcp; w.I = a.V;
+        w.B = a.ht; w.ldb = Mcp; w.J = a.D;
+        w.K = mcp;
+        w.n_jtiles = (a.D + kBJ - 1) / kBJ;
+        w.C = a.dw; w.ldc = a.D; w.accumulate = m0 > 0;
+        if ((e = launch_gemm<EPI_STORE>(w, (int)(Vp / kBI) * w.n_jtiles, stream)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace vce

@@ -7,7 +7,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include "../../include/vocab_ce.h"
 #include "../../include/wkv7.h"
+#include "vce_kernels.h"
 #include "wkv7_kernels.h"
 
 namespace {
@@ -88,6 +90,45 @@ wkv7::SegParams seg_params(const wkv7_desc *d, bool need_ckpt) {
     s.ckpt_slots = d->ckpt_slots;
     s.need_ckpt = need_ckpt ? 1 : 0;
     return s;
+}
+
+
+// Vocabulary cross-entropy: size limits and workspace layout.
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+size_t pad256(size_t x) { return (x + 255) / 256 * 256; }
+
+wkv7_status vce_check_sizes(int32_t M, int32_t D, int32_t V) {
+    if (M < 1 || M > (1 << 28)) return WKV7_ERR_INVALID_ARGUMENT;
+    if (D < 64 || D > 65536 || D % 64 != 0) return WKV7_ERR_INVALID_ARGUMENT;
+    if (V < 1 || V > (1 << 24)) return WKV7_ERR_INVALID_ARGUMENT;
+    return WKV7_OK;
+}
+
+struct VceBwdLayout {
+    int32_t Mc;
+    size_t wt, ht, g, gt, total;     // byte offsets
+};
+
+// [W^T: D x Vp][h_chunk^T: D x Mcp][G: Mcp x Vp][G^T: Vp x Mcp], bf16, each 256-byte aligned.
+wkv7_status vce_bwd_layout(int32_t M, int32_t D, int32_t V, int32_t row_chunk, VceBwdLayout *l) {
+    wkv7_status st = vce_check_sizes(M, D, V);
+    if (st != WKV7_OK) return st;
+    if (row_chunk < 1) return WKV7_ERR_INVALID_ARGUMENT;
+    l->Mc = row_chunk < M ? row_chunk : M;
+    const int64_t Vp = vce::round_up(V, vce::kBI), Mcp = vce::round_up(l->Mc, vce::kBJ);
+    if ((Vp / vce::kBI) * (Mcp / vce::kBJ) > (1 << 24)) return WKV7_ERR_INVALID_ARGUMENT;
+    l->wt = 0;
+    l->ht = l->wt + pad256((size_t)D * Vp * 2);
+    l->g = l->ht + pad256((size_t)D * Mcp * 2);
+    l->gt = l->g + pad256((size_t)Mcp * Vp * 2);
+    l->total = l->gt + pad256((size_t)Vp * Mcp * 2);
+    return WKV7_OK;
+}
+
+size_t vce_fwd_bytes(int32_t M, int32_t V) {
+    const vce::FwdPlan f = vce::fwd_plan(M, V);
+    return pad256((size_t)f.nsplit * M * 8) + pad256((size_t)M * 4);
 }
 
 }  // namespace
@@ -279,6 +320,93 @@ wkv7_status wkv7_decode_step_fused(int32_t B, int32_t H, int32_t N, int32_t dtyp
     if (!out) return WKV7_ERR_INVALID_ARGUMENT;
     return decode_impl(B, H, N, dtype, decay, r, w, k, v, a, b, s_in, s_out, y,
                        g, ln_w, ln_b, r_k, eps, out, stream);
+}
+
+wkv7_status vce_forward_workspace_bytes(int32_t M, int32_t D, int32_t V, size_t *bytes) {
+    wkv7_status st = vce_check_sizes(M, D, V);
+    if (st != WKV7_OK) return st;
+    if (!bytes) return WKV7_ERR_INVALID_ARGUMENT;
+    *bytes = vce_fwd_bytes(M, V);
+    return WKV7_OK;
+}
+
+wkv7_status vce_backward_workspace_bytes(int32_t M, int32_t D, int32_t V, int32_t row_chunk,
+                                         size_t *bytes) {
+    VceBwdLayout l;
+    wkv7_status st = vce_bwd_layout(M, D, V, row_chunk, &l);
+    if (st != WKV7_OK) return st;
+    if (!bytes) return WKV7_ERR_INVALID_ARGUMENT;
+    *bytes = l.total;
+    return WKV7_OK;
+}
+
+wkv7_status vce_forward(int32_t M, int32_t D, int32_t V, const void *h, const void *w,
+                        const int32_t *targets, float *loss, float *lse, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    wkv7_status st = vce_check_sizes(M, D, V);
+    if (st != WKV7_OK) return st;
+    if (!h || !w || !aligned16(h) || !aligned16(w)) return WKV7_ERR_INVALID_ARGUMENT;
+    if (!targets || !loss || !lse || !aligned4(targets) || !aligned4(loss) || !aligned4(lse))
+        return WKV7_ERR_INVALID_ARGUMENT;
+    if (!workspace || !aligned16(workspace)) return WKV7_ERR_INVALID_ARGUMENT;
+    const size_t need = vce_fwd_bytes(M, V);
+    if (workspace_bytes < need) return WKV7_ERR_WORKSPACE_TOO_SMALL;
+    const size_t row = (size_t)M * 4;
+    if (ranges_overlap(loss, row, lse, row)) return WKV7_ERR_INVALID_ARGUMENT;
+    const void *ins[3] = {h, w, targets};
+    const size_t in_bytes[3] = {(size_t)M * D * 2, (size_t)V * D * 2, row};
+    for (int q = 0; q < 3; ++q)
+        if (ranges_overlap(ins[q], in_bytes[q], loss, row) || ranges_overlap(ins[q], in_bytes[q], lse, row) ||
+            ranges_overlap(ins[q], in_bytes[q], workspace, need))
+            return WKV7_ERR_INVALID_ARGUMENT;
+    if (ranges_overlap(loss, row, workspace, need) || ranges_overlap(lse, row, workspace, need))
+        return WKV7_ERR_INVALID_ARGUMENT;
+    if ((st = check_device()) != WKV7_OK) return st;
+    const vce::FwdPlan f = vce::fwd_plan(M, V);
+    vce::FwdArgs a;
+    a.M = M; a.D = D; a.V = V;
+    a.h = (const uint16_t *)h; a.w = (const uint16_t *)w;
+    a.targets = targets; a.loss = loss; a.lse = lse;
+    a.part = (float2 *)workspace;
+    a.zt = (float *)((char *)workspace + pad256((size_t)f.nsplit * M * 8));
+    if (vce::launch_forward(a, (hipStream_t)stream) != hipSuccess) return WKV7_ERR_HIP;
+    return WKV7_OK;
+}
+
+wkv7_status vce_backward(int32_t M, int32_t D, int32_t V, int32_t row_chunk, const void *h,
+                         const void *w, const int32_t *targets, const float *lse,
+                         const float *dloss, float *dh, float *dw, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    VceBwdLayout l;
+    wkv7_status st = vce_bwd_layout(M, D, V, row_chunk, &l);
+    if (st != WKV7_OK) return st;
+    if (!h || !w || !aligned16(h) || !aligned16(w)) return WKV7_ERR_INVALID_ARGUMENT;
+    if (!targets || !lse || !dloss || !dh || !dw) return WKV7_ERR_INVALID_ARGUMENT;
+    if (!aligned4(targets) || !aligned4(lse) || !aligned4(dloss) || !aligned4(dh) || !aligned4(dw))
+        return WKV7_ERR_INVALID_ARGUMENT;
+    if (!workspace || !aligned16(workspace)) return WKV7_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < l.total) return WKV7_ERR_WORKSPACE_TOO_SMALL;
+    const size_t row = (size_t)M * 4;
+    const void *ins[5] = {h, w, targets, lse, dloss};
+    const size_t in_bytes[5] = {(size_t)M * D * 2, (size_t)V * D * 2, row, row, row};
+    void *outs[3] = {dh, dw, workspace};
+    const size_t out_bytes[3] = {(size_t)M * D * 4, (size_t)V * D * 4, l.total};
+    for (int o = 0; o < 3; ++o) {
+        for (int q = 0; q < 5; ++q)
+            if (ranges_overlap(ins[q], in_bytes[q], outs[o], out_bytes[o])) return WKV7_ERR_INVALID_ARGUMENT;
+        for (int o2 = o + 1; o2 < 3; ++o2)
+            if (ranges_overlap(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return WKV7_ERR_INVALID_ARGUMENT;
+    }
+    if ((st = check_device()) != WKV7_OK) return st;
+    char *ws = (char *)workspace;
+    vce::BwdArgs a;
+    a.M = M; a.D = D; a.V = V; a.Mc = l.Mc;
+    a.h = (const uint16_t *)h; a.w = (const uint16_t *)w;
+    a.targets = targets; a.lse = lse; a.dloss = dloss; a.dh = dh; a.dw = dw;
+    a.wt = (uint16_t *)(ws + l.wt); a.ht = (uint16_t *)(ws + l.ht);
+    a.g = (uint16_t *)(ws + l.g); a.gt = (uint16_t *)(ws + l.gt);
+    if (vce::launch_backward(a, (hipStream_t)stream) != hipSuccess) return WKV7_ERR_HIP;
+    return WKV7_OK;
 }
 
 }  // extern "C"

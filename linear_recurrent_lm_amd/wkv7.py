@@ -13,6 +13,7 @@ w as log(decay); grad_f32=True writes the gradients in fp32.
 from __future__ import annotations
 
 import ctypes
+import glob
 import os
 import re
 
@@ -48,9 +49,11 @@ _lib = None
 
 
 def declared_functions() -> list[str]:
-    """Names of the functions include/wkv7.h declares."""
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(wkv7_[a-z_]+)\s*\(", text)))
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for path in sorted(glob.glob(os.path.join(os.path.dirname(HEADER), "*.h"))):
+        names |= set(re.findall(r"\b((?:wkv7|vce)_[a-z_]+)\s*\(", open(path).read()))
+    return sorted(names)
 
 
 def lib():
@@ -73,9 +76,14 @@ def lib():
         L.wkv7_status_string.argtypes = [i32]
         L.wkv7_status_string.restype = ctypes.c_char_p
         L.wkv7_abi_version.restype = i32
+        L.vce_forward_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+        L.vce_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.vce_forward.argtypes = [i32, i32, i32] + [vp] * 6 + [sz, vp]
+        L.vce_backward.argtypes = [i32, i32, i32, i32] + [vp] * 8 + [sz, vp]
         for fn in ("wkv7_forward", "wkv7_backward", "wkv7_decode_step", "wkv7_decode_step_fused",
                    "wkv7_checkpoint_slots",
-                   "wkv7_workspace_bytes", "wkv7_segments_check"):
+                   "wkv7_workspace_bytes", "wkv7_segments_check", "vce_forward_workspace_bytes",
+                   "vce_backward_workspace_bytes", "vce_forward", "vce_backward"):
             getattr(L, fn).restype = i32
         _lib = L
     return _lib

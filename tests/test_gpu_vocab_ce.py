@@ -1,0 +1,158 @@
+"""GPU parity of the vocabulary cross-entropy (include/vocab_ce.h) against the
+fp64 oracle (oracle/vocab_ce.py), through the C ABI.
+
+Tolerances. The logits are fp32 sums of exact bf16 products, so loss and lse
+carry fp32 rounding only: 2e-5 of max(1, |loss|). The gradient products take
+G rounded to bf16 (at most 2^-8 of each entry), which alone moves a row of dh
+or dW by up to 4.5e-3 of its largest entry on these inputs (the oracle's G
+rounded the same way, in fp64): gradients are held to 2e-2 of each row's
+largest entry. A row whose largest reference entry is below 1e-3 of
+the tensor's largest is judged against that floor instead."""
+import numpy as np
+import pytest
+
+from linear_recurrent_lm_amd import synth
+from oracle import vocab_ce as O
+
+pytestmark = pytest.mark.gpu
+
+TOL_LOSS = 2e-5
+TOL_GRAD = 2e-2
+
+
+@pytest.fixture(scope="module")
+def C():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_recurrent_lm_amd import vocab_ce, wkv7
+    wkv7.lib()
+    return vocab_ce
+
+
+def dev(c):
+    import torch
+    h = torch.from_numpy(c.h).to("cuda:0").to(torch.bfloat16)
+    w = torch.from_numpy(c.W).to("cuda:0").to(torch.bfloat16)
+    t = torch.from_numpy(c.targets).to("cuda:0")
+    dl = torch.from_numpy(c.dloss).to("cuda:0")
+    return h, w, t, dl
+
+
+def host(x):
+    return x.cpu().numpy().astype(np.float64)
+
+
+def loss_err(x, ref):
+    return float(np.max(np.abs(x - ref))) / max(1.0, float(np.max(np.abs(ref))))
+
+
+def row_err(x, ref):
+    top = float(np.max(np.abs(ref)))
+    if top == 0.0:
+        return float(np.max(np.abs(x)))
+    num = np.max(np.abs(x - ref), axis=1)
+    den = np.maximum(np.max(np.abs(ref), axis=1), 1e-3 * top)
+    return float(np.max(num / den))
+
+
+def run(C, c, row_chunk):
+    import torch
+    h, w, t, dl = dev(c)
+    loss, lse = C.vce_forward(h, w, t)
+    dh, dw = C.vce_backward(h, w, t, lse, dl, row_chunk=row_chunk)
+    torch.cuda.synchronize()
+    return host(loss), host(lse), host(dh), host(dw)
+
+
+CASES = {
+    # M, D, V, row_chunk, logit std: ragged token and vocabulary tiles, several chunks
+    "ragged_3_chunks": (300, 128, 1000, 128, 2.0),
+    "ragged_one_chunk": (300, 128, 1000, 4096, 2.0),
+    "odd_chunk": (129, 64, 257, 100, 2.0),
+    "wide_many_vtiles": (200, 512, 3000, 64, 2.0),
+    "large_logits": (64, 192, 2000, 64, 30.0),
+    "single_row_vocab": (1, 64, 1, 1, 2.0),
+    "two_classes": (70, 64, 2, 32, 2.0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_small_parity(C, case):
+    M, D, V, chunk, std = CASES[case]
+    c = synth.make_ce_inputs(M, D, V, seed=61, logit_std=std, pad_frac=0.1, dloss="normal")
+    if M > 2:
+        c.targets[0], c.targets[1] = 0, V - 1          # both ends of the vocabulary
+    loss, lse, dh, dw = run(C, c, chunk)
+    rl, rs = O.forward(c.h, c.W, c.targets)
+    rdh, rdw = O.backward(c.h, c.W, c.targets, c.dloss)
+    assert loss_err(loss, rl) <= TOL_LOSS
+    assert loss_err(lse, rs) <= TOL_LOSS
+    assert row_err(dh, rdh) <= TOL_GRAD
+    assert row_err(dw, rdw) <= TOL_GRAD
+    pad = (c.targets < 0) | (c.targets >= V)
+    assert np.all(loss[pad] == 0.0)
+    assert np.all(dh[pad] == 0.0)
+
+
+def test_all_rows_padded(C):
+    c = synth.make_ce_inputs(150, 64, 700, seed=62, pad_frac=1.0, dloss="normal")
+    loss, lse, dh, dw = run(C, c, 64)
+    assert np.all(loss == 0.0) and np.all(dh == 0.0) and np.all(dw == 0.0)
+    assert loss_err(lse, O.forward(c.h, c.W, c.targets)[1]) <= TOL_LOSS
+
+
+def test_deterministic(C):
+    c = synth.make_ce_inputs(300, 128, 1000, seed=63, dloss="normal")
+    a = run(C, c, 128)
+    b = run(C, c, 128)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_full_vocab_and_width(C):
+    """V = 65536 (the World vocabulary) and D = 2048 at M = 512 in two chunks:
+    every output against the oracle."""
+    c = synth.make_ce_inputs(512, 2048, 65536, seed=64, dloss="normal")
+    loss, lse, dh, dw = run(C, c, 256)
+    rl, rs = O.forward(c.h, c.W, c.targets)
+    assert loss_err(loss, rl) <= TOL_LOSS
+    assert loss_err(lse, rs) <= TOL_LOSS
+    rdh, rdw = O.backward(c.h, c.W, c.targets, c.dloss)
+    assert row_err(dh, rdh) <= TOL_GRAD
+    assert row_err(dw, rdw) <= TOL_GRAD
+
+
+def test_training_workload_sampled(C):
+    """M = 16384 (4 x 4096 tokens), D = 2048, V = 65536, mean-reduction dloss,
+    in the launch configuration the benchmark times (chunks of 4096 rows):
+    loss, lse and dh on sampled rows against the oracle on that row alone;
+    dh and dW unchanged when the rows are taken in one chunk instead of four;
+    and the column sums of dW, which are exactly zero before G is rounded, within
+    the rounding bound 2^-7 sum_m dloss_m |h[m, d]| (each unmasked row of G sums
+    to zero and has absolute sum 2 dloss_m (1 - p_t) <= 2 dloss_m)."""
+    import torch
+    M, D, V = 16384, 2048, 65536
+    c = synth.make_ce_inputs(M, D, V, seed=65)
+    h, w, t, dl = dev(c)
+    loss, lse = C.vce_forward(h, w, t)
+    dh, dw = C.vce_backward(h, w, t, lse, dl, row_chunk=4096)
+    torch.cuda.synchronize()
+    rows = np.random.Generator(np.random.PCG64(65)).choice(M, 12, replace=False)
+    rows[0] = M - 1
+    W64 = c.W.astype(np.float64)
+    for m in rows:
+        sl = slice(m, m + 1)
+        rl, rs = O.forward(c.h[sl], W64, c.targets[sl])
+        assert loss_err(host(loss[sl]), rl) <= TOL_LOSS, m
+        assert loss_err(host(lse[sl]), rs) <= TOL_LOSS, m
+        rdh, _ = O.backward(c.h[sl], W64, c.targets[sl], c.dloss[sl])
+        assert row_err(host(dh[sl]), rdh) <= TOL_GRAD, m
+    del W64
+    colsum = dw.double().sum(dim=0).abs()
+    bound = 2.0 ** -7 * (dl.double()[:, None] * h.double().abs()).sum(dim=0) + 1e-9
+    assert bool((colsum <= bound).all())
+    dh1, dw1 = C.vce_backward(h, w, t, lse, dl, row_chunk=M)
+    torch.cuda.synchronize()
+    assert torch.equal(dh1, dh)
+    assert ((dw1 - dw).abs().amax(dim=1) <= 1e-4 * dw.abs().amax(dim=1) + 1e-12).all()

@@ -1,0 +1,91 @@
+"""C-ABI checks of the vocabulary cross-entropy entry points that need no GPU:
+the workspace queries and the argument validation, which must reject bad
+sizes, pointers, alignments, overlaps and short workspaces with the
+documented status codes before touching the HIP runtime."""
+import ctypes
+
+import pytest
+
+from linear_recurrent_lm_amd import vocab_ce as C
+from linear_recurrent_lm_amd import wkv7 as W
+
+INVALID, UNSUPPORTED, WS = 1, 2, 3
+
+# Fake, widely spaced, 16-byte aligned device addresses: validation must fail
+# on the argument under test before any of these could be dereferenced.
+P = [ctypes.c_void_p((q + 1) << 40) for q in range(12)]
+BIG = 1 << 38
+
+
+def fwd(M=300, D=128, V=1000, h=P[0], w=P[1], t=P[2], loss=P[3], lse=P[4], ws=P[5], nbytes=BIG):
+    return W.lib().vce_forward(M, D, V, h, w, t, loss, lse, ws, nbytes, None)
+
+
+def bwd(M=300, D=128, V=1000, chunk=128, h=P[0], w=P[1], t=P[2], lse=P[3], dl=P[4], dh=P[5],
+        dw=P[6], ws=P[7], nbytes=BIG):
+    return W.lib().vce_backward(M, D, V, chunk, h, w, t, lse, dl, dh, dw, ws, nbytes, None)
+
+
+def test_declared_and_exported():
+    names = set(W.declared_functions())
+    want = {"vce_forward", "vce_backward", "vce_forward_workspace_bytes",
+            "vce_backward_workspace_bytes"}
+    assert want <= names
+    for n in want:
+        assert hasattr(W.lib(), n)
+
+
+def test_workspace_queries():
+    # forward: one (max, sum) pair per row and split plus the target logits
+    assert C.vce_forward_workspace_bytes(16384, 2048, 65536) >= 16384 * 8 + 16384 * 4
+    # backward: W^T, the chunk's h^T, G and G^T, padded to 256 vocabulary rows and 128 token rows
+    Vp, Mcp, D = 65536, 4096, 2048
+    want = 2 * (D * Vp + D * Mcp + 2 * Mcp * Vp)
+    assert C.vce_backward_workspace_bytes(16384, D, 65536, 4096) == want
+    # the chunk is capped at M; the vocabulary pads to a multiple of 256
+    assert (C.vce_backward_workspace_bytes(100, 64, 1000, 4096)
+            == 2 * (64 * 1024 + 64 * 128 + 2 * 128 * 1024))
+    # a smaller chunk needs less
+    assert (C.vce_backward_workspace_bytes(16384, D, 65536, 1024)
+            < C.vce_backward_workspace_bytes(16384, D, 65536, 4096))
+
+
+@pytest.mark.parametrize("M,D,V", [(0, 128, 10), (-1, 128, 10), ((1 << 28) + 1, 128, 10),
+                                   (4, 0, 10), (4, 96, 10), (4, 32, 10), (4, 65600, 10),
+                                   (4, 128, 0), (4, 128, (1 << 24) + 1)])
+def test_bad_sizes(M, D, V):
+    assert fwd(M=M, D=D, V=V) == INVALID
+    assert bwd(M=M, D=D, V=V) == INVALID
+    with pytest.raises(W.WKV7Error):
+        C.vce_forward_workspace_bytes(M, D, V)
+    with pytest.raises(W.WKV7Error):
+        C.vce_backward_workspace_bytes(M, D, V, 64)
+
+
+def test_forward_rejects_bad_pointers():
+    for name in ("h", "w", "t", "loss", "lse", "ws"):
+        assert fwd(**{name: None}) == INVALID, name
+    assert fwd(h=ctypes.c_void_p(P[0].value + 8)) == INVALID      # bf16 operands: 16-byte aligned
+    assert fwd(w=ctypes.c_void_p(P[1].value + 4)) == INVALID
+    assert fwd(loss=ctypes.c_void_p(P[3].value + 2)) == INVALID
+    assert fwd(ws=ctypes.c_void_p(P[5].value + 4)) == INVALID
+    assert fwd(lse=ctypes.c_void_p(P[3].value + 64)) == INVALID    # overlaps loss
+    assert fwd(loss=ctypes.c_void_p(P[0].value + 256)) == INVALID  # overlaps h
+    assert fwd(ws=ctypes.c_void_p(P[1].value + 4096)) == INVALID   # overlaps w
+    need = C.vce_forward_workspace_bytes(300, 128, 1000)
+    assert fwd(nbytes=need - 1) == WS
+
+
+def test_backward_rejects_bad_arguments():
+    assert bwd(chunk=0) == INVALID
+    for name in ("h", "w", "t", "lse", "dl", "dh", "dw", "ws"):
+        assert bwd(**{name: None}) == INVALID, name
+    assert bwd(dh=ctypes.c_void_p(P[5].value + 2)) == INVALID
+    assert bwd(h=ctypes.c_void_p(P[0].value + 8)) == INVALID
+    assert bwd(dw=ctypes.c_void_p(P[5].value + 1024)) == INVALID   # overlaps dh
+    assert bwd(dh=ctypes.c_void_p(P[0].value + 1024)) == INVALID   # overlaps h
+    assert bwd(ws=ctypes.c_void_p(P[6].value + 4096)) == INVALID   # overlaps dw
+    need = C.vce_backward_workspace_bytes(300, 128, 1000, 128)
+    assert bwd(nbytes=need - 1) == WS
+    # a huge vocabulary tiled with a huge chunk exceeds the launchable grid
+    assert bwd(M=1 << 26, V=1 << 24, chunk=1 << 26) == INVALID
