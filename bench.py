@@ -6,7 +6,10 @@ dy ~ N(0,1)): wkv7_forward writing 16-token checkpoints, then wkv7_backward.
 Inputs are resident in HBM before timing starts. The JSON line reports whole
 step throughput in tokens/s (a token spans all H heads), the roofline of the
 dominant kernel (HIP events on the launch stream), and the fp64 oracle timed
-on the host's cores over a bounded sample of the same workload.
+on the host's cores over a bounded sample of the same workload. Further
+objects time the other calls of the library on their own workloads
+(prefill, ragged batches, decode, the I/O variants, and the LM-head
+cross-entropy over the 65536-entry vocabulary).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -33,6 +36,7 @@ FWD_CKPT_BYTES = FWD_BYTES + 1024   # + one fp32 checkpoint per 16 tokens: 1920
 BWD_BYTES = 6 * 128 + 128 + 1024 + 6 * 128  # 2688
 PEAK_HBM = 8.0e12               # B/s
 PEAK_FP32 = 157.3e12            # FLOP/s, vector or matrix fp32
+PEAK_BF16 = 2.5e15              # FLOP/s, dense bf16 MFMA
 
 
 def parse():
@@ -282,6 +286,32 @@ def main():
     log_ms = _time_ms(log_step, args.warmup, args.steps, ev)
     del lts, g32
 
+    # Vocabulary cross-entropy of the LM head on the training batch's tokens:
+    # M = 4 x 4096 rows, D = 2048 (the 1.5B width), V = 65536 (World
+    # vocabulary), 5% pad rows, mean reduction; backward in vocabulary
+    # chunks of 16384 rows. Flops as executed: 2MVD forward, 6MVD backward (the logits are
+    # recomputed instead of stored).
+    from linear_recurrent_lm_amd import vocab_ce as VC
+    CM, CD, CV, CCH = B * T, 2048, 65536, 16384
+    cin = synth.make_ce_inputs(CM, CD, CV, seed=7)
+    ch = torch.from_numpy(cin.h).to(dev).to(torch.bfloat16)
+    cw = torch.from_numpy(cin.W).to(dev).to(torch.bfloat16)
+    ct = torch.from_numpy(cin.targets).to(dev)
+    cdl = torch.from_numpy(cin.dloss).to(dev)
+    del cin
+    closs = torch.empty(CM, device=dev, dtype=torch.float32)
+    clse = torch.empty_like(closs)
+    cdh = torch.empty((CM, CD), device=dev, dtype=torch.float32)
+    cdw = torch.empty((CV, CD), device=dev, dtype=torch.float32)
+    cfws = torch.empty(VC.vce_forward_workspace_bytes(CM, CD, CV), device=dev, dtype=torch.uint8)
+    cbws = torch.empty(VC.vce_backward_workspace_bytes(CM, CD, CV, CCH), device=dev, dtype=torch.uint8)
+    ce_f_ms = _time_ms(lambda: VC.vce_forward(ch, cw, ct, loss=closs, lse=clse, workspace=cfws),
+                       args.warmup, args.steps, ev)
+    ce_b_ms = _time_ms(lambda: VC.vce_backward(ch, cw, ct, clse, cdl, vocab_chunk=CCH, dh=cdh, dw=cdw,
+                                               workspace=cbws), args.warmup, args.steps, ev)
+    ce_flop = 2.0 * CM * CV * CD
+    del ch, cw, ct, cdl, closs, clse, cdh, cdw, cfws, cbws
+
     f_ms, b_ms = float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
     th = tok * H
     kernels = {
@@ -352,6 +382,14 @@ def main():
                         "(forward with checkpoints + backward)",
             "ms": log_ms, "tokens_per_s": tok / (log_ms * 1e-3)},
     }
+    out["vocab_ce"] = {
+        "workload": "LM-head cross-entropy, bf16 h [16384, 2048] and W [65536, 2048], 5% pad rows, "
+                    "mean reduction, backward in vocabulary chunks of 16384 rows",
+        "forward_ms": ce_f_ms, "backward_ms": ce_b_ms,
+        "tokens_per_s": CM / ((ce_f_ms + ce_b_ms) * 1e-3),
+        "forward_tflops": ce_flop / (ce_f_ms * 1e-3) / 1e12,
+        "backward_tflops": 3 * ce_flop / (ce_b_ms * 1e-3) / 1e12,
+        "mfma_bf16_frac": 4 * ce_flop / ((ce_f_ms + ce_b_ms) * 1e-3) / PEAK_BF16}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

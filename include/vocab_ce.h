@@ -27,10 +27,11 @@
  * before the two gradient products; everything else stays in fp32.
  *
  * Workspace. Both calls take a caller-provided device workspace; the library
- * allocates nothing. The backward processes the rows in chunks of
- * row_chunk: its workspace holds the chunk's G in both orders (about
- * 4 * row_chunk * V bytes) plus transposed copies of W and of the chunk's h.
- * That is the whole memory floor; the [M, V] logits never exist.
+ * allocates nothing. The backward processes the vocabulary in chunks of
+ * vocab_chunk rows (rounded up to a multiple of 256): its workspace holds the
+ * chunk's G in both orders (about 4 * M * vocab_chunk bytes) plus transposed
+ * copies of W and h. That is the whole memory floor; the [M, V] logits never
+ * exist.
  *
  * Errors. Every argument is checked on the host before anything is
  * enqueued; on an error nothing is launched. Status codes are those of
@@ -51,15 +52,16 @@ extern "C" {
 
 /*
  * Sizes accepted by every call: 1 <= M <= 2^28, 64 <= D <= 65536 with D a
- * multiple of 64, 1 <= V <= 2^24, 1 <= row_chunk. Anything else:
+ * multiple of 64, 1 <= V <= 2^24, 1 <= vocab_chunk. Anything else:
  * WKV7_ERR_INVALID_ARGUMENT.
  */
 
 /* Workspace bytes of vce_forward for (M, D, V); *bytes is written on success. */
 wkv7_status vce_forward_workspace_bytes(int32_t M, int32_t D, int32_t V, size_t *bytes);
 
-/* Workspace bytes of vce_backward; rows are processed min(row_chunk, M) at a time. */
-wkv7_status vce_backward_workspace_bytes(int32_t M, int32_t D, int32_t V, int32_t row_chunk,
+/* Workspace bytes of vce_backward; the vocabulary is processed vocab_chunk rows
+ * (rounded up to a multiple of 256, at most V) at a time. */
+wkv7_status vce_backward_workspace_bytes(int32_t M, int32_t D, int32_t V, int32_t vocab_chunk,
                                          size_t *bytes);
 
 /*
@@ -87,10 +89,10 @@ wkv7_status vce_forward(int32_t M, int32_t D, int32_t V, const void *h, const vo
  *   dh    : fp32 [M, D] output; dw : fp32 [V, D] output (overwritten, not
  *           accumulated into). Neither may overlap an input, each other or
  *           the workspace.
- *   workspace : >= vce_backward_workspace_bytes(M, D, V, row_chunk), 16-byte aligned.
+ *   workspace : >= vce_backward_workspace_bytes(M, D, V, vocab_chunk), 16-byte aligned.
  * Errors as for vce_forward.
  */
-wkv7_status vce_backward(int32_t M, int32_t D, int32_t V, int32_t row_chunk, const void *h,
+wkv7_status vce_backward(int32_t M, int32_t D, int32_t V, int32_t vocab_chunk, const void *h,
                          const void *w, const int32_t *targets, const float *lse,
                          const float *dloss, float *dh, float *dw, void *workspace,
                          size_t workspace_bytes, void *stream);

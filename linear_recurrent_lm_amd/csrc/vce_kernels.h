@@ -6,10 +6,12 @@
 
 namespace vce {
 
-// Macro tile of the bf16 MFMA GEMM: BI rows of A by BJ rows of B, BK along
-// the contraction per pipeline stage.
+// Macro tile of the bf16 MFMA GEMM: BI rows of A (vocabulary rows in the
+// logit tiles) by BJ rows of B (token rows), BK along the contraction per
+// pipeline stage. Token rows are padded to a multiple of kBJ, vocabulary
+// rows (and a chunk of them) to a multiple of kBI.
 constexpr int kBI = 256;
-constexpr int kBJ = 128;
+constexpr int kBJ = 256;
 constexpr int kBK = 64;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -31,12 +33,12 @@ struct FwdArgs {
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
 
 struct BwdArgs {
-    int M, D, V, Mc;                 // Mc: rows per chunk
+    int M, D, V, Vc;                 // Vc: vocabulary rows per chunk
     const uint16_t *h, *w;
     const int32_t *targets;
     const float *lse, *dloss;
     float *dh, *dw;
-    uint16_t *wt, *ht, *g, *gt;      // workspace: W^T [D, Vp], h_chunk^T [D, Mcp], G [Mcp, Vp], G^T [Vp, Mcp]
+    uint16_t *wt, *ht, *g, *gt;      // workspace: W^T [D, Vp], h^T [D, Mp], G [Mp, Vcp], G^T [Vcp, Mp]
 };
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 

@@ -14,20 +14,25 @@
 //         the vocabulary tiles of its split, in base-2 units; the target
 //         logit is taken from the tile that holds it. The [M, V] logits are
 //         never stored; a small kernel merges the splits into lse and loss.
-//   GRAD  the same tiles recomputed for one chunk of rows: G = dloss (2^(z
-//         log2 e - lse log2 e) - [v == t]) rounded to bf16 and stored twice,
-//         G [m][v] (contiguous along v, for dh) and G^T [v][m] (contiguous
-//         along m, for dW). The chunk bounds the memory to chunk x V.
-//   STORE dh = G (W^T)^T and dW = G^T (h^T)^T, with W^T and the chunk's h^T
-//         transposed copies padded with zeros, so that every product
-//         contracts along a contiguous, 64-aligned dimension; dW accumulates
-//         over chunks.
+//   GRAD  the same tiles recomputed for one chunk of vocabulary rows: G =
+//         dloss (2^(z log2 e - lse log2 e) - [v == t]) rounded to bf16 and
+//         stored twice, G [m][v] (contiguous along v, for dh) and G^T [v][m]
+//         (contiguous along m, for dW). The chunk bounds the memory to
+//         M x chunk.
+//   STORE dW rows of the chunk = G^T (h^T)^T, written once, and dh += G
+//         (W^T)^T, with W^T and h^T transposed copies padded with zeros, so
+//         that every product contracts along a contiguous, 64-aligned
+//         dimension. Chunking the vocabulary (not the rows) leaves only the
+//         smaller dh [M, D] to accumulate.
 //
-// The core: 256 threads as 2 x 2 waves, macro tile 256 x 128, wave tile
-// 128 x 64 = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (128 fp32
-// accumulators per lane). Operands go global -> registers -> LDS, 64 along k
-// per stage, double-buffered with one barrier per stage: the loads of stage
-// s+1 are in flight while the MFMAs of stage s run. LDS rows are padded to
+// The core: 256 threads as 2 x 2 waves, macro tile 256 x 256, wave tile
+// 128 x 128 = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32
+// accumulators per lane; per k-step a wave reads 8 operand fragments for 16
+// MFMAs). The dh product, whose chunk gives few row tiles, uses 256 x 128
+// macro tiles (4 x 2 blocks per wave) so that it still fills the chip. Operands go global -> registers -> LDS, 64 along k
+// per stage, double-buffered in LDS with one barrier per stage; the global
+// loads run two stages ahead (two register sets), so they have the MFMA time
+// of two stages to land. LDS rows are padded to
 // 72 elements (144 B), so the 16-byte operand reads of 16 consecutive rows
 // cover all 64 banks once. Workgroup ids are remapped so that the
 // workgroups on one XCD (ids are dealt to the 8 XCDs in turn) take
@@ -43,11 +48,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // plain vector: s
 
 constexpr int kThreads = 256;
 constexpr int LDK = kBK + 8;                         // LDS row stride (elements)
-constexpr int WI = 4, WJ = 2;                        // 32 x 32 blocks per wave
+constexpr int WI = 4;                                // 32 x 32 blocks per wave along i
 constexpr int A_LOADS = kBI * kBK / 8 / kThreads;    // 16-byte loads per thread and stage
-constexpr int B_LOADS = kBJ * kBK / 8 / kThreads;
-constexpr int STAGE = (kBI + kBJ) * LDK;             // elements per stage
-constexpr size_t kGemmLds = 2 * STAGE * sizeof(uint16_t);
+// Along j a wave holds WJ blocks (WJ = 4: 256 x 256 macro tile; WJ = 2: 256 x 128).
+template <int WJ> struct Tile {
+    static constexpr int BJ = 64 * WJ;
+    static constexpr int B_LOADS = BJ * kBK / 8 / kThreads;
+    static constexpr int STAGE = (kBI + BJ) * LDK;             // elements per stage
+    static constexpr size_t LDS = 2 * STAGE * sizeof(uint16_t);
+};
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -60,6 +69,7 @@ struct GemmArgs {
     int n_jtiles;
     // FWD
     int V, tiles_per_split, n_itiles;
+    int v_base;                  // GRAD: vocabulary index of A's row 0
     const int32_t *targets;
     float2 *part;
     float *zt;
@@ -87,8 +97,10 @@ __device__ __forceinline__ void lse_merge(float &m, float &s, float om, float os
     m = mx;
 }
 
-template <int EPI>
+template <int EPI, int WJ>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
+    constexpr int BJ = Tile<WJ>::BJ, B_LOADS = Tile<WJ>::B_LOADS, STAGE = Tile<WJ>::STAGE;
+    constexpr int WSJ = 32 * WJ;                     // columns per wave
     extern __shared__ __align__(16) uint16_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wi = wave >> 1, wj = wave & 1;
@@ -102,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
         it_begin = b / p.n_jtiles;
         it_end = it_begin + 1;
     }
-    const int j0 = jt * kBJ;
+    const int j0 = jt * BJ;
 
     // Per-thread global rows of the staged tiles (rows past the live range
     // are clamped to the last live row; their results are never used).
@@ -123,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
         run_m[bj] = -INFINITY;
         run_s[bj] = 0.f;
         tgt[bj] = -1;
-        const int m = j0 + wj * 64 + bj * 32 + (lane & 31);
+        const int m = j0 + wj * WSJ + bj * 32 + (lane & 31);
         if ((EPI == EPI_FWD || EPI == EPI_GRAD) && m < p.J) {
             const int t = p.targets[m];
             tgt[bj] = (t >= 0 && t < p.V) ? t : -1;
@@ -147,51 +159,99 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 
-        u32x4 ra[A_LOADS], rb[B_LOADS];
-#define VCE_GLOAD(k0)                                                                      \
-    do {                                                                                   \
-        _Pragma("unroll") for (int q = 0; q < A_LOADS; ++q) ra[q] = *(const u32x4 *)(asrc[q] + (k0)); \
-        _Pragma("unroll") for (int q = 0; q < B_LOADS; ++q) rb[q] = *(const u32x4 *)(bsrc[q] + (k0)); \
+        // Global loads run ahead of the MFMAs: two stages with two register
+        // sets (x, y) for the 256 x 128 tile, one stage with one set for the
+        // 256 x 256 tile (whose stage has twice the MFMA work and whose
+        // accumulators leave no room for a second set).
+        u32x4 xa[A_LOADS], xb[B_LOADS];
+        u32x4 ya[WJ == 4 ? 1 : A_LOADS], yb[WJ == 4 ? 1 : B_LOADS];
+#define VCE_GLOAD(RA, RB, k0)                                                               \
+    do {                                                                                    \
+        _Pragma("unroll") for (int q = 0; q < A_LOADS; ++q) RA[q] = *(const u32x4 *)(asrc[q] + (k0)); \
+        _Pragma("unroll") for (int q = 0; q < B_LOADS; ++q) RB[q] = *(const u32x4 *)(bsrc[q] + (k0)); \
     } while (0)
-#define VCE_LSTORE(buf)                                                                    \
-    do {                                                                                   \
-        uint16_t *sa_ = lds + (buf) * STAGE;                                               \
-        uint16_t *sb_ = sa_ + kBI * LDK;                                                   \
-        _Pragma("unroll") for (int q = 0; q < A_LOADS; ++q)                                \
-            *(u32x4 *)(sa_ + (q * 32 + lrow) * LDK + lchunk) = ra[q];                      \
-        _Pragma("unroll") for (int q = 0; q < B_LOADS; ++q)                                \
-            *(u32x4 *)(sb_ + (q * 32 + lrow) * LDK + lchunk) = rb[q];                      \
+#define VCE_LSTORE(RA, RB, buf)                                                             \
+    do {                                                                                    \
+        uint16_t *sa_ = lds + (buf) * STAGE;                                                \
+        uint16_t *sb_ = sa_ + kBI * LDK;                                                    \
+        _Pragma("unroll") for (int q = 0; q < A_LOADS; ++q)                                 \
+            *(u32x4 *)(sa_ + (q * 32 + lrow) * LDK + lchunk) = RA[q];                       \
+        _Pragma("unroll") for (int q = 0; q < B_LOADS; ++q)                                 \
+            *(u32x4 *)(sb_ + (q * 32 + lrow) * LDK + lchunk) = RB[q];                       \
+    } while (0)
+#define VCE_FRAGS(F, G, kk)                                                                 \
+    do {                                                                                    \
+        _Pragma("unroll") for (int bi = 0; bi < WI; ++bi)                                   \
+            F[bi] = *(const bf16x8 *)(sa_ + bi * 32 * LDK + (kk) * 16);                     \
+        _Pragma("unroll") for (int bj = 0; bj < WJ; ++bj)                                   \
+            G[bj] = *(const bf16x8 *)(sb_ + bj * 32 * LDK + (kk) * 16);                     \
+    } while (0)
+#define VCE_MFMAS(F, G)                                                                     \
+    do {                                                                                    \
+        _Pragma("unroll") for (int bi = 0; bi < WI; ++bi)                                   \
+            _Pragma("unroll") for (int bj = 0; bj < WJ; ++bj)                               \
+                acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[bi], G[bj], acc[bi][bj], 0, 0, 0); \
+    } while (0)
+// The fragments of k-step kk+1 are read while the MFMAs of k-step kk run;
+// the scheduling barriers keep the compiler from hoisting every read of
+// the stage (which would need 96 more registers).
+#define VCE_COMPUTE(buf)                                                                    \
+    do {                                                                                    \
+        const uint16_t *sa_ = lds + (buf) * STAGE + (wi * 128 + (lane & 31)) * LDK + (lane >> 5) * 8; \
+        const uint16_t *sb_ = lds + (buf) * STAGE + kBI * LDK + (wj * WSJ + (lane & 31)) * LDK + (lane >> 5) * 8; \
+        bf16x8 f0[WI], g0[WJ], f1[WI], g1[WJ];                                              \
+        VCE_FRAGS(f0, g0, 0);                                                               \
+        VCE_FRAGS(f1, g1, 1);                                                               \
+        VCE_MFMAS(f0, g0);                                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                  \
+        VCE_FRAGS(f0, g0, 2);                                                               \
+        VCE_MFMAS(f1, g1);                                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                  \
+        VCE_FRAGS(f1, g1, 3);                                                               \
+        VCE_MFMAS(f0, g0);                                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                  \
+        VCE_MFMAS(f1, g1);                                                                  \
     } while (0)
 
         __syncthreads();               // the previous tile's epilogue may still read LDS
-        VCE_GLOAD(0);
-        VCE_LSTORE(0);
-        __syncthreads();
-        for (int s = 0; s < nk; ++s) {
-            const int buf = s & 1;
-            if (s + 1 < nk) VCE_GLOAD((s + 1) * kBK);
-            const uint16_t *sa = lds + buf * STAGE + (wi * 128 + (lane & 31)) * LDK + (lane >> 5) * 8;
-            const uint16_t *sb = lds + buf * STAGE + kBI * LDK + (wj * 64 + (lane & 31)) * LDK + (lane >> 5) * 8;
-#pragma unroll
-            for (int kk = 0; kk < kBK / 16; ++kk) {
-                bf16x8 af[WI], bf[WJ];
-#pragma unroll
-                for (int bi = 0; bi < WI; ++bi) af[bi] = *(const bf16x8 *)(sa + bi * 32 * LDK + kk * 16);
-#pragma unroll
-                for (int bj = 0; bj < WJ; ++bj) bf[bj] = *(const bf16x8 *)(sb + bj * 32 * LDK + kk * 16);
-#pragma unroll
-                for (int bi = 0; bi < WI; ++bi)
-#pragma unroll
-                    for (int bj = 0; bj < WJ; ++bj)
-                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
-            }
-            if (s + 1 < nk) VCE_LSTORE(buf ^ 1);
+        if constexpr (WJ == 4) {
+            VCE_GLOAD(xa, xb, 0);
+            VCE_LSTORE(xa, xb, 0);
             __syncthreads();
+            for (int s = 0; s < nk; ++s) {
+                const int buf = s & 1;
+                if (s + 1 < nk) VCE_GLOAD(xa, xb, (s + 1) * kBK);
+                VCE_COMPUTE(buf);
+                if (s + 1 < nk) VCE_LSTORE(xa, xb, buf ^ 1);
+                __syncthreads();
+            }
+        } else {
+            VCE_GLOAD(xa, xb, 0);
+            if (nk > 1) VCE_GLOAD(ya, yb, kBK);
+            VCE_LSTORE(xa, xb, 0);
+            __syncthreads();
+            int s = 0;
+            for (; s + 1 < nk; s += 2) {
+                // stage s from buffer 0; y holds stage s+1, x takes stage s+2
+                if (s + 2 < nk) VCE_GLOAD(xa, xb, (s + 2) * kBK);
+                VCE_COMPUTE(0);
+                VCE_LSTORE(ya, yb, 1);
+                __syncthreads();
+                // stage s+1 from buffer 1; x holds stage s+2, y takes stage s+3
+                if (s + 3 < nk) VCE_GLOAD(ya, yb, (s + 3) * kBK);
+                VCE_COMPUTE(1);
+                if (s + 2 < nk) VCE_LSTORE(xa, xb, 0);
+                __syncthreads();
+            }
+            if (s < nk) {              // an odd stage count ends in buffer 0
+                VCE_COMPUTE(0);
+                __syncthreads();
+            }
         }
 
         // Accumulator (bi, bj, r) of lane l is C[i][j] with
         //   i = i0 + wi*128 + bi*32 + 8*(r/4) + 4*(l/32) + r%4,
-        //   j = j0 + wj*64 + bj*32 + l%32.
+        //   j = j0 + wj*32*WJ + bj*32 + l%32.
         const int ib = i0 + wi * 128 + 4 * (lane >> 5);
         if (EPI == EPI_FWD) {
 #pragma unroll
@@ -228,13 +288,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
                             if (bi == tbi && r == tr) z = acc[bi][bj][r];
-                    p.zt[j0 + wj * 64 + bj * 32 + (lane & 31)] = z;
+                    p.zt[j0 + wj * WSJ + bj * 32 + (lane & 31)] = z;
                 }
             }
         } else if (EPI == EPI_GRAD) {
 #pragma unroll
             for (int bj = 0; bj < WJ; ++bj) {
-                const int m = j0 + wj * 64 + bj * 32 + (lane & 31);
+                const int m = j0 + wj * WSJ + bj * 32 + (lane & 31);
                 const bool live = m < p.J && tgt[bj] >= 0;
                 const float l2 = live ? p.lse[m] * kLog2e : 0.f;
                 const float dl = live ? p.dloss[m] : 0.f;
@@ -248,8 +308,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
                         for (int e = 0; e < 4; ++e) {
                             const int v = vb + e;
                             float x = exp2f(fmaf(acc[bi][bj][r4 * 4 + e], kLog2e, -l2));
-                            x = (v == tgt[bj]) ? x - 1.f : x;
-                            x = (live && v < p.V) ? x * dl : 0.f;
+                            x = (v + p.v_base == tgt[bj]) ? x - 1.f : x;
+                            x = (live && v < p.I) ? x * dl : 0.f;
                             g[e] = to_bf16(x);
                             p.Gt[(int64_t)v * p.ldgt + m] = g[e];
                         }
@@ -262,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
         } else {
 #pragma unroll
             for (int bj = 0; bj < WJ; ++bj) {
-                const int j = j0 + wj * 64 + bj * 32 + (lane & 31);
+                const int j = j0 + wj * WSJ + bj * 32 + (lane & 31);
                 if (j >= p.J) continue;
 #pragma unroll
                 for (int bi = 0; bi < WI; ++bi)
@@ -280,6 +340,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 
 #undef VCE_GLOAD
 #undef VCE_LSTORE
+#undef VCE_COMPUTE
+#undef VCE_FRAGS
+#undef VCE_MFMAS
 
     if (EPI == EPI_FWD) {
         // Merge the two lanes that share each column, then the two waves
@@ -293,15 +356,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
         __syncthreads();
         if (wi == 1 && lane < 32)
 #pragma unroll
-            for (int bj = 0; bj < WJ; ++bj) red[wj * 64 + bj * 32 + lane] = make_float2(run_m[bj], run_s[bj]);
+            for (int bj = 0; bj < WJ; ++bj) red[wj * WSJ + bj * 32 + lane] = make_float2(run_m[bj], run_s[bj]);
         __syncthreads();
         if (wi == 0 && lane < 32) {
             const int split = b / p.n_jtiles;
 #pragma unroll
             for (int bj = 0; bj < WJ; ++bj) {
-                const float2 o = red[wj * 64 + bj * 32 + lane];
+                const float2 o = red[wj * WSJ + bj * 32 + lane];
                 lse_merge(run_m[bj], run_s[bj], o.x, o.y);
-                const int m = j0 + wj * 64 + bj * 32 + lane;
+                const int m = j0 + wj * WSJ + bj * 32 + lane;
                 if (m < p.J) p.part[(int64_t)split * p.J + m] = make_float2(run_m[bj], run_s[bj]);
             }
         }
@@ -345,12 +408,12 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t *in, 
     }
 }
 
-template <int EPI>
+template <int EPI, int WJ>
 hipError_t launch_gemm(const GemmArgs &a, int blocks, hipStream_t stream) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<EPI>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<EPI, WJ>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Tile<WJ>::LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gemm_kernel<EPI>, dim3((unsigned)blocks), dim3(kThreads), kGemmLds, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<EPI, WJ>), dim3((unsigned)blocks), dim3(kThreads), Tile<WJ>::LDS, stream, a);
     return hipGetLastError();
 }
 
@@ -383,7 +446,7 @@ hipError_t launch_forward(const FwdArgs &a, hipStream_t stream) {
     g.n_jtiles = f.n_jtiles;
     g.V = a.V; g.tiles_per_split = f.tiles_per_split; g.n_itiles = f.n_itiles;
     g.targets = a.targets; g.part = a.part; g.zt = a.zt;
-    hipError_t e = launch_gemm<EPI_FWD>(g, f.n_jtiles * f.nsplit, stream);
+    hipError_t e = launch_gemm<EPI_FWD, 4>(g, f.n_jtiles * f.nsplit, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((a.M + 255) / 256)), dim3(256), 0, stream, a.M, a.V,
                        f.nsplit, a.part, a.zt, a.targets, a.loss, a.lse);
@@ -393,38 +456,38 @@ hipError_t launch_forward(const FwdArgs &a, hipStream_t stream) {
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
     hipError_t e;
     const int64_t Vp = round_up(a.V, kBI);
-    const int64_t Mcp = round_up(a.Mc, kBJ);
+    const int64_t Mp = round_up(a.M, kBJ);
+    const int64_t Vcp = round_up(a.Vc, kBI);
     if ((e = launch_transpose(a.w, a.D, a.V, a.D, a.wt, Vp, stream)) != hipSuccess) return e;
-    for (int m0 = 0; m0 < a.M; m0 += a.Mc) {
-        const int mc = a.M - m0 < a.Mc ? a.M - m0 : a.Mc;
-        const int mcp = (int)round_up(mc, kBJ);
-        if ((e = launch_transpose(a.h + (int64_t)m0 * a.D, a.D, mc, a.D, a.ht, Mcp, stream)) != hipSuccess)
-            return e;
+    if ((e = launch_transpose(a.h, a.D, a.M, a.D, a.ht, Mp, stream)) != hipSuccess) return e;
+    for (int v0 = 0; v0 < a.V; v0 += a.Vc) {
+        const int vc = a.V - v0 < a.Vc ? a.V - v0 : a.Vc;
+        const int vcp = (int)round_up(vc, kBI);
 
-        GemmArgs g{};                 // G and G^T of this chunk
-        g.A = a.w; g.lda = a.D; g.I = a.V;
-        g.B = a.h + (int64_t)m0 * a.D; g.ldb = a.D; g.J = mc;
-        g.K = a.D; g.V = a.V;
-        g.n_jtiles = mcp / kBJ;
-        g.targets = a.targets + m0; g.lse = a.lse + m0; g.dloss = a.dloss + m0;
-        g.G = a.g; g.ldg = Vp; g.Gt = a.gt; g.ldgt = Mcp;
-        if ((e = launch_gemm<EPI_GRAD>(g, (int)(Vp / kBI) * g.n_jtiles, stream)) != hipSuccess) return e;
+        GemmArgs g{};                 // G and G^T for vocabulary rows [v0, v0 + vc)
+        g.A = a.w + (int64_t)v0 * a.D; g.lda = a.D; g.I = vc;
+        g.B = a.h; g.ldb = a.D; g.J = a.M;
+        g.K = a.D; g.V = a.V; g.v_base = v0;
+        g.n_jtiles = (int)(Mp / kBJ);
+        g.targets = a.targets; g.lse = a.lse; g.dloss = a.dloss;
+        g.G = a.g; g.ldg = Vcp; g.Gt = a.gt; g.ldgt = Mp;
+        if ((e = launch_gemm<EPI_GRAD, 4>(g, vcp / kBI * g.n_jtiles, stream)) != hipSuccess) return e;
 
-        GemmArgs d{};                 // dh rows of the chunk = G W
-        d.A = a.g; d.lda = Vp; d.I = mc;
-        d.B = a.wt; d.ldb = Vp; d.J = a.D;
-        d.K = (int)Vp;
-        d.n_jtiles = (a.D + kBJ - 1) / kBJ;
-        d.C = a.dh + (int64_t)m0 * a.D; d.ldc = a.D; d.accumulate = 0;
-        if ((e = launch_gemm<EPI_STORE>(d, (mc + kBI - 1) / kBI * d.n_jtiles, stream)) != hipSuccess) return e;
+        GemmArgs d{};                 // dh (+)= G W over the chunk's vocabulary rows
+        d.A = a.g; d.lda = Vcp; d.I = a.M;
+        d.B = a.wt + v0; d.ldb = Vp; d.J = a.D;
+        d.K = vcp;
+        d.n_jtiles = (a.D + 127) / 128;
+        d.C = a.dh; d.ldc = a.D; d.accumulate = v0 > 0;
+        if ((e = launch_gemm<EPI_STORE, 2>(d, (int)(Mp / kBI) * d.n_jtiles, stream)) != hipSuccess) return e;
 
-        GemmArgs w{};                 // dW (+)= G^T h over the chunk
-        w.A = a.gt; w.lda = Mcp; w.I = a.V;
-        w.B = a.ht; w.ldb = Mcp; w.J = a.D;
-        w.K = mcp;
+        GemmArgs w{};                 // dW rows [v0, v0 + vc) = G^T h
+        w.A = a.gt; w.lda = Mp; w.I = vc;
+        w.B = a.ht; w.ldb = Mp; w.J = a.D;
+        w.K = (int)Mp;
         w.n_jtiles = (a.D + kBJ - 1) / kBJ;
-        w.C = a.dw; w.ldc = a.D; w.accumulate = m0 > 0;
-        if ((e = launch_gemm<EPI_STORE>(w, (int)(Vp / kBI) * w.n_jtiles, stream)) != hipSuccess) return e;
+        w.C = a.dw + (int64_t)v0 * a.D; w.ldc = a.D; w.accumulate = 0;
+        if ((e = launch_gemm<EPI_STORE, 4>(w, vcp / kBI * w.n_jtiles, stream)) != hipSuccess) return e;
     }
     return hipSuccess;
 }

@@ -106,23 +106,26 @@ wkv7_status vce_check_sizes(int32_t M, int32_t D, int32_t V) {
 }
 
 struct VceBwdLayout {
-    int32_t Mc;
+    int32_t Vc;
     size_t wt, ht, g, gt, total;     // byte offsets
 };
 
-// [W^T: D x Vp][h_chunk^T: D x Mcp][G: Mcp x Vp][G^T: Vp x Mcp], bf16, each 256-byte aligned.
-wkv7_status vce_bwd_layout(int32_t M, int32_t D, int32_t V, int32_t row_chunk, VceBwdLayout *l) {
+// [W^T: D x Vp][h^T: D x Mp][G: Mp x Vcp][G^T: Vcp x Mp], bf16, each 256-byte aligned.
+wkv7_status vce_bwd_layout(int32_t M, int32_t D, int32_t V, int32_t vocab_chunk, VceBwdLayout *l) {
     wkv7_status st = vce_check_sizes(M, D, V);
     if (st != WKV7_OK) return st;
-    if (row_chunk < 1) return WKV7_ERR_INVALID_ARGUMENT;
-    l->Mc = row_chunk < M ? row_chunk : M;
-    const int64_t Vp = vce::round_up(V, vce::kBI), Mcp = vce::round_up(l->Mc, vce::kBJ);
-    if ((Vp / vce::kBI) * (Mcp / vce::kBJ) > (1 << 24)) return WKV7_ERR_INVALID_ARGUMENT;
+    if (vocab_chunk < 1) return WKV7_ERR_INVALID_ARGUMENT;
+    // whole tiles of kBI vocabulary rows per chunk
+    const int64_t vc = vce::round_up(vocab_chunk < V ? vocab_chunk : V, vce::kBI);
+    l->Vc = (int32_t)(vc < V ? vc : V);
+    const int64_t Vp = vce::round_up(V, vce::kBI), Mp = vce::round_up(M, vce::kBJ);
+    const int64_t Vcp = vce::round_up(l->Vc, vce::kBI);
+    if ((Vcp / vce::kBI) * (Mp / vce::kBJ) > (1 << 24)) return WKV7_ERR_INVALID_ARGUMENT;
     l->wt = 0;
     l->ht = l->wt + pad256((size_t)D * Vp * 2);
-    l->g = l->ht + pad256((size_t)D * Mcp * 2);
-    l->gt = l->g + pad256((size_t)Mcp * Vp * 2);
-    l->total = l->gt + pad256((size_t)Vp * Mcp * 2);
+    l->g = l->ht + pad256((size_t)D * Mp * 2);
+    l->gt = l->g + pad256((size_t)Mp * Vcp * 2);
+    l->total = l->gt + pad256((size_t)Vcp * Mp * 2);
     return WKV7_OK;
 }
 
@@ -330,10 +333,10 @@ wkv7_status vce_forward_workspace_bytes(int32_t M, int32_t D, int32_t V, size_t 
     return WKV7_OK;
 }
 
-wkv7_status vce_backward_workspace_bytes(int32_t M, int32_t D, int32_t V, int32_t row_chunk,
+wkv7_status vce_backward_workspace_bytes(int32_t M, int32_t D, int32_t V, int32_t vocab_chunk,
                                          size_t *bytes) {
     VceBwdLayout l;
-    wkv7_status st = vce_bwd_layout(M, D, V, row_chunk, &l);
+    wkv7_status st = vce_bwd_layout(M, D, V, vocab_chunk, &l);
     if (st != WKV7_OK) return st;
     if (!bytes) return WKV7_ERR_INVALID_ARGUMENT;
     *bytes = l.total;
@@ -373,12 +376,12 @@ wkv7_status vce_forward(int32_t M, int32_t D, int32_t V, const void *h, const vo
     return WKV7_OK;
 }
 
-wkv7_status vce_backward(int32_t M, int32_t D, int32_t V, int32_t row_chunk, const void *h,
+wkv7_status vce_backward(int32_t M, int32_t D, int32_t V, int32_t vocab_chunk, const void *h,
                          const void *w, const int32_t *targets, const float *lse,
                          const float *dloss, float *dh, float *dw, void *workspace,
                          size_t workspace_bytes, void *stream) {
     VceBwdLayout l;
-    wkv7_status st = vce_bwd_layout(M, D, V, row_chunk, &l);
+    wkv7_status st = vce_bwd_layout(M, D, V, vocab_chunk, &l);
     if (st != WKV7_OK) return st;
     if (!h || !w || !aligned16(h) || !aligned16(w)) return WKV7_ERR_INVALID_ARGUMENT;
     if (!targets || !lse || !dloss || !dh || !dw) return WKV7_ERR_INVALID_ARGUMENT;
@@ -400,7 +403,7 @@ wkv7_status vce_backward(int32_t M, int32_t D, int32_t V, int32_t row_chunk, con
     if ((st = check_device()) != WKV7_OK) return st;
     char *ws = (char *)workspace;
     vce::BwdArgs a;
-    a.M = M; a.D = D; a.V = V; a.Mc = l.Mc;
+    a.M = M; a.D = D; a.V = V; a.Vc = l.Vc;
     a.h = (const uint16_t *)h; a.w = (const uint16_t *)w;
     a.targets = targets; a.lse = lse; a.dloss = dloss; a.dh = dh; a.dw = dw;
     a.wt = (uint16_t *)(ws + l.wt); a.ht = (uint16_t *)(ws + l.ht);

@@ -30,10 +30,10 @@ def vce_forward_workspace_bytes(M: int, D: int, V: int) -> int:
     return out.value
 
 
-def vce_backward_workspace_bytes(M: int, D: int, V: int, row_chunk: int) -> int:
+def vce_backward_workspace_bytes(M: int, D: int, V: int, vocab_chunk: int) -> int:
     out = ctypes.c_size_t(0)
     _check("vce_backward_workspace_bytes",
-           _W.lib().vce_backward_workspace_bytes(M, D, V, row_chunk, ctypes.byref(out)))
+           _W.lib().vce_backward_workspace_bytes(M, D, V, vocab_chunk, ctypes.byref(out)))
     return out.value
 
 
@@ -69,9 +69,9 @@ def vce_forward(h, w, targets, *, loss=None, lse=None, workspace=None):
     return loss, lse
 
 
-def vce_backward(h, w, targets, lse, dloss, *, row_chunk: int = 4096, dh=None, dw=None,
+def vce_backward(h, w, targets, lse, dloss, *, vocab_chunk: int = 16384, dh=None, dw=None,
                  workspace=None):
-    """Returns (dh [M, D], dw [V, D]) in fp32; rows are processed row_chunk at a time."""
+    """Returns (dh [M, D], dw [V, D]) in fp32; the vocabulary is processed vocab_chunk rows at a time."""
     torch, dev, M, D, V = _inputs(h, w, targets)
     _W._req(lse, "lse", dev, torch.float32, (M,))
     _W._req(dloss, "dloss", dev, torch.float32, (M,))
@@ -79,8 +79,8 @@ def vce_backward(h, w, targets, lse, dloss, *, row_chunk: int = 4096, dh=None, d
     dw = torch.empty(V, D, dtype=torch.float32, device=dev) if dw is None else dw
     _W._req(dh, "dh", dev, torch.float32, (M, D))
     _W._req(dw, "dw", dev, torch.float32, (V, D))
-    ws = _workspace(torch, dev, vce_backward_workspace_bytes(M, D, V, row_chunk), workspace)
+    ws = _workspace(torch, dev, vce_backward_workspace_bytes(M, D, V, vocab_chunk), workspace)
     _check("vce_backward", _W.lib().vce_backward(
-        M, D, V, row_chunk, _W._ptr(h), _W._ptr(w), _W._ptr(targets), _W._ptr(lse),
+        M, D, V, vocab_chunk, _W._ptr(h), _W._ptr(w), _W._ptr(targets), _W._ptr(lse),
         _W._ptr(dloss), _W._ptr(dh), _W._ptr(dw), _W._ptr(ws), ws.numel(), _W._stream()))
     return dh, dw

@@ -21,7 +21,7 @@ def fwd(M=300, D=128, V=1000, h=P[0], w=P[1], t=P[2], loss=P[3], lse=P[4], ws=P[
     return W.lib().vce_forward(M, D, V, h, w, t, loss, lse, ws, nbytes, None)
 
 
-def bwd(M=300, D=128, V=1000, chunk=128, h=P[0], w=P[1], t=P[2], lse=P[3], dl=P[4], dh=P[5],
+def bwd(M=300, D=128, V=1000, chunk=256, h=P[0], w=P[1], t=P[2], lse=P[3], dl=P[4], dh=P[5],
         dw=P[6], ws=P[7], nbytes=BIG):
     return W.lib().vce_backward(M, D, V, chunk, h, w, t, lse, dl, dh, dw, ws, nbytes, None)
 
@@ -38,16 +38,19 @@ def test_declared_and_exported():
 def test_workspace_queries():
     # forward: one (max, sum) pair per row and split plus the target logits
     assert C.vce_forward_workspace_bytes(16384, 2048, 65536) >= 16384 * 8 + 16384 * 4
-    # backward: W^T, the chunk's h^T, G and G^T, padded to 256 vocabulary rows and 128 token rows
-    Vp, Mcp, D = 65536, 4096, 2048
-    want = 2 * (D * Vp + D * Mcp + 2 * Mcp * Vp)
-    assert C.vce_backward_workspace_bytes(16384, D, 65536, 4096) == want
-    # the chunk is capped at M; the vocabulary pads to a multiple of 256
+    # backward: W^T, h^T, and G and G^T of one vocabulary chunk; vocabulary and
+    # token rows padded to multiples of 256
+    Vp, Mp, Vcp, D = 65536, 16384, 16384, 2048
+    want = 2 * (D * Vp + D * Mp + 2 * Mp * Vcp)
+    assert C.vce_backward_workspace_bytes(16384, D, 65536, 16384) == want
+    # the chunk is rounded up to whole 256-row tiles and capped at V
     assert (C.vce_backward_workspace_bytes(100, 64, 1000, 4096)
-            == 2 * (64 * 1024 + 64 * 128 + 2 * 128 * 1024))
+            == 2 * (64 * 1024 + 64 * 256 + 2 * 256 * 1024))
+    assert (C.vce_backward_workspace_bytes(100, 64, 1000, 300)
+            == 2 * (64 * 1024 + 64 * 256 + 2 * 256 * 512))
     # a smaller chunk needs less
-    assert (C.vce_backward_workspace_bytes(16384, D, 65536, 1024)
-            < C.vce_backward_workspace_bytes(16384, D, 65536, 4096))
+    assert (C.vce_backward_workspace_bytes(16384, D, 65536, 4096)
+            < C.vce_backward_workspace_bytes(16384, D, 65536, 16384))
 
 
 @pytest.mark.parametrize("M,D,V", [(0, 128, 10), (-1, 128, 10), ((1 << 28) + 1, 128, 10),
@@ -85,7 +88,7 @@ def test_backward_rejects_bad_arguments():
     assert bwd(dw=ctypes.c_void_p(P[5].value + 1024)) == INVALID   # overlaps dh
     assert bwd(dh=ctypes.c_void_p(P[0].value + 1024)) == INVALID   # overlaps h
     assert bwd(ws=ctypes.c_void_p(P[6].value + 4096)) == INVALID   # overlaps dw
-    need = C.vce_backward_workspace_bytes(300, 128, 1000, 128)
+    need = C.vce_backward_workspace_bytes(300, 128, 1000, 256)
     assert bwd(nbytes=need - 1) == WS
-    # a huge vocabulary tiled with a huge chunk exceeds the launchable grid
-    assert bwd(M=1 << 26, V=1 << 24, chunk=1 << 26) == INVALID
+    # many token rows tiled with a huge vocabulary chunk exceed the launchable grid
+    assert bwd(M=1 << 26, V=1 << 24, chunk=1 << 24) == INVALID
