@@ -25,18 +25,19 @@
 //         dimension. Chunking the vocabulary (not the rows) leaves only the
 //         smaller dh [M, D] to accumulate.
 //
-// The core: 256 threads as 2 x 2 waves, macro tile 256 x 256, wave tile
-// 128 x 128 = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32
-// accumulators per lane; per k-step a wave reads 8 operand fragments for 16
-// MFMAs). The dh product, whose chunk gives few row tiles, uses 256 x 128
-// macro tiles (4 x 2 blocks per wave) so that it still fills the chip. Operands go global -> registers -> LDS, 64 along k
-// per stage, double-buffered in LDS with one barrier per stage; the global
-// loads run two stages ahead (two register sets), so they have the MFMA time
-// of two stages to land. LDS rows are padded to
-// 72 elements (144 B), so the 16-byte operand reads of 16 consecutive rows
-// cover all 64 banks once. Workgroup ids are remapped so that the
-// workgroups on one XCD (ids are dealt to the 8 XCDs in turn) take
-// consecutive tiles and share their A tile in that XCD's L2.
+// The core: macro tile 256 x 256 of v_mfma_f32_32x32x16_bf16 blocks, as
+// 2 x 4 waves with 128 x 64 wave tiles (two waves per SIMD) or 2 x 2 waves
+// with 128 x 128 wave tiles (one wave per SIMD, 256 accumulators per lane);
+// the product picks the shape. Operands go global -> registers -> LDS, 64
+// along k per stage, double-buffered in LDS with one barrier per stage: the
+// global loads of stage s+1 are in flight while the MFMAs of stage s run,
+// and the fragments of k-step kk+1 are read from LDS between the MFMAs of
+// k-step kk. LDS rows are padded to 72 elements (144 B), so the 16-byte
+// operand reads of consecutive rows fall in distinct banks. Workgroup ids
+// are remapped so that the workgroups on one XCD (ids are dealt to the 8
+// XCDs in turn) take consecutive tiles, and in the backward products each
+// run of 32 of them covers a 4 x 8 block of tiles, sharing A and B tiles in
+// that XCD's L2.
 #include "vce_kernels.h"
 
 namespace vce {
@@ -46,21 +47,32 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // plain vector: stays in registers
 
-constexpr int kThreads = 256;
 constexpr int LDK = kBK + 8;                         // LDS row stride (elements)
 constexpr int WI = 4;                                // 32 x 32 blocks per wave along i
-constexpr int A_LOADS = kBI * kBK / 8 / kThreads;    // 16-byte loads per thread and stage
-// Along j a wave holds WJ blocks (WJ = 4: 256 x 256 macro tile; WJ = 2: 256 x 128).
-template <int WJ> struct Tile {
-    static constexpr int BJ = 64 * WJ;
-    static constexpr int B_LOADS = BJ * kBK / 8 / kThreads;
-    static constexpr int STAGE = (kBI + BJ) * LDK;             // elements per stage
+// A workgroup is 2 x NWJ waves; along j a wave holds WJ blocks. Used shapes:
+//   WJ = 4, NWJ = 2: 256 threads, 256 x 256 macro tile (one wave per SIMD);
+//   WJ = 2, NWJ = 4: 512 threads, 256 x 256 macro tile (two waves per SIMD).
+template <int WJ, int NWJ> struct Cfg {
+    static constexpr int THREADS = 128 * NWJ;
+    static constexpr int BJ = 32 * WJ * NWJ;
+    static constexpr int RPL = THREADS / 8;                      // tile rows per load instruction
+    static constexpr int A_LOADS = kBI * kBK / 8 / THREADS;      // 16-byte loads per thread and stage
+    static constexpr int B_LOADS = BJ * kBK / 8 / THREADS;
+    static constexpr int STAGE = (kBI + BJ) * LDK;               // elements per stage
     static constexpr size_t LDS = 2 * STAGE * sizeof(uint16_t);
 };
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 enum { EPI_FWD = 0, EPI_GRAD = 1, EPI_STORE = 2 };
+// Shapes per product (measured): the logit tiles of the forward and the two
+// gradient products run 8 waves (two per SIMD hide each other's barrier and
+// load waits); the gradient-tile kernel keeps 4 waves with 256 accumulators
+// per lane, since its epilogue needs the registers a second wave would take.
+#define VCE_FWD_CFG 2, 4
+#define VCE_GRAD_CFG 4, 2
+#define VCE_DW_CFG 2, 4
+#define VCE_DH_CFG 2, 4
 
 struct GemmArgs {
     const uint16_t *A, *B;
@@ -87,6 +99,21 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
     return (n & 7) ? b : (b & 7) * (n >> 3) + (b >> 3);
 }
 
+// Tile (ti, tj) of logical workgroup b in an n_i x n_j grid. Each run of 32
+// consecutive ids -- the workgroups one XCD holds at a time -- covers a
+// 4 x 8 block of tiles, so that they share 4 A tiles and 8 B tiles in that
+// XCD's L2 instead of 1 A tile and 32 B tiles.
+__device__ __forceinline__ void tile_of(int b, int n_i, int n_j, int &ti, int &tj) {
+    if ((n_i & 3) == 0 && (n_j & 7) == 0) {
+        const int g = b >> 5, w = b & 31, ngj = n_j >> 3;
+        ti = (g / ngj) * 4 + (w >> 3);
+        tj = (g % ngj) * 8 + (w & 7);
+        return;
+    }
+    ti = b / n_j;
+    tj = b % n_j;
+}
+
 __device__ __forceinline__ uint16_t to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // (max, sum) pairs in base-2 units: sum_x 2^(x - max).
@@ -97,21 +124,28 @@ __device__ __forceinline__ void lse_merge(float &m, float &s, float om, float os
     m = mx;
 }
 
-template <int EPI, int WJ>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
-    constexpr int BJ = Tile<WJ>::BJ, B_LOADS = Tile<WJ>::B_LOADS, STAGE = Tile<WJ>::STAGE;
+template <int EPI, int WJ, int NWJ>
+__global__ __launch_bounds__(128 * NWJ) void gemm_kernel(GemmArgs p) {   // Cfg::THREADS
+    using C = Cfg<WJ, NWJ>;
+    constexpr int BJ = C::BJ, A_LOADS = C::A_LOADS, B_LOADS = C::B_LOADS, STAGE = C::STAGE, RPL = C::RPL;
     constexpr int WSJ = 32 * WJ;                     // columns per wave
     extern __shared__ __align__(16) uint16_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wi = wave >> 1, wj = wave & 1;
+    const int wi = wave / NWJ, wj = wave % NWJ;
     const int b = xcd_remap(blockIdx.x, gridDim.x);
-    const int jt = b % p.n_jtiles;
+    int ti, jt;                    // FWD: ti = vocabulary split; else the row tile of A
+    if (EPI == EPI_FWD) {            // measured: the grouping does not help the forward
+        ti = b / p.n_jtiles;
+        jt = b % p.n_jtiles;
+    } else {
+        tile_of(b, gridDim.x / p.n_jtiles, p.n_jtiles, ti, jt);
+    }
     int it_begin, it_end;
     if (EPI == EPI_FWD) {
-        it_begin = (b / p.n_jtiles) * p.tiles_per_split;
+        it_begin = ti * p.tiles_per_split;
         it_end = min(it_begin + p.tiles_per_split, p.n_itiles);
     } else {
-        it_begin = b / p.n_jtiles;
+        it_begin = ti;
         it_end = it_begin + 1;
     }
     const int j0 = jt * BJ;
@@ -122,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
     const uint16_t *bsrc[B_LOADS];
 #pragma unroll
     for (int q = 0; q < B_LOADS; ++q) {
-        const int gj = min(j0 + q * 32 + lrow, p.J - 1);
+        const int gj = min(j0 + q * RPL + lrow, p.J - 1);
         bsrc[q] = p.B + (int64_t)gj * p.ldb + lchunk;
     }
 
@@ -148,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
         const uint16_t *asrc[A_LOADS];
 #pragma unroll
         for (int q = 0; q < A_LOADS; ++q) {
-            const int gi = min(i0 + q * 32 + lrow, p.I - 1);
+            const int gi = min(i0 + q * RPL + lrow, p.I - 1);
             asrc[q] = p.A + (int64_t)gi * p.lda + lchunk;
         }
         f32x16 acc[WI][WJ];
@@ -159,12 +193,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 
-        // Global loads run ahead of the MFMAs: two stages with two register
-        // sets (x, y) for the 256 x 128 tile, one stage with one set for the
-        // 256 x 256 tile (whose stage has twice the MFMA work and whose
-        // accumulators leave no room for a second set).
+        // Global loads run one stage ahead of the MFMAs (one register set;
+        // the accumulators leave no room for a second).
         u32x4 xa[A_LOADS], xb[B_LOADS];
-        u32x4 ya[WJ == 4 ? 1 : A_LOADS], yb[WJ == 4 ? 1 : B_LOADS];
 #define VCE_GLOAD(RA, RB, k0)                                                               \
     do {                                                                                    \
         _Pragma("unroll") for (int q = 0; q < A_LOADS; ++q) RA[q] = *(const u32x4 *)(asrc[q] + (k0)); \
@@ -175,9 +206,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
         uint16_t *sa_ = lds + (buf) * STAGE;                                                \
         uint16_t *sb_ = sa_ + kBI * LDK;                                                    \
         _Pragma("unroll") for (int q = 0; q < A_LOADS; ++q)                                 \
-            *(u32x4 *)(sa_ + (q * 32 + lrow) * LDK + lchunk) = RA[q];                       \
+            *(u32x4 *)(sa_ + (q * RPL + lrow) * LDK + lchunk) = RA[q];                       \
         _Pragma("unroll") for (int q = 0; q < B_LOADS; ++q)                                 \
-            *(u32x4 *)(sb_ + (q * 32 + lrow) * LDK + lchunk) = RB[q];                       \
+            *(u32x4 *)(sb_ + (q * RPL + lrow) * LDK + lchunk) = RB[q];                       \
     } while (0)
 #define VCE_FRAGS(F, G, kk)                                                                 \
     do {                                                                                    \
@@ -195,58 +226,45 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 // The fragments of k-step kk+1 are read while the MFMAs of k-step kk run;
 // the scheduling barriers keep the compiler from hoisting every read of
 // the stage (which would need 96 more registers).
+// One k-step: the MFMAs of (F, G) with the reads of the next fragments
+// (FN, GN) spread between them, one read after each of the first MFMAs.
+#define VCE_STEP(F, G, FN, GN, kkn)                                                          \
+    do {                                                                                    \
+        VCE_FRAGS(FN, GN, kkn);                                                             \
+        VCE_MFMAS(F, G);                                                                    \
+        _Pragma("unroll") for (int q_ = 0; q_ < WI + WJ; ++q_) {                            \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                              \
+        }                                                                                   \
+        __builtin_amdgcn_sched_group_barrier(0x008, WI * WJ - WI - WJ, 0);                  \
+        __builtin_amdgcn_sched_barrier(0);                                                  \
+    } while (0)
+// The fragments of k-step kk+1 are read while the MFMAs of k-step kk run;
+// the scheduling barriers keep the compiler from hoisting every read of
+// the stage (which would need 96 more registers).
 #define VCE_COMPUTE(buf)                                                                    \
     do {                                                                                    \
         const uint16_t *sa_ = lds + (buf) * STAGE + (wi * 128 + (lane & 31)) * LDK + (lane >> 5) * 8; \
         const uint16_t *sb_ = lds + (buf) * STAGE + kBI * LDK + (wj * WSJ + (lane & 31)) * LDK + (lane >> 5) * 8; \
         bf16x8 f0[WI], g0[WJ], f1[WI], g1[WJ];                                              \
         VCE_FRAGS(f0, g0, 0);                                                               \
-        VCE_FRAGS(f1, g1, 1);                                                               \
-        VCE_MFMAS(f0, g0);                                                                  \
         __builtin_amdgcn_sched_barrier(0);                                                  \
-        VCE_FRAGS(f0, g0, 2);                                                               \
-        VCE_MFMAS(f1, g1);                                                                  \
-        __builtin_amdgcn_sched_barrier(0);                                                  \
-        VCE_FRAGS(f1, g1, 3);                                                               \
-        VCE_MFMAS(f0, g0);                                                                  \
-        __builtin_amdgcn_sched_barrier(0);                                                  \
+        VCE_STEP(f0, g0, f1, g1, 1);                                                        \
+        VCE_STEP(f1, g1, f0, g0, 2);                                                        \
+        VCE_STEP(f0, g0, f1, g1, 3);                                                        \
         VCE_MFMAS(f1, g1);                                                                  \
     } while (0)
 
         __syncthreads();               // the previous tile's epilogue may still read LDS
-        if constexpr (WJ == 4) {
-            VCE_GLOAD(xa, xb, 0);
-            VCE_LSTORE(xa, xb, 0);
+        VCE_GLOAD(xa, xb, 0);
+        VCE_LSTORE(xa, xb, 0);
+        __syncthreads();
+        for (int s = 0; s < nk; ++s) {
+            const int buf = s & 1;
+            if (s + 1 < nk) VCE_GLOAD(xa, xb, (s + 1) * kBK);
+            VCE_COMPUTE(buf);
+            if (s + 1 < nk) VCE_LSTORE(xa, xb, buf ^ 1);
             __syncthreads();
-            for (int s = 0; s < nk; ++s) {
-                const int buf = s & 1;
-                if (s + 1 < nk) VCE_GLOAD(xa, xb, (s + 1) * kBK);
-                VCE_COMPUTE(buf);
-                if (s + 1 < nk) VCE_LSTORE(xa, xb, buf ^ 1);
-                __syncthreads();
-            }
-        } else {
-            VCE_GLOAD(xa, xb, 0);
-            if (nk > 1) VCE_GLOAD(ya, yb, kBK);
-            VCE_LSTORE(xa, xb, 0);
-            __syncthreads();
-            int s = 0;
-            for (; s + 1 < nk; s += 2) {
-                // stage s from buffer 0; y holds stage s+1, x takes stage s+2
-                if (s + 2 < nk) VCE_GLOAD(xa, xb, (s + 2) * kBK);
-                VCE_COMPUTE(0);
-                VCE_LSTORE(ya, yb, 1);
-                __syncthreads();
-                // stage s+1 from buffer 1; x holds stage s+2, y takes stage s+3
-                if (s + 3 < nk) VCE_GLOAD(ya, yb, (s + 3) * kBK);
-                VCE_COMPUTE(1);
-                if (s + 2 < nk) VCE_LSTORE(xa, xb, 0);
-                __syncthreads();
-            }
-            if (s < nk) {              // an odd stage count ends in buffer 0
-                VCE_COMPUTE(0);
-                __syncthreads();
-            }
         }
 
         // Accumulator (bi, bj, r) of lane l is C[i][j] with
@@ -341,6 +359,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 #undef VCE_GLOAD
 #undef VCE_LSTORE
 #undef VCE_COMPUTE
+#undef VCE_STEP
 #undef VCE_FRAGS
 #undef VCE_MFMAS
 
@@ -359,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
             for (int bj = 0; bj < WJ; ++bj) red[wj * WSJ + bj * 32 + lane] = make_float2(run_m[bj], run_s[bj]);
         __syncthreads();
         if (wi == 0 && lane < 32) {
-            const int split = b / p.n_jtiles;
+            const int split = ti;
 #pragma unroll
             for (int bj = 0; bj < WJ; ++bj) {
                 const float2 o = red[wj * WSJ + bj * 32 + lane];
@@ -408,12 +427,13 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t *in, 
     }
 }
 
-template <int EPI, int WJ>
+template <int EPI, int WJ, int NWJ>
 hipError_t launch_gemm(const GemmArgs &a, int blocks, hipStream_t stream) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<EPI, WJ>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Tile<WJ>::LDS);
+    using C = Cfg<WJ, NWJ>;
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<EPI, WJ, NWJ>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_kernel<EPI, WJ>), dim3((unsigned)blocks), dim3(kThreads), Tile<WJ>::LDS, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<EPI, WJ, NWJ>), dim3((unsigned)blocks), dim3(C::THREADS), C::LDS, stream, a);
     return hipGetLastError();
 }
 
@@ -446,7 +466,7 @@ hipError_t launch_forward(const FwdArgs &a, hipStream_t stream) {
     g.n_jtiles = f.n_jtiles;
     g.V = a.V; g.tiles_per_split = f.tiles_per_split; g.n_itiles = f.n_itiles;
     g.targets = a.targets; g.part = a.part; g.zt = a.zt;
-    hipError_t e = launch_gemm<EPI_FWD, 4>(g, f.n_jtiles * f.nsplit, stream);
+    hipError_t e = launch_gemm<EPI_FWD, VCE_FWD_CFG>(g, f.n_jtiles * f.nsplit, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((a.M + 255) / 256)), dim3(256), 0, stream, a.M, a.V,
                        f.nsplit, a.part, a.zt, a.targets, a.loss, a.lse);
@@ -471,23 +491,23 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
         g.n_jtiles = (int)(Mp / kBJ);
         g.targets = a.targets; g.lse = a.lse; g.dloss = a.dloss;
         g.G = a.g; g.ldg = Vcp; g.Gt = a.gt; g.ldgt = Mp;
-        if ((e = launch_gemm<EPI_GRAD, 4>(g, vcp / kBI * g.n_jtiles, stream)) != hipSuccess) return e;
+        if ((e = launch_gemm<EPI_GRAD, VCE_GRAD_CFG>(g, vcp / kBI * g.n_jtiles, stream)) != hipSuccess) return e;
 
         GemmArgs d{};                 // dh (+)= G W over the chunk's vocabulary rows
         d.A = a.g; d.lda = Vcp; d.I = a.M;
         d.B = a.wt + v0; d.ldb = Vp; d.J = a.D;
         d.K = vcp;
-        d.n_jtiles = (a.D + 127) / 128;
+        d.n_jtiles = (a.D + Cfg<VCE_DH_CFG>::BJ - 1) / Cfg<VCE_DH_CFG>::BJ;
         d.C = a.dh; d.ldc = a.D; d.accumulate = v0 > 0;
-        if ((e = launch_gemm<EPI_STORE, 2>(d, (int)(Mp / kBI) * d.n_jtiles, stream)) != hipSuccess) return e;
+        if ((e = launch_gemm<EPI_STORE, VCE_DH_CFG>(d, (int)(Mp / kBI) * d.n_jtiles, stream)) != hipSuccess) return e;
 
         GemmArgs w{};                 // dW rows [v0, v0 + vc) = G^T h
         w.A = a.gt; w.lda = Mp; w.I = vc;
         w.B = a.ht; w.ldb = Mp; w.J = a.D;
         w.K = (int)Mp;
-        w.n_jtiles = (a.D + kBJ - 1) / kBJ;
+        w.n_jtiles = (a.D + Cfg<VCE_DW_CFG>::BJ - 1) / Cfg<VCE_DW_CFG>::BJ;
         w.C = a.dw + (int64_t)v0 * a.D; w.ldc = a.D; w.accumulate = 0;
-        if ((e = launch_gemm<EPI_STORE, 4>(w, vcp / kBI * w.n_jtiles, stream)) != hipSuccess) return e;
+        if ((e = launch_gemm<EPI_STORE, VCE_DW_CFG>(w, vcp / kBI * w.n_jtiles, stream)) != hipSuccess) return e;
     }
     return hipSuccess;
 }
