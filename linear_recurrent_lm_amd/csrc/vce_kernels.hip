@@ -26,9 +26,8 @@
 //         smaller dh [M, D] to accumulate.
 //
 // The core: macro tile 256 x 256 of v_mfma_f32_32x32x16_bf16 blocks, as
-// 2 x 4 waves with 128 x 64 wave tiles (two waves per SIMD) or 2 x 2 waves
-// with 128 x 128 wave tiles (one wave per SIMD, 256 accumulators per lane);
-// the product picks the shape. Operands go global -> registers -> LDS, 64
+// 2 x 4 waves with 128 x 64 wave tiles (two waves per SIMD, 128 fp32
+// accumulators per lane). Operands go global -> registers -> LDS, 64
 // along k per stage, double-buffered in LDS with one barrier per stage: the
 // global loads of stage s+1 are in flight while the MFMAs of stage s run,
 // and the fragments of k-step kk+1 are read from LDS between the MFMAs of
@@ -49,9 +48,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // plain vector: s
 
 constexpr int LDK = kBK + 8;                         // LDS row stride (elements)
 constexpr int WI = 4;                                // 32 x 32 blocks per wave along i
-// A workgroup is 2 x NWJ waves; along j a wave holds WJ blocks. Used shapes:
-//   WJ = 4, NWJ = 2: 256 threads, 256 x 256 macro tile (one wave per SIMD);
-//   WJ = 2, NWJ = 4: 512 threads, 256 x 256 macro tile (two waves per SIMD).
+// A workgroup is 2 x NWJ waves; along j a wave holds WJ blocks (in use:
+// WJ = 2, NWJ = 4: 512 threads, 256 x 256 macro tile, two waves per SIMD).
 template <int WJ, int NWJ> struct Cfg {
     static constexpr int THREADS = 128 * NWJ;
     static constexpr int BJ = 32 * WJ * NWJ;
@@ -65,14 +63,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 enum { EPI_FWD = 0, EPI_GRAD = 1, EPI_STORE = 2 };
-// Shapes per product (measured): the logit tiles of the forward and the two
-// gradient products run 8 waves (two per SIMD hide each other's barrier and
-// load waits); the gradient-tile kernel keeps 4 waves with 256 accumulators
-// per lane, since its epilogue needs the registers a second wave would take.
-#define VCE_FWD_CFG 2, 4
-#define VCE_GRAD_CFG 4, 2
-#define VCE_DW_CFG 2, 4
-#define VCE_DH_CFG 2, 4
+// Every product runs 2 x 4 waves with 128 x 64 wave tiles: two waves per
+// SIMD hide each other's barrier and load waits (measured faster than 2 x 2
+// waves with 256 accumulators per lane for each of the four products).
+#define VCE_SHAPE 2, 4
 
 struct GemmArgs {
     const uint16_t *A, *B;
@@ -310,32 +304,47 @@ __global__ __launch_bounds__(128 * NWJ) void gemm_kernel(GemmArgs p) {   // Cfg:
                 }
             }
         } else if (EPI == EPI_GRAD) {
+            // G [m][v]: each lane holds 4 consecutive v of one m, one 8-byte
+            // store. G^T [v][m]: neighbouring lanes hold neighbouring m, so an
+            // even lane stores (m, m+1) of one row and its odd neighbour
+            // (m-1, m) of the next, after one lane exchange: 4-byte stores.
+            const bool odd = lane & 1;
 #pragma unroll
             for (int bj = 0; bj < WJ; ++bj) {
                 const int m = j0 + wj * WSJ + bj * 32 + (lane & 31);
                 const bool live = m < p.J && tgt[bj] >= 0;
                 const float l2 = live ? p.lse[m] * kLog2e : 0.f;
                 const float dl = live ? p.dloss[m] : 0.f;
+                const int tl = tgt[bj] - p.v_base;       // target as a local row
+                uint16_t *gcol = p.G + (int64_t)m * p.ldg;
+                uint16_t *gtcol = p.Gt + (m & ~1);
 #pragma unroll
-                for (int bi = 0; bi < WI; ++bi)
+                for (int bi = 0; bi < WI; ++bi) {
 #pragma unroll
                     for (int r4 = 0; r4 < 4; ++r4) {
                         const int vb = ib + bi * 32 + 8 * r4;
-                        uint16_t g[4];
+                        uint32_t g[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int v = vb + e;
                             float x = exp2f(fmaf(acc[bi][bj][r4 * 4 + e], kLog2e, -l2));
-                            x = (v + p.v_base == tgt[bj]) ? x - 1.f : x;
+                            x = (v == tl) ? x - 1.f : x;
                             x = (live && v < p.I) ? x * dl : 0.f;
                             g[e] = to_bf16(x);
-                            p.Gt[(int64_t)v * p.ldgt + m] = g[e];
                         }
                         uint2 pk;
-                        pk.x = (uint32_t)g[0] | ((uint32_t)g[1] << 16);
-                        pk.y = (uint32_t)g[2] | ((uint32_t)g[3] << 16);
-                        *(uint2 *)(p.G + (int64_t)m * p.ldg + vb) = pk;
+                        pk.x = g[0] | (g[1] << 16);
+                        pk.y = g[2] | (g[3] << 16);
+                        *(uint2 *)(gcol + vb) = pk;
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const uint32_t recv = __shfl_xor(odd ? g[2 * q] : g[2 * q + 1], 1);
+                            const uint32_t word = odd ? (recv | (g[2 * q + 1] << 16)) : (g[2 * q] | (recv << 16));
+                            *(uint32_t *)(gtcol + (int64_t)(vb + 2 * q + (odd ? 1 : 0)) * p.ldgt) = word;
+                        }
                     }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         } else {
 #pragma unroll
@@ -466,7 +475,7 @@ hipError_t launch_forward(const FwdArgs &a, hipStream_t stream) {
     g.n_jtiles = f.n_jtiles;
     g.V = a.V; g.tiles_per_split = f.tiles_per_split; g.n_itiles = f.n_itiles;
     g.targets = a.targets; g.part = a.part; g.zt = a.zt;
-    hipError_t e = launch_gemm<EPI_FWD, VCE_FWD_CFG>(g, f.n_jtiles * f.nsplit, stream);
+    hipError_t e = launch_gemm<EPI_FWD, VCE_SHAPE>(g, f.n_jtiles * f.nsplit, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((a.M + 255) / 256)), dim3(256), 0, stream, a.M, a.V,
                        f.nsplit, a.part, a.zt, a.targets, a.loss, a.lse);
@@ -491,23 +500,23 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
         g.n_jtiles = (int)(Mp / kBJ);
         g.targets = a.targets; g.lse = a.lse; g.dloss = a.dloss;
         g.G = a.g; g.ldg = Vcp; g.Gt = a.gt; g.ldgt = Mp;
-        if ((e = launch_gemm<EPI_GRAD, VCE_GRAD_CFG>(g, vcp / kBI * g.n_jtiles, stream)) != hipSuccess) return e;
+        if ((e = launch_gemm<EPI_GRAD, VCE_SHAPE>(g, vcp / kBI * g.n_jtiles, stream)) != hipSuccess) return e;
 
         GemmArgs d{};                 // dh (+)= G W over the chunk's vocabulary rows
         d.A = a.g; d.lda = Vcp; d.I = a.M;
         d.B = a.wt + v0; d.ldb = Vp; d.J = a.D;
         d.K = vcp;
-        d.n_jtiles = (a.D + Cfg<VCE_DH_CFG>::BJ - 1) / Cfg<VCE_DH_CFG>::BJ;
+        d.n_jtiles = (a.D + Cfg<VCE_SHAPE>::BJ - 1) / Cfg<VCE_SHAPE>::BJ;
         d.C = a.dh; d.ldc = a.D; d.accumulate = v0 > 0;
-        if ((e = launch_gemm<EPI_STORE, VCE_DH_CFG>(d, (int)(Mp / kBI) * d.n_jtiles, stream)) != hipSuccess) return e;
+        if ((e = launch_gemm<EPI_STORE, VCE_SHAPE>(d, (int)(Mp / kBI) * d.n_jtiles, stream)) != hipSuccess) return e;
 
         GemmArgs w{};                 // dW rows [v0, v0 + vc) = G^T h
         w.A = a.gt; w.lda = Mp; w.I = vc;
         w.B = a.ht; w.ldb = Mp; w.J = a.D;
         w.K = (int)Mp;
-        w.n_jtiles = (a.D + Cfg<VCE_DW_CFG>::BJ - 1) / Cfg<VCE_DW_CFG>::BJ;
+        w.n_jtiles = (a.D + Cfg<VCE_SHAPE>::BJ - 1) / Cfg<VCE_SHAPE>::BJ;
         w.C = a.dw + (int64_t)v0 * a.D; w.ldc = a.D; w.accumulate = 0;
-        if ((e = launch_gemm<EPI_STORE, VCE_DW_CFG>(w, vcp / kBI * w.n_jtiles, stream)) != hipSuccess) return e;
+        if ((e = launch_gemm<EPI_STORE, VCE_SHAPE>(w, vcp / kBI * w.n_jtiles, stream)) != hipSuccess) return e;
     }
     return hipSuccess;
 }
