@@ -304,19 +304,23 @@ __global__ __launch_bounds__(128 * NWJ) void gemm_kernel(GemmArgs p) {   // Cfg:
                 }
             }
         } else if (EPI == EPI_GRAD) {
-            // G [m][v]: each lane holds 4 consecutive v of one m, one 8-byte
-            // store. G^T [v][m]: neighbouring lanes hold neighbouring m, so an
-            // even lane stores (m, m+1) of one row and its odd neighbour
-            // (m-1, m) of the next, after one lane exchange: 4-byte stores.
+            // G^T [v][m]: neighbouring lanes hold neighbouring m, so an even
+            // lane stores (m, m+1) of one row and its odd neighbour (m-1, m)
+            // of the next, after one lane exchange: 4-byte stores.
+            // G [m][v]: a lane holds 4 consecutive v of one m; they go to LDS
+            // as the tile [m][v] and leave as 16-byte row segments (a direct
+            // store would touch a different row in every lane).
+            constexpr int TLD = kBI + 8;                 // LDS row stride of the [m][v] tile
             const bool odd = lane & 1;
 #pragma unroll
             for (int bj = 0; bj < WJ; ++bj) {
-                const int m = j0 + wj * WSJ + bj * 32 + (lane & 31);
+                const int ml = wj * WSJ + bj * 32 + (lane & 31);
+                const int m = j0 + ml;
                 const bool live = m < p.J && tgt[bj] >= 0;
                 const float l2 = live ? p.lse[m] * kLog2e : 0.f;
                 const float dl = live ? p.dloss[m] : 0.f;
                 const int tl = tgt[bj] - p.v_base;       // target as a local row
-                uint16_t *gcol = p.G + (int64_t)m * p.ldg;
+                uint16_t *trow = lds + ml * TLD + wi * 128 + 4 * (lane >> 5);
                 uint16_t *gtcol = p.Gt + (m & ~1);
 #pragma unroll
                 for (int bi = 0; bi < WI; ++bi) {
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(128 * NWJ) void gemm_kernel(GemmArgs p) {   // Cfg:
                         uint2 pk;
                         pk.x = g[0] | (g[1] << 16);
                         pk.y = g[2] | (g[3] << 16);
-                        *(uint2 *)(gcol + vb) = pk;
+                        *(uint2 *)(trow + bi * 32 + 8 * r4) = pk;
 #pragma unroll
                         for (int q = 0; q < 2; ++q) {
                             const uint32_t recv = __shfl_xor(odd ? g[2 * q] : g[2 * q + 1], 1);
@@ -345,6 +349,14 @@ __global__ __launch_bounds__(128 * NWJ) void gemm_kernel(GemmArgs p) {   // Cfg:
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
+            }
+            __syncthreads();
+            constexpr int CPR = kBI / 8;                 // 16-byte segments per row
+#pragma unroll 4
+            for (int c = tid; c < BJ * CPR; c += C::THREADS) {
+                const int row = c / CPR, seg = c % CPR;
+                const u32x4 val = *(const u32x4 *)(lds + row * TLD + seg * 8);
+                *(u32x4 *)(p.G + (int64_t)(j0 + row) * p.ldg + i0 + seg * 8) = val;
             }
         } else {
 #pragma unroll
