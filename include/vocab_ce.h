@@ -52,8 +52,10 @@ extern "C" {
 
 /*
  * Sizes accepted by every call: 1 <= M <= 2^28, 64 <= D <= 65536 with D a
- * multiple of 64, 1 <= V <= 2^24, 1 <= vocab_chunk. Anything else:
- * WKV7_ERR_INVALID_ARGUMENT.
+ * multiple of 64, 1 <= V <= 2^24, 1 <= vocab_chunk, and no launch of more
+ * than 2^22 workgroups: with 256 x 256 tiles, ceil(M/256) * ceil(chunk/256),
+ * ceil(M/256) * ceil(D/256) and ceil(chunk/256) * ceil(D/256) are each at
+ * most 2^22. Anything else: WKV7_ERR_INVALID_ARGUMENT.
  */
 
 /* Workspace bytes of vce_forward for (M, D, V); *bytes is written on success. */

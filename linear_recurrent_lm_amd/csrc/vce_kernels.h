@@ -16,6 +16,10 @@ constexpr int kBK = 64;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// Largest grid (workgroups) a launch may take: 2^22 workgroups of at most 512
+// threads keep every launch below 2^31 threads.
+constexpr int64_t kMaxBlocks = (int64_t)1 << 22;
+
 // Forward split of the vocabulary: enough workgroups to fill the chip.
 struct FwdPlan {
     int n_itiles, n_jtiles, nsplit, tiles_per_split;

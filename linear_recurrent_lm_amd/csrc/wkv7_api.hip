@@ -102,6 +102,8 @@ wkv7_status vce_check_sizes(int32_t M, int32_t D, int32_t V) {
     if (M < 1 || M > (1 << 28)) return WKV7_ERR_INVALID_ARGUMENT;
     if (D < 64 || D > 65536 || D % 64 != 0) return WKV7_ERR_INVALID_ARGUMENT;
     if (V < 1 || V > (1 << 24)) return WKV7_ERR_INVALID_ARGUMENT;
+    const vce::FwdPlan f = vce::fwd_plan(M, V);
+    if ((int64_t)f.n_jtiles * f.nsplit > vce::kMaxBlocks) return WKV7_ERR_INVALID_ARGUMENT;
     return WKV7_OK;
 }
 
@@ -120,7 +122,13 @@ wkv7_status vce_bwd_layout(int32_t M, int32_t D, int32_t V, int32_t vocab_chunk,
     l->Vc = (int32_t)(vc < V ? vc : V);
     const int64_t Vp = vce::round_up(V, vce::kBI), Mp = vce::round_up(M, vce::kBJ);
     const int64_t Vcp = vce::round_up(l->Vc, vce::kBI);
-    if ((Vcp / vce::kBI) * (Mp / vce::kBJ) > (1 << 24)) return WKV7_ERR_INVALID_ARGUMENT;
+    // every launch (workgroups of up to 512 threads) must stay below 2^31 threads
+    const int64_t dt = vce::round_up(D, vce::kBJ) / vce::kBJ;
+    const int64_t grids[3] = {(Vcp / vce::kBI) * (Mp / vce::kBJ),     // gradient tiles
+                              (Mp / vce::kBI) * dt,                   // dh
+                              (Vcp / vce::kBI) * dt};                 // dW
+    for (int64_t g : grids)
+        if (g > vce::kMaxBlocks) return WKV7_ERR_INVALID_ARGUMENT;
     l->wt = 0;
     l->ht = l->wt + pad256((size_t)D * Vp * 2);
     l->g = l->ht + pad256((size_t)D * Mp * 2);

@@ -90,5 +90,12 @@ def test_backward_rejects_bad_arguments():
     assert bwd(ws=ctypes.c_void_p(P[6].value + 4096)) == INVALID   # overlaps dw
     need = C.vce_backward_workspace_bytes(300, 128, 1000, 256)
     assert bwd(nbytes=need - 1) == WS
-    # many token rows tiled with a huge vocabulary chunk exceed the launchable grid
+    # grids beyond 2^22 workgroups are refused: gradient tiles (rows x chunk),
+    # dh (rows x width) and dW (chunk x width)
     assert bwd(M=1 << 26, V=1 << 24, chunk=1 << 24) == INVALID
+    assert bwd(M=1 << 28, D=65536, V=256, chunk=256) == INVALID
+    assert bwd(M=256, D=65536, V=1 << 24, chunk=1 << 24) == INVALID
+    with pytest.raises(W.WKV7Error):
+        C.vce_backward_workspace_bytes(1 << 28, 65536, 256, 256)
+    # the largest grid that is still allowed: 2^14 row tiles x 2^8 vocabulary tiles
+    assert C.vce_backward_workspace_bytes(1 << 22, 64, 1 << 16, 1 << 16) > 0
