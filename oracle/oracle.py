@@ -202,3 +202,28 @@ def decode_step_fused(r, w, k, v, a, b, s_in, g, ln_w, ln_b, r_k, eps):
     bonus = (_d(r) * _d(k) * _d(r_k)[None]).sum(axis=-1, keepdims=True)
     out = (yn + bonus * _d(v)) * _d(g)
     return out, y, s_out
+
+
+def gdn_decode_step(q, k, v, g, beta, s_in):
+    """One token of a gated DeltaNet layer through the remap the rwkv-lab page
+    ("Highlight result -- GDN in RWKV-7") states, at matched head size N:
+    with q^ = q / ||q||, k^ = k / ||k||,
+
+        r = q^,  w = exp(g) on every key,  k_write = beta k^,  a = -k^,
+        b = k^ exp(g) beta,  out = wkv7(r, w, k_write, v, a, b) / sqrt(N).
+
+    q, k [B, Hk, N] (key heads); v [B, H, N]; g, beta [B, H] (per value head);
+    state [B, H, N, N]. Value head h reads key head h // (H / Hk): groups of
+    consecutive value heads share a key head. Returns (out, s_out) in fp64."""
+    q, k, v = _d(q), _d(k), _d(v)
+    g, beta = _d(g), _d(beta)
+    B, Hk, N = q.shape
+    H = v.shape[1]
+    kh = np.arange(H) // (H // Hk)
+    qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    r, kk = qn[:, kh], kn[:, kh]
+    w = np.broadcast_to(np.exp(g)[..., None], (B, H, N))
+    bt = beta[..., None]
+    y, s_out = decode_step(r, w, bt * kk, v, -kk, kk * np.exp(g)[..., None] * bt, s_in)
+    return np.asarray(y) / np.sqrt(N), s_out

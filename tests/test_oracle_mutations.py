@@ -5,6 +5,8 @@ it. This shows the pins constrain the oracle, not merely agree with it."""
 import os
 import subprocess
 
+import numpy as np
+
 import pytest
 
 from oracle import oracle as O
@@ -114,3 +116,41 @@ def test_epilogue_slip_is_caught(mutation, monkeypatch):
 def test_epilogue_restatement_passes_pins(monkeypatch):
     monkeypatch.setattr(O, "decode_step_fused", _epilogue("none"))
     assert [n for n, (fn, tol) in P.PINS.items() if n.startswith("p13") and not fn() <= tol] == []
+
+
+def _gdn(mut):
+    """A restatement of the GDN remap with one planted slip."""
+    def step(q, k, v, g, beta, s_in):
+        q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+        g, beta = np.asarray(g, np.float64), np.asarray(beta, np.float64)
+        B, Hk, N = q.shape
+        H = v.shape[1]
+        kh = np.arange(H) // (H // Hk)
+        qn = q if mut == "r_unnormalised" else q / np.linalg.norm(q, axis=-1, keepdims=True)
+        kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+        kraw = k[:, kh] if mut == "kwrite_unnormalised" else kn[:, kh]
+        r, kk = qn[:, kh], kn[:, kh]
+        w = np.broadcast_to(np.exp(g)[..., None], (B, H, N))
+        bt = beta[..., None]
+        a = kk if mut == "a_sign" else -kk
+        b = kk * (1.0 if mut == "b_no_decay" else np.exp(g)[..., None]) * (1.0 if mut == "b_no_beta" else bt)
+        y, s_out = O.decode_step(r, w, bt * kraw, v, a, b, s_in)
+        scale = 1.0 / N if mut == "scale_over_n" else 1.0 / np.sqrt(N)
+        return np.asarray(y) * scale, s_out
+    return step
+
+
+GDN_SLIPS = ["a_sign", "b_no_beta", "b_no_decay", "scale_over_n", "kwrite_unnormalised",
+             "r_unnormalised"]
+
+
+@pytest.mark.parametrize("mutation", GDN_SLIPS)
+def test_gdn_slip_is_caught(mutation, monkeypatch):
+    monkeypatch.setattr(O, "gdn_decode_step", _gdn(mutation))
+    failed = [n for n, (fn, tol) in P.PINS.items() if n.startswith("p15") and not fn() <= tol]
+    assert failed, f"no pin detects GDN slip {mutation}"
+
+
+def test_gdn_restatement_passes_pins(monkeypatch):
+    monkeypatch.setattr(O, "gdn_decode_step", _gdn("none"))
+    assert [n for n, (fn, tol) in P.PINS.items() if n.startswith("p15") and not fn() <= tol] == []

@@ -379,6 +379,80 @@ def pin_p13_state_unchanged(seed=36):
     return max(rel(y, y_ref), rel(s1, s_ref))
 
 
+
+# P15: the GDN remap (rwkv-lab, "Highlight result -- GDN in RWKV-7").
+def _gdn_inputs(seed, B=2, Hk=2, H=4, N=128):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((B, Hk, N))
+    k = rng.standard_normal((B, Hk, N))
+    v = rng.standard_normal((B, H, N))
+    g = -rng.uniform(0.01, 1.0, (B, H))
+    beta = rng.uniform(0.05, 1.0, (B, H))
+    s = 0.1 * rng.standard_normal((B, H, N, N))
+    return q, k, v, g, beta, s
+
+
+def _gdn_textbook(q, k, v, g, beta, s):
+    """The gated delta rule written as matrices, per (b, value head):
+    S' = exp(g) S (I - beta k^ k^T) + beta v k^T,  o = S' q^ / sqrt(N)."""
+    B, Hk, N = q.shape
+    H = v.shape[1]
+    out = np.empty((B, H, N))
+    s1 = np.empty_like(s)
+    for b in range(B):
+        for h in range(H):
+            kh = h // (H // Hk)
+            qh = q[b, kh] / np.linalg.norm(q[b, kh])
+            kk = k[b, kh] / np.linalg.norm(k[b, kh])
+            S = np.exp(g[b, h]) * s[b, h] @ (np.eye(N) - beta[b, h] * np.outer(kk, kk)) \
+                + beta[b, h] * np.outer(v[b, h], kk)
+            s1[b, h] = S
+            out[b, h] = S @ qh / np.sqrt(N)
+    return out, s1
+
+
+def pin_p15_gated_delta_rule(seed=37):
+    """The remapped WKV-7 step equals the textbook gated delta rule (N = 128
+    and N = 64, two value heads per key head)."""
+    err = 0.0
+    for N in (128, 64):
+        inp = _gdn_inputs(seed, N=N)
+        o1, s1 = O.gdn_decode_step(*inp)
+        o2, s2 = _gdn_textbook(*inp)
+        err = max(err, rel(o1, o2), rel(s1, s2))
+    return err
+
+
+def pin_p15_delta_writes_v(seed=38):
+    """With no decay and beta = 1 the delta rule overwrites the value stored
+    at key k^: the new state maps k^ to v exactly."""
+    q, k, v, g, beta, s = _gdn_inputs(seed)
+    _, s1 = O.gdn_decode_step(q, k, v, np.zeros_like(g), np.ones_like(beta), s)
+    err = 0.0
+    for b in range(2):
+        for h in range(4):
+            kk = k[b, h // 2] / np.linalg.norm(k[b, h // 2])
+            err = max(err, rel(s1[b, h] @ kk, v[b, h]))
+    return err
+
+
+def pin_p15_beta_zero(seed=39):
+    """beta = 0 only decays the state: S' = exp(g) S, o = exp(g) S q^ / sqrt(N)."""
+    q, k, v, g, beta, s = _gdn_inputs(seed)
+    o1, s1 = O.gdn_decode_step(q, k, v, g, np.zeros_like(beta), s)
+    s_want = np.exp(g)[..., None, None] * s
+    qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    o_want = np.einsum("bhij,bhj->bhi", s_want, qn[:, [0, 0, 1, 1]]) / np.sqrt(128)
+    return max(rel(s1, s_want), rel(o1, o_want))
+
+
+def pin_p15_norm_invariance(seed=40):
+    """q and k enter only through their directions."""
+    q, k, v, g, beta, s = _gdn_inputs(seed)
+    o1, s1 = O.gdn_decode_step(q, k, v, g, beta, s)
+    o2, s2 = O.gdn_decode_step(3.7 * q, 0.21 * k, v, g, beta, s)
+    return max(rel(o2, o1), rel(s2, s1))
+
 PINS = {
     "p1_cumulative": (pin_p1, 1e-12),
     "p2_w0_last_outer": (pin_p2, 1e-12),
@@ -400,6 +474,10 @@ PINS = {
     "p13_fused_gate_and_bias": (pin_p13_gate_and_bias, 1e-12),
     "p13_fused_bonus_locality": (pin_p13_bonus_locality, 1e-12),
     "p13_fused_state_unchanged": (pin_p13_state_unchanged, 0.0),
+    "p15_gdn_gated_delta_rule": (pin_p15_gated_delta_rule, 1e-12),
+    "p15_gdn_delta_writes_v": (pin_p15_delta_writes_v, 1e-12),
+    "p15_gdn_beta_zero": (pin_p15_beta_zero, 1e-12),
+    "p15_gdn_norm_invariance": (pin_p15_norm_invariance, 1e-12),
 }
 
 
