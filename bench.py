@@ -267,6 +267,20 @@ def main():
         decode_loop()
     loop_graph_ms = _time_ms(loop_graph.replay, args.warmup, args.steps, ev)
 
+    # Gated DeltaNet decode through the RWKV-7 remap at GDN's layer geometry:
+    # 32 value heads over 16 key heads, N = 128, B = 128 sequences, bf16.
+    gin = synth.make_gdn_inputs(128, 32, 16, 128, seed=9, dtype="bf16")
+    gq, gk, gv = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (gin.q, gin.k, gin.v))
+    gg, gb = torch.from_numpy(gin.g).to(dev), torch.from_numpy(gin.beta).to(dev)
+    gs_in = torch.from_numpy(gin.s0).to(dev)
+    gs_out = torch.empty_like(gs_in)
+    gout = torch.empty_like(gv)
+    del gin
+    gdn_ms = _time_ms(lambda: W.wkv7_gdn_decode_step(gq, gk, gv, gg, gb, gs_in, s_out=gs_out, out=gout),
+                      args.warmup, args.steps, ev)
+    gdn_bytes = 128 * 32 * (2 * 128 * 128 * 4 + 2 * 128 * 2 + 8) + 128 * 16 * 2 * 128 * 2
+    del gq, gk, gv, gg, gb, gs_in, gs_out, gout
+
     # I/O variants: the prefill workload drawn in fp16; the training step with
     # w given as log(decay) and fp32 gradients.
     fin = synth.make_inputs(16, 1024, H, N, seed=2, dtype="f16", s0_std=0.1)
@@ -373,6 +387,12 @@ def main():
         "workload": "bf16 B=1 H=32, %d fused steps with the state in place" % K,
         "us_per_step_launched": loop_eager_ms * 1e3 / K,
         "us_per_step_graph_replay": loop_graph_ms * 1e3 / K}
+    out["gdn_decode_step"] = {
+        "workload": "gated DeltaNet via the RWKV-7 remap, bf16 B=128, 32 value heads over 16 key heads, "
+                    "N=128, fp32 state in and out",
+        "us": gdn_ms * 1e3, "sequence_steps_per_s": 128 / (gdn_ms * 1e-3),
+        "GB_per_s": gdn_bytes / (gdn_ms * 1e-3) / 1e9,
+        "hbm_frac": gdn_bytes / (gdn_ms * 1e-3) / PEAK_HBM}
     out["variants"] = {
         "prefill_forward_f16": {"workload": "fp16 B=16 T=1024 H=32, initial state N(0,0.1^2)",
                                 "ms": f16_ms, "tokens_per_s": 16 * 1024 / (f16_ms * 1e-3),

@@ -196,6 +196,32 @@ wkv7_status wkv7_decode_step_fused(int32_t B, int32_t H, int32_t N, int32_t dtyp
                                    const void *g, const float *ln_w, const float *ln_b,
                                    const float *r_k, float eps, void *out, void *y, void *stream);
 
+/*
+ * One token of a gated DeltaNet (GDN) layer, computed through the RWKV-7
+ * remap of the rwkv-lab page (section "Highlight result -- GDN in RWKV-7"):
+ * with q^ = q/||q|| and k^ = k/||k|| of the value head's key head,
+ *     r = q^, w = exp(g) on every key, k_write = beta k^, a = -k^,
+ *     b = k^ exp(g) beta,
+ *     S' = S diag(w) + (S a) b^T + v k_write^T,   out = S' r / sqrt(N)
+ * (the gated delta rule S' = exp(g) S (I - beta k^ k^T) + beta v k^T).
+ *   N      : head size, 64 or 128 (GDN's matched geometry is 128; anything
+ *            else: WKV7_ERR_UNSUPPORTED).
+ *   H, Hk  : value heads and key heads, Hk divides H; value head h reads key
+ *            head h / (H / Hk) (groups of consecutive value heads share one).
+ *   q, k   : [B, Hk, N]; v, out : [B, H, N]; all of type dtype (fp32, bf16
+ *            or fp16), 16-byte aligned. A q or k of length zero gives
+ *            non-finite outputs, as the definition divides by the length.
+ *   g, beta: fp32 [B, H], 4-byte aligned: the log-decay and the write
+ *            strength of each (sequence, value head).
+ *   s_in, s_out : fp32 [B, H, N, N] (row = value index), 16-byte aligned;
+ *            s_out == s_in updates in place; a partial overlap, or out
+ *            overlapping s_out, is WKV7_ERR_INVALID_ARGUMENT.
+ */
+wkv7_status wkv7_gdn_decode_step(int32_t B, int32_t H, int32_t Hk, int32_t N, int32_t dtype,
+                                 const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *s_in, float *s_out, void *out,
+                                 void *stream);
+
 /* Number of checkpoint slots a dense forward needs: B * ceil(T / 16). */
 wkv7_status wkv7_checkpoint_slots(int32_t B, int32_t T, int64_t *slots);
 

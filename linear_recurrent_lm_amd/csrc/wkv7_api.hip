@@ -333,6 +333,32 @@ wkv7_status wkv7_decode_step_fused(int32_t B, int32_t H, int32_t N, int32_t dtyp
                        g, ln_w, ln_b, r_k, eps, out, stream);
 }
 
+wkv7_status wkv7_gdn_decode_step(int32_t B, int32_t H, int32_t Hk, int32_t N, int32_t dtype,
+                                 const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *s_in, float *s_out, void *out,
+                                 void *stream) {
+    if (N != 64 && N != 128) return WKV7_ERR_UNSUPPORTED;
+    if (!dtype_ok(dtype)) return WKV7_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || Hk < 1 || H % Hk != 0 || (int64_t)B * H > INT32_MAX)
+        return WKV7_ERR_INVALID_ARGUMENT;
+    const void *streams[6] = {q, k, v, s_in, s_out, out};
+    wkv7_status st = check_streams(streams, 6);
+    if (st != WKV7_OK) return st;
+    if (!g || !beta || !aligned4(g) || !aligned4(beta)) return WKV7_ERR_INVALID_ARGUMENT;
+    const size_t state_bytes = (size_t)B * H * N * N * sizeof(float);
+    if (s_in != s_out && ranges_overlap(s_in, state_bytes, s_out, state_bytes))
+        return WKV7_ERR_INVALID_ARGUMENT;
+    if (ranges_overlap(out, (size_t)B * H * N * elem_size(dtype), s_out, state_bytes))
+        return WKV7_ERR_INVALID_ARGUMENT;
+    if ((st = check_device()) != WKV7_OK) return st;
+    wkv7::GdnArgs a{};
+    a.B = B; a.H = H; a.Hk = Hk; a.N = N; a.dtype = dtype;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.s_in = s_in; a.s_out = s_out; a.out = out;
+    if (wkv7::launch_gdn_decode(a, (hipStream_t)stream) != hipSuccess) return WKV7_ERR_HIP;
+    return WKV7_OK;
+}
+
 wkv7_status vce_forward_workspace_bytes(int32_t M, int32_t D, int32_t V, size_t *bytes) {
     wkv7_status st = vce_check_sizes(M, D, V);
     if (st != WKV7_OK) return st;

@@ -60,6 +60,19 @@ hipError_t launch_backward_sweep(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecArgs &a, hipStream_t stream);
 
+// One token of a gated DeltaNet layer through the RWKV-7 remap.
+struct GdnArgs {
+    int32_t B, H, Hk, N;             // value heads H share Hk key heads; N = 64 or 128
+    int dtype;
+    const void *q, *k;               // [B][Hk][N], I/O type
+    const void *v;                   // [B][H][N], I/O type
+    const float *g, *beta;           // [B][H]
+    const float *s_in;
+    float *s_out;                    // [B][H][N][N]
+    void *out;                       // [B][H][N], I/O type
+};
+hipError_t launch_gdn_decode(const GdnArgs &a, hipStream_t stream);
+
 // Segment mode: write zeros to `nptr` token streams at tokens no sequence covers.
 hipError_t launch_zero_uncovered(const SegParams &seg, int dtype, void *const *ptrs,
                                  int nptr, hipStream_t stream);

@@ -260,3 +260,30 @@ def make_ce_inputs(M: int, D: int, V: int, *, seed: int = 5, logit_std: float = 
     else:
         dl = rng.standard_normal(M, dtype=np.float32)
     return CEInputs(h, W, t, dl)
+
+
+@dataclasses.dataclass
+class GDNInputs:
+    """One token of a gated DeltaNet layer: q, k [B, Hk, N] and v [B, H, N]
+    (values of the I/O dtype held in fp32), g, beta [B, H] fp32, state
+    [B, H, N, N] fp32."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    g: np.ndarray
+    beta: np.ndarray
+    s0: np.ndarray
+
+
+def make_gdn_inputs(B: int, H: int, Hk: int, N: int = 128, *, seed: int = 8, dtype: str = "bf16",
+                    state_std: float = 0.1) -> GDNInputs:
+    """q, k, v ~ N(0, 1) rounded to dtype; g = -U(0.01, 1) (a log-decay);
+    beta ~ U(0.05, 1) (a sigmoid output); state ~ N(0, state_std^2)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = round_to(rng.standard_normal((B, Hk, N), dtype=np.float32), dtype)
+    k = round_to(rng.standard_normal((B, Hk, N), dtype=np.float32), dtype)
+    v = round_to(rng.standard_normal((B, H, N), dtype=np.float32), dtype)
+    g = (-rng.uniform(0.01, 1.0, (B, H))).astype(np.float32)
+    beta = rng.uniform(0.05, 1.0, (B, H)).astype(np.float32)
+    s0 = rng.standard_normal((B, H, N, N), dtype=np.float32) * np.float32(state_std)
+    return GDNInputs(q, k, v, g, beta, s0)

@@ -76,11 +76,13 @@ def lib():
         L.wkv7_status_string.argtypes = [i32]
         L.wkv7_status_string.restype = ctypes.c_char_p
         L.wkv7_abi_version.restype = i32
+        L.wkv7_gdn_decode_step.argtypes = [i32] * 5 + [vp] * 9
         L.vce_forward_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.vce_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.vce_forward.argtypes = [i32, i32, i32] + [vp] * 6 + [sz, vp]
         L.vce_backward.argtypes = [i32, i32, i32, i32] + [vp] * 8 + [sz, vp]
         for fn in ("wkv7_forward", "wkv7_backward", "wkv7_decode_step", "wkv7_decode_step_fused",
+                   "wkv7_gdn_decode_step",
                    "wkv7_checkpoint_slots",
                    "wkv7_workspace_bytes", "wkv7_segments_check", "vce_forward_workspace_bytes",
                    "vce_backward_workspace_bytes", "vce_forward", "vce_backward"):
@@ -309,6 +311,32 @@ def wkv7_decode_step_fused(r, w, k, v, a, b, s_in, g, ln_w, ln_b, r_k, eps, s_ou
         _ptr(s_out), _ptr(g), _ptr(ln_w), _ptr(ln_b), _ptr(r_k), float(eps), _ptr(out), _ptr(y),
         _stream()))
     return out, s_out, y
+
+
+def wkv7_gdn_decode_step(q, k, v, g, beta, s_in, s_out=None, out=None):
+    """One token of a gated DeltaNet layer through the RWKV-7 remap: q, k
+    [B, Hk, N], v [B, H, N] (one dtype), g, beta fp32 [B, H], state fp32
+    [B, H, N, N] (N = 64 or 128). s_out=s_in updates in place. Returns
+    (out [B, H, N], s_out)."""
+    torch = _torch()
+    dev = v.device
+    B, H, N = v.shape
+    Hk = q.shape[1]
+    dt = v.dtype
+    _req(q, "q", dev, dt, (B, Hk, N))
+    _req(k, "k", dev, dt, (B, Hk, N))
+    _req(v, "v", dev, dt)
+    _req(g, "g", dev, torch.float32, (B, H))
+    _req(beta, "beta", dev, torch.float32, (B, H))
+    _req(s_in, "s_in", dev, torch.float32, (B, H, N, N))
+    s_out = torch.empty_like(s_in) if s_out is None else s_out
+    _req(s_out, "s_out", dev, torch.float32, (B, H, N, N))
+    out = torch.empty_like(v) if out is None else out
+    _req(out, "out", dev, dt, (B, H, N))
+    _check("wkv7_gdn_decode_step", lib().wkv7_gdn_decode_step(
+        B, H, Hk, N, _dtype_code(v), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(s_in), _ptr(s_out), _ptr(out), _stream()))
+    return out, s_out
 
 
 def wkv7_abi_version() -> int:

@@ -122,6 +122,30 @@ def test_fused_decode_rejects_bad_arguments():
     assert call(s_in=P[7], s_out=ctypes.c_void_p(P[7].value + 16)) == INVALID
 
 
+def test_gdn_decode_rejects_bad_arguments():
+    L = W.lib()
+
+    def call(B=4, H=4, Hk=2, N=128, dt=1, q=P[0], k=P[1], v=P[2], g=P[3], beta=P[4],
+             s_in=P[5], s_out=P[6], out=P[7]):
+        return L.wkv7_gdn_decode_step(B, H, Hk, N, dt, q, k, v, g, beta, s_in, s_out, out, None)
+    assert call(N=96) == UNSUPPORTED
+    assert call(N=256) == UNSUPPORTED
+    assert call(dt=3) == UNSUPPORTED
+    assert call(B=0) == INVALID
+    assert call(Hk=0) == INVALID
+    assert call(H=6, Hk=4) == INVALID                      # key heads must divide value heads
+    for name in ("q", "k", "v", "g", "beta", "s_in", "s_out", "out"):
+        assert call(**{name: None}) == INVALID, name
+    assert call(q=ctypes.c_void_p(P[0].value + 8)) == INVALID
+    assert call(g=ctypes.c_void_p(P[3].value + 2)) == INVALID
+    far = [ctypes.c_void_p((q + 1) << 40) for q in range(8)]
+    # partial overlap of the states, and out inside s_out
+    assert call(s_in=far[5], s_out=ctypes.c_void_p(far[5].value + 16), q=far[0], k=far[1],
+                v=far[2], g=far[3], beta=far[4], out=far[7]) == INVALID
+    assert call(s_in=far[5], s_out=far[6], out=ctypes.c_void_p(far[6].value + 64), q=far[0],
+                k=far[1], v=far[2], g=far[3], beta=far[4]) == INVALID
+
+
 def test_checkpoint_slots():
     assert W.checkpoint_slots(3, 33) == 9
     assert W.checkpoint_slots(2, 16) == 2

@@ -1,0 +1,89 @@
+"""GPU parity of the gated DeltaNet decode step (wkv7_gdn_decode_step: one
+token through the RWKV-7 remap, head size 128 or 64) against the fp64
+oracle's gdn_decode_step, through the C ABI. Tolerances as for the WKV-7
+decode step: 1e-5 for fp32 outputs and every state, 2e-2 for bf16 outputs,
+2e-3 for fp16."""
+import numpy as np
+import pytest
+
+from linear_recurrent_lm_amd import synth
+from oracle import oracle as O
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": U.TOL_F32, "bf16": U.TOL_BF16_Y, "f16": U.TOL_F16}
+
+
+@pytest.fixture(scope="module")
+def W():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_recurrent_lm_amd import wkv7
+    wkv7.lib()
+    return wkv7
+
+
+def unit_err(x, ref):
+    """[B, H, N]: unit = (b, h)."""
+    num = np.max(np.abs(x - ref), axis=-1)
+    den = np.maximum(np.max(np.abs(ref), axis=-1), 1e-30)
+    return float(np.max(num / den))
+
+
+def run(W, inp, dtype, in_place=False):
+    import torch
+    q, k, v = (U.dev_stream(x, dtype) for x in (inp.q, inp.k, inp.v))
+    s_in = U.dev_f32(inp.s0)
+    out, s_out = W.wkv7_gdn_decode_step(q, k, v, U.dev_f32(inp.g), U.dev_f32(inp.beta), s_in,
+                                        s_out=s_in if in_place else None)
+    torch.cuda.synchronize()
+    if in_place:
+        assert s_out.data_ptr() == s_in.data_ptr()
+    return U.host(out), U.host(s_out)
+
+
+@pytest.mark.parametrize("N", [128, 64])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_gdn_decode_parity(W, N, dtype):
+    inp = synth.make_gdn_inputs(3, 8, 4, N, seed=44, dtype=dtype)
+    out, s_out = run(W, inp, dtype)
+    ro, rs = O.gdn_decode_step(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.s0)
+    assert unit_err(out, ro) <= TOL[dtype]
+    assert U.unit_err_state(s_out, rs) <= U.TOL_F32
+
+
+def test_gdn_decode_in_place_one_head_per_key(W):
+    inp = synth.make_gdn_inputs(5, 4, 4, 128, seed=45, dtype="f32")
+    out, s_out = run(W, inp, "f32", in_place=True)
+    ro, rs = O.gdn_decode_step(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.s0)
+    assert unit_err(out, ro) <= U.TOL_F32
+    assert U.unit_err_state(s_out, rs) <= U.TOL_F32
+
+
+def test_gdn_decode_workload_all_units(W):
+    """GDN's layer geometry (32 value heads over 16 key heads, N = 128), bf16,
+    B = 64: every unit."""
+    inp = synth.make_gdn_inputs(64, 32, 16, 128, seed=46, dtype="bf16")
+    out, s_out = run(W, inp, "bf16")
+    ro, rs = O.gdn_decode_step(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.s0)
+    assert unit_err(out, ro) <= U.TOL_BF16_Y
+    assert U.unit_err_state(s_out, rs) <= U.TOL_F32
+
+
+def test_gdn_decode_chain(W):
+    """Four steps with the state carried in place equal four oracle steps."""
+    import torch
+    B, H, Hk, N = 2, 4, 2, 128
+    steps = [synth.make_gdn_inputs(B, H, Hk, N, seed=47 + t, dtype="f32") for t in range(4)]
+    s_dev = U.dev_f32(steps[0].s0)
+    s_ref = steps[0].s0.astype(np.float64)
+    for inp in steps:
+        q, k, v = (U.dev_f32(x) for x in (inp.q, inp.k, inp.v))
+        out, _ = W.wkv7_gdn_decode_step(q, k, v, U.dev_f32(inp.g), U.dev_f32(inp.beta), s_dev,
+                                        s_out=s_dev)
+        ro, s_ref = O.gdn_decode_step(inp.q, inp.k, inp.v, inp.g, inp.beta, s_ref)
+        torch.cuda.synchronize()
+        assert unit_err(U.host(out), ro) <= U.TOL_F32
+    assert U.unit_err_state(U.host(s_dev), s_ref) <= U.TOL_F32
