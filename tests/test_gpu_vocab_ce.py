@@ -157,3 +157,44 @@ def test_training_workload_sampled(C):
     torch.cuda.synchronize()
     assert torch.equal(dw1, dw)
     assert ((dh1 - dh).abs().amax(dim=1) <= 1e-4 * dh.abs().amax(dim=1) + 1e-12).all()
+
+
+def test_graph_replay(C):
+    """Forward and backward captured in one graph (caller-owned workspaces,
+    nothing allocated or cleared inside): three replays, with eager work and
+    synchronisations between them, each bit-identical to the eager run."""
+    import torch
+    M, D, V = 300, 128, 1000
+    c = synth.make_ce_inputs(M, D, V, seed=66, dloss="normal")
+    h, w, t, dl = dev(c)
+    fws = torch.empty(C.vce_forward_workspace_bytes(M, D, V), dtype=torch.uint8, device="cuda:0")
+    bws = torch.empty(C.vce_backward_workspace_bytes(M, D, V, 512), dtype=torch.uint8, device="cuda:0")
+    outs = [torch.empty(M, device="cuda:0"), torch.empty(M, device="cuda:0"),
+            torch.empty(M, D, device="cuda:0"), torch.empty(V, D, device="cuda:0")]
+
+    def step(o):
+        C.vce_forward(h, w, t, loss=o[0], lse=o[1], workspace=fws)
+        C.vce_backward(h, w, t, o[1], dl, vocab_chunk=512, dh=o[2], dw=o[3], workspace=bws)
+
+    eager = [torch.empty_like(x) for x in outs]
+    step(eager)
+    torch.cuda.synchronize()
+    want = [x.clone() for x in eager]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(outs)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(outs)
+    for rep in range(3):
+        for x in outs:
+            x.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(outs, want):
+            assert torch.equal(x, y), rep
+        step(eager)                      # eager work between replays
+        torch.cuda.synchronize()
