@@ -217,9 +217,6 @@ __global__ __launch_bounds__(128 * NWJ) void gemm_kernel(GemmArgs p) {   // Cfg:
             _Pragma("unroll") for (int bj = 0; bj < WJ; ++bj)                               \
                 acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[bi], G[bj], acc[bi][bj], 0, 0, 0); \
     } while (0)
-// The fragments of k-step kk+1 are read while the MFMAs of k-step kk run;
-// the scheduling barriers keep the compiler from hoisting every read of
-// the stage (which would need 96 more registers).
 // One k-step: the MFMAs of (F, G) with the reads of the next fragments
 // (FN, GN) spread between them, one read after each of the first MFMAs.
 #define VCE_STEP(F, G, FN, GN, kkn)                                                          \
