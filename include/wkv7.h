@@ -158,6 +158,8 @@ wkv7_status wkv7_backward(const wkv7_desc *d,
 /*
  * One decode step for B independent sequences (the rwkv-metal page's
  * wkv7_step; the rwkv-lab page's in-place one-token state transition).
+ *   N     : head size, 64, or 128 (the matched head size of the rwkv-lab
+ *           page's GDN conversion target); anything else: WKV7_ERR_UNSUPPORTED.
  *   dtype : wkv7_dtype of r..b and y; decay : wkv7_decay of w.
  *   r..b  : [B,H,N] one token per sequence (dtype).
  *   s_in  : [B,H,N,N] fp32 state before the token.
@@ -175,7 +177,8 @@ wkv7_status wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, int
  * ("RWKV community research additions") describes a one-token kernel that
  * carries the fp32 state update through GroupNorm, the RWKV bonus and output
  * gating, and the rwkv-metal page ("What's inside") names ln_x a GroupNorm per
- * head. The pages print no formula; the reading taken, per (sequence, head h),
+ * head. Head size N = 64 only (other N: WKV7_ERR_UNSUPPORTED). The pages
+ * print no formula; the reading taken, per (sequence, head h),
  * with y the plain step's output and mean / var the population mean and
  * variance of its N values:
  *   yn_i  = (y_i - mean(y)) / sqrt(var(y) + eps) * ln_w[h][i] + ln_b[h][i]

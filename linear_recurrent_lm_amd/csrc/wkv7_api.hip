@@ -284,7 +284,7 @@ static wkv7_status decode_impl(int32_t B, int32_t H, int32_t N, int32_t dtype, i
                                void *y, const void *g, const float *ln_w, const float *ln_b,
                                const float *r_k, float eps, void *out, void *stream) {
     const bool fused = out != nullptr;
-    if (N != kN) return WKV7_ERR_UNSUPPORTED;
+    if (N != kN && (fused || N != 128)) return WKV7_ERR_UNSUPPORTED;   // 128: plain step only
     if (!dtype_ok(dtype)) return WKV7_ERR_UNSUPPORTED;
     if (decay != WKV7_DECAY_MULT && decay != WKV7_DECAY_LOG) return WKV7_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || (int64_t)B * H > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
@@ -297,7 +297,7 @@ static wkv7_status decode_impl(int32_t B, int32_t H, int32_t N, int32_t dtype, i
         if (y && !aligned16(y)) return WKV7_ERR_INVALID_ARGUMENT;
         if (!(eps >= 0.f) || !std::isfinite(eps)) return WKV7_ERR_INVALID_ARGUMENT;
     }
-    const size_t state_bytes = (size_t)B * H * kN * kN * sizeof(float);
+    const size_t state_bytes = (size_t)B * H * N * N * sizeof(float);
     if (s_in != s_out && ranges_overlap(s_in, state_bytes, s_out, state_bytes))
         return WKV7_ERR_INVALID_ARGUMENT;
     if ((st = check_device()) != WKV7_OK) return st;
@@ -310,7 +310,9 @@ static wkv7_status decode_impl(int32_t B, int32_t H, int32_t N, int32_t dtype, i
         args.g = g; args.ln_w = ln_w; args.ln_b = ln_b; args.r_k = r_k;
         args.eps = eps; args.out = out;
     }
-    if (wkv7::launch_decode(args, (hipStream_t)stream) != hipSuccess) return WKV7_ERR_HIP;
+    const hipError_t e = N == 128 ? wkv7::launch_decode128(args, (hipStream_t)stream)
+                                  : wkv7::launch_decode(args, (hipStream_t)stream);
+    if (e != hipSuccess) return WKV7_ERR_HIP;
     return WKV7_OK;
 }
 

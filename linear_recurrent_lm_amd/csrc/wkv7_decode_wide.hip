@@ -1,6 +1,19 @@
-// One token of a gated DeltaNet (GDN) layer, computed as the WKV-7 step the
-// rwkv-lab page ("Highlight result -- GDN in RWKV-7") maps it to, at GDN's
-// matched head size (N = 128; N = 64 also accepted). With q^ = q/||q|| and
+// Decode steps at head size 128 (and the GDN step at 64 too): one token per
+// (sequence, head), fp32 state in and out, bound by HBM traffic (64 KiB of
+// state in and 64 KiB out per (sequence, head) at N = 128).
+//
+// One 256-thread workgroup per (sequence, head): each state load instruction
+// covers 4 KiB of contiguous memory (float4 index m*256 + tid), a lane owns
+// 4 key columns of N*N/1024 rows, and the N/4 lanes that share a row reduce
+// S a and S r (and, for GDN, the squared lengths of q and k) by lane
+// exchange.
+//
+// The WKV-7 step (the rwkv-metal page's wkv7_step at the 128-wide heads the
+// rwkv-lab conversion target uses) reads r, w, k, v, a, b as given:
+//     S' = S diag(w) + (S a) b^T + v k^T,   y = S' r.
+//
+// The gated DeltaNet (GDN) step is the WKV-7 step the rwkv-lab page
+// ("Highlight result -- GDN in RWKV-7") maps it to. With q^ = q/||q|| and
 // k^ = k/||k||:
 //     r = q^,  w = exp(g) on every key,  k_write = beta k^,  a = -k^,
 //     b = k^ exp(g) beta,
@@ -8,13 +21,6 @@
 // which is the gated delta rule S' = exp(g) S (I - beta k^ k^T) + beta v k^T.
 // Value head h reads key head h / (H / Hk): groups of consecutive value heads
 // share a key head (GDN's geometry is 32 value heads over 16 key heads).
-//
-// Bound by HBM traffic like the WKV-7 decode step (64 KiB of fp32 state in and
-// 64 KiB out per (sequence, head) at N = 128). One 256-thread workgroup per
-// (sequence, value head): each state load instruction covers 4 KiB of
-// contiguous memory (float4 index m*256 + tid), a lane owns 4 key columns of
-// N*N/1024 rows, and the N/4 lanes that share a row reduce S a, S r and the
-// squared lengths of q and k by lane exchange.
 #include "wkv7_kernels.h"
 
 namespace wkv7 {
@@ -91,6 +97,54 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(GdnArgs p) {
     }
 }
 
+// The WKV-7 step at N = 128 (same layout as above).
+template <typename TI>
+__global__ __launch_bounds__(256) void decode128_kernel(DecArgs p) {
+    constexpr int N = 128, LPR = 32, RPI = 8, IT = 16;
+    const int64_t unit = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int c0 = (tid % LPR) * 4;
+    const int rl = tid / LPR;
+    const int64_t sb = unit * (int64_t)(N * N);
+    const int64_t vb = unit * N;
+
+    f32x4 S[IT];
+#pragma unroll
+    for (int m = 0; m < IT; ++m)
+        S[m] = __builtin_nontemporal_load((const f32x4 *)(p.s_in + sb) + m * 256 + tid);
+    float r[4], w[4], k[4], a[4], b[4], vv[IT];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = IO<TI>::ld((const TI *)p.r, vb + c0 + e);
+        w[e] = IO<TI>::ld((const TI *)p.w, vb + c0 + e);
+        k[e] = IO<TI>::ld((const TI *)p.k, vb + c0 + e);
+        a[e] = IO<TI>::ld((const TI *)p.a, vb + c0 + e);
+        b[e] = IO<TI>::ld((const TI *)p.b, vb + c0 + e);
+    }
+    decay_of<4>(w, p.logw);
+#pragma unroll
+    for (int m = 0; m < IT; ++m) vv[m] = IO<TI>::ld((const TI *)p.v, vb + m * RPI + rl);
+
+    float yv[IT];
+#pragma unroll
+    for (int m = 0; m < IT; ++m) {
+        const float sa = sum_lanes<LPR>(S[m].x * a[0] + S[m].y * a[1] + S[m].z * a[2] + S[m].w * a[3]);
+        const float vi = vv[m];
+        S[m].x = fmaf(S[m].x, w[0], fmaf(sa, b[0], vi * k[0]));
+        S[m].y = fmaf(S[m].y, w[1], fmaf(sa, b[1], vi * k[1]));
+        S[m].z = fmaf(S[m].z, w[2], fmaf(sa, b[2], vi * k[2]));
+        S[m].w = fmaf(S[m].w, w[3], fmaf(sa, b[3], vi * k[3]));
+        yv[m] = sum_lanes<LPR>(S[m].x * r[0] + S[m].y * r[1] + S[m].z * r[2] + S[m].w * r[3]);
+    }
+#pragma unroll
+    for (int m = 0; m < IT; ++m)
+        __builtin_nontemporal_store(S[m], (f32x4 *)(p.s_out + sb) + m * 256 + tid);
+    if (tid % LPR == 0) {
+#pragma unroll
+        for (int m = 0; m < IT; ++m) IO<TI>::st((TI *)p.y, vb + m * RPI + rl, yv[m]);
+    }
+}
+
 template <int N>
 hipError_t launch_n(const GdnArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)a.B * a.H));
@@ -104,6 +158,14 @@ hipError_t launch_n(const GdnArgs &a, hipStream_t stream) {
 
 hipError_t launch_gdn_decode(const GdnArgs &a, hipStream_t stream) {
     return a.N == 128 ? launch_n<128>(a, stream) : launch_n<64>(a, stream);
+}
+
+hipError_t launch_decode128(const DecArgs &a, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)a.B * a.H));
+    if (a.dtype == 1) hipLaunchKernelGGL(decode128_kernel<uint16_t>, grid, dim3(256), 0, stream, a);
+    else if (a.dtype == 2) hipLaunchKernelGGL(decode128_kernel<_Float16>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(decode128_kernel<float>, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace wkv7

@@ -72,6 +72,8 @@ struct GdnArgs {
     void *out;                       // [B][H][N], I/O type
 };
 hipError_t launch_gdn_decode(const GdnArgs &a, hipStream_t stream);
+// The WKV-7 step (not fused) at head size 128.
+hipError_t launch_decode128(const DecArgs &a, hipStream_t stream);
 
 // Segment mode: write zeros to `nptr` token streams at tokens no sequence covers.
 hipError_t launch_zero_uncovered(const SegParams &seg, int dtype, void *const *ptrs,

@@ -263,17 +263,18 @@ def wkv7_backward(r, w, k, v, a, b, ckpt, dy=None, ds_out=None, *,
 
 
 def wkv7_decode_step(r, w, k, v, a, b, s_in, s_out=None, y=None, *, decay: str = "mult"):
-    """One token per (sequence, head): streams [B, H, 64], state [B, H, 64, 64].
-    Pass s_out=s_in to update the state in place. Returns (y, s_out)."""
+    """One token per (sequence, head): streams [B, H, n], state [B, H, n, n]
+    with head size n = 64 or 128. Pass s_out=s_in to update the state in
+    place. Returns (y, s_out)."""
     torch = _torch()
     B, H, n = r.shape
     dev = r.device
     for name, t in zip("rwkvab", (r, w, k, v, a, b)):
         _req(t, name, dev, r.dtype, r.shape)
-    _req(s_in, "s_in", dev, torch.float32, (B, H, N, N))
+    _req(s_in, "s_in", dev, torch.float32, (B, H, n, n))
     if s_out is None:
         s_out = torch.empty_like(s_in)
-    _req(s_out, "s_out", dev, torch.float32, (B, H, N, N))
+    _req(s_out, "s_out", dev, torch.float32, (B, H, n, n))
     y = torch.empty_like(r) if y is None else y
     _check("wkv7_decode_step", lib().wkv7_decode_step(
         B, H, n, _dtype_code(r), _decay(decay), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(s_in),

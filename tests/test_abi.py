@@ -92,11 +92,14 @@ def test_decode_rejects_bad_arguments():
     call = lambda B=4, H=2, N=64, dt=1, dc=0, s_in=P[7], s_out=P[8], y=P[6]: L.wkv7_decode_step(
         B, H, N, dt, dc, *P[:6], s_in, s_out, y, None)
     assert call(N=32) == UNSUPPORTED
+    assert call(N=96) == UNSUPPORTED
+    assert call(N=256) == UNSUPPORTED
     assert call(dt=3) == UNSUPPORTED
     assert call(dc=5) == UNSUPPORTED
     assert call(B=0) == INVALID
     assert call(s_in=None) == INVALID
     assert call(y=None) == INVALID
+    assert call(N=128, y=None) == INVALID      # head size 128 passes the size check, then fails here
     # overlapping but not identical state buffers
     assert call(s_in=P[7], s_out=ctypes.c_void_p(P[7].value + 16)) == INVALID
 
@@ -109,6 +112,7 @@ def test_fused_decode_rejects_bad_arguments():
         return L.wkv7_decode_step_fused(B, H, N, dt, dc, *P[:6], s_in, s_out, g, ln_w, ln_b, r_k,
                                         eps, out, y, None)
     assert call(N=32) == UNSUPPORTED
+    assert call(N=128) == UNSUPPORTED          # the fused epilogue is built for head size 64
     assert call(dt=3) == UNSUPPORTED
     assert call(dc=5) == UNSUPPORTED
     assert call(B=0) == INVALID
