@@ -227,3 +227,22 @@ def gdn_decode_step(q, k, v, g, beta, s_in):
     bt = beta[..., None]
     y, s_out = decode_step(r, w, bt * kk, v, -kk, kk * np.exp(g)[..., None] * bt, s_in)
     return np.asarray(y) / np.sqrt(N), s_out
+
+
+def gdn_forward(q, k, v, g, beta, s0=None):
+    """A sequence of gated DeltaNet tokens through the same remap as
+    gdn_decode_step, token by token (rwkv-lab, "Highlight result -- GDN in
+    RWKV-7"). q, k [B, T, Hk, N]; v [B, T, H, N]; g, beta [B, T, H]; s0
+    [B, H, N, N] or None (zero). Returns (out [B, T, H, N], s_out) in fp64."""
+    q, k, v = _d(q), _d(k), _d(v)
+    g, beta = _d(g), _d(beta)
+    B, T, Hk, N = q.shape
+    H = v.shape[2]
+    kh = np.arange(H) // (H // Hk)
+    qn = (q / np.linalg.norm(q, axis=-1, keepdims=True))[:, :, kh]
+    kn = (k / np.linalg.norm(k, axis=-1, keepdims=True))[:, :, kh]
+    dec = np.exp(g)[..., None]
+    bt = beta[..., None]
+    w = np.broadcast_to(dec, (B, T, H, N))
+    out = forward(qn, w, bt * kn, v, -kn, kn * dec * bt, s0=s0)
+    return out["y"] / np.sqrt(N), out["s_out"]

@@ -453,6 +453,42 @@ def pin_p15_norm_invariance(seed=40):
     o2, s2 = O.gdn_decode_step(3.7 * q, 0.21 * k, v, g, beta, s)
     return max(rel(o2, o1), rel(s2, s1))
 
+
+def pin_p16_gdn_forward_textbook(seed=41):
+    """A sequence of GDN tokens equals the textbook gated delta rule applied
+    token by token (N = 128, two value heads per key head, random s0)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, T, Hk, H, N = 2, 6, 2, 4, 128
+    q = rng.standard_normal((B, T, Hk, N))
+    k = rng.standard_normal((B, T, Hk, N))
+    v = rng.standard_normal((B, T, H, N))
+    g = -rng.uniform(0.01, 1.0, (B, T, H))
+    beta = rng.uniform(0.05, 1.0, (B, T, H))
+    s = 0.1 * rng.standard_normal((B, H, N, N))
+    out, s_out = O.gdn_forward(q, k, v, g, beta, s)
+    err = 0.0
+    for t in range(T):
+        o_t, s = _gdn_textbook(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], s)
+        err = max(err, rel(out[:, t], o_t))
+    return max(err, rel(s_out, s))
+
+
+def pin_p16_gdn_forward_zero_state(seed=42):
+    """Without s0 the sequence starts from the zero state: the first token's
+    output is beta_0 <k^_0, q^_0> v_0 / sqrt(N)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, T, Hk, H, N = 1, 3, 1, 2, 64
+    q = rng.standard_normal((B, T, Hk, N))
+    k = rng.standard_normal((B, T, Hk, N))
+    v = rng.standard_normal((B, T, H, N))
+    g = -rng.uniform(0.01, 1.0, (B, T, H))
+    beta = rng.uniform(0.05, 1.0, (B, T, H))
+    out, _ = O.gdn_forward(q, k, v, g, beta)
+    qn = q[0, 0, 0] / np.linalg.norm(q[0, 0, 0])
+    kn = k[0, 0, 0] / np.linalg.norm(k[0, 0, 0])
+    want = beta[0, 0, :, None] * np.dot(kn, qn) * v[0, 0] / np.sqrt(N)
+    return rel(out[0, 0], want)
+
 PINS = {
     "p1_cumulative": (pin_p1, 1e-12),
     "p2_w0_last_outer": (pin_p2, 1e-12),
@@ -478,6 +514,8 @@ PINS = {
     "p15_gdn_delta_writes_v": (pin_p15_delta_writes_v, 1e-12),
     "p15_gdn_beta_zero": (pin_p15_beta_zero, 1e-12),
     "p15_gdn_norm_invariance": (pin_p15_norm_invariance, 1e-12),
+    "p16_gdn_forward_textbook": (pin_p16_gdn_forward_textbook, 1e-12),
+    "p16_gdn_forward_zero_state": (pin_p16_gdn_forward_zero_state, 1e-12),
 }
 
 
