@@ -280,6 +280,19 @@ def main():
                       args.warmup, args.steps, ev)
     gdn_bytes = 128 * 32 * (2 * 128 * 128 * 4 + 2 * 128 * 2 + 8) + 128 * 16 * 2 * 128 * 2
     del gq, gk, gv, gg, gb, gs_in, gs_out, gout
+    # GDN prefill through the remap: B=16, T=1024, same geometry. Per token and
+    # value head: <S, k^> (2N^2), the update exp(g) S + c k^ (3N^2) and
+    # <S, q^> (2N^2) flops.
+    gsq = synth.make_gdn_sequence(16, 1024, 32, 16, 128, seed=11, dtype="bf16")
+    sq, sk, sv = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (gsq.q, gsq.k, gsq.v))
+    sg, sb = torch.from_numpy(gsq.g).to(dev), torch.from_numpy(gsq.beta).to(dev)
+    del gsq
+    sout = torch.empty_like(sv)
+    sws = torch.empty(W.wkv7_gdn_workspace_bytes(16, 1024, 16, 128), device=dev, dtype=torch.uint8)
+    gdnf_ms = _time_ms(lambda: W.wkv7_gdn_forward(sq, sk, sv, sg, sb, None, out=sout, workspace=sws),
+                       args.warmup, args.steps, ev)
+    gdnf_flop = 7 * 128 * 128 * 16 * 1024 * 32
+    del sq, sk, sv, sg, sb, sout, sws
 
     # I/O variants: the prefill workload drawn in fp16; the training step with
     # w given as log(decay) and fp32 gradients.
@@ -393,6 +406,11 @@ def main():
         "us": gdn_ms * 1e3, "sequence_steps_per_s": 128 / (gdn_ms * 1e-3),
         "GB_per_s": gdn_bytes / (gdn_ms * 1e-3) / 1e9,
         "hbm_frac": gdn_bytes / (gdn_ms * 1e-3) / PEAK_HBM}
+    out["gdn_prefill_forward"] = {
+        "workload": "gated DeltaNet via the RWKV-7 remap, bf16 B=16 T=1024, 32 value heads over 16 key "
+                    "heads, N=128, zero initial state",
+        "ms": gdnf_ms, "tokens_per_s": 16 * 1024 / (gdnf_ms * 1e-3),
+        "fp32_frac": gdnf_flop / (gdnf_ms * 1e-3) / PEAK_FP32}
     out["variants"] = {
         "prefill_forward_f16": {"workload": "fp16 B=16 T=1024 H=32, initial state N(0,0.1^2)",
                                 "ms": f16_ms, "tokens_per_s": 16 * 1024 / (f16_ms * 1e-3),

@@ -225,6 +225,32 @@ wkv7_status wkv7_gdn_decode_step(int32_t B, int32_t H, int32_t Hk, int32_t N, in
                                  const float *beta, const float *s_in, float *s_out, void *out,
                                  void *stream);
 
+/*
+ * Workspace bytes of wkv7_gdn_forward: q^ and k^ in fp32, 2 * B*T*Hk*N * 4
+ * (each part 256-byte aligned). N = 64 or 128 (else WKV7_ERR_UNSUPPORTED);
+ * B, T, Hk >= 1 with B*T*Hk <= 2^24 (else WKV7_ERR_INVALID_ARGUMENT).
+ */
+wkv7_status wkv7_gdn_workspace_bytes(int32_t B, int32_t T, int32_t Hk, int32_t N, size_t *bytes);
+
+/*
+ * A dense batch of gated DeltaNet tokens (B rows of T tokens) through the
+ * same remap as wkv7_gdn_decode_step (rwkv-lab, "Highlight result -- GDN in
+ * RWKV-7"), token by token from s0 (or zero):
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k^_t k^_t^T) + beta_t v_t k^_t^T,
+ *     out_t = S_t q^_t / sqrt(N).
+ *   q, k   : [B, T, Hk, N]; v, out : [B, T, H, N]; type dtype, 16-byte aligned.
+ *   g, beta: fp32 [B, T, H], 4-byte aligned.
+ *   s0     : fp32 [B, H, N, N] or NULL (zero initial state).
+ *   s_out  : fp32 [B, H, N, N] final state, or NULL.
+ *   workspace : >= wkv7_gdn_workspace_bytes(B, T, Hk, N), 16-byte aligned.
+ * Value head h reads key head h / (H / Hk). H % Hk == 0 and B*H <= 2^24.
+ * Outputs may not overlap inputs, each other or the workspace.
+ */
+wkv7_status wkv7_gdn_forward(int32_t B, int32_t T, int32_t H, int32_t Hk, int32_t N, int32_t dtype,
+                             const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, const float *s0, void *out, float *s_out,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
 /* Number of checkpoint slots a dense forward needs: B * ceil(T / 16). */
 wkv7_status wkv7_checkpoint_slots(int32_t B, int32_t T, int64_t *slots);
 

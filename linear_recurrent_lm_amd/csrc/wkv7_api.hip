@@ -361,6 +361,59 @@ wkv7_status wkv7_gdn_decode_step(int32_t B, int32_t H, int32_t Hk, int32_t N, in
     return WKV7_OK;
 }
 
+wkv7_status wkv7_gdn_workspace_bytes(int32_t B, int32_t T, int32_t Hk, int32_t N, size_t *bytes) {
+    if (N != 64 && N != 128) return WKV7_ERR_UNSUPPORTED;
+    // the row pre-pass takes 4 token rows per 256-thread workgroup
+    if (B < 1 || T < 1 || Hk < 1 || (int64_t)B * T * Hk > (1 << 24)) return WKV7_ERR_INVALID_ARGUMENT;
+    if (!bytes) return WKV7_ERR_INVALID_ARGUMENT;
+    *bytes = 2 * pad256((size_t)B * T * Hk * N * sizeof(float));
+    return WKV7_OK;
+}
+
+wkv7_status wkv7_gdn_forward(int32_t B, int32_t T, int32_t H, int32_t Hk, int32_t N, int32_t dtype,
+                             const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, const float *s0, void *out, float *s_out,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    size_t need = 0;
+    wkv7_status st = wkv7_gdn_workspace_bytes(B, T, Hk, N, &need);
+    if (st != WKV7_OK) return st;
+    if (!dtype_ok(dtype)) return WKV7_ERR_UNSUPPORTED;
+    // one N-lane workgroup per (sequence, value head)
+    if (H < 1 || H % Hk != 0 || (int64_t)B * H > (1 << 24) || (int64_t)B * T * H * N > kMaxElems)
+        return WKV7_ERR_INVALID_ARGUMENT;
+    const void *streams[4] = {q, k, v, out};
+    if ((st = check_streams(streams, 4)) != WKV7_OK) return st;
+    if (!g || !beta || !aligned4(g) || !aligned4(beta)) return WKV7_ERR_INVALID_ARGUMENT;
+    if ((s0 && !aligned16(s0)) || (s_out && !aligned16(s_out))) return WKV7_ERR_INVALID_ARGUMENT;
+    if (!workspace || !aligned16(workspace)) return WKV7_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < need) return WKV7_ERR_WORKSPACE_TOO_SMALL;
+    const size_t es = elem_size(dtype);
+    const size_t state_bytes = (size_t)B * H * N * N * sizeof(float);
+    const size_t out_bytes = (size_t)B * T * H * N * es;
+    const void *ins[6] = {q, k, v, g, beta, s0};
+    const size_t in_bytes[6] = {(size_t)B * T * Hk * N * es, (size_t)B * T * Hk * N * es, out_bytes,
+                                (size_t)B * T * H * 4, (size_t)B * T * H * 4, s0 ? state_bytes : 0};
+    const void *outs[3] = {out, s_out, workspace};
+    const size_t outs_bytes[3] = {out_bytes, s_out ? state_bytes : 0, need};
+    for (int o = 0; o < 3; ++o) {
+        if (!outs[o] || !outs_bytes[o]) continue;
+        for (int q2 = 0; q2 < 6; ++q2)
+            if (ins[q2] && in_bytes[q2] && ranges_overlap(ins[q2], in_bytes[q2], outs[o], outs_bytes[o]))
+                return WKV7_ERR_INVALID_ARGUMENT;
+        for (int o2 = o + 1; o2 < 3; ++o2)
+            if (outs[o2] && outs_bytes[o2] && ranges_overlap(outs[o], outs_bytes[o], outs[o2], outs_bytes[o2]))
+                return WKV7_ERR_INVALID_ARGUMENT;
+    }
+    if ((st = check_device()) != WKV7_OK) return st;
+    wkv7::GdnFwdArgs a{};
+    a.B = B; a.T = T; a.H = H; a.Hk = Hk; a.N = N; a.dtype = dtype;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.s0 = s0; a.out = out; a.s_out = s_out;
+    a.qn = (float *)workspace;
+    a.kn = (float *)((char *)workspace + need / 2);
+    if (wkv7::launch_gdn_forward(a, (hipStream_t)stream) != hipSuccess) return WKV7_ERR_HIP;
+    return WKV7_OK;
+}
+
 wkv7_status vce_forward_workspace_bytes(int32_t M, int32_t D, int32_t V, size_t *bytes) {
     wkv7_status st = vce_check_sizes(M, D, V);
     if (st != WKV7_OK) return st;

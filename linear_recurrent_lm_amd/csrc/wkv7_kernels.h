@@ -72,6 +72,19 @@ struct GdnArgs {
     void *out;                       // [B][H][N], I/O type
 };
 hipError_t launch_gdn_decode(const GdnArgs &a, hipStream_t stream);
+// A sequence of GDN tokens through the remap (dense batch, no checkpoints).
+struct GdnFwdArgs {
+    int32_t B, T, H, Hk, N;
+    int dtype;
+    const void *q, *k;               // [B][T][Hk][N], I/O type
+    const void *v;                   // [B][T][H][N], I/O type
+    const float *g, *beta;           // [B][T][H]
+    const float *s0;                 // [B][H][N][N] or null (zero)
+    void *out;                       // [B][T][H][N], I/O type
+    float *s_out;                    // [B][H][N][N] or null
+    float *qn, *kn;                  // workspace: q^, k^ in fp32, [B][T][Hk][N] each
+};
+hipError_t launch_gdn_forward(const GdnFwdArgs &a, hipStream_t stream);
 // The WKV-7 step (not fused) at head size 128.
 hipError_t launch_decode128(const DecArgs &a, hipStream_t stream);
 

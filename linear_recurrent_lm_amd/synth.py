@@ -287,3 +287,18 @@ def make_gdn_inputs(B: int, H: int, Hk: int, N: int = 128, *, seed: int = 8, dty
     beta = rng.uniform(0.05, 1.0, (B, H)).astype(np.float32)
     s0 = rng.standard_normal((B, H, N, N), dtype=np.float32) * np.float32(state_std)
     return GDNInputs(q, k, v, g, beta, s0)
+
+
+def make_gdn_sequence(B: int, T: int, H: int, Hk: int, N: int = 128, *, seed: int = 10,
+                      dtype: str = "bf16", s0_std: float = 0.0) -> GDNInputs:
+    """A dense batch of GDN tokens, q, k [B, T, Hk, N], v [B, T, H, N],
+    g, beta [B, T, H], drawn as in make_gdn_inputs; s0 ~ N(0, s0_std^2)
+    [B, H, N, N], or None when s0_std is 0."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = round_to(rng.standard_normal((B, T, Hk, N), dtype=np.float32), dtype)
+    k = round_to(rng.standard_normal((B, T, Hk, N), dtype=np.float32), dtype)
+    v = round_to(rng.standard_normal((B, T, H, N), dtype=np.float32), dtype)
+    g = (-rng.uniform(0.01, 1.0, (B, T, H))).astype(np.float32)
+    beta = rng.uniform(0.05, 1.0, (B, T, H)).astype(np.float32)
+    s0 = (rng.standard_normal((B, H, N, N), dtype=np.float32) * np.float32(s0_std)) if s0_std else None
+    return GDNInputs(q, k, v, g, beta, s0)

@@ -77,12 +77,14 @@ def lib():
         L.wkv7_status_string.restype = ctypes.c_char_p
         L.wkv7_abi_version.restype = i32
         L.wkv7_gdn_decode_step.argtypes = [i32] * 5 + [vp] * 9
+        L.wkv7_gdn_workspace_bytes.argtypes = [i32] * 4 + [ctypes.POINTER(sz)]
+        L.wkv7_gdn_forward.argtypes = [i32] * 6 + [vp] * 9 + [sz, vp]
         L.vce_forward_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.vce_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.vce_forward.argtypes = [i32, i32, i32] + [vp] * 6 + [sz, vp]
         L.vce_backward.argtypes = [i32, i32, i32, i32] + [vp] * 8 + [sz, vp]
         for fn in ("wkv7_forward", "wkv7_backward", "wkv7_decode_step", "wkv7_decode_step_fused",
-                   "wkv7_gdn_decode_step",
+                   "wkv7_gdn_decode_step", "wkv7_gdn_workspace_bytes", "wkv7_gdn_forward",
                    "wkv7_checkpoint_slots",
                    "wkv7_workspace_bytes", "wkv7_segments_check", "vce_forward_workspace_bytes",
                    "vce_backward_workspace_bytes", "vce_forward", "vce_backward"):
@@ -337,6 +339,39 @@ def wkv7_gdn_decode_step(q, k, v, g, beta, s_in, s_out=None, out=None):
     _check("wkv7_gdn_decode_step", lib().wkv7_gdn_decode_step(
         B, H, Hk, N, _dtype_code(v), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
         _ptr(s_in), _ptr(s_out), _ptr(out), _stream()))
+    return out, s_out
+
+
+def wkv7_gdn_workspace_bytes(B, T, Hk, N) -> int:
+    out = ctypes.c_size_t(0)
+    _check("wkv7_gdn_workspace_bytes", lib().wkv7_gdn_workspace_bytes(B, T, Hk, N, ctypes.byref(out)))
+    return out.value
+
+
+def wkv7_gdn_forward(q, k, v, g, beta, s0=None, *, out=None, want_state=True, workspace=None):
+    """A dense batch of gated DeltaNet tokens through the RWKV-7 remap: q, k
+    [B, T, Hk, N], v [B, T, H, N] (one dtype), g, beta fp32 [B, T, H], s0
+    fp32 [B, H, N, N] or None. Returns (out [B, T, H, N], s_out or None)."""
+    torch = _torch()
+    dev = v.device
+    B, T, H, N = v.shape
+    Hk = q.shape[2]
+    dt = v.dtype
+    _req(q, "q", dev, dt, (B, T, Hk, N))
+    _req(k, "k", dev, dt, (B, T, Hk, N))
+    _req(v, "v", dev, dt)
+    _req(g, "g", dev, torch.float32, (B, T, H))
+    _req(beta, "beta", dev, torch.float32, (B, T, H))
+    if s0 is not None:
+        _req(s0, "s0", dev, torch.float32, (B, H, N, N))
+    out = torch.empty_like(v) if out is None else out
+    _req(out, "out", dev, dt, (B, T, H, N))
+    s_out = torch.empty((B, H, N, N), device=dev, dtype=torch.float32) if want_state else None
+    need = wkv7_gdn_workspace_bytes(B, T, Hk, N)
+    ws = torch.empty(need, device=dev, dtype=torch.uint8) if workspace is None else workspace
+    _check("wkv7_gdn_forward", lib().wkv7_gdn_forward(
+        B, T, H, Hk, N, _dtype_code(v), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
+        _ptr(out), _ptr(s_out), _ptr(ws), ws.numel(), _stream()))
     return out, s_out
 
 

@@ -150,6 +150,32 @@ def test_gdn_decode_rejects_bad_arguments():
                 k=far[1], v=far[2], g=far[3], beta=far[4]) == INVALID
 
 
+def test_gdn_forward_rejects_bad_arguments():
+    L = W.lib()
+    far = [ctypes.c_void_p((q + 1) << 40) for q in range(12)]
+    BIG = 1 << 38
+
+    def call(B=2, T=8, H=4, Hk=2, N=128, dt=1, q=far[0], k=far[1], v=far[2], g=far[3],
+             beta=far[4], s0=None, out=far[5], s_out=far[6], ws=far[7], nbytes=BIG):
+        return L.wkv7_gdn_forward(B, T, H, Hk, N, dt, q, k, v, g, beta, s0, out, s_out, ws,
+                                  nbytes, None)
+    assert call(N=96) == UNSUPPORTED
+    assert call(dt=7) == UNSUPPORTED
+    assert call(T=0) == INVALID
+    assert call(H=6, Hk=4) == INVALID
+    for name in ("q", "k", "v", "g", "beta", "out", "ws"):
+        assert call(**{name: None}) == INVALID, name
+    assert call(q=ctypes.c_void_p(far[0].value + 8)) == INVALID
+    assert call(s0=ctypes.c_void_p(far[8].value + 4)) == INVALID
+    assert call(out=ctypes.c_void_p(far[2].value + 64)) == INVALID       # out overlaps v
+    assert call(s_out=ctypes.c_void_p(far[7].value + 256)) == INVALID    # s_out overlaps the workspace
+    need = W.wkv7_gdn_workspace_bytes(2, 8, 2, 128)
+    assert need == 2 * 2 * 8 * 2 * 128 * 4
+    assert call(nbytes=need - 1) == WS
+    with pytest.raises(W.WKV7Error):
+        W.wkv7_gdn_workspace_bytes(2, 8, 2, 96)
+
+
 def test_checkpoint_slots():
     assert W.checkpoint_slots(3, 33) == 9
     assert W.checkpoint_slots(2, 16) == 2

@@ -87,3 +87,59 @@ def test_gdn_decode_chain(W):
         torch.cuda.synchronize()
         assert unit_err(U.host(out), ro) <= U.TOL_F32
     assert U.unit_err_state(U.host(s_dev), s_ref) <= U.TOL_F32
+
+
+def run_seq(W, inp, dtype):
+    import torch
+    q, k, v = (U.dev_stream(x, dtype) for x in (inp.q, inp.k, inp.v))
+    s0 = None if inp.s0 is None else U.dev_f32(inp.s0)
+    out, s_out = W.wkv7_gdn_forward(q, k, v, U.dev_f32(inp.g), U.dev_f32(inp.beta), s0)
+    torch.cuda.synchronize()
+    return U.host(out), U.host(s_out)
+
+
+@pytest.mark.parametrize("N", [128, 64])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_gdn_forward_parity(W, N, dtype):
+    """T = 37 tokens, two value heads per key head, with an initial state."""
+    inp = synth.make_gdn_sequence(3, 37, 4, 2, N, seed=51, dtype=dtype, s0_std=0.1)
+    out, s_out = run_seq(W, inp, dtype)
+    ro, rs = O.gdn_forward(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.s0)
+    assert U.unit_err_dense(out, ro) <= TOL[dtype]
+    assert U.unit_err_state(s_out, rs) <= U.TOL_F32
+
+
+@pytest.mark.parametrize("T", [1, 2, 16])
+def test_gdn_forward_short_and_zero_state(W, T):
+    inp = synth.make_gdn_sequence(2, T, 2, 2, 128, seed=52 + T, dtype="f32")
+    out, s_out = run_seq(W, inp, "f32")
+    ro, rs = O.gdn_forward(inp.q, inp.k, inp.v, inp.g, inp.beta, None)
+    assert U.unit_err_dense(out, ro) <= U.TOL_F32
+    assert U.unit_err_state(s_out, rs) <= U.TOL_F32
+
+
+def test_gdn_forward_equals_decode_steps(W):
+    """The sequence call equals T decode steps with the state carried."""
+    import torch
+    inp = synth.make_gdn_sequence(2, 9, 4, 2, 128, seed=55, dtype="f32", s0_std=0.1)
+    out, s_out = run_seq(W, inp, "f32")
+    st = U.dev_f32(inp.s0)
+    for t in range(9):
+        o, _ = W.wkv7_gdn_decode_step(*(U.dev_f32(np.ascontiguousarray(x[:, t])) for x in (inp.q, inp.k, inp.v)),
+                                      U.dev_f32(np.ascontiguousarray(inp.g[:, t])),
+                                      U.dev_f32(np.ascontiguousarray(inp.beta[:, t])), st, s_out=st)
+        torch.cuda.synchronize()
+        assert unit_err(U.host(o), out[:, t]) <= U.TOL_F32
+    assert U.unit_err_state(U.host(st), s_out) <= U.TOL_F32
+
+
+def test_gdn_forward_prefill_sampled(W):
+    """Prefill at GDN's layer geometry: B = 16, T = 1024, 32 value heads over
+    16 key heads, N = 128, bf16; rows 0 and 15 (all heads) against the oracle."""
+    inp = synth.make_gdn_sequence(16, 1024, 32, 16, 128, seed=56, dtype="bf16")
+    out, s_out = run_seq(W, inp, "bf16")
+    for b in (0, 15):
+        sl = slice(b, b + 1)
+        ro, rs = O.gdn_forward(inp.q[sl], inp.k[sl], inp.v[sl], inp.g[sl], inp.beta[sl], None)
+        assert U.unit_err_dense(out[sl], ro) <= U.TOL_BF16_Y, b
+        assert U.unit_err_state(s_out[sl], rs) <= U.TOL_F32, b
