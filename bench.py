@@ -293,6 +293,16 @@ def main():
                        args.warmup, args.steps, ev)
     gdnf_flop = 7 * 128 * 128 * 16 * 1024 * 32
     del sq, sk, sv, sg, sb, sout, sws
+    # The WKV-7 forward at head size 128 (token-order kernel), prefill shape.
+    win = synth.make_inputs(16, 1024, 32, 128, seed=12, dtype="bf16", s0_std=0.1)
+    wts = [torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in win.streams()]
+    ws0 = torch.from_numpy(win.s0).to(dev)
+    del win
+    wy = torch.empty_like(wts[0])
+    wso = torch.empty_like(ws0)
+    f128_ms = _time_ms(lambda: W.wkv7_forward(*wts, ws0, y=wy, s_out=wso), args.warmup, args.steps, ev)
+    f128_flop = 9 * 128 * 128 * 16 * 1024 * 32
+    del wts, ws0, wy, wso
 
     # I/O variants: the prefill workload drawn in fp16; the training step with
     # w given as log(decay) and fp32 gradients.
@@ -411,6 +421,10 @@ def main():
                     "heads, N=128, zero initial state",
         "ms": gdnf_ms, "tokens_per_s": 16 * 1024 / (gdnf_ms * 1e-3),
         "fp32_frac": gdnf_flop / (gdnf_ms * 1e-3) / PEAK_FP32}
+    out["prefill_forward_n128"] = {
+        "workload": "WKV-7 forward at head size 128, bf16 B=16 T=1024 H=32, initial state N(0,0.1^2)",
+        "ms": f128_ms, "tokens_per_s": 16 * 1024 / (f128_ms * 1e-3),
+        "fp32_frac": f128_flop / (f128_ms * 1e-3) / PEAK_FP32}
     out["variants"] = {
         "prefill_forward_f16": {"workload": "fp16 B=16 T=1024 H=32, initial state N(0,0.1^2)",
                                 "ms": f16_ms, "tokens_per_s": 16 * 1024 / (f16_ms * 1e-3),

@@ -96,7 +96,7 @@ typedef struct {
     int32_t B;                  /* rows */
     int32_t T;                  /* tokens per row, >= 1 */
     int32_t H;                  /* heads, 1 <= H <= 65536 */
-    int32_t N;                  /* head size; must be 64 */
+    int32_t N;                  /* head size: 64, or 128 for wkv7_forward only */
     int32_t dtype;              /* wkv7_dtype of r,w,k,v,a,b,y,dy and dr..db */
     int32_t num_seqs;           /* 0 = dense mode */
     const int32_t *seq_start;   /* device [num_seqs]: flat start token b*T + t */

@@ -31,16 +31,18 @@ size_t elem_size(int dtype) { return dtype == WKV7_F32 ? 4 : 2; }
 
 bool dtype_ok(int32_t dtype) { return dtype == WKV7_F32 || dtype == WKV7_BF16 || dtype == WKV7_F16; }
 
-wkv7_status check_desc(const wkv7_desc *d) {
+// wide: the call also takes head size 128 (the forward does; the backward
+// and its workspace query do not).
+wkv7_status check_desc(const wkv7_desc *d, bool wide = false) {
     if (!d) return WKV7_ERR_INVALID_ARGUMENT;
-    if (d->N != kN) return WKV7_ERR_UNSUPPORTED;
+    if (d->N != kN && !(wide && d->N == 128)) return WKV7_ERR_UNSUPPORTED;
     if (!dtype_ok(d->dtype)) return WKV7_ERR_UNSUPPORTED;
     if (d->decay != WKV7_DECAY_MULT && d->decay != WKV7_DECAY_LOG) return WKV7_ERR_UNSUPPORTED;
     if (d->grad_f32 != 0 && d->grad_f32 != 1) return WKV7_ERR_INVALID_ARGUMENT;
     if (d->B < 1 || d->T < 1 || d->H < 1 || d->H > kMaxHeads) return WKV7_ERR_INVALID_ARGUMENT;
     const int64_t toks = (int64_t)d->B * d->T;
     if (toks > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
-    if (toks * d->H * kN > kMaxElems) return WKV7_ERR_INVALID_ARGUMENT;
+    if (toks * d->H * d->N > kMaxElems) return WKV7_ERR_INVALID_ARGUMENT;
     if (d->num_seqs < 0) return WKV7_ERR_INVALID_ARGUMENT;
     if (d->num_seqs > 0 && (!d->seq_start || !d->seq_len)) return WKV7_ERR_INVALID_ARGUMENT;
     const int64_t S = d->num_seqs > 0 ? d->num_seqs : d->B;
@@ -206,12 +208,12 @@ wkv7_status wkv7_segments_check(int32_t B, int32_t T, int32_t num_seqs, const in
 wkv7_status wkv7_forward(const wkv7_desc *d, const void *r, const void *w, const void *k,
                          const void *v, const void *a, const void *b, const float *s0, void *y,
                          float *s_out, float *ckpt, void *stream) {
-    wkv7_status st = check_desc(d);
+    wkv7_status st = check_desc(d, true);
     if (st != WKV7_OK) return st;
     const void *streams[7] = {r, w, k, v, a, b, y};
     if ((st = check_streams(streams, 7)) != WKV7_OK) return st;
     if ((s0 && !aligned16(s0)) || (s_out && !aligned16(s_out))) return WKV7_ERR_INVALID_ARGUMENT;
-    const size_t state_bytes = (size_t)num_states(d) * d->H * kN * kN * sizeof(float);
+    const size_t state_bytes = (size_t)num_states(d) * d->H * d->N * d->N * sizeof(float);
     if (s0 && s_out && ranges_overlap(s0, state_bytes, s_out, state_bytes))
         return WKV7_ERR_INVALID_ARGUMENT;
     if ((st = check_ckpt(d, ckpt)) != WKV7_OK) return st;
@@ -225,11 +227,15 @@ wkv7_status wkv7_forward(const wkv7_desc *d, const void *r, const void *w, const
     args.r = r; args.w = w; args.k = k; args.v = v; args.a = a; args.b = b;
     args.s0 = s0; args.y = y; args.s_out = s_out; args.ckpt = ckpt;
     if (d->num_seqs > 0) {
+        // a [.., H, 128] stream is laid out as [.., 2H, 64]
+        wkv7::SegParams zs = args.seg;
+        zs.H = d->H * (d->N / kN);
         void *outs[1] = {y};
-        if (wkv7::launch_zero_uncovered(args.seg, d->dtype, outs, 1, hs) != hipSuccess)
+        if (wkv7::launch_zero_uncovered(zs, d->dtype, outs, 1, hs) != hipSuccess)
             return WKV7_ERR_HIP;
     }
-    if (wkv7::launch_forward(args, hs) != hipSuccess) return WKV7_ERR_HIP;
+    const hipError_t e = d->N == 128 ? wkv7::launch_forward128(args, hs) : wkv7::launch_forward(args, hs);
+    if (e != hipSuccess) return WKV7_ERR_HIP;
     return WKV7_OK;
 }
 

@@ -72,6 +72,9 @@ struct GdnArgs {
     void *out;                       // [B][H][N], I/O type
 };
 hipError_t launch_gdn_decode(const GdnArgs &a, hipStream_t stream);
+// The WKV-7 forward at head size 128 (FwdArgs as for 64; token order).
+hipError_t launch_forward128(const FwdArgs &a, hipStream_t stream);
+
 // A sequence of GDN tokens through the remap (dense batch, no checkpoints).
 struct GdnFwdArgs {
     int32_t B, T, H, Hk, N;

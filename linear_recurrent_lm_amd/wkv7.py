@@ -163,9 +163,9 @@ def _decay(decay):
     return DECAY[decay]
 
 
-def _desc(B, T, H, dtype, seg: Segments | None, decay="mult", grad_f32=False):
+def _desc(B, T, H, dtype, seg: Segments | None, decay="mult", grad_f32=False, n=N):
     d = Desc()
-    d.B, d.T, d.H, d.N, d.dtype = B, T, H, N, dtype
+    d.B, d.T, d.H, d.N, d.dtype = B, T, H, n, dtype
     d.decay = _decay(decay)
     d.grad_f32 = 1 if grad_f32 else 0
     if seg is None:
@@ -191,29 +191,28 @@ def checkpoint_slots(B, T, seg: Segments | None = None) -> int:
 def wkv7_forward(r, w, k, v, a, b, s0=None, *, segments: Segments | None = None,
                  checkpoints: bool = False, state_out: bool = True, y=None, s_out=None,
                  ckpt=None, decay: str = "mult"):
-    """y, s_out, ckpt = wkv7_forward(...). s_out/ckpt are None when not requested."""
+    """y, s_out, ckpt = wkv7_forward(...). s_out/ckpt are None when not requested.
+    Head size n = 64 (chunked kernels) or 128 (token-order kernel)."""
     torch = _torch()
     B, T, H, n = r.shape
-    if n != N:
-        raise ValueError("head size must be 64")
     dev = r.device
     for name, t in zip("rwkvab", (r, w, k, v, a, b)):
         _req(t, name, dev, r.dtype, r.shape)
     S = segments.num_seqs if segments is not None else B
     if s0 is not None:
-        _req(s0, "s0", dev, torch.float32, (S, H, N, N))
+        _req(s0, "s0", dev, torch.float32, (S, H, n, n))
     y = torch.empty_like(r) if y is None else y
     _req(y, "y", dev, r.dtype, r.shape)
     if state_out and s_out is None:
-        s_out = torch.empty((S, H, N, N), device=dev, dtype=torch.float32)
+        s_out = torch.empty((S, H, n, n), device=dev, dtype=torch.float32)
     if not state_out:
         s_out = None
     if checkpoints and ckpt is None:
-        ckpt = torch.empty((checkpoint_slots(B, T, segments), H, N, N), device=dev,
+        ckpt = torch.empty((checkpoint_slots(B, T, segments), H, n, n), device=dev,
                            dtype=torch.float32)
     if not checkpoints:
         ckpt = None
-    d = _desc(B, T, H, _dtype_code(r), segments, decay)
+    d = _desc(B, T, H, _dtype_code(r), segments, decay, n=n)
     _check("wkv7_forward", lib().wkv7_forward(
         ctypes.byref(d), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(s0), _ptr(y),
         _ptr(s_out), _ptr(ckpt), _stream()))

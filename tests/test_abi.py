@@ -47,7 +47,11 @@ def test_version_and_status_strings():
 
 def test_forward_rejects_bad_descriptors():
     assert fwd(None) == INVALID
-    assert fwd(desc(N=128)) == UNSUPPORTED
+    assert fwd(desc(N=96)) == UNSUPPORTED
+    assert fwd(desc(N=256)) == UNSUPPORTED
+    # head size 128 is a forward size: with N = 128 the other checks still apply
+    assert fwd(desc(N=128, B=0)) == INVALID
+    assert fwd(desc(N=128, dtype=7)) == UNSUPPORTED
     assert fwd(desc(dtype=7)) == UNSUPPORTED
     assert fwd(desc(dtype=-1)) == UNSUPPORTED
     assert fwd(desc(decay=2)) == UNSUPPORTED                    # neither multiplicative nor log
@@ -81,6 +85,7 @@ def test_backward_rejects_bad_arguments():
     call = lambda d, ckpt=P[6], grads=grads, ws=None, wsb=0: L.wkv7_backward(
         ctypes.byref(d), *P[:6], ckpt, None, None, *grads, None, ws, wsb, None)
     assert call(desc(N=32)) == UNSUPPORTED
+    assert call(desc(N=128)) == UNSUPPORTED        # the backward is built for head size 64
     assert call(d, ckpt=None) == INVALID
     for q in range(6):
         g = list(grads); g[q] = None
@@ -191,6 +196,7 @@ def test_workspace_query():
     assert W.wkv7_workspace_bytes(3, 33, 2, 0) == 9 * 2 * per * 4
     n = ctypes.c_size_t()
     assert W.lib().wkv7_workspace_bytes(ctypes.byref(desc(N=48)), ctypes.byref(n)) == UNSUPPORTED
+    assert W.lib().wkv7_workspace_bytes(ctypes.byref(desc(N=128)), ctypes.byref(n)) == UNSUPPORTED
 
 
 def test_segments_check_matches_layout_helpers():
