@@ -4,8 +4,9 @@
  * The operation (RWKV-7 "Goose" WKV-7, the recurrence the rwkv-metal page's
  * section "The Metal WKV-7 kernel" and the model card's "Transformers
  * quickstart" section describe as the one custom kernel of the model): per
- * independent unit -- one (sequence, head) pair -- with head size N = 64 and
- * an fp32 state S in R^{64x64} indexed [value i, key j], every token t does
+ * independent unit -- one (sequence, head) pair -- with head size N = 64 (the
+ * forward and the decode steps also take N = 128) and an fp32 state S in
+ * R^{NxN} indexed [value i, key j], every token t does
  *
  *     S_t = S_{t-1} diag(w_t) + (S_{t-1} a_t) b_t^T + v_t k_t^T,   y_t = S_t r_t
  *
@@ -76,7 +77,7 @@ extern "C" {
 typedef enum {
     WKV7_OK = 0,
     WKV7_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, bad size, bad table */
-    WKV7_ERR_UNSUPPORTED = 2,        /* e.g. N != 64, unknown dtype, no gfx950 device */
+    WKV7_ERR_UNSUPPORTED = 2,        /* e.g. a head size the call does not take, unknown dtype, no gfx950 device */
     WKV7_ERR_WORKSPACE_TOO_SMALL = 3,
     WKV7_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
 } wkv7_status;
