@@ -55,35 +55,44 @@ __global__ __launch_bounds__(N) void gdn_fwd_kernel(int32_t T, int32_t H, int32_
                                                    const TI *__restrict__ v, const float *__restrict__ g,
                                                    const float *__restrict__ beta, const float *__restrict__ s0,
                                                    TI *__restrict__ out, float *__restrict__ s_out) {
-    constexpr int TB = 16;                 // tokens per staged block
+    constexpr int TB = 8;                  // tokens per staged block
+    constexpr int KH = N / 2;              // keys per lane
+    constexpr int NQ = KH / 4;             // 16-byte quads per lane and row
     constexpr int LD = TB * 2 * N / 4 / N; // float4 loads per thread per block (k^ and q^ rows)
-    __shared__ __align__(16) float rows[2][TB][2][N];   // [buffer][token][k^, q^][N]
+    __shared__ __align__(16) float rows[2][TB][2][N];   // [buffer][token][k^, q^][N], halves interleaved
     const int64_t unit = blockIdx.x;       // b * H + h
     const int h = (int)(unit % H);
     const int64_t b = unit / H;
     const int kh = h / (H / Hk);
-    const int i = threadIdx.x;
-    const int64_t srow = (unit * N + i) * N;
+    const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
+    const int hf = ln >> 5;                           // key half: keys [hf KH, hf KH + KH)
+    const int i0 = wv * 64 + (ln & 31), i1 = i0 + 32; // the lane's two state rows
+    const int64_t srow0 = (unit * N + i0) * N + hf * KH;
+    const int64_t srow1 = srow0 + 32 * N;
 
-    float S[N];
+    float S0[KH], S1[KH];
     if (s0) {
 #pragma unroll
-        for (int j = 0; j < N; j += 4) {
-            const f32x4 x = *(const f32x4 *)(s0 + srow + j);
-            S[j] = x.x; S[j + 1] = x.y; S[j + 2] = x.z; S[j + 3] = x.w;
+        for (int j = 0; j < KH; j += 4) {
+            const f32x4 x = *(const f32x4 *)(s0 + srow0 + j);
+            S0[j] = x.x; S0[j + 1] = x.y; S0[j + 2] = x.z; S0[j + 3] = x.w;
+            const f32x4 z = *(const f32x4 *)(s0 + srow1 + j);
+            S1[j] = z.x; S1[j + 1] = z.y; S1[j + 2] = z.z; S1[j + 3] = z.w;
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < N; ++j) S[j] = 0.f;
+        for (int j = 0; j < KH; ++j) S0[j] = S1[j] = 0.f;
     }
 
-    // Block loads: element c = q*N + i of the block's [TB][2][N/4] float4s
-    // (token, k^ or q^, column quad); tokens past T are clamped to T-1.
+    // Block loads: element c = q*N + tid of the block's [TB][2][N/4] float4s
+    // (token, k^ or q^, column quad); tokens past T are clamped to T-1. Quad
+    // c4 of key half c4 / NQ is stored at slot 2 (c4 % NQ) + c4 / NQ, so the
+    // two halves' broadcast reads fall in different banks.
     f32x4 st[LD];
     auto load_block = [&](int t0) {
 #pragma unroll
         for (int q = 0; q < LD; ++q) {
-            const int c = q * N + i;
+            const int c = q * N + tid;
             const int tt = c / (N / 2), which = (c / (N / 4)) & 1, quad = c % (N / 4);
             const int64_t tok = b * T + min(t0 + tt, T - 1);
             const float *src = which ? qn : kn;
@@ -93,9 +102,9 @@ __global__ __launch_bounds__(N) void gdn_fwd_kernel(int32_t T, int32_t H, int32_
     auto store_block = [&](int buf) {
 #pragma unroll
         for (int q = 0; q < LD; ++q) {
-            const int c = q * N + i;
+            const int c = q * N + tid;
             const int tt = c / (N / 2), which = (c / (N / 4)) & 1, quad = c % (N / 4);
-            *(f32x4 *)&rows[buf][tt][which][quad * 4] = st[q];
+            *(f32x4 *)&rows[buf][tt][which][4 * (2 * (quad % NQ) + quad / NQ)] = st[q];
         }
     };
 
@@ -110,46 +119,71 @@ __global__ __launch_bounds__(N) void gdn_fwd_kernel(int32_t T, int32_t H, int32_
         const int tn = min(TB, T - t0);
         for (int tt = 0; tt < tn; ++tt) {
             const int64_t tok = b * T + t0 + tt;
-            const float *kr = rows[buf][tt][0];
-            const float *qr = rows[buf][tt][1];
+            // the lane's key half: quad q of it at 8 q floats from here
+            const float *kr = rows[buf][tt][0] + 4 * hf;
+            const float *qr = rows[buf][tt][1] + 4 * hf;
             const float e = expf(g[tok * H + h]);
             const float bt = beta[tok * H + h];
-            const float vi = IO<TI>::ld(v, (tok * H + h) * N + i);
-            float s4[4] = {0.f, 0.f, 0.f, 0.f};
+            const float v0 = IO<TI>::ld(v, (tok * H + h) * N + i0);
+            const float v1 = IO<TI>::ld(v, (tok * H + h) * N + i1);
+            float p0[4] = {0.f, 0.f, 0.f, 0.f}, p1[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < N; j += 4) {
-                const f32x4 kq = *(const f32x4 *)(kr + j);
-                s4[0] = fmaf(S[j], kq.x, s4[0]);
-                s4[1] = fmaf(S[j + 1], kq.y, s4[1]);
-                s4[2] = fmaf(S[j + 2], kq.z, s4[2]);
-                s4[3] = fmaf(S[j + 3], kq.w, s4[3]);
+            for (int q = 0; q < NQ; ++q) {
+                const f32x4 kq = *(const f32x4 *)(kr + 8 * q);
+                const int j = 4 * q;
+                p0[0] = fmaf(S0[j], kq.x, p0[0]);
+                p0[1] = fmaf(S0[j + 1], kq.y, p0[1]);
+                p0[2] = fmaf(S0[j + 2], kq.z, p0[2]);
+                p0[3] = fmaf(S0[j + 3], kq.w, p0[3]);
+                p1[0] = fmaf(S1[j], kq.x, p1[0]);
+                p1[1] = fmaf(S1[j + 1], kq.y, p1[1]);
+                p1[2] = fmaf(S1[j + 2], kq.z, p1[2]);
+                p1[3] = fmaf(S1[j + 3], kq.w, p1[3]);
             }
-            const float c = bt * fmaf(-e, (s4[0] + s4[1]) + (s4[2] + s4[3]), vi);
-            float y4[4] = {0.f, 0.f, 0.f, 0.f};
+            float sa0 = (p0[0] + p0[1]) + (p0[2] + p0[3]);
+            float sa1 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
+            sa0 += __shfl_xor(sa0, 32);
+            sa1 += __shfl_xor(sa1, 32);
+            const float c0 = bt * fmaf(-e, sa0, v0);
+            const float c1 = bt * fmaf(-e, sa1, v1);
+            float y0[4] = {0.f, 0.f, 0.f, 0.f}, y1[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < N; j += 4) {
-                const f32x4 kq = *(const f32x4 *)(kr + j);
-                const f32x4 qq = *(const f32x4 *)(qr + j);
-                S[j] = fmaf(kq.x, c, S[j] * e);
-                S[j + 1] = fmaf(kq.y, c, S[j + 1] * e);
-                S[j + 2] = fmaf(kq.z, c, S[j + 2] * e);
-                S[j + 3] = fmaf(kq.w, c, S[j + 3] * e);
-                y4[0] = fmaf(S[j], qq.x, y4[0]);
-                y4[1] = fmaf(S[j + 1], qq.y, y4[1]);
-                y4[2] = fmaf(S[j + 2], qq.z, y4[2]);
-                y4[3] = fmaf(S[j + 3], qq.w, y4[3]);
+            for (int q = 0; q < NQ; ++q) {
+                const f32x4 kq = *(const f32x4 *)(kr + 8 * q);
+                const f32x4 qq = *(const f32x4 *)(qr + 8 * q);
+                const int j = 4 * q;
+                S0[j] = fmaf(kq.x, c0, S0[j] * e);
+                S0[j + 1] = fmaf(kq.y, c0, S0[j + 1] * e);
+                S0[j + 2] = fmaf(kq.z, c0, S0[j + 2] * e);
+                S0[j + 3] = fmaf(kq.w, c0, S0[j + 3] * e);
+                S1[j] = fmaf(kq.x, c1, S1[j] * e);
+                S1[j + 1] = fmaf(kq.y, c1, S1[j + 1] * e);
+                S1[j + 2] = fmaf(kq.z, c1, S1[j + 2] * e);
+                S1[j + 3] = fmaf(kq.w, c1, S1[j + 3] * e);
+                y0[0] = fmaf(S0[j], qq.x, y0[0]);
+                y0[1] = fmaf(S0[j + 1], qq.y, y0[1]);
+                y0[2] = fmaf(S0[j + 2], qq.z, y0[2]);
+                y0[3] = fmaf(S0[j + 3], qq.w, y0[3]);
+                y1[0] = fmaf(S1[j], qq.x, y1[0]);
+                y1[1] = fmaf(S1[j + 1], qq.y, y1[1]);
+                y1[2] = fmaf(S1[j + 2], qq.z, y1[2]);
+                y1[3] = fmaf(S1[j + 3], qq.w, y1[3]);
             }
-            IO<TI>::st(out, (tok * H + h) * N + i, ((y4[0] + y4[1]) + (y4[2] + y4[3])) * scale);
+            float o0 = (y0[0] + y0[1]) + (y0[2] + y0[3]);
+            float o1 = (y1[0] + y1[1]) + (y1[2] + y1[3]);
+            o0 += __shfl_xor(o0, 32);
+            o1 += __shfl_xor(o1, 32);
+            // key half 0 writes row i0, key half 1 row i1: 64 consecutive outputs per wave
+            IO<TI>::st(out, (tok * H + h) * N + (hf ? i1 : i0), (hf ? o1 : o0) * scale);
         }
         if (blk + 1 < nblk) store_block(buf ^ 1);
         __syncthreads();
     }
     if (s_out) {
 #pragma unroll
-        for (int j = 0; j < N; j += 4) {
-            f32x4 x;
-            x.x = S[j]; x.y = S[j + 1]; x.z = S[j + 2]; x.w = S[j + 3];
-            *(f32x4 *)(s_out + srow + j) = x;
+        for (int j = 0; j < KH; j += 4) {
+            *(f32x4 *)(s_out + srow0 + j) = f32x4{S0[j], S0[j + 1], S0[j + 2], S0[j + 3]};
+            *(f32x4 *)(s_out + srow1 + j) = f32x4{S1[j], S1[j + 1], S1[j + 2], S1[j + 3]};
         }
     }
 }
