@@ -6,17 +6,17 @@
 // at every 16th token of a sequence (the state entering tokens 0, 16, 32...).
 //
 // One workgroup of 128 lanes (two waves) per (sequence, head). In wave v,
-// lane l holds key half l / 32 (64 keys) of state rows 64 v + l % 32 and
-// 64 v + l % 32 + 32, so every row value a lane reads serves two state rows;
-// the two key halves of a row add their partial dot products with one lane
-// exchange inside the wave. The r, w, k, a, b rows of a block of tokens (16
-// for 16-bit streams, 8 for fp32) are staged in LDS as fp32 (w already
-// exponentiated when it holds log(decay)), double-buffered with the next
-// block's loads in flight, and read as 16-byte broadcasts, one address per
-// key half; the halves' 16-byte chunks alternate in a row so that the two
-// addresses fall in different banks. Per token and lane: 128 multiply-adds
-// for the two rows' S a, 3 x 128 for their update and 128 for S r, against 80
-// broadcasts per wave.
+// lane l holds key quarter l / 16 (32 keys) of the four state rows
+// 64 v + l % 16 + 16 m, m = 0..3, so every row value a lane reads serves four
+// state rows; the four key quarters of a row add their partial dot products
+// with two lane exchanges inside the wave. The r, w, k, a, b rows of a block
+// of tokens (8 for 16-bit streams, 4 for fp32) are staged in LDS as fp32 (w
+// already exponentiated when it holds log(decay)), double-buffered with the
+// next block's loads in flight, and read as 16-byte broadcasts, one address
+// per key quarter; the quarters' 16-byte chunks alternate in a row so that the
+// four addresses fall in different banks. Per token and lane: 128
+// multiply-adds for the rows' S a, 3 x 128 for their update and 128 for S r,
+// against 40 broadcasts per wave (one row per lane over all keys takes 160).
 #include "wkv7_kernels.h"
 
 namespace wkv7 {
@@ -71,25 +71,26 @@ __global__ __launch_bounds__(128) void fwd128_kernel(FwdArgs p) {
     const int64_t unit = blockIdx.x;
     const int sq = (int)(unit / H), h = (int)(unit % H);
     const Unit u = resolve_unit(p.seg, sq);
+    constexpr int RPL = 4, KL = N / RPL, NQ = KL / 4;   // rows per lane, keys per lane, quads
     const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
-    const int kh = ln >> 5;                          // key half: keys [64 kh, 64 kh + 64)
-    const int i0 = wv * 64 + (ln & 31), i1 = i0 + 32; // the lane's two state rows
+    const int kq = ln >> 4;                          // key quarter: keys [32 kq, 32 kq + 32)
+    const int rb = wv * 64 + (ln & 15);              // the lane's rows: rb + 16 m, m = 0..3
     const int64_t ts = (int64_t)H * N;               // stream pitch of one token
-    const int64_t srow0 = ((int64_t)unit * N + i0) * N + kh * 64;
-    const int64_t srow1 = srow0 + 32 * N;
+    const int64_t srow = ((int64_t)unit * N + rb) * N + kq * KL;
 
-    float S0[64], S1[64];
-    if (p.s0) {
+    float S[RPL][KL];
 #pragma unroll
-        for (int j = 0; j < 64; j += 4) {
-            const f32x4 x = *(const f32x4 *)(p.s0 + srow0 + j);
-            S0[j] = x.x; S0[j + 1] = x.y; S0[j + 2] = x.z; S0[j + 3] = x.w;
-            const f32x4 z = *(const f32x4 *)(p.s0 + srow1 + j);
-            S1[j] = z.x; S1[j + 1] = z.y; S1[j + 2] = z.z; S1[j + 3] = z.w;
+    for (int m = 0; m < RPL; ++m) {
+        if (p.s0) {
+#pragma unroll
+            for (int j = 0; j < KL; j += 4) {
+                const f32x4 x = *(const f32x4 *)(p.s0 + srow + 16 * m * N + j);
+                S[m][j] = x.x; S[m][j + 1] = x.y; S[m][j + 2] = x.z; S[m][j + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < KL; ++j) S[m][j] = 0.f;
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 64; ++j) S0[j] = S1[j] = 0.f;
     }
     const TI *src[5] = {(const TI *)p.r, (const TI *)p.w, (const TI *)p.k, (const TI *)p.a, (const TI *)p.b};
 
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(128) void fwd128_kernel(FwdArgs p) {
         }                                                                                   \
     } while (0)
     // element f of a staged row sits at 4 * slot(f / 4) + f % 4, where the
-    // 16-byte chunk c of key half c / 16 goes to slot 2 (c % 16) + c / 16
+    // 16-byte chunk c of key quarter c / 8 goes to slot 4 (c % 8) + c / 8
 #define F128_STORE(buf)                                                                     \
     do {                                                                                    \
         _Pragma("unroll") for (int q = 0; q < LOADS; ++q) {                                 \
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(128) void fwd128_kernel(FwdArgs p) {
             float *d_ = vec[buf][tt][row];                                                  \
             _Pragma("unroll") for (int e = 0; e < EPL; e += 4) {                            \
                 const int c4 = (ch * EPL + e) >> 2;                                         \
-                *(f32x4 *)(d_ + 4 * (2 * (c4 & 15) + (c4 >> 4))) =                          \
+                *(f32x4 *)(d_ + 4 * (4 * (c4 & 7) + (c4 >> 3))) =                           \
                     f32x4{x[e], x[e + 1], x[e + 2], x[e + 3]};                              \
             }                                                                               \
         }                                                                                   \
@@ -143,66 +144,71 @@ __global__ __launch_bounds__(128) void fwd128_kernel(FwdArgs p) {
             const int t = t0 + tt;
             const int64_t tok = u.start + t;
             if (p.ckpt && (t % kChunk) == 0) {
-                float *c = p.ckpt + ((u.ckpt + t / kChunk) * H + h) * (int64_t)(N * N) + (int64_t)i0 * N + kh * 64;
+                float *c = p.ckpt + ((u.ckpt + t / kChunk) * H + h) * (int64_t)(N * N) + (int64_t)rb * N + kq * KL;
 #pragma unroll
-                for (int j = 0; j < 64; j += 4) {
-                    *(f32x4 *)(c + j) = f32x4{S0[j], S0[j + 1], S0[j + 2], S0[j + 3]};
-                    *(f32x4 *)(c + 32 * N + j) = f32x4{S1[j], S1[j + 1], S1[j + 2], S1[j + 3]};
+                for (int m = 0; m < RPL; ++m)
+#pragma unroll
+                    for (int j = 0; j < KL; j += 4)
+                        *(f32x4 *)(c + 16 * m * N + j) = f32x4{S[m][j], S[m][j + 1], S[m][j + 2], S[m][j + 3]};
+            }
+            // the lane's key quarter: quad q of it at 16 q floats from here
+            const float *rr = vec[buf][tt][0] + 4 * kq, *wr = vec[buf][tt][1] + 4 * kq;
+            const float *kr = vec[buf][tt][2] + 4 * kq, *ar = vec[buf][tt][3] + 4 * kq;
+            const float *br = vec[buf][tt][4] + 4 * kq;
+            float vv[RPL], x[RPL];
+#pragma unroll
+            for (int m = 0; m < RPL; ++m) vv[m] = IO<TI>::ld((const TI *)p.v, tok * ts + h * N + rb + 16 * m);
+            float pa[RPL][2];
+#pragma unroll
+            for (int m = 0; m < RPL; ++m) pa[m][0] = pa[m][1] = 0.f;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const f32x4 a4 = *(const f32x4 *)(ar + 16 * q);
+                const int j = 4 * q;
+#pragma unroll
+                for (int m = 0; m < RPL; ++m) {
+                    pa[m][0] = fmaf(S[m][j], a4.x, pa[m][0]);
+                    pa[m][1] = fmaf(S[m][j + 1], a4.y, pa[m][1]);
+                    pa[m][0] = fmaf(S[m][j + 2], a4.z, pa[m][0]);
+                    pa[m][1] = fmaf(S[m][j + 3], a4.w, pa[m][1]);
                 }
             }
-            // the lane's key half: quad q of it at 8 q floats from here
-            const float *rr = vec[buf][tt][0] + 4 * kh, *wr = vec[buf][tt][1] + 4 * kh;
-            const float *kr = vec[buf][tt][2] + 4 * kh, *ar = vec[buf][tt][3] + 4 * kh;
-            const float *br = vec[buf][tt][4] + 4 * kh;
-            const float v0 = IO<TI>::ld((const TI *)p.v, tok * ts + h * N + i0);
-            const float v1 = IO<TI>::ld((const TI *)p.v, tok * ts + h * N + i1);
-            float p0[4] = {0.f, 0.f, 0.f, 0.f}, p1[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const f32x4 a4 = *(const f32x4 *)(ar + 8 * q);
-                const int j = 4 * q;
-                p0[0] = fmaf(S0[j], a4.x, p0[0]);
-                p0[1] = fmaf(S0[j + 1], a4.y, p0[1]);
-                p0[2] = fmaf(S0[j + 2], a4.z, p0[2]);
-                p0[3] = fmaf(S0[j + 3], a4.w, p0[3]);
-                p1[0] = fmaf(S1[j], a4.x, p1[0]);
-                p1[1] = fmaf(S1[j + 1], a4.y, p1[1]);
-                p1[2] = fmaf(S1[j + 2], a4.z, p1[2]);
-                p1[3] = fmaf(S1[j + 3], a4.w, p1[3]);
+            for (int m = 0; m < RPL; ++m) {
+                x[m] = pa[m][0] + pa[m][1];
+                x[m] += __shfl_xor(x[m], 16);
+                x[m] += __shfl_xor(x[m], 32);
             }
-            float x0 = (p0[0] + p0[1]) + (p0[2] + p0[3]);
-            float x1 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
-            x0 += __shfl_xor(x0, 32);
-            x1 += __shfl_xor(x1, 32);
-            float y0[4] = {0.f, 0.f, 0.f, 0.f}, y1[4] = {0.f, 0.f, 0.f, 0.f};
+            float py[RPL][2];
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const f32x4 w4 = *(const f32x4 *)(wr + 8 * q), b4 = *(const f32x4 *)(br + 8 * q);
-                const f32x4 k4 = *(const f32x4 *)(kr + 8 * q), r4 = *(const f32x4 *)(rr + 8 * q);
+            for (int m = 0; m < RPL; ++m) py[m][0] = py[m][1] = 0.f;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const f32x4 w4 = *(const f32x4 *)(wr + 16 * q), b4 = *(const f32x4 *)(br + 16 * q);
+                const f32x4 k4 = *(const f32x4 *)(kr + 16 * q), r4 = *(const f32x4 *)(rr + 16 * q);
                 const int j = 4 * q;
-                S0[j] = fmaf(S0[j], w4.x, fmaf(x0, b4.x, v0 * k4.x));
-                S0[j + 1] = fmaf(S0[j + 1], w4.y, fmaf(x0, b4.y, v0 * k4.y));
-                S0[j + 2] = fmaf(S0[j + 2], w4.z, fmaf(x0, b4.z, v0 * k4.z));
-                S0[j + 3] = fmaf(S0[j + 3], w4.w, fmaf(x0, b4.w, v0 * k4.w));
-                S1[j] = fmaf(S1[j], w4.x, fmaf(x1, b4.x, v1 * k4.x));
-                S1[j + 1] = fmaf(S1[j + 1], w4.y, fmaf(x1, b4.y, v1 * k4.y));
-                S1[j + 2] = fmaf(S1[j + 2], w4.z, fmaf(x1, b4.z, v1 * k4.z));
-                S1[j + 3] = fmaf(S1[j + 3], w4.w, fmaf(x1, b4.w, v1 * k4.w));
-                y0[0] = fmaf(S0[j], r4.x, y0[0]);
-                y0[1] = fmaf(S0[j + 1], r4.y, y0[1]);
-                y0[2] = fmaf(S0[j + 2], r4.z, y0[2]);
-                y0[3] = fmaf(S0[j + 3], r4.w, y0[3]);
-                y1[0] = fmaf(S1[j], r4.x, y1[0]);
-                y1[1] = fmaf(S1[j + 1], r4.y, y1[1]);
-                y1[2] = fmaf(S1[j + 2], r4.z, y1[2]);
-                y1[3] = fmaf(S1[j + 3], r4.w, y1[3]);
+#pragma unroll
+                for (int m = 0; m < RPL; ++m) {
+                    S[m][j] = fmaf(S[m][j], w4.x, fmaf(x[m], b4.x, vv[m] * k4.x));
+                    S[m][j + 1] = fmaf(S[m][j + 1], w4.y, fmaf(x[m], b4.y, vv[m] * k4.y));
+                    S[m][j + 2] = fmaf(S[m][j + 2], w4.z, fmaf(x[m], b4.z, vv[m] * k4.z));
+                    S[m][j + 3] = fmaf(S[m][j + 3], w4.w, fmaf(x[m], b4.w, vv[m] * k4.w));
+                    py[m][0] = fmaf(S[m][j], r4.x, py[m][0]);
+                    py[m][1] = fmaf(S[m][j + 1], r4.y, py[m][1]);
+                    py[m][0] = fmaf(S[m][j + 2], r4.z, py[m][0]);
+                    py[m][1] = fmaf(S[m][j + 3], r4.w, py[m][1]);
+                }
             }
-            float o0 = (y0[0] + y0[1]) + (y0[2] + y0[3]);
-            float o1 = (y1[0] + y1[1]) + (y1[2] + y1[3]);
-            o0 += __shfl_xor(o0, 32);
-            o1 += __shfl_xor(o1, 32);
-            // key half 0 writes row i0, key half 1 row i1: 64 consecutive outputs per wave
-            IO<TI>::st((TI *)p.y, tok * ts + h * N + (kh ? i1 : i0), kh ? o1 : o0);
+            float o[RPL];
+#pragma unroll
+            for (int m = 0; m < RPL; ++m) {
+                o[m] = py[m][0] + py[m][1];
+                o[m] += __shfl_xor(o[m], 16);
+                o[m] += __shfl_xor(o[m], 32);
+            }
+            // key quarter m writes row rb + 16 m: 64 consecutive outputs per wave
+            const float om = kq == 0 ? o[0] : kq == 1 ? o[1] : kq == 2 ? o[2] : o[3];
+            IO<TI>::st((TI *)p.y, tok * ts + h * N + rb + 16 * kq, om);
         }
         if (blk + 1 < nblk) F128_STORE(buf ^ 1);
         __syncthreads();
@@ -211,10 +217,10 @@ __global__ __launch_bounds__(128) void fwd128_kernel(FwdArgs p) {
 #undef F128_STORE
     if (p.s_out) {
 #pragma unroll
-        for (int j = 0; j < 64; j += 4) {
-            *(f32x4 *)(p.s_out + srow0 + j) = f32x4{S0[j], S0[j + 1], S0[j + 2], S0[j + 3]};
-            *(f32x4 *)(p.s_out + srow1 + j) = f32x4{S1[j], S1[j + 1], S1[j + 2], S1[j + 3]};
-        }
+        for (int m = 0; m < RPL; ++m)
+#pragma unroll
+            for (int j = 0; j < KL; j += 4)
+                *(f32x4 *)(p.s_out + srow + 16 * m * N + j) = f32x4{S[m][j], S[m][j + 1], S[m][j + 2], S[m][j + 3]};
     }
 }
 
