@@ -8,11 +8,13 @@
 //
 // Two kernels. A pre-pass writes q^ and k^ in fp32 to the workspace (one
 // wave per token row). The recurrence then runs token by token with one
-// workgroup of N lanes per (sequence, value head): lane i holds state row i
-// in N registers. The k^ and q^ rows of 16 tokens at a time are staged in
-// LDS (double-buffered; the next block's loads fly while this block runs)
-// and read by every lane as 16-byte broadcasts. Per token and lane: N
-// multiply-adds for <S_i, k^>, 2N for the update, N for <S_i, q^>.
+// workgroup of N lanes per (sequence, value head). In wave v, lane l holds
+// key half l / 32 of state rows 64 v + l % 32 and 64 v + l % 32 + 32, so every
+// k^ or q^ value it reads serves two rows; the halves add their partial dot
+// products with one lane exchange inside the wave. The k^ and q^ rows of 8
+// tokens at a time are staged in LDS (double-buffered; the next block's loads
+// fly while this block runs) and read as 16-byte broadcasts. Per token and
+// row: N multiply-adds for <S_i, k^>, 2N for the update, N for <S_i, q^>.
 // Value head h reads key head h / (H / Hk).
 #include "wkv7_kernels.h"
 
