@@ -71,7 +71,9 @@ extern "C" {
 #endif
 
 #define WKV7_ABI_VERSION 2
-#define WKV7_HEAD_SIZE 64
+#define WKV7_HEAD_SIZE 64        /* the head size every call takes */
+#define WKV7_HEAD_SIZE_WIDE 128  /* also taken by wkv7_forward, wkv7_decode_step
+                                    and the gated DeltaNet calls */
 #define WKV7_CHUNK 16
 
 typedef enum {
@@ -114,10 +116,11 @@ typedef struct {
  *   r, w, k, v, a, b : [B,T,H,N] inputs; w is the multiplicative decay.
  *   s0    : [S,H,N,N] fp32 initial states, or NULL for zeros.
  *   y     : [B,T,H,N] output (dtype); required.
- *   s_out : [S,H,N,N] fp32 final states, or NULL. May not alias s0.
+ *   s_out : [S,H,N,N] fp32 final states, or NULL.
  *   ckpt  : [slots,H,N,N] fp32 checkpoints for wkv7_backward, or NULL
  *           (inference forward). Dense mode needs B*ceil(T/16) slots.
- * All pointers 16-byte aligned.
+ * All pointers 16-byte aligned. No output (y, s_out, ckpt) may share a byte
+ * with an input or another output: WKV7_ERR_INVALID_ARGUMENT.
  */
 wkv7_status wkv7_forward(const wkv7_desc *d,
                          const void *r, const void *w, const void *k,
@@ -143,6 +146,8 @@ wkv7_status wkv7_forward(const wkv7_desc *d,
  *           head) and reads them back within the same call; calls that may run
  *           concurrently need separate workspaces. Too small or NULL when
  *           needed: WKV7_ERR_WORKSPACE_TOO_SMALL, before any HIP call.
+ * No output (dr..db, ds0, workspace) may share a byte with an input (r..b,
+ * ckpt, dy, ds_out) or another output: WKV7_ERR_INVALID_ARGUMENT.
  * The recurrence is recomputed from the 16-token checkpoints in fp32, not
  * reconstructed by dividing by the decay. Two kernels run back to back on
  * `stream`: a reverse sweep that carries only the state gradient, then the
@@ -167,6 +172,8 @@ wkv7_status wkv7_backward(const wkv7_desc *d,
  *   s_out : [B,H,N,N] fp32 state after the token; may equal s_in (in place),
  *           otherwise must not overlap it.
  *   y     : [B,H,N] output (dtype).
+ * Apart from s_out == s_in, no output (s_out, y) may share a byte with an
+ * input or the other output: WKV7_ERR_INVALID_ARGUMENT.
  */
 wkv7_status wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, int32_t decay,
                              const void *r, const void *w, const void *k,
@@ -192,7 +199,8 @@ wkv7_status wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, int
  *   out        : [B,H,N] output (dtype); required.
  *   y          : [B,H,N] the plain step's y (dtype), or NULL to skip it.
  * The state is updated exactly as by wkv7_decode_step. All pointers 16-byte
- * aligned.
+ * aligned. Apart from s_out == s_in, no output (s_out, out, y) may share a
+ * byte with an input (r..b, s_in, g, ln_w, ln_b, r_k) or another output.
  */
 wkv7_status wkv7_decode_step_fused(int32_t B, int32_t H, int32_t N, int32_t dtype, int32_t decay,
                                    const void *r, const void *w, const void *k, const void *v,
@@ -201,25 +209,28 @@ wkv7_status wkv7_decode_step_fused(int32_t B, int32_t H, int32_t N, int32_t dtyp
                                    const float *r_k, float eps, void *out, void *y, void *stream);
 
 /*
- * One token of a gated DeltaNet (GDN) layer, computed through the RWKV-7
- * remap of the rwkv-lab page (section "Highlight result -- GDN in RWKV-7"):
- * with q^ = q/||q|| and k^ = k/||k|| of the value head's key head,
- *     r = q^, w = exp(g) on every key, k_write = beta k^, a = -k^,
- *     b = k^ exp(g) beta,
- *     S' = S diag(w) + (S a) b^T + v k_write^T,   out = S' r / sqrt(N)
- * (the gated delta rule S' = exp(g) S (I - beta k^ k^T) + beta v k^T).
+ * One token of a gated DeltaNet (GDN) layer, computed as one WKV-7 step (the
+ * mapping of the rwkv-lab page, section "Highlight result -- GDN in
+ * RWKV-7"). The gated delta rule
+ *     S' = e^g S (I - beta k^ k^T) + beta v k^T,   out = S' q^ / sqrt(N)
+ * equals S diag(e^g) + (S (-k^)) (beta e^g k^)^T + v (beta k^)^T: a WKV-7
+ * step with decay e^g on every key, a = -k^, b = beta e^g k^ and write key
+ * beta k^, read out with r = q^. Here q^ and k^ are the value head's key-head
+ * q and k over max(||.||_2, 1e-12).
  *   N      : head size, 64 or 128 (GDN's matched geometry is 128; anything
  *            else: WKV7_ERR_UNSUPPORTED).
  *   H, Hk  : value heads and key heads, Hk divides H; value head h reads key
  *            head h / (H / Hk) (groups of consecutive value heads share one).
  *   q, k   : [B, Hk, N]; v, out : [B, H, N]; all of type dtype (fp32, bf16
- *            or fp16), 16-byte aligned. A q or k of length zero gives
- *            non-finite outputs, as the definition divides by the length.
+ *            or fp16), 16-byte aligned. A q or k of length zero
+ *            normalises to zero (the 1e-12 floor), so it stays finite: a
+ *            zero k leaves the state only decayed, a zero q gives out = 0.
  *   g, beta: fp32 [B, H], 4-byte aligned: the log-decay and the write
  *            strength of each (sequence, value head).
  *   s_in, s_out : fp32 [B, H, N, N] (row = value index), 16-byte aligned;
- *            s_out == s_in updates in place; a partial overlap, or out
- *            overlapping s_out, is WKV7_ERR_INVALID_ARGUMENT.
+ *            s_out == s_in updates in place. Any other overlap between an
+ *            output (s_out, out) and an input or the other output is
+ *            WKV7_ERR_INVALID_ARGUMENT.
  */
 wkv7_status wkv7_gdn_decode_step(int32_t B, int32_t H, int32_t Hk, int32_t N, int32_t dtype,
                                  const void *q, const void *k, const void *v, const float *g,
@@ -234,11 +245,11 @@ wkv7_status wkv7_gdn_decode_step(int32_t B, int32_t H, int32_t Hk, int32_t N, in
 wkv7_status wkv7_gdn_workspace_bytes(int32_t B, int32_t T, int32_t Hk, int32_t N, size_t *bytes);
 
 /*
- * A dense batch of gated DeltaNet tokens (B rows of T tokens) through the
- * same remap as wkv7_gdn_decode_step (rwkv-lab, "Highlight result -- GDN in
- * RWKV-7"), token by token from s0 (or zero):
+ * A dense batch of gated DeltaNet tokens (B rows of T tokens), each computed
+ * as the WKV-7 step of wkv7_gdn_decode_step (rwkv-lab, "Highlight result --
+ * GDN in RWKV-7"), token by token from s0 (or zero):
  *     S_t = exp(g_t) S_{t-1} (I - beta_t k^_t k^_t^T) + beta_t v_t k^_t^T,
- *     out_t = S_t q^_t / sqrt(N).
+ *     out_t = S_t q^_t / sqrt(N),   x^ = x / max(||x||_2, 1e-12).
  *   q, k   : [B, T, Hk, N]; v, out : [B, T, H, N]; type dtype, 16-byte aligned.
  *   g, beta: fp32 [B, T, H], 4-byte aligned.
  *   s0     : fp32 [B, H, N, N] or NULL (zero initial state).

@@ -3,7 +3,8 @@
     python -m linear_recurrent_lm_amd.build [--resource-usage]
 
 Every .hip file under csrc/ is compiled for gfx950 only and linked into
-linear_recurrent_lm_amd/libwkv7.so. Packed-FP32 instruction selection is
+linear_recurrent_lm_amd/libwkv7.so; the issue-pipe probe under csrc/probe/
+goes into its own libwkv7_probe.so. Packed-FP32 instruction selection is
 disabled for all device code (-target-feature -packed-fp32-ops).
 """
 from __future__ import annotations
@@ -18,6 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(os.path.dirname(HERE), "_build", "obj")
 LIB = os.path.join(HERE, "libwkv7.so")
+PROBE_SRC = os.path.join(CSRC, "probe", "pipe_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libwkv7_probe.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -62,5 +65,18 @@ def build(resource_usage: bool = False, jobs: int | None = None) -> str:
     return LIB
 
 
+def build_probe() -> str:
+    """The issue-pipe probe (csrc/probe/), a library of its own that only the
+    measurement script loads."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     print(build(resource_usage="--resource-usage" in sys.argv))
+    print(build_probe())

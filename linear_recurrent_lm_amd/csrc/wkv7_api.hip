@@ -29,6 +29,28 @@ bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
 
 size_t elem_size(int dtype) { return dtype == WKV7_F32 ? 4 : 2; }
 
+// A buffer as a byte range; a null pointer or zero size takes no part in the
+// overlap checks.
+struct Range {
+    const void *p;
+    size_t n;
+};
+
+// Does any output range overlap an input range or another output range?
+// Outputs are written while inputs are still read (and by other lanes of the
+// same kernels), so no output may share a byte with any other buffer.
+bool any_overlap(const Range *ins, int nin, const Range *outs, int nout) {
+    for (int o = 0; o < nout; ++o) {
+        if (!outs[o].p || !outs[o].n) continue;
+        for (int q = 0; q < nin; ++q)
+            if (ins[q].p && ins[q].n && ranges_overlap(ins[q].p, ins[q].n, outs[o].p, outs[o].n)) return true;
+        for (int o2 = o + 1; o2 < nout; ++o2)
+            if (outs[o2].p && outs[o2].n && ranges_overlap(outs[o].p, outs[o].n, outs[o2].p, outs[o2].n))
+                return true;
+    }
+    return false;
+}
+
 bool dtype_ok(int32_t dtype) { return dtype == WKV7_F32 || dtype == WKV7_BF16 || dtype == WKV7_F16; }
 
 // wide: the call also takes head size 128 (the forward does; the backward
@@ -51,6 +73,18 @@ wkv7_status check_desc(const wkv7_desc *d, bool wide = false) {
 }
 
 int64_t num_states(const wkv7_desc *d) { return d->num_seqs > 0 ? d->num_seqs : d->B; }
+
+// Bytes of one [B, T, H, N] token stream with elements of `dtype`.
+size_t stream_bytes(const wkv7_desc *d, int32_t dtype) {
+    return (size_t)d->B * d->T * d->H * d->N * elem_size(dtype);
+}
+
+// Bytes of the checkpoint buffer the descriptor implies.
+size_t ckpt_bytes(const wkv7_desc *d) {
+    const int64_t slots = d->num_seqs > 0 ? (d->ckpt_slots > 0 ? d->ckpt_slots : 0)
+                                          : (int64_t)d->B * ((d->T + kChunk - 1) / kChunk);
+    return (size_t)slots * d->H * d->N * d->N * sizeof(float);
+}
 
 wkv7_status check_streams(const void *const *ptrs, int n) {
     for (int q = 0; q < n; ++q)
@@ -213,10 +247,14 @@ wkv7_status wkv7_forward(const wkv7_desc *d, const void *r, const void *w, const
     const void *streams[7] = {r, w, k, v, a, b, y};
     if ((st = check_streams(streams, 7)) != WKV7_OK) return st;
     if ((s0 && !aligned16(s0)) || (s_out && !aligned16(s_out))) return WKV7_ERR_INVALID_ARGUMENT;
-    const size_t state_bytes = (size_t)num_states(d) * d->H * d->N * d->N * sizeof(float);
-    if (s0 && s_out && ranges_overlap(s0, state_bytes, s_out, state_bytes))
-        return WKV7_ERR_INVALID_ARGUMENT;
     if ((st = check_ckpt(d, ckpt)) != WKV7_OK) return st;
+    {
+        const size_t state_bytes = (size_t)num_states(d) * d->H * d->N * d->N * sizeof(float);
+        const size_t sb = stream_bytes(d, d->dtype);
+        const Range ins[7] = {{r, sb}, {w, sb}, {k, sb}, {v, sb}, {a, sb}, {b, sb}, {s0, state_bytes}};
+        const Range outs[3] = {{y, sb}, {s_out, state_bytes}, {ckpt, ckpt_bytes(d)}};
+        if (any_overlap(ins, 7, outs, 3)) return WKV7_ERR_INVALID_ARGUMENT;
+    }
     if ((st = check_device()) != WKV7_OK) return st;
 
     hipStream_t hs = (hipStream_t)stream;
@@ -256,6 +294,16 @@ wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, cons
     if ((st = wkv7_workspace_bytes(d, &need)) != WKV7_OK) return st;
     if (workspace_bytes < need || (need > 0 && !workspace)) return WKV7_ERR_WORKSPACE_TOO_SMALL;
     if (workspace && !aligned16(workspace)) return WKV7_ERR_INVALID_ARGUMENT;
+    {
+        const size_t state_bytes = (size_t)num_states(d) * d->H * d->N * d->N * sizeof(float);
+        const size_t sb = stream_bytes(d, d->dtype);
+        const size_t gb = stream_bytes(d, d->grad_f32 ? WKV7_F32 : d->dtype);
+        const Range ins[9] = {{r, sb}, {w, sb}, {k, sb}, {v, sb}, {a, sb}, {b, sb},
+                              {ckpt, ckpt_bytes(d)}, {dy, sb}, {ds_out, state_bytes}};
+        const Range outs[8] = {{dr, gb}, {dw, gb}, {dk, gb}, {dv, gb}, {da, gb}, {db, gb},
+                               {ds0, state_bytes}, {workspace, need}};
+        if (any_overlap(ins, 9, outs, 8)) return WKV7_ERR_INVALID_ARGUMENT;
+    }
     if ((st = check_device()) != WKV7_OK) return st;
 
     hipStream_t hs = (hipStream_t)stream;
@@ -306,6 +354,16 @@ static wkv7_status decode_impl(int32_t B, int32_t H, int32_t N, int32_t dtype, i
     const size_t state_bytes = (size_t)B * H * N * N * sizeof(float);
     if (s_in != s_out && ranges_overlap(s_in, state_bytes, s_out, state_bytes))
         return WKV7_ERR_INVALID_ARGUMENT;
+    {
+        // in place (s_out == s_in) the state is an output only
+        const size_t tb = (size_t)B * H * N * elem_size(dtype), pb = (size_t)H * N * sizeof(float);
+        const Range ins[11] = {{r, tb}, {w, tb}, {k, tb}, {v, tb}, {a, tb}, {b, tb},
+                               {s_in == s_out ? nullptr : s_in, state_bytes},
+                               {fused ? g : nullptr, tb}, {fused ? ln_w : nullptr, pb},
+                               {fused ? ln_b : nullptr, pb}, {fused ? r_k : nullptr, pb}};
+        const Range outs[3] = {{s_out, state_bytes}, {y, tb}, {fused ? out : nullptr, tb}};
+        if (any_overlap(ins, 11, outs, 3)) return WKV7_ERR_INVALID_ARGUMENT;
+    }
     if ((st = check_device()) != WKV7_OK) return st;
     wkv7::DecArgs args{};
     args.B = B; args.H = H; args.dtype = dtype;
@@ -356,8 +414,14 @@ wkv7_status wkv7_gdn_decode_step(int32_t B, int32_t H, int32_t Hk, int32_t N, in
     const size_t state_bytes = (size_t)B * H * N * N * sizeof(float);
     if (s_in != s_out && ranges_overlap(s_in, state_bytes, s_out, state_bytes))
         return WKV7_ERR_INVALID_ARGUMENT;
-    if (ranges_overlap(out, (size_t)B * H * N * elem_size(dtype), s_out, state_bytes))
-        return WKV7_ERR_INVALID_ARGUMENT;
+    {
+        const size_t es = elem_size(dtype);
+        const size_t qb = (size_t)B * Hk * N * es, vb = (size_t)B * H * N * es, sc = (size_t)B * H * 4;
+        const Range ins[6] = {{q, qb}, {k, qb}, {v, vb}, {g, sc}, {beta, sc},
+                              {s_in == s_out ? nullptr : s_in, state_bytes}};
+        const Range outs[2] = {{s_out, state_bytes}, {out, vb}};
+        if (any_overlap(ins, 6, outs, 2)) return WKV7_ERR_INVALID_ARGUMENT;
+    }
     if ((st = check_device()) != WKV7_OK) return st;
     wkv7::GdnArgs a{};
     a.B = B; a.H = H; a.Hk = Hk; a.N = N; a.dtype = dtype;

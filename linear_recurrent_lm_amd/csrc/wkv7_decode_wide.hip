@@ -12,13 +12,14 @@
 // rwkv-lab conversion target uses) reads r, w, k, v, a, b as given:
 //     S' = S diag(w) + (S a) b^T + v k^T,   y = S' r.
 //
-// The gated DeltaNet (GDN) step is the WKV-7 step the rwkv-lab page
-// ("Highlight result -- GDN in RWKV-7") maps it to. With q^ = q/||q|| and
-// k^ = k/||k||:
-//     r = q^,  w = exp(g) on every key,  k_write = beta k^,  a = -k^,
-//     b = k^ exp(g) beta,
-//     S' = S diag(w) + (S a) b^T + v k_write^T,   out = S' r / sqrt(N),
-// which is the gated delta rule S' = exp(g) S (I - beta k^ k^T) + beta v k^T.
+// The gated DeltaNet (GDN) step runs as one WKV-7 step, the mapping of the
+// rwkv-lab page ("Highlight result -- GDN in RWKV-7"). The gated delta rule
+//     S' = e^g S (I - beta k^ k^T) + beta v k^T
+// expands to S diag(e^g) + (S (-k^)) (beta e^g k^)^T + v (beta k^)^T: a WKV-7
+// step whose decay is e^g on every key, whose a and b are -k^ and beta e^g k^,
+// and whose write key is beta k^. Reading it out with r = q^ and scaling by
+// 1/sqrt(N) gives GDN's output. Here q^ and k^ are q and k over
+// max(||.||_2, 1e-12).
 // Value head h reads key head h / (H / Hk): groups of consecutive value heads
 // share a key head (GDN's geometry is 32 value heads over 16 key heads).
 #include "wkv7_kernels.h"
@@ -62,8 +63,11 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(GdnArgs p) {
     }
 #pragma unroll
     for (int m = 0; m < IT; ++m) vv[m] = IO<TI>::ld((const TI *)p.v, vb + m * RPI + rl);
-    const float qs = 1.f / sqrtf(sum_lanes<LPR>(q[0] * q[0] + q[1] * q[1] + q[2] * q[2] + q[3] * q[3]));
-    const float ks = 1.f / sqrtf(sum_lanes<LPR>(k[0] * k[0] + k[1] * k[1] + k[2] * k[2] + k[3] * k[3]));
+    // x / max(||x||, 1e-12): a zero q or k normalises to zero, not NaN
+    const float qs = 1.f / fmaxf(sqrtf(sum_lanes<LPR>(q[0] * q[0] + q[1] * q[1] + q[2] * q[2] + q[3] * q[3])),
+                                 kGdnNormEps);
+    const float ks = 1.f / fmaxf(sqrtf(sum_lanes<LPR>(k[0] * k[0] + k[1] * k[1] + k[2] * k[2] + k[3] * k[3])),
+                                 kGdnNormEps);
     const float decay = expf(p.g[unit]);
     const float beta = p.beta[unit];
     float r[4], a[4], b[4], kw[4];

@@ -10,6 +10,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kN = 64;       // head size
 constexpr int kChunk = 16;   // checkpoint interval in tokens
+// Gated DeltaNet q and k are normalised as x / max(||x||_2, kGdnNormEps).
+constexpr float kGdnNormEps = 1e-12f;
 
 // Unit resolution: one (sequence, head) pair. Dense mode: sequence = row.
 struct SegParams {

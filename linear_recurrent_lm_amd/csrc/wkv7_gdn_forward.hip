@@ -4,6 +4,7 @@
 // k_write = beta k^, a = -k^, b = k^ exp(g) beta, the WKV-7 row update of
 // value row i is
 //     S_i <- exp(g) S_i + beta (v_i - exp(g) <S_i, k^>) k^,   out_i = <S_i, q^> / sqrt(N)
+// (q^, k^: q and k over max(||.||_2, 1e-12), so a zero row gives a zero vector)
 // (the gated delta rule, since the decay is one scalar per token and head).
 //
 // Two kernels. A pre-pass writes q^ and k^ in fp32 to the workspace (one
@@ -43,7 +44,8 @@ __global__ __launch_bounds__(256) void gdn_norm_kernel(const TI *__restrict__ q,
         sa += __shfl_xor(sa, m);
         sb += __shfl_xor(sb, m);
     }
-    const float ia = 1.f / sqrtf(sa), ib = 1.f / sqrtf(sb);
+    // x / max(||x||, 1e-12): a zero row normalises to zero, not NaN
+    const float ia = 1.f / fmaxf(sqrtf(sa), kGdnNormEps), ib = 1.f / fmaxf(sqrtf(sb), kGdnNormEps);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         qn[o + e] = a[e] * ia;

@@ -40,6 +40,7 @@ def vce_backward_workspace_bytes(M: int, D: int, V: int, vocab_chunk: int) -> in
 def _inputs(h, w, targets):
     torch = _W._torch()
     dev = h.device
+    _W._cuda(h, "h")
     M, D = h.shape
     V = w.shape[0]
     _W._req(h, "h", dev, torch.bfloat16, (M, D))
@@ -65,7 +66,7 @@ def vce_forward(h, w, targets, *, loss=None, lse=None, workspace=None):
     ws = _workspace(torch, dev, vce_forward_workspace_bytes(M, D, V), workspace)
     _check("vce_forward", _W.lib().vce_forward(
         M, D, V, _W._ptr(h), _W._ptr(w), _W._ptr(targets), _W._ptr(loss), _W._ptr(lse),
-        _W._ptr(ws), ws.numel(), _W._stream()))
+        _W._ptr(ws), _W._nbytes(ws), _W._stream()))
     return loss, lse
 
 
@@ -82,5 +83,5 @@ def vce_backward(h, w, targets, lse, dloss, *, vocab_chunk: int = 16384, dh=None
     ws = _workspace(torch, dev, vce_backward_workspace_bytes(M, D, V, vocab_chunk), workspace)
     _check("vce_backward", _W.lib().vce_backward(
         M, D, V, vocab_chunk, _W._ptr(h), _W._ptr(w), _W._ptr(targets), _W._ptr(lse),
-        _W._ptr(dloss), _W._ptr(dh), _W._ptr(dw), _W._ptr(ws), ws.numel(), _W._stream()))
+        _W._ptr(dloss), _W._ptr(dh), _W._ptr(dw), _W._ptr(ws), _W._nbytes(ws), _W._stream()))
     return dh, dw

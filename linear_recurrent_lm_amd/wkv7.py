@@ -123,8 +123,21 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _cuda(t, name):
+    """The first tensor of a call fixes its device, which must be a GPU."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) device tensor")
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def _req(t, name, dev, dtype=None, shape=None):
-    if not t.is_cuda or t.device != dev:
+    """Every tensor a call passes to the library, the caller's own output and
+    workspace buffers included: same device, contiguous, and (when given) the
+    dtype and shape the C ABI assumes, since it cannot see buffer sizes."""
+    if t.device != dev:
         raise ValueError(f"{name} must be on {dev}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -196,6 +209,7 @@ def wkv7_forward(r, w, k, v, a, b, s0=None, *, segments: Segments | None = None,
     torch = _torch()
     B, T, H, n = r.shape
     dev = r.device
+    _cuda(r, "r")
     for name, t in zip("rwkvab", (r, w, k, v, a, b)):
         _req(t, name, dev, r.dtype, r.shape)
     S = segments.num_seqs if segments is not None else B
@@ -207,11 +221,15 @@ def wkv7_forward(r, w, k, v, a, b, s0=None, *, segments: Segments | None = None,
         s_out = torch.empty((S, H, n, n), device=dev, dtype=torch.float32)
     if not state_out:
         s_out = None
+    if s_out is not None:
+        _req(s_out, "s_out", dev, torch.float32, (S, H, n, n))
+    slots = checkpoint_slots(B, T, segments)
     if checkpoints and ckpt is None:
-        ckpt = torch.empty((checkpoint_slots(B, T, segments), H, n, n), device=dev,
-                           dtype=torch.float32)
+        ckpt = torch.empty((slots, H, n, n), device=dev, dtype=torch.float32)
     if not checkpoints:
         ckpt = None
+    if ckpt is not None:
+        _req(ckpt, "ckpt", dev, torch.float32, (slots, H, n, n))
     d = _desc(B, T, H, _dtype_code(r), segments, decay, n=n)
     _check("wkv7_forward", lib().wkv7_forward(
         ctypes.byref(d), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(s0), _ptr(y),
@@ -234,6 +252,7 @@ def wkv7_backward(r, w, k, v, a, b, ckpt, dy=None, ds_out=None, *,
     torch = _torch()
     B, T, H, n = r.shape
     dev = r.device
+    _cuda(r, "r")
     for name, t in zip("rwkvab", (r, w, k, v, a, b)):
         _req(t, name, dev, r.dtype, r.shape)
     S = segments.num_seqs if segments is not None else B
@@ -252,7 +271,9 @@ def wkv7_backward(r, w, k, v, a, b, ckpt, dy=None, ds_out=None, *,
     need = wkv7_workspace_bytes(B, T, H, _dtype_code(r), segments)
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None:
+        _req(workspace, "workspace", dev)
+    ws_bytes = 0 if workspace is None else _nbytes(workspace)
     d = _desc(B, T, H, _dtype_code(r), segments, decay, grad_f32)
     _check("wkv7_backward", lib().wkv7_backward(
         ctypes.byref(d), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(ckpt), _ptr(dy),
@@ -270,6 +291,7 @@ def wkv7_decode_step(r, w, k, v, a, b, s_in, s_out=None, y=None, *, decay: str =
     torch = _torch()
     B, H, n = r.shape
     dev = r.device
+    _cuda(r, "r")
     for name, t in zip("rwkvab", (r, w, k, v, a, b)):
         _req(t, name, dev, r.dtype, r.shape)
     _req(s_in, "s_in", dev, torch.float32, (B, H, n, n))
@@ -277,6 +299,7 @@ def wkv7_decode_step(r, w, k, v, a, b, s_in, s_out=None, y=None, *, decay: str =
         s_out = torch.empty_like(s_in)
     _req(s_out, "s_out", dev, torch.float32, (B, H, n, n))
     y = torch.empty_like(r) if y is None else y
+    _req(y, "y", dev, r.dtype, r.shape)
     _check("wkv7_decode_step", lib().wkv7_decode_step(
         B, H, n, _dtype_code(r), _decay(decay), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(s_in),
         _ptr(s_out), _ptr(y), _stream()))
@@ -293,6 +316,7 @@ def wkv7_decode_step_fused(r, w, k, v, a, b, s_in, g, ln_w, ln_b, r_k, eps, s_ou
     torch = _torch()
     B, H, n = r.shape
     dev = r.device
+    _cuda(r, "r")
     for name, t in zip("rwkvab", (r, w, k, v, a, b)):
         _req(t, name, dev, r.dtype, r.shape)
     _req(g, "g", dev, r.dtype, r.shape)
@@ -322,6 +346,7 @@ def wkv7_gdn_decode_step(q, k, v, g, beta, s_in, s_out=None, out=None):
     (out [B, H, N], s_out)."""
     torch = _torch()
     dev = v.device
+    _cuda(v, "v")
     B, H, N = v.shape
     Hk = q.shape[1]
     dt = v.dtype
@@ -353,6 +378,7 @@ def wkv7_gdn_forward(q, k, v, g, beta, s0=None, *, out=None, want_state=True, wo
     fp32 [B, H, N, N] or None. Returns (out [B, T, H, N], s_out or None)."""
     torch = _torch()
     dev = v.device
+    _cuda(v, "v")
     B, T, H, N = v.shape
     Hk = q.shape[2]
     dt = v.dtype
@@ -368,9 +394,10 @@ def wkv7_gdn_forward(q, k, v, g, beta, s0=None, *, out=None, want_state=True, wo
     s_out = torch.empty((B, H, N, N), device=dev, dtype=torch.float32) if want_state else None
     need = wkv7_gdn_workspace_bytes(B, T, Hk, N)
     ws = torch.empty(need, device=dev, dtype=torch.uint8) if workspace is None else workspace
+    _req(ws, "workspace", dev)
     _check("wkv7_gdn_forward", lib().wkv7_gdn_forward(
         B, T, H, Hk, N, _dtype_code(v), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
-        _ptr(out), _ptr(s_out), _ptr(ws), ws.numel(), _stream()))
+        _ptr(out), _ptr(s_out), _ptr(ws), _nbytes(ws), _stream()))
     return out, s_out
 
 

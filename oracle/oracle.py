@@ -204,13 +204,24 @@ def decode_step_fused(r, w, k, v, a, b, s_in, g, ln_w, ln_b, r_k, eps):
     return out, y, s_out
 
 
-def gdn_decode_step(q, k, v, g, beta, s_in):
-    """One token of a gated DeltaNet layer through the remap the rwkv-lab page
-    ("Highlight result -- GDN in RWKV-7") states, at matched head size N:
-    with q^ = q / ||q||, k^ = k / ||k||,
+GDN_NORM_EPS = 1e-12
 
-        r = q^,  w = exp(g) on every key,  k_write = beta k^,  a = -k^,
-        b = k^ exp(g) beta,  out = wkv7(r, w, k_write, v, a, b) / sqrt(N).
+
+def gdn_normalize(x):
+    """x / max(||x||_2, 1e-12) over the last axis: the plain L2 normalisation,
+    guarded so that a zero row (padding, a masked token) gives zeros."""
+    x = _d(x)
+    return x / np.maximum(np.linalg.norm(x, axis=-1, keepdims=True), GDN_NORM_EPS)
+
+
+def gdn_decode_step(q, k, v, g, beta, s_in):
+    """One token of a gated DeltaNet layer at matched head size N, computed as
+    one WKV-7 step (the mapping of the rwkv-lab page, "Highlight result -- GDN
+    in RWKV-7"). The gated delta rule S' = e^g S (I - beta k^ k^T) + beta v k^T
+    expands to S diag(e^g) + (S (-k^)) (beta e^g k^)^T + v (beta k^)^T, i.e. a
+    WKV-7 step with decay e^g on every key, a = -k^, b = beta e^g k^ and write
+    key beta k^; its readout with r = q^, over sqrt(N), is GDN's output. q^ and
+    k^ come from gdn_normalize.
 
     q, k [B, Hk, N] (key heads); v [B, H, N]; g, beta [B, H] (per value head);
     state [B, H, N, N]. Value head h reads key head h // (H / Hk): groups of
@@ -220,8 +231,8 @@ def gdn_decode_step(q, k, v, g, beta, s_in):
     B, Hk, N = q.shape
     H = v.shape[1]
     kh = np.arange(H) // (H // Hk)
-    qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
-    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    qn = gdn_normalize(q)
+    kn = gdn_normalize(k)
     r, kk = qn[:, kh], kn[:, kh]
     w = np.broadcast_to(np.exp(g)[..., None], (B, H, N))
     bt = beta[..., None]
@@ -230,8 +241,8 @@ def gdn_decode_step(q, k, v, g, beta, s_in):
 
 
 def gdn_forward(q, k, v, g, beta, s0=None):
-    """A sequence of gated DeltaNet tokens through the same remap as
-    gdn_decode_step, token by token (rwkv-lab, "Highlight result -- GDN in
+    """A sequence of gated DeltaNet tokens, each computed as the WKV-7 step
+    of gdn_decode_step, token by token (rwkv-lab, "Highlight result -- GDN in
     RWKV-7"). q, k [B, T, Hk, N]; v [B, T, H, N]; g, beta [B, T, H]; s0
     [B, H, N, N] or None (zero). Returns (out [B, T, H, N], s_out) in fp64."""
     q, k, v = _d(q), _d(k), _d(v)
@@ -239,8 +250,8 @@ def gdn_forward(q, k, v, g, beta, s0=None):
     B, T, Hk, N = q.shape
     H = v.shape[2]
     kh = np.arange(H) // (H // Hk)
-    qn = (q / np.linalg.norm(q, axis=-1, keepdims=True))[:, :, kh]
-    kn = (k / np.linalg.norm(k, axis=-1, keepdims=True))[:, :, kh]
+    qn = gdn_normalize(q)[:, :, kh]
+    kn = gdn_normalize(k)[:, :, kh]
     dec = np.exp(g)[..., None]
     bt = beta[..., None]
     w = np.broadcast_to(dec, (B, T, H, N))

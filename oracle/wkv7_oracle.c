@@ -15,10 +15,11 @@
  *     S[i,j]  = S[i,j]*w_t[j] + sa[i]*b_t[j] + v_t[i]*k_t[j]
  *     y_t[i]  = sum_j S[i,j] * r_t[j]                  (reads the updated S_t)
  *
- * The a-term reads the undecayed S_{t-1}; this is the reading under which the
- * gated-delta-rule remap printed on the rwkv-lab page (section "Highlight
- * result - GDN in RWKV-7", b = normalize(k)*exp(g)*beta) reproduces the gated
- * delta rule. Training forwards also store the state entering every 16th token
+ * The a-term reads the undecayed S_{t-1}. This is the reading under which the
+ * rwkv-lab page's mapping of a gated DeltaNet step onto this kernel (section
+ * "Highlight result - GDN in RWKV-7") reproduces the gated delta rule: there
+ * the b vector carries the step's decay factor itself, which is right only if
+ * the (S a) b^T term starts from the undecayed state. Training forwards also store the state entering every 16th token
  * of the unit (rwkv-metal page, section "The Metal WKV-7 kernel": a state
  * checkpoint every 16 tokens), chunk c holding the state entering token 16c,
  * so chunk 0 holds the initial state.

@@ -233,3 +233,86 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(W, "LIB_PATH", "/nonexistent/libwkv7.so")
     with pytest.raises(RuntimeError, match="missing"):
         W.lib()
+
+
+# Fake device addresses 2^40 bytes apart: no two buffers of the small shapes
+# below overlap unless a test places one inside another on purpose. Every call
+# here is expected to fail validation (with no GPU, a call that passed it would
+# return the HIP error instead, failing the test).
+FAR = [ctypes.c_void_p((q + 1) << 40) for q in range(24)]
+
+
+def inside(p, off=64):
+    return ctypes.c_void_p(p.value + off)
+
+
+def test_forward_rejects_overlapping_outputs():
+    d = desc()                          # B=2, T=32, H=4, bf16: 32 KiB streams
+    L = W.lib()
+    base = dict(ptrs=FAR[:6], s0=FAR[6], y=FAR[7], s_out=FAR[8], ckpt=FAR[9])
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.wkv7_forward(ctypes.byref(d), *a["ptrs"], a["s0"], a["y"], a["s_out"], a["ckpt"], None)
+    for q in range(6):                                  # y over each input stream
+        assert call(y=inside(FAR[q])) == INVALID, q
+    assert call(y=inside(FAR[6])) == INVALID            # y over s0
+    assert call(s_out=inside(FAR[3])) == INVALID        # s_out over v
+    assert call(s_out=inside(FAR[6])) == INVALID        # s_out over s0
+    assert call(ckpt=inside(FAR[0])) == INVALID         # checkpoints over r
+    assert call(ckpt=inside(FAR[7])) == INVALID         # checkpoints over y
+    assert call(y=inside(FAR[8])) == INVALID            # y over s_out
+
+
+def test_backward_rejects_overlapping_outputs():
+    d = desc()
+    L = W.lib()
+    need = W.wkv7_workspace_bytes(2, 32, 4, 1)
+    base = dict(ins=FAR[:6], ckpt=FAR[6], dy=FAR[7], ds_out=FAR[8], grads=FAR[9:15], ds0=FAR[15],
+                ws=FAR[16])
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.wkv7_backward(ctypes.byref(d), *a["ins"], a["ckpt"], a["dy"], a["ds_out"], *a["grads"],
+                               a["ds0"], a["ws"], need, None)
+    for q in range(6):
+        g = list(FAR[9:15]); g[q] = inside(FAR[q])      # gradient over its own input
+        assert call(grads=g) == INVALID, q
+    g = list(FAR[9:15]); g[2] = inside(FAR[9])          # two gradients sharing bytes
+    assert call(grads=g) == INVALID
+    assert call(ds0=inside(FAR[6])) == INVALID          # ds0 over the checkpoints
+    assert call(ws=inside(FAR[7])) == INVALID           # workspace over dy
+    assert call(ws=inside(FAR[9])) == INVALID           # workspace over dr
+    assert call(ds0=inside(FAR[8])) == INVALID          # ds0 over ds_out
+
+
+def test_decode_rejects_overlapping_outputs():
+    L = W.lib()
+
+    def call(y=FAR[6], s_in=FAR[7], s_out=FAR[8], ins=None):
+        return L.wkv7_decode_step(4, 2, 64, 1, 0, *(ins or FAR[:6]), s_in, s_out, y, None)
+    for q in range(6):                 # y over r..b (the kernel reads r while writing y)
+        assert call(y=inside(FAR[q], 16)) == INVALID, q
+    assert call(y=inside(FAR[7])) == INVALID            # y over s_in
+    assert call(y=inside(FAR[7]), s_out=FAR[7]) == INVALID   # y over the in-place state
+    ins = list(FAR[:6]); ins[4] = inside(FAR[8])        # s_out over an input
+    assert call(ins=ins) == INVALID
+
+    def fused(out=FAR[13], y=None, g=FAR[9], ln_w=FAR[10]):
+        return L.wkv7_decode_step_fused(4, 2, 64, 1, 0, *FAR[:6], FAR[7], FAR[8], g, ln_w, FAR[11],
+                                        FAR[12], 1e-5, out, y, None)
+    assert fused(out=inside(FAR[0], 16)) == INVALID     # out over r
+    assert fused(out=inside(FAR[9])) == INVALID         # out over the gate
+    assert fused(y=inside(FAR[13])) == INVALID          # y over out
+    assert fused(ln_w=inside(FAR[8])) == INVALID        # a parameter inside s_out
+
+
+def test_gdn_decode_rejects_overlapping_outputs():
+    L = W.lib()
+
+    def call(out=FAR[7], s_in=FAR[5], s_out=FAR[6], q=FAR[0], v=FAR[2]):
+        return L.wkv7_gdn_decode_step(4, 4, 2, 128, 1, q, FAR[1], v, FAR[3], FAR[4], s_in, s_out, out, None)
+    assert call(out=inside(FAR[2])) == INVALID          # out over v
+    assert call(out=inside(FAR[5])) == INVALID          # out over s_in (out of place)
+    assert call(out=inside(FAR[5]), s_out=FAR[5]) == INVALID  # out over the in-place state
+    assert call(q=inside(FAR[6])) == INVALID            # s_out over q

@@ -489,6 +489,41 @@ def pin_p16_gdn_forward_zero_state(seed=42):
     want = beta[0, 0, :, None] * np.dot(kn, qn) * v[0, 0] / np.sqrt(N)
     return rel(out[0, 0], want)
 
+def pin_p16_gdn_zero_rows(seed=43):
+    """A token whose k is all zero only decays the state (S_t = e^g S_{t-1}),
+    and a token whose q is all zero outputs exactly zero: the normalisation
+    x / max(||x||, 1e-12) sends a zero row to zero instead of 0/0. Both are
+    checked in the middle of a sequence, with every later token against the
+    textbook rule from the decayed state."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, T, Hk, H, N = 2, 7, 2, 4, 128
+    q = rng.standard_normal((B, T, Hk, N))
+    k = rng.standard_normal((B, T, Hk, N))
+    v = rng.standard_normal((B, T, H, N))
+    g = -rng.uniform(0.01, 1.0, (B, T, H))
+    beta = rng.uniform(0.05, 1.0, (B, T, H))
+    s = 0.1 * rng.standard_normal((B, H, N, N))
+    k[:, 3] = 0.0
+    q[:, 5] = 0.0
+    out, s_out = O.gdn_forward(q, k, v, g, beta, s)
+    if not (np.all(np.isfinite(out)) and np.all(np.isfinite(s_out))):
+        return np.inf
+    err = float(np.max(np.abs(out[:, 5])))                 # zero q: zero output
+    st = s
+    for t in range(T):
+        if t == 3:                                        # zero k: decay only
+            st = np.exp(g[:, t])[..., None, None] * st
+            qn = q[:, t] / np.linalg.norm(q[:, t], axis=-1, keepdims=True)
+            o_t = np.einsum("bhij,bhj->bhi", st, qn[:, [0, 0, 1, 1]]) / np.sqrt(N)
+        elif t == 5:
+            _, st = _gdn_textbook(np.ones_like(q[:, t]), k[:, t], v[:, t], g[:, t], beta[:, t], st)
+            o_t = np.zeros_like(out[:, t])
+        else:
+            o_t, st = _gdn_textbook(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], st)
+        err = max(err, rel(out[:, t], o_t))
+    return max(err, rel(s_out, st))
+
+
 PINS = {
     "p1_cumulative": (pin_p1, 1e-12),
     "p2_w0_last_outer": (pin_p2, 1e-12),
@@ -516,6 +551,7 @@ PINS = {
     "p15_gdn_norm_invariance": (pin_p15_norm_invariance, 1e-12),
     "p16_gdn_forward_textbook": (pin_p16_gdn_forward_textbook, 1e-12),
     "p16_gdn_forward_zero_state": (pin_p16_gdn_forward_zero_state, 1e-12),
+    "p16_gdn_zero_rows": (pin_p16_gdn_zero_rows, 1e-12),
 }
 
 
