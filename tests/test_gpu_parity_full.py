@@ -1,0 +1,196 @@
+"""GPU parity at the full workload sizes: more units of the training
+workload's gradients, every sequence of the ragged workload in both of its
+layouts, the ragged backward, and the leak bound of the decay clamp. The
+oracle computes each checked (sequence, head) unit on its own."""
+import numpy as np
+import pytest
+
+from linear_recurrent_lm_amd import synth
+from oracle import oracle as O
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dr", "dw", "dk", "dv", "da", "db")
+
+
+@pytest.fixture(scope="module")
+def W():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_recurrent_lm_amd import wkv7
+    wkv7.lib()
+    return wkv7
+
+
+def _dev(inp, names=("r", "w", "k", "v", "a", "b")):
+    return [U.dev_stream(getattr(inp, n), inp.dtype) for n in names]
+
+
+def _host32(t):
+    """Device tensor -> fp32 numpy (the full ragged outputs are large; fp32
+    holds every bf16 value exactly)."""
+    return t.float().cpu().numpy()
+
+
+def test_training_gradients_16_units(W):
+    """bf16 B=4 T=4096 H=32, zero state, dy ~ N(0, 1), in the bench's launch
+    configuration (the forward in 32-row workgroups, two per unit; the
+    backward's sweep likewise): gradients, ds0 and checkpoints of 16 units,
+    four heads of every row b, each unit covering both 32-row halves."""
+    import torch
+    B, T, H = 4, 4096, 32
+    inp = synth.make_inputs(B, T, H, 64, seed=3, dtype="bf16", with_dy=True)
+    ts = _dev(inp)
+    y, s_out, ckpt = W.wkv7_forward(*ts, None, checkpoints=True)
+    g = W.wkv7_backward(*ts, ckpt, U.dev_stream(inp.dy, "bf16"), None)
+    torch.cuda.synchronize()
+    ch = U.host(ckpt)
+    nc = T // 16
+    rng = np.random.default_rng(33)
+    worst = {}
+    for b in range(B):
+        heads = sorted(rng.choice(H, 4, replace=False).tolist())
+        sl = [np.ascontiguousarray(x[b:b + 1]) for x in inp.streams()]
+        dy = np.ascontiguousarray(inp.dy[b:b + 1])
+        units = [(0, h) for h in heads]
+        ref = O.backward(*sl, dy=dy, units=units)
+        fr = O.forward(*sl, checkpoints=True, units=units)
+        for h in heads:
+            for n in GRADS:
+                gh = U.host(g[n][b:b + 1, :, h:h + 1])
+                worst[n] = max(worst.get(n, 0.0), U.unit_err_dense(gh, ref[n][:, :, h:h + 1]))
+            worst["ds0"] = max(worst.get("ds0", 0.0),
+                               U.unit_err_state(U.host(g["ds0"][b:b + 1, h:h + 1]), ref["ds0"][:, h:h + 1]))
+            worst["ckpt"] = max(worst.get("ckpt", 0.0), U.unit_err_ckpt(
+                ch[b * nc:(b + 1) * nc, h:h + 1], fr["ckpt"][:, h:h + 1], [0], [nc]))
+    assert worst["ckpt"] <= U.TOL_F32, worst
+    assert all(v <= U.TOL_GRAD for k, v in worst.items() if k != "ckpt"), worst
+
+
+@pytest.fixture(scope="module")
+def ragged():
+    """The 64-sequence ragged workload, drawn once: (H, lengths, per-stream
+    [total tokens, H, 64] arrays with sequence i's tokens contiguous)."""
+    H = 32
+    lengths = synth.ragged_lengths(64, 16, 2048, seed=4)
+    flat, _ = synth.make_segment_inputs(lengths, H, 64, seed=12, dtype="bf16", with_dy=True)
+    return H, lengths, flat
+
+
+def _oracle_sequence(flat, lengths, q, heads=None, backward=False):
+    """Oracle on sequence q alone, from its own tokens of the flat draw."""
+    off = int(np.sum(lengths[:q]))
+    L = int(lengths[q])
+    sl = [np.ascontiguousarray(flat[n][None, off:off + L]) for n in ("r", "w", "k", "v", "a", "b")]
+    units = None if heads is None else [(0, h) for h in heads]
+    if backward:
+        dy = np.ascontiguousarray(flat["dy"][None, off:off + L])
+        return O.backward(*sl, dy=dy, units=units)
+    return O.forward(*sl, units=units)
+
+
+def test_ragged_all_sequences_packed_and_padded(W, ragged):
+    """The 64-sequence ragged workload (lengths U[16, 2048], H=32, bf16, zero
+    initial states) run packed in 4 streams with resets and right-padded as
+    [64, 2048]: every sequence and head against the oracle in both layouts,
+    and both layouts give equal final states."""
+    import torch
+    H, lengths, flat = ragged
+    T_pk, st_pk, ln_pk = synth.packed_layout(lengths, 4)
+    order, st_s, ln_s = synth.sorted_table(st_pk, ln_pk)
+    layouts = {}
+    for name in ("packed", "padded"):
+        if name == "packed":
+            B, T = 4, T_pk
+            inp = synth.scatter_segments(flat, lengths, st_pk, B, T, dtype="bf16")
+            st, ln, seq_of = st_s, ln_s, order                # table entry e is sequence order[e]
+        else:
+            B, T = 64, 2048
+            st, ln = synth.padded_layout(lengths, T)
+            inp = synth.scatter_segments(flat, lengths, st, B, T, dtype="bf16")
+            seq_of = np.arange(64)
+        seg = W.Segments(B, T, st, ln, "cuda:0")
+        ts = _dev(inp)
+        del inp
+        y, s_out, _ = W.wkv7_forward(*ts, None, segments=seg)
+        torch.cuda.synchronize()
+        del ts
+        layouts[name] = (_host32(y).reshape(B * T, H, 64), U.host(s_out), np.asarray(st), seq_of)
+        del y, s_out
+        torch.cuda.empty_cache()
+    worst_y = worst_s = 0.0
+    for q in range(64):
+        ref = _oracle_sequence(flat, lengths, q)
+        L = int(lengths[q])
+        for name, (yh, sh, st, seq_of) in layouts.items():
+            e = int(np.nonzero(seq_of == q)[0][0])
+            s0 = int(st[e])
+            worst_y = max(worst_y, U.unit_err_dense(yh[None, s0:s0 + L], ref["y"]))
+            worst_s = max(worst_s, U.unit_err_state(sh[e:e + 1], ref["s_out"]))
+    assert worst_y <= U.TOL_BF16_Y and worst_s <= U.TOL_F32, (worst_y, worst_s)
+    (_, s_pk, _, o_pk), (_, s_pd, _, _) = layouts["packed"], layouts["padded"]
+    inv = np.empty_like(o_pk)
+    inv[o_pk] = np.arange(64)
+    assert U.unit_err_state(s_pk[inv], s_pd) <= U.TOL_F32
+
+
+def test_ragged_backward_sampled_sequences(W, ragged):
+    """The ragged workload packed in 4 streams, forward with checkpoints and
+    backward: every head of five sequences (four drawn, plus the longest)
+    against the oracle's backward of that sequence alone."""
+    import torch
+    H, lengths, flat = ragged
+    T, st, ln = synth.packed_layout(lengths, 4)
+    order, st_s, ln_s = synth.sorted_table(st, ln)
+    inp = synth.scatter_segments(flat, lengths, st, 4, T, dtype="bf16")
+    seg = W.Segments(4, T, st_s, ln_s, "cuda:0")
+    ts = _dev(inp)
+    _, _, ckpt = W.wkv7_forward(*ts, None, segments=seg, checkpoints=True)
+    g = W.wkv7_backward(*ts, ckpt, U.dev_stream(inp.dy, "bf16"), None, segments=seg)
+    torch.cuda.synchronize()
+    gh = {n: _host32(g[n]).reshape(4 * T, H, 64) for n in GRADS}
+    ds0 = U.host(g["ds0"])
+    rng = np.random.default_rng(8)
+    picks = sorted(set(rng.choice(64, 4, replace=False).tolist()) | {int(np.argmax(lengths))})
+    worst = {}
+    for q in picks:
+        ref = _oracle_sequence(flat, lengths, q, backward=True)
+        e = int(np.nonzero(order == q)[0][0])
+        s0, L = int(st_s[e]), int(lengths[q])
+        for n in GRADS:
+            worst[n] = max(worst.get(n, 0.0), U.unit_err_dense(gh[n][None, s0:s0 + L], ref[n]))
+        worst["ds0"] = max(worst.get("ds0", 0.0), U.unit_err_state(ds0[e:e + 1], ref["ds0"]))
+    assert all(v <= U.TOL_GRAD for v in worst.values()), worst
+
+
+def test_decay_clamp_leak_bound(W):
+    """The chunked kernels clamp decay factors at 2^-30. A token with w = 0 and
+    a = 0 on every key wipes the state exactly (S_t = v_t k_t^T); with a large
+    initial state, |S_0| ~ 1e3 (1e4 times the workloads' 0.1), what the clamp
+    lets through is about 2^-30 |S_0| ~ 1e-6 of the O(1) state that follows.
+    Forward outputs, states, checkpoints and fp32 gradients stay within the
+    fp32 tolerances; a clamp as coarse as 2^-20 would exceed them here."""
+    import torch
+    B, T, H = 2, 48, 2
+    inp = synth.make_inputs(B, T, H, 64, seed=61, dtype="f32", with_dy=True, ds_out_std=0.1)
+    rng = np.random.default_rng(61)
+    inp.s0 = (1e3 * rng.standard_normal((B, H, 64, 64))).astype(np.float32)
+    inp.w[:, 21] = 0.0          # inside chunk 1, within its second 4-token group
+    inp.a[:, 21] = 0.0
+    ts = _dev(inp)
+    s0 = U.dev_f32(inp.s0)
+    y, s_out, ckpt = W.wkv7_forward(*ts, s0, checkpoints=True)
+    g = W.wkv7_backward(*ts, ckpt, U.dev_stream(inp.dy, "f32"), U.dev_f32(inp.ds_out))
+    torch.cuda.synchronize()
+    ref = O.forward(*inp.streams(), s0=inp.s0, checkpoints=True)
+    gr = O.backward(*inp.streams(), s0=inp.s0, dy=inp.dy, ds_out=inp.ds_out)
+    # the wipe is exact in the oracle: the state after token 21 has no trace of S_0
+    assert U.unit_err_dense(U.host(y)[:, 22:], ref["y"][:, 22:]) <= U.TOL_F32
+    assert U.unit_err_dense(U.host(y), ref["y"]) <= U.TOL_F32
+    assert U.unit_err_state(U.host(s_out), ref["s_out"]) <= U.TOL_F32
+    assert U.unit_err_ckpt(U.host(ckpt), ref["ckpt"], [0, 3], [3, 3]) <= U.TOL_F32
+    for n in GRADS:
+        assert U.unit_err_dense(U.host(g[n]), gr[n]) <= 1e-4, n
+    assert U.unit_err_state(U.host(g["ds0"]), gr["ds0"]) <= 1e-4
