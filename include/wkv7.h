@@ -75,6 +75,9 @@ extern "C" {
 #define WKV7_HEAD_SIZE_WIDE 128  /* also taken by wkv7_forward, wkv7_decode_step
                                     and the gated DeltaNet calls */
 #define WKV7_CHUNK 16
+/* static scratch of wkv7_backward_noalloc per device: 128 MiB, enough for
+   B*ceil(T/16)*H <= 6241 (e.g. B=1, T=3120, H=32) */
+#define WKV7_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
 
 typedef enum {
     WKV7_OK = 0,
@@ -160,6 +163,27 @@ wkv7_status wkv7_backward(const wkv7_desc *d,
                           void *dr, void *dw, void *dk, void *dv, void *da, void *db,
                           float *ds0, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * wkv7_backward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments and results are those of wkv7_backward, without the workspace:
+ * the per-chunk results of the first kernel go to a static device array of
+ * WKV7_STATIC_SCRATCH_BYTES that the library holds on every device it runs
+ * on until the process ends. A descriptor whose wkv7_workspace_bytes exceeds
+ * that size gets WKV7_ERR_WORKSPACE_TOO_SMALL before any HIP call. The call
+ * allocates nothing; its first call on a device looks up the array's address
+ * there. Every call on one device uses the same array, and each call writes
+ * every entry it reads before reading it: calls that may overlap in time on
+ * one device (on different streams, or from several threads) race and must
+ * be serialised by the caller.
+ */
+wkv7_status wkv7_backward_noalloc(const wkv7_desc *d,
+                                  const void *r, const void *w, const void *k,
+                                  const void *v, const void *a, const void *b,
+                                  const float *ckpt, const void *dy, const float *ds_out,
+                                  void *dr, void *dw, void *dk, void *dv, void *da, void *db,
+                                  float *ds0, void *stream);
 
 /*
  * One decode step for B independent sequences (the rwkv-metal page's

@@ -178,6 +178,36 @@ size_t vce_fwd_bytes(int32_t M, int32_t V) {
     return pad256((size_t)f.nsplit * M * 8) + pad256((size_t)M * 4);
 }
 
+// Device address of `scratch` (below) on each device, looked up once per
+// device on the first wkv7_backward_noalloc call made with it current. In host
+// code the array's name is only a stand-in for the symbol, never an address
+// a kernel may use.
+std::atomic<void *> g_scratch[64];
+
+wkv7_status scratch_address(void **out);
+
+}  // namespace
+
+// Static scratch of wkv7_backward_noalloc: the backward's per-chunk workspace
+// for callers that cannot allocate. Each device holds its own copy for the
+// life of the process; calls on one device share it.
+static __device__ __align__(256) unsigned char scratch[WKV7_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+wkv7_status scratch_address(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return WKV7_ERR_HIP;
+    if (dev < 0 || dev >= 64) return WKV7_ERR_UNSUPPORTED;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return WKV7_ERR_HIP;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return WKV7_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -277,11 +307,13 @@ wkv7_status wkv7_forward(const wkv7_desc *d, const void *r, const void *w, const
     return WKV7_OK;
 }
 
-wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, const void *k,
-                          const void *v, const void *a, const void *b, const float *ckpt,
-                          const void *dy, const float *ds_out, void *dr, void *dw, void *dk,
-                          void *dv, void *da, void *db, float *ds0, void *workspace,
-                          size_t workspace_bytes, void *stream) {
+// The backward with the caller's workspace, or (use_scratch) with the
+// library's static scratch of this device in its place.
+static wkv7_status backward_impl(const wkv7_desc *d, const void *r, const void *w, const void *k,
+                                 const void *v, const void *a, const void *b, const float *ckpt,
+                                 const void *dy, const float *ds_out, void *dr, void *dw, void *dk,
+                                 void *dv, void *da, void *db, float *ds0, void *workspace,
+                                 size_t workspace_bytes, bool use_scratch, void *stream) {
     wkv7_status st = check_desc(d);
     if (st != WKV7_OK) return st;
     const void *streams[12] = {r, w, k, v, a, b, dr, dw, dk, dv, da, db};
@@ -292,8 +324,12 @@ wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, cons
     if ((st = check_ckpt(d, ckpt)) != WKV7_OK) return st;
     size_t need = 0;
     if ((st = wkv7_workspace_bytes(d, &need)) != WKV7_OK) return st;
-    if (workspace_bytes < need || (need > 0 && !workspace)) return WKV7_ERR_WORKSPACE_TOO_SMALL;
-    if (workspace && !aligned16(workspace)) return WKV7_ERR_INVALID_ARGUMENT;
+    if (use_scratch) {
+        if (need > WKV7_STATIC_SCRATCH_BYTES) return WKV7_ERR_WORKSPACE_TOO_SMALL;
+    } else {
+        if (workspace_bytes < need || (need > 0 && !workspace)) return WKV7_ERR_WORKSPACE_TOO_SMALL;
+        if (workspace && !aligned16(workspace)) return WKV7_ERR_INVALID_ARGUMENT;
+    }
     {
         const size_t state_bytes = (size_t)num_states(d) * d->H * d->N * d->N * sizeof(float);
         const size_t sb = stream_bytes(d, d->dtype);
@@ -305,6 +341,7 @@ wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, cons
         if (any_overlap(ins, 9, outs, 8)) return WKV7_ERR_INVALID_ARGUMENT;
     }
     if ((st = check_device()) != WKV7_OK) return st;
+    if (use_scratch && (st = scratch_address(&workspace)) != WKV7_OK) return st;
 
     hipStream_t hs = (hipStream_t)stream;
     wkv7::BwdArgs args;
@@ -330,6 +367,23 @@ wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, cons
     if (wkv7::launch_backward_sweep(args, hs) != hipSuccess) return WKV7_ERR_HIP;
     if (wkv7::launch_backward(args, hs) != hipSuccess) return WKV7_ERR_HIP;
     return WKV7_OK;
+}
+
+wkv7_status wkv7_backward(const wkv7_desc *d, const void *r, const void *w, const void *k,
+                          const void *v, const void *a, const void *b, const float *ckpt,
+                          const void *dy, const float *ds_out, void *dr, void *dw, void *dk,
+                          void *dv, void *da, void *db, float *ds0, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    return backward_impl(d, r, w, k, v, a, b, ckpt, dy, ds_out, dr, dw, dk, dv, da, db, ds0,
+                         workspace, workspace_bytes, false, stream);
+}
+
+wkv7_status wkv7_backward_noalloc(const wkv7_desc *d, const void *r, const void *w, const void *k,
+                                  const void *v, const void *a, const void *b, const float *ckpt,
+                                  const void *dy, const float *ds_out, void *dr, void *dw, void *dk,
+                                  void *dv, void *da, void *db, float *ds0, void *stream) {
+    return backward_impl(d, r, w, k, v, a, b, ckpt, dy, ds_out, dr, dw, dk, dv, da, db, ds0,
+                         nullptr, 0, true, stream);
 }
 
 static wkv7_status decode_impl(int32_t B, int32_t H, int32_t N, int32_t dtype, int32_t decay,

@@ -67,6 +67,7 @@ def lib():
         dptr = ctypes.POINTER(Desc)
         L.wkv7_forward.argtypes = [dptr] + [vp] * 11
         L.wkv7_backward.argtypes = [dptr] + [vp] * 16 + [vp, sz, vp]
+        L.wkv7_backward_noalloc.argtypes = [dptr] + [vp] * 17
         L.wkv7_decode_step.argtypes = [i32, i32, i32, i32, i32] + [vp] * 10
         L.wkv7_decode_step_fused.argtypes = ([i32, i32, i32, i32, i32] + [vp] * 12
                                              + [ctypes.c_float, vp, vp, vp])
@@ -83,7 +84,7 @@ def lib():
         L.vce_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.vce_forward.argtypes = [i32, i32, i32] + [vp] * 6 + [sz, vp]
         L.vce_backward.argtypes = [i32, i32, i32, i32] + [vp] * 8 + [sz, vp]
-        for fn in ("wkv7_forward", "wkv7_backward", "wkv7_decode_step", "wkv7_decode_step_fused",
+        for fn in ("wkv7_forward", "wkv7_backward", "wkv7_backward_noalloc", "wkv7_decode_step", "wkv7_decode_step_fused",
                    "wkv7_gdn_decode_step", "wkv7_gdn_workspace_bytes", "wkv7_gdn_forward",
                    "wkv7_checkpoint_slots",
                    "wkv7_workspace_bytes", "wkv7_segments_check", "vce_forward_workspace_bytes",
@@ -244,11 +245,8 @@ def wkv7_workspace_bytes(B, T, H, dtype, segments: Segments | None = None) -> in
     return int(n.value)
 
 
-def wkv7_backward(r, w, k, v, a, b, ckpt, dy=None, ds_out=None, *,
-                  segments: Segments | None = None, want_ds0: bool = True, workspace=None,
-                  grads=None, decay: str = "mult", grad_f32: bool = False):
-    """Returns dict dr, dw, dk, dv, da, db (dtype of r, or fp32 with grad_f32)
-    and ds0 (fp32 or None). With decay="log", dw is the gradient w.r.t. log(decay)."""
+def _backward_args(r, w, k, v, a, b, ckpt, dy, ds_out, segments, want_ds0, grads, grad_f32):
+    """Validated outputs (allocated when not given) of a backward call."""
     torch = _torch()
     B, T, H, n = r.shape
     dev = r.device
@@ -268,13 +266,25 @@ def wkv7_backward(r, w, k, v, a, b, ckpt, dy=None, ds_out=None, *,
     for nm in names:
         _req(grads[nm], nm, dev, gdt, r.shape)
     ds0 = torch.empty((S, H, N, N), device=dev, dtype=torch.float32) if want_ds0 else None
+    return grads, ds0
+
+
+def wkv7_backward(r, w, k, v, a, b, ckpt, dy=None, ds_out=None, *,
+                  segments: Segments | None = None, want_ds0: bool = True, workspace=None,
+                  grads=None, decay: str = "mult", grad_f32: bool = False):
+    """Returns dict dr, dw, dk, dv, da, db (dtype of r, or fp32 with grad_f32)
+    and ds0 (fp32 or None). With decay="log", dw is the gradient w.r.t. log(decay)."""
+    torch = _torch()
+    B, T, H, n = r.shape
+    grads, ds0 = _backward_args(r, w, k, v, a, b, ckpt, dy, ds_out, segments, want_ds0, grads, grad_f32)
     need = wkv7_workspace_bytes(B, T, H, _dtype_code(r), segments)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+        workspace = torch.empty(need, device=r.device, dtype=torch.uint8)
     if workspace is not None:
-        _req(workspace, "workspace", dev)
+        _req(workspace, "workspace", r.device)
     ws_bytes = 0 if workspace is None else _nbytes(workspace)
     d = _desc(B, T, H, _dtype_code(r), segments, decay, grad_f32)
+    names = ("dr", "dw", "dk", "dv", "da", "db")
     _check("wkv7_backward", lib().wkv7_backward(
         ctypes.byref(d), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(ckpt), _ptr(dy),
         _ptr(ds_out), *[_ptr(grads[nm]) for nm in names], _ptr(ds0), _ptr(workspace),
@@ -282,6 +292,36 @@ def wkv7_backward(r, w, k, v, a, b, ckpt, dy=None, ds_out=None, *,
     out = dict(grads)
     out["ds0"] = ds0
     return out
+
+
+def wkv7_backward_noalloc(r, w, k, v, a, b, ckpt, dy=None, ds_out=None, *,
+                          segments: Segments | None = None, want_ds0: bool = True, grads=None,
+                          ds0=None, decay: str = "mult", grad_f32: bool = False):
+    """wkv7_backward with the library's static per-device scratch instead of a
+    workspace (the C call allocates nothing; pass grads and ds0 to allocate
+    nothing here either). Returns the same dict as wkv7_backward."""
+    torch = _torch()
+    B, T, H, n = r.shape
+    if ds0 is not None:
+        want_ds0 = False
+    grads, ds0_new = _backward_args(r, w, k, v, a, b, ckpt, dy, ds_out, segments, want_ds0, grads,
+                                    grad_f32)
+    if ds0 is None:
+        ds0 = ds0_new
+    else:
+        S = segments.num_seqs if segments is not None else B
+        _req(ds0, "ds0", r.device, torch.float32, (S, H, N, N))
+    d = _desc(B, T, H, _dtype_code(r), segments, decay, grad_f32)
+    names = ("dr", "dw", "dk", "dv", "da", "db")
+    _check("wkv7_backward_noalloc", lib().wkv7_backward_noalloc(
+        ctypes.byref(d), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(ckpt), _ptr(dy),
+        _ptr(ds_out), *[_ptr(grads[nm]) for nm in names], _ptr(ds0), _stream()))
+    out = dict(grads)
+    out["ds0"] = ds0
+    return out
+
+
+STATIC_SCRATCH_BYTES = 128 << 20
 
 
 def wkv7_decode_step(r, w, k, v, a, b, s_in, s_out=None, y=None, *, decay: str = "mult"):

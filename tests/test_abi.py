@@ -316,3 +316,24 @@ def test_gdn_decode_rejects_overlapping_outputs():
     assert call(out=inside(FAR[5])) == INVALID          # out over s_in (out of place)
     assert call(out=inside(FAR[5]), s_out=FAR[5]) == INVALID  # out over the in-place state
     assert call(q=inside(FAR[6])) == INVALID            # s_out over q
+
+
+def test_backward_noalloc_size_limit_and_checks():
+    """The static-scratch backward refuses descriptors whose per-chunk results
+    exceed WKV7_STATIC_SCRATCH_BYTES, and validates like wkv7_backward."""
+    L = W.lib()
+    big = desc(B=4, T=4096, H=32)
+    assert W.wkv7_workspace_bytes(4, 4096, 32, 1) > W.STATIC_SCRATCH_BYTES
+
+    def call(d, ckpt=FAR[6], grads=None, dr=None):
+        g = list(grads or FAR[9:15])
+        return L.wkv7_backward_noalloc(ctypes.byref(d), *FAR[:6], ckpt, None, None, *g, None, None)
+    assert call(big) == WS
+    assert call(desc(N=128)) == UNSUPPORTED
+    assert call(desc(), ckpt=None) == INVALID
+    g = list(FAR[9:15]); g[1] = inside(FAR[1])
+    assert call(desc(), grads=g) == INVALID
+    # the header's limit and the binding's agree
+    text = open(W.HEADER).read()
+    assert "#define WKV7_STATIC_SCRATCH_BYTES ((size_t)128 << 20)" in text
+    assert W.STATIC_SCRATCH_BYTES == 128 << 20
