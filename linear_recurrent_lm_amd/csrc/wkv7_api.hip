@@ -173,6 +173,12 @@ wkv7_status vce_bwd_layout(int32_t M, int32_t D, int32_t V, int32_t vocab_chunk,
     return WKV7_OK;
 }
 
+// Segment mode: the backward's list of (sequence, chunk group) work items
+// after the per-chunk results: a count and at most ceil(slots / 8) +
+// num_seqs int32 pairs.
+int64_t glist_cap(int64_t slots, int64_t num_seqs) { return (slots + 7) / 8 + num_seqs; }
+size_t glist_bytes(int64_t slots, int64_t num_seqs) { return (size_t)(1 + 2 * glist_cap(slots, num_seqs)) * 4; }
+
 size_t vce_fwd_bytes(int32_t M, int32_t V) {
     const vce::FwdPlan f = vce::fwd_plan(M, V);
     return pad256((size_t)f.nsplit * M * 8) + pad256((size_t)M * 4);
@@ -245,6 +251,7 @@ wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes) {
         slots = (int64_t)d->B * ((d->T + kChunk - 1) / kChunk);
     }
     *bytes = (size_t)slots * d->H * (kN * kN + kChunk * kN + kChunk * kChunk) * sizeof(float);
+    if (d->num_seqs > 0) *bytes += pad256(glist_bytes(slots, d->num_seqs));
     return WKV7_OK;
 }
 
@@ -324,6 +331,13 @@ static wkv7_status backward_impl(const wkv7_desc *d, const void *r, const void *
     if ((st = check_ckpt(d, ckpt)) != WKV7_OK) return st;
     size_t need = 0;
     if ((st = wkv7_workspace_bytes(d, &need)) != WKV7_OK) return st;
+    {
+        // the second pass's grid: work items x heads (segment mode) or
+        // ceil(T / 128) chunk groups x B x H (dense) workgroups
+        const int64_t items = d->num_seqs > 0 ? glist_cap(d->ckpt_slots, d->num_seqs)
+                                              : (int64_t)d->B * ((d->T + 127) / 128);
+        if (items * d->H > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
+    }
     if (use_scratch) {
         if (need > WKV7_STATIC_SCRATCH_BYTES) return WKV7_ERR_WORKSPACE_TOO_SMALL;
     } else {
@@ -358,6 +372,14 @@ static wkv7_status backward_impl(const wkv7_desc *d, const void *r, const void *
         const int64_t slots = d->num_seqs > 0 ? d->ckpt_slots : (int64_t)d->B * ((d->T + kChunk - 1) / kChunk);
         args.ws_dr = args.ws + slots * d->H * kN * kN;
         args.ws_w = args.ws_dr + slots * d->H * kChunk * kN;
+        args.glist = nullptr;
+        args.glist_cap = 0;
+        if (d->num_seqs > 0) {
+            // 256-byte aligned start after the fp32 arrays
+            const size_t off = (size_t)slots * d->H * (kN * kN + kChunk * kN + kChunk * kChunk) * sizeof(float);
+            args.glist = (int32_t *)((char *)workspace + pad256(off));
+            args.glist_cap = glist_cap(slots, d->num_seqs);
+        }
     }
     if (d->num_seqs > 0) {
         void *outs[6] = {dr, dw, dk, dv, da, db};

@@ -175,15 +175,68 @@ __device__ __forceinline__ void tile_scatter(float *sM, bool isA, bool isB, int 
 
 template <int V> struct IC { static constexpr int value = V; };
 
+// Segment mode: the list of the second pass's work items, one per (sequence,
+// group of kChunksPerGroup consecutive chunks), so that the launch covers the
+// chunks the sequences have rather than ceil(T / 16) chunks for every
+// sequence (packed rows are long; most sequences are short). One workgroup:
+// each thread counts the groups of a block of sequences, an exclusive scan of
+// the counts gives each block its first entry. glist[0] = number of entries
+// (at most cap); entry e is (glist[1 + 2e], glist[2 + 2e]) = (sequence, group).
+// Invalid table entries count as empty, as in the kernels.
+__global__ __launch_bounds__(1024) void group_list_kernel(SegParams seg, int32_t *glist, int64_t cap) {
+    __shared__ int64_t part[1024];
+    const int tid = threadIdx.x;
+    const int n = seg.num_seqs;
+    const int per = (n + 1023) / 1024;
+    const int s0 = min(n, tid * per), s1 = min(n, s0 + per);
+    auto groups = [&](int s) {
+        const Unit u = resolve_unit(seg, s);
+        const int64_t nch = ((int64_t)u.len + kChunk - 1) / kChunk;
+        return (nch + kChunksPerGroup - 1) / kChunksPerGroup;
+    };
+    int64_t sum = 0;
+    for (int s = s0; s < s1; ++s) sum += groups(s);
+    part[tid] = sum;
+    __syncthreads();
+    // inclusive scan of the 1024 block counts (Hillis-Steele)
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int64_t x = tid >= d ? part[tid - d] : 0;
+        __syncthreads();
+        part[tid] += x;
+        __syncthreads();
+    }
+    int64_t off = part[tid] - sum;
+    for (int s = s0; s < s1; ++s) {
+        const int64_t gs = groups(s);
+        for (int64_t g = 0; g < gs; ++g, ++off) {
+            if (off < cap) {
+                glist[1 + 2 * off] = s;
+                glist[2 + 2 * off] = (int32_t)g;
+            }
+        }
+    }
+    if (tid == 1023) glist[0] = (int32_t)(part[1023] < cap ? part[1023] : cap);
+}
+
 template <typename TI>
 __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32_t units) {
     extern __shared__ __align__(16) float sm[];
-    // Workgroup -> (unit, group of kChunksPerGroup chunks).
-    const int unit = blockIdx.x % units;
-    const int grp = blockIdx.x / units;
+    // Workgroup -> (unit, group of kChunksPerGroup chunks): dense rows by
+    // workgroup index, segment mode through the pre-pass's work list.
     const int H = p.seg.H;
-    const int h = unit % H;
-    const int sq = unit / H;
+    int h, sq, grp;
+    if (p.glist) {
+        const int64_t e = blockIdx.x / H;
+        h = blockIdx.x % H;
+        if (e >= p.glist[0]) return;
+        sq = p.glist[1 + 2 * e];
+        grp = p.glist[2 + 2 * e];
+    } else {
+        const int unit = blockIdx.x % units;
+        grp = blockIdx.x / units;
+        h = unit % H;
+        sq = unit / H;
+    }
     const Unit u = resolve_unit(p.seg, sq);
 
     const int tid = threadIdx.x;
@@ -955,7 +1008,16 @@ hipError_t launch_backward(const BwdArgs &args, hipStream_t stream) {
             : a.dtype == 2 ? bwd_chunk_kernel<_Float16> : bwd_chunk_kernel<float>;
     hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    // A sequence lies within one row of T tokens, so it has at most ceil(T / 16) chunks.
+    if (a.seg.num_seqs > 0 && a.glist) {
+        // work items from the segment table: at most ceil(slots / 8) + num_seqs
+        hipLaunchKernelGGL(group_list_kernel, dim3(1), dim3(1024), 0, stream, a.seg, a.glist, a.glist_cap);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(fn, dim3((unsigned)(a.glist_cap * a.seg.H)), dim3(kThreads), lds, stream, a, units);
+        return hipGetLastError();
+    }
+    // A row has ceil(T / 16) chunks.
+    a.glist = nullptr;
     const int max_chunks = (a.seg.T + kChunk - 1) / kChunk;
     const int64_t groups = (max_chunks + kChunksPerGroup - 1) / kChunksPerGroup;
     hipLaunchKernelGGL(fn, dim3((unsigned)(groups * units)), dim3(kThreads), lds, stream, a, units);

@@ -569,8 +569,9 @@ template <typename TI>
 hipError_t launch_sweep_typed(const BwdArgs &a, hipStream_t stream) {
     const int S = a.seg.num_seqs > 0 ? a.seg.num_seqs : a.seg.B;
     const int32_t units = S * a.seg.H;
-    if (units >= 256) return launch_sweep<TI, 4, 1>(a, units, stream);
-    if (units >= 128) return launch_sweep<TI, 4, 2>(a, units, stream);
+    const int nrb = row_blocks_for(units);
+    if (nrb == 1) return launch_sweep<TI, 4, 1>(a, units, stream);
+    if (nrb == 2) return launch_sweep<TI, 4, 2>(a, units, stream);
     return launch_sweep<TI, 2, 2>(a, units, stream);
 }
 

@@ -621,8 +621,9 @@ hipError_t launch_typed(const FwdArgs &a, hipStream_t stream) {
     // One workgroup per CU (LDS); split value rows across workgroups when
     // there are fewer units than CUs, and then key columns across the state
     // waves that share rows.
-    if (units >= 256) return launch_ws<TI, 4, 1>(a, units, stream);
-    if (units >= 128) return launch_ws<TI, 4, 2>(a, units, stream);
+    const int nrb = row_blocks_for(units);
+    if (nrb == 1) return launch_ws<TI, 4, 1>(a, units, stream);
+    if (nrb == 2) return launch_ws<TI, 4, 2>(a, units, stream);
     return launch_ws<TI, 2, 2>(a, units, stream);
 }
 

@@ -33,6 +33,10 @@ struct BwdArgs {
     float *ws;                       // per-slot dS_C of the sweep ([slots][H][N][N] fp32)
     float *ws_dr;                    // per-slot drhs = W^T dX of the sweep ([slots][H][16][N] fp32)
     float *ws_w;                     // per-slot W = (I - L_ab)^-1 of the sweep ([slots][H][16][16] fp32)
+    // segment mode: the work items of the second pass, [count][(sequence,
+    // chunk group) x glist_cap], written by a pre-pass into the workspace
+    int32_t *glist;
+    int64_t glist_cap;
     const void *staged[8];           // filled by the launcher: r w k a b v dy, null
 };
 

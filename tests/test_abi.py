@@ -194,7 +194,11 @@ def test_workspace_query():
     per = 64 * 64 + 16 * 64 + 16 * 16
     assert W.wkv7_workspace_bytes(4, 64, 8, 1) == 4 * 4 * 8 * per * 4
     assert W.wkv7_workspace_bytes(3, 33, 2, 0) == 9 * 2 * per * 4
+    # segment mode adds the work-item list: a count and ceil(slots / 8) + num_seqs pairs, 256-aligned
     n = ctypes.c_size_t()
+    d = desc(num_seqs=3, seq_start=0x9000, seq_len=0x9000, ckpt_slots=9, H=2)
+    assert W.lib().wkv7_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value == 9 * 2 * per * 4 + 256
     assert W.lib().wkv7_workspace_bytes(ctypes.byref(desc(N=48)), ctypes.byref(n)) == UNSUPPORTED
     assert W.lib().wkv7_workspace_bytes(ctypes.byref(desc(N=128)), ctypes.byref(n)) == UNSUPPORTED
 
