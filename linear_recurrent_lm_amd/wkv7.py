@@ -20,7 +20,9 @@ import re
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libwkv7.so")
+# WKV7_LIBRARY names another build of the same library (the host-only
+# AddressSanitizer build the CPU tests use); by default the in-tree one.
+LIB_PATH = os.environ.get("WKV7_LIBRARY") or os.path.join(HERE, "libwkv7.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "wkv7.h")
 
 N = 64
