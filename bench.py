@@ -182,19 +182,21 @@ def pipe_probe():
         return float(np.median(lo)), float(np.median(hi)), paired, mhz
 
     names = {0: "v_mfma_f32_16x16x4_f32", 1: "v_mfma_f32_32x32x2_f32", 2: "v_mfma_f32_16x16x32_bf16",
+             4: "v_mfma_f32_16x16x16_bf16", 5: "v_mfma_f32_16x16x32_bf16 (eight chains)",
+             6: "v_mfma_f32_16x16x32_bf16 (one chain)", 7: "v_mfma_f32_16x16x4_f32 (one chain)",
              3: "v_fma_f32 (second VALU wave)"}
     out = {"workgroups": blocks, "waves": "8 per workgroup: waves 0-3 MFMA (4 independent chains) or, for "
                                           "the last entry, fp32 FMA; waves 4-7 fp32 FMA (8 independent chains); "
                                           "wave w and w+4 share a SIMD"}
     for kind, name in names.items():
-        mi = 2048 if kind < 3 else 8192
+        mi = 8192 if kind == 3 else 2048
         run(kind, 1, mi, 0)
         m_alone, _, paired, mhz = run(kind, 1, mi, 0)
         _, v_probe, _, _ = run(kind, 2, 0, 4096)
         vi = max(1, int(round(4096 * m_alone / v_probe)))
         _, v_alone, _, _ = run(kind, 2, 0, vi)
         m_both, v_both, paired2, _ = run(kind, 3, mi, vi)
-        per = 4 if kind < 3 else 8
+        per = 8 if kind == 3 else 4
         out[name] = {"first_side_instructions_per_wave": per * mi, "valu_fma_per_wave": 8 * vi,
                      "cycles_first_alone": m_alone, "cycles_valu_alone": v_alone,
                      "cycles_both_first_waves": m_both, "cycles_both_valu_waves": v_both,

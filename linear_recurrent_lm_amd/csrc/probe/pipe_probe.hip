@@ -21,6 +21,7 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int64_t cycles_now() {
     int64_t t;
@@ -37,7 +38,9 @@ __device__ __forceinline__ int64_t realtime_now() {
 __device__ __forceinline__ void consume(float x) { asm volatile("; consume %0" ::"v"(x) : "memory"); }
 
 // kind 0: v_mfma_f32_16x16x4_f32; 1: v_mfma_f32_32x32x2_f32;
-// 2: v_mfma_f32_16x16x32_bf16.
+// 2: v_mfma_f32_16x16x32_bf16; 4: v_mfma_f32_16x16x16_bf16;
+// 5: v_mfma_f32_16x16x32_bf16 with eight accumulator chains;
+// 6: v_mfma_f32_16x16x32_bf16, one chain; 7: v_mfma_f32_16x16x4_f32, one chain.
 template <int KIND>
 __device__ float mfma_loop(int iters, float x) {
     if constexpr (KIND == 0) {
@@ -58,6 +61,43 @@ __device__ float mfma_loop(int iters, float x) {
             c3 = __builtin_amdgcn_mfma_f32_32x32x2f32(x, x, c3, 0, 0, 0);
         }
         return c0[0] + c1[1] + c2[2] + c3[3];
+    } else if constexpr (KIND == 4) {
+        i16x4 a;
+        for (int e = 0; e < 4; ++e) a[e] = (short)(__builtin_bit_cast(unsigned, x + 0.125f * e) >> 16);
+        f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0;
+        for (int i = 0; i < iters; ++i) {
+            c0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, a, c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, a, c1, 0, 0, 0);
+            c2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, a, c2, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, a, c3, 0, 0, 0);
+        }
+        return c0[0] + c1[1] + c2[2] + c3[3];
+    } else if constexpr (KIND == 6) {
+        bf16x8 a;
+        for (int e = 0; e < 8; ++e) a[e] = (__bf16)(x + 0.125f * e);
+        f32x4 c0 = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < iters; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, c0, 0, 0, 0);
+        }
+        return c0[0] + c0[3];
+    } else if constexpr (KIND == 7) {
+        f32x4 c0 = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < iters; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(x, x, c0, 0, 0, 0);
+        }
+        return c0[0] + c0[3];
+    } else if constexpr (KIND == 5) {
+        bf16x8 a;
+        for (int e = 0; e < 8; ++e) a[e] = (__bf16)(x + 0.125f * e);
+        f32x4 c[8];
+        for (int q = 0; q < 8; ++q) c[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < iters; i += 2) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) c[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, c[q], 0, 0, 0);
+        }
+        return c[0][0] + c[1][1] + c[2][2] + c[3][3] + c[4][0] + c[5][1] + c[6][2] + c[7][3];
     } else {
         bf16x8 a;
         for (int e = 0; e < 8; ++e) a[e] = (__bf16)(x + 0.125f * e);
@@ -135,7 +175,9 @@ extern "C" {
 
 // Runs the probe on `blocks` workgroups (rec: device int64 [blocks * 32],
 // sink: device float [blocks * 512]). kind: 0 = fp32 16x16x4, 1 = fp32
-// 32x32x2, 2 = bf16 16x16x32 MFMA, 3 = VALU on waves 0-3 as well;
+// 32x32x2, 2 = bf16 16x16x32 MFMA, 3 = VALU on waves 0-3 as well,
+// 4 = bf16 16x16x16, 5 = bf16 16x16x32 on eight chains, 6 = bf16 16x16x32
+// on one chain, 7 = fp32 16x16x4 on one chain;
 // side_mask: 1 = waves 0-3 on, 2 = waves 4-7 on. Returns 0 on success,
 // else the HIP error code.
 int wkv7_probe_pipe(int kind, int side_mask, int mfma_iters, int valu_iters, int blocks, int64_t *rec,
@@ -155,6 +197,18 @@ int wkv7_probe_pipe(int kind, int side_mask, int mfma_iters, int valu_iters, int
         break;
     case 3:
         hipLaunchKernelGGL(pipe_probe_kernel<3>, dim3(blocks), dim3(512), 0, s, side_mask, mfma_iters, valu_iters, m, c, rec, sink);
+        break;
+    case 4:
+        hipLaunchKernelGGL(pipe_probe_kernel<4>, dim3(blocks), dim3(512), 0, s, side_mask, mfma_iters, valu_iters, m, c, rec, sink);
+        break;
+    case 5:
+        hipLaunchKernelGGL(pipe_probe_kernel<5>, dim3(blocks), dim3(512), 0, s, side_mask, mfma_iters, valu_iters, m, c, rec, sink);
+        break;
+    case 6:
+        hipLaunchKernelGGL(pipe_probe_kernel<6>, dim3(blocks), dim3(512), 0, s, side_mask, mfma_iters, valu_iters, m, c, rec, sink);
+        break;
+    case 7:
+        hipLaunchKernelGGL(pipe_probe_kernel<7>, dim3(blocks), dim3(512), 0, s, side_mask, mfma_iters, valu_iters, m, c, rec, sink);
         break;
     default:
         return (int)hipErrorInvalidValue;

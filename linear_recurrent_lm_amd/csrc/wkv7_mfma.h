@@ -13,6 +13,49 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// bf16 MFMA with fp32 accumulation. The 16x16 tiles keep the fp32 layouts
+// above: lane l supplies row l % 16 of A and column l % 16 of B, and the
+// contraction elements of lane group g = l / 16 are its 8 consecutive vector
+// elements; D[4 g + r][l % 16] comes back in
+// element r. Only the pairing of a lane's element e in A with the same
+// lane group's element e in B matters, so each caller chooses which logical
+// contraction index element e stands for, the same way on both sides.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma_bf16_k32(u32x4_t a, u32x4_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ u32x4_t cat(u32x2_t a, u32x2_t b) { return u32x4_t{a.x, a.y, b.x, b.y}; }
+
+// Two fp32 values to one word of two bf16 (lo in bits 0-15), each rounded to
+// nearest even: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Three-piece bf16 split of two fp32 values, x = h + m + l: each piece is the
+// previous remainder rounded to bf16 and each remainder is exact in fp32, so
+// the pieces carry 24 significant bits (|x - h - m - l| <= 2^-24 |x|). The
+// products h_a h_b + h_a m_b + m_a h_b + h_a l_b + m_a m_b + l_a h_b then
+// reproduce an fp32 product up to terms of order 2^-24 |a b| (for |x| above
+// about 2^-110, where the last piece is still a normal number).
+__device__ __forceinline__ void split3(float x0, float x1, uint32_t &h, uint32_t &m, uint32_t &l) {
+    h = pk_bf16(x0, x1);
+    x0 -= bf_lo(h);
+    x1 -= bf_hi(h);
+    m = pk_bf16(x0, x1);
+    x0 -= bf_lo(m);
+    x1 -= bf_hi(m);
+    l = pk_bf16(x0, x1);
+}
+
 // 16x16 product over K = 64: D[m][n] = sum_j A_m[j] B_n[j], where this lane
 // supplies row m = lane % 16 of A (arow) and row n = lane % 16 of B (brow),
 // both 16-byte aligned rows of 64 floats.

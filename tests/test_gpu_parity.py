@@ -146,6 +146,36 @@ def test_workgroup_shapes_f32(W, H):
     assert U.unit_err_state(g["ds0"], gr["ds0"]) <= 1e-4
 
 
+@pytest.mark.parametrize("decay", ["mult", "log"])
+def test_split_path_fast_and_slow_chunks(W, decay):
+    """bf16 with 256 units (B=8, H=32) runs 64-row workgroups, whose state
+    products are three-piece bf16 MFMAs. A chunk whose decays are all at least
+    2^-6 builds its 16x16 matrices from MFMA tiles of the hand-off rows, any
+    other chunk from the split-point rows: chunk 1 holds a token with decay 0
+    (1e-13 as a logarithm), chunk 3 decays of 2^-10 on some keys; chunks 0, 2
+    and the partial chunk 4 take the tile path. Every unit's y, final state and
+    checkpoints against the oracle, for both decay inputs."""
+    import torch
+    B, T, H = 8, 77, 32
+    inp = synth.make_inputs(B, T, H, 64, seed=500, dtype="bf16", s0_std=0.1, decay=decay)
+    if decay == "mult":
+        inp.w[:, 21] = 0.0
+        inp.w[:, 50, :, :5] = 2.0 ** -10
+    else:
+        inp.w[:, 21] = synth.round_bf16(np.float32(np.log(1e-13)))
+        inp.w[:, 50, :, :5] = synth.round_bf16(np.float32(np.log(2.0 ** -10)))
+    ts = [U.dev_stream(x, "bf16") for x in inp.streams()]
+    y, s_out, ckpt = W.wkv7_forward(*ts, U.dev_f32(inp.s0), checkpoints=True, decay=decay)
+    torch.cuda.synchronize()
+    w = inp.w.astype(np.float64)
+    dec = np.exp(w) if decay == "log" else w
+    ref = O.forward(inp.r, dec, inp.k, inp.v, inp.a, inp.b, s0=inp.s0, checkpoints=True)
+    nc = -(-T // 16)
+    assert U.unit_err_dense(U.host(y), ref["y"]) <= U.TOL_BF16_Y
+    assert U.unit_err_state(U.host(s_out), ref["s_out"]) <= U.TOL_F32
+    assert U.unit_err_ckpt(U.host(ckpt), ref["ckpt"], [b * nc for b in range(B)], [nc] * B) <= U.TOL_F32
+
+
 def test_forward_deterministic(W):
     import torch
     inp = synth.make_inputs(2, 100, 4, 64, seed=9, dtype="bf16", s0_std=0.1)
