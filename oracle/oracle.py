@@ -257,3 +257,48 @@ def gdn_forward(q, k, v, g, beta, s0=None):
     w = np.broadcast_to(dec, (B, T, H, N))
     out = forward(qn, w, bt * kn, v, -kn, kn * dec * bt, s0=s0)
     return out["y"] / np.sqrt(N), out["s_out"]
+
+
+def gdn_backward(q, k, v, g, beta, s0=None, dout=None, ds_out=None):
+    """Reverse-mode gradients of L = sum <dout, out> + <ds_out, S_T> for
+    gdn_forward (rwkv-lab, "Highlight result -- GDN in RWKV-7"), by the chain
+    rule from the WKV-7 backward through the remap and the normalisation:
+
+        r = q^, w = e^g, k_w = beta k^, a = -k^, b = beta e^g k^, out = y / sqrt(N)
+        dq^ = dr;  dk^ = beta dk_w - da + beta e^g db
+        dg = e^g (sum_j dw_j + beta sum_j db_j k^_j)
+        dbeta = sum_j dk_w,j k^_j + e^g sum_j db_j k^_j
+        x^ = x / max(|x|, 1e-12):  dx = (dx^ - x^ <x^, dx^>) / |x|  (|x| > 1e-12),
+                                   dx = dx^ / 1e-12 otherwise
+
+    Value heads that share a key head add their dq^, dk^. Shapes as in
+    gdn_forward; dout [B, T, H, N] and ds_out [B, H, N, N] or None (zero).
+    Returns dict dq, dk [B, T, Hk, N], dv [B, T, H, N], dg, dbeta [B, T, H]
+    and ds0 [B, H, N, N], all fp64."""
+    q, k, v = _d(q), _d(k), _d(v)
+    g, beta = _d(g), _d(beta)
+    B, T, Hk, N = q.shape
+    H = v.shape[2]
+    grp = H // Hk
+    kh = np.arange(H) // grp
+    qd = np.maximum(np.linalg.norm(q, axis=-1, keepdims=True), GDN_NORM_EPS)
+    kd = np.maximum(np.linalg.norm(k, axis=-1, keepdims=True), GDN_NORM_EPS)
+    qn, kn = q / qd, k / kd
+    r, kk = qn[:, :, kh], kn[:, :, kh]
+    dec = np.exp(g)[..., None]
+    bt = beta[..., None]
+    w = np.broadcast_to(dec, (B, T, H, N))
+    dy = None if dout is None else _d(dout) / np.sqrt(N)
+    gr = backward(r, w, bt * kk, v, -kk, kk * dec * bt, s0=s0, dy=dy, ds_out=ds_out)
+    dkk = bt * gr["dk"] - gr["da"] + bt * dec * gr["db"]
+    dg = np.exp(g) * (np.sum(gr["dw"], axis=-1) + beta * np.sum(gr["db"] * kk, axis=-1))
+    dbeta = np.sum(gr["dk"] * kk, axis=-1) + np.exp(g) * np.sum(gr["db"] * kk, axis=-1)
+    dqn = gr["dr"].reshape(B, T, Hk, grp, N).sum(axis=3)
+    dkn = dkk.reshape(B, T, Hk, grp, N).sum(axis=3)
+
+    def through_norm(xn, xd, dxn):
+        proj = np.sum(xn * dxn, axis=-1, keepdims=True)
+        return np.where(xd > GDN_NORM_EPS, (dxn - xn * proj) / xd, dxn / GDN_NORM_EPS)
+
+    return {"dq": through_norm(qn, qd, dqn), "dk": through_norm(kn, kd, dkn), "dv": gr["dv"],
+            "dg": dg, "dbeta": dbeta, "ds0": gr["ds0"]}

@@ -154,3 +154,54 @@ def test_gdn_slip_is_caught(mutation, monkeypatch):
 def test_gdn_restatement_passes_pins(monkeypatch):
     monkeypatch.setattr(O, "gdn_decode_step", _gdn("none"))
     assert [n for n, (fn, tol) in P.PINS.items() if n.startswith("p15") and not fn() <= tol] == []
+
+
+def _gdn_backward(mut):
+    """A restatement of the GDN backward's chain rule with one planted slip."""
+    def bwd(q, k, v, g, beta, s0=None, dout=None, ds_out=None):
+        q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+        g, beta = np.asarray(g, np.float64), np.asarray(beta, np.float64)
+        B, T, Hk, N = q.shape
+        H = v.shape[2]
+        grp = H // Hk
+        kh = np.arange(H) // grp
+        qd = np.linalg.norm(q, axis=-1, keepdims=True)
+        kd = np.linalg.norm(k, axis=-1, keepdims=True)
+        qn, kn = q / qd, k / kd
+        r, kk = qn[:, :, kh], kn[:, :, kh]
+        dec, bt = np.exp(g)[..., None], beta[..., None]
+        w = np.broadcast_to(dec, (B, T, H, N))
+        gr = O.backward(r, w, bt * kk, v, -kk, kk * dec * bt, s0=s0,
+                        dy=None if dout is None else dout / np.sqrt(N), ds_out=ds_out)
+        dkk = bt * gr["dk"] + (gr["da"] if mut == "da_sign" else -gr["da"]) + bt * dec * gr["db"]
+        dg = (1.0 if mut == "dg_no_decay" else np.exp(g)) * (
+            np.sum(gr["dw"], axis=-1) + (0.0 if mut == "dg_no_b_term" else beta * np.sum(gr["db"] * kk, axis=-1)))
+        dbeta = np.sum(gr["dk"] * kk, axis=-1) + (0.0 if mut == "dbeta_no_b_term" else np.exp(g) * np.sum(gr["db"] * kk, axis=-1))
+        if mut == "no_group_sum":
+            dqn, dkn = gr["dr"][:, :, ::grp], dkk[:, :, ::grp]
+        else:
+            dqn = gr["dr"].reshape(B, T, Hk, grp, N).sum(axis=3)
+            dkn = dkk.reshape(B, T, Hk, grp, N).sum(axis=3)
+        def through(xn, xd, dxn):
+            if mut == "norm_no_projection":
+                return dxn / xd
+            return (dxn - xn * np.sum(xn * dxn, axis=-1, keepdims=True)) / xd
+        return {"dq": through(qn, qd, dqn), "dk": through(kn, kd, dkn), "dv": gr["dv"],
+                "dg": dg, "dbeta": dbeta, "ds0": gr["ds0"]}
+    return bwd
+
+
+GDN_BACKWARD_SLIPS = ["da_sign", "dg_no_decay", "dg_no_b_term", "dbeta_no_b_term", "no_group_sum",
+                      "norm_no_projection"]
+
+
+@pytest.mark.parametrize("mutation", GDN_BACKWARD_SLIPS)
+def test_gdn_backward_slip_is_caught(mutation, monkeypatch):
+    monkeypatch.setattr(O, "gdn_backward", _gdn_backward(mutation))
+    failed = [n for n, (fn, tol) in P.PINS.items() if n.startswith("p17") and not fn() <= tol]
+    assert failed, f"no pin detects GDN backward slip {mutation}"
+
+
+def test_gdn_backward_restatement_passes_pins(monkeypatch):
+    monkeypatch.setattr(O, "gdn_backward", _gdn_backward("none"))
+    assert [n for n, (fn, tol) in P.PINS.items() if n.startswith("p17") and not fn() <= tol] == []

@@ -524,6 +524,64 @@ def pin_p16_gdn_zero_rows(seed=43):
     return max(err, rel(s_out, st))
 
 
+# P17: the GDN backward through the remap (oracle.gdn_backward).
+def _gdn_seq(seed, B, T, Hk, H, N):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((B, T, Hk, N))
+    k = rng.standard_normal((B, T, Hk, N))
+    v = rng.standard_normal((B, T, H, N))
+    g = -rng.uniform(0.01, 1.0, (B, T, H))
+    beta = rng.uniform(0.05, 1.0, (B, T, H))
+    s0 = 0.3 * rng.standard_normal((B, H, N, N))
+    dout = rng.standard_normal((B, T, H, N))
+    dso = rng.standard_normal((B, H, N, N))
+    return dict(q=q, k=k, v=v, g=g, beta=beta, s0=s0), dout, dso
+
+
+def pin_p17_gdn_finite_differences(seed=51, eps=1e-6):
+    """Central finite differences of L = sum <dout, out> + <ds_out, S_T>
+    through gdn_forward, w.r.t. every element of q, k, v, g, beta and S_0
+    (two value heads over one key head, N = 6)."""
+    args, dout, dso = _gdn_seq(seed, 1, 4, 1, 2, 6)
+
+    def loss(**kw):
+        out, s_out = O.gdn_forward(**{**args, **kw})
+        return np.sum(dout * out) + np.sum(dso * s_out)
+
+    gb = O.gdn_backward(**args, dout=dout, ds_out=dso)
+    worst = 0.0
+    for name, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"),
+                        ("beta", "dbeta"), ("s0", "ds0")):
+        x = args[name]; fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            h = eps * max(1.0, abs(x[idx]))
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            fd[idx] = (loss(**{name: xp}) - loss(**{name: xm})) / (2 * h)
+        worst = max(worst, rel(gb[gname], fd))
+    return worst
+
+
+def pin_p17_gdn_identities(seed=52):
+    """At N = 128 (32 value heads' geometry scaled down to 4 over 2 key
+    heads): <dq, q> = <dk, k> = 0 per token and key head (the output does
+    not depend on the lengths of q and k); sum <dv, v> + <ds0, S_0> = L (out
+    and S_T are linear in (v, S_0) jointly); with beta = 0 nothing is
+    written, so dk = dv = 0 exactly."""
+    args, dout, dso = _gdn_seq(seed, 2, 5, 2, 4, 128)
+    out, s_out = O.gdn_forward(**args)
+    gb = O.gdn_backward(**args, dout=dout, ds_out=dso)
+    L = np.sum(dout * out) + np.sum(dso * s_out)
+    scale = np.max(np.abs(gb["dq"])) * np.max(np.abs(args["q"])) * 128
+    worst = float(np.max(np.abs(np.sum(gb["dq"] * args["q"], axis=-1)))) / scale
+    scale = np.max(np.abs(gb["dk"])) * np.max(np.abs(args["k"])) * 128
+    worst = max(worst, float(np.max(np.abs(np.sum(gb["dk"] * args["k"], axis=-1)))) / scale)
+    euler = np.sum(gb["dv"] * args["v"]) + np.sum(gb["ds0"] * args["s0"])
+    worst = max(worst, abs(L - euler) / abs(L))
+    g0 = O.gdn_backward(**{**args, "beta": np.zeros_like(args["beta"])}, dout=dout, ds_out=dso)
+    return max(worst, float(np.max(np.abs(g0["dk"]))), float(np.max(np.abs(g0["dv"]))))
+
+
 PINS = {
     "p1_cumulative": (pin_p1, 1e-12),
     "p2_w0_last_outer": (pin_p2, 1e-12),
@@ -552,6 +610,8 @@ PINS = {
     "p16_gdn_forward_textbook": (pin_p16_gdn_forward_textbook, 1e-12),
     "p16_gdn_forward_zero_state": (pin_p16_gdn_forward_zero_state, 1e-12),
     "p16_gdn_zero_rows": (pin_p16_gdn_zero_rows, 1e-12),
+    "p17_gdn_backward_finite_differences": (pin_p17_gdn_finite_differences, 1e-6),
+    "p17_gdn_backward_identities": (pin_p17_gdn_identities, 1e-12),
 }
 
 
