@@ -19,7 +19,7 @@ a "leg" that --only can select, so that a profiler run covers one leg:
     decode    decode step B=512 H=32 (warm and after a 1 GiB cache flush),
               the fused step, and a B=1 loop launched and graph-replayed
     gdn       gated DeltaNet decode and prefill through the RWKV-7 remap
-    n128      forward at head size 128
+    n128      forward at head size 128; forward with checkpoints + backward
     variants  fp16 prefill; the step with log decay and fp32 gradients
     ce        LM-head cross-entropy over the 65536-entry vocabulary
 
@@ -528,6 +528,24 @@ def leg_n128(args, W, synth, out):
         "workload": "WKV-7 forward at head size 128, bf16 B=16 T=1024 H=32, initial state N(0,0.1^2)",
         "ms": f128_ms, "tokens_per_s": 16 * 1024 / (f128_ms * 1e-3),
         "fp32_frac": f128_flop / (f128_ms * 1e-3) / PEAK_FP32}
+    # training step at head size 128 on the same shape: forward with
+    # checkpoints, then the backward from dy ~ N(0, 1) and the initial state
+    B, T, H = 16, 1024, 32
+    rng = np.random.default_rng(13)
+    dy = torch.from_numpy(rng.standard_normal((B, T, H, 128), dtype=np.float32)).to("cuda:0").to(torch.bfloat16)
+    ck = torch.empty((W.checkpoint_slots(B, T), H, 128, 128), device="cuda:0", dtype=torch.float32)
+    grads = {n: torch.empty_like(wts[0]) for n in ("dr", "dw", "dk", "dv", "da", "db")}
+    ws = torch.empty(W.wkv7_workspace_bytes(B, T, H, W.BF16, n=128), device="cuda:0", dtype=torch.uint8)
+    fc_ms = _time_ms(lambda: W.wkv7_forward(*wts, ws0, checkpoints=True, y=wy, s_out=wso, ckpt=ck),
+                     args.warmup, args.steps)
+    b_ms = _time_ms(lambda: W.wkv7_backward(*wts, ck, dy, None, grads=grads, want_ds0=True, workspace=ws),
+                    args.warmup, args.steps)
+    th = B * T * H
+    out["train_n128"] = {
+        "workload": "WKV-7 at head size 128, bf16 B=16 T=1024 H=32: forward with 16-token checkpoints, "
+                    "then the backward (token order, fp32 accumulators)",
+        "forward_ckpt_ms": fc_ms, "backward_ms": b_ms, "tokens_per_s": B * T / ((fc_ms + b_ms) * 1e-3),
+        "backward_fp32_frac": 26 * 128 * 128 * th / (b_ms * 1e-3) / PEAK_FP32}
 
 
 def leg_variants(args, W, synth, out):
@@ -621,6 +639,9 @@ KERNEL_LABELS = {
     "decode_kernel": "WKV-7 decode step",
     "decode128_kernel": "WKV-7 decode step, head size 128",
     "fwd128_kernel": "WKV-7 forward, head size 128 (token order)",
+    "bwd128_kernel": "WKV-7 backward, head size 128 (token order, 8-row blocks)",
+    "bwd128_zero_kernel": "WKV-7 backward, head size 128: accumulator clear",
+    "bwd128_finish_kernel": "WKV-7 backward, head size 128: accumulators to gradients",
     "gdn_decode_kernel": "gated DeltaNet decode step",
     "gdn_norm_kernel": "gated DeltaNet prefill: q^, k^ pre-pass",
     "gdn_fwd_kernel": "gated DeltaNet prefill: recurrence",

@@ -72,8 +72,9 @@ extern "C" {
 
 #define WKV7_ABI_VERSION 2
 #define WKV7_HEAD_SIZE 64        /* the head size every call takes */
-#define WKV7_HEAD_SIZE_WIDE 128  /* also taken by wkv7_forward, wkv7_decode_step
-                                    and the gated DeltaNet calls */
+#define WKV7_HEAD_SIZE_WIDE 128  /* also taken by wkv7_forward, wkv7_backward,
+                                    wkv7_workspace_bytes, wkv7_decode_step and
+                                    the gated DeltaNet calls */
 #define WKV7_CHUNK 16
 /* static scratch of wkv7_backward_noalloc per device: 128 MiB, enough for
    B*ceil(T/16)*H <= 6241 (e.g. B=1, T=3120, H=32) */
@@ -152,9 +153,13 @@ wkv7_status wkv7_forward(const wkv7_desc *d,
  * No output (dr..db, ds0, workspace) may share a byte with an input (r..b,
  * ckpt, dy, ds_out) or another output: WKV7_ERR_INVALID_ARGUMENT.
  * The recurrence is recomputed from the 16-token checkpoints in fp32, not
- * reconstructed by dividing by the decay. Two kernels run back to back on
- * `stream`: a reverse sweep that carries only the state gradient, then the
- * per-chunk gradients, all chunks in parallel.
+ * reconstructed by dividing by the decay. N = 64: two kernels run back to
+ * back on `stream`, a reverse sweep that carries only the state gradient,
+ * then the per-chunk gradients, all chunks in parallel. N = 128: token by
+ * token, blocks of 8 value rows per workgroup through the whole sequence in
+ * reverse; their shares of dr, dk, db, dw, da are added in fp32 in the
+ * workspace with atomics (so the summation order, and the last bits of
+ * those gradients, can differ between calls), then converted.
  */
 wkv7_status wkv7_backward(const wkv7_desc *d,
                           const void *r, const void *w, const void *k,
@@ -176,7 +181,8 @@ wkv7_status wkv7_backward(const wkv7_desc *d,
  * there. Every call on one device uses the same array, and each call writes
  * every entry it reads before reading it: calls that may overlap in time on
  * one device (on different streams, or from several threads) race and must
- * be serialised by the caller.
+ * be serialised by the caller. Head size 64 only (N = 128:
+ * WKV7_ERR_UNSUPPORTED).
  */
 wkv7_status wkv7_backward_noalloc(const wkv7_desc *d,
                                   const void *r, const void *w, const void *k,
@@ -290,11 +296,12 @@ wkv7_status wkv7_gdn_forward(int32_t B, int32_t T, int32_t H, int32_t Hk, int32_
 /* Number of checkpoint slots a dense forward needs: B * ceil(T / 16). */
 wkv7_status wkv7_checkpoint_slots(int32_t B, int32_t T, int64_t *slots);
 
-/* Workspace bytes wkv7_backward needs for this descriptor: checkpoint slots
- * (B * ceil(T / 16) dense, the segment table's slot count otherwise) x H x
- * (64 x 64 + 16 x 64 + 16 x 16) x 4; in segment mode plus 4 x (1 + 2 x
- * (ceil(slots / 8) + num_seqs)) bytes rounded up to 256 (the list of
- * (sequence, 8-chunk group) work items of the second kernel). */
+/* Workspace bytes wkv7_backward needs for this descriptor. N = 64:
+ * checkpoint slots (B * ceil(T / 16) dense, the segment table's slot count
+ * otherwise) x H x (64 x 64 + 16 x 64 + 16 x 16) x 4; in segment mode plus
+ * 4 x (1 + 2 x (ceil(slots / 8) + num_seqs)) bytes rounded up to 256 (the
+ * list of (sequence, 8-chunk group) work items of the second kernel).
+ * N = 128: 5 x B x T x H x 128 x 4 (fp32 accumulators of five gradients). */
 wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes);
 
 /*

@@ -53,8 +53,8 @@ bool any_overlap(const Range *ins, int nin, const Range *outs, int nout) {
 
 bool dtype_ok(int32_t dtype) { return dtype == WKV7_F32 || dtype == WKV7_BF16 || dtype == WKV7_F16; }
 
-// wide: the call also takes head size 128 (the forward does; the backward
-// and its workspace query do not).
+// wide: the call also takes head size 128 (the forward, the backward and its
+// workspace query do; the allocation-free backward does not).
 wkv7_status check_desc(const wkv7_desc *d, bool wide = false) {
     if (!d) return WKV7_ERR_INVALID_ARGUMENT;
     if (d->N != kN && !(wide && d->N == 128)) return WKV7_ERR_UNSUPPORTED;
@@ -239,8 +239,14 @@ wkv7_status wkv7_checkpoint_slots(int32_t B, int32_t T, int64_t *slots) {
 
 wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes) {
     if (!bytes) return WKV7_ERR_INVALID_ARGUMENT;
-    const wkv7_status st = check_desc(d);
+    const wkv7_status st = check_desc(d, true);
     if (st != WKV7_OK) return st;
+    if (d->N == 128) {
+        // the fp32 accumulators of dr, dk, db, dw, da ([B, T, H, 128] each)
+        if (d->num_seqs > 0 && d->ckpt_slots < 0) return WKV7_ERR_INVALID_ARGUMENT;
+        *bytes = (size_t)5 * d->B * d->T * d->H * 128 * sizeof(float);
+        return WKV7_OK;
+    }
     // per checkpoint slot and head: the fp32 64x64 state gradient leaving the
     // chunk, the fp32 16x64 drhs and the fp32 16x16 W of the chunk
     int64_t slots = 0;
@@ -321,8 +327,9 @@ static wkv7_status backward_impl(const wkv7_desc *d, const void *r, const void *
                                  const void *dy, const float *ds_out, void *dr, void *dw, void *dk,
                                  void *dv, void *da, void *db, float *ds0, void *workspace,
                                  size_t workspace_bytes, bool use_scratch, void *stream) {
-    wkv7_status st = check_desc(d);
+    wkv7_status st = check_desc(d, !use_scratch);
     if (st != WKV7_OK) return st;
+    const bool wide = d->N == 128;
     const void *streams[12] = {r, w, k, v, a, b, dr, dw, dk, dv, da, db};
     if ((st = check_streams(streams, 12)) != WKV7_OK) return st;
     if (dy && !aligned16(dy)) return WKV7_ERR_INVALID_ARGUMENT;
@@ -334,8 +341,9 @@ static wkv7_status backward_impl(const wkv7_desc *d, const void *r, const void *
     {
         // the second pass's grid: work items x heads (segment mode) or
         // ceil(T / 128) chunk groups x B x H (dense) workgroups
-        const int64_t items = d->num_seqs > 0 ? glist_cap(d->ckpt_slots, d->num_seqs)
-                                              : (int64_t)d->B * ((d->T + 127) / 128);
+        const int64_t items = wide ? (num_states(d) + 7) / 8 * 8 * 16
+                              : d->num_seqs > 0 ? glist_cap(d->ckpt_slots, d->num_seqs)
+                                                : (int64_t)d->B * ((d->T + 127) / 128);
         if (items * d->H > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
     }
     if (use_scratch) {
@@ -368,6 +376,21 @@ static wkv7_status backward_impl(const wkv7_desc *d, const void *r, const void *
     args.dr = dr; args.dw = dw; args.dk = dk; args.dv = dv; args.da = da; args.db = db;
     args.ds0 = ds0;
     args.ws = (float *)workspace;
+    if (wide) {
+        args.ws_dr = args.ws_w = nullptr;
+        args.glist = nullptr;
+        args.glist_cap = 0;
+        if (d->num_seqs > 0) {
+            // a [.., H, 128] stream is laid out as [.., 2H, 64]
+            wkv7::SegParams zs = args.seg;
+            zs.H = d->H * 2;
+            void *outs[6] = {dr, dw, dk, dv, da, db};
+            if (wkv7::launch_zero_uncovered(zs, d->grad_f32 ? WKV7_F32 : d->dtype, outs, 6, hs) != hipSuccess)
+                return WKV7_ERR_HIP;
+        }
+        if (wkv7::launch_backward128(args, (float *)workspace, hs) != hipSuccess) return WKV7_ERR_HIP;
+        return WKV7_OK;
+    }
     {
         const int64_t slots = d->num_seqs > 0 ? d->ckpt_slots : (int64_t)d->B * ((d->T + kChunk - 1) / kChunk);
         args.ws_dr = args.ws + slots * d->H * kN * kN;

@@ -240,8 +240,8 @@ def wkv7_forward(r, w, k, v, a, b, s0=None, *, segments: Segments | None = None,
     return y, s_out, ckpt
 
 
-def wkv7_workspace_bytes(B, T, H, dtype, segments: Segments | None = None) -> int:
-    d = _desc(B, T, H, dtype, segments)
+def wkv7_workspace_bytes(B, T, H, dtype, segments: Segments | None = None, n: int = N) -> int:
+    d = _desc(B, T, H, dtype, segments, n=n)
     n = ctypes.c_size_t(0)
     _check("wkv7_workspace_bytes", lib().wkv7_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
     return int(n.value)
@@ -256,18 +256,18 @@ def _backward_args(r, w, k, v, a, b, ckpt, dy, ds_out, segments, want_ds0, grads
     for name, t in zip("rwkvab", (r, w, k, v, a, b)):
         _req(t, name, dev, r.dtype, r.shape)
     S = segments.num_seqs if segments is not None else B
-    _req(ckpt, "ckpt", dev, torch.float32, (checkpoint_slots(B, T, segments), H, N, N))
+    _req(ckpt, "ckpt", dev, torch.float32, (checkpoint_slots(B, T, segments), H, n, n))
     if dy is not None:
         _req(dy, "dy", dev, r.dtype, r.shape)
     if ds_out is not None:
-        _req(ds_out, "ds_out", dev, torch.float32, (S, H, N, N))
+        _req(ds_out, "ds_out", dev, torch.float32, (S, H, n, n))
     names = ("dr", "dw", "dk", "dv", "da", "db")
     gdt = torch.float32 if grad_f32 else r.dtype
     if grads is None:
         grads = {nm: torch.empty(r.shape, device=dev, dtype=gdt) for nm in names}
     for nm in names:
         _req(grads[nm], nm, dev, gdt, r.shape)
-    ds0 = torch.empty((S, H, N, N), device=dev, dtype=torch.float32) if want_ds0 else None
+    ds0 = torch.empty((S, H, n, n), device=dev, dtype=torch.float32) if want_ds0 else None
     return grads, ds0
 
 
@@ -275,17 +275,18 @@ def wkv7_backward(r, w, k, v, a, b, ckpt, dy=None, ds_out=None, *,
                   segments: Segments | None = None, want_ds0: bool = True, workspace=None,
                   grads=None, decay: str = "mult", grad_f32: bool = False):
     """Returns dict dr, dw, dk, dv, da, db (dtype of r, or fp32 with grad_f32)
-    and ds0 (fp32 or None). With decay="log", dw is the gradient w.r.t. log(decay)."""
+    and ds0 (fp32 or None). With decay="log", dw is the gradient w.r.t. log(decay).
+    Head size n = 64 (chunked kernels) or 128 (token-order kernel)."""
     torch = _torch()
     B, T, H, n = r.shape
     grads, ds0 = _backward_args(r, w, k, v, a, b, ckpt, dy, ds_out, segments, want_ds0, grads, grad_f32)
-    need = wkv7_workspace_bytes(B, T, H, _dtype_code(r), segments)
+    need = wkv7_workspace_bytes(B, T, H, _dtype_code(r), segments, n=n)
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=r.device, dtype=torch.uint8)
     if workspace is not None:
         _req(workspace, "workspace", r.device)
     ws_bytes = 0 if workspace is None else _nbytes(workspace)
-    d = _desc(B, T, H, _dtype_code(r), segments, decay, grad_f32)
+    d = _desc(B, T, H, _dtype_code(r), segments, decay, grad_f32, n=n)
     names = ("dr", "dw", "dk", "dv", "da", "db")
     _check("wkv7_backward", lib().wkv7_backward(
         ctypes.byref(d), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(ckpt), _ptr(dy),
@@ -312,8 +313,8 @@ def wkv7_backward_noalloc(r, w, k, v, a, b, ckpt, dy=None, ds_out=None, *,
         ds0 = ds0_new
     else:
         S = segments.num_seqs if segments is not None else B
-        _req(ds0, "ds0", r.device, torch.float32, (S, H, N, N))
-    d = _desc(B, T, H, _dtype_code(r), segments, decay, grad_f32)
+        _req(ds0, "ds0", r.device, torch.float32, (S, H, n, n))
+    d = _desc(B, T, H, _dtype_code(r), segments, decay, grad_f32, n=n)
     names = ("dr", "dw", "dk", "dv", "da", "db")
     _check("wkv7_backward_noalloc", lib().wkv7_backward_noalloc(
         ctypes.byref(d), *[_ptr(t) for t in (r, w, k, v, a, b)], _ptr(ckpt), _ptr(dy),

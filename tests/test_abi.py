@@ -85,7 +85,10 @@ def test_backward_rejects_bad_arguments():
     call = lambda d, ckpt=P[6], grads=grads, ws=None, wsb=0: L.wkv7_backward(
         ctypes.byref(d), *P[:6], ckpt, None, None, *grads, None, ws, wsb, None)
     assert call(desc(N=32)) == UNSUPPORTED
-    assert call(desc(N=128)) == UNSUPPORTED        # the backward is built for head size 64
+    assert call(desc(N=96)) == UNSUPPORTED
+    assert call(desc(N=128)) == WS                 # head size 128 needs its accumulator workspace
+    need = W.wkv7_workspace_bytes(2, 32, 4, 1, n=128)
+    assert call(desc(N=128), ws=ctypes.c_void_p(1 << 44), wsb=need - 1) == WS
     assert call(d, ckpt=None) == INVALID
     for q in range(6):
         g = list(grads); g[q] = None
@@ -200,7 +203,9 @@ def test_workspace_query():
     assert W.lib().wkv7_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
     assert n.value == 9 * 2 * per * 4 + 256
     assert W.lib().wkv7_workspace_bytes(ctypes.byref(desc(N=48)), ctypes.byref(n)) == UNSUPPORTED
-    assert W.lib().wkv7_workspace_bytes(ctypes.byref(desc(N=128)), ctypes.byref(n)) == UNSUPPORTED
+    # head size 128: fp32 accumulators of dr, dk, db, dw, da, [B, T, H, 128] each
+    assert W.lib().wkv7_workspace_bytes(ctypes.byref(desc(N=128)), ctypes.byref(n)) == 0
+    assert n.value == 5 * 2 * 32 * 4 * 128 * 4
 
 
 def test_segments_check_matches_layout_helpers():
