@@ -543,7 +543,7 @@ def leg_n128(args, W, synth, out):
     th = B * T * H
     out["train_n128"] = {
         "workload": "WKV-7 at head size 128, bf16 B=16 T=1024 H=32: forward with 16-token checkpoints, "
-                    "then the backward (token order, fp32 accumulators)",
+                    "then the backward (token order, one workgroup per sequence and head)",
         "forward_ckpt_ms": fc_ms, "backward_ms": b_ms, "tokens_per_s": B * T / ((fc_ms + b_ms) * 1e-3),
         "backward_fp32_frac": 26 * 128 * 128 * th / (b_ms * 1e-3) / PEAK_FP32}
 
@@ -639,9 +639,7 @@ KERNEL_LABELS = {
     "decode_kernel": "WKV-7 decode step",
     "decode128_kernel": "WKV-7 decode step, head size 128",
     "fwd128_kernel": "WKV-7 forward, head size 128 (token order)",
-    "bwd128_kernel": "WKV-7 backward, head size 128 (token order, 8-row blocks)",
-    "bwd128_zero_kernel": "WKV-7 backward, head size 128: accumulator clear",
-    "bwd128_finish_kernel": "WKV-7 backward, head size 128: accumulators to gradients",
+    "bwd128_kernel": "WKV-7 backward, head size 128 (token order, one workgroup per unit)",
     "gdn_decode_kernel": "gated DeltaNet decode step",
     "gdn_norm_kernel": "gated DeltaNet prefill: q^, k^ pre-pass",
     "gdn_fwd_kernel": "gated DeltaNet prefill: recurrence",

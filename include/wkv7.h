@@ -5,7 +5,7 @@
  * section "The Metal WKV-7 kernel" and the model card's "Transformers
  * quickstart" section describe as the one custom kernel of the model): per
  * independent unit -- one (sequence, head) pair -- with head size N = 64 (the
- * forward and the decode steps also take N = 128) and an fp32 state S in
+ * forward, the backward and the decode steps also take N = 128) and an fp32 state S in
  * R^{NxN} indexed [value i, key j], every token t does
  *
  *     S_t = S_{t-1} diag(w_t) + (S_{t-1} a_t) b_t^T + v_t k_t^T,   y_t = S_t r_t
@@ -103,7 +103,7 @@ typedef struct {
     int32_t B;                  /* rows */
     int32_t T;                  /* tokens per row, >= 1 */
     int32_t H;                  /* heads, 1 <= H <= 65536 */
-    int32_t N;                  /* head size: 64, or 128 for wkv7_forward only */
+    int32_t N;                  /* head size: 64, or 128 (wkv7_forward, wkv7_backward) */
     int32_t dtype;              /* wkv7_dtype of r,w,k,v,a,b,y,dy and dr..db */
     int32_t num_seqs;           /* 0 = dense mode */
     const int32_t *seq_start;   /* device [num_seqs]: flat start token b*T + t */
@@ -156,10 +156,9 @@ wkv7_status wkv7_forward(const wkv7_desc *d,
  * reconstructed by dividing by the decay. N = 64: two kernels run back to
  * back on `stream`, a reverse sweep that carries only the state gradient,
  * then the per-chunk gradients, all chunks in parallel. N = 128: token by
- * token, blocks of 8 value rows per workgroup through the whole sequence in
- * reverse; their shares of dr, dk, db, dw, da are added in fp32 in the
- * workspace with atomics (so the summation order, and the last bits of
- * those gradients, can differ between calls), then converted.
+ * token, one workgroup per (sequence, head) through the whole sequence in
+ * reverse, every gradient summed within the workgroup (no workspace; the
+ * results do not depend on scheduling).
  */
 wkv7_status wkv7_backward(const wkv7_desc *d,
                           const void *r, const void *w, const void *k,
@@ -301,7 +300,7 @@ wkv7_status wkv7_checkpoint_slots(int32_t B, int32_t T, int64_t *slots);
  * otherwise) x H x (64 x 64 + 16 x 64 + 16 x 16) x 4; in segment mode plus
  * 4 x (1 + 2 x (ceil(slots / 8) + num_seqs)) bytes rounded up to 256 (the
  * list of (sequence, 8-chunk group) work items of the second kernel).
- * N = 128: 5 x B x T x H x 128 x 4 (fp32 accumulators of five gradients). */
+ * N = 128: 0 (the backward needs no workspace). */
 wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes);
 
 /*

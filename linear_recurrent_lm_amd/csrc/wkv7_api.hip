@@ -242,9 +242,9 @@ wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes) {
     const wkv7_status st = check_desc(d, true);
     if (st != WKV7_OK) return st;
     if (d->N == 128) {
-        // the fp32 accumulators of dr, dk, db, dw, da ([B, T, H, 128] each)
+        // one workgroup per (sequence, head) sums every gradient itself
         if (d->num_seqs > 0 && d->ckpt_slots < 0) return WKV7_ERR_INVALID_ARGUMENT;
-        *bytes = (size_t)5 * d->B * d->T * d->H * 128 * sizeof(float);
+        *bytes = 0;
         return WKV7_OK;
     }
     // per checkpoint slot and head: the fp32 64x64 state gradient leaving the
@@ -340,8 +340,9 @@ static wkv7_status backward_impl(const wkv7_desc *d, const void *r, const void *
     if ((st = wkv7_workspace_bytes(d, &need)) != WKV7_OK) return st;
     {
         // the second pass's grid: work items x heads (segment mode) or
-        // ceil(T / 128) chunk groups x B x H (dense) workgroups
-        const int64_t items = wide ? (num_states(d) + 7) / 8 * 8 * 16
+        // ceil(T / 128) chunk groups x B x H (dense) workgroups; at head
+        // size 128, one workgroup per (sequence, head)
+        const int64_t items = wide ? num_states(d)
                               : d->num_seqs > 0 ? glist_cap(d->ckpt_slots, d->num_seqs)
                                                 : (int64_t)d->B * ((d->T + 127) / 128);
         if (items * d->H > INT32_MAX) return WKV7_ERR_INVALID_ARGUMENT;
@@ -388,7 +389,7 @@ static wkv7_status backward_impl(const wkv7_desc *d, const void *r, const void *
             if (wkv7::launch_zero_uncovered(zs, d->grad_f32 ? WKV7_F32 : d->dtype, outs, 6, hs) != hipSuccess)
                 return WKV7_ERR_HIP;
         }
-        if (wkv7::launch_backward128(args, (float *)workspace, hs) != hipSuccess) return WKV7_ERR_HIP;
+        if (wkv7::launch_backward128(args, hs) != hipSuccess) return WKV7_ERR_HIP;
         return WKV7_OK;
     }
     {

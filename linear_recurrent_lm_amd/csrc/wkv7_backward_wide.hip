@@ -7,44 +7,61 @@
 //     dw_t = colsum(dS o S_{t-1});       da_t = S_{t-1}^T dsa
 //     dS <- dS diag(w_t) + dsa a_t^T    (the gradient of the state before t)
 // where sa_t = S_{t-1} a_t. S_{t-1} is never rebuilt from S_t (that divides by
-// w): each chunk's states are recomputed forward from its checkpoint.
+// w): the states are recomputed forward from the chunk's checkpoint.
 //
-// The value rows of the state evolve independently, in the recurrence and in
-// its adjoint: dS's row i needs only row i of S, v_i and dy_i. A workgroup
-// therefore owns 8 value rows of one (sequence, head) through the whole
-// sequence, in reverse: 16 workgroups per unit. Thread t holds keys 4 (t % 32)
-// .. + 3 of row t / 32 (a wave holds two rows), with dS and, for one half of
-// a chunk at a time, the 8 recomputed states of its 4 elements and sa in
-// registers. Row sums (S a,
-// dS k, dS b) reduce over the 32 lanes of a row. The key-indexed gradients
-// (dr, dk, db, dw, da) are sums over all 128 rows: each workgroup adds its
-// 8 rows' share to fp32 accumulators in the workspace with hardware atomics,
-// and a last kernel writes them out in the gradients' dtype; dv and ds0 are
-// per row and written directly.
+// One 1024-thread workgroup owns a whole (sequence, head). Thread t holds the
+// 4 x 4 block of the state and of dS at value rows 4 (t / 32) .. + 3 and keys
+// 4 (t % 32) .. + 3, so a row spreads over the 32 lanes of a half-wave and a
+// key over the 32 half-waves.
+// - Row sums (S a, dS k, dS b) add the thread's 4 keys, then reduce over the
+//   half-wave with register-to-register lane exchanges (no LDS).
+// - Key sums (the five key-indexed gradients dr, dk, db, dw, da over all 128
+//   rows) add the thread's 4 rows, swap halves of their 20 values with the
+//   other half-wave (each half keeps 10 and adds the partner's), and the 16
+//   waves' partial sums meet in LDS, where 640 threads add them and write the
+//   gradients. The partial-sum area is double-buffered by token, so one
+//   barrier per token separates its writes from the sums.
+// Nothing is accumulated across workgroups: every gradient element is written
+// once, in its own dtype, and the result does not depend on scheduling.
 //
-// Per chunk the r, w, k, a, b rows of its 16 tokens and the block's v and dy
-// are staged in LDS as fp32 (w exponentiated for log-decay input), from
-// registers loaded while the previous chunk ran.
+// States: a chunk is walked back in segments of kSeg tokens. Each segment
+// starts from the chunk's checkpoint (re-read; it stays in L2), steps forward
+// to the segment's first token without storing, then keeps the states before
+// each of its tokens in registers for the reverse pass (2.5 forward steps per
+// token for kSeg = 4).
 #include "wkv7_kernels.h"
 #include "wkv7_mfma.h"
 
 namespace wkv7 {
 namespace {
 
-constexpr int kWN = 128;            // head size
-constexpr int kRowsPerBlock = 8;
-constexpr int kBlocksPerUnit = kWN / kRowsPerBlock;
-constexpr int kWThreads = 256;
+constexpr int kWN = 128;              // head size
+constexpr int kWThreads = 1024;
+constexpr int kSeg = 4;               // tokens per recompute segment
 enum { SW = 0, SA, SB, SK, SR, NSTAGE };     // staged key-indexed rows
-enum { GR = 0, GK, GB, GW, GA, NACC };       // accumulated key-indexed gradients
+enum { GR = 0, GK, GB, GW, GA, NGRAD };      // key-indexed gradients
 
-// LDS (floats): staged rows [NSTAGE][16][128], v and dy of the block's rows
-// [2][16][8], partial column sums [8 rows][NACC][128]: 62.5 KB, two
-// workgroups per CU
+// LDS (floats): staged rows [NSTAGE][16][128] (w exponentiated for log
+// input), v and dy by value row [2][16][128], S a of each token [16][128],
+// and the key sums' partial-sum area [2 buffers][16 waves][20 x 32].
 constexpr int L_ST = 0;
 constexpr int L_VD = L_ST + NSTAGE * kChunk * kWN;
-constexpr int L_PART = L_VD + 2 * kChunk * kRowsPerBlock;
-constexpr int L_TOTAL = L_PART + kRowsPerBlock * NACC * kWN;
+constexpr int L_SAV = L_VD + 2 * kChunk * kWN;
+constexpr int L_PART = L_SAV + kChunk * kWN;
+constexpr int kPartWave = 20 * 32;
+constexpr int L_TOTAL = L_PART + 2 * 16 * kPartWave;
+static_assert(L_TOTAL * 4 <= 160 * 1024, "LDS budget");
+
+// Partial-sum slot of value v (0..19) of key group kq: the 32 key groups of a
+// value are consecutive, XOR-swizzled so that the summing threads (32
+// consecutive keys: 8 key groups x 4 values) hit 32 distinct banks.
+__device__ __forceinline__ int part_slot(int v, int kq) { return v * 32 + (kq ^ (8 * (v & 3))); }
+// Which value v holds gradient g of key 4 kq + e after the half-wave swap:
+// the lower half keeps dr, dk and db of keys e = 0, 1; the upper half dw, da
+// and db of keys e = 2, 3.
+__device__ __forceinline__ int grad_value(int g, int e) {
+    return g == GR ? e : g == GK ? 4 + e : g == GB ? (e < 2 ? 8 + e : 16 + e) : g == GW ? 10 + e : 14 + e;
+}
 
 // 8 consecutive elements in flight (one 16-byte load, two for fp32)
 template <typename TI> struct Raw8;
@@ -78,208 +95,324 @@ __device__ __forceinline__ void un8(const Raw8<float> &r, float *x) {
     x[4] = r.q[1].x; x[5] = r.q[1].y; x[6] = r.q[1].z; x[7] = r.q[1].w;
 }
 
-// sum over the 32 lanes of a row (lanes 0-31 or 32-63 of the wave)
-__device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1) x += __shfl_xor(x, m, 32);
-    return x;
+// Lane exchanges without the LDS crossbar: DPP moves within rows of 16 lanes
+// (fused into the adds) and the gfx950 row swaps. swap16(A, B) exchanges the
+// odd 16-lane rows of A with the even rows of B; swap32(A, B) the upper 32
+// lanes of A with the lower 32 of B.
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+    return __builtin_amdgcn_update_dpp(0.f, x, CTRL, 0xf, 0xf, false);
+}
+constexpr int kRowRor8 = 0x128, kHalfMirror = 0x141, kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;
+__device__ __forceinline__ void swap16(float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+// sum over the 16 lanes of a row, in every lane: pairs 8 apart, then the
+// mirror within 8, then the quads' two exchanges
+__device__ __forceinline__ float sum16(float k) {
+    k += dpp<kRowRor8>(k);
+    k += dpp<kHalfMirror>(k);
+    k += dpp<kQuadXor1>(k);
+    k += dpp<kQuadXor2>(k);
+    return k;
+}
+
+// x[r]: this thread's partial sums (its 4 keys) of rows 4 (t / 32) + r; on
+// return, the sums over all 128 keys, in every lane of the half-wave. The
+// half-wave's even 16-lane row keeps rows 0, 1 and its odd row rows 2, 3,
+// each adding the other row's share; each row of lanes sums its two, then two
+// swaps hand every lane all four.
+__device__ __forceinline__ void row_sums(float (&x)[4], int lane) {
+    float a0 = x[0], a2 = x[2], a1 = x[1], a3 = x[3];
+    swap16(a0, a2);
+    swap16(a1, a3);
+    float k0 = sum16(a0 + a2), k1 = sum16(a1 + a3);   // even row: rows 0, 1; odd row: rows 2, 3
+    float g1a = k0, g1b = k1, g2a = k1, g2b = k0;
+    swap16(g1a, g1b);                                  // even: rows 0, 2; odd: rows 1, 3
+    swap16(g2a, g2b);                                  // even: rows 1, 3; odd: rows 0, 2
+    const bool odd = (lane & 16) != 0;
+    x[0] = odd ? g2a : g1a;
+    x[1] = odd ? g1a : g2a;
+    x[2] = odd ? g2b : g1b;
+    x[3] = odd ? g1b : g2b;
 }
 
 template <typename TI, typename TO>
-__global__ __launch_bounds__(kWThreads, 2) void bwd128_kernel(BwdArgs p, float *acc, int32_t units) {
-    __shared__ __align__(16) float sm[L_TOTAL];
-    const int g8 = blockIdx.x / (8 * kBlocksPerUnit), wq = blockIdx.x % (8 * kBlocksPerUnit);
-    const int unit = g8 * 8 + (wq & 7);             // a unit's row blocks share an XCD
-    const int rb = wq >> 3;
+__global__ __launch_bounds__(kWThreads, 1) void bwd128_kernel(BwdArgs p, int32_t units) {
+    extern __shared__ __align__(16) float sm[];
+    const int unit = blockIdx.x;
     if (unit >= units) return;
     const int H = p.seg.H;
     const int h = unit % H, sq = unit / H;
     const Unit u = resolve_unit(p.seg, sq);
-    const int tid = threadIdx.x;
-    const int r8 = tid >> 5, kq = tid & 31;
-    const int row = rb * kRowsPerBlock + r8;        // value row of this thread
+    // The thread indices are re-derived from an opaque copy of the thread id
+    // in each phase, so that the many addresses built from them are formed
+    // where they are used instead of being hoisted out of the loops and kept
+    // live (or spilled) throughout.
+    int tid, wave, lane, hf, kq, row0, key0;
+    auto relane = [&]() {
+        int x = (int)threadIdx.x;
+        asm volatile("" : "+v"(x));
+        tid = x; wave = x >> 6; lane = x & 63; hf = lane >> 5; kq = lane & 31;
+        row0 = 4 * (2 * wave + hf); key0 = 4 * kq;
+    };
+    relane();
     const int64_t ts = (int64_t)H * kWN;            // token pitch of a stream
     const int64_t base = (u.start * H + h) * kWN;
     const int64_t sbase = ((int64_t)sq * H + h) * (int64_t)(kWN * kWN);
-    const int64_t toks = (int64_t)p.seg.B * p.seg.T;
     const int nch = (u.len + kChunk - 1) / kChunk;
 
-    // dS: row `row`, keys 4 kq .. 4 kq + 3
-    float4 dS = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (p.ds_out) dS = *(const float4 *)(p.ds_out + sbase + (int64_t)row * kWN + 4 * kq);
+    // dS: rows row0 .. + 3, keys key0 .. + 3 (element 4 r + e)
+    float dS[16];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p.ds_out) x = *(const float4 *)(p.ds_out + sbase + (int64_t)(row0 + r) * kWN + key0);
+        dS[4 * r] = x.x; dS[4 * r + 1] = x.y; dS[4 * r + 2] = x.z; dS[4 * r + 3] = x.w;
+    }
 
-    // staging: thread t loads 8 keys (t % 16) * 8 of token t / 16 of each row
-    // stream, and (t < 128) v or dy of row t % 8 of token (t / 8) % 16
-    const int se = tid >> 4, sc = (tid & 15) * 8;
-    const TI *srcs[NSTAGE] = {(const TI *)p.w, (const TI *)p.a, (const TI *)p.b,
-                              (const TI *)p.k, (const TI *)p.r};
-    Raw8<TI> raw[NSTAGE];
-    TI rvd = TI(0);
-    const int ve = (tid >> 3) & 15, vr = tid & 7;
-    const bool vd_dy = tid >= 128 && tid < 256;
-    auto issue = [&](int cc) {
-        const int Lc = min(kChunk, u.len - cc * kChunk);
-        const int64_t t0 = (int64_t)cc * kChunk;
-        const int64_t o = base + (t0 + min(se, Lc - 1)) * ts + sc;
+    auto keyrow = [&](int s, int e) { return *(const float4 *)(sm + L_ST + (s * kChunk + e) * kWN + key0); };
+    auto valrow = [&](int s, int e) { return *(const float4 *)(sm + L_VD + (s * kChunk + e) * kWN + row0); };
+    // one forward step of this thread's 16 elements; sa = S a of its rows
+    auto step = [&](float (&S)[16], int e, float (&sa)[4]) {
+        const float4 w4 = keyrow(SW, e), a4 = keyrow(SA, e), b4 = keyrow(SB, e), k4 = keyrow(SK, e);
+        const float4 v4 = valrow(0, e);
+        const float w[4] = {w4.x, w4.y, w4.z, w4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
+        const float k[4] = {k4.x, k4.y, k4.z, k4.w}, v[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
-        for (int s = 0; s < NSTAGE; ++s) ld8(srcs[s] + o, raw[s]);
-        const int64_t ov = base + (t0 + min(ve, Lc - 1)) * ts + rb * kRowsPerBlock + vr;
-        if (!vd_dy) rvd = ((const TI *)p.v)[ov];
-        else rvd = p.dy ? ((const TI *)p.dy)[ov] : TI(0);
+        for (int r = 0; r < 4; ++r)
+            sa[r] = fmaf(S[4 * r], a4.x, fmaf(S[4 * r + 1], a4.y, fmaf(S[4 * r + 2], a4.z, S[4 * r + 3] * a4.w)));
+        row_sums(sa, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2)
+                S[4 * r + e2] = fmaf(S[4 * r + e2], w[e2], fmaf(sa[r], b[e2], v[r] * k[e2]));
     };
-    auto stage = [&]() {
+
+    int buf = 0;
+    // the reverse step of token e of the chunk starting at token t0, with P
+    // the state before it
+    auto token = [&](const float (&P)[16], int e, int64_t t0) {
+        relane();
+        // operands are read where they are first used, to keep few live
+        auto f4 = [](float4 x, float (&o)[4]) { o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w; };
+        float dy[4], rr[4];
+        f4(valrow(1, e), dy);
+        f4(keyrow(SR, e), rr);
+        float *part = sm + L_PART + (buf * 16 + wave) * kPartWave;
+        // key sums of this thread's rows for two gradients: the lower half
+        // keeps the first, the upper the second, each adding the partner's
+        auto pair_out = [&](const float (&g1)[4], const float (&g2)[4], int v1, int v2) {
 #pragma unroll
-        for (int s = 0; s < NSTAGE; ++s) {
-            float x[8];
-            un8(raw[s], x);
-            if (s == SW) decay_of<8>(x, p.logw);
-            float *d = sm + L_ST + (s * kChunk + se) * kWN + sc;
-            *(float4 *)d = make_float4(x[0], x[1], x[2], x[3]);
-            *(float4 *)(d + 4) = make_float4(x[4], x[5], x[6], x[7]);
+            for (int e2 = 0; e2 < 4; ++e2) {
+                float lo = g1[e2], hi = g2[e2];
+                swap32(lo, hi);                         // lower half: both g1; upper: both g2
+                part[part_slot((hf ? v2 : v1) + e2, kq)] = lo + hi;
+            }
+        };
+        // dS becomes the gradient of S_t: add dy_t r_t^T
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) dS[4 * r + e2] = fmaf(dy[r], rr[e2], dS[4 * r + e2]);
+        float k[4], b[4];
+        f4(keyrow(SK, e), k);
+        f4(keyrow(SB, e), b);
+        float dv[4], dsa[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            dv[r] = fmaf(dS[4 * r], k[0], fmaf(dS[4 * r + 1], k[1], fmaf(dS[4 * r + 2], k[2], dS[4 * r + 3] * k[3])));
+            dsa[r] = fmaf(dS[4 * r], b[0], fmaf(dS[4 * r + 1], b[1], fmaf(dS[4 * r + 2], b[2], dS[4 * r + 3] * b[3])));
         }
-        sm[L_VD + (vd_dy ? kChunk * kRowsPerBlock : 0) + ve * kRowsPerBlock + vr] = IO<TI>::ld(&rvd, 0);
+        row_sums(dv, lane);
+        row_sums(dsa, lane);
+        float w[4], v[4], sa[4];
+        f4(keyrow(SW, e), w);
+        f4(valrow(0, e), v);
+        f4(*(const float4 *)(sm + L_SAV + e * kWN + row0), sa);
+        {   // dr = S_t^T dy (S_t rebuilt from P), dw = colsum(dS o P)
+            float gr[4], gw[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                float x = 0.f, y = 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float st = fmaf(P[4 * r + e2], w[e2], fmaf(sa[r], b[e2], v[r] * k[e2]));
+                    x = fmaf(st, dy[r], x);
+                    y = fmaf(dS[4 * r + e2], P[4 * r + e2], y);
+                }
+                gr[e2] = x;
+                gw[e2] = y;
+            }
+            pair_out(gr, gw, grad_value(GR, 0), grad_value(GW, 0));
+        }
+        {   // dk = dS^T v, da = P^T dsa
+            float gk[4], ga[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                float x = 0.f, y = 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    x = fmaf(dS[4 * r + e2], v[r], x);
+                    y = fmaf(P[4 * r + e2], dsa[r], y);
+                }
+                gk[e2] = x;
+                ga[e2] = y;
+            }
+            pair_out(gk, ga, grad_value(GK, 0), grad_value(GA, 0));
+        }
+        {   // db = dS^T sa
+            float gb[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                float x = 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x = fmaf(dS[4 * r + e2], sa[r], x);
+                gb[e2] = x;
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                float lo = gb[i], hi = gb[2 + i];
+                swap32(lo, hi);                         // lower half: key i; upper: key 2 + i
+                part[part_slot(hf ? grad_value(GB, 2 + i) : grad_value(GB, i), kq)] = lo + hi;
+            }
+        }
+        // dv of the thread's rows: lanes 0-3 of each half write one row each
+        if (kq < 4) {
+            const float x = kq == 0 ? dv[0] : kq == 1 ? dv[1] : kq == 2 ? dv[2] : dv[3];
+            IO<TO>::st((TO *)p.dv, base + (t0 + e) * ts + row0 + kq, x);
+        }
+        // the gradient of the state before token t
+        float a[4];
+        f4(keyrow(SA, e), a);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) dS[4 * r + e2] = fmaf(dS[4 * r + e2], w[e2], dsa[r] * a[e2]);
+        __syncthreads();
+        // the 16 waves' partial sums: thread f < 640 owns gradient f / 128 of key f % 128
+        if (tid < NGRAD * kWN) {
+            const int g = tid >> 7, j = tid & 127;
+            const float *q = sm + L_PART + buf * 16 * kPartWave + part_slot(grad_value(g, j & 3), j >> 2);
+            float x = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < 16; ++wv) x += q[wv * kPartWave];
+            if (g == GW && p.logw) x *= sm[L_ST + (SW * kChunk + e) * kWN + j];   // d/d log(w) = w d/dw
+            void *gp = g == GR ? p.dr : g == GK ? p.dk : g == GB ? p.db : g == GW ? p.dw : p.da;
+            IO<TO>::st((TO *)gp, base + (t0 + e) * ts + j, x);
+        }
+        buf ^= 1;
     };
-    auto rowv = [&](int s, int e) { return *(const float4 *)(sm + L_ST + (s * kChunk + e) * kWN + 4 * kq); };
 
-    if (nch > 0) issue(nch - 1);
 #pragma unroll 1
     for (int c = nch - 1; c >= 0; --c) {
         const int Lc = min(kChunk, u.len - c * kChunk);
         const int64_t t0 = (int64_t)c * kChunk;
         __syncthreads();                            // the previous chunk is done with the staged rows
-        stage();
-        if (c > 0) issue(c - 1);
-        const float4 S0 = *(const float4 *)(p.ckpt + ((u.ckpt + c) * H + h) * (int64_t)(kWN * kWN) +
-                                            (int64_t)row * kWN + 4 * kq);
-        __syncthreads();
-        // one forward step of this thread's 4 elements; returns sa = S a
-        auto step = [&](float4 &S, int e) {
-            const float4 w4 = rowv(SW, e), a4 = rowv(SA, e), b4 = rowv(SB, e), k4 = rowv(SK, e);
-            const float vi = sm[L_VD + e * kRowsPerBlock + r8];
-            const float s_ = row_sum(S.x * a4.x + S.y * a4.y + S.z * a4.z + S.w * a4.w);
-            S.x = fmaf(S.x, w4.x, fmaf(s_, b4.x, vi * k4.x));
-            S.y = fmaf(S.y, w4.y, fmaf(s_, b4.y, vi * k4.y));
-            S.z = fmaf(S.z, w4.z, fmaf(s_, b4.z, vi * k4.z));
-            S.w = fmaf(S.w, w4.w, fmaf(s_, b4.w, vi * k4.w));
-            return s_;
-        };
-        // the chunk in two halves of 8 tokens, the later one first: the
-        // states before each token of a half are recomputed from the
-        // checkpoint (the later half's start from the first half's end)
-#pragma unroll 1
-        for (int half = 1; half >= 0; --half) {
-            const int e0 = 8 * half;
-            if (e0 >= Lc) continue;
-            float4 S = S0;
-            if (half == 1) {
+        relane();
+        // stage: items 0..1279 are 8 keys of the 5 key-indexed rows, items
+        // 1280..1791 8 rows of v or dy; token rows clamped into the sequence
 #pragma unroll
-                for (int e = 0; e < 8; ++e) step(S, e);
-            }
-            float4 Sp[8];
-            float sa[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                Sp[e] = S;
-                sa[e] = 0.f;
-                if (e0 + e < Lc) sa[e] = step(S, e0 + e);
-            }
-#pragma unroll
-            for (int e = 7; e >= 0; --e) {
-                const int te = e0 + e;
-                if (te < Lc) {
-                    const float4 w4 = rowv(SW, te), a4 = rowv(SA, te), b4 = rowv(SB, te);
-                    const float4 k4 = rowv(SK, te), r4 = rowv(SR, te);
-                    const float vi = sm[L_VD + te * kRowsPerBlock + r8];
-                    const float dyi = sm[L_VD + (kChunk + te) * kRowsPerBlock + r8];
-                    const float4 P = Sp[e];
-                    const float s_ = sa[e];
-                    float4 St;                                  // S_t
-                    St.x = fmaf(P.x, w4.x, fmaf(s_, b4.x, vi * k4.x));
-                    St.y = fmaf(P.y, w4.y, fmaf(s_, b4.y, vi * k4.y));
-                    St.z = fmaf(P.z, w4.z, fmaf(s_, b4.z, vi * k4.z));
-                    St.w = fmaf(P.w, w4.w, fmaf(s_, b4.w, vi * k4.w));
-                    dS.x = fmaf(dyi, r4.x, dS.x);
-                    dS.y = fmaf(dyi, r4.y, dS.y);
-                    dS.z = fmaf(dyi, r4.z, dS.z);
-                    dS.w = fmaf(dyi, r4.w, dS.w);
-                    const float dvi = row_sum(dS.x * k4.x + dS.y * k4.y + dS.z * k4.z + dS.w * k4.w);
-                    const float dsa = row_sum(dS.x * b4.x + dS.y * b4.y + dS.z * b4.z + dS.w * b4.w);
-                    if (kq == 0) IO<TO>::st((TO *)p.dv, base + (t0 + te) * ts + row, dvi);
-                    // this row's share of the key-indexed gradients
-                    float *pt = sm + L_PART + r8 * NACC * kWN + 4 * kq;
-                    *(float4 *)(pt + GR * kWN) = make_float4(St.x * dyi, St.y * dyi, St.z * dyi, St.w * dyi);
-                    *(float4 *)(pt + GK * kWN) = make_float4(dS.x * vi, dS.y * vi, dS.z * vi, dS.w * vi);
-                    *(float4 *)(pt + GB * kWN) = make_float4(dS.x * s_, dS.y * s_, dS.z * s_, dS.w * s_);
-                    *(float4 *)(pt + GW * kWN) = make_float4(dS.x * P.x, dS.y * P.y, dS.z * P.z, dS.w * P.w);
-                    *(float4 *)(pt + GA * kWN) = make_float4(P.x * dsa, P.y * dsa, P.z * dsa, P.w * dsa);
-                    dS.x = fmaf(dS.x, w4.x, dsa * a4.x);
-                    dS.y = fmaf(dS.y, w4.y, dsa * a4.y);
-                    dS.z = fmaf(dS.z, w4.z, dsa * a4.z);
-                    dS.w = fmaf(dS.w, w4.w, dsa * a4.w);
-                    __syncthreads();
-                    // the block's 8 rows summed, then added across the unit's blocks
-                    if (tid < kWN) {
-                        const float *q = sm + L_PART + tid;
-                        const int64_t o = ((t0 + te + u.start) * H + h) * kWN + tid;
-#pragma unroll
-                        for (int g = 0; g < NACC; ++g) {
-                            float x = 0.f;
-#pragma unroll
-                            for (int r = 0; r < kRowsPerBlock; ++r) x += q[(r * NACC + g) * kWN];
-                            if (g == GW && p.logw) x *= sm[L_ST + (SW * kChunk + te) * kWN + tid];
-                            unsafeAtomicAdd(acc + (int64_t)g * toks * ts + o, x);
-                        }
-                    }
-                    __syncthreads();                    // the partials are free for the next token
+        for (int it = 0; it < 2; ++it) {
+            const int i = tid + it * kWThreads;
+            if (i < NSTAGE * 256) {
+                const int s = i >> 8, e = (i >> 4) & 15, g = i & 15;
+                const TI *src = (const TI *)(s == SW ? p.w : s == SA ? p.a : s == SB ? p.b : s == SK ? p.k : p.r);
+                Raw8<TI> raw;
+                ld8(src + base + (t0 + min(e, Lc - 1)) * ts + 8 * g, raw);
+                float x[8];
+                un8(raw, x);
+                if (s == SW) decay_of<8>(x, p.logw);
+                float *d = sm + L_ST + (s * kChunk + e) * kWN + 8 * g;
+                *(float4 *)d = make_float4(x[0], x[1], x[2], x[3]);
+                *(float4 *)(d + 4) = make_float4(x[4], x[5], x[6], x[7]);
+            } else if (i < NSTAGE * 256 + 512) {
+                const int i2 = i - NSTAGE * 256;
+                const int s = i2 >> 8, e = (i2 >> 4) & 15, g = i2 & 15;
+                float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                const TI *src = (const TI *)(s == 0 ? p.v : p.dy);
+                if (src) {
+                    Raw8<TI> raw;
+                    ld8(src + base + (t0 + min(e, Lc - 1)) * ts + 8 * g, raw);
+                    un8(raw, x);
                 }
+                float *d = sm + L_VD + (s * kChunk + e) * kWN + 8 * g;
+                *(float4 *)d = make_float4(x[0], x[1], x[2], x[3]);
+                *(float4 *)(d + 4) = make_float4(x[4], x[5], x[6], x[7]);
+            }
+        }
+        __syncthreads();
+        const float *ck = p.ckpt + ((u.ckpt + c) * H + h) * (int64_t)(kWN * kWN);
+#pragma unroll 1
+        for (int q = (Lc + kSeg - 1) / kSeg - 1; q >= 0; --q) {
+            relane();
+            float S[16];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float4 x = *(const float4 *)(ck + (int64_t)(row0 + r) * kWN + key0);
+                S[4 * r] = x.x; S[4 * r + 1] = x.y; S[4 * r + 2] = x.z; S[4 * r + 3] = x.w;
+            }
+            float sa[4];
+#pragma unroll 1
+            for (int e = 0; e < kSeg * q; ++e) step(S, e, sa);
+            // the states before each token of the segment, and their S a
+            float Sp[kSeg][16];
+#pragma unroll
+            for (int e = 0; e < kSeg; ++e) {
+                const int te = kSeg * q + e;
+                if (te < Lc) {
+#pragma unroll
+                    for (int x = 0; x < 16; ++x) Sp[e][x] = S[x];
+                    step(S, te, sa);
+                    *(float4 *)(sm + L_SAV + te * kWN + row0) = make_float4(sa[0], sa[1], sa[2], sa[3]);
+                }
+            }
+#pragma unroll
+            for (int e = kSeg - 1; e >= 0; --e) {
+                const int te = kSeg * q + e;
+                if (te < Lc) token(Sp[e], te, t0);
             }
         }
     }
-    if (p.ds0) *(float4 *)(p.ds0 + sbase + (int64_t)row * kWN + 4 * kq) = dS;
-}
-
-__global__ void bwd128_zero_kernel(float4 *p, int64_t n4) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
-// accumulators -> dr, dk, db, dw, da in the gradients' dtype
-template <typename TO>
-__global__ void bwd128_finish_kernel(BwdArgs p, const float *acc, int64_t n) {
-    void *outs[NACC] = {p.dr, p.dk, p.db, p.dw, p.da};
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    if (p.ds0) {
 #pragma unroll
-        for (int g = 0; g < NACC; ++g) IO<TO>::st((TO *)outs[g], i, acc[(int64_t)g * n + i]);
+        for (int r = 0; r < 4; ++r)
+            *(float4 *)(p.ds0 + sbase + (int64_t)(row0 + r) * kWN + key0) =
+                make_float4(dS[4 * r], dS[4 * r + 1], dS[4 * r + 2], dS[4 * r + 3]);
     }
 }
 
 template <typename TI, typename TO>
-hipError_t launch_t(const BwdArgs &a, float *acc, hipStream_t stream) {
+hipError_t launch_t(const BwdArgs &a, hipStream_t stream) {
     const int64_t units = (int64_t)(a.seg.num_seqs > 0 ? a.seg.num_seqs : a.seg.B) * a.seg.H;
-    const int64_t n = (int64_t)a.seg.B * a.seg.T * a.seg.H * kWN;
-    hipLaunchKernelGGL(bwd128_zero_kernel, dim3(2048), dim3(256), 0, stream, (float4 *)acc, (int64_t)NACC * n / 4);
-    hipError_t e = hipGetLastError();
+    const size_t lds = (size_t)L_TOTAL * sizeof(float);
+    hipError_t e = hipFuncSetAttribute((const void *)bwd128_kernel<TI, TO>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    const int64_t blocks = (units + 7) / 8 * 8 * kBlocksPerUnit;
-    hipLaunchKernelGGL((bwd128_kernel<TI, TO>), dim3((unsigned)blocks), dim3(kWThreads), 0, stream, a, acc,
+    hipLaunchKernelGGL((bwd128_kernel<TI, TO>), dim3((unsigned)units), dim3(kWThreads), lds, stream, a,
                        (int32_t)units);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd128_finish_kernel<TO>, dim3(2048), dim3(256), 0, stream, a, (const float *)acc, n);
     return hipGetLastError();
 }
 
 template <typename TI>
-hipError_t launch_ti(const BwdArgs &a, float *acc, hipStream_t stream) {
-    if (a.grad_f32) return launch_t<TI, float>(a, acc, stream);
-    return launch_t<TI, TI>(a, acc, stream);
+hipError_t launch_ti(const BwdArgs &a, hipStream_t stream) {
+    if (a.grad_f32) return launch_t<TI, float>(a, stream);
+    return launch_t<TI, TI>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_backward128(const BwdArgs &a, float *acc, hipStream_t stream) {
-    if (a.dtype == 1) return launch_ti<uint16_t>(a, acc, stream);
-    if (a.dtype == 2) return launch_ti<_Float16>(a, acc, stream);
-    return launch_ti<float>(a, acc, stream);
+hipError_t launch_backward128(const BwdArgs &a, hipStream_t stream) {
+    if (a.dtype == 1) return launch_ti<uint16_t>(a, stream);
+    if (a.dtype == 2) return launch_ti<_Float16>(a, stream);
+    return launch_ti<float>(a, stream);
 }
 
 }  // namespace wkv7

@@ -64,7 +64,7 @@ hipError_t launch_backward_sweep(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 // Head size 128: token-order backward of 8-row blocks; acc is a workspace of
 // 5 x B*T*H*128 fp32 (the key-indexed gradients before their final dtype).
-hipError_t launch_backward128(const BwdArgs &a, float *acc, hipStream_t stream);
+hipError_t launch_backward128(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecArgs &a, hipStream_t stream);
 
 // One token of a gated DeltaNet layer through the RWKV-7 remap.

@@ -86,9 +86,10 @@ def test_backward_rejects_bad_arguments():
         ctypes.byref(d), *P[:6], ckpt, None, None, *grads, None, ws, wsb, None)
     assert call(desc(N=32)) == UNSUPPORTED
     assert call(desc(N=96)) == UNSUPPORTED
-    assert call(desc(N=128)) == WS                 # head size 128 needs its accumulator workspace
-    need = W.wkv7_workspace_bytes(2, 32, 4, 1, n=128)
-    assert call(desc(N=128), ws=ctypes.c_void_p(1 << 44), wsb=need - 1) == WS
+    # head size 128 takes no workspace; its other checks still apply
+    assert W.wkv7_workspace_bytes(2, 32, 4, 1, n=128) == 0
+    assert call(desc(N=128), ckpt=None) == INVALID
+    assert call(desc(N=128, dtype=7)) == UNSUPPORTED
     assert call(d, ckpt=None) == INVALID
     for q in range(6):
         g = list(grads); g[q] = None
@@ -203,9 +204,10 @@ def test_workspace_query():
     assert W.lib().wkv7_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
     assert n.value == 9 * 2 * per * 4 + 256
     assert W.lib().wkv7_workspace_bytes(ctypes.byref(desc(N=48)), ctypes.byref(n)) == UNSUPPORTED
-    # head size 128: fp32 accumulators of dr, dk, db, dw, da, [B, T, H, 128] each
+    # head size 128: none (one workgroup per unit sums every gradient)
+    n.value = 123
     assert W.lib().wkv7_workspace_bytes(ctypes.byref(desc(N=128)), ctypes.byref(n)) == 0
-    assert n.value == 5 * 2 * 32 * 4 * 128 * 4
+    assert n.value == 0
 
 
 def test_segments_check_matches_layout_helpers():
