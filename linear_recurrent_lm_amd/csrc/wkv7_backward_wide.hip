@@ -95,34 +95,6 @@ __device__ __forceinline__ void un8(const Raw8<float> &r, float *x) {
     x[4] = r.q[1].x; x[5] = r.q[1].y; x[6] = r.q[1].z; x[7] = r.q[1].w;
 }
 
-// Lane exchanges without the LDS crossbar: DPP moves within rows of 16 lanes
-// (fused into the adds) and the gfx950 row swaps. swap16(A, B) exchanges the
-// odd 16-lane rows of A with the even rows of B; swap32(A, B) the upper 32
-// lanes of A with the lower 32 of B.
-template <int CTRL> __device__ __forceinline__ float dpp(float x) {
-    return __builtin_amdgcn_update_dpp(0.f, x, CTRL, 0xf, 0xf, false);
-}
-constexpr int kRowRor8 = 0x128, kHalfMirror = 0x141, kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;
-__device__ __forceinline__ void swap16(float &a, float &b) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void swap32(float &a, float &b) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-}
-// sum over the 16 lanes of a row, in every lane: pairs 8 apart, then the
-// mirror within 8, then the quads' two exchanges
-__device__ __forceinline__ float sum16(float k) {
-    k += dpp<kRowRor8>(k);
-    k += dpp<kHalfMirror>(k);
-    k += dpp<kQuadXor1>(k);
-    k += dpp<kQuadXor2>(k);
-    return k;
-}
-
 // x[r]: this thread's partial sums (its 4 keys) of rows 4 (t / 32) + r; on
 // return, the sums over all 128 keys, in every lane of the half-wave. The
 // half-wave's even 16-lane row keeps rows 0, 1 and its odd row rows 2, 3,

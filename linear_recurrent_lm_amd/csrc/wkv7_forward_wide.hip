@@ -18,6 +18,7 @@
 // multiply-adds for the rows' S a, 3 x 128 for their update and 128 for S r,
 // against 40 broadcasts per wave (one row per lane over all keys takes 160).
 #include "wkv7_kernels.h"
+#include "wkv7_mfma.h"
 
 namespace wkv7 {
 namespace {
@@ -174,11 +175,8 @@ __global__ __launch_bounds__(128) void fwd128_kernel(FwdArgs p) {
                 }
             }
 #pragma unroll
-            for (int m = 0; m < RPL; ++m) {
-                x[m] = pa[m][0] + pa[m][1];
-                x[m] += __shfl_xor(x[m], 16);
-                x[m] += __shfl_xor(x[m], 32);
-            }
+            for (int m = 0; m < RPL; ++m) x[m] = pa[m][0] + pa[m][1];
+            sum_rows_all(x);                       // over the four key quarters (lane rows)
             float py[RPL][2];
 #pragma unroll
             for (int m = 0; m < RPL; ++m) py[m][0] = py[m][1] = 0.f;
@@ -201,13 +199,10 @@ __global__ __launch_bounds__(128) void fwd128_kernel(FwdArgs p) {
             }
             float o[RPL];
 #pragma unroll
-            for (int m = 0; m < RPL; ++m) {
-                o[m] = py[m][0] + py[m][1];
-                o[m] += __shfl_xor(o[m], 16);
-                o[m] += __shfl_xor(o[m], 32);
-            }
-            // key quarter m writes row rb + 16 m: 64 consecutive outputs per wave
-            const float om = kq == 0 ? o[0] : kq == 1 ? o[1] : kq == 2 ? o[2] : o[3];
+            for (int m = 0; m < RPL; ++m) o[m] = py[m][0] + py[m][1];
+            // key quarter m holds row rb + 16 m's total and writes it: 64
+            // consecutive outputs per wave
+            const float om = sum_rows_scatter(o);
             IO<TI>::st((TI *)p.y, tok * ts + h * N + rb + 16 * kq, om);
         }
         if (blk + 1 < nblk) F128_STORE(buf ^ 1);

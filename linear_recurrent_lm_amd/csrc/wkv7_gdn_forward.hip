@@ -18,6 +18,7 @@
 // row: N multiply-adds for <S_i, k^>, 2N for the update, N for <S_i, q^>.
 // Value head h reads key head h / (H / Hk).
 #include "wkv7_kernels.h"
+#include "wkv7_mfma.h"
 
 namespace wkv7 {
 namespace {
@@ -146,8 +147,12 @@ __global__ __launch_bounds__(N) void gdn_fwd_kernel(int32_t T, int32_t H, int32_
             }
             float sa0 = (p0[0] + p0[1]) + (p0[2] + p0[3]);
             float sa1 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
-            sa0 += __shfl_xor(sa0, 32);
-            sa1 += __shfl_xor(sa1, 32);
+            // over the key halves: the lower half's total of row i0 and the
+            // upper's of row i1, then both to every lane
+            swap32(sa0, sa1);
+            sa0 += sa1;
+            sa1 = sa0;
+            swap32(sa0, sa1);
             const float c0 = bt * fmaf(-e, sa0, v0);
             const float c1 = bt * fmaf(-e, sa1, v1);
             float y0[4] = {0.f, 0.f, 0.f, 0.f}, y1[4] = {0.f, 0.f, 0.f, 0.f};
@@ -175,10 +180,9 @@ __global__ __launch_bounds__(N) void gdn_fwd_kernel(int32_t T, int32_t H, int32_
             }
             float o0 = (y0[0] + y0[1]) + (y0[2] + y0[3]);
             float o1 = (y1[0] + y1[1]) + (y1[2] + y1[3]);
-            o0 += __shfl_xor(o0, 32);
-            o1 += __shfl_xor(o1, 32);
+            swap32(o0, o1);                        // lower half: row i0's total, upper: row i1's
             // key half 0 writes row i0, key half 1 row i1: 64 consecutive outputs per wave
-            IO<TI>::st(out, (tok * H + h) * N + (hf ? i1 : i0), (hf ? o1 : o0) * scale);
+            IO<TI>::st(out, (tok * H + h) * N + (hf ? i1 : i0), (o0 + o1) * scale);
         }
         if (blk + 1 < nblk) store_block(buf ^ 1);
         __syncthreads();

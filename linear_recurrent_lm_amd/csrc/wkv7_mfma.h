@@ -1,5 +1,6 @@
-// Device helpers shared by the chunk kernels: FP32 MFMA tiles, DPP lane
-// permutations within quads, and raw staging of 8-element input groups.
+// Device helpers shared by the kernels: FP32 and bf16 MFMA tiles, lane
+// exchanges in registers (DPP, gfx950 row swaps), and raw staging of
+// 8-element input groups.
 #pragma once
 
 #include "wkv7_device.h"
@@ -88,6 +89,55 @@ __device__ __forceinline__ float quad_sum(float v) {
     v += quad_perm<0xb1>(v);      // lanes ^1
     v += quad_perm<0x4e>(v);      // lanes ^2
     return v;
+}
+
+// Lane exchanges without the LDS crossbar: DPP moves within rows of 16 lanes
+// (fused into the adds that use them) and the gfx950 row swaps. swap16(A, B)
+// exchanges the odd 16-lane rows of A with the even rows of B: afterwards A
+// holds (A row 0, B row 0, A row 2, B row 2) and B (A row 1, B row 1, A row 3,
+// B row 3). swap32(A, B) exchanges the upper 32 lanes of A with the lower 32
+// of B: afterwards A holds (A low, B low) and B (A high, B high).
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+    return __builtin_amdgcn_update_dpp(0.f, x, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppRowRor8 = 0x128, kDppHalfMirror = 0x141, kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E;
+__device__ __forceinline__ void swap16(float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+// Sum over the 16 lanes of a row, in every lane: pairs 8 apart, then the
+// mirror within 8, then the quads' two exchanges.
+__device__ __forceinline__ float sum16(float k) {
+    k += dpp<kDppRowRor8>(k);
+    k += dpp<kDppHalfMirror>(k);
+    k += dpp<kDppQuadXor1>(k);
+    k += dpp<kDppQuadXor2>(k);
+    return k;
+}
+// x[q] summed over the four 16-lane rows of the wave: on return lane row q
+// holds the total of x[q] (a reduce-scatter; 2 + 1 swaps).
+__device__ __forceinline__ float sum_rows_scatter(const float (&x)[4]) {
+    float a0 = x[0], a1 = x[1], a2 = x[2], a3 = x[3];
+    swap16(a0, a1);
+    swap16(a2, a3);
+    float y01 = a0 + a1, y23 = a2 + a3;          // rows 0, 2: x0, x2 over rows (0,1)/(2,3); rows 1, 3: x1, x3
+    swap32(y01, y23);
+    return y01 + y23;                            // lower half: x0 (row 0), x1 (row 1); upper: x2, x3
+}
+// The same totals in every lane (3 more swaps).
+__device__ __forceinline__ void sum_rows_all(float (&x)[4]) {
+    float z = sum_rows_scatter(x), zl = z, zh = z;
+    swap32(zl, zh);                              // zl: row q & 1's total, zh: row 2 + (q & 1)'s
+    float e0 = zl, o0 = zl, e1 = zh, o1 = zh;
+    swap16(e0, o0);                              // e0: row 0's total, o0: row 1's
+    swap16(e1, o1);                              // e1: row 2's, o1: row 3's
+    x[0] = e0; x[1] = o0; x[2] = e1; x[3] = o1;
 }
 
 // Raw input data in flight: K groups of 8 elements per staging thread, kept
