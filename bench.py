@@ -18,7 +18,7 @@ a "leg" that --only can select, so that a profiler run covers one leg:
               right-padded [64, 2048], forward; packed forward + backward
     decode    decode step B=512 H=32 (warm and after a 1 GiB cache flush),
               the fused step, and a B=1 loop launched and graph-replayed
-    gdn       gated DeltaNet decode and prefill through the RWKV-7 remap
+    gdn       gated DeltaNet decode, prefill and its backward through the RWKV-7 remap
     n128      forward at head size 128; forward with checkpoints + backward
     variants  fp16 prefill; the step with log decay and fp32 gradients
     ce        LM-head cross-entropy over the 65536-entry vocabulary
@@ -501,6 +501,13 @@ def leg_gdn(args, W, synth, out):
     gdnf_ms = _time_ms(lambda: W.wkv7_gdn_forward(sq, sk, sv, sg, sb, None, out=sout, workspace=sws),
                        args.warmup, args.steps)
     gdnf_flop = 7 * 128 * 128 * 16 * 1024 * 32
+    # the backward on the same batch: gradients of out (dout ~ N(0, 1)) back to
+    # q, k, v, g, beta through the remap and the normalisation
+    sdo = torch.randn(sv.shape, device=dev, dtype=torch.float32, generator=torch.Generator(dev).manual_seed(12)).to(torch.bfloat16)
+    bws = torch.empty(W.wkv7_gdn_backward_workspace_bytes(16, 1024, 32, 16, 128), device=dev, dtype=torch.uint8)
+    gdnb_ms = _time_ms(lambda: W.wkv7_gdn_backward(sq, sk, sv, sg, sb, None, sdo, None, want_ds0=False,
+                                                   workspace=bws), args.warmup, args.steps)
+    del bws, sdo
     out["gdn_decode_step"] = {
         "workload": "gated DeltaNet via the RWKV-7 remap, bf16 B=128, 32 value heads over 16 key heads, "
                     "N=128, fp32 state in and out",
@@ -512,6 +519,11 @@ def leg_gdn(args, W, synth, out):
                     "heads, N=128, zero initial state",
         "ms": gdnf_ms, "tokens_per_s": 16 * 1024 / (gdnf_ms * 1e-3),
         "fp32_frac": gdnf_flop / (gdnf_ms * 1e-3) / PEAK_FP32}
+    out["gdn_prefill_backward"] = {
+        "workload": "gated DeltaNet backward via the RWKV-7 remap, same batch, dout ~ N(0,1): remap to fp32 "
+                    "streams, WKV-7 forward with checkpoints and backward at N=128, pull-back",
+        "ms": gdnb_ms, "tokens_per_s": 16 * 1024 / (gdnb_ms * 1e-3),
+        "fp32_frac_wkv7_backward_flops": 26 * 128 * 128 * 16 * 1024 * 32 / (gdnb_ms * 1e-3) / PEAK_FP32}
 
 
 def leg_n128(args, W, synth, out):
@@ -643,6 +655,9 @@ KERNEL_LABELS = {
     "gdn_decode_kernel": "gated DeltaNet decode step",
     "gdn_norm_kernel": "gated DeltaNet prefill: q^, k^ pre-pass",
     "gdn_fwd_kernel": "gated DeltaNet prefill: recurrence",
+    "gdn_remap_kernel": "gated DeltaNet backward: remapped fp32 streams",
+    "gdn_pull_value_kernel": "gated DeltaNet backward: dg, dbeta, dv",
+    "gdn_pull_key_kernel": "gated DeltaNet backward: dq, dk through the normalisation",
     "gemm_kernel": "cross-entropy GEMM core",
     "combine_kernel": "cross-entropy: merge of the vocabulary splits",
     "transpose_pad_kernel": "cross-entropy: padded transpose",
@@ -654,7 +669,7 @@ LEG_WORKLOADS = {
     "small": "forward fp32 B=1 T=64 H=1",
     "ragged": "64 sequences U[16, 2048], packed (4 streams) and right-padded [64, 2048]",
     "decode": "decode B=512 H=32; fused step; B=1 loop",
-    "gdn": "gated DeltaNet decode B=128 and prefill B=16 T=1024 (32 value heads over 16 key heads, N=128)",
+    "gdn": "gated DeltaNet decode B=128, prefill forward and backward B=16 T=1024 (32 value heads over 16 key heads, N=128)",
     "n128": "forward at head size 128, B=16 T=1024 H=32",
     "variants": "fp16 prefill; training step with log decay and fp32 gradients",
     "ce": "cross-entropy M=16384 D=2048 V=65536",

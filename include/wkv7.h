@@ -292,6 +292,43 @@ wkv7_status wkv7_gdn_forward(int32_t B, int32_t T, int32_t H, int32_t Hk, int32_
                              const float *beta, const float *s0, void *out, float *s_out,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Workspace bytes of wkv7_gdn_backward: q^, k^ ([B,T,Hk,N] fp32 each), seven
+ * remapped streams and six WKV-7 gradients ([B,T,H,N] fp32 each), the
+ * checkpoints (B * ceil(T/16) x H x N x N fp32) and the WKV-7 backward's
+ * workspace for fp32 streams at head size N, each part 256-byte aligned.
+ * Sizes are checked as for wkv7_gdn_forward.
+ */
+wkv7_status wkv7_gdn_backward_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Hk, int32_t N,
+                                              size_t *bytes);
+
+/*
+ * Reverse-mode gradients of L = sum <dout, out> + <ds_out, S_T> for
+ * wkv7_gdn_forward (rwkv-lab, "Highlight result -- GDN in RWKV-7"), through
+ * the RWKV-7 remap r = q^, w = exp(g), k_w = beta k^, a = -k^,
+ * b = beta exp(g) k^ and the normalisation x^ = x / max(||x||_2, 1e-12):
+ *     dk^ = beta dk_w - da + beta exp(g) db,  dq^ = dr (summed over the value
+ *     heads of a key head);  dg = exp(g) (sum_j dw_j + beta sum_j db_j k^_j);
+ *     dbeta = sum_j dk_w,j k^_j + exp(g) sum_j db_j k^_j;
+ *     dx = (dx^ - x^ <x^, dx^>) / ||x|| (||x|| > 1e-12), dx^ / 1e-12 otherwise.
+ *   q, k, v, g, beta, s0 : as for wkv7_gdn_forward.
+ *   dout   : [B,T,H,N] (dtype) gradient of out, or NULL (zero).
+ *   ds_out : fp32 [B,H,N,N] gradient of the final state, or NULL (zero).
+ *   dq, dk : [B,T,Hk,N] (dtype); dv : [B,T,H,N] (dtype); dg, dbeta : fp32
+ *            [B,T,H]; ds0 : fp32 [B,H,N,N] gradient of s0, or NULL.
+ *   workspace : >= wkv7_gdn_backward_workspace_bytes(B, T, H, Hk, N),
+ *            16-byte aligned, caller-owned; no two calls may share it at once.
+ * The remapped streams are written in fp32, the WKV-7 forward (for its
+ * checkpoints) and backward run on them at head size N, and two kernels
+ * pull the gradients back. No output may overlap an input, another output
+ * or the workspace: WKV7_ERR_INVALID_ARGUMENT, before any HIP call.
+ */
+wkv7_status wkv7_gdn_backward(int32_t B, int32_t T, int32_t H, int32_t Hk, int32_t N, int32_t dtype,
+                              const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, const float *s0, const void *dout, const float *ds_out,
+                              void *dq, void *dk, void *dv, float *dg, float *dbeta, float *ds0,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
 /* Number of checkpoint slots a dense forward needs: B * ceil(T / 16). */
 wkv7_status wkv7_checkpoint_slots(int32_t B, int32_t T, int64_t *slots);
 

@@ -584,6 +584,104 @@ wkv7_status wkv7_gdn_forward(int32_t B, int32_t T, int32_t H, int32_t Hk, int32_
     return WKV7_OK;
 }
 
+// Workspace of wkv7_gdn_backward, in 256-byte aligned parts: q^, k^
+// ([B][T][Hk][N] fp32 each), the remapped streams r, w, k_w, v, a, b and dy
+// and the WKV-7 gradients dr (first the discarded forward y), dw, dk, dv,
+// da, db ([B][T][H][N] fp32 each), the checkpoints, and the WKV-7
+// backward's own workspace.
+struct GdnBwdLayout {
+    size_t key, val, ckpt, wkv, total;
+};
+static wkv7_status gdn_bwd_layout(int32_t B, int32_t T, int32_t H, int32_t Hk, int32_t N, GdnBwdLayout *l) {
+    size_t dummy = 0;
+    wkv7_status st = wkv7_gdn_workspace_bytes(B, T, Hk, N, &dummy);
+    if (st != WKV7_OK) return st;
+    if (H < 1 || H % Hk != 0 || (int64_t)B * H > (1 << 24) || (int64_t)B * T * H * N > kMaxElems ||
+        (int64_t)B * T > INT32_MAX || H > 65536)
+        return WKV7_ERR_INVALID_ARGUMENT;
+    wkv7_desc d{};
+    d.B = B; d.T = T; d.H = H; d.N = N; d.dtype = WKV7_F32; d.grad_f32 = 1;
+    size_t wkv = 0;
+    if ((st = wkv7_workspace_bytes(&d, &wkv)) != WKV7_OK) return st;
+    int64_t slots = 0;
+    if ((st = wkv7_checkpoint_slots(B, T, &slots)) != WKV7_OK) return st;
+    l->key = pad256((size_t)B * T * Hk * N * sizeof(float));
+    l->val = pad256((size_t)B * T * H * N * sizeof(float));
+    l->ckpt = pad256((size_t)slots * H * N * N * sizeof(float));
+    l->wkv = pad256(wkv);
+    l->total = 2 * l->key + 13 * l->val + l->ckpt + l->wkv;
+    return WKV7_OK;
+}
+
+wkv7_status wkv7_gdn_backward_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Hk, int32_t N,
+                                              size_t *bytes) {
+    GdnBwdLayout l;
+    const wkv7_status st = gdn_bwd_layout(B, T, H, Hk, N, &l);
+    if (st != WKV7_OK) return st;
+    if (!bytes) return WKV7_ERR_INVALID_ARGUMENT;
+    *bytes = l.total;
+    return WKV7_OK;
+}
+
+wkv7_status wkv7_gdn_backward(int32_t B, int32_t T, int32_t H, int32_t Hk, int32_t N, int32_t dtype,
+                              const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, const float *s0, const void *dout, const float *ds_out,
+                              void *dq, void *dk, void *dv, float *dg, float *dbeta, float *ds0,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+    GdnBwdLayout l;
+    wkv7_status st = gdn_bwd_layout(B, T, H, Hk, N, &l);
+    if (st != WKV7_OK) return st;
+    if (!dtype_ok(dtype)) return WKV7_ERR_UNSUPPORTED;
+    const void *streams[6] = {q, k, v, dq, dk, dv};
+    if ((st = check_streams(streams, 6)) != WKV7_OK) return st;
+    if (dout && !aligned16(dout)) return WKV7_ERR_INVALID_ARGUMENT;
+    if (!g || !beta || !dg || !dbeta || !aligned4(g) || !aligned4(beta) || !aligned4(dg) || !aligned4(dbeta))
+        return WKV7_ERR_INVALID_ARGUMENT;
+    if ((s0 && !aligned16(s0)) || (ds_out && !aligned16(ds_out)) || (ds0 && !aligned16(ds0)))
+        return WKV7_ERR_INVALID_ARGUMENT;
+    if (!workspace || !aligned16(workspace)) return WKV7_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < l.total) return WKV7_ERR_WORKSPACE_TOO_SMALL;
+    {
+        const size_t es = elem_size(dtype);
+        const size_t kb = (size_t)B * T * Hk * N * es, vb = (size_t)B * T * H * N * es;
+        const size_t sb = (size_t)B * T * H * sizeof(float), state = (size_t)B * H * N * N * sizeof(float);
+        const Range ins[8] = {{q, kb}, {k, kb}, {v, vb}, {g, sb}, {beta, sb}, {s0, state}, {dout, vb},
+                              {ds_out, state}};
+        const Range outs[7] = {{dq, kb}, {dk, kb}, {dv, vb}, {dg, sb}, {dbeta, sb}, {ds0, state},
+                               {workspace, l.total}};
+        if (any_overlap(ins, 8, outs, 7)) return WKV7_ERR_INVALID_ARGUMENT;
+    }
+    if ((st = check_device()) != WKV7_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    auto part = [&](size_t &off, size_t n) { float *x = (float *)(ws + off); off += n; return x; };
+    size_t off = 0;
+    wkv7::GdnBwdArgs a{};
+    a.B = B; a.T = T; a.H = H; a.Hk = Hk; a.N = N; a.dtype = dtype;
+    a.q = q; a.k = k; a.v = v; a.dout = dout; a.g = g; a.beta = beta;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta;
+    a.qn = part(off, l.key); a.kn = part(off, l.key);
+    a.r = part(off, l.val); a.w = part(off, l.val); a.kw = part(off, l.val); a.v32 = part(off, l.val);
+    a.a = part(off, l.val); a.b = part(off, l.val); a.dy = part(off, l.val);
+    float *gr = part(off, l.val), *gw = part(off, l.val), *gk = part(off, l.val);
+    float *gv = part(off, l.val), *ga = part(off, l.val), *gb = part(off, l.val);
+    a.gr = gr; a.gw = gw; a.gk = gk; a.gv = gv; a.ga = ga; a.gb = gb;
+    float *ckpt = part(off, l.ckpt);
+    void *wkv_ws = l.wkv ? (void *)(ws + off) : nullptr;
+    if (wkv7::launch_gdn_remap(a, hs) != hipSuccess) return WKV7_ERR_HIP;
+    wkv7_desc d{};
+    d.B = B; d.T = T; d.H = H; d.N = N; d.dtype = WKV7_F32; d.grad_f32 = 1;
+    // the forward for the checkpoints; its y goes to dr's part, which the
+    // backward overwrites
+    if ((st = wkv7_forward(&d, a.r, a.w, a.kw, a.v32, a.a, a.b, s0, gr, nullptr, ckpt, stream)) != WKV7_OK)
+        return st;
+    if ((st = wkv7_backward(&d, a.r, a.w, a.kw, a.v32, a.a, a.b, ckpt, dout ? a.dy : nullptr, ds_out, gr, gw,
+                            gk, gv, ga, gb, ds0, wkv_ws, l.wkv, stream)) != WKV7_OK)
+        return st;
+    if (wkv7::launch_gdn_pullback(a, hs) != hipSuccess) return WKV7_ERR_HIP;
+    return WKV7_OK;
+}
+
 wkv7_status vce_forward_workspace_bytes(int32_t M, int32_t D, int32_t V, size_t *bytes) {
     wkv7_status st = vce_check_sizes(M, D, V);
     if (st != WKV7_OK) return st;

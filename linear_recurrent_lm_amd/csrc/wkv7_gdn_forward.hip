@@ -216,6 +216,26 @@ hipError_t launch_typed(const GdnFwdArgs &a, hipStream_t stream) {
 
 }  // namespace
 
+namespace {
+template <typename TI>
+hipError_t normalize_t(int N, const void *q, const void *k, float *qn, float *kn, int64_t rows, hipStream_t stream) {
+    if (N == 128)
+        hipLaunchKernelGGL((gdn_norm_kernel<TI, 128>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                           (const TI *)q, (const TI *)k, qn, kn, rows);
+    else
+        hipLaunchKernelGGL((gdn_norm_kernel<TI, 64>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                           (const TI *)q, (const TI *)k, qn, kn, rows);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gdn_normalize(int dtype, int N, const void *q, const void *k, float *qn, float *kn,
+                                int64_t rows, hipStream_t stream) {
+    if (dtype == 1) return normalize_t<uint16_t>(N, q, k, qn, kn, rows, stream);
+    if (dtype == 2) return normalize_t<_Float16>(N, q, k, qn, kn, rows, stream);
+    return normalize_t<float>(N, q, k, qn, kn, rows, stream);
+}
+
 hipError_t launch_gdn_forward(const GdnFwdArgs &a, hipStream_t stream) {
     if (a.dtype == 1) return launch_typed<uint16_t>(a, stream);
     if (a.dtype == 2) return launch_typed<_Float16>(a, stream);

@@ -95,6 +95,26 @@ struct GdnFwdArgs {
     float *qn, *kn;                  // workspace: q^, k^ in fp32, [B][T][Hk][N] each
 };
 hipError_t launch_gdn_forward(const GdnFwdArgs &a, hipStream_t stream);
+// q^, k^ of wkv7_gdn_forward's pre-pass, for `rows` token rows of N.
+hipError_t launch_gdn_normalize(int dtype, int N, const void *q, const void *k, float *qn, float *kn,
+                                int64_t rows, hipStream_t stream);
+struct GdnBwdArgs {
+    int32_t B, T, H, Hk, N;
+    int dtype;
+    const void *q, *k;               // [B][T][Hk][N], I/O type
+    const void *v, *dout;            // [B][T][H][N], I/O type; dout may be null (zero)
+    const float *g, *beta;           // [B][T][H]
+    void *dq, *dk;                   // [B][T][Hk][N], I/O type
+    void *dv;                        // [B][T][H][N], I/O type
+    float *dg, *dbeta;               // [B][T][H]
+    // fp32 workspace: q^, k^ [B][T][Hk][N]; the remapped WKV-7 streams and
+    // dy = dout / sqrt(N), [B][T][H][N]; the WKV-7 gradients, [B][T][H][N]
+    float *qn, *kn;
+    float *r, *w, *kw, *v32, *a, *b, *dy;
+    const float *gr, *gw, *gk, *gv, *ga, *gb;
+};
+hipError_t launch_gdn_remap(const GdnBwdArgs &a, hipStream_t stream);
+hipError_t launch_gdn_pullback(const GdnBwdArgs &a, hipStream_t stream);
 // The WKV-7 step (not fused) at head size 128.
 hipError_t launch_decode128(const DecArgs &a, hipStream_t stream);
 

@@ -82,12 +82,15 @@ def lib():
         L.wkv7_gdn_decode_step.argtypes = [i32] * 5 + [vp] * 9
         L.wkv7_gdn_workspace_bytes.argtypes = [i32] * 4 + [ctypes.POINTER(sz)]
         L.wkv7_gdn_forward.argtypes = [i32] * 6 + [vp] * 9 + [sz, vp]
+        L.wkv7_gdn_backward_workspace_bytes.argtypes = [i32] * 5 + [ctypes.POINTER(sz)]
+        L.wkv7_gdn_backward.argtypes = [i32] * 6 + [vp] * 15 + [sz, vp]
         L.vce_forward_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.vce_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.vce_forward.argtypes = [i32, i32, i32] + [vp] * 6 + [sz, vp]
         L.vce_backward.argtypes = [i32, i32, i32, i32] + [vp] * 8 + [sz, vp]
         for fn in ("wkv7_forward", "wkv7_backward", "wkv7_backward_noalloc", "wkv7_decode_step", "wkv7_decode_step_fused",
                    "wkv7_gdn_decode_step", "wkv7_gdn_workspace_bytes", "wkv7_gdn_forward",
+                   "wkv7_gdn_backward_workspace_bytes", "wkv7_gdn_backward",
                    "wkv7_checkpoint_slots",
                    "wkv7_workspace_bytes", "wkv7_segments_check", "vce_forward_workspace_bytes",
                    "vce_backward_workspace_bytes", "vce_forward", "vce_backward"):
@@ -442,6 +445,47 @@ def wkv7_gdn_forward(q, k, v, g, beta, s0=None, *, out=None, want_state=True, wo
         B, T, H, Hk, N, _dtype_code(v), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
         _ptr(out), _ptr(s_out), _ptr(ws), _nbytes(ws), _stream()))
     return out, s_out
+
+
+def wkv7_gdn_backward_workspace_bytes(B, T, H, Hk, N) -> int:
+    out = ctypes.c_size_t(0)
+    _check("wkv7_gdn_backward_workspace_bytes",
+           lib().wkv7_gdn_backward_workspace_bytes(B, T, H, Hk, N, ctypes.byref(out)))
+    return int(out.value)
+
+
+def wkv7_gdn_backward(q, k, v, g, beta, s0=None, dout=None, ds_out=None, *, want_ds0=True, workspace=None):
+    """Gradients of sum <dout, out> + <ds_out, S_T> for wkv7_gdn_forward.
+    Returns dict dq, dk ([B, T, Hk, N]), dv ([B, T, H, N]) in the inputs'
+    dtype, dg, dbeta (fp32 [B, T, H]) and ds0 (fp32 [B, H, N, N] or None)."""
+    torch = _torch()
+    dev = v.device
+    _cuda(v, "v")
+    B, T, H, N = v.shape
+    Hk = q.shape[2]
+    dt = v.dtype
+    _req(q, "q", dev, dt, (B, T, Hk, N))
+    _req(k, "k", dev, dt, (B, T, Hk, N))
+    _req(v, "v", dev, dt)
+    _req(g, "g", dev, torch.float32, (B, T, H))
+    _req(beta, "beta", dev, torch.float32, (B, T, H))
+    if s0 is not None:
+        _req(s0, "s0", dev, torch.float32, (B, H, N, N))
+    if dout is not None:
+        _req(dout, "dout", dev, dt, (B, T, H, N))
+    if ds_out is not None:
+        _req(ds_out, "ds_out", dev, torch.float32, (B, H, N, N))
+    res = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dg": torch.empty_like(g), "dbeta": torch.empty_like(beta),
+           "ds0": torch.empty((B, H, N, N), device=dev, dtype=torch.float32) if want_ds0 else None}
+    need = wkv7_gdn_backward_workspace_bytes(B, T, H, Hk, N)
+    ws = torch.empty(need, device=dev, dtype=torch.uint8) if workspace is None else workspace
+    _req(ws, "workspace", dev)
+    _check("wkv7_gdn_backward", lib().wkv7_gdn_backward(
+        B, T, H, Hk, N, _dtype_code(v), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
+        _ptr(dout), _ptr(ds_out), _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dg"]),
+        _ptr(res["dbeta"]), _ptr(res["ds0"]), _ptr(ws), _nbytes(ws), _stream()))
+    return res
 
 
 def wkv7_abi_version() -> int:

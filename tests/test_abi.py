@@ -185,6 +185,36 @@ def test_gdn_forward_rejects_bad_arguments():
         W.wkv7_gdn_workspace_bytes(2, 8, 2, 96)
 
 
+def test_gdn_backward_rejects_bad_arguments():
+    L = W.lib()
+    far = [ctypes.c_void_p((q + 1) << 40) for q in range(16)]
+    BIG = 1 << 38
+
+    def call(B=2, T=8, H=4, Hk=2, N=128, dt=1, q=far[0], k=far[1], v=far[2], g=far[3], beta=far[4],
+             s0=None, dout=far[5], ds_out=None, dq=far[6], dk=far[7], dv=far[8], dg=far[9], dbeta=far[10],
+             ds0=far[11], ws=far[12], nbytes=BIG):
+        return L.wkv7_gdn_backward(B, T, H, Hk, N, dt, q, k, v, g, beta, s0, dout, ds_out, dq, dk, dv, dg,
+                                   dbeta, ds0, ws, nbytes, None)
+    assert call(N=96) == UNSUPPORTED
+    assert call(dt=7) == UNSUPPORTED
+    assert call(T=0) == INVALID
+    assert call(H=6, Hk=4) == INVALID
+    for name in ("q", "k", "v", "g", "beta", "dq", "dk", "dv", "dg", "dbeta", "ws"):
+        assert call(**{name: None}) == INVALID, name
+    assert call(dout=ctypes.c_void_p(far[5].value + 8)) == INVALID          # misaligned
+    assert call(ds0=ctypes.c_void_p(far[11].value + 4)) == INVALID
+    assert call(dv=ctypes.c_void_p(far[2].value + 64)) == INVALID           # dv overlaps v
+    assert call(dg=ctypes.c_void_p(far[12].value + 256)) == INVALID         # dg overlaps the workspace
+    assert call(dq=far[7]) == INVALID                                      # dq is dk
+    need = W.wkv7_gdn_backward_workspace_bytes(2, 8, 4, 2, 128)
+    key, val = 2 * 8 * 2 * 128 * 4, 2 * 8 * 4 * 128 * 4
+    assert need == 2 * key + 13 * val + 2 * 4 * 128 * 128 * 4              # + checkpoints; no WKV-7 workspace
+    assert W.wkv7_gdn_backward_workspace_bytes(2, 8, 4, 2, 64) > 0
+    assert call(nbytes=need - 1) == WS
+    with pytest.raises(W.WKV7Error):
+        W.wkv7_gdn_backward_workspace_bytes(2, 8, 4, 2, 96)
+
+
 def test_checkpoint_slots():
     assert W.checkpoint_slots(3, 33) == 9
     assert W.checkpoint_slots(2, 16) == 2
