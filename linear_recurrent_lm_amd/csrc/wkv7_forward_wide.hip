@@ -5,18 +5,20 @@
 // (resolve_unit), initial state or zero, final state, and a state checkpoint
 // at every 16th token of a sequence (the state entering tokens 0, 16, 32...).
 //
-// One workgroup of 128 lanes (two waves) per (sequence, head). In wave v,
-// lane l holds key quarter l / 16 (32 keys) of the four state rows
-// 64 v + l % 16 + 16 m, m = 0..3, so every row value a lane reads serves four
+// One workgroup of 256 lanes (four waves) per (sequence, head). In wave v,
+// lane l holds key quarter l / 16 (32 keys) of the two state rows
+// 32 v + l % 16 + 16 m, m = 0..1, so every row value a lane reads serves two
 // state rows; the four key quarters of a row add their partial dot products
-// with two lane exchanges inside the wave. The r, w, k, a, b rows of a block
-// of tokens (8 for 16-bit streams, 4 for fp32) are staged in LDS as fp32 (w
-// already exponentiated when it holds log(decay)), double-buffered with the
-// next block's loads in flight, and read as 16-byte broadcasts, one address
-// per key quarter; the quarters' 16-byte chunks alternate in a row so that the
-// four addresses fall in different banks. Per token and lane: 128
-// multiply-adds for the rows' S a, 3 x 128 for their update and 128 for S r,
-// against 40 broadcasts per wave (one row per lane over all keys takes 160).
+// with register swaps between the wave's 16-lane rows. Four waves of 64
+// elements per lane run two waves per SIMD at the prefill shape (512 units
+// on 256 CUs), against one for two waves of 128 elements: 1.59 against 2.25
+// ms. The r, w, k, a, b rows of a block of tokens (8 for 16-bit streams, 4
+// for fp32) are staged in LDS as fp32 (w already exponentiated when it holds
+// log(decay)), double-buffered with the next block's loads in flight, and
+// read as 16-byte broadcasts, one address per key quarter; the quarters'
+// 16-byte chunks alternate in a row so that the four addresses fall in
+// different banks. Per token and lane: 64 multiply-adds for the rows' S a,
+// 3 x 64 for their update and 64 for S r, against 40 broadcasts per wave.
 #include "wkv7_kernels.h"
 #include "wkv7_mfma.h"
 
@@ -59,23 +61,24 @@ __device__ __forceinline__ void unpack<_Float16>(const u32x4 &x, float *out) {
 }
 
 template <typename TI>
-__global__ __launch_bounds__(128) void fwd128_kernel(FwdArgs p) {
+__global__ __launch_bounds__(256) void fwd128_kernel(FwdArgs p) {
     constexpr int N = 128;
     constexpr int EPL = 16 / (int)sizeof(TI);        // elements per 16-byte load
     constexpr int TB = sizeof(TI) == 2 ? 8 : 4;      // tokens per staged block
     constexpr int CPR = N / EPL;                     // 16-byte chunks per row
-    constexpr int LOADS = TB * 5 * CPR / N;          // loads per lane and block
-    static_assert(TB * 5 * CPR % N == 0, "whole loads per lane");
+    constexpr int NT = 256;                          // threads
+    constexpr int TOTAL = TB * 5 * CPR;              // 16-byte chunks per block
+    constexpr int LOADS = (TOTAL + NT - 1) / NT;     // loads per lane and block
     __shared__ __align__(16) float vec[2][TB][5][N];  // [buffer][token][r w k a b][N]
 
     const int H = p.seg.H;
     const int64_t unit = blockIdx.x;
     const int sq = (int)(unit / H), h = (int)(unit % H);
     const Unit u = resolve_unit(p.seg, sq);
-    constexpr int RPL = 4, KL = N / RPL, NQ = KL / 4;   // rows per lane, keys per lane, quads
+    constexpr int RPL = 2, KL = 32, NQ = KL / 4;        // rows per lane, keys per lane, quads
     const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
     const int kq = ln >> 4;                          // key quarter: keys [32 kq, 32 kq + 32)
-    const int rb = wv * 64 + (ln & 15);              // the lane's rows: rb + 16 m, m = 0..3
+    const int rb = wv * 32 + (ln & 15);              // the lane's rows: rb + 16 m, m = 0..1
     const int64_t ts = (int64_t)H * N;               // stream pitch of one token
     const int64_t srow = ((int64_t)unit * N + rb) * N + kq * KL;
 
@@ -101,7 +104,8 @@ __global__ __launch_bounds__(128) void fwd128_kernel(FwdArgs p) {
 #define F128_LOAD(t0)                                                                       \
     do {                                                                                    \
         _Pragma("unroll") for (int q = 0; q < LOADS; ++q) {                                 \
-            const int c = q * N + tid;                                                      \
+            const int c = q * NT + tid;                                                     \
+            if (c >= TOTAL) break;                                                          \
             const int tt = c / (5 * CPR), row = (c / CPR) % 5, ch = c % CPR;                \
             const int64_t tok = u.start + min((t0) + tt, u.len - 1);                        \
             const TI *s_ = row == 0 ? src[0] : row == 1 ? src[1] : row == 2 ? src[2]        \
@@ -114,7 +118,8 @@ __global__ __launch_bounds__(128) void fwd128_kernel(FwdArgs p) {
 #define F128_STORE(buf)                                                                     \
     do {                                                                                    \
         _Pragma("unroll") for (int q = 0; q < LOADS; ++q) {                                 \
-            const int c = q * N + tid;                                                      \
+            const int c = q * NT + tid;                                                     \
+            if (c >= TOTAL) break;                                                          \
             const int tt = c / (5 * CPR), row = (c / CPR) % 5, ch = c % CPR;                \
             float x[EPL];                                                                   \
             unpack<TI>(st[q], x);                                                           \
@@ -176,7 +181,16 @@ __global__ __launch_bounds__(128) void fwd128_kernel(FwdArgs p) {
             }
 #pragma unroll
             for (int m = 0; m < RPL; ++m) x[m] = pa[m][0] + pa[m][1];
-            sum_rows_all(x);                       // over the four key quarters (lane rows)
+            {   // over the four key quarters (lane rows): rows 0, 2 of lanes
+                // end with x0's total, rows 1, 3 with x1's, then both to all
+                float a0 = x[0], a1 = x[1];
+                swap16(a0, a1);
+                float y = a0 + a1, y2 = y;
+                swap32(y, y2);
+                float t = y + y2, t2 = t;
+                swap16(t, t2);
+                x[0] = t; x[1] = t2;
+            }
             float py[RPL][2];
 #pragma unroll
             for (int m = 0; m < RPL; ++m) py[m][0] = py[m][1] = 0.f;
@@ -202,8 +216,15 @@ __global__ __launch_bounds__(128) void fwd128_kernel(FwdArgs p) {
             for (int m = 0; m < RPL; ++m) o[m] = py[m][0] + py[m][1];
             // key quarter m holds row rb + 16 m's total and writes it: 64
             // consecutive outputs per wave
-            const float om = sum_rows_scatter(o);
-            IO<TI>::st((TI *)p.y, tok * ts + h * N + rb + 16 * kq, om);
+            float om;
+            {
+                float a0 = o[0], a1 = o[1];
+                swap16(a0, a1);
+                float y = a0 + a1, y2 = y;
+                swap32(y, y2);
+                om = y + y2;                       // rows 0, 2: o0's total; rows 1, 3: o1's
+            }
+            if (kq < RPL) IO<TI>::st((TI *)p.y, tok * ts + h * N + rb + 16 * kq, om);
         }
         if (blk + 1 < nblk) F128_STORE(buf ^ 1);
         __syncthreads();
@@ -221,7 +242,7 @@ __global__ __launch_bounds__(128) void fwd128_kernel(FwdArgs p) {
 
 template <typename TI>
 hipError_t launch_t(const FwdArgs &a, int64_t units, hipStream_t stream) {
-    hipLaunchKernelGGL(fwd128_kernel<TI>, dim3((unsigned)units), dim3(128), 0, stream, a);
+    hipLaunchKernelGGL(fwd128_kernel<TI>, dim3((unsigned)units), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
