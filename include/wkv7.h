@@ -304,9 +304,11 @@ wkv7_status wkv7_gdn_backward_workspace_bytes(int32_t B, int32_t T, int32_t H, i
 
 /*
  * Reverse-mode gradients of L = sum <dout, out> + <ds_out, S_T> for
- * wkv7_gdn_forward (rwkv-lab, "Highlight result -- GDN in RWKV-7"), through
- * the RWKV-7 remap r = q^, w = exp(g), k_w = beta k^, a = -k^,
- * b = beta exp(g) k^ and the normalisation x^ = x / max(||x||_2, 1e-12):
+ * wkv7_gdn_forward (rwkv-lab, "Highlight result -- GDN in RWKV-7"). That
+ * forward is the WKV-7 step with decay exp(g) on every key, a-vector -k^,
+ * b-vector beta exp(g) k^, written key k_w = beta k^ and read vector q^ (the
+ * gated delta rule expanded); the gradients go back through it and through
+ * the normalisation x^ = x / max(||x||_2, 1e-12):
  *     dk^ = beta dk_w - da + beta exp(g) db,  dq^ = dr (summed over the value
  *     heads of a key head);  dg = exp(g) (sum_j dw_j + beta sum_j db_j k^_j);
  *     dbeta = sum_j dk_w,j k^_j + exp(g) sum_j db_j k^_j;

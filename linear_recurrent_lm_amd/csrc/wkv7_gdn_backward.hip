@@ -1,16 +1,18 @@
-// Gated DeltaNet (GDN) backward through the RWKV-7 remap of the rwkv-lab page
-// ("Highlight result -- GDN in RWKV-7"). The forward is the WKV-7 recurrence
-// on the remapped streams
-//     r = q^,  w = exp(g),  k_w = beta k^,  a = -k^,  b = beta exp(g) k^,
-//     out = y / sqrt(N),   x^ = x / max(||x||_2, 1e-12),
-// with value head h reading key head h / (H / Hk). The backward writes those
-// streams (and dy = dout / sqrt(N)) in fp32, runs the WKV-7 forward (for the
-// checkpoints) and backward on them, and pulls the WKV-7 gradients back:
-//     dk^ = beta dk_w - da + beta exp(g) db,  dq^ = dr   (summed over the
-//         value heads of a key head)
-//     dg  = exp(g) (sum_j dw_j + beta sum_j db_j k^_j)
-//     dbeta = sum_j dk_w,j k^_j + exp(g) sum_j db_j k^_j
-//     dx = (dx^ - x^ <x^, dx^>) / ||x||   (||x|| > 1e-12; else dx^ / 1e-12)
+// Gated DeltaNet (GDN) backward, through the WKV-7 form of the gated delta
+// rule that the rwkv-lab page's section "Highlight result -- GDN in RWKV-7"
+// proposes. The rule S' = e^g S (I - beta k^ k^T) + beta v k^T is the WKV-7
+// step with decay e^g on every key, a-vector -k^, b-vector beta e^g k^ and
+// written key beta k^; the output reads along q^ and is scaled by 1/sqrt(N)
+// (x^ = x / max(||x||_2, 1e-12); value head h reads key head h / (H / Hk)).
+// The backward writes those five vectors, v and dy = dout / sqrt(N) as fp32
+// streams, runs the WKV-7 forward (for the checkpoints) and backward on them,
+// and applies the chain rule to the WKV-7 gradients:
+//     the key's total dk^ = beta dk_w - da + beta e^g db, and dq^ = dr, each
+//         summed over the value heads of a key head;
+//     dg = e^g (sum_j dw_j + beta sum_j db_j k^_j)   (every key's decay is e^g);
+//     dbeta = sum_j dk_w,j k^_j + e^g sum_j db_j k^_j;
+//     through the normalisation dx = (dx^ - x^ <x^, dx^>) / ||x|| when
+//         ||x|| > 1e-12, and dx^ / 1e-12 otherwise.
 // This file holds the remap and the pull-back; the WKV-7 calls are the
 // library's own.
 #include "wkv7_kernels.h"

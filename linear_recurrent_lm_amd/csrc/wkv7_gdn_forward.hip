@@ -1,11 +1,13 @@
-// A sequence of gated DeltaNet (GDN) tokens through the RWKV-7 remap of the
-// rwkv-lab page ("Highlight result -- GDN in RWKV-7"), at head size 128 (or
-// 64). With q^ = q/||q||, k^ = k/||k|| and the remap r = q^, w = exp(g),
-// k_write = beta k^, a = -k^, b = k^ exp(g) beta, the WKV-7 row update of
-// value row i is
+// A sequence of gated DeltaNet (GDN) tokens, run as WKV-7 steps as the
+// rwkv-lab page's section "Highlight result -- GDN in RWKV-7" proposes, at
+// head size 128 (or 64). Expanding the gated delta rule
+//     S' = e^g S (I - beta k^ k^T) + beta v k^T
+// gives S' = S diag(e^g) + (S a) b^T + v k_w^T with the decay e^g on every
+// key, a = -k^ and b = beta e^g k^ (the sign could sit on either), and the
+// written key k_w = beta k^; the output reads S' along q^ and is scaled by
+// 1/sqrt(N). For value row i:
 //     S_i <- exp(g) S_i + beta (v_i - exp(g) <S_i, k^>) k^,   out_i = <S_i, q^> / sqrt(N)
-// (q^, k^: q and k over max(||.||_2, 1e-12), so a zero row gives a zero vector)
-// (the gated delta rule, since the decay is one scalar per token and head).
+// (q^, k^: q and k over max(||.||_2, 1e-12), so a zero row gives a zero vector).
 //
 // Two kernels. A pre-pass writes q^ and k^ in fp32 to the workspace (one
 // wave per token row). The recurrence then runs token by token with one

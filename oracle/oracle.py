@@ -262,9 +262,12 @@ def gdn_forward(q, k, v, g, beta, s0=None):
 def gdn_backward(q, k, v, g, beta, s0=None, dout=None, ds_out=None):
     """Reverse-mode gradients of L = sum <dout, out> + <ds_out, S_T> for
     gdn_forward (rwkv-lab, "Highlight result -- GDN in RWKV-7"), by the chain
-    rule from the WKV-7 backward through the remap and the normalisation:
+    rule from the WKV-7 backward through the remap and the normalisation.
+    gdn_forward runs the gated delta rule as a WKV-7 step whose decay is e^g
+    on every key, whose a- and b-vectors are -k^ and beta e^g k^, whose
+    written key is beta k^ (k_w) and whose read vector is q^, with the output
+    scaled by 1/sqrt(N). Each of those is linear in k^ or q^, so:
 
-        r = q^, w = e^g, k_w = beta k^, a = -k^, b = beta e^g k^, out = y / sqrt(N)
         dq^ = dr;  dk^ = beta dk_w - da + beta e^g db
         dg = e^g (sum_j dw_j + beta sum_j db_j k^_j)
         dbeta = sum_j dk_w,j k^_j + e^g sum_j db_j k^_j
