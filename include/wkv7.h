@@ -337,8 +337,8 @@ wkv7_status wkv7_checkpoint_slots(int32_t B, int32_t T, int64_t *slots);
 /* Workspace bytes wkv7_backward needs for this descriptor. N = 64:
  * checkpoint slots (B * ceil(T / 16) dense, the segment table's slot count
  * otherwise) x H x (64 x 64 + 16 x 64 + 16 x 16) x 4; in segment mode plus
- * 4 x (1 + 2 x (ceil(slots / 8) + num_seqs)) bytes rounded up to 256 (the
- * list of (sequence, 8-chunk group) work items of the second kernel).
+ * 4 x (1 + 2 x (ceil(slots / 8) + num_seqs)) bytes rounded up to 256 (room
+ * for the list of (sequence, chunk group) work items of the second kernel).
  * N = 128: 0 (the backward needs no workspace). */
 wkv7_status wkv7_workspace_bytes(const wkv7_desc *d, size_t *bytes);
 

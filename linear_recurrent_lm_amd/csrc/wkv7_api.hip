@@ -175,7 +175,8 @@ wkv7_status vce_bwd_layout(int32_t M, int32_t D, int32_t V, int32_t vocab_chunk,
 
 // Segment mode: the backward's list of (sequence, chunk group) work items
 // after the per-chunk results: a count and at most ceil(slots / 8) +
-// num_seqs int32 pairs.
+// num_seqs int32 pairs (a bound for groups of 8 or more chunks; the kernel's
+// groups are 16).
 int64_t glist_cap(int64_t slots, int64_t num_seqs) { return (slots + 7) / 8 + num_seqs; }
 size_t glist_bytes(int64_t slots, int64_t num_seqs) { return (size_t)(1 + 2 * glist_cap(slots, num_seqs)) * 4; }
 

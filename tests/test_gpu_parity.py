@@ -197,7 +197,7 @@ def run_backward(W, inp, segments=None):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("T", [1, 16, 17, 40, 273])     # 273: 18 chunks, groups of 8, 8 and 2
+@pytest.mark.parametrize("T", [1, 16, 17, 40, 273])     # 273: 18 chunks, workgroups of 16 and 2
 def test_backward_shapes(W, T, dtype):
     B, H = 2, 3
     inp = synth.make_inputs(B, T, H, 64, seed=200 + T, dtype=dtype, s0_std=0.1,
