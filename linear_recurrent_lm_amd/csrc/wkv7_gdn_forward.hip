@@ -121,6 +121,16 @@ __global__ __launch_bounds__(2 * N) void gdn_fwd_kernel(int32_t T, int32_t H, in
         return lo + hi;
     };
 
+    // The state is kept as S = G Sh, G the running product of the decays
+    // since the last fold: the decay then leaves the per-element update,
+    //     Sh_i <- Sh_i + (c_i / G') k^,   c_i = beta (v_i - G' <Sh_i, k^>),
+    //     out_i = G' <Sh_i, q^> / sqrt(N),  G' = G exp(g),
+    // which is the gated delta rule for S_i. When G' would fall below 2^-60
+    // (or exp(g) is 0), G' is first folded into Sh (Sh <- G' Sh, G' = 1),
+    // which leaves the same formula exact, so 1 / G' stays below 2^60 and
+    // every term is an fp32 number.
+    constexpr float kFoldBelow = 0x1p-60f;
+    float G = 1.f;
     const float scale = 1.f / sqrtf((float)N);
     load_block(0);
     store_block(0);
@@ -138,6 +148,14 @@ __global__ __launch_bounds__(2 * N) void gdn_fwd_kernel(int32_t T, int32_t H, in
             const float e = expf(g[tok * H + h]);
             const float bt = beta[tok * H + h];
             const float v0 = IO<TI>::ld(v, (tok * H + h) * N + i0);
+            float Gn = G * e;
+            if (!(Gn >= kFoldBelow)) {                           // uniform: g is per (token, head)
+                // fold the running product and this token's decay into Sh
+#pragma unroll
+                for (int j = 0; j < KH; ++j) S0[j] *= Gn;
+                Gn = 1.f;
+            }
+            const float btg = bt / Gn;                         // off the dot product's path
             float p0[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
@@ -148,24 +166,27 @@ __global__ __launch_bounds__(2 * N) void gdn_fwd_kernel(int32_t T, int32_t H, in
                 p0[2] = fmaf(S0[j + 2], kq.z, p0[2]);
                 p0[3] = fmaf(S0[j + 3], kq.w, p0[3]);
             }
-            const float sa0 = halves((p0[0] + p0[1]) + (p0[2] + p0[3]));
-            const float c0 = bt * fmaf(-e, sa0, v0);
+            const float sk = halves((p0[0] + p0[1]) + (p0[2] + p0[3]));   // <Sh, k^>
+            // S_{t-1} = G Sh, so e <S_{t-1}, k^> = Gn <Sh, k^> (after a fold Sh
+            // already holds e S_{t-1} and Gn is 1)
+            const float ci = btg * fmaf(-Gn, sk, v0);
             float y0[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const f32x4 kq = *(const f32x4 *)(kr + 8 * q);
                 const f32x4 qq = *(const f32x4 *)(qr + 8 * q);
                 const int j = 4 * q;
-                S0[j] = fmaf(kq.x, c0, S0[j] * e);
-                S0[j + 1] = fmaf(kq.y, c0, S0[j + 1] * e);
-                S0[j + 2] = fmaf(kq.z, c0, S0[j + 2] * e);
-                S0[j + 3] = fmaf(kq.w, c0, S0[j + 3] * e);
+                S0[j] = fmaf(kq.x, ci, S0[j]);
+                S0[j + 1] = fmaf(kq.y, ci, S0[j + 1]);
+                S0[j + 2] = fmaf(kq.z, ci, S0[j + 2]);
+                S0[j + 3] = fmaf(kq.w, ci, S0[j + 3]);
                 y0[0] = fmaf(S0[j], qq.x, y0[0]);
                 y0[1] = fmaf(S0[j + 1], qq.y, y0[1]);
                 y0[2] = fmaf(S0[j + 2], qq.z, y0[2]);
                 y0[3] = fmaf(S0[j + 3], qq.w, y0[3]);
             }
-            const float o0 = halves((y0[0] + y0[1]) + (y0[2] + y0[3]));
+            G = Gn;
+            const float o0 = halves((y0[0] + y0[1]) + (y0[2] + y0[3])) * G;
             // key half 0 writes the row: 32 consecutive outputs per wave
             if (hf == 0) IO<TI>::st(out, (tok * H + h) * N + i0, o0 * scale);
         }
@@ -175,7 +196,7 @@ __global__ __launch_bounds__(2 * N) void gdn_fwd_kernel(int32_t T, int32_t H, in
     if (s_out) {
 #pragma unroll
         for (int j = 0; j < KH; j += 4)
-            *(f32x4 *)(s_out + srow0 + j) = f32x4{S0[j], S0[j + 1], S0[j + 2], S0[j + 3]};
+            *(f32x4 *)(s_out + srow0 + j) = f32x4{S0[j] * G, S0[j + 1] * G, S0[j + 2] * G, S0[j + 3] * G};
     }
 }
 
