@@ -94,6 +94,28 @@ def test_forward128_segments(W, layout):
     assert U.unit_err_ckpt(U.host(ck), ref["ckpt"], seg.host_ckpt, nch) <= U.TOL_F32
 
 
+@pytest.mark.parametrize("decay", ["mult", "log"])
+def test_forward128_zero_and_tiny_decay(W, decay):
+    """Blocks whose decays are all at least 2^-6 run on a decay-normalised
+    state; the others (a zero decay at token 5, 1e-12 at tokens 33..37, 2^-10
+    on some keys at token 50) take the direct update. Both kinds, in both
+    decay inputs, against the oracle: y, the final state and the checkpoints."""
+    B, T, H = 2, 61, 2
+    inp = synth.make_inputs(B, T, H, N, seed=69, dtype="f32", s0_std=0.2, decay=decay)
+    vals = {5: 0.0, 33: 1e-12, 34: 1e-12, 35: 1e-12, 36: 1e-12, 37: 1e-12}
+    for t, x in vals.items():
+        inp.w[:, t] = np.log(x) if decay == "log" and x > 0 else (-1e30 if decay == "log" else x)
+    inp.w[:, 50, :, :9] = np.log(2.0 ** -10) if decay == "log" else 2.0 ** -10
+    y, s_out, ck = run(W, inp, "f32", decay=decay)
+    w = inp.w.astype(np.float64)
+    dec = np.exp(w) if decay == "log" else w
+    ref = O.forward(inp.r, dec, inp.k, inp.v, inp.a, inp.b, s0=inp.s0, checkpoints=True)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(s_out))
+    assert U.unit_err_dense(y, ref["y"]) <= U.TOL_F32
+    assert U.unit_err_state(s_out, ref["s_out"]) <= U.TOL_F32
+    assert U.unit_err_state(ck, ref["ckpt"]) <= U.TOL_F32
+
+
 def test_forward128_prefill_sampled(W):
     """Prefill shape B = 16, T = 1024, H = 32 at head size 128, bf16, random
     initial state: rows 0 and 15 (all heads) against the oracle."""
