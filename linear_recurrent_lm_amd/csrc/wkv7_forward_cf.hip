@@ -201,14 +201,19 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
                 const int src = part == 2 ? RB : RK;
                 float *rowm = sm + (part == 2 ? L::BH : L::KH);
                 float *keym = sm + (part == 2 ? L::BT : L::KT) + j * L::TLD;
+                float xs[16];
                 float sg = 1.f;
 #pragma unroll
                 for (int s = 15; s >= 0; --s) {
-                    const float x = in_at(src, s, j) * sg;
-                    rowm[s * L::LD + j] = x;
-                    keym[s] = x;
+                    xs[s] = in_at(src, s, j) * sg;
+                    rowm[s * L::LD + j] = xs[s];
                     sg *= wv[s];
                 }
+                // by key: 16-byte stores (a pitch of 20 words puts 8 lanes'
+                // stores on 32 distinct banks; single words would collide 8-way)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *(float4 *)(keym + 4 * q) = make_float4(xs[4 * q], xs[4 * q + 1], xs[4 * q + 2], xs[4 * q + 3]);
             }
             // one vote per wave (part 0 lanes decide; others agree)
             const bool all_ok = __all(ok);
@@ -275,20 +280,33 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
         }
         lds_barrier();
 
-        // ---- W = (I - L_ab)^-1 by forward substitution (wave 0, lane c holds
-        //      column c); every wave: rhs = A^ S_0^T + L_ak V, Y = R^ S_0^T + M_rk V
-        if (wave == 0 && lane < 16) {
+        // ---- W = (I - L_ab)^-1 by forward substitution on wave 0: the quad
+        //      of lanes 4 c .. 4 c + 3 owns column c, lane q of it the terms
+        //      s = q mod 4 of W[t][c] = [t == c] + sum_{s<t} L_ab[t][s] W[s][c],
+        //      completed by a quad sum; every wave: rhs = A^ S_0^T + L_ak V,
+        //      Y = R^ S_0^T + M_rk V
+        if (wave == 0) {
             const float *lab = sm + L::MAT + MLAB * 16 * L::MLD;
-            float wc[16];
+            const int cc = lane >> 2, qq = lane & 3;
+            // L_ab[t][4 m + qq] for 4 m < t, read before the chain starts;
+            // entries with s >= t are stored as zero and W entries not yet
+            // formed are zero, so every term is taken without a test
+            float lr[16][4];
+#pragma unroll
+            for (int t = 1; t < 16; ++t)
+#pragma unroll
+                for (int m = 0; 4 * m < t; ++m) lr[t][m] = lab[t * L::MLD + 4 * m + qq];
+            float wq[4] = {0.f, 0.f, 0.f, 0.f};           // W[4 m + qq][cc]
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-                float x = t == lane ? 1.f : 0.f;
+                float x = (t == cc && qq == 0) ? 1.f : 0.f;
 #pragma unroll
-                for (int s = 0; s < t; ++s) x = fmaf(lab[t * L::MLD + s], wc[s], x);
-                wc[t] = x;
+                for (int m = 0; 4 * m < t; ++m) x = fmaf(lr[t][m], wq[m], x);
+                x = quad_sum(x);
+                if ((t & 3) == qq) wq[t >> 2] = x;
             }
 #pragma unroll
-            for (int t = 0; t < 16; ++t) sm[L::MAT + MW * 16 * L::MLD + t * L::MLD + lane] = wc[t];
+            for (int m = 0; m < 4; ++m) sm[L::MAT + MW * 16 * L::MLD + (4 * m + qq) * L::MLD + cc] = wq[m];
         }
         float vf[4];                                     // V[token 4 g + s][row]
 #pragma unroll
