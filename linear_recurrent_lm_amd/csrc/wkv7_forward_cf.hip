@@ -1,4 +1,4 @@
-// WKV-7 forward in chunk form (C = 16) on FP32 MFMA, one lean workgroup per
+// WKV-7 forward in chunk form (C = 16) on MFMA, one lean workgroup per
 // (sequence, head): N / 16 waves, wave w holding value rows 16 w .. 16 w + 15
 // of the state in MFMA accumulators. Dense batches only.
 //
@@ -17,19 +17,28 @@
 // The four 16 x 16 matrices: when every decay of the chunk is at least 2^-6,
 // gamma_15 >= 2^-96 and L_ab = A- B^^T, L_ak = A- K^^T, M_rb = R- B^^T,
 // M_rk = R- K^^T with A- = A^ / gamma_15 and R- = R^ / gamma_15 exactly (each
-// factor to rounding): four MFMA products. Other chunks form the entries as
-// dot products with the decay products taken pair by pair (VALU). W =
+// factor to rounding): four MFMA products (with bf16 streams the 1 / gamma_15
+// goes on the B^ and K^ side instead). Other chunks form the entries as dot
+// products with the decay products taken pair by pair (VALU). W =
 // (I - L_ab)^-1 comes from forward substitution by one wave.
 //
-// Per chunk: stage r, w, k, a, b, v in LDS (fp32, w exponentiated for a
-// log-decay input, tokens past the end as identity tokens) from registers
-// loaded during the previous chunk; the prefix and suffix products and the
-// scaled rows (one thread per key and row kind); the matrices and the dense
-// products A^ S_0^T, R^ S_0^T; W and the right-hand sides; X, Y and the state
-// update. Five LDS barriers per chunk. The workgroup uses 111 KB of LDS at
-// N = 128 (one per CU, eight waves) and 60 KB at N = 64 (two per CU); the
-// library uses it for dense batches at head size 128, where it replaces a
-// token-order loop that runs the same flops on the VALU.
+// Two arithmetic layouts. fp32 and fp16 streams take every product on FP32
+// MFMA (16x16x4). bf16 streams take them on bf16 MFMA (16x16x32) in split
+// form: each operand of a product that feeds the state is carried as three
+// bf16 pieces (x = h + m + l, 24 significant bits) and six piece products
+// accumulate in fp32, which reproduces the fp32 product; V needs one piece
+// (its values are bf16), and the products that feed only y take fewer. On
+// gfx950 FP32 MFMAs hold the SIMD's VALU while they run and bf16 MFMAs do
+// not, so the split form also lets the row and staging work overlap them.
+//
+// Per chunk, four LDS barriers: the prefix and suffix products and the
+// scaled rows (one thread per key and row kind); the dense products A^ S_0^T,
+// R^ S_0^T and the matrices; W and the right-hand sides; X, Y and the state
+// update, behind whose MFMAs the next chunk's r, w, k, a, b, v are staged in
+// LDS (fp32, w exponentiated for a log-decay input, tokens past the end as
+// identity tokens) from registers loaded one chunk earlier. At N = 128 the
+// workgroup (eight waves) uses 129 KB of LDS in split form and 111 KB
+// otherwise, one per CU; at N = 64 69 KB and 60 KB, two per CU.
 //
 // MFMA layout (v_mfma_f32_16x16x4_f32): lane l supplies A[l % 16][l / 16] and
 // B[l / 16][l % 16]; element r of the result is D[4 (l / 16) + r][l % 16].
@@ -38,6 +47,9 @@
 // B-operand layout of A^ S_0^T when the contraction step (T, r) takes key
 // 16 T + 4 g + r from lane group g = l / 16. Products over the 16 tokens take
 // token 4 g + s at step s, which is element s of the D layout of X, rhs and Y.
+// The bf16 form keeps these layouts: a K = 32 step gives each lane group 8
+// elements, standing for keys 16 T + 4 g + e of two key tiles, or for tokens
+// 4 g + e with two piece pairs.
 #include "wkv7_kernels.h"
 #include "wkv7_mfma.h"
 
@@ -46,22 +58,34 @@ namespace {
 
 constexpr float kCfFastMinW = 0x1p-6f;
 
-template <int N> struct CfLay {
+// SP: the split-bf16 layout (bf16 streams), where the rows that feed the
+// state products are also held as bf16 pieces (words of two bf16).
+template <int N, bool SP> struct CfLay {
     static constexpr int LD = N + 4;                     // row pitch of [16][N] rows
     static constexpr int TLD = 20;                       // row pitch of [N][16] key-major rows
     static constexpr int MLD = 17;                       // row pitch of 16 x 16 matrices
+    static constexpr int PW = N / 2 + 2;                 // words per bf16 row of N keys
+    static constexpr int BKW = 50;                       // words per key: B^ h m l, K^ h m l (8 each)
     static constexpr int IN = 0;                         // [6][16][LD] r w k a b v
+    static constexpr int RWS = SP ? 0 : 16 * LD;         // fp32 rows (fp32 layout only)
     static constexpr int AH = IN + 6 * 16 * LD;          // [16][LD] A^
-    static constexpr int RH = AH + 16 * LD;              // [16][LD] R^
-    static constexpr int BH = RH + 16 * LD;              // [16][LD] B^
-    static constexpr int KH = BH + 16 * LD;              // [16][LD] K^
-    static constexpr int BT = KH + 16 * LD;              // [N][TLD] B^ by key
-    static constexpr int KT = BT + N * TLD;              // [N][TLD] K^ by key
-    static constexpr int MAT = KT + N * TLD;             // [5][16][MLD] L_ab L_ak M_rb M_rk W
+    static constexpr int RH = AH + RWS;                  // [16][LD] R^
+    static constexpr int BH = RH + RWS;                  // [16][LD] B^
+    static constexpr int KH = BH + RWS;                  // [16][LD] K^
+    static constexpr int BT = KH + RWS;                  // [N][TLD] B^ by key (fp32 layout)
+    static constexpr int KT = BT + N * TLD;              // [N][TLD] K^ by key (fp32 layout)
+    static constexpr int BK = BT;                        // [N][BKW] words, pieces by key (SP)
+    static constexpr int QA = BT + (SP ? N * BKW : 2 * N * TLD);   // [3][16][PW] words, A^ pieces (SP)
+    static constexpr int QR = QA + (SP ? 3 * 16 * PW : 0);         // [2][16][PW] words, R^ h and m (SP)
+    static constexpr int QB = QR + (SP ? 2 * 16 * PW : 0);         // [3][16][PW] words, B^ / gamma_15 (SP)
+    static constexpr int QK = QB + (SP ? 3 * 16 * PW : 0);         // [3][16][PW] words, K^ / gamma_15 (SP)
+    static constexpr int MAT = QK + (SP ? 3 * 16 * PW : 0);        // [5][16][MLD] L_ab L_ak M_rb M_rk W
     static constexpr int GAM = MAT + 5 * 16 * MLD;       // [N] gamma_15
     static constexpr int IGAM = GAM + N;                 // [N] 1 / gamma_15 (fast chunks)
     static constexpr int FLAG = IGAM + N;                // [N / 16] per-wave votes
     static constexpr int TOTAL = FLAG + N / 16;
+    static_assert(QA % 2 == 0 && QR % 2 == 0 && QB % 2 == 0 && QK % 2 == 0 && GAM % 4 == 0,
+                  "8-byte piece rows, 16-byte decay rows");
 };
 enum { RR = 0, RW, RK, RA, RB, RV };
 enum { MLAB = 0, MLAK, MMRB, MMRK, MW };
@@ -92,7 +116,8 @@ __device__ __forceinline__ void unpack16(const Ld16<float> &r, float *x) {
 
 template <typename TI, int N>
 __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units) {
-    using L = CfLay<N>;
+    constexpr bool SP = std::is_same<TI, uint16_t>::value;   // bf16 streams: split-bf16 products
+    using L = CfLay<N, SP>;
     constexpr int NT = 4 * N, NW = N / 16, NTILE = N / 16;
     constexpr int EPL = 16 / (int)sizeof(TI);            // elements per 16-byte load
     constexpr int GPR = N / EPL;                         // loads per row
@@ -157,21 +182,22 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
     };
     auto in_at = [&](int s, int t, int j) { return sm[L::IN + (s * 16 + t) * L::LD + j]; };
 
-    if (nch > 0) issue(0);
+    if (nch > 0) {
+        issue(0);
+        stage(0);
+        if (nch > 1) issue(1);
+    }
 #pragma unroll 1
     for (int c = 0; c < nch; ++c) {
         const int Lc = min(kChunk, u.len - c * kChunk);
         const int64_t t0 = (int64_t)c * kChunk;
-        lds_barrier();                                   // the previous chunk is done with LDS
-        // ---- stage the chunk; the state entering it is its checkpoint
-        stage(c);
-        if (c + 1 < nch) issue(c + 1);
+        // the state entering the chunk is its checkpoint
         if (p.ckpt) {
             float *ck = p.ckpt + ((u.ckpt + c) * H + h) * (int64_t)(N * N) + (int64_t)row * N + 4 * g;
 #pragma unroll
             for (int T = 0; T < NTILE; ++T) *(float4 *)(ck + 16 * T) = make_float4(S[T][0], S[T][1], S[T][2], S[T][3]);
         }
-        lds_barrier();
+        lds_barrier();                                   // chunk staged; the previous chunk done with LDS
         // ---- prefix and suffix decay products of key j; part 0: A^, gamma_15
         //      and the fast-chunk vote, 1: R^, 2: B^, 3: K^
         {
@@ -180,23 +206,48 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
 #pragma unroll
             for (int t = 0; t < 16; ++t) wv[t] = in_at(RW, t, j);
             bool ok = true;
+            // SP: bf16 pieces by token, keys j and j + 1 (j even) in one word:
+            // the even lane of the pair writes tokens 0..7, the odd lane
+            // tokens 8..15, each taking its partner's value across the pair
+            auto token_pieces = [&](const float (&xs)[16], int off, auto npieces) {
+                const bool odd = j & 1;
+                uint32_t *q = (uint32_t *)(sm + off) + (j >> 1);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float mine = odd ? xs[i + 8] : xs[i];
+                    const float recv = quad_perm<0xb1>(odd ? xs[i] : xs[i + 8]);
+                    const float lo = odd ? recv : mine, hi = odd ? mine : recv;
+                    const int t = i + (odd ? 8 : 0);
+                    uint32_t ph, pm, pl;
+                    split3(lo, hi, ph, pm, pl);
+                    q[t * L::PW] = ph;
+                    q[(16 + t) * L::PW] = pm;
+                    if constexpr (decltype(npieces)::value == 3) q[(32 + t) * L::PW] = pl;
+                }
+            };
             if (part == 0) {
+                float xs[16];
                 float gm = 1.f;
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
-                    sm[L::AH + t * L::LD + j] = in_at(RA, t, j) * gm;
+                    xs[t] = in_at(RA, t, j) * gm;
+                    if constexpr (!SP) sm[L::AH + t * L::LD + j] = xs[t];
                     gm *= wv[t];
                     ok = ok && wv[t] >= kCfFastMinW;
                 }
                 sm[L::GAM + j] = gm;
                 sm[L::IGAM + j] = 1.f / gm;
+                if constexpr (SP) token_pieces(xs, L::QA, std::integral_constant<int, 3>{});
             } else if (part == 1) {
+                float xs[16];
                 float gm = 1.f;
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
                     gm *= wv[t];
-                    sm[L::RH + t * L::LD + j] = in_at(RR, t, j) * gm;
+                    xs[t] = in_at(RR, t, j) * gm;
+                    if constexpr (!SP) sm[L::RH + t * L::LD + j] = xs[t];
                 }
+                if constexpr (SP) token_pieces(xs, L::QR, std::integral_constant<int, 2>{});
             } else {
                 const int src = part == 2 ? RB : RK;
                 float *rowm = sm + (part == 2 ? L::BH : L::KH);
@@ -206,14 +257,36 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
 #pragma unroll
                 for (int s = 15; s >= 0; --s) {
                     xs[s] = in_at(src, s, j) * sg;
-                    rowm[s * L::LD + j] = xs[s];
+                    if constexpr (!SP) rowm[s * L::LD + j] = xs[s];
                     sg *= wv[s];
                 }
-                // by key: 16-byte stores (a pitch of 20 words puts 8 lanes'
-                // stores on 32 distinct banks; single words would collide 8-way)
+                if constexpr (SP) {
+                    // bf16 pieces by key, two tokens to a word: h, m, l at
+                    // words 0, 8, 16 (B^) or 24, 32, 40 (K^) of the key's row
+                    uint32_t ph[8], pm[8], pl[8];
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *(float4 *)(keym + 4 * q) = make_float4(xs[4 * q], xs[4 * q + 1], xs[4 * q + 2], xs[4 * q + 3]);
+                    for (int i = 0; i < 8; ++i) split3(xs[2 * i], xs[2 * i + 1], ph[i], pm[i], pl[i]);
+                    uint32_t *q = (uint32_t *)(sm + L::BK) + j * L::BKW + (part == 2 ? 0 : 24);
+#pragma unroll
+                    for (int i = 0; i < 8; i += 2) {
+                        *(u32x2_t *)(q + i) = u32x2_t{ph[i], ph[i + 1]};
+                        *(u32x2_t *)(q + 8 + i) = u32x2_t{pm[i], pm[i + 1]};
+                        *(u32x2_t *)(q + 16 + i) = u32x2_t{pl[i], pl[i + 1]};
+                    }
+                    // and by token, divided by gamma_15 (sg now), for the
+                    // matrices of fast chunks (other chunks never read them)
+                    const float ig = 1.f / sg;
+                    float xt[16];
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) xt[t] = xs[t] * ig;
+                    token_pieces(xt, part == 2 ? L::QB : L::QK, std::integral_constant<int, 3>{});
+                } else {
+                    // by key: 16-byte stores (a pitch of 20 words puts 8 lanes'
+                    // stores on 32 distinct banks; single words would collide 8-way)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *(float4 *)(keym + 4 * q) = make_float4(xs[4 * q], xs[4 * q + 1], xs[4 * q + 2], xs[4 * q + 3]);
+                }
             }
             // one vote per wave (part 0 lanes decide; others agree)
             const bool all_ok = __all(ok);
@@ -227,16 +300,85 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
         // ---- A^ S_0^T and R^ S_0^T for the wave's rows (D layout: element r
         //      = [token 4 g + r][row]); the four matrices
         f32x4 da = {0.f, 0.f, 0.f, 0.f}, dr = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (SP) {
+            // A^ S_0^T from six piece products (both operands in three bf16
+            // pieces), R^ S_0^T (y only) from the high pieces. A K = 32 MFMA
+            // covers the key tiles 2 P and 2 P + 1: element e of lane group g
+            // stands for key 16 (2 P + e / 4) + 4 g + e % 4, which is where
+            // the state tiles hold them.
+            const uint32_t *qa = (const uint32_t *)(sm + L::QA) + l16 * L::PW + 2 * g;
+            const uint32_t *qr = (const uint32_t *)(sm + L::QR) + l16 * L::PW + 2 * g;
+            f32x4 db = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int T = 0; T < NTILE; ++T) {
-            const float4 a4 = *(const float4 *)(sm + L::AH + l16 * L::LD + 16 * T + 4 * g);
-            const float4 r4 = *(const float4 *)(sm + L::RH + l16 * L::LD + 16 * T + 4 * g);
-            da = mfma4(a4.x, S[T][0], da); dr = mfma4(r4.x, S[T][0], dr);
-            da = mfma4(a4.y, S[T][1], da); dr = mfma4(r4.y, S[T][1], dr);
-            da = mfma4(a4.z, S[T][2], da); dr = mfma4(r4.z, S[T][2], dr);
-            da = mfma4(a4.w, S[T][3], da); dr = mfma4(r4.w, S[T][3], dr);
+            for (int P = 0; P < NTILE / 2; ++P) {
+                uint32_t h[4], m[4], l[4];
+                split3(S[2 * P][0], S[2 * P][1], h[0], m[0], l[0]);
+                split3(S[2 * P][2], S[2 * P][3], h[1], m[1], l[1]);
+                split3(S[2 * P + 1][0], S[2 * P + 1][1], h[2], m[2], l[2]);
+                split3(S[2 * P + 1][2], S[2 * P + 1][3], h[3], m[3], l[3]);
+                const u32x4_t sh = {h[0], h[1], h[2], h[3]}, smd = {m[0], m[1], m[2], m[3]},
+                              sl = {l[0], l[1], l[2], l[3]};
+                auto row8 = [&](const uint32_t *q) {
+                    return cat(*(const u32x2_t *)(q + 16 * P), *(const u32x2_t *)(q + 16 * P + 8));
+                };
+                const u32x4_t ah = row8(qa), am = row8(qa + 16 * L::PW), al = row8(qa + 32 * L::PW);
+                da = mfma_bf16_k32(al, sh, da);
+                db = mfma_bf16_k32(ah, sl, db);
+                da = mfma_bf16_k32(am, smd, da);
+                dr = mfma_bf16_k32(row8(qr), sh, dr);
+                db = mfma_bf16_k32(am, sh, db);
+                da = mfma_bf16_k32(ah, smd, da);
+                db = mfma_bf16_k32(ah, sh, db);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) da[r] += db[r];
+        } else {
+#pragma unroll
+            for (int T = 0; T < NTILE; ++T) {
+                const float4 a4 = *(const float4 *)(sm + L::AH + l16 * L::LD + 16 * T + 4 * g);
+                const float4 r4 = *(const float4 *)(sm + L::RH + l16 * L::LD + 16 * T + 4 * g);
+                da = mfma4(a4.x, S[T][0], da); dr = mfma4(r4.x, S[T][0], dr);
+                da = mfma4(a4.y, S[T][1], da); dr = mfma4(r4.y, S[T][1], dr);
+                da = mfma4(a4.z, S[T][2], da); dr = mfma4(r4.z, S[T][2], dr);
+                da = mfma4(a4.w, S[T][3], da); dr = mfma4(r4.w, S[T][3], dr);
+            }
         }
-        if (fast) {
+        if (fast && SP) {
+            // product pm (wave pm % NW): L_ab = A^ (B^ / gamma_15)^T and L_ak
+            // from six piece products, M_rb = R^ (B^ / gamma_15)^T and M_rk
+            // (y only) from three (two pieces a side: the sums over keys
+            // cancel, so one piece a side leaves errors near 1% of y); key
+            // slots as in A^ S_0^T
+            for (int pm = wave; pm < 4; pm += NW) {
+                const uint32_t *qa = (const uint32_t *)(sm + (pm < 2 ? L::QA : L::QR)) + l16 * L::PW + 2 * g;
+                const uint32_t *qc = (const uint32_t *)(sm + ((pm & 1) ? L::QK : L::QB)) + l16 * L::PW + 2 * g;
+                f32x4 m = {0.f, 0.f, 0.f, 0.f}, m2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int P = 0; P < NTILE / 2; ++P) {
+                    auto row8 = [&](const uint32_t *q) {
+                        return cat(*(const u32x2_t *)(q + 16 * P), *(const u32x2_t *)(q + 16 * P + 8));
+                    };
+                    const u32x4_t ah = row8(qa), ch = row8(qc), am = row8(qa + 16 * L::PW),
+                                  cm = row8(qc + 16 * L::PW);
+                    if (pm < 2) {
+                        const u32x4_t al = row8(qa + 32 * L::PW), cl = row8(qc + 32 * L::PW);
+                        m = mfma_bf16_k32(al, ch, m);
+                        m2 = mfma_bf16_k32(ah, cl, m2);
+                        m = mfma_bf16_k32(am, cm, m);
+                    }
+                    m2 = mfma_bf16_k32(am, ch, m2);
+                    m = mfma_bf16_k32(ah, cm, m);
+                    m2 = mfma_bf16_k32(ah, ch, m2);
+                }
+                float *dst = sm + L::MAT + pm * 16 * L::MLD;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * g + r, s = l16;
+                    const bool keep = pm < 2 ? s < t : s <= t;
+                    dst[t * L::MLD + s] = keep ? m[r] + m2[r] : 0.f;
+                }
+            }
+        } else if (fast) {
             // product pm (wave pm % NW): rows A- (pm < 2) or R-, columns B^ (even) or K^
             for (int pm = wave; pm < 4; pm += NW) {
                 const float *lrow = sm + (pm < 2 ? L::AH : L::RH) + l16 * L::LD;
@@ -311,13 +453,26 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
         float vf[4];                                     // V[token 4 g + s][row]
 #pragma unroll
         for (int s = 0; s < 4; ++s) vf[s] = in_at(RV, 4 * g + s, row);
+        // V of bf16 streams is exact in bf16 (one piece)
+        const uint32_t vb0 = SP ? pk_bf16(vf[0], vf[1]) : 0u, vb1 = SP ? pk_bf16(vf[2], vf[3]) : 0u;
+        const u32x4_t vv = {vb0, vb1, vb0, vb1};
         {
             const float *lak = sm + L::MAT + MLAK * 16 * L::MLD + l16 * L::MLD + 4 * g;
-            const float *mrk = sm + L::MAT + MMRK * 16 * L::MLD + l16 * L::MLD + 4 * g;
+            if constexpr (SP) {
+                // L_ak V: L_ak in three pieces; element e of lane group g is
+                // token 4 g + e % 4 with piece e / 4 of the pair
+                uint32_t h0, m0, l0, h1, m1, l1;
+                split3(lak[0], lak[1], h0, m0, l0);
+                split3(lak[2], lak[3], h1, m1, l1);
+                da = mfma_bf16_k32(u32x4_t{l0, l1, 0u, 0u}, vv, da);
+                da = mfma_bf16_k32(u32x4_t{h0, h1, m0, m1}, vv, da);
+            } else {
+                const float *mrk = sm + L::MAT + MMRK * 16 * L::MLD + l16 * L::MLD + 4 * g;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                da = mfma4(lak[s], vf[s], da);
-                dr = mfma4(mrk[s], vf[s], dr);
+                for (int s = 0; s < 4; ++s) {
+                    da = mfma4(lak[s], vf[s], da);
+                    dr = mfma4(mrk[s], vf[s], dr);
+                }
             }
         }
         lds_barrier();
@@ -329,14 +484,44 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
 #pragma unroll
             for (int s = 0; s < 4; ++s) xx = mfma4(wm[s], da[s], xx);
             const float *mrb = sm + L::MAT + MMRB * 16 * L::MLD + l16 * L::MLD + 4 * g;
+            if constexpr (SP) {
+                // y only: M_rb X + M_rk V in one MFMA, one piece each
+                const float *mrk = sm + L::MAT + MMRK * 16 * L::MLD + l16 * L::MLD + 4 * g;
+                dr = mfma_bf16_k32(u32x4_t{pk_bf16(mrb[0], mrb[1]), pk_bf16(mrb[2], mrb[3]),
+                                           pk_bf16(mrk[0], mrk[1]), pk_bf16(mrk[2], mrk[3])},
+                                   u32x4_t{pk_bf16(xx[0], xx[1]), pk_bf16(xx[2], xx[3]), vb0, vb1}, dr);
+            } else {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) dr = mfma4(mrb[s], xx[s], dr);
+                for (int s = 0; s < 4; ++s) dr = mfma4(mrb[s], xx[s], dr);
+            }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 4 * g + r;
             if (t < Lc) IO<TI>::st((TI *)p.y, base + (t0 + t) * ts + row, dr[r]);
         }
+        if constexpr (SP) {
+            // X^T B^ from six piece products, V^T K^ from three (V exact):
+            // element e of lane group g is token 4 g + e % 4, piece pair e / 4
+            uint32_t xh0, xm0, xl0, xh1, xm1, xl1;
+            split3(xx[0], xx[1], xh0, xm0, xl0);
+            split3(xx[2], xx[3], xh1, xm1, xl1);
+#pragma unroll
+            for (int T = 0; T < NTILE; ++T) {
+                const float4 gm = *(const float4 *)(sm + L::GAM + 16 * T + 4 * g);
+                f32x4 acc = f32x4{S[T][0] * gm.x, S[T][1] * gm.y, S[T][2] * gm.z, S[T][3] * gm.w};
+                const uint32_t *q = (const uint32_t *)(sm + L::BK) + (16 * T + l16) * L::BKW + 2 * g;
+                const u32x2_t bh = *(const u32x2_t *)q, bm = *(const u32x2_t *)(q + 8),
+                              bl = *(const u32x2_t *)(q + 16), kh = *(const u32x2_t *)(q + 24),
+                              km = *(const u32x2_t *)(q + 32), kl = *(const u32x2_t *)(q + 40);
+                acc = mfma_bf16_k32(cat(kl, u32x2_t{0u, 0u}), vv, acc);
+                acc = mfma_bf16_k32(cat(bl, bm), u32x4_t{xh0, xh1, xm0, xm1}, acc);
+                acc = mfma_bf16_k32(cat(bm, bh), u32x4_t{xh0, xh1, xl0, xl1}, acc);
+                acc = mfma_bf16_k32(cat(kh, km), vv, acc);
+                acc = mfma_bf16_k32(cat(bh, bh), u32x4_t{xh0, xh1, xm0, xm1}, acc);
+                S[T] = acc;
+            }
+        } else
 #pragma unroll
         for (int T = 0; T < NTILE; ++T) {
             const float4 gm = *(const float4 *)(sm + L::GAM + 16 * T + 4 * g);
@@ -349,6 +534,12 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
             acc = mfma4(b4.w, xx[3], acc); acc = mfma4(k4.w, vf[3], acc);
             S[T] = acc;
         }
+        // ---- stage the next chunk behind the update's MFMAs: every read of
+        //      the staged rows came before the last barrier
+        if (c + 1 < nch) {
+            stage(c + 1);
+            if (c + 2 < nch) issue(c + 2);
+        }
     }
     if (p.s_out) {
 #pragma unroll
@@ -360,7 +551,7 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
 template <typename TI, int N>
 hipError_t launch_cf(const FwdArgs &a, hipStream_t stream) {
     const int64_t units = (int64_t)a.seg.B * a.seg.H;
-    const size_t lds = (size_t)CfLay<N>::TOTAL * sizeof(float);
+    const size_t lds = (size_t)CfLay<N, std::is_same<TI, uint16_t>::value>::TOTAL * sizeof(float);
     hipError_t e = hipFuncSetAttribute((const void *)fwd_cf_kernel<TI, N>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
