@@ -31,12 +31,13 @@
 // gfx950 FP32 MFMAs hold the SIMD's VALU while they run and bf16 MFMAs do
 // not, so the split form also lets the row and staging work overlap them.
 //
-// Per chunk, four LDS barriers: the prefix and suffix products and the
-// scaled rows (one thread per key and row kind); the dense products A^ S_0^T,
-// R^ S_0^T and the matrices; W and the right-hand sides; X, Y and the state
-// update, behind whose MFMAs the next chunk's r, w, k, a, b, v are staged in
-// LDS (fp32, w exponentiated for a log-decay input, tokens past the end as
-// identity tokens) from registers loaded one chunk earlier. At N = 128 the
+// Per chunk, three LDS barriers (four on chunks with small decays): the
+// prefix and suffix products and the scaled rows (one thread per key and row
+// kind); the dense products A^ S_0^T, R^ S_0^T and the matrices, after which
+// the wave that formed L_ab goes on to W; the right-hand sides, X, Y and the
+// state update, behind whose MFMAs the next chunk's r, w, k, a, b, v are
+// staged in LDS (fp32, w exponentiated for a log-decay input, tokens past the
+// end as identity tokens) from registers loaded one chunk earlier. At N = 128 the
 // workgroup (eight waves) uses 129 KB of LDS in split form and 111 KB
 // otherwise, one per CU; at N = 64 69 KB and 60 KB, two per CU.
 //
@@ -65,7 +66,7 @@ template <int N, bool SP> struct CfLay {
     static constexpr int TLD = 20;                       // row pitch of [N][16] key-major rows
     static constexpr int MLD = 17;                       // row pitch of 16 x 16 matrices
     static constexpr int PW = N / 2 + 2;                 // words per bf16 row of N keys
-    static constexpr int BKW = 50;                       // words per key: B^ h m l, K^ h m l (8 each)
+    static constexpr int BKW = 50;                       // words per key: per token quad B^ l h m, K^ l h m
     static constexpr int IN = 0;                         // [6][16][LD] r w k a b v
     static constexpr int RWS = SP ? 0 : 16 * LD;         // fp32 rows (fp32 layout only)
     static constexpr int AH = IN + 6 * 16 * LD;          // [16][LD] A^
@@ -119,6 +120,7 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
     constexpr bool SP = std::is_same<TI, uint16_t>::value;   // bf16 streams: split-bf16 products
     using L = CfLay<N, SP>;
     constexpr int NT = 4 * N, NW = N / 16, NTILE = N / 16;
+    constexpr int WSV = NW >= 8 ? 4 : 0;                 // the wave that forms L_ab and W
     constexpr int EPL = 16 / (int)sizeof(TI);            // elements per 16-byte load
     constexpr int GPR = N / EPL;                         // loads per row
     constexpr int LOADS = 6 * 16 * GPR / NT;             // loads per thread and chunk
@@ -149,8 +151,16 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
         }
     }
 
-    const TI *srcs[6] = {(const TI *)p.r, (const TI *)p.w, (const TI *)p.k, (const TI *)p.a, (const TI *)p.b,
-                         (const TI *)p.v};
+    // each load's stream is uniform per wave: a select over the kernel's own
+    // pointers keeps the loads global (through an array of pointers they
+    // become flat loads, which also count against the LDS wait counter)
+    const TI *sp[LOADS];
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) {
+        const int s = __builtin_amdgcn_readfirstlane((q * NT + tid) / (16 * GPR));
+        const void *vp = s == RR ? p.r : s == RW ? p.w : s == RK ? p.k : s == RA ? p.a : s == RB ? p.b : p.v;
+        sp[q] = (const TI *)vp + base;
+    }
     Ld16<TI> raw[LOADS];
     auto issue = [&](int c) {
         const int Lc = min(kChunk, u.len - c * kChunk);
@@ -158,8 +168,8 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
 #pragma unroll
         for (int q = 0; q < LOADS; ++q) {
             const int i = q * NT + tid;
-            const int s = i / (16 * GPR), e = (i / GPR) % 16, gq = i % GPR;
-            raw[q] = *(const Ld16<TI> *)(srcs[s] + base + (t0 + min(e, Lc - 1)) * ts + gq * EPL);
+            const int e = (i / GPR) % 16, gq = i % GPR;
+            raw[q] = *(const Ld16<TI> *)(sp[q] + (t0 + min(e, Lc - 1)) * ts + gq * EPL);
         }
     };
     auto stage = [&](int c) {
@@ -171,7 +181,7 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
             float x[EPL];
             unpack16(raw[q], x);
             if (s == RW) decay_of<EPL>(x, p.logw);
-            if (e >= Lc) {                               // identity token past the end
+            if (Lc < kChunk && e >= Lc) {                // identity token past the end
 #pragma unroll
                 for (int k = 0; k < EPL; ++k) x[k] = s == RW ? 1.f : 0.f;
             }
@@ -202,9 +212,14 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
         //      and the fast-chunk vote, 1: R^, 2: B^, 3: K^
         {
             const int j = tid % N, part = tid / N;
-            float wv[16];
+            // every read of the staged rows first, so that one wait covers them
+            const int src = part == 0 ? RA : part == 1 ? RR : part == 2 ? RB : RK;
+            float wv[16], xin[16];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) wv[t] = in_at(RW, t, j);
+            for (int t = 0; t < 16; ++t) {
+                wv[t] = in_at(RW, t, j);
+                xin[t] = in_at(src, t, j);
+            }
             bool ok = true;
             // SP: bf16 pieces by token, keys j and j + 1 (j even) in one word:
             // the even lane of the pair writes tokens 0..7, the odd lane
@@ -230,13 +245,13 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
                 float gm = 1.f;
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
-                    xs[t] = in_at(RA, t, j) * gm;
+                    xs[t] = xin[t] * gm;
                     if constexpr (!SP) sm[L::AH + t * L::LD + j] = xs[t];
                     gm *= wv[t];
                     ok = ok && wv[t] >= kCfFastMinW;
                 }
                 sm[L::GAM + j] = gm;
-                sm[L::IGAM + j] = 1.f / gm;
+                if constexpr (!SP) sm[L::IGAM + j] = 1.f / gm;
                 if constexpr (SP) token_pieces(xs, L::QA, std::integral_constant<int, 3>{});
             } else if (part == 1) {
                 float xs[16];
@@ -244,38 +259,38 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
                     gm *= wv[t];
-                    xs[t] = in_at(RR, t, j) * gm;
+                    xs[t] = xin[t] * gm;
                     if constexpr (!SP) sm[L::RH + t * L::LD + j] = xs[t];
                 }
                 if constexpr (SP) token_pieces(xs, L::QR, std::integral_constant<int, 2>{});
             } else {
-                const int src = part == 2 ? RB : RK;
                 float *rowm = sm + (part == 2 ? L::BH : L::KH);
                 float *keym = sm + (part == 2 ? L::BT : L::KT) + j * L::TLD;
                 float xs[16];
                 float sg = 1.f;
 #pragma unroll
                 for (int s = 15; s >= 0; --s) {
-                    xs[s] = in_at(src, s, j) * sg;
+                    xs[s] = xin[s] * sg;
                     if constexpr (!SP) rowm[s * L::LD + j] = xs[s];
                     sg *= wv[s];
                 }
                 if constexpr (SP) {
-                    // bf16 pieces by key, two tokens to a word: h, m, l at
-                    // words 0, 8, 16 (B^) or 24, 32, 40 (K^) of the key's row
+                    // bf16 pieces by key, two tokens to a word: for token quad
+                    // g, words 12 g .. 12 g + 5 hold B^'s pieces l, h, m (two
+                    // words each) and the next six K^'s
                     uint32_t ph[8], pm[8], pl[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) split3(xs[2 * i], xs[2 * i + 1], ph[i], pm[i], pl[i]);
-                    uint32_t *q = (uint32_t *)(sm + L::BK) + j * L::BKW + (part == 2 ? 0 : 24);
+                    uint32_t *q = (uint32_t *)(sm + L::BK) + j * L::BKW + (part == 2 ? 0 : 6);
 #pragma unroll
-                    for (int i = 0; i < 8; i += 2) {
-                        *(u32x2_t *)(q + i) = u32x2_t{ph[i], ph[i + 1]};
-                        *(u32x2_t *)(q + 8 + i) = u32x2_t{pm[i], pm[i + 1]};
-                        *(u32x2_t *)(q + 16 + i) = u32x2_t{pl[i], pl[i + 1]};
+                    for (int gg = 0; gg < 4; ++gg) {
+                        *(u32x2_t *)(q + 12 * gg) = u32x2_t{pl[2 * gg], pl[2 * gg + 1]};
+                        *(u32x2_t *)(q + 12 * gg + 2) = u32x2_t{ph[2 * gg], ph[2 * gg + 1]};
+                        *(u32x2_t *)(q + 12 * gg + 4) = u32x2_t{pm[2 * gg], pm[2 * gg + 1]};
                     }
                     // and by token, divided by gamma_15 (sg now), for the
                     // matrices of fast chunks (other chunks never read them)
-                    const float ig = 1.f / sg;
+                    const float ig = __builtin_amdgcn_rcpf(sg);   // within 1 ulp (read on fast chunks only)
                     float xt[16];
 #pragma unroll
                     for (int t = 0; t < 16; ++t) xt[t] = xs[t] * ig;
@@ -349,7 +364,7 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
             // (y only) from three (two pieces a side: the sums over keys
             // cancel, so one piece a side leaves errors near 1% of y); key
             // slots as in A^ S_0^T
-            for (int pm = wave; pm < 4; pm += NW) {
+            for (int pm = (wave + NW - WSV) % NW; pm < 4; pm += NW) {
                 const uint32_t *qa = (const uint32_t *)(sm + (pm < 2 ? L::QA : L::QR)) + l16 * L::PW + 2 * g;
                 const uint32_t *qc = (const uint32_t *)(sm + ((pm & 1) ? L::QK : L::QB)) + l16 * L::PW + 2 * g;
                 f32x4 m = {0.f, 0.f, 0.f, 0.f}, m2 = {0.f, 0.f, 0.f, 0.f};
@@ -380,7 +395,7 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
             }
         } else if (fast) {
             // product pm (wave pm % NW): rows A- (pm < 2) or R-, columns B^ (even) or K^
-            for (int pm = wave; pm < 4; pm += NW) {
+            for (int pm = (wave + NW - WSV) % NW; pm < 4; pm += NW) {
                 const float *lrow = sm + (pm < 2 ? L::AH : L::RH) + l16 * L::LD;
                 const float *crow = sm + ((pm & 1) ? L::KH : L::BH) + l16 * L::LD;
                 f32x4 m = {0.f, 0.f, 0.f, 0.f};
@@ -419,15 +434,17 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
                 }
                 sm[L::MAT + pm * 16 * L::MLD + t * L::MLD + s] = acc;
             }
+            lds_barrier();                               // (fast is the same on every wave)
         }
-        lds_barrier();
 
-        // ---- W = (I - L_ab)^-1 by forward substitution on wave 0: the quad
+        // ---- W = (I - L_ab)^-1 by forward substitution on the wave that
+        //      wrote L_ab on fast chunks (once its own LDS writes are done),
+        //      after the barrier on other chunks: the quad
         //      of lanes 4 c .. 4 c + 3 owns column c, lane q of it the terms
         //      s = q mod 4 of W[t][c] = [t == c] + sum_{s<t} L_ab[t][s] W[s][c],
-        //      completed by a quad sum; every wave: rhs = A^ S_0^T + L_ak V,
-        //      Y = R^ S_0^T + M_rk V
-        if (wave == 0) {
+        //      completed by a quad sum. The other waves go on to the barrier.
+        if (wave == WSV) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             const float *lab = sm + L::MAT + MLAB * 16 * L::MLD;
             const int cc = lane >> 2, qq = lane & 3;
             // L_ab[t][4 m + qq] for 4 m < t, read before the chain starts;
@@ -450,9 +467,14 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
 #pragma unroll
             for (int m = 0; m < 4; ++m) sm[L::MAT + MW * 16 * L::MLD + (4 * m + qq) * L::MLD + cc] = wq[m];
         }
+        // V is read before the barrier: after it, waves that finish early
+        // stage the next chunk over these rows
         float vf[4];                                     // V[token 4 g + s][row]
 #pragma unroll
         for (int s = 0; s < 4; ++s) vf[s] = in_at(RV, 4 * g + s, row);
+        lds_barrier();
+
+        // ---- rhs = A^ S_0^T + L_ak V (and Y += M_rk V on the fp32 layout)
         // V of bf16 streams is exact in bf16 (one piece)
         const uint32_t vb0 = SP ? pk_bf16(vf[0], vf[1]) : 0u, vb1 = SP ? pk_bf16(vf[2], vf[3]) : 0u;
         const u32x4_t vv = {vb0, vb1, vb0, vb1};
@@ -475,7 +497,6 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
                 }
             }
         }
-        lds_barrier();
 
         // ---- X = W rhs; Y += M_rb X; y out; S <- S diag(gamma_15) + X^T B^ + V^T K^
         f32x4 xx = {0.f, 0.f, 0.f, 0.f};
@@ -495,30 +516,30 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
                 for (int s = 0; s < 4; ++s) dr = mfma4(mrb[s], xx[s], dr);
             }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 4 * g + r;
-            if (t < Lc) IO<TI>::st((TI *)p.y, base + (t0 + t) * ts + row, dr[r]);
-        }
         if constexpr (SP) {
             // X^T B^ from six piece products, V^T K^ from three (V exact):
-            // element e of lane group g is token 4 g + e % 4, piece pair e / 4
+            // element e of lane group g is token 4 g + e % 4, piece pair e / 4.
+            // A key's row holds, per token quad, B^ pieces l h m then K^
+            // pieces l h m, so each A operand is one 16-byte read: (l, h)
+            // with (X_h, X_l), (h, m) with (X_h, X_h) and (X_m, X_m), and for
+            // K^ (l, h) with (V, 0), (h, m) with (V, V).
             uint32_t xh0, xm0, xl0, xh1, xm1, xl1;
             split3(xx[0], xx[1], xh0, xm0, xl0);
             split3(xx[2], xx[3], xh1, xm1, xl1);
+            const u32x4_t xhl = {xh0, xh1, xl0, xl1}, xhh = {xh0, xh1, xh0, xh1}, xmm = {xm0, xm1, xm0, xm1},
+                          v0 = {vb0, vb1, 0u, 0u};
 #pragma unroll
             for (int T = 0; T < NTILE; ++T) {
                 const float4 gm = *(const float4 *)(sm + L::GAM + 16 * T + 4 * g);
                 f32x4 acc = f32x4{S[T][0] * gm.x, S[T][1] * gm.y, S[T][2] * gm.z, S[T][3] * gm.w};
-                const uint32_t *q = (const uint32_t *)(sm + L::BK) + (16 * T + l16) * L::BKW + 2 * g;
-                const u32x2_t bh = *(const u32x2_t *)q, bm = *(const u32x2_t *)(q + 8),
-                              bl = *(const u32x2_t *)(q + 16), kh = *(const u32x2_t *)(q + 24),
-                              km = *(const u32x2_t *)(q + 32), kl = *(const u32x2_t *)(q + 40);
-                acc = mfma_bf16_k32(cat(kl, u32x2_t{0u, 0u}), vv, acc);
-                acc = mfma_bf16_k32(cat(bl, bm), u32x4_t{xh0, xh1, xm0, xm1}, acc);
-                acc = mfma_bf16_k32(cat(bm, bh), u32x4_t{xh0, xh1, xl0, xl1}, acc);
-                acc = mfma_bf16_k32(cat(kh, km), vv, acc);
-                acc = mfma_bf16_k32(cat(bh, bh), u32x4_t{xh0, xh1, xm0, xm1}, acc);
+                const uint32_t *q = (const uint32_t *)(sm + L::BK) + (16 * T + l16) * L::BKW + 12 * g;
+                const u32x4_t blh = *(const u32x4a8_t *)q, bhm = *(const u32x4a8_t *)(q + 2),
+                              klh = *(const u32x4a8_t *)(q + 6), khm = *(const u32x4a8_t *)(q + 8);
+                acc = mfma_bf16_k32(klh, v0, acc);
+                acc = mfma_bf16_k32(blh, xhl, acc);
+                acc = mfma_bf16_k32(bhm, xmm, acc);
+                acc = mfma_bf16_k32(khm, vv, acc);
+                acc = mfma_bf16_k32(bhm, xhh, acc);
                 S[T] = acc;
             }
         } else
@@ -535,11 +556,18 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
             S[T] = acc;
         }
         // ---- stage the next chunk behind the update's MFMAs: every read of
-        //      the staged rows came before the last barrier
-        if (c + 1 < nch) {
-            stage(c + 1);
-            if (c + 2 < nch) issue(c + 2);
+        //      the staged rows came before the last barrier. y leaves after
+        //      the staging has waited for its loads: loads and stores share
+        //      one wait counter, so stores issued before that wait would hold
+        //      it until they are acknowledged.
+        if (c + 1 < nch) stage(c + 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * g + r;
+            if (t < Lc) IO<TI>::st((TI *)p.y, base + (t0 + t) * ts + row, dr[r]);
         }
+        __builtin_amdgcn_sched_barrier(0);               // the stores stay ahead of the loads
+        if (c + 2 < nch) issue(c + 2);
     }
     if (p.s_out) {
 #pragma unroll

@@ -26,6 +26,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+// four words at an 8-byte (not 16-byte) aligned LDS address
+typedef uint32_t u32x4a8_t __attribute__((ext_vector_type(4), aligned(8)));
 
 __device__ __forceinline__ f32x4 mfma_bf16_k32(u32x4_t a, u32x4_t b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
