@@ -271,7 +271,10 @@ __global__ __launch_bounds__(kWThreads, 1) void bwd128_kernel(BwdArgs p, int32_t
         __syncthreads();
         // the 16 waves' partial sums: thread f < 640 owns gradient f / 128 of key f % 128
         if (tid < NGRAD * kWN) {
-            const int g = tid >> 7, j = tid & 127;
+            // g is uniform per wave: a scalar select of the output pointer (a
+            // per-lane one loads it from the argument block with a vector
+            // load, whose wait would also wait for every store in flight)
+            const int g = __builtin_amdgcn_readfirstlane(tid >> 7), j = tid & 127;
             const float *q = sm + L_PART + buf * 16 * kPartWave + part_slot(grad_value(g, j & 3), j >> 2);
             float x = 0.f;
 #pragma unroll
