@@ -651,10 +651,12 @@ KERNEL_LABELS = {
     "decode_kernel": "WKV-7 decode step",
     "decode128_kernel": "WKV-7 decode step, head size 128",
     "fwd128_kernel": "WKV-7 forward, head size 128 (token order)",
+    "fwd_cf_kernel": "WKV-7 forward, head size 128 (chunk form, split-bf16 MFMA for bf16 streams)",
     "bwd128_kernel": "WKV-7 backward, head size 128 (token order, one workgroup per unit)",
     "gdn_decode_kernel": "gated DeltaNet decode step",
     "gdn_norm_kernel": "gated DeltaNet prefill: q^, k^ pre-pass",
-    "gdn_fwd_kernel": "gated DeltaNet prefill: recurrence",
+    "gdn_fwd_kernel": "gated DeltaNet prefill: recurrence (token order; fp32 and fp16 I/O)",
+    "gdn_cf_kernel": "gated DeltaNet prefill: recurrence in chunk form (bf16 I/O, split-bf16 MFMA)",
     "gdn_remap_kernel": "gated DeltaNet backward: remapped fp32 streams",
     "gdn_pull_value_kernel": "gated DeltaNet backward: dg, dbeta, dv",
     "gdn_pull_key_kernel": "gated DeltaNet backward: dq, dk through the normalisation",

@@ -207,6 +207,8 @@ hipError_t launch_typed_n(const GdnFwdArgs &a, hipStream_t stream) {
                        (const TI *)a.q, (const TI *)a.k, a.qn, a.kn, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // bf16 I/O: the chunk form on split-bf16 MFMA; other types token by token
+    if constexpr (std::is_same<TI, uint16_t>::value) return launch_gdn_forward_cf(a, stream);
     hipLaunchKernelGGL((gdn_fwd_kernel<TI, N>), dim3((unsigned)((int64_t)a.B * a.H)), dim3(2 * N), 0, stream,
                        a.T, a.H, a.Hk, (const float *)a.qn, (const float *)a.kn, (const TI *)a.v, a.g, a.beta,
                        a.s0, (TI *)a.out, a.s_out);

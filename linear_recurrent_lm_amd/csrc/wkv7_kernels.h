@@ -97,6 +97,9 @@ struct GdnFwdArgs {
     float *qn, *kn;                  // workspace: q^, k^ in fp32, [B][T][Hk][N] each
 };
 hipError_t launch_gdn_forward(const GdnFwdArgs &a, hipStream_t stream);
+// The recurrence of a bf16 GDN prefill in chunk form, after the q^, k^
+// pre-pass (qn, kn filled).
+hipError_t launch_gdn_forward_cf(const GdnFwdArgs &a, hipStream_t stream);
 // q^, k^ of wkv7_gdn_forward's pre-pass, for `rows` token rows of N.
 hipError_t launch_gdn_normalize(int dtype, int N, const void *q, const void *k, float *qn, float *kn,
                                 int64_t rows, hipStream_t stream);

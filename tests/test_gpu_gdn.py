@@ -146,35 +146,39 @@ def test_gdn_forward_prefill_sampled(W):
 
 
 @pytest.mark.parametrize("N", [128, 64])
-def test_gdn_forward_strong_and_zero_decay(W, N):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gdn_forward_strong_and_zero_decay(W, N, dtype):
     """Decays that drive the running decay product below 2^-60 within a few
     tokens (g = -30 at tokens 3..6), an exact zero decay (g = -inf at token
-    11) and mild decays elsewhere: the prefill keeps its state divided by
-    that product and folds it back before it gets that small, and out and the
-    final state still match the oracle."""
-    inp = synth.make_gdn_sequence(2, 24, 4, 2, N, seed=59, dtype="f32", s0_std=0.1)
+    11) and mild decays elsewhere. fp32 I/O runs token by token with the
+    state divided by that product and folded back before it gets that small;
+    bf16 I/O runs the chunk form, whose pair decays are products of e^g (zero
+    included). out and the final state still match the oracle."""
+    inp = synth.make_gdn_sequence(2, 40, 4, 2, N, seed=59, dtype=dtype, s0_std=0.1)
     inp.g[:, 3:7] = -30.0
     inp.g[:, 11] = -np.inf
-    out, s_out = run_seq(W, inp, "f32")
+    inp.g[:, 20:22] = -30.0
+    out, s_out = run_seq(W, inp, dtype)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(s_out))
     ro, rs = O.gdn_forward(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.s0)
-    assert U.unit_err_dense(out, ro) <= U.TOL_F32
+    assert U.unit_err_dense(out, ro) <= TOL[dtype]
     assert U.unit_err_state(s_out, rs) <= U.TOL_F32
 
 
 @pytest.mark.parametrize("N", [128, 64])
-def test_gdn_zero_q_and_k_rows(W, N):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gdn_zero_q_and_k_rows(W, N, dtype):
     """All-zero k (token 5) and all-zero q (token 9) rows in the middle of a
     sequence, as padding or masked tokens give: the state stays finite, a zero
     k only decays it, a zero q outputs zero; the decode step agrees."""
     import torch
-    inp = synth.make_gdn_sequence(2, 16, 4, 2, N, seed=57, dtype="f32", s0_std=0.1)
+    inp = synth.make_gdn_sequence(2, 16, 4, 2, N, seed=57, dtype=dtype, s0_std=0.1)
     inp.k[:, 5] = 0.0
     inp.q[:, 9] = 0.0
-    out, s_out = run_seq(W, inp, "f32")
+    out, s_out = run_seq(W, inp, dtype)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(s_out))
     ro, rs = O.gdn_forward(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.s0)
-    assert U.unit_err_dense(out, ro) <= U.TOL_F32
+    assert U.unit_err_dense(out, ro) <= TOL[dtype]
     assert U.unit_err_state(s_out, rs) <= U.TOL_F32
     assert np.max(np.abs(out[:, 9])) == 0.0
     dec = synth.make_gdn_inputs(2, 4, 2, N, seed=58, dtype="f32")
