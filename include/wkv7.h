@@ -285,6 +285,8 @@ wkv7_status wkv7_gdn_workspace_bytes(int32_t B, int32_t T, int32_t Hk, int32_t N
  *   s_out  : fp32 [B, H, N, N] final state, or NULL.
  *   workspace : >= wkv7_gdn_workspace_bytes(B, T, Hk, N), 16-byte aligned.
  * Value head h reads key head h / (H / Hk). H % Hk == 0 and B*H <= 2^24.
+ * bf16 I/O evaluates the recurrence 16 tokens at a time in its chunk form
+ * (products in three bf16 pieces, fp32 state); fp32 and fp16 token by token.
  * Outputs may not overlap inputs, each other or the workspace.
  */
 wkv7_status wkv7_gdn_forward(int32_t B, int32_t T, int32_t H, int32_t Hk, int32_t N, int32_t dtype,
