@@ -91,11 +91,46 @@ enum { ZA1 = 0, ZB1, ZA2, ZB2 };             // pair products: dA_rows, dB_rows 
 // (rows 12..15); block column parts (b db + k dk) of R = 8 (0..7) and R = 4 / 12 (0..3, 8..11)
 enum { UCHA = 0, UCHR, UCHC, UR12A, UR12R, UR3A, UR3R, UC2, UC13, kUTerms };
 
+// Products for bf16 streams (SPL): both operands in two bf16 pieces, three
+// piece products (h h, h l, l h) on v_mfma_f32_16x16x32_bf16 with fp32
+// accumulation, which leaves the VALU free while they run (FP32 MFMAs hold
+// it). A K = 32 step gives lane group kq the 8 contraction indices
+// k0 + 16 (e / 4) + 4 kq + e % 4, so the output layout is the FP32 one.
+__device__ __forceinline__ f32x4 mm_pieces(f32x4 acc, const float (&a)[8], const float (&b)[8]) {
+    uint32_t ah[4], al[4], bh[4], bl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        split2(a[2 * i], a[2 * i + 1], ah[i], al[i]);
+        split2(b[2 * i], b[2 * i + 1], bh[i], bl[i]);
+    }
+    const u32x4_t Ah = {ah[0], ah[1], ah[2], ah[3]}, Al = {al[0], al[1], al[2], al[3]};
+    const u32x4_t Bh = {bh[0], bh[1], bh[2], bh[3]}, Bl = {bl[0], bl[1], bl[2], bl[3]};
+    f32x4 lo = mfma_bf16_k32(Al, Bh, f32x4{0.f, 0.f, 0.f, 0.f});
+    lo = mfma_bf16_k32(Ah, Bl, lo);
+    acc = mfma_bf16_k32(Ah, Bh, acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] += lo[r];
+    return acc;
+}
+
 // acc[m][n] += sum_k A[m][k] B[k][n] with A row-major (pitch lda) and B given
 // transposed, Bt[n][k] row-major (pitch ldb): both operands 16-byte loads.
-template <int KDIM>
+template <int KDIM, bool SPL = false>
 __device__ __forceinline__ f32x4 mm_AtBt(f32x4 acc, const float *A, int lda, const float *Bt, int ldb,
                                          int l16, int kq) {
+    if constexpr (SPL && KDIM % 32 == 0) {
+#pragma unroll
+        for (int k0 = 0; k0 < KDIM; k0 += 32) {
+            const float4 a0 = *(const float4 *)(A + l16 * lda + k0 + 4 * kq);
+            const float4 a1 = *(const float4 *)(A + l16 * lda + k0 + 16 + 4 * kq);
+            const float4 b0 = *(const float4 *)(Bt + l16 * ldb + k0 + 4 * kq);
+            const float4 b1 = *(const float4 *)(Bt + l16 * ldb + k0 + 16 + 4 * kq);
+            const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            acc = mm_pieces(acc, a, b);
+        }
+        return acc;
+    }
 #pragma unroll
     for (int k0 = 0; k0 < KDIM; k0 += 16) {
         const float4 a = *(const float4 *)(A + l16 * lda + k0 + 4 * kq);
@@ -108,9 +143,22 @@ __device__ __forceinline__ f32x4 mm_AtBt(f32x4 acc, const float *A, int lda, con
 
 // acc += A B with A row-major (16-byte loads along k) and B row-major [k][n]
 // (scalar loads; consecutive lanes read consecutive n).
-template <int KDIM>
+template <int KDIM, bool SPL = false>
 __device__ __forceinline__ f32x4 mm_AtB(f32x4 acc, const float *A, int lda, const float *B, int ldb,
                                         int l16, int kq) {
+    if constexpr (SPL && KDIM % 32 == 0) {
+#pragma unroll
+        for (int k0 = 0; k0 < KDIM; k0 += 32) {
+            const float4 a0 = *(const float4 *)(A + l16 * lda + k0 + 4 * kq);
+            const float4 a1 = *(const float4 *)(A + l16 * lda + k0 + 16 + 4 * kq);
+            const float *bp = B + (k0 + 4 * kq) * ldb + l16;
+            const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const float b[8] = {bp[0], bp[ldb], bp[2 * ldb], bp[3 * ldb],
+                                bp[16 * ldb], bp[17 * ldb], bp[18 * ldb], bp[19 * ldb]};
+            acc = mm_pieces(acc, a, b);
+        }
+        return acc;
+    }
 #pragma unroll
     for (int k0 = 0; k0 < KDIM; k0 += 16) {
         const float4 a = *(const float4 *)(A + l16 * lda + k0 + 4 * kq);
@@ -220,6 +268,9 @@ __global__ __launch_bounds__(1024) void group_list_kernel(SegParams seg, int32_t
 
 template <typename TI>
 __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32_t units) {
+    // bf16 streams: the K = 64 products in two bf16 pieces (gradients within
+    // about 2^-16 of the FP32 products; the bf16 gradient bound is 5e-2)
+    constexpr bool kSplitBwd = std::is_same<TI, uint16_t>::value;
     extern __shared__ __align__(16) float sm[];
     // Workgroup -> (unit, group of kChunksPerGroup chunks): dense rows by
     // workgroup index, segment mode through the pre-pass's work list.
@@ -520,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             const int jc = 16 * w4;
             const bool isR = wave < 12;
             f32x4 g = {0.f, 0.f, 0.f, 0.f};
-            g = mm_AtB<64>(g, isR ? sDY : sV, LD, (isR ? s_S0 : s_DS) + jc, LD, l16, kq);
+            g = mm_AtB<64, kSplitBwd>(g, isR ? sDY : sV, LD, (isR ? s_S0 : s_DS) + jc, LD, l16, kq);
             float *dst = s_G + (isR ? 1 : 3) * 16 * LD + jc + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = g[r];
@@ -534,7 +585,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         //      16 (w-10)..; wave 14: dM_rk = dY V^T
         f32x4 pa = {0.f, 0.f, 0.f, 0.f};            // waves 0-3 (then rhs, X)
         if (wave < 4) {
-            pa = mm_AtBt<64>(pa, s_Q, LD, s_S0 + 16 * w4 * LD, LD, l16, kq);
+            pa = mm_AtBt<64, kSplitBwd>(pa, s_Q, LD, s_S0 + 16 * w4 * LD, LD, l16, kq);
         } else if (wave < 6) {
             // the tile index is made a compile-time constant so that the
             // scatter's index map folds
@@ -550,7 +601,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                     arow = s_AR + ((m & 4) ? 16 + m : 4 + m) * LD;
                     brow = s_BL + (16 + l16) * LD;
                 }
-                const f32x4 d = rows_product(arow, brow, kq);
+                const f32x4 d = kSplitBwd ? mm_AtBt<64, true>(f32x4{0.f, 0.f, 0.f, 0.f}, arow, 0, brow, 0, 0, kq)
+                                          : rows_product(arow, brow, kq);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const TileEntry e = tile_entry(tile, 4 * kq + r, l16);
@@ -601,7 +653,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             s_dgC[(wave - 10) * 64 + j] = acc0 + acc1;
         } else if (wave == 14) {
             f32x4 gm = {0.f, 0.f, 0.f, 0.f};
-            gm = mm_AtBt<64>(gm, sDY, LD, sV, LD, l16, kq);
+            gm = mm_AtBt<64, kSplitBwd>(gm, sDY, LD, sV, LD, l16, kq);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * kq + r;
@@ -631,7 +683,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = o[r];
         } else if (wave < 8) {
             const int i0 = 16 * w4;
-            dvp = mm_AtBt<64>(dvp, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq);
+            dvp = mm_AtBt<64, kSplitBwd>(dvp, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq);
             dvp = mm_TB(dvp, Mmrk, 16, sDY + i0, LD, l16, kq);
         } else if (wide && c < c_hi - 1) {
             flush_wide(c + 1);
@@ -649,7 +701,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             const float *lhs = mi < 2 ? s_DR : sDY;
             const float *rt = mi == 1 ? sV : s_X;
             f32x4 gm = {0.f, 0.f, 0.f, 0.f};
-            gm = mm_AtBt<64>(gm, lhs, LD, rt, LD, l16, kq);
+            gm = mm_AtBt<64, kSplitBwd>(gm, lhs, LD, rt, LD, l16, kq);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * kq + r;
@@ -675,7 +727,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         } else if (wave < 4) {
             const int jc = 16 * w4;
             f32x4 g = {0.f, 0.f, 0.f, 0.f};
-            g = mm_AtB<64>(g, s_DR, LD, s_S0 + jc, LD, l16, kq);
+            g = mm_AtB<64, kSplitBwd>(g, s_DR, LD, s_S0 + jc, LD, l16, kq);
             float *dst = s_G + jc + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = g[r];
@@ -732,7 +784,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             if (wave < 12) {          // dB^ = X dS_C (key columns 16 (w & 3)..)
                 const int jc = 16 * w4;
                 f32x4 g = {0.f, 0.f, 0.f, 0.f};
-                g = mm_AtB<64>(g, s_X, LD, s_DS + jc, LD, l16, kq);
+                g = mm_AtB<64, kSplitBwd>(g, s_X, LD, s_DS + jc, LD, l16, kq);
                 float *dst = s_G + 2 * 16 * LD + jc + l16;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = g[r];

@@ -59,6 +59,14 @@ __device__ __forceinline__ void split3(float x0, float x1, uint32_t &h, uint32_t
     l = pk_bf16(x0, x1);
 }
 
+// Two-piece bf16 split of two fp32 values, x = h + l: h is x rounded to bf16,
+// l the remainder rounded to bf16, so |x - h - l| <= 2^-18 |x|. The products
+// h_a h_b + h_a l_b + l_a h_b then reproduce a b to about 2^-16 |a b|.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t &h, uint32_t &l) {
+    h = pk_bf16(x0, x1);
+    l = pk_bf16(x0 - bf_lo(h), x1 - bf_hi(h));
+}
+
 // 16x16 product over K = 64: D[m][n] = sum_j A_m[j] B_n[j], where this lane
 // supplies row m = lane % 16 of A (arow) and row n = lane % 16 of B (brow),
 // both 16-byte aligned rows of 64 floats.
