@@ -650,7 +650,6 @@ KERNEL_LABELS = {
     "zero_uncovered_kernel": "segment mode: zeros at uncovered tokens",
     "decode_kernel": "WKV-7 decode step",
     "decode128_kernel": "WKV-7 decode step, head size 128",
-    "fwd128_kernel": "WKV-7 forward, head size 128 (token order)",
     "fwd_cf_kernel": "WKV-7 forward, head size 128 (chunk form, split-bf16 MFMA for bf16 streams)",
     "bwd128_kernel": "WKV-7 backward, head size 128 (token order, one workgroup per unit)",
     "gdn_decode_kernel": "gated DeltaNet decode step",

@@ -316,11 +316,11 @@ wkv7_status wkv7_forward(const wkv7_desc *d, const void *r, const void *w, const
         if (wkv7::launch_zero_uncovered(zs, d->dtype, outs, 1, hs) != hipSuccess)
             return WKV7_ERR_HIP;
     }
-    // head size 128: the lean chunk form for dense batches, token order for
-    // segment tables; head size 64: the warp-specialised chunk form
+    // head size 128: the lean chunk form; head size 64: the warp-specialised
+    // chunk form
     hipError_t e;
     if (d->N == 128)
-        e = d->num_seqs == 0 ? wkv7::launch_forward_cf(args, 128, hs) : wkv7::launch_forward128(args, hs);
+        e = wkv7::launch_forward_cf(args, 128, hs);
     else
         e = wkv7::launch_forward(args, hs);
     if (e != hipSuccess) return WKV7_ERR_HIP;

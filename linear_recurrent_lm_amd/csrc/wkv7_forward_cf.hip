@@ -1,6 +1,7 @@
 // WKV-7 forward in chunk form (C = 16) on MFMA, one lean workgroup per
 // (sequence, head): N / 16 waves, wave w holding value rows 16 w .. 16 w + 15
-// of the state in MFMA accumulators. Dense batches only.
+// of the state in MFMA accumulators. Dense batches, or one workgroup per
+// (sequence of a segment table, head).
 //
 // For a chunk with entering state S_0, gamma_t = prod_{u<=t} w_u (per key),
 // sigma_s = prod_{u>s} w_u and x_t = S_{t-1} a_t, the recurrence
@@ -578,7 +579,7 @@ __global__ __launch_bounds__(4 * N) void fwd_cf_kernel(FwdArgs p, int32_t units)
 
 template <typename TI, int N>
 hipError_t launch_cf(const FwdArgs &a, hipStream_t stream) {
-    const int64_t units = (int64_t)a.seg.B * a.seg.H;
+    const int64_t units = (int64_t)(a.seg.num_seqs > 0 ? a.seg.num_seqs : a.seg.B) * a.seg.H;
     const size_t lds = (size_t)CfLay<N, std::is_same<TI, uint16_t>::value>::TOTAL * sizeof(float);
     hipError_t e = hipFuncSetAttribute((const void *)fwd_cf_kernel<TI, N>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -79,9 +79,8 @@ struct GdnArgs {
     void *out;                       // [B][H][N], I/O type
 };
 hipError_t launch_gdn_decode(const GdnArgs &a, hipStream_t stream);
-// The WKV-7 forward at head size 128 (FwdArgs as for 64; token order).
-hipError_t launch_forward128(const FwdArgs &a, hipStream_t stream);
-// The lean chunk-form forward (dense batches; head size n = 64 or 128).
+// The lean chunk-form forward (dense batches or segment tables; head size n
+// = 64 or 128).
 hipError_t launch_forward_cf(const FwdArgs &a, int n, hipStream_t stream);
 
 // A sequence of GDN tokens through the remap (dense batch, no checkpoints).
