@@ -678,10 +678,19 @@ wkv7_status wkv7_gdn_backward(int32_t B, int32_t T, int32_t H, int32_t Hk, int32
     if (wkv7::launch_gdn_remap(a, hs) != hipSuccess) return WKV7_ERR_HIP;
     wkv7_desc d{};
     d.B = B; d.T = T; d.H = H; d.N = N; d.dtype = WKV7_F32; d.grad_f32 = 1;
-    // the forward for the checkpoints; its y goes to dr's part, which the
-    // backward overwrites
-    if ((st = wkv7_forward(&d, a.r, a.w, a.kw, a.v32, a.a, a.b, s0, gr, nullptr, ckpt, stream)) != WKV7_OK)
-        return st;
+    if (dtype == WKV7_BF16) {
+        // the checkpoints from the GDN chunk form on q^, k^ (remap's pre-pass)
+        // and the bf16 v: the same states as the remapped WKV-7 forward's
+        wkv7::GdnFwdArgs f{};
+        f.B = B; f.T = T; f.H = H; f.Hk = Hk; f.N = N; f.dtype = dtype;
+        f.v = v; f.g = g; f.beta = beta; f.s0 = s0; f.qn = a.qn; f.kn = a.kn; f.ckpt = ckpt;
+        if (wkv7::launch_gdn_forward_cf(f, hs) != hipSuccess) return WKV7_ERR_HIP;
+    } else {
+        // the forward for the checkpoints; its y goes to dr's part, which the
+        // backward overwrites
+        if ((st = wkv7_forward(&d, a.r, a.w, a.kw, a.v32, a.a, a.b, s0, gr, nullptr, ckpt, stream)) != WKV7_OK)
+            return st;
+    }
     if ((st = wkv7_backward(&d, a.r, a.w, a.kw, a.v32, a.a, a.b, ckpt, dout ? a.dy : nullptr, ds_out, gr, gw,
                             gk, gv, ga, gb, ds0, wkv_ws, l.wkv, stream)) != WKV7_OK)
         return st;

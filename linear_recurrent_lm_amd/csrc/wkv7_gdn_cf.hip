@@ -37,7 +37,8 @@
 // sides, X, Y and the update, behind whose MFMAs the next chunk's q^, k^, v,
 // e^g and beta are staged (tokens past the end as identity tokens: q^ = k^ =
 // v = 0, e^g = 1, beta = 0). The workgroup uses 73 KB of LDS at N = 128 and
-// 40 KB at N = 64.
+// 40 KB at N = 64. Optionally the state entering each chunk is stored (the
+// checkpoints of the GDN backward) and the output skipped.
 #include "wkv7_kernels.h"
 #include "wkv7_mfma.h"
 
@@ -70,7 +71,8 @@ __global__ __launch_bounds__(4 * N) void gdn_cf_kernel(int32_t T, int32_t H, int
                                                   const float *__restrict__ qn, const float *__restrict__ kn,
                                                   const uint16_t *__restrict__ v, const float *__restrict__ gg,
                                                   const float *__restrict__ beta, const float *__restrict__ s0,
-                                                  uint16_t *__restrict__ out, float *__restrict__ s_out) {
+                                                  uint16_t *__restrict__ out, float *__restrict__ s_out,
+                                                  float *__restrict__ ckpt) {
     using L = GcLay<N>;
     constexpr int NW = N / 16, NTILE = N / 16;
     constexpr int WKK = NW >= 8 ? 4 : 0;                 // forms k^ k^T, L_ab, L_ak and W
@@ -164,6 +166,12 @@ __global__ __launch_bounds__(4 * N) void gdn_cf_kernel(int32_t T, int32_t H, int
     for (int c = 0; c < nch; ++c) {
         const int Lc = min(kChunk, T - c * kChunk);
         const int64_t t0 = (int64_t)c * kChunk;
+        // the state entering the chunk is its checkpoint (slot b * nch + c)
+        if (ckpt) {
+            float *ck = ckpt + ((b * nch + c) * H + h) * (int64_t)(N * N) + (int64_t)row * N + 4 * g;
+#pragma unroll
+            for (int TT = 0; TT < NTILE; ++TT) *(float4 *)(ck + 16 * TT) = make_float4(S[TT][0], S[TT][1], S[TT][2], S[TT][3]);
+        }
         lds_barrier();                                   // chunk staged; the previous chunk done with LDS
         // ---- scaled rows of key j; part 0: A^ and gamma_15, 1: R^, 2: B^, 3: K^
         {
@@ -406,7 +414,7 @@ __global__ __launch_bounds__(4 * N) void gdn_cf_kernel(int32_t T, int32_t H, int
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 4 * g + r;
-            if (t < Lc) IO<uint16_t>::st(out, ((b * T + t0 + t) * H + h) * N + row, dr[r] * scale);
+            if (out && t < Lc) IO<uint16_t>::st(out, ((b * T + t0 + t) * H + h) * N + row, dr[r] * scale);
         }
         __builtin_amdgcn_sched_barrier(0);               // the stores stay ahead of the loads
         if (c + 2 < nch) issue(c + 2);
@@ -427,7 +435,7 @@ hipError_t launch_n(const GdnFwdArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gdn_cf_kernel<N>), dim3((unsigned)((int64_t)a.B * a.H)), dim3(4 * N), lds, stream, a.T, a.H,
                        a.Hk, (const float *)a.qn, (const float *)a.kn, (const uint16_t *)a.v, a.g, a.beta, a.s0,
-                       (uint16_t *)a.out, a.s_out);
+                       (uint16_t *)a.out, a.s_out, a.ckpt);
     return hipGetLastError();
 }
 

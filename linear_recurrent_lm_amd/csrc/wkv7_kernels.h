@@ -94,6 +94,8 @@ struct GdnFwdArgs {
     void *out;                       // [B][T][H][N], I/O type
     float *s_out;                    // [B][H][N][N] or null
     float *qn, *kn;                  // workspace: q^, k^ in fp32, [B][T][Hk][N] each
+    float *ckpt;                     // chunk form only: [B * ceil(T / 16)][H][N][N], the state
+                                     // entering each 16-token chunk, or null
 };
 hipError_t launch_gdn_forward(const GdnFwdArgs &a, hipStream_t stream);
 // The recurrence of a bf16 GDN prefill in chunk form, after the q^, k^
