@@ -95,18 +95,24 @@ enum { UCHA = 0, UCHR, UCHC, UR12A, UR12R, UR3A, UR3R, UC2, UC13, kUTerms };
 // piece products (h h, h l, l h) on v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation, which leaves the VALU free while they run (FP32 MFMAs hold
 // it). A K = 32 step gives lane group kq the 8 contraction indices
-// k0 + 16 (e / 4) + 4 kq + e % 4, so the output layout is the FP32 one.
+// k0 + 16 (e / 4) + 4 kq + e % 4, so the output layout is the FP32 one. An
+// operand that holds bf16 values (v, dy: AX, BX) is its own high piece, and
+// its low piece and that piece's product are skipped.
+template <bool AX, bool BX>
 __device__ __forceinline__ f32x4 mm_pieces(f32x4 acc, const float (&a)[8], const float (&b)[8]) {
     uint32_t ah[4], al[4], bh[4], bl[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        split2(a[2 * i], a[2 * i + 1], ah[i], al[i]);
-        split2(b[2 * i], b[2 * i + 1], bh[i], bl[i]);
+        if constexpr (AX) ah[i] = pk_bf16(a[2 * i], a[2 * i + 1]);
+        else split2(a[2 * i], a[2 * i + 1], ah[i], al[i]);
+        if constexpr (BX) bh[i] = pk_bf16(b[2 * i], b[2 * i + 1]);
+        else split2(b[2 * i], b[2 * i + 1], bh[i], bl[i]);
     }
-    const u32x4_t Ah = {ah[0], ah[1], ah[2], ah[3]}, Al = {al[0], al[1], al[2], al[3]};
-    const u32x4_t Bh = {bh[0], bh[1], bh[2], bh[3]}, Bl = {bl[0], bl[1], bl[2], bl[3]};
-    f32x4 lo = mfma_bf16_k32(Al, Bh, f32x4{0.f, 0.f, 0.f, 0.f});
-    lo = mfma_bf16_k32(Ah, Bl, lo);
+    const u32x4_t Ah = {ah[0], ah[1], ah[2], ah[3]}, Bh = {bh[0], bh[1], bh[2], bh[3]};
+    if constexpr (AX && BX) return mfma_bf16_k32(Ah, Bh, acc);
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!AX) lo = mfma_bf16_k32(u32x4_t{al[0], al[1], al[2], al[3]}, Bh, lo);
+    if constexpr (!BX) lo = mfma_bf16_k32(Ah, u32x4_t{bl[0], bl[1], bl[2], bl[3]}, lo);
     acc = mfma_bf16_k32(Ah, Bh, acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] += lo[r];
@@ -115,7 +121,7 @@ __device__ __forceinline__ f32x4 mm_pieces(f32x4 acc, const float (&a)[8], const
 
 // acc[m][n] += sum_k A[m][k] B[k][n] with A row-major (pitch lda) and B given
 // transposed, Bt[n][k] row-major (pitch ldb): both operands 16-byte loads.
-template <int KDIM, bool SPL = false>
+template <int KDIM, bool SPL = false, bool AX = false, bool BX = false>
 __device__ __forceinline__ f32x4 mm_AtBt(f32x4 acc, const float *A, int lda, const float *Bt, int ldb,
                                          int l16, int kq) {
     if constexpr (SPL && KDIM % 32 == 0) {
@@ -127,7 +133,7 @@ __device__ __forceinline__ f32x4 mm_AtBt(f32x4 acc, const float *A, int lda, con
             const float4 b1 = *(const float4 *)(Bt + l16 * ldb + k0 + 16 + 4 * kq);
             const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
             const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-            acc = mm_pieces(acc, a, b);
+            acc = mm_pieces<AX, BX>(acc, a, b);
         }
         return acc;
     }
@@ -143,7 +149,7 @@ __device__ __forceinline__ f32x4 mm_AtBt(f32x4 acc, const float *A, int lda, con
 
 // acc += A B with A row-major (16-byte loads along k) and B row-major [k][n]
 // (scalar loads; consecutive lanes read consecutive n).
-template <int KDIM, bool SPL = false>
+template <int KDIM, bool SPL = false, bool AX = false, bool BX = false>
 __device__ __forceinline__ f32x4 mm_AtB(f32x4 acc, const float *A, int lda, const float *B, int ldb,
                                         int l16, int kq) {
     if constexpr (SPL && KDIM % 32 == 0) {
@@ -155,7 +161,7 @@ __device__ __forceinline__ f32x4 mm_AtB(f32x4 acc, const float *A, int lda, cons
             const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
             const float b[8] = {bp[0], bp[ldb], bp[2 * ldb], bp[3 * ldb],
                                 bp[16 * ldb], bp[17 * ldb], bp[18 * ldb], bp[19 * ldb]};
-            acc = mm_pieces(acc, a, b);
+            acc = mm_pieces<AX, BX>(acc, a, b);
         }
         return acc;
     }
@@ -176,6 +182,17 @@ template <> __device__ __forceinline__ uint16_t out_bits<_Float16>(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 template <> __device__ __forceinline__ uint16_t out_bits<float>(float) { return 0; }   // not used
+
+// acc += sum over 16 indices k = 4 kq + e of a[e] b[e] (this lane's values),
+// with a in two bf16 pieces and b holding bf16 values: one K = 32 MFMA whose
+// element e of lane group kq is index 4 kq + e % 4, piece e / 4 of a.
+__device__ __forceinline__ f32x4 mm_k16_bx(f32x4 acc, const float (&a)[4], const float (&b)[4]) {
+    uint32_t h0, l0, h1, l1;
+    split2(a[0], a[1], h0, l0);
+    split2(a[2], a[3], h1, l1);
+    const uint32_t b0 = pk_bf16(b[0], b[1]), b1 = pk_bf16(b[2], b[3]);
+    return mfma_bf16_k32(u32x4_t{h0, h1, l0, l1}, u32x4_t{b0, b1, b0, b1}, acc);
+}
 
 // acc += A^T B for A = [k][m], B = [k][n] row-major with 16 rows k.
 __device__ __forceinline__ f32x4 mm_TB(f32x4 acc, const float *A, int lda, const float *B, int ldb,
@@ -571,7 +588,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             const int jc = 16 * w4;
             const bool isR = wave < 12;
             f32x4 g = {0.f, 0.f, 0.f, 0.f};
-            g = mm_AtB<64, kSplitBwd>(g, isR ? sDY : sV, LD, (isR ? s_S0 : s_DS) + jc, LD, l16, kq);
+            g = mm_AtB<64, kSplitBwd, true>(g, isR ? sDY : sV, LD, (isR ? s_S0 : s_DS) + jc, LD, l16, kq);
             float *dst = s_G + (isR ? 1 : 3) * 16 * LD + jc + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = g[r];
@@ -653,7 +670,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             s_dgC[(wave - 10) * 64 + j] = acc0 + acc1;
         } else if (wave == 14) {
             f32x4 gm = {0.f, 0.f, 0.f, 0.f};
-            gm = mm_AtBt<64, kSplitBwd>(gm, sDY, LD, sV, LD, l16, kq);
+            gm = mm_AtBt<64, kSplitBwd, true, true>(gm, sDY, LD, sV, LD, l16, kq);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * kq + r;
@@ -673,7 +690,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         //      chunk's loads of S_0, dS_C, drhs and W (waves 8-15 in P5).
         f32x4 dvp = {0.f, 0.f, 0.f, 0.f};           // waves 4-7
         if (wave < 4) {
-            pa = mm_AtB<16>(pa, Mlak, 16, sV + 16 * w4, LD, l16, kq);
+            if constexpr (kSplitBwd) {                 // L_ak V, v holding bf16 values
+                const float4 m4 = *(const float4 *)(Mlak + l16 * 16 + 4 * kq);
+                const float *vp = sV + 16 * w4 + 4 * kq * LD + l16;
+                const float am[4] = {m4.x, m4.y, m4.z, m4.w}, bv[4] = {vp[0], vp[LD], vp[2 * LD], vp[3 * LD]};
+                pa = mm_k16_bx(pa, am, bv);
+            } else {
+                pa = mm_AtB<16>(pa, Mlak, 16, sV + 16 * w4, LD, l16, kq);
+            }
             f32x4 o = {0.f, 0.f, 0.f, 0.f};
             const float4 wr = *(const float4 *)(Mw + l16 * 16 + 4 * kq);
             o = mfma4(wr.x, pa[0], o); o = mfma4(wr.y, pa[1], o);
@@ -684,7 +708,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         } else if (wave < 8) {
             const int i0 = 16 * w4;
             dvp = mm_AtBt<64, kSplitBwd>(dvp, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq);
-            dvp = mm_TB(dvp, Mmrk, 16, sDY + i0, LD, l16, kq);
+            if constexpr (kSplitBwd) {                 // M_rk^T dY, dy holding bf16 values
+                float am[4], bv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    am[e] = Mmrk[(4 * kq + e) * 16 + l16];
+                    bv[e] = sDY[(4 * kq + e) * LD + i0 + l16];
+                }
+                dvp = mm_k16_bx(dvp, am, bv);
+            } else {
+                dvp = mm_TB(dvp, Mmrk, 16, sDY + i0, LD, l16, kq);
+            }
         } else if (wide && c < c_hi - 1) {
             flush_wide(c + 1);
         }
@@ -701,7 +735,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             const float *lhs = mi < 2 ? s_DR : sDY;
             const float *rt = mi == 1 ? sV : s_X;
             f32x4 gm = {0.f, 0.f, 0.f, 0.f};
-            gm = mm_AtBt<64, kSplitBwd>(gm, lhs, LD, rt, LD, l16, kq);
+            gm = mm_AtBt<64, kSplitBwd, mi == 2, mi == 1>(gm, lhs, LD, rt, LD, l16, kq);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * kq + r;
