@@ -97,7 +97,9 @@ enum { UCHA = 0, UCHR, UCHC, UR12A, UR12R, UR3A, UR3R, UC2, UC13, kUTerms };
 // it). A K = 32 step gives lane group kq the 8 contraction indices
 // k0 + 16 (e / 4) + 4 kq + e % 4, so the output layout is the FP32 one. An
 // operand that holds bf16 values (v, dy: AX, BX) is its own high piece, and
-// its low piece and that piece's product are skipped.
+// its low piece and that piece's product are skipped. The one-piece form
+// (both set for operands that are not bf16 values) rounds each operand to
+// bf16 and issues one MFMA per K = 32 step.
 template <bool AX, bool BX>
 __device__ __forceinline__ f32x4 mm_pieces(f32x4 acc, const float (&a)[8], const float (&b)[8]) {
     uint32_t ah[4], al[4], bh[4], bl[4];
@@ -184,14 +186,27 @@ template <> __device__ __forceinline__ uint16_t out_bits<_Float16>(float x) {
 template <> __device__ __forceinline__ uint16_t out_bits<float>(float) { return 0; }   // not used
 
 // acc += sum over 16 indices k = 4 kq + e of a[e] b[e] (this lane's values),
-// with a in two bf16 pieces and b holding bf16 values: one K = 32 MFMA whose
-// element e of lane group kq is index 4 kq + e % 4, piece e / 4 of a.
+// with b holding bf16 values: one K = 32 MFMA. With a in two bf16 pieces,
+// element e of lane group kq is index 4 kq + e % 4, piece e / 4 of a; with
+// a rounded to one piece (ONE), elements 4..7 are zero.
+template <bool ONE>
 __device__ __forceinline__ f32x4 mm_k16_bx(f32x4 acc, const float (&a)[4], const float (&b)[4]) {
+    const uint32_t b0 = pk_bf16(b[0], b[1]), b1 = pk_bf16(b[2], b[3]);
+    if constexpr (ONE) {
+        return mfma_bf16_k32(u32x4_t{pk_bf16(a[0], a[1]), pk_bf16(a[2], a[3]), 0u, 0u},
+                             u32x4_t{b0, b1, 0u, 0u}, acc);
+    }
     uint32_t h0, l0, h1, l1;
     split2(a[0], a[1], h0, l0);
     split2(a[2], a[3], h1, l1);
-    const uint32_t b0 = pk_bf16(b[0], b[1]), b1 = pk_bf16(b[2], b[3]);
     return mfma_bf16_k32(u32x4_t{h0, h1, l0, l1}, u32x4_t{b0, b1, b0, b1}, acc);
+}
+
+// acc += sum over 16 indices k = 4 kq + e of a[e] b[e], both rounded to one
+// bf16 piece: the FP32 form is four 16x16x4 MFMAs with a[e], b[e] at step e.
+__device__ __forceinline__ f32x4 mm_k16_one(f32x4 acc, const float (&a)[4], const float (&b)[4]) {
+    return mfma_bf16_k32(u32x4_t{pk_bf16(a[0], a[1]), pk_bf16(a[2], a[3]), 0u, 0u},
+                         u32x4_t{pk_bf16(b[0], b[1]), pk_bf16(b[2], b[3]), 0u, 0u}, acc);
 }
 
 // acc += A^T B for A = [k][m], B = [k][n] row-major with 16 rows k.
@@ -283,11 +298,17 @@ __global__ __launch_bounds__(1024) void group_list_kernel(SegParams seg, int32_t
     if (tid == 1023) glist[0] = (int32_t)(part[1023] < cap ? part[1023] : cap);
 }
 
-template <typename TI>
+template <typename TI, bool ONE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32_t units) {
-    // bf16 streams: the K = 64 products in two bf16 pieces (gradients within
-    // about 2^-16 of the FP32 products; the bf16 gradient bound is 5e-2)
+    // bf16 streams: every product on bf16 MFMA. With fp32 gradients (ONE
+    // false) the K = 64 products take two bf16 pieces a side, within about
+    // 2^-16 of the FP32 products, and the K = 16 products of fp32 operands
+    // stay on FP32 MFMA. With bf16 gradients (ONE) every operand is rounded
+    // to one bf16 piece: the gradients leave in bf16 (2^-9 relative), and
+    // the products' own rounding is of that order (measured max per-unit
+    // error 6e-3 against the 5e-2 bound, 3e-3 with two pieces).
     constexpr bool kSplitBwd = std::is_same<TI, uint16_t>::value;
+    constexpr bool kOne = kSplitBwd && ONE;
     extern __shared__ __align__(16) float sm[];
     // Workgroup -> (unit, group of kChunksPerGroup chunks): dense rows by
     // workgroup index, segment mode through the pre-pass's work list.
@@ -588,7 +609,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             const int jc = 16 * w4;
             const bool isR = wave < 12;
             f32x4 g = {0.f, 0.f, 0.f, 0.f};
-            g = mm_AtB<64, kSplitBwd, true>(g, isR ? sDY : sV, LD, (isR ? s_S0 : s_DS) + jc, LD, l16, kq);
+            g = mm_AtB<64, kSplitBwd, true, kOne>(g, isR ? sDY : sV, LD, (isR ? s_S0 : s_DS) + jc, LD, l16, kq);
             float *dst = s_G + (isR ? 1 : 3) * 16 * LD + jc + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = g[r];
@@ -602,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         //      16 (w-10)..; wave 14: dM_rk = dY V^T
         f32x4 pa = {0.f, 0.f, 0.f, 0.f};            // waves 0-3 (then rhs, X)
         if (wave < 4) {
-            pa = mm_AtBt<64, kSplitBwd>(pa, s_Q, LD, s_S0 + 16 * w4 * LD, LD, l16, kq);
+            pa = mm_AtBt<64, kSplitBwd, kOne, kOne>(pa, s_Q, LD, s_S0 + 16 * w4 * LD, LD, l16, kq);
         } else if (wave < 6) {
             // the tile index is made a compile-time constant so that the
             // scatter's index map folds
@@ -618,7 +639,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                     arow = s_AR + ((m & 4) ? 16 + m : 4 + m) * LD;
                     brow = s_BL + (16 + l16) * LD;
                 }
-                const f32x4 d = kSplitBwd ? mm_AtBt<64, true>(f32x4{0.f, 0.f, 0.f, 0.f}, arow, 0, brow, 0, 0, kq)
+                const f32x4 d = kSplitBwd ? mm_AtBt<64, true, kOne, kOne>(f32x4{0.f, 0.f, 0.f, 0.f}, arow, 0, brow, 0, 0, kq)
                                           : rows_product(arow, brow, kq);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -694,20 +715,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                 const float4 m4 = *(const float4 *)(Mlak + l16 * 16 + 4 * kq);
                 const float *vp = sV + 16 * w4 + 4 * kq * LD + l16;
                 const float am[4] = {m4.x, m4.y, m4.z, m4.w}, bv[4] = {vp[0], vp[LD], vp[2 * LD], vp[3 * LD]};
-                pa = mm_k16_bx(pa, am, bv);
+                pa = mm_k16_bx<kOne>(pa, am, bv);
             } else {
                 pa = mm_AtB<16>(pa, Mlak, 16, sV + 16 * w4, LD, l16, kq);
             }
             f32x4 o = {0.f, 0.f, 0.f, 0.f};
             const float4 wr = *(const float4 *)(Mw + l16 * 16 + 4 * kq);
-            o = mfma4(wr.x, pa[0], o); o = mfma4(wr.y, pa[1], o);
-            o = mfma4(wr.z, pa[2], o); o = mfma4(wr.w, pa[3], o);
+            if constexpr (kOne) {
+                o = mm_k16_one(o, {wr.x, wr.y, wr.z, wr.w}, {pa[0], pa[1], pa[2], pa[3]});
+            } else {
+                o = mfma4(wr.x, pa[0], o); o = mfma4(wr.y, pa[1], o);
+                o = mfma4(wr.z, pa[2], o); o = mfma4(wr.w, pa[3], o);
+            }
             float *dst = s_X + 16 * w4 + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = o[r];
         } else if (wave < 8) {
             const int i0 = 16 * w4;
-            dvp = mm_AtBt<64, kSplitBwd>(dvp, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq);
+            dvp = mm_AtBt<64, kSplitBwd, kOne, kOne>(dvp, s_BK + 16 * LD, LD, s_DS + i0 * LD, LD, l16, kq);
             if constexpr (kSplitBwd) {                 // M_rk^T dY, dy holding bf16 values
                 float am[4], bv[4];
 #pragma unroll
@@ -715,7 +740,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
                     am[e] = Mmrk[(4 * kq + e) * 16 + l16];
                     bv[e] = sDY[(4 * kq + e) * LD + i0 + l16];
                 }
-                dvp = mm_k16_bx(dvp, am, bv);
+                dvp = mm_k16_bx<kOne>(dvp, am, bv);
             } else {
                 dvp = mm_TB(dvp, Mmrk, 16, sDY + i0, LD, l16, kq);
             }
@@ -735,7 +760,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             const float *lhs = mi < 2 ? s_DR : sDY;
             const float *rt = mi == 1 ? sV : s_X;
             f32x4 gm = {0.f, 0.f, 0.f, 0.f};
-            gm = mm_AtBt<64, kSplitBwd, mi == 2, mi == 1>(gm, lhs, LD, rt, LD, l16, kq);
+            gm = mm_AtBt<64, kSplitBwd, mi == 2 || kOne, mi == 1 || kOne>(gm, lhs, LD, rt, LD, l16, kq);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * kq + r;
@@ -751,17 +776,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         //      waves 12, 13, 14: dL_ab, dL_ak, dM_rb
         if (wave >= 4 && wave < 8) {
             const int i0 = 16 * w4;
+            float am[4], bm[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int k = 4 * kq + e;
-                dvp = mfma4(Mlak[k * 16 + l16], s_DR[k * LD + i0 + l16], dvp);
+                am[e] = Mlak[(4 * kq + e) * 16 + l16];
+                bm[e] = s_DR[(4 * kq + e) * LD + i0 + l16];
+            }
+            if constexpr (kOne) {
+                dvp = mm_k16_one(dvp, am, bm);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dvp = mfma4(am[e], bm[e], dvp);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) gput(0, 4 * kq + r, i0 + l16, dvp[r], pdv[r]);
         } else if (wave < 4) {
             const int jc = 16 * w4;
             f32x4 g = {0.f, 0.f, 0.f, 0.f};
-            g = mm_AtB<64, kSplitBwd>(g, s_DR, LD, s_S0 + jc, LD, l16, kq);
+            g = mm_AtB<64, kSplitBwd, kOne, kOne>(g, s_DR, LD, s_S0 + jc, LD, l16, kq);
             float *dst = s_G + jc + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = g[r];
@@ -809,8 +841,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (kOne) {
+                    z = mm_k16_one(z, av, bv[q]);
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) z = mfma4(av[e], bv[q][e], z);
+                    for (int e = 0; e < 4; ++e) z = mfma4(av[e], bv[q][e], z);
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) zo[(4 * kq + r) * LD + 16 * q] = z[r];
             }
@@ -818,7 +854,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             if (wave < 12) {          // dB^ = X dS_C (key columns 16 (w & 3)..)
                 const int jc = 16 * w4;
                 f32x4 g = {0.f, 0.f, 0.f, 0.f};
-                g = mm_AtB<64, kSplitBwd>(g, s_X, LD, s_DS + jc, LD, l16, kq);
+                g = mm_AtB<64, kSplitBwd, kOne, kOne>(g, s_X, LD, s_DS + jc, LD, l16, kq);
                 float *dst = s_G + 2 * 16 * LD + jc + l16;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dst[(4 * kq + r) * LD] = g[r];
@@ -1090,8 +1126,9 @@ hipError_t launch_backward(const BwdArgs &args, hipStream_t stream) {
     const int S = a.seg.num_seqs > 0 ? a.seg.num_seqs : a.seg.B;
     const int32_t units = S * a.seg.H;
     const size_t lds = (size_t)LDS_FLOATS * sizeof(float);
-    auto fn = a.dtype == 1 ? bwd_chunk_kernel<uint16_t>
-            : a.dtype == 2 ? bwd_chunk_kernel<_Float16> : bwd_chunk_kernel<float>;
+    // bf16 streams: one-piece products for bf16 gradients, two pieces for fp32 ones
+    auto fn = a.dtype == 1 ? (a.grad_f32 ? bwd_chunk_kernel<uint16_t, false> : bwd_chunk_kernel<uint16_t, true>)
+            : a.dtype == 2 ? bwd_chunk_kernel<_Float16, false> : bwd_chunk_kernel<float, false>;
     hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     if (a.seg.num_seqs > 0 && a.glist) {
