@@ -147,16 +147,20 @@ def test_workgroup_shapes_f32(W, H):
 
 
 @pytest.mark.parametrize("decay", ["mult", "log"])
-def test_split_path_fast_and_slow_chunks(W, decay):
-    """bf16 with 256 units (B=8, H=32) runs 64-row workgroups, whose state
-    products are three-piece bf16 MFMAs. A chunk whose decays are all at least
-    2^-6 builds its 16x16 matrices from MFMA tiles of the hand-off rows, any
-    other chunk from the split-point rows: chunk 1 holds a token with decay 0
-    (1e-13 as a logarithm), chunk 3 decays of 2^-10 on some keys; chunks 0, 2
-    and the partial chunk 4 take the tile path. Every unit's y, final state and
-    checkpoints against the oracle, for both decay inputs."""
+@pytest.mark.parametrize("B,H", [(8, 32), (4, 32), (2, 3)])
+def test_bf16_fast_and_slow_chunks(W, decay, B, H):
+    """bf16 streams with a zero decay (1e-13 as a logarithm) in chunk 1 and
+    decays of 2^-10 on some keys in chunk 3. With 256 units (B=8, H=32) the
+    forward runs 64-row workgroups whose state products are three-piece bf16
+    MFMAs; there a chunk whose decays are all at least 2^-6 builds its 16x16
+    matrices from bf16 MFMA tiles of decay-scaled rows (chunks 0, 2 and the
+    partial chunk 4), any other chunk from the split-point rows. With 128
+    units (B=4, H=32) and 6 units (B=2, H=3) the forward runs 32- and 16-row
+    workgroups on FP32 MFMA, every chunk from the split-point rows. Every
+    unit's y, final state and checkpoints against the oracle, for both decay
+    inputs."""
     import torch
-    B, T, H = 8, 77, 32
+    T = 77
     inp = synth.make_inputs(B, T, H, 64, seed=500, dtype="bf16", s0_std=0.1, decay=decay)
     if decay == "mult":
         inp.w[:, 21] = 0.0
