@@ -761,6 +761,10 @@ def summarize(root):
             if cset:
                 lines.append(f"    rocprofv3 --pmc {' '.join(PMC_SETS[s])} -f csv -d gpurun_out/prof/{s}/{leg} "
                              f"-o {s} -- python3 bench.py --only {leg} --steps 2 --warmup 1 --no-cpu-baseline")
+        for s, c in (("pmc_fetch", "FETCH_SIZE"), ("pmc_write", "WRITE_SIZE")):
+            if s in pmc_sets and c in scale:
+                lines.append(f"    rocprofv3 --pmc {c} -f csv -d gpurun_out/prof/{s}/copy -o {s} -- "
+                             f"python3 bench.py --copy-calibration")
         lines += ["", f"    python3 bench.py --summarize gpurun_out/prof", ""]
         lines += ["Durations are per dispatch from the kernel trace; counters are per dispatch (summed over the "
                   "chip's instances), from counter runs in which rocprofv3 serialises dispatches.", ""]
