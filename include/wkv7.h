@@ -155,7 +155,11 @@ wkv7_status wkv7_forward(const wkv7_desc *d,
  * The recurrence is recomputed from the 16-token checkpoints in fp32, not
  * reconstructed by dividing by the decay. N = 64: two kernels run back to
  * back on `stream`, a reverse sweep that carries only the state gradient,
- * then the per-chunk gradients, all chunks in parallel. N = 128: token by
+ * then the per-chunk gradients, all chunks in parallel; with bf16 streams
+ * the second kernel's products run on bf16 MFMA with fp32 accumulation, each
+ * operand rounded to one bf16 piece for bf16 gradients (the order of the
+ * gradients' own bf16 rounding) and split into two pieces (about 2^-16
+ * relative) when grad_f32 = 1. N = 128: token by
  * token, one workgroup per (sequence, head) through the whole sequence in
  * reverse, every gradient summed within the workgroup (no workspace; the
  * results do not depend on scheduling).
