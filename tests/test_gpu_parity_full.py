@@ -67,6 +67,10 @@ def test_training_gradients_16_units(W):
                 ch[b * nc:(b + 1) * nc, h:h + 1], fr["ckpt"][:, h:h + 1], [0], [nc]))
     assert worst["ckpt"] <= U.TOL_F32, worst
     assert all(v <= U.TOL_GRAD for k, v in worst.items() if k != "ckpt"), worst
+    # The gradient products of bf16 streams take one bf16 piece per operand;
+    # their error stays of the order of the gradients' own bf16 rounding
+    # (measured 6e-3, 3e-3 with exact products), well inside the bound.
+    assert all(v <= 2e-2 for k, v in worst.items() if k != "ckpt"), worst
 
 
 @pytest.fixture(scope="module")
