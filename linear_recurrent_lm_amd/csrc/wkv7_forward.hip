@@ -41,7 +41,10 @@
 // not depend on the state (decay rows, the 16x16 matrices, W) for chunk c
 // while the state waves advance through chunk c-1; the two sides meet through
 // a double-buffered LDS hand-off, two workgroup barriers per chunk (W of a
-// chunk is solved one phase later, while the state waves run its D1).
+// chunk is solved one phase later, while the state waves run its D1). With
+// bf16 streams the products that feed only y run on bf16 MFMA with one piece
+// per operand; with bf16 streams in 64-row workgroups every state product
+// runs in split bf16 (three pieces) as well.
 #include <type_traits>
 
 #include "wkv7_kernels.h"
@@ -121,6 +124,11 @@ template <typename TI, int NMW, int KS, bool SPLIT>
 __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdArgs p, int32_t units) {
     using L = Lay<SPLIT>;
     static_assert(!SPLIT || sizeof(TI) == 2, "split path: 16-bit streams");
+    // bf16 streams on the FP32-MFMA state path: the products that feed only
+    // y (R^ S_0^T, M_rk V, M_rb X) round their operands to one bf16 piece and
+    // run on bf16 MFMA, which leaves the SIMD's VALU to the operand waves; y
+    // leaves in bf16 (2^-9), the state products stay FP32
+    constexpr bool kY1 = !SPLIT && std::is_same<TI, uint16_t>::value;
     constexpr int NG = NMW / KS;       // 16-row groups per workgroup
     constexpr int RB = 16 * NG;        // value rows per workgroup
     constexpr int NRB = 64 / RB;       // row blocks per unit
@@ -331,27 +339,55 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
                 const float4 lak = *(const float4 *)(mrow + MLAK * 16 * MLD);
                 const float4 mrk = *(const float4 *)(mrow + MMRK * 16 * MLD);
                 mrb = *(const float4 *)(mrow + MMRB * 16 * MLD);
+                if constexpr (kY1) {
+                    // state product on FP32 MFMA; the y-only R^ S_0^T as one
+                    // bf16 MFMA per key tile pair (K = 32 keys)
 #pragma unroll
-                for (int qq = 0; qq < NQ; ++qq) {
-                    const int q = q0 + qq;
-                    const float4 a4 = *(const float4 *)(buf + L::B_Q + l16 * QLD + 16 * q + 4 * kq);
-                    const float4 r4 = *(const float4 *)(buf + L::B_Q + (16 + l16) * QLD + 16 * q + 4 * kq);
-                    d1a = mfma4(a4.x, acc[qq][0], d1a);
-                    d1r = mfma4(r4.x, acc[qq][0], d1r);
-                    d1a = mfma4(a4.y, acc[qq][1], d1a);
-                    d1r = mfma4(r4.y, acc[qq][1], d1r);
-                    d1a = mfma4(a4.z, acc[qq][2], d1a);
-                    d1r = mfma4(r4.z, acc[qq][2], d1r);
-                    d1a = mfma4(a4.w, acc[qq][3], d1a);
-                    d1r = mfma4(r4.w, acc[qq][3], d1r);
+                    for (int qq = 0; qq < NQ; ++qq) {
+                        const float4 a4 = *(const float4 *)(buf + L::B_Q + l16 * QLD + 16 * (q0 + qq) + 4 * kq);
+                        d1a = mfma4(a4.x, acc[qq][0], d1a);
+                        d1a = mfma4(a4.y, acc[qq][1], d1a);
+                        d1a = mfma4(a4.z, acc[qq][2], d1a);
+                        d1a = mfma4(a4.w, acc[qq][3], d1a);
+                    }
+#pragma unroll
+                    for (int qq = 0; qq < NQ; qq += 2) {
+                        const float *rr = buf + L::B_Q + (16 + l16) * QLD + 16 * (q0 + qq) + 4 * kq;
+                        const float4 r4 = *(const float4 *)rr, s4 = *(const float4 *)(rr + 16);
+                        d1r = mfma_bf16_k32(
+                            u32x4_t{pk_bf16(r4.x, r4.y), pk_bf16(r4.z, r4.w), pk_bf16(s4.x, s4.y), pk_bf16(s4.z, s4.w)},
+                            u32x4_t{pk_bf16(acc[qq][0], acc[qq][1]), pk_bf16(acc[qq][2], acc[qq][3]),
+                                    pk_bf16(acc[qq + 1][0], acc[qq + 1][1]), pk_bf16(acc[qq + 1][2], acc[qq + 1][3])},
+                            d1r);
+                    }
+                } else {
+#pragma unroll
+                    for (int qq = 0; qq < NQ; ++qq) {
+                        const int q = q0 + qq;
+                        const float4 a4 = *(const float4 *)(buf + L::B_Q + l16 * QLD + 16 * q + 4 * kq);
+                        const float4 r4 = *(const float4 *)(buf + L::B_Q + (16 + l16) * QLD + 16 * q + 4 * kq);
+                        d1a = mfma4(a4.x, acc[qq][0], d1a);
+                        d1r = mfma4(r4.x, acc[qq][0], d1r);
+                        d1a = mfma4(a4.y, acc[qq][1], d1a);
+                        d1r = mfma4(r4.y, acc[qq][1], d1r);
+                        d1a = mfma4(a4.z, acc[qq][2], d1a);
+                        d1r = mfma4(r4.z, acc[qq][2], d1r);
+                        d1a = mfma4(a4.w, acc[qq][3], d1a);
+                        d1r = mfma4(r4.w, acc[qq][3], d1r);
+                    }
                 }
                 if (KS == 1 || kh == 0) {
                     d1a = mfma4(lak.x, vb.x, d1a); d1a = mfma4(lak.y, vb.y, d1a);
                     d1a = mfma4(lak.z, vb.z, d1a); d1a = mfma4(lak.w, vb.w, d1a);
                 }
                 if (KS == 1 || kh == 1) {
-                    d1r = mfma4(mrk.x, vb.x, d1r); d1r = mfma4(mrk.y, vb.y, d1r);
-                    d1r = mfma4(mrk.z, vb.z, d1r); d1r = mfma4(mrk.w, vb.w, d1r);
+                    if constexpr (kY1) {
+                        d1r = mfma_bf16_k32(u32x4_t{pk_bf16(mrk.x, mrk.y), pk_bf16(mrk.z, mrk.w), 0u, 0u},
+                                            u32x4_t{pk_bf16(vb.x, vb.y), pk_bf16(vb.z, vb.w), 0u, 0u}, d1r);
+                    } else {
+                        d1r = mfma4(mrk.x, vb.x, d1r); d1r = mfma4(mrk.y, vb.y, d1r);
+                        d1r = mfma4(mrk.z, vb.z, d1r); d1r = mfma4(mrk.w, vb.w, d1r);
+                    }
                 }
                 if (KS > 1) {
                     *(float4 *)xch_own = make_float4(d1a[0], d1a[1], d1a[2], d1a[3]);
@@ -393,8 +429,13 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
                     acc[qq] = a;
                 }
                 if (KS == 1 || kh == 0) {
-                    d1r = mfma4(mrb.x, xx[0], d1r); d1r = mfma4(mrb.y, xx[1], d1r);
-                    d1r = mfma4(mrb.z, xx[2], d1r); d1r = mfma4(mrb.w, xx[3], d1r);
+                    if constexpr (kY1) {
+                        d1r = mfma_bf16_k32(u32x4_t{pk_bf16(mrb.x, mrb.y), pk_bf16(mrb.z, mrb.w), 0u, 0u},
+                                            u32x4_t{pk_bf16(xx[0], xx[1]), pk_bf16(xx[2], xx[3]), 0u, 0u}, d1r);
+                    } else {
+                        d1r = mfma4(mrb.x, xx[0], d1r); d1r = mfma4(mrb.y, xx[1], d1r);
+                        d1r = mfma4(mrb.z, xx[2], d1r); d1r = mfma4(mrb.w, xx[3], d1r);
+                    }
                     const int t0 = cm * kChunk;
                     const int L = min(kChunk, u.len - t0);
 #pragma unroll
