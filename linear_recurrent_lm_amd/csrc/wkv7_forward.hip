@@ -75,6 +75,16 @@ __device__ __forceinline__ int stage_block(int b) { return 8 * (b >> 3) + ((b + 
 __device__ __forceinline__ int stage_pos(int c) { return 4 * stage_block(c >> 2) + (c & 3); }
 
 enum { IR = 0, IW, IK, IA, IB, IV };
+// acc += sum over 16 indices of a[e] v[e] (this lane's 4 of them), a fp32 in
+// three bf16 pieces and v holding bf16 values: two K = 32 bf16 MFMAs
+__device__ __forceinline__ f32x4 mm_k16_3v(f32x4 acc, float4 a, float4 v) {
+    uint32_t h0, m0, l0, h1, m1, l1;
+    split3(a.x, a.y, h0, m0, l0);
+    split3(a.z, a.w, h1, m1, l1);
+    const uint32_t v0 = pk_bf16(v.x, v.y), v1 = pk_bf16(v.z, v.w);
+    acc = mfma_bf16_k32(u32x4_t{l0, l1, 0u, 0u}, u32x4_t{v0, v1, 0u, 0u}, acc);
+    return mfma_bf16_k32(u32x4_t{h0, h1, m0, m1}, u32x4_t{v0, v1, v0, v1}, acc);
+}
 enum { MLAK = 0, MMRK, MMRB, MWI };
 
 // LDS layout (floats): the operand waves' private rows, then two hand-off
@@ -127,7 +137,9 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
     // bf16 streams on the FP32-MFMA state path: the products that feed only
     // y (R^ S_0^T, M_rk V, M_rb X) round their operands to one bf16 piece and
     // run on bf16 MFMA, which leaves the SIMD's VALU to the operand waves; y
-    // leaves in bf16 (2^-9), the state products stay FP32
+    // leaves in bf16 (2^-9). The state products against v (L_ak V, K^^T V)
+    // take the fp32 operand in three bf16 pieces (24 bits) against v's
+    // exact bf16 values; the others stay FP32
     constexpr bool kY1 = !SPLIT && std::is_same<TI, uint16_t>::value;
     constexpr int NG = NMW / KS;       // 16-row groups per workgroup
     constexpr int RB = 16 * NG;        // value rows per workgroup
@@ -377,8 +389,12 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
                     }
                 }
                 if (KS == 1 || kh == 0) {
-                    d1a = mfma4(lak.x, vb.x, d1a); d1a = mfma4(lak.y, vb.y, d1a);
-                    d1a = mfma4(lak.z, vb.z, d1a); d1a = mfma4(lak.w, vb.w, d1a);
+                    if constexpr (kY1) {
+                        d1a = mm_k16_3v(d1a, lak, vb);
+                    } else {
+                        d1a = mfma4(lak.x, vb.x, d1a); d1a = mfma4(lak.y, vb.y, d1a);
+                        d1a = mfma4(lak.z, vb.z, d1a); d1a = mfma4(lak.w, vb.w, d1a);
+                    }
                 }
                 if (KS == 1 || kh == 1) {
                     if constexpr (kY1) {
@@ -402,8 +418,12 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void fwd_ws_kernel(FwdA
                     const float4 k4 = *(const float4 *)(br + 16);
                     f32x4 a = acc[qq];
                     a[0] *= g4.x; a[1] *= g4.y; a[2] *= g4.z; a[3] *= g4.w;
-                    a = mfma4(k4.x, vb.x, a); a = mfma4(k4.y, vb.y, a);
-                    a = mfma4(k4.z, vb.z, a); a = mfma4(k4.w, vb.w, a);
+                    if constexpr (kY1) {
+                        a = mm_k16_3v(a, k4, vb);
+                    } else {
+                        a = mfma4(k4.x, vb.x, a); a = mfma4(k4.y, vb.y, a);
+                        a = mfma4(k4.z, vb.z, a); a = mfma4(k4.w, vb.w, a);
+                    }
                     acc[qq] = a;
                 }
             }
