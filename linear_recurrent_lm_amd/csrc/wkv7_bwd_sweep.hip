@@ -25,7 +25,12 @@
 // A^, R^, gamma_C, dY and the 16x16 matrices M_rb and W (L_ab only feeds W),
 // with the same split-point products and within-sub-chunk dot products, into
 // a double-buffered LDS hand-off; two workgroup barriers per chunk. The
-// decay is clamped to w >= 2^-30 throughout, as in the second pass.
+// decay is clamped to w >= 2^-30 throughout, as in the second pass. The
+// products run on FP32 MFMA, except that with bf16 streams the two against
+// dy (whose values are exact in bf16) take their other operand in three bf16
+// pieces on bf16 MFMA.
+#include <type_traits>
+
 #include "wkv7_kernels.h"
 #include "wkv7_mfma.h"
 
@@ -42,6 +47,19 @@ constexpr float kMinW = 9.313225746154785e-10f;   // 2^-30
 // staged streams
 enum { SR = 0, SW, SA, SB, SDY, kStreams };
 enum { MMRBT = 0, MWT };
+
+// acc += sum over 16 indices of a[e] y[e] (this lane's 4 of them), a fp32 in
+// three bf16 pieces (24 bits) and y holding bf16 values (dy of bf16 streams):
+// two K = 32 bf16 MFMAs, which leave the SIMD's VALU free where the four
+// FP32 ones held it
+__device__ __forceinline__ f32x4 mm_k16_3x(f32x4 acc, float4 a, float4 y) {
+    uint32_t h0, m0, l0, h1, m1, l1;
+    split3(a.x, a.y, h0, m0, l0);
+    split3(a.z, a.w, h1, m1, l1);
+    const uint32_t y0 = pk_bf16(y.x, y.y), y1 = pk_bf16(y.z, y.w);
+    acc = mfma_bf16_k32(u32x4_t{l0, l1, 0u, 0u}, u32x4_t{y0, y1, 0u, 0u}, acc);
+    return mfma_bf16_k32(u32x4_t{h0, h1, m0, m1}, u32x4_t{y0, y1, y0, y1}, acc);
+}
 
 namespace lay {
 constexpr int IN = 0;                       // [2][5][16][64] r w a b dy, by chunk parity
@@ -71,6 +89,9 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
     constexpr int NRB = 64 / RB;       // row blocks per unit
     constexpr int NQ = 4 / KS;         // 16-column key tiles per state wave
     static_assert(KS == 1 || KS == 2, "key split of 1 or 2");
+    // bf16 streams: the products against dy (exact in bf16) take the other
+    // operand in three bf16 pieces on bf16 MFMA
+    constexpr bool kX3 = std::is_same<TI, uint16_t>::value;
     extern __shared__ __align__(16) float sm[];
 
     int unit, rb;
@@ -143,8 +164,12 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
                 const float4 dyb = *(const float4 *)(buf + lay::B_DYT + irow * VLD + 4 * kq);
                 if (KS == 1 || kh == 0) {
                     const float4 mrbt = *(const float4 *)(buf + lay::B_M + MMRBT * 16 * MLD + l16 * MLD + 4 * kq);
-                    dx = mfma4(mrbt.x, dyb.x, dx); dx = mfma4(mrbt.y, dyb.y, dx);
-                    dx = mfma4(mrbt.z, dyb.z, dx); dx = mfma4(mrbt.w, dyb.w, dx);
+                    if constexpr (kX3) {
+                        dx = mm_k16_3x(dx, mrbt, dyb);
+                    } else {
+                        dx = mfma4(mrbt.x, dyb.x, dx); dx = mfma4(mrbt.y, dyb.y, dx);
+                        dx = mfma4(mrbt.z, dyb.z, dx); dx = mfma4(mrbt.w, dyb.w, dx);
+                    }
                 }
                 if (KS > 1) *(float4 *)xch_own = make_float4(dx[0], dx[1], dx[2], dx[3]);
 #pragma unroll
@@ -154,8 +179,12 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
                     const float4 r4 = *(const float4 *)(buf + lay::B_ART + (16 * q + l16) * KLD + 16 + 4 * kq);
                     f32x4 a = acc[qq];
                     a[0] *= g4.x; a[1] *= g4.y; a[2] *= g4.z; a[3] *= g4.w;
-                    a = mfma4(r4.x, dyb.x, a); a = mfma4(r4.y, dyb.y, a);
-                    a = mfma4(r4.z, dyb.z, a); a = mfma4(r4.w, dyb.w, a);
+                    if constexpr (kX3) {
+                        a = mm_k16_3x(a, r4, dyb);
+                    } else {
+                        a = mfma4(r4.x, dyb.x, a); a = mfma4(r4.y, dyb.y, a);
+                        a = mfma4(r4.z, dyb.z, a); a = mfma4(r4.w, dyb.w, a);
+                    }
                     acc[qq] = a;
                 }
             }
