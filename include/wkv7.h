@@ -147,7 +147,8 @@ wkv7_status wkv7_forward(const wkv7_desc *d,
  *           64x64; the chunk's 16x16 inverse W of its unit-lower triangular
  *           system; and the 16x64 product of W's transpose with the chunk's
  *           gradient of that system's solution; per checkpoint slot and
- *           head) and reads them back within the same call; calls that may run
+ *           head; the first and third in bf16 when the streams and the
+ *           gradients are bf16) and reads them back within the same call; calls that may run
  *           concurrently need separate workspaces. Too small or NULL when
  *           needed: WKV7_ERR_WORKSPACE_TOO_SMALL, before any HIP call.
  * No output (dr..db, ds0, workspace) may share a byte with an input (r..b,

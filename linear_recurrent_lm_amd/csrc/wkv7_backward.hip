@@ -382,6 +382,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
     // not loaded and stages as zeros.
     Raw<TI, 1> raw;
     float4 ckr, dsr, drr, wwr;                  // checkpoint S_0, dS_C, drhs, W of the chunk in flight
+    uint2 dsh, drh;                              // dS_C, drhs in flight as bf16 (kOne: the sweep stores them so)
     const int sst = __builtin_amdgcn_readfirstlane(tid >> 7);
     const TI *ssp = sst < 7 && p.staged[sst] ? (const TI *)p.staged[sst] + base : nullptr;
     // The loads of a chunk are issued in three groups, the inputs in the
@@ -400,9 +401,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
         // float4 tid of a 64x64 state: row tid / 16, column 4 (tid % 16)
         const int64_t so = ((u.ckpt + cc) * H + h) * (int64_t)(kN * kN) + tid * 4;
         ckr = *(const float4 *)(p.ckpt + so);
-        dsr = *(const float4 *)(p.ws + so);
         // drhs [16][64]: float4 tid of waves 0-3; W [16][16]: float4 lane of wave 14
-        if (wave < 4) drr = *(const float4 *)(p.ws_dr + ((u.ckpt + cc) * H + h) * (int64_t)(kChunk * kN) + tid * 4);
+        const int64_t dro = ((u.ckpt + cc) * H + h) * (int64_t)(kChunk * kN) + tid * 4;
+        if constexpr (kOne) {
+            dsh = *(const uint2 *)((const uint16_t *)p.ws + so);
+            if (wave < 4) drh = *(const uint2 *)((const uint16_t *)p.ws_dr + dro);
+        } else {
+            dsr = *(const float4 *)(p.ws + so);
+            if (wave < 4) drr = *(const float4 *)(p.ws_dr + dro);
+        }
         if (wave == 14) wwr = *(const float4 *)(p.ws_w + ((u.ckpt + cc) * H + h) * (int64_t)(kChunk * kChunk) + lane * 4);
     };
     issue_in(c_hi - 1);
@@ -492,6 +499,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs p, int32
             *(float4 *)(d + 4) = make_float4(x[4], x[5], x[6], x[7]);
         }
         *(float4 *)(s_S0 + (tid >> 4) * LD + (tid & 15) * 4) = ckr;
+        if constexpr (kOne) {
+            dsr = make_float4(bf_lo(dsh.x), bf_hi(dsh.x), bf_lo(dsh.y), bf_hi(dsh.y));
+            if (wave < 4) drr = make_float4(bf_lo(drh.x), bf_hi(drh.x), bf_lo(drh.y), bf_hi(drh.y));
+        }
         *(float4 *)(s_DS + (tid >> 4) * LD + (tid & 15) * 4) = dsr;
         if (wave < 4) *(float4 *)(s_DR + (tid >> 4) * LD + (tid & 15) * 4) = drr;
         if (wave == 14) *(float4 *)(s_M + MW * 256 + lane * 4) = wwr;

@@ -82,7 +82,9 @@ constexpr int TOTAL = XCH + 4 * 256;
 static_assert(BUF % 4 == 0 && BUF_SIZE % 4 == 0 && IN_SIZE % 4 == 0, "16-byte aligned buffers");
 }  // namespace lay
 
-template <typename TI, int NMW, int KS>
+// HB: dS_C and drhs go to the workspace in bf16 (bf16 streams with bf16
+// gradients, whose second pass rounds every operand to one bf16 piece)
+template <typename TI, int NMW, int KS, bool HB>
 __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdArgs p, int32_t units) {
     constexpr int NG = NMW / KS;       // 16-row groups per workgroup
     constexpr int RB = 16 * NG;        // value rows per workgroup
@@ -147,11 +149,17 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
             //      dX = B^ dS_C^T (over this wave's key columns) + M_rb^T dY (one
             //      key part when split); dS^T = diag(gamma) dS^T + R^^T dY
             if (k >= 1) {
-                float *wp = p.ws + ((u.ckpt + cs) * H + h) * (int64_t)(kN * kN) + (int64_t)irow * kN;
+                const int64_t wo = ((u.ckpt + cs) * H + h) * (int64_t)(kN * kN) + (int64_t)irow * kN;
 #pragma unroll
-                for (int qq = 0; qq < NQ; ++qq)
-                    *(float4 *)(wp + 16 * (q0 + qq) + 4 * kq) =
-                        make_float4(acc[qq][0], acc[qq][1], acc[qq][2], acc[qq][3]);
+                for (int qq = 0; qq < NQ; ++qq) {
+                    const int64_t o = wo + 16 * (q0 + qq) + 4 * kq;
+                    if constexpr (HB) {
+                        *(uint2 *)((uint16_t *)p.ws + o) =
+                            make_uint2(pk_bf16(acc[qq][0], acc[qq][1]), pk_bf16(acc[qq][2], acc[qq][3]));
+                    } else {
+                        *(float4 *)(p.ws + o) = make_float4(acc[qq][0], acc[qq][1], acc[qq][2], acc[qq][3]);
+                    }
+                }
 #pragma unroll
                 for (int qq = 0; qq < NQ; ++qq) {
                     const int q = q0 + qq;
@@ -201,9 +209,12 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
                 dr = mfma4(wt.x, dx[0], dr); dr = mfma4(wt.y, dx[1], dr);
                 dr = mfma4(wt.z, dx[2], dr); dr = mfma4(wt.w, dx[3], dr);
                 if (KS == 1 || kh == 0) {        // drhs[t][i] of this chunk for the second pass
-                    float *dp = p.ws_dr + ((u.ckpt + cs) * H + h) * (int64_t)(kChunk * kN) + irow;
+                    const int64_t dof = ((u.ckpt + cs) * H + h) * (int64_t)(kChunk * kN) + irow;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) dp[(4 * kq + r) * kN] = dr[r];
+                    for (int r = 0; r < 4; ++r) {
+                        if constexpr (HB) ((uint16_t *)p.ws_dr)[dof + (4 * kq + r) * kN] = f32_to_bf16(dr[r]);
+                        else p.ws_dr[dof + (4 * kq + r) * kN] = dr[r];
+                    }
                 }
 #pragma unroll
                 for (int qq = 0; qq < NQ; ++qq) {
@@ -582,11 +593,11 @@ __global__ __launch_bounds__(64 * (NMW + kPrepWaves), 1) void dsweep_kernel(BwdA
     }
 }
 
-template <typename TI, int NMW, int KS>
+template <typename TI, int NMW, int KS, bool HB>
 hipError_t launch_sweep(const BwdArgs &a, int32_t units, hipStream_t stream) {
     constexpr int NRB = 64 / (16 * NMW / KS);
     const size_t lds = (size_t)lay::TOTAL * sizeof(float);
-    auto fn = dsweep_kernel<TI, NMW, KS>;
+    auto fn = dsweep_kernel<TI, NMW, KS, HB>;
     hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t blocks = NRB == 1 ? units : ((int64_t)units + 7) / 8 * 8 * NRB;
@@ -594,22 +605,25 @@ hipError_t launch_sweep(const BwdArgs &a, int32_t units, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename TI>
+template <typename TI, bool HB>
 hipError_t launch_sweep_typed(const BwdArgs &a, hipStream_t stream) {
     const int S = a.seg.num_seqs > 0 ? a.seg.num_seqs : a.seg.B;
     const int32_t units = S * a.seg.H;
     const int nrb = row_blocks_for(units);
-    if (nrb == 1) return launch_sweep<TI, 4, 1>(a, units, stream);
-    if (nrb == 2) return launch_sweep<TI, 4, 2>(a, units, stream);
-    return launch_sweep<TI, 2, 2>(a, units, stream);
+    if (nrb == 1) return launch_sweep<TI, 4, 1, HB>(a, units, stream);
+    if (nrb == 2) return launch_sweep<TI, 4, 2, HB>(a, units, stream);
+    return launch_sweep<TI, 2, 2, HB>(a, units, stream);
 }
 
 }  // namespace
 
 hipError_t launch_backward_sweep(const BwdArgs &a, hipStream_t stream) {
-    if (a.dtype == 1) return launch_sweep_typed<uint16_t>(a, stream);
-    if (a.dtype == 2) return launch_sweep_typed<_Float16>(a, stream);
-    return launch_sweep_typed<float>(a, stream);
+    // bf16 streams with bf16 gradients: dS_C and drhs travel in bf16 (the
+    // second pass's products round them to one bf16 piece anyway)
+    if (a.dtype == 1) return a.grad_f32 ? launch_sweep_typed<uint16_t, false>(a, stream)
+                                        : launch_sweep_typed<uint16_t, true>(a, stream);
+    if (a.dtype == 2) return launch_sweep_typed<_Float16, false>(a, stream);
+    return launch_sweep_typed<float, false>(a, stream);
 }
 
 }  // namespace wkv7

@@ -30,8 +30,9 @@ struct BwdArgs {
     const float *ds_out;
     void *dr, *dw, *dk, *dv, *da, *db;
     float *ds0;
-    float *ws;                       // per-slot dS_C of the sweep ([slots][H][N][N] fp32)
-    float *ws_dr;                    // per-slot drhs = W^T dX of the sweep ([slots][H][16][N] fp32)
+    float *ws;                       // per-slot dS_C of the sweep ([slots][H][N][N] fp32, or the same array in
+                                     // bf16 at the region's start for bf16 streams with bf16 gradients)
+    float *ws_dr;                    // per-slot drhs = W^T dX of the sweep ([slots][H][16][N] fp32; bf16 likewise)
     float *ws_w;                     // per-slot W = (I - L_ab)^-1 of the sweep ([slots][H][16][16] fp32)
     // segment mode: the work items of the second pass, [count][(sequence,
     // chunk group) x glist_cap], written by a pre-pass into the workspace
