@@ -28,7 +28,13 @@
 // starts from the chunk's checkpoint (re-read; it stays in L2), steps forward
 // to the segment's first token without storing, then keeps the states before
 // each of its tokens in registers for the reverse pass (2.5 forward steps per
-// token for kSeg = 4).
+// token for kSeg = 4). Those states enter only their token's own gradients
+// (dr, dw, da), never the recursion of dS, so with bf16 streams and bf16
+// gradients they are kept as bf16 pairs, half the registers, and a segment
+// spans 8 tokens (1.5 forward steps per token); the recomputed chain itself
+// stays fp32.
+#include <type_traits>
+
 #include "wkv7_kernels.h"
 #include "wkv7_mfma.h"
 
@@ -38,6 +44,7 @@ namespace {
 constexpr int kWN = 128;              // head size
 constexpr int kWThreads = 1024;
 constexpr int kSeg = 4;               // tokens per recompute segment
+constexpr int kSegHS = 8;             // the same with the segment's states in bf16
 enum { SW = 0, SA, SB, SK, SR, NSTAGE };     // staged key-indexed rows
 enum { GR = 0, GK, GB, GW, GA, NGRAD };      // key-indexed gradients
 
@@ -118,6 +125,10 @@ __device__ __forceinline__ void row_sums(float (&x)[4], int lane) {
 template <typename TI, typename TO>
 __global__ __launch_bounds__(kWThreads, 1) void bwd128_kernel(BwdArgs p, int32_t units) {
     extern __shared__ __align__(16) float sm[];
+    // bf16 streams with bf16 gradients: the states before the tokens of a
+    // segment are held as bf16 pairs, so a segment spans 8 tokens
+    constexpr bool kHS = std::is_same<TI, uint16_t>::value && std::is_same<TO, uint16_t>::value;
+    constexpr int kSegT = kHS ? kSegHS : kSeg;
     const int unit = blockIdx.x;
     if (unit >= units) return;
     const int H = p.seg.H;
@@ -171,7 +182,7 @@ __global__ __launch_bounds__(kWThreads, 1) void bwd128_kernel(BwdArgs p, int32_t
     int buf = 0;
     // the reverse step of token e of the chunk starting at token t0, with P
     // the state before it
-    auto token = [&](const float (&P)[16], int e, int64_t t0) {
+    auto token = [&](auto P, int e, int64_t t0) {
         relane();
         // operands are read where they are first used, to keep few live
         auto f4 = [](float4 x, float (&o)[4]) { o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w; };
@@ -216,9 +227,9 @@ __global__ __launch_bounds__(kWThreads, 1) void bwd128_kernel(BwdArgs p, int32_t
                 float x = 0.f, y = 0.f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float st = fmaf(P[4 * r + e2], w[e2], fmaf(sa[r], b[e2], v[r] * k[e2]));
+                    const float st = fmaf(P(4 * r + e2), w[e2], fmaf(sa[r], b[e2], v[r] * k[e2]));
                     x = fmaf(st, dy[r], x);
-                    y = fmaf(dS[4 * r + e2], P[4 * r + e2], y);
+                    y = fmaf(dS[4 * r + e2], P(4 * r + e2), y);
                 }
                 gr[e2] = x;
                 gw[e2] = y;
@@ -233,7 +244,7 @@ __global__ __launch_bounds__(kWThreads, 1) void bwd128_kernel(BwdArgs p, int32_t
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     x = fmaf(dS[4 * r + e2], v[r], x);
-                    y = fmaf(P[4 * r + e2], dsa[r], y);
+                    y = fmaf(P(4 * r + e2), dsa[r], y);
                 }
                 gk[e2] = x;
                 ga[e2] = y;
@@ -326,7 +337,7 @@ __global__ __launch_bounds__(kWThreads, 1) void bwd128_kernel(BwdArgs p, int32_t
         __syncthreads();
         const float *ck = p.ckpt + ((u.ckpt + c) * H + h) * (int64_t)(kWN * kWN);
 #pragma unroll 1
-        for (int q = (Lc + kSeg - 1) / kSeg - 1; q >= 0; --q) {
+        for (int q = (Lc + kSegT - 1) / kSegT - 1; q >= 0; --q) {
             relane();
             float S[16];
 #pragma unroll
@@ -336,23 +347,36 @@ __global__ __launch_bounds__(kWThreads, 1) void bwd128_kernel(BwdArgs p, int32_t
             }
             float sa[4];
 #pragma unroll 1
-            for (int e = 0; e < kSeg * q; ++e) step(S, e, sa);
+            for (int e = 0; e < kSegT * q; ++e) step(S, e, sa);
             // the states before each token of the segment, and their S a
-            float Sp[kSeg][16];
+            float Sp[kHS ? 1 : kSegT][16];
+            uint32_t Sh[kHS ? kSegT : 1][8];
 #pragma unroll
-            for (int e = 0; e < kSeg; ++e) {
-                const int te = kSeg * q + e;
+            for (int e = 0; e < kSegT; ++e) {
+                const int te = kSegT * q + e;
                 if (te < Lc) {
+                    if constexpr (kHS) {
 #pragma unroll
-                    for (int x = 0; x < 16; ++x) Sp[e][x] = S[x];
+                        for (int x = 0; x < 8; ++x) Sh[e][x] = pk_bf16(S[2 * x], S[2 * x + 1]);
+                    } else {
+#pragma unroll
+                        for (int x = 0; x < 16; ++x) Sp[e][x] = S[x];
+                    }
                     step(S, te, sa);
                     *(float4 *)(sm + L_SAV + te * kWN + row0) = make_float4(sa[0], sa[1], sa[2], sa[3]);
                 }
             }
 #pragma unroll
-            for (int e = kSeg - 1; e >= 0; --e) {
-                const int te = kSeg * q + e;
-                if (te < Lc) token(Sp[e], te, t0);
+            for (int e = kSegT - 1; e >= 0; --e) {
+                const int te = kSegT * q + e;
+                if (te < Lc) {
+                    if constexpr (kHS) {
+                        token([&](int x) { const uint32_t w2 = Sh[e][x >> 1]; return (x & 1) ? bf_hi(w2) : bf_lo(w2); },
+                              te, t0);
+                    } else {
+                        token([&](int x) { return Sp[e][x]; }, te, t0);
+                    }
+                }
             }
         }
     }
