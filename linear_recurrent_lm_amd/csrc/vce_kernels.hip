@@ -37,6 +37,8 @@
 // XCDs in turn) take consecutive tiles, and in the backward products each
 // run of 32 of them covers a 4 x 8 block of tiles, sharing A and B tiles in
 // that XCD's L2.
+#include <type_traits>
+
 #include "vce_kernels.h"
 
 namespace vce {
@@ -262,17 +264,23 @@ __global__ __launch_bounds__(128 * NWJ) void gemm_kernel(GemmArgs p) {   // Cfg:
         //   i = i0 + wi*128 + bi*32 + 8*(r/4) + 4*(l/32) + r%4,
         //   j = j0 + wj*32*WJ + bj*32 + l%32.
         const int ib = i0 + wi * 128 + 4 * (lane >> 5);
+        // tiles wholly inside the row range skip the per-element bounds tests
+        const bool inside = i0 + 2 * 128 <= (EPI == EPI_FWD ? p.V : p.I);
         if (EPI == EPI_FWD) {
-#pragma unroll
-            for (int bj = 0; bj < WJ; ++bj) {
+            // (max, sum) of this lane's column over the tile's rows, folded
+            // into the running pair; exp2 of arguments <= 0 on the hardware
+            // instruction (v_exp_f32)
+            auto fold = [&](int bj, auto IN) {
+                constexpr bool in = decltype(IN)::value;
                 float tmax = -INFINITY;
 #pragma unroll
                 for (int bi = 0; bi < WI; ++bi)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int v = ib + bi * 32 + 8 * (r >> 2) + (r & 3);
-                        if (v < p.V) tmax = fmaxf(tmax, acc[bi][bj][r] * kLog2e);
+                        if (in || v < p.V) tmax = fmaxf(tmax, acc[bi][bj][r]);
                     }
+                tmax *= kLog2e;
                 const float mnew = fmaxf(run_m[bj], tmax);
                 if (mnew != -INFINITY) {
                     float sum = 0.f;
@@ -281,12 +289,17 @@ __global__ __launch_bounds__(128 * NWJ) void gemm_kernel(GemmArgs p) {   // Cfg:
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int v = ib + bi * 32 + 8 * (r >> 2) + (r & 3);
-                            const float e = exp2f(fmaf(acc[bi][bj][r], kLog2e, -mnew));
-                            sum += v < p.V ? e : 0.f;
+                            const float e = __builtin_amdgcn_exp2f(fmaf(acc[bi][bj][r], kLog2e, -mnew));
+                            sum += (in || v < p.V) ? e : 0.f;
                         }
-                    run_s[bj] = run_s[bj] * exp2f(run_m[bj] - mnew) + sum;
+                    run_s[bj] = run_s[bj] * __builtin_amdgcn_exp2f(run_m[bj] - mnew) + sum;
                     run_m[bj] = mnew;
                 }
+            };
+#pragma unroll
+            for (int bj = 0; bj < WJ; ++bj) {
+                if (inside) fold(bj, std::true_type{});
+                else fold(bj, std::false_type{});
                 // Target logit: the one lane that holds row t of this column.
                 const int d = tgt[bj] - ib;
                 if (d >= 0 && d < 128 && ((d >> 2) & 1) == 0) {
@@ -328,9 +341,9 @@ __global__ __launch_bounds__(128 * NWJ) void gemm_kernel(GemmArgs p) {   // Cfg:
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int v = vb + e;
-                            float x = exp2f(fmaf(acc[bi][bj][r4 * 4 + e], kLog2e, -l2));
+                            float x = __builtin_amdgcn_exp2f(fmaf(acc[bi][bj][r4 * 4 + e], kLog2e, -l2));
                             x = (v == tl) ? x - 1.f : x;
-                            x = (live && v < p.I) ? x * dl : 0.f;
+                            x = (live && (inside || v < p.I)) ? x * dl : 0.f;
                             g[e] = to_bf16(x);
                         }
                         uint2 pk;
