@@ -119,3 +119,33 @@ def test_decode_variants(W, dtype, decay):
     tol = {"f32": U.TOL_F32, "bf16": U.TOL_BF16_Y, "f16": U.TOL_F16}[dtype]
     assert float(np.max(num / den)) <= tol
     assert U.unit_err_state(U.host(s_out), sr) <= U.TOL_F32
+
+
+def test_backward_gradient_dtypes_share_one_workspace(W):
+    """bf16 streams hand the per-chunk results of the sweep to the gradient
+    pass in bf16 for bf16 gradients and in fp32 for fp32 gradients. Calls of
+    either kind, alternating on one workspace buffer, each match the oracle
+    (bf16 gradients at the gradient bound, fp32 ones at 1e-4) and repeat
+    bit for bit."""
+    import torch
+    inp = synth.make_inputs(2, 273, 3, 64, seed=440, dtype="bf16", s0_std=0.1, with_dy=True,
+                            ds_out_std=0.1)
+    ts = [U.dev_stream(x, "bf16") for x in inp.streams()]
+    _, _, ckpt = W.wkv7_forward(*ts, U.dev_f32(inp.s0), checkpoints=True)
+    dy, dso = U.dev_stream(inp.dy, "bf16"), U.dev_f32(inp.ds_out)
+    ws = torch.empty(W.wkv7_workspace_bytes(2, 273, 3, W.BF16), dtype=torch.uint8, device="cuda:0")
+    _, g_ref = _oracle(inp)
+    first = {}
+    for call, f32 in enumerate((False, True, False, True)):
+        g = W.wkv7_backward(*ts, ckpt, dy, dso, grad_f32=f32, workspace=ws)
+        torch.cuda.synchronize()
+        h = {k: U.host(v) for k, v in g.items()}
+        tol = 1e-4 if f32 else U.TOL_GRAD
+        for n in NAMES:
+            assert U.unit_err_dense(h[n], g_ref[n]) <= tol, (call, n)
+        assert U.unit_err_state(h["ds0"], g_ref["ds0"]) <= 1e-4, call
+        if f32 in first:
+            for n in NAMES + ("ds0",):
+                assert np.array_equal(h[n], first[f32][n]), (call, n)
+        else:
+            first[f32] = h
