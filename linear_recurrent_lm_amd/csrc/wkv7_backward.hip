@@ -56,7 +56,7 @@ namespace wkv7 {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kChunksPerGroup = 16;               // chunks per workgroup (consecutive)
+constexpr int kChunksPerGroup = 32;               // chunks per workgroup (consecutive)
 constexpr int LD = 68;                            // row pitch of 16x64 / 64x64 arrays
 constexpr float kMinW = 9.313225746154785e-10f;   // 2^-30
 
